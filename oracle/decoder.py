@@ -1,0 +1,243 @@
+"""Plain CPU decode step of a pre-norm decoder stack with a per-session
+cache: the definition the frame-synchronous batched step must reproduce.
+
+Test infrastructure (see the package docstring).
+
+What the step computes, with the pages it follows:
+
+* Each session advances by exactly one frame per step; a frame is one
+  decoder forward at the session's next position (PersonaPlex 7B page,
+  "What Real-time Means for a Full-duplex Agent": the model processes one
+  80 ms frame at a time).
+* The sessions of a batch are independent; batching only shares the weight
+  read (Nemotron VoiceChat case study, "The solution" and "Under the hood";
+  the bandwidth blog, section 2 on concurrency).  So the batched step is S
+  single-session steps; here the projections are done as one matrix product
+  over the batch rows (a library primitive), which changes nothing per row.
+* Weights and activations in bf16, temporal cache in FP8 (PersonaPlex
+  page, "Compressing the Temporal KV cache"); the talker cache in fp32
+  (Nemotron profile.json, serving_profile precision map).
+* A session's window holds at most 1500 frames (profile.json,
+  serving_profile context_steps).
+* The depth stack runs 8 sequential steps per frame (PersonaPlex page,
+  "Predictable GPU execution").
+
+The pages give no block diagram.  Readings used (the textbook pre-norm
+decoder): RMSNorm x * (mean(x^2) + eps)^(-1/2) * g before attention and
+before the FFN, residual adds after each, final RMSNorm on the output, no
+biases; rotary embedding on adjacent pairs (2i, 2i+1) with angle
+p * base^(-2i/D), the table computed in float64 and rounded to float32;
+attention scale 1/sqrt(D), causal over 0..p including the new frame; query
+head h reads kv head floor(h * H_kv / H_q); SwiGLU FFN silu(gate) * up.  With
+an FP8 cache the new frame's key/value are stored as codes of k / sigma and
+v / sigma (static per-(layer, K|V, kv-head) scales) and every position,
+the new one included, is read back as sigma * decode(code).
+
+Arithmetic is float32 by default (``dtype=np.float64`` for the rounding
+check); inputs and weights are used exactly as given.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import fp8
+
+
+# ----------------------------------------------------------------------------
+# building blocks
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float, dtype=np.float32) -> np.ndarray:
+    """x * (mean(x^2) + eps)^(-1/2) * g over the last axis."""
+    x = x.astype(dtype)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    r = (1.0 / np.sqrt(ms + dtype(eps))).astype(dtype)
+    return (x * r * g.astype(dtype)).astype(dtype)
+
+
+def rope_table(max_pos: int, head_dim: int, base: float, dtype=np.float32):
+    """cos and sin of p * base^(-2i/D) for p < max_pos, i < D/2, evaluated
+    in float64 and rounded once to ``dtype``: arrays [max_pos][D/2]."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(dtype), np.sin(ang).astype(dtype)
+
+
+def rope(x: np.ndarray, pos: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate the pairs (2i, 2i+1) of each head vector of x [n, H, D] by the
+    angles of position pos[n]."""
+    c = cos[pos][:, None, :]
+    s = sin[pos][:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+# ----------------------------------------------------------------------------
+# cache
+
+
+class Cache:
+    """Per-slot caches of one stack: ``kv[slot]`` is [L][2 (K|V)][H_kv][T][D],
+    uint8 E4M3 codes for an FP8 cache, else values in the oracle dtype."""
+
+    def __init__(self, n_layers: int, n_kv_heads: int, max_context: int, head_dim: int,
+                 fp8_cache: bool, dtype=np.float32):
+        self.shape = (n_layers, 2, n_kv_heads, max_context, head_dim)
+        self.fp8 = fp8_cache
+        self.dtype = dtype
+        self.kv: dict[int, np.ndarray] = {}
+
+    def slot(self, s: int) -> np.ndarray:
+        if s not in self.kv:
+            self.kv[s] = np.zeros(self.shape, dtype=np.uint8 if self.fp8 else self.dtype)
+        return self.kv[s]
+
+    def store(self, s: int, layer: int, kv: int, pos: int, vec: np.ndarray, scale: np.ndarray):
+        """Write the new frame's [H_kv][D] key or value at ``pos``."""
+        c = self.slot(s)
+        if self.fp8:
+            c[layer, kv, :, pos, :] = fp8.encode(vec.astype(np.float32) /
+                                                 scale.astype(np.float32)[:, None])
+        else:
+            c[layer, kv, :, pos, :] = vec.astype(self.dtype)
+
+    def prefill(self, s: int, layer: int, values: np.ndarray, scale: np.ndarray):
+        """Fill positions 0..n-1 of one layer from raw values [2][H_kv][n][D]
+        stored the same way as new frames."""
+        c = self.slot(s)
+        n = values.shape[2]
+        if self.fp8:
+            c[layer, :, :, :n, :] = fp8.encode(values.astype(np.float32) /
+                                               scale.astype(np.float32)[:, :, None, None])
+        else:
+            c[layer, :, :, :n, :] = values.astype(self.dtype)
+
+    def read(self, s: int, layer: int, kv: int, g: int, n: int, scale: float) -> np.ndarray:
+        """Positions 0..n-1 of kv-head g read back: [n][D] in the oracle dtype."""
+        c = self.slot(s)[layer, kv, g, :n, :]
+        if self.fp8:
+            return fp8.decode(c, np.float32).astype(self.dtype) * self.dtype(scale)
+        return c.astype(self.dtype)
+
+
+# ----------------------------------------------------------------------------
+# one decoder stack, one frame
+
+
+def _stack_step(x, pos, slots, layers, n_layers, shape, eps, cos, sin, cache, kv_scale,
+                g_final, dtype):
+    """Advance rows x [n][d] (row i = slot slots[i] at new-frame index
+    pos[i]) through ``n_layers`` layers; returns the final-normed output."""
+    hq, hkv, hd = shape
+    n = x.shape[0]
+    x = x.astype(dtype)
+    inv_sqrt_d = dtype(1.0 / np.sqrt(hd))
+    for l in range(n_layers):
+        w = {k: v.astype(dtype) for k, v in layers(l).items()}
+        a = rmsnorm(x, w["g_attn"], eps, dtype)
+        q = (a @ w["wq"].T).reshape(n, hq, hd)
+        k = (a @ w["wk"].T).reshape(n, hkv, hd)
+        v = (a @ w["wv"].T).reshape(n, hkv, hd)
+        q = rope(q, pos, cos, sin)
+        k = rope(k, pos, cos, sin)
+        o = np.empty((n, hq, hd), dtype=dtype)
+        for i in range(n):
+            s, p = int(slots[i]), int(pos[i])
+            cache.store(s, l, 0, p, k[i], kv_scale[l, 0])
+            cache.store(s, l, 1, p, v[i], kv_scale[l, 1])
+            for h in range(hq):
+                g = (h * hkv) // hq
+                kh = cache.read(s, l, 0, g, p + 1, kv_scale[l, 0, g])
+                vh = cache.read(s, l, 1, g, p + 1, kv_scale[l, 1, g])
+                sc = (kh @ q[i, h]) * inv_sqrt_d
+                sc = sc - np.max(sc)
+                e = np.exp(sc)
+                wts = e / np.sum(e)
+                o[i, h] = wts @ vh
+        x = x + o.reshape(n, hq * hd) @ w["wo"].T
+        b = rmsnorm(x, w["g_ffn"], eps, dtype)
+        hid = silu(b @ w["w_gate"].T) * (b @ w["w_up"].T)
+        x = x + hid @ w["w_down"].T
+    return rmsnorm(x, g_final, eps, dtype)
+
+
+class Oracle:
+    """Reference decode step for one configuration.
+
+    ``model`` supplies float32 weights: ``layer(l)`` -> dict with wq, wk, wv,
+    wo, w_gate, w_up, w_down ([out, in]) and g_attn, g_ffn; attributes
+    g_final, kv_scale [L][2][H_kv] (ignored for fp32 caches), and for a
+    depth stack w_in, depth_layer(l), depth_g_final.
+    """
+
+    def __init__(self, cfg: dict, model, dtype=np.float32):
+        self.cfg = cfg
+        self.model = model
+        self.dtype = dtype
+        self.cache = Cache(cfg["n_layers"], cfg["n_kv_heads"], cfg["max_context"],
+                           cfg["head_dim"], cfg["kv_dtype"] == "fp8", dtype)
+        self.cos, self.sin = rope_table(cfg["max_context"], cfg["head_dim"], cfg["rope_base"], dtype)
+        if cfg["kv_dtype"] == "fp8":
+            self.kv_scale = np.asarray(model.kv_scale, dtype=np.float32)
+        else:
+            self.kv_scale = np.ones((cfg["n_layers"], 2, cfg["n_kv_heads"]), dtype=np.float32)
+        self.depth = cfg.get("depth_steps", 0) > 0
+        if self.depth:
+            if cfg["kv_dtype"] != "f32":
+                raise ValueError("the depth stack is defined with an fp32 cache only")
+            self.dcos, self.dsin = rope_table(cfg["depth_steps"], cfg["depth_head_dim"],
+                                              cfg["rope_base"], dtype)
+
+    def step(self, slots, x, pos):
+        """One frame for the active rows: slots[i] at new-frame index pos[i]
+        with input x[i].  Writes the new cache entries; returns y [n][d] and,
+        with a depth stack, the depth outputs [n][steps][depth_d]."""
+        cfg = self.cfg
+        slots = np.asarray(slots, dtype=np.int64)
+        pos = np.asarray(pos, dtype=np.int64)
+        if np.any(pos >= cfg["max_context"]) or np.any(pos < 0):
+            raise ValueError("position outside the context window")
+        y = _stack_step(np.asarray(x), pos, slots, self.model.layer, cfg["n_layers"],
+                        (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]), cfg["rms_eps"],
+                        self.cos, self.sin, self.cache, self.kv_scale, self.model.g_final,
+                        self.dtype)
+        if not self.depth:
+            return y
+        return y, self.depth_loop(y)
+
+    def depth_loop(self, y):
+        """Per-frame inner loop: c = W_in y; z_{-1} = 0; for k in 0..steps-1
+        run the depth stack on c + z_{k-1} at depth position k over a cache
+        holding only this frame's depth positions; emit z_k."""
+        cfg = self.cfg
+        n = y.shape[0]
+        dt = self.dtype
+        c = y.astype(dt) @ self.model.w_in.astype(dt).T
+        dcache = Cache(cfg["depth_layers"], cfg["depth_kv_heads"], cfg["depth_steps"],
+                       cfg["depth_head_dim"], False, dt)
+        ones = np.ones((cfg["depth_layers"], 2, cfg["depth_kv_heads"]), dtype=np.float32)
+        z = np.zeros((n, cfg["depth_d"]), dtype=dt)
+        out = np.empty((n, cfg["depth_steps"], cfg["depth_d"]), dtype=dt)
+        rows = np.arange(n)
+        for k in range(cfg["depth_steps"]):
+            z = _stack_step(c + z, np.full(n, k, dtype=np.int64), rows, self.model.depth_layer,
+                            cfg["depth_layers"],
+                            (cfg["depth_heads"], cfg["depth_kv_heads"], cfg["depth_head_dim"]),
+                            cfg["rms_eps"], self.dcos, self.dsin, dcache, ones,
+                            self.model.depth_g_final, dt)
+            out[:, k] = z
+        return out
+
+    def prefill(self, slot: int, layer: int, values: np.ndarray):
+        """Fill positions 0..n-1 of ``slot`` at ``layer`` from raw key/value
+        vectors [2][H_kv][n][D] (quantised like new frames)."""
+        self.cache.prefill(slot, layer, values, self.kv_scale[layer])

@@ -1,0 +1,326 @@
+"""Pins of the oracle's decoder step and full recompute against things
+other than themselves:
+
+* a library-built reference (torch CPU, float64): F.rms_norm,
+  F.scaled_dot_product_attention with a causal mask (GQA via enable_gqa),
+  F.silu, and the rotary embedding as complex multiplication
+  (x_{2i} + j x_{2i+1}) * exp(j p theta_i); FP8 storage through torch's own
+  float8_e4m3fn conversion;
+* incremental decode equal to the full causal recompute;
+* session isolation (other slots' inputs, caches and activity do not change
+  a session's output);
+* closed-form special cases (empty stack, constant rows, first frame,
+  zero query projection, zero gate);
+* float64 and float32 oracles agreeing to 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import synth
+from oracle import Oracle, forward_full, depth_full, rope, rope_table, fp8
+
+
+def small_cfg(**over):
+    base = synth.get_config("tiny")
+    base.update(over)
+    return base
+
+
+def rel_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+# ---------------------------------------------------------------------------
+# library-built reference
+
+
+def torch_reference(cfg, model, X, *, depth=False, fp8_cache=None):
+    """Full causal forward in float64 built from torch library routines."""
+    if depth:
+        L, hq, hkv, hd = (cfg["depth_layers"], cfg["depth_heads"], cfg["depth_kv_heads"],
+                          cfg["depth_head_dim"])
+        layer, g_final = model.depth_layer, model.depth_g_final
+        fp8_cache = False
+    else:
+        L, hq, hkv, hd = cfg["n_layers"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+        layer, g_final = model.layer, model.g_final
+        if fp8_cache is None:
+            fp8_cache = cfg["kv_dtype"] == "fp8"
+    eps = cfg["rms_eps"]
+    x = torch.from_numpy(np.asarray(X, dtype=np.float64))
+    T, d = x.shape
+    i = torch.arange(hd // 2, dtype=torch.float64)
+    theta = cfg["rope_base"] ** (-2.0 * i / hd)
+    ang = torch.arange(T, dtype=torch.float64)[:, None] * theta[None, :]
+    rot = torch.polar(torch.ones_like(ang), ang)
+
+    def rot_rows(t):  # t [T, H, hd]
+        c = torch.view_as_complex(t.reshape(T, t.shape[1], hd // 2, 2).contiguous())
+        return torch.view_as_real(c * rot[:, None, :]).reshape(T, t.shape[1], hd)
+
+    for l in range(L):
+        w = {k: torch.from_numpy(np.asarray(v, dtype=np.float64)) for k, v in layer(l).items()}
+        a = F.rms_norm(x, (d,), weight=w["g_attn"], eps=eps)
+        q = rot_rows((a @ w["wq"].T).reshape(T, hq, hd))
+        k = rot_rows((a @ w["wk"].T).reshape(T, hkv, hd))
+        v = (a @ w["wv"].T).reshape(T, hkv, hd)
+        if fp8_cache:
+            sk = torch.from_numpy(np.asarray(model.kv_scale[l, 0], dtype=np.float32))[None, :, None]
+            sv = torch.from_numpy(np.asarray(model.kv_scale[l, 1], dtype=np.float32))[None, :, None]
+            kq = (k.float() / sk)
+            vq = (v.float() / sv)
+            assert float(kq.abs().max()) < 448 and float(vq.abs().max()) < 448
+            k = kq.to(torch.float8_e4m3fn).to(torch.float64) * sk.double()
+            v = vq.to(torch.float8_e4m3fn).to(torch.float64) * sv.double()
+        o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
+                                           v.transpose(0, 1)[None], is_causal=True,
+                                           enable_gqa=(hq != hkv))
+        o = o[0].transpose(0, 1).reshape(T, hq * hd)
+        x = x + o @ w["wo"].T
+        b = F.rms_norm(x, (d,), weight=w["g_ffn"], eps=eps)
+        x = x + (F.silu(b @ w["w_gate"].T) * (b @ w["w_up"].T)) @ w["w_down"].T
+    g = torch.from_numpy(np.asarray(g_final, dtype=np.float64))
+    return F.rms_norm(x, (d,), weight=g, eps=eps).numpy()
+
+
+def frames(cfg, session, T):
+    return np.stack([synth.frame_input(cfg, session, t) for t in range(T)])
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = small_cfg()
+    model = synth.Model(cfg, gain_noise=True)
+    return cfg, model
+
+
+def test_full_matches_library_reference_fp32_cache(tiny):
+    cfg, model = tiny
+    X = frames(cfg, 0, 16)
+    ref = torch_reference(cfg, model, X)
+    got = forward_full(cfg, model, X, dtype=np.float64)
+    assert rel_err(got, ref) < 1e-12
+
+
+def test_full_matches_library_reference_fp8_cache():
+    cfg = small_cfg(kv_dtype="fp8")
+    model = synth.Model(cfg, gain_noise=True)
+    X = frames(cfg, 3, 12)
+    ref = torch_reference(cfg, model, X)
+    got = forward_full(cfg, model, X, dtype=np.float64)
+    assert rel_err(got, ref) < 1e-12
+
+
+def test_full_matches_library_reference_gqa():
+    cfg = small_cfg(n_heads=4, n_kv_heads=1, head_dim=32, d_model=128, d_ffn=256)
+    model = synth.Model(cfg, gain_noise=True)
+    X = frames(cfg, 1, 9)
+    ref = torch_reference(cfg, model, X)
+    got = forward_full(cfg, model, X, dtype=np.float64)
+    assert rel_err(got, ref) < 1e-12
+
+
+def _run_incremental(cfg, model, sessions, T, dtype):
+    orc = Oracle(cfg, model, dtype=dtype)
+    outs = {s: [] for s in sessions}
+    for t in range(T):
+        x = np.stack([synth.frame_input(cfg, s, t) for s in sessions])
+        y = orc.step(sessions, x, [t] * len(sessions))
+        for i, s in enumerate(sessions):
+            outs[s].append(y[i])
+    return {s: np.stack(v) for s, v in outs.items()}, orc
+
+
+@pytest.mark.parametrize("kv", ["f32", "fp8"])
+def test_incremental_equals_full_recompute(kv):
+    """Check (a): 16 frames stepped one at a time equal the causal forward
+    over all 16 frames, for every frame."""
+    cfg = small_cfg(kv_dtype=kv)
+    model = synth.Model(cfg, gain_noise=True)
+    outs, _ = _run_incremental(cfg, model, [0, 1], 16, np.float64)
+    for s in (0, 1):
+        full = forward_full(cfg, model, frames(cfg, s, 16), dtype=np.float64)
+        assert rel_err(outs[s], full) < 1e-10
+        # and in float32, within the rounding budget of the step
+    outs32, _ = _run_incremental(cfg, model, [0, 1], 16, np.float32)
+    for s in (0, 1):
+        full = forward_full(cfg, model, frames(cfg, s, 16), dtype=np.float64)
+        assert rel_err(outs32[s], full) < 1e-5 if kv == "f32" else 2e-3
+
+
+def test_session_isolation(tiny):
+    """Check (b): perturbing other slots' inputs, caches and activity leaves
+    a session's output and cache bit-identical."""
+    cfg, model = tiny
+    base = Oracle(cfg, model)
+    pert = Oracle(cfg, model)
+    rng = np.random.default_rng(5)
+    # slot 1 is the session under test in both; slot 0 differs
+    for t in range(6):
+        x1 = synth.frame_input(cfg, 11, t)
+        xa = synth.frame_input(cfg, 21, t)
+        xb = (rng.standard_normal(cfg["d_model"]) * 3).astype(np.float32)
+        ya = base.step([0, 1], np.stack([xa, x1]), [t, t])
+        yb = pert.step([0, 1], np.stack([xb, x1]), [t, t])
+        assert np.array_equal(ya[1], yb[1])
+    # garbage in slot 0's cache of the perturbed run, then slot 0 inactive
+    pert.cache.slot(0)[...] = rng.standard_normal(pert.cache.shape).astype(np.float32) * 1e3
+    x1 = synth.frame_input(cfg, 11, 6)
+    ya = base.step([0, 1], np.stack([synth.frame_input(cfg, 21, 6), x1]), [6, 6])
+    yb = pert.step([1], x1[None], [6])
+    # the row count differs here (2 vs 1), so the BLAS blocking may differ
+    assert rel_err(yb[0], ya[1]) < 1e-6
+    assert np.array_equal(base.cache.slot(1), pert.cache.slot(1)) or \
+        rel_err(pert.cache.slot(1), base.cache.slot(1)) < 1e-6
+
+
+def test_empty_stack_is_rmsnorm_of_input():
+    cfg = small_cfg(n_layers=0)
+    model = synth.Model(cfg, gain_noise=True)
+    e = synth.frame_input(cfg, 0, 0)
+    y = Oracle(cfg, model, dtype=np.float64).step([0], e[None], [0])[0]
+    ms = np.mean(e.astype(np.float64) ** 2)
+    expect = e.astype(np.float64) / np.sqrt(ms + cfg["rms_eps"]) * model.g_final.astype(np.float64)
+    assert rel_err(y, expect) < 1e-14
+
+
+def test_constant_row():
+    cfg = small_cfg(n_layers=0)
+    model = synth.Model(cfg, gain_noise=True)
+    c = 0.37
+    y = Oracle(cfg, model, dtype=np.float64).step([0], np.full((1, cfg["d_model"]), c), [0])[0]
+    expect = model.g_final.astype(np.float64) * c / np.sqrt(c * c + cfg["rms_eps"])
+    assert rel_err(y, expect) < 1e-14
+
+
+def _one_layer(kv="f32", zero=()):
+    cfg = small_cfg(n_layers=1, kv_dtype=kv)
+    return cfg, synth.Model(cfg, gain_noise=True, zero=zero)
+
+
+def test_first_frame_attends_to_itself_only():
+    """p = 0: the softmax has one weight equal to 1, so the output does not
+    depend on the query/key projections and attention returns V_hat_0."""
+    cfg, m = _one_layer(zero=("w_gate",))
+    e = synth.frame_input(cfg, 0, 0)
+    y = Oracle(cfg, m, dtype=np.float64).step([0], e[None], [0])[0]
+    w = m.layer(0)
+    e64 = e.astype(np.float64)
+    a = e64 / np.sqrt(np.mean(e64 ** 2) + cfg["rms_eps"]) * w["g_attn"]
+    x = e64 + w["wo"] @ (w["wv"] @ a)
+    expect = x / np.sqrt(np.mean(x ** 2) + cfg["rms_eps"]) * m.g_final
+    assert rel_err(y, expect) < 1e-12
+    # different q/k projections: same output
+    cfg2, m2 = _one_layer(zero=("w_gate", "wq", "wk"))
+    y2 = Oracle(cfg2, m2, dtype=np.float64).step([0], e[None], [0])[0]
+    assert rel_err(y2, y) < 1e-13
+
+
+@pytest.mark.parametrize("kv", ["f32", "fp8"])
+def test_zero_query_gives_uniform_average(kv):
+    """W_q = 0: every score is 0, so attention is the plain mean of the
+    cached values over positions 0..p (new frame included)."""
+    cfg, m = _one_layer(kv, zero=("wq", "w_gate"))
+    orc = Oracle(cfg, m, dtype=np.float64)
+    p = 9
+    vals = synth.prefill_values(cfg, 4, 0, p)
+    orc.prefill(0, 0, vals)
+    e = synth.frame_input(cfg, 4, p)
+    y = orc.step([0], e[None], [p])[0]
+    w = m.layer(0)
+    e64 = e.astype(np.float64)
+    a = e64 / np.sqrt(np.mean(e64 ** 2) + cfg["rms_eps"]) * w["g_attn"]
+    vnew = (w["wv"] @ a).reshape(cfg["n_kv_heads"], cfg["head_dim"])
+    V = np.concatenate([vals[1].astype(np.float64), vnew[:, None, :]], axis=1)  # [H][p+1][D]
+    if kv == "fp8":
+        s = m.kv_scale[0, 1].astype(np.float32)[:, None, None]
+        V = fp8.decode(fp8.encode(V.astype(np.float32) / s)).astype(np.float64) * s
+    o = V.mean(axis=1).reshape(-1)
+    x = e64 + w["wo"] @ o
+    expect = x / np.sqrt(np.mean(x ** 2) + cfg["rms_eps"]) * m.g_final
+    assert rel_err(y, expect) < 1e-12
+
+
+def test_zero_gate_ffn_adds_nothing():
+    cfg, m = _one_layer(zero=("w_gate",))
+    cfg2, m2 = _one_layer(zero=("w_gate", "w_down"))
+    o1 = Oracle(cfg, m, dtype=np.float64)
+    o2 = Oracle(cfg2, m2, dtype=np.float64)
+    for t in range(4):
+        e = synth.frame_input(cfg, 2, t)[None]
+        assert np.array_equal(o1.step([0], e, [t]), o2.step([0], e, [t]))
+
+
+def test_float64_and_float32_agree():
+    cfg = small_cfg()
+    model = synth.Model(cfg)
+    o64, _ = _run_incremental(cfg, model, [0, 1], 8, np.float64)
+    o32, _ = _run_incremental(cfg, model, [0, 1], 8, np.float32)
+    for s in (0, 1):
+        assert rel_err(o32[s], o64[s]) < 1e-5
+
+
+def test_talker_shape_float64_and_float32_agree():
+    cfg = small_cfg(n_layers=2, d_model=128, n_heads=4, n_kv_heads=1, head_dim=64, d_ffn=384,
+                    depth_steps=3, depth_layers=2, depth_d=96, depth_heads=2, depth_kv_heads=2,
+                    depth_head_dim=48, depth_ffn=160)
+    model = synth.Model(cfg)
+    ys = {}
+    for dt in (np.float64, np.float32):
+        orc = Oracle(cfg, model, dtype=dt)
+        for t in range(4):
+            x = np.stack([synth.frame_input(cfg, s, t) for s in (0, 1)])
+            ys[dt] = orc.step([0, 1], x, [t, t])
+    assert rel_err(ys[np.float32][0], ys[np.float64][0]) < 1e-5
+    assert rel_err(ys[np.float32][1], ys[np.float64][1]) < 1e-5
+
+
+def test_depth_loop_is_teacher_forced_causal_forward():
+    """The depth loop's k-th output equals row k of a causal forward of the
+    depth stack over the inputs it actually saw (c + z_{k-1}), and that
+    forward equals the library-built reference."""
+    cfg = small_cfg(n_layers=1, d_model=128, n_heads=4, n_kv_heads=1, head_dim=64, d_ffn=384,
+                    depth_steps=8, depth_layers=2, depth_d=96, depth_heads=2, depth_kv_heads=2,
+                    depth_head_dim=48, depth_ffn=160)
+    model = synth.Model(cfg, gain_noise=True)
+    orc = Oracle(cfg, model, dtype=np.float64)
+    x = np.stack([synth.frame_input(cfg, s, 0) for s in (0, 1)])
+    y, z = orc.step([0, 1], x, [0, 0])
+    for i in range(2):
+        c = model.w_in.astype(np.float64) @ y[i]
+        inputs = np.stack([c] + [c + z[i, k] for k in range(cfg["depth_steps"] - 1)])
+        full = depth_full(cfg, model, inputs, dtype=np.float64)
+        assert rel_err(z[i], full) < 1e-10
+        ref = torch_reference(cfg, model, inputs, depth=True)
+        assert rel_err(full, ref) < 1e-12
+
+
+def test_rope_pins():
+    D, base = 64, 10000.0
+    cos, sin = rope_table(1500, D, base, np.float64)
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    # table against a float64 evaluation: within one float32 ulp
+    c32, s32 = rope_table(1500, D, base, np.float32)
+    assert np.all(np.abs(c32 - cos) <= np.spacing(np.abs(c32).astype(np.float32)))
+    assert np.all(np.abs(s32 - sin) <= np.spacing(np.abs(s32).astype(np.float32)))
+    # pair norms preserved
+    for p in (0, 1, 77, 1499):
+        r = rope(q, np.array([p]), cos, sin)
+        assert np.allclose(np.hypot(r[..., 0::2], r[..., 1::2]),
+                           np.hypot(q[..., 0::2], q[..., 1::2]), rtol=1e-13)
+    # scores depend only on the offset
+    for m, n, c in ((5, 3, 100), (0, 0, 1400), (1499, 10, -8)):
+        a = np.sum(rope(q, np.array([m]), cos, sin) * rope(k, np.array([n]), cos, sin))
+        b = np.sum(rope(q, np.array([m + c]), cos, sin) * rope(k, np.array([n + c]), cos, sin))
+        assert abs(a - b) < 1e-10
+    # direction: the complex-multiplication form of the same rotation
+    p = 321
+    zc = (q[0, 0, 0::2] + 1j * q[0, 0, 1::2]) * np.exp(1j * p * base ** (-np.arange(D // 2) * 2.0 / D))
+    r = rope(q, np.array([p]), cos, sin)[0, 0]
+    assert np.allclose(r[0::2], zc.real, atol=1e-12) and np.allclose(r[1::2], zc.imag, atol=1e-12)
