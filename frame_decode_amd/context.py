@@ -1,0 +1,155 @@
+"""Context: one serving profile on one GPU, driven through the C ABI.
+
+Method names follow the C calls (fd_alloc_slots, fd_step, ...).  Buffers
+are torch uint8 device tensors sized by fd_plan; the weights passed in are
+torch device tensors in nn.Linear [out, in] layout (bf16 or fp32), gains
+and FP8 scales fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import abi
+from .abi import (FdBuffers, FdConfig, FdError, FdKvView, FdLayerWeights, FdSizes, FdWeights,
+                  config_from_dict)
+
+
+def _lib():
+    from . import lib
+    return lib()
+
+
+def _check(st: int, ctx=None):
+    if st != abi.FD_OK:
+        L = _lib()
+        msg = L.fd_last_error(ctx).decode() if ctx is not None else L.fd_last_error(None).decode()
+        raise FdError(st, f"{L.fd_status_str(st).decode()}: {msg}")
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def fd_plan(cfg: dict) -> dict:
+    c = config_from_dict(cfg)
+    s = FdSizes()
+    _check(_lib().fd_plan(ctypes.byref(c), ctypes.byref(s)))
+    return {"packed_weights": s.packed_weights, "kv_arena": s.kv_arena,
+            "workspace": s.workspace, "slot_table": s.slot_table}
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class Context:
+    """Owns the device buffers and the fd_ctx of one profile.
+
+    weights: {"layers": [ {wq, wk, wv, wo, w_gate, w_up, w_down, g_attn,
+    g_ffn} ...], "g_final", "kv_scale" (FP8 caches), and with a depth stack
+    "w_in", "depth_layers", "depth_g_final"} as torch device tensors.
+    """
+
+    def __init__(self, cfg: dict, weights: dict, device="cuda", stream=None):
+        self.cfg = dict(cfg)
+        self.device = torch.device(device)
+        self._c = config_from_dict(cfg)
+        self.sizes = fd_plan(cfg)
+        mk = lambda n: torch.empty(max(int(n), 256), dtype=torch.uint8, device=self.device)  # noqa: E731
+        self.packed = mk(self.sizes["packed_weights"])
+        self.arena = mk(self.sizes["kv_arena"])
+        self.workspace = mk(self.sizes["workspace"])
+        self.slot_table = mk(self.sizes["slot_table"])
+        self._keep = []  # ctypes arrays referenced by FdWeights during init
+
+        def layer_array(layers):
+            arr = (FdLayerWeights * max(1, len(layers)))()
+            for i, lw in enumerate(layers):
+                for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "g_attn", "g_ffn"):
+                    setattr(arr[i], n, _ptr(lw[n]))
+            self._keep.append(arr)
+            return arr
+
+        w = FdWeights()
+        w.layers = layer_array(weights["layers"])
+        w.g_final = _ptr(weights["g_final"])
+        w.kv_scale = _ptr(weights.get("kv_scale"))
+        if cfg.get("depth_steps", 0):
+            w.w_in = _ptr(weights["w_in"])
+            w.depth_layers = layer_array(weights["depth_layers"])
+            w.depth_g_final = _ptr(weights["depth_g_final"])
+        b = FdBuffers(_ptr(self.packed), _ptr(self.arena), _ptr(self.workspace),
+                      _ptr(self.slot_table))
+        self._ctx = ctypes.c_void_p()
+        _check(_lib().fd_init(ctypes.byref(self._c), ctypes.byref(w), ctypes.byref(b),
+                              ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(self._ctx)))
+        self._keep.clear()
+
+    # -- C calls ------------------------------------------------------------
+    def fd_alloc_slots(self, n: int) -> list[int]:
+        out = (ctypes.c_int32 * max(1, n))()
+        _check(_lib().fd_alloc_slots(self._ctx, n, out), self._ctx)
+        return [int(out[i]) for i in range(n)]
+
+    def fd_free(self, slots) -> None:
+        arr = (ctypes.c_int32 * max(1, len(slots)))(*[int(s) for s in slots])
+        _check(_lib().fd_free(self._ctx, arr, len(slots)), self._ctx)
+
+    def fd_step(self, x_in, y_out, depth_out=None, stream=None) -> None:
+        _check(_lib().fd_step(self._ctx, ctypes.c_void_p(_ptr(x_in)), ctypes.c_void_p(_ptr(y_out)),
+                              ctypes.c_void_p(_ptr(depth_out)),
+                              ctypes.c_void_p(_stream_handle(stream))), self._ctx)
+
+    def fd_set_position(self, slot: int, pos: int) -> None:
+        _check(_lib().fd_set_position(self._ctx, slot, pos), self._ctx)
+
+    def fd_slot_state(self, slot: int) -> tuple[int, int]:
+        a, p = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib().fd_slot_state(self._ctx, slot, ctypes.byref(a), ctypes.byref(p)), self._ctx)
+        return int(a.value), int(p.value)
+
+    def fd_kv_write(self, slot: int, layer: int, t0: int, values: torch.Tensor, stream=None) -> None:
+        """values: fp32 device tensor [2][n_kv_heads][n][head_dim]."""
+        assert values.dtype == torch.float32 and values.is_contiguous() and values.dim() == 4
+        _check(_lib().fd_kv_write(self._ctx, slot, layer, t0, int(values.shape[2]),
+                                  ctypes.c_void_p(_ptr(values)),
+                                  ctypes.c_void_p(_stream_handle(stream))), self._ctx)
+
+    def fd_kv_layout(self) -> dict:
+        v = FdKvView()
+        _check(_lib().fd_kv_layout(self._ctx, ctypes.byref(v)), self._ctx)
+        return {f: getattr(v, f) for f, _ in FdKvView._fields_}
+
+    def fd_sync(self, stream=None) -> None:
+        _check(_lib().fd_sync(self._ctx, ctypes.c_void_p(_stream_handle(stream))), self._ctx)
+
+    def fd_destroy(self) -> None:
+        if self._ctx:
+            _check(_lib().fd_destroy(self._ctx))
+            self._ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.fd_destroy()
+        except Exception:
+            pass
+
+    # -- views --------------------------------------------------------------
+    def arena_view(self) -> torch.Tensor:
+        """The cache arena as a [S][L][2][H_kv][T][D] tensor (uint8 codes or fp32)."""
+        c = self.cfg
+        eb = 1 if c["kv_dtype"] == "fp8" else 4
+        n = c["max_slots"] * c["n_layers"] * 2 * c["n_kv_heads"] * c["max_context"] * c["head_dim"]
+        t = self.arena[: n * eb]
+        if eb == 4:
+            t = t.view(torch.float32)
+        return t.view(c["max_slots"], c["n_layers"], 2, c["n_kv_heads"], c["max_context"],
+                      c["head_dim"])
+
+    def slot_table_view(self) -> torch.Tensor:
+        S = self.cfg["max_slots"]
+        return self.slot_table[: 8 * S].view(torch.int32).view(2, S)

@@ -1,0 +1,572 @@
+// C ABI of the decode step: profile validation, weight packing, the slot
+// table, and the per-frame launch sequence.  Declarations and contracts are
+// in include/fd.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/fd.h"
+#include "fd_kernels.h"
+#include "fd_plan.h"
+#include "slot_pool.h"
+
+namespace {
+
+thread_local std::string g_global_err;
+
+constexpr int kRing = 4;
+
+}  // namespace
+
+struct fd_ctx {
+    fd::Plan plan;
+    fd::SlotPool slots;
+    fd_buffers buf{};
+    int device = 0;
+    std::string err;
+    int32_t* pinned[kRing] = {};
+    hipEvent_t ev[kRing] = {};
+    bool ev_used[kRing] = {};
+    int ring = 0;
+    explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context) {}
+};
+
+namespace {
+
+fd_status fail(fd_ctx* c, fd_status st, const std::string& msg) {
+    if (c) c->err = msg;
+    else g_global_err = msg;
+    return st;
+}
+
+fd_status hip_fail(fd_ctx* c, hipError_t e, const char* where) {
+    return fail(c, FD_E_DEVICE, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p) { return p && ((uintptr_t)p % fd::kAlign) == 0; }
+
+uint8_t* P(const fd_ctx* c, uint64_t off) { return (uint8_t*)c->buf.packed_weights + off; }
+uint8_t* Wk(const fd_ctx* c, uint64_t off) { return (uint8_t*)c->buf.workspace + off; }
+
+int32_t* slot_active(const fd_ctx* c) { return (int32_t*)c->buf.slot_table; }
+int32_t* slot_pos(const fd_ctx* c) { return (int32_t*)c->buf.slot_table + c->plan.S; }
+
+fd_status check_layer(const fd_layer_weights& lw) {
+    if (!lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.w_gate || !lw.w_up || !lw.w_down ||
+        !lw.g_attn || !lw.g_ffn)
+        return FD_E_INVAL;
+    return FD_OK;
+}
+
+hipError_t pack(const fd::GemmShape& g, int wt, const void* s0, int r0, const void* s1, int r1,
+                const void* s2, int interleave, uint8_t* dst, hipStream_t st) {
+    fd::PackArgs a{};
+    a.src[0] = s0;
+    a.src[1] = s1;
+    a.src[2] = s2;
+    a.rows[0] = r0;
+    a.rows[1] = r1;
+    a.rows[2] = 0;
+    a.interleave = interleave;
+    a.N = g.N;
+    a.K = g.K;
+    a.KB = g.KB;
+    a.dst = dst;
+    return fd::launch_pack(a, wt, st);
+}
+
+hipError_t pack_stack(fd_ctx* c, const fd::StackPlan& sp, const fd_layer_weights* lw,
+                      const float* g_final, hipStream_t st) {
+    const fd::StackDims& d = sp.dims;
+    const int wt = c->plan.wt;
+    hipError_t e = hipSuccess;
+    for (int l = 0; l < d.L && e == hipSuccess; ++l) {
+        const fd::LayerOffsets& lo = sp.layers[l];
+        e = pack(sp.qkv, wt, lw[l].wq, d.hq * d.hd, lw[l].wk, d.hkv * d.hd, lw[l].wv, 0,
+                 P(c, lo.qkv), st);
+        if (e == hipSuccess) e = pack(sp.o, wt, lw[l].wo, d.d, nullptr, 0, nullptr, 0, P(c, lo.o), st);
+        if (e == hipSuccess)
+            e = pack(sp.gu, wt, lw[l].w_gate, 0, lw[l].w_up, 0, nullptr, 1, P(c, lo.gu), st);
+        if (e == hipSuccess)
+            e = pack(sp.down, wt, lw[l].w_down, d.d, nullptr, 0, nullptr, 0, P(c, lo.down), st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(P(c, lo.g_attn), lw[l].g_attn, 4ull * d.d, hipMemcpyDeviceToDevice, st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(P(c, lo.g_ffn), lw[l].g_ffn, 4ull * d.d, hipMemcpyDeviceToDevice, st);
+    }
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(P(c, sp.g_final), g_final, 4ull * d.d, hipMemcpyDeviceToDevice, st);
+    return e;
+}
+
+// Constant tables of one stack: rotary cos/sin (double -> fp32), and the
+// per-(layer, kv head) scale factors used by the append and the softmax.
+hipError_t upload_tables(fd_ctx* c, const fd::StackPlan& sp, const std::vector<float>& sig,
+                         bool fp8, hipStream_t st) {
+    const fd::StackDims& d = sp.dims;
+    const int Lm = std::max(d.L, 1);
+    std::vector<float> rope((size_t)d.T * d.hd);
+    for (int p = 0; p < d.T; ++p)
+        for (int i = 0; i < d.hd / 2; ++i) {
+            const double theta = std::pow((double)c->plan.cfg.rope_base, -2.0 * i / d.hd);
+            const double ang = (double)p * theta;
+            rope[((size_t)p * (d.hd / 2) + i) * 2 + 0] = (float)std::cos(ang);
+            rope[((size_t)p * (d.hd / 2) + i) * 2 + 1] = (float)std::sin(ang);
+        }
+    std::vector<float> qs((size_t)Lm * d.hkv), kv((size_t)Lm * 2 * d.hkv), vs((size_t)Lm * d.hkv);
+    const double log2e = 1.4426950408889634;
+    for (int l = 0; l < d.L; ++l)
+        for (int g = 0; g < d.hkv; ++g) {
+            const float sk = fp8 ? sig[((size_t)l * 2 + 0) * d.hkv + g] : 1.0f;
+            const float sv = fp8 ? sig[((size_t)l * 2 + 1) * d.hkv + g] : 1.0f;
+            qs[(size_t)l * d.hkv + g] = (float)(log2e * (double)sk / std::sqrt((double)d.hd));
+            kv[((size_t)l * 2 + 0) * d.hkv + g] = sk;
+            kv[((size_t)l * 2 + 1) * d.hkv + g] = sv;
+            vs[(size_t)l * d.hkv + g] = sv;
+        }
+    hipError_t e = hipMemcpyAsync(P(c, sp.rope), rope.data(), rope.size() * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(P(c, sp.qscale), qs.data(), qs.size() * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(P(c, sp.kvsig), kv.data(), kv.size() * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(P(c, sp.vscale), vs.data(), vs.size() * 4, hipMemcpyHostToDevice, st);
+    // pageable sources: make sure the copies are done before the vectors die
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    return e;
+}
+
+struct CacheRef {
+    uint8_t* base;
+    uint64_t slot, layer, kv, head, pos;
+    int fp8;
+};
+
+// One decoder stack over the session rows already embedded in ws_x/ws_xg
+// (norm partial sums in ss_a).  Leaves the residual stream in ws_x and its
+// final partial sums in ss_a; returns their count through *nss_out.
+hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, int pos_override,
+                     hipStream_t st, int* nss_out) {
+    const fd::Plan& pl = c->plan;
+    const fd::StackDims& d = sp.dims;
+    const int wt = pl.wt;
+    const float inv_d = 1.0f / (float)d.d;
+    const float eps = pl.cfg.rms_eps;
+    int nss = 1;
+    hipError_t e = hipSuccess;
+    for (int l = 0; l < d.L && e == hipSuccess; ++l) {
+        const fd::LayerOffsets& lo = sp.layers[l];
+        uint8_t* layer_cache = cache.base + (size_t)l * cache.layer;
+
+        fd::GemmArgs g{};
+        g.Sp = pl.Sp;
+        g.S = pl.S;
+        g.MT = pl.MT;
+        g.part = (float*)Wk(c, pl.ws_part);
+        g.cnt = (int*)Wk(c, pl.ws_cnt);
+        g.inv_d = inv_d;
+        g.eps = eps;
+        g.active = slot_active(c);
+        g.pos = slot_pos(c);
+        g.pos_override = pos_override;
+
+        // QKV with the attention norm, rotary, append
+        fd::GemmArgs q = g;
+        const fd::GemmShape& sq = sp.qkv;
+        q.W = P(c, lo.qkv);
+        q.X = Wk(c, pl.ws_xg);
+        q.K = sq.K; q.KB = sq.KB; q.NB = sq.NB; q.P = sq.P; q.MG = sq.MG;
+        q.epi = fd::EPI_QKV;
+        q.ss_in = (const float*)Wk(c, pl.ws_ss_a);
+        q.nss = nss;
+        q.q_out = (float*)Wk(c, pl.ws_q);
+        q.hq = d.hq; q.hkv = d.hkv; q.hd = d.hd;
+        q.rope = (const float*)P(c, sp.rope);
+        q.rope_T = d.T;
+        q.qscale = (const float*)P(c, sp.qscale) + (size_t)l * d.hkv;
+        q.kvsig = (const float*)P(c, sp.kvsig) + (size_t)l * 2 * d.hkv;
+        q.kv_fp8 = cache.fp8;
+        q.arena = layer_cache;
+        q.slot_stride = cache.slot; q.kv_stride = cache.kv; q.head_stride = cache.head; q.pos_stride = cache.pos;
+        e = fd::launch_gemm(q, wt, sq.R, sq.MTG, sq.grid(), st);
+        if (e != hipSuccess) break;
+
+        fd::AttnArgs at{};
+        at.q = (const float*)Wk(c, pl.ws_q);
+        at.arena = layer_cache;
+        at.slot_stride = cache.slot; at.kv_stride = cache.kv; at.head_stride = cache.head; at.pos_stride = cache.pos;
+        at.vscale = (const float*)P(c, sp.vscale) + (size_t)l * d.hkv;
+        at.active = slot_active(c);
+        at.pos = slot_pos(c);
+        at.pos_override = pos_override;
+        at.S = pl.S; at.hq = d.hq; at.hkv = d.hkv; at.tc = sp.attn.tc; at.n_chunks = sp.attn.n_chunks;
+        at.T = d.T;
+        at.part = (float*)Wk(c, pl.ws_apart);
+        at.cnt = (int*)Wk(c, pl.ws_acnt);
+        at.o_out = Wk(c, pl.ws_o);
+        e = fd::launch_attn(at, wt, q.kv_fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
+        if (e != hipSuccess) break;
+
+        fd::GemmArgs o = g;
+        const fd::GemmShape& so = sp.o;
+        o.W = P(c, lo.o);
+        o.X = Wk(c, pl.ws_o);
+        o.K = so.K; o.KB = so.KB; o.NB = so.NB; o.P = so.P; o.MG = so.MG;
+        o.epi = fd::EPI_RESID;
+        o.x = (float*)Wk(c, pl.ws_x);
+        o.xg = Wk(c, pl.ws_xg);
+        o.g_next = (const float*)P(c, lo.g_ffn);
+        o.ss_out = (float*)Wk(c, pl.ws_ss_f);
+        o.ld = d.d;
+        e = fd::launch_gemm(o, wt, so.R, so.MTG, so.grid(), st);
+        if (e != hipSuccess) break;
+
+        fd::GemmArgs u = g;
+        const fd::GemmShape& su = sp.gu;
+        u.W = P(c, lo.gu);
+        u.X = Wk(c, pl.ws_xg);
+        u.K = su.K; u.KB = su.KB; u.NB = su.NB; u.P = su.P; u.MG = su.MG;
+        u.epi = fd::EPI_GU;
+        u.ss_in = (const float*)Wk(c, pl.ws_ss_f);
+        u.nss = so.n_groups;
+        u.h_out = Wk(c, pl.ws_h);
+        u.F = d.f;
+        e = fd::launch_gemm(u, wt, su.R, su.MTG, su.grid(), st);
+        if (e != hipSuccess) break;
+
+        fd::GemmArgs dn = g;
+        const fd::GemmShape& sd = sp.down;
+        dn.W = P(c, lo.down);
+        dn.X = Wk(c, pl.ws_h);
+        dn.K = sd.K; dn.KB = sd.KB; dn.NB = sd.NB; dn.P = sd.P; dn.MG = sd.MG;
+        dn.epi = fd::EPI_RESID;
+        dn.x = (float*)Wk(c, pl.ws_x);
+        dn.xg = Wk(c, pl.ws_xg);
+        dn.g_next = (const float*)P(c, l + 1 < d.L ? sp.layers[l + 1].g_attn : sp.g_final);
+        dn.ss_out = (float*)Wk(c, pl.ws_ss_a);
+        dn.ld = d.d;
+        e = fd::launch_gemm(dn, wt, sd.R, sd.MTG, sd.grid(), st);
+        nss = sd.n_groups;
+    }
+    *nss_out = nss;
+    return e;
+}
+
+hipError_t flush_slots(fd_ctx* c, hipStream_t st) {
+    if (!c->slots.dirty()) return hipSuccess;
+    const int i = c->ring;
+    c->ring = (c->ring + 1) % kRing;
+    hipError_t e = hipSuccess;
+    if (c->ev_used[i]) e = hipEventSynchronize(c->ev[i]);
+    if (e != hipSuccess) return e;
+    c->slots.image(c->pinned[i]);
+    e = hipMemcpyAsync(c->buf.slot_table, c->pinned[i], 8ull * c->plan.S, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(c->ev[i], st);
+    if (e != hipSuccess) return e;
+    c->ev_used[i] = true;
+    c->slots.clear_dirty();
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fd_status_str(fd_status s) {
+    switch (s) {
+        case FD_OK: return "FD_OK";
+        case FD_E_INVAL: return "FD_E_INVAL";
+        case FD_E_UNSUPPORTED: return "FD_E_UNSUPPORTED";
+        case FD_E_NOSLOT: return "FD_E_NOSLOT";
+        case FD_E_BADSLOT: return "FD_E_BADSLOT";
+        case FD_E_CTXFULL: return "FD_E_CTXFULL";
+        case FD_E_DEVICE: return "FD_E_DEVICE";
+        case FD_E_STATE: return "FD_E_STATE";
+        default: return "FD_E_UNKNOWN";
+    }
+}
+
+const char* fd_last_error(fd_ctx* ctx) { return ctx ? ctx->err.c_str() : g_global_err.c_str(); }
+
+fd_status fd_plan(const fd_config* cfg, fd_sizes* out) {
+    if (!cfg || !out) return fail(nullptr, FD_E_INVAL, "null argument");
+    fd::Plan p;
+    std::string err;
+    fd_status st = fd::make_plan(*cfg, &p, &err);
+    if (st != FD_OK) return fail(nullptr, st, err);
+    out->packed_weights = p.packed_bytes;
+    out->kv_arena = p.kv_bytes_total;
+    out->workspace = p.workspace_bytes;
+    out->slot_table = p.slot_table_bytes;
+    return FD_OK;
+}
+
+fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* buf, void* stream,
+                  fd_ctx** out) {
+    if (!cfg || !w || !buf || !out) return fail(nullptr, FD_E_INVAL, "null argument");
+    fd::Plan p;
+    std::string err;
+    fd_status st = fd::make_plan(*cfg, &p, &err);
+    if (st != FD_OK) return fail(nullptr, st, err);
+    if (!aligned(buf->packed_weights) || !aligned(buf->kv_arena) || !aligned(buf->workspace) ||
+        !aligned(buf->slot_table))
+        return fail(nullptr, FD_E_INVAL, "buffers must be non-null and 256-byte aligned");
+    if (p.main.dims.L > 0 && !w->layers) return fail(nullptr, FD_E_INVAL, "null layer array");
+    for (int l = 0; l < p.main.dims.L; ++l)
+        if (check_layer(w->layers[l]) != FD_OK) return fail(nullptr, FD_E_INVAL, "null weight pointer");
+    if (!w->g_final) return fail(nullptr, FD_E_INVAL, "null g_final");
+    if (p.kv_fp8 && !w->kv_scale) return fail(nullptr, FD_E_INVAL, "FP8 cache needs kv_scale");
+    if (p.depth) {
+        if (!w->w_in || !w->depth_g_final || (p.dstack.dims.L > 0 && !w->depth_layers))
+            return fail(nullptr, FD_E_INVAL, "null depth-stack pointer");
+        for (int l = 0; l < p.dstack.dims.L; ++l)
+            if (check_layer(w->depth_layers[l]) != FD_OK)
+                return fail(nullptr, FD_E_INVAL, "null depth weight pointer");
+    }
+
+    fd_ctx* c = new (std::nothrow) fd_ctx(p);
+    if (!c) return fail(nullptr, FD_E_DEVICE, "out of host memory");
+    c->buf = *buf;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipGetDevice(&c->device);
+    for (int i = 0; i < kRing && e == hipSuccess; ++i) {
+        e = hipHostMalloc((void**)&c->pinned[i], 8ull * p.S, hipHostMallocDefault);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
+    }
+    // scales to the host (FP8 only) for the derived tables
+    std::vector<float> sig;
+    if (e == hipSuccess && p.kv_fp8) {
+        sig.resize((size_t)p.main.dims.L * 2 * p.main.dims.hkv);
+        if (!sig.empty()) {
+            e = hipMemcpyAsync(sig.data(), w->kv_scale, sig.size() * 4, hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess) e = hipStreamSynchronize(s);
+        }
+        for (float v : sig)
+            if (e == hipSuccess && !(v > 0.0f && std::isfinite(v))) {
+                delete c;
+                return fail(nullptr, FD_E_INVAL, "kv_scale entries must be finite and > 0");
+            }
+    }
+    if (e == hipSuccess) e = hipMemsetAsync(buf->workspace, 0, p.workspace_bytes, s);
+    if (e == hipSuccess) e = hipMemsetAsync(buf->slot_table, 0, p.slot_table_bytes, s);
+    if (e == hipSuccess) e = pack_stack(c, p.main, w->layers, w->g_final, s);
+    if (e == hipSuccess) e = upload_tables(c, p.main, sig, p.kv_fp8, s);
+    if (e == hipSuccess && p.depth) {
+        e = pack(p.win, p.wt, w->w_in, p.win.N, nullptr, 0, nullptr, 0, P(c, p.w_in), s);
+        if (e == hipSuccess) e = pack_stack(c, p.dstack, w->depth_layers, w->depth_g_final, s);
+        if (e == hipSuccess) e = upload_tables(c, p.dstack, std::vector<float>(), false, s);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        std::string msg = std::string("fd_init: ") + hipGetErrorString(e);
+        fd_destroy(c);
+        return fail(nullptr, FD_E_DEVICE, msg);
+    }
+    c->slots.mark_dirty();
+    *out = c;
+    return FD_OK;
+}
+
+fd_status fd_alloc_slots(fd_ctx* c, int32_t n, int32_t* slots_out) {
+    if (!c) return FD_E_INVAL;
+    fd_status st = c->slots.alloc(n, slots_out);
+    if (st != FD_OK) return fail(c, st, st == FD_E_NOSLOT ? "not enough free slots" : "bad argument");
+    return FD_OK;
+}
+
+fd_status fd_free(fd_ctx* c, const int32_t* ids, int32_t n) {
+    if (!c) return FD_E_INVAL;
+    fd_status st = c->slots.free(ids, n);
+    if (st != FD_OK) return fail(c, st, "invalid, unallocated or repeated slot id");
+    return FD_OK;
+}
+
+fd_status fd_set_position(fd_ctx* c, int32_t slot, int32_t pos) {
+    if (!c) return FD_E_INVAL;
+    fd_status st = c->slots.set_position(slot, pos);
+    if (st != FD_OK) return fail(c, st, "bad slot or position");
+    return FD_OK;
+}
+
+fd_status fd_slot_state(fd_ctx* c, int32_t slot, int32_t* active, int32_t* pos) {
+    if (!c) return FD_E_INVAL;
+    fd_status st = c->slots.state(slot, active, pos);
+    if (st != FD_OK) return fail(c, st, "bad slot");
+    return FD_OK;
+}
+
+fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, void* stream) {
+    if (!c) return FD_E_INVAL;
+    if (!x_in || !y_out) return fail(c, FD_E_INVAL, "null x_in or y_out");
+    const fd::Plan& pl = c->plan;
+    if (pl.depth && !depth_out) return fail(c, FD_E_INVAL, "profile has a depth stack: depth_out required");
+    int full = -1;
+    if (c->slots.any_full(&full))
+        return fail(c, FD_E_CTXFULL, "slot " + std::to_string(full) + " has a full window");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = flush_slots(c, st);
+    if (e != hipSuccess) return hip_fail(c, e, "slot table upload");
+
+    const fd::StackPlan& mp = pl.main;
+    const fd::StackDims& md = mp.dims;
+    fd::EmbedArgs em{};
+    em.x_in = x_in;
+    em.active = slot_active(c);
+    em.S = pl.S;
+    em.d = md.d;
+    em.x = (float*)Wk(c, pl.ws_x);
+    em.xg = Wk(c, pl.ws_xg);
+    em.g = (const float*)P(c, md.L > 0 ? mp.layers[0].g_attn : mp.g_final);
+    em.ss_out = (float*)Wk(c, pl.ws_ss_a);
+    e = fd::launch_embed(em, pl.wt, pl.Sp, st);
+    int nss = 1;
+    CacheRef mc{(uint8_t*)c->buf.kv_arena, pl.kv_slot_stride, pl.kv_layer_stride, pl.kv_kv_stride,
+                pl.kv_head_stride, pl.kv_pos_stride, pl.kv_fp8};
+    if (e == hipSuccess) e = run_stack(c, mp, mc, -1, st, &nss);
+    if (e == hipSuccess) {
+        fd::FinalArgs f{};
+        f.x = (const float*)Wk(c, pl.ws_x);
+        f.ss = (const float*)Wk(c, pl.ws_ss_a);
+        f.nss = nss;
+        f.inv_d = 1.0f / (float)md.d;
+        f.eps = pl.cfg.rms_eps;
+        f.g = (const float*)P(c, mp.g_final);
+        f.active = slot_active(c);
+        f.S = pl.S;
+        f.d = md.d;
+        f.y_out = y_out;
+        f.ldy = md.d;
+        f.y_off = 0;
+        f.yw = pl.depth ? Wk(c, pl.ws_yw) : nullptr;
+        f.pos = slot_pos(c);
+        f.advance = 1;
+        e = fd::launch_final(f, pl.wt, pl.Sp, st);
+    }
+    if (e == hipSuccess && pl.depth) {
+        const fd::StackPlan& dp = pl.dstack;
+        const fd::StackDims& dd = dp.dims;
+        fd::GemmArgs g{};
+        g.W = P(c, pl.w_in);
+        g.X = Wk(c, pl.ws_yw);
+        g.K = pl.win.K; g.KB = pl.win.KB; g.NB = pl.win.NB; g.P = pl.win.P; g.MG = pl.win.MG;
+        g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
+        g.part = (float*)Wk(c, pl.ws_part);
+        g.cnt = (int*)Wk(c, pl.ws_cnt);
+        g.epi = fd::EPI_F32;
+        g.y = (float*)Wk(c, pl.ws_c);
+        g.ld = dd.d;
+        e = fd::launch_gemm(g, pl.wt, pl.win.R, pl.win.MTG, pl.win.grid(), st);
+        const uint64_t pos_b = (uint64_t)dd.hd * 4, head_b = pos_b * dd.T, kv_b = head_b * dd.hkv,
+                       layer_b = kv_b * 2, slot_b = layer_b * dd.L;
+        CacheRef dc{Wk(c, pl.ws_dkv), slot_b, layer_b, kv_b, head_b, pos_b, 0};
+        for (int k = 0; k < dd.T && e == hipSuccess; ++k) {
+            fd::EmbedArgs de{};
+            de.c = (const float*)Wk(c, pl.ws_c);
+            de.z = k ? (const float*)Wk(c, pl.ws_z) : nullptr;
+            de.active = slot_active(c);
+            de.S = pl.S;
+            de.d = dd.d;
+            de.x = (float*)Wk(c, pl.ws_x);
+            de.xg = Wk(c, pl.ws_xg);
+            de.g = (const float*)P(c, dd.L > 0 ? dp.layers[0].g_attn : dp.g_final);
+            de.ss_out = (float*)Wk(c, pl.ws_ss_a);
+            e = fd::launch_embed(de, pl.wt, pl.Sp, st);
+            int dnss = 1;
+            if (e == hipSuccess) e = run_stack(c, dp, dc, k, st, &dnss);
+            if (e == hipSuccess) {
+                fd::FinalArgs f{};
+                f.x = (const float*)Wk(c, pl.ws_x);
+                f.ss = (const float*)Wk(c, pl.ws_ss_a);
+                f.nss = dnss;
+                f.inv_d = 1.0f / (float)dd.d;
+                f.eps = pl.cfg.rms_eps;
+                f.g = (const float*)P(c, dp.g_final);
+                f.active = slot_active(c);
+                f.S = pl.S;
+                f.d = dd.d;
+                f.y_out = depth_out;
+                f.ldy = dd.T * dd.d;
+                f.y_off = k * dd.d;
+                f.zf = (float*)Wk(c, pl.ws_z);
+                f.advance = 0;
+                e = fd::launch_final(f, pl.wt, pl.Sp, st);
+            }
+        }
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "fd_step launch");
+    c->slots.advance();
+    return FD_OK;
+}
+
+fd_status fd_kv_write(fd_ctx* c, int32_t slot, int32_t layer, int32_t t0, int32_t n, const float* src,
+                      void* stream) {
+    if (!c) return FD_E_INVAL;
+    const fd::Plan& pl = c->plan;
+    if (slot < 0 || slot >= pl.S) return fail(c, FD_E_BADSLOT, "slot out of range");
+    if (layer < 0 || layer >= pl.main.dims.L) return fail(c, FD_E_INVAL, "layer out of range");
+    if (n < 0 || t0 < 0 || (int64_t)t0 + n > pl.cfg.max_context)
+        return fail(c, FD_E_INVAL, "positions outside the window");
+    if (n == 0) return FD_OK;
+    if (!src || ((uintptr_t)src & 15)) return fail(c, FD_E_INVAL, "src must be non-null and 16-byte aligned");
+    fd::KvWriteArgs a{};
+    a.src = src;
+    a.dst = (uint8_t*)c->buf.kv_arena + (size_t)slot * pl.kv_slot_stride + (size_t)layer * pl.kv_layer_stride;
+    a.kv_stride = pl.kv_kv_stride;
+    a.head_stride = pl.kv_head_stride;
+    a.pos_stride = pl.kv_pos_stride;
+    a.kvsig = (const float*)P(c, pl.main.kvsig) + (size_t)layer * 2 * pl.main.dims.hkv;
+    a.hkv = pl.main.dims.hkv;
+    a.hd = pl.main.dims.hd;
+    a.t0 = t0;
+    a.n = n;
+    a.kv_fp8 = pl.kv_fp8;
+    hipError_t e = fd::launch_kv_write(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(c, e, "fd_kv_write");
+    return FD_OK;
+}
+
+fd_status fd_kv_layout(fd_ctx* c, fd_kv_view* out) {
+    if (!c || !out) return FD_E_INVAL;
+    const fd::Plan& pl = c->plan;
+    out->base = c->buf.kv_arena;
+    out->slot_stride = pl.kv_slot_stride;
+    out->layer_stride = pl.kv_layer_stride;
+    out->kv_stride = pl.kv_kv_stride;
+    out->head_stride = pl.kv_head_stride;
+    out->pos_stride = pl.kv_pos_stride;
+    out->elem_bytes = pl.kv_bytes;
+    out->n_layers = pl.main.dims.L;
+    out->n_kv_heads = pl.main.dims.hkv;
+    out->max_context = pl.cfg.max_context;
+    out->head_dim = pl.main.dims.hd;
+    out->max_slots = pl.S;
+    out->kv_scale = pl.kv_fp8 ? (const float*)P(c, pl.main.kvsig) : nullptr;
+    out->slot_active = slot_active(c);
+    out->slot_pos = slot_pos(c);
+    return FD_OK;
+}
+
+fd_status fd_sync(fd_ctx* c, void* stream) {
+    if (!c) return FD_E_INVAL;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(c, e, "fd_sync");
+    return FD_OK;
+}
+
+fd_status fd_destroy(fd_ctx* c) {
+    if (!c) return FD_E_INVAL;
+    for (int i = 0; i < kRing; ++i) {
+        if (c->ev[i]) {
+            if (c->ev_used[i]) (void)hipEventSynchronize(c->ev[i]);
+            (void)hipEventDestroy(c->ev[i]);
+        }
+        if (c->pinned[i]) (void)hipHostFree(c->pinned[i]);
+    }
+    delete c;
+    return FD_OK;
+}
+
+}  // extern "C"

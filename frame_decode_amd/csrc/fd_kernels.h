@@ -1,0 +1,121 @@
+// Kernel argument blocks and launchers of the decode step (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fd {
+
+enum Epilogue : int {
+    EPI_QKV = 0,    // rows x rstd, rotary on q and k, q scaled for the softmax, k/v appended to the cache
+    EPI_RESID = 1,  // x += acc; xg = act(x * g_next); per-row partial sums of x^2
+    EPI_GU = 2,     // rows x rstd, h = silu(gate) * up
+    EPI_F32 = 3,    // plain fp32 store
+};
+
+struct GemmArgs {
+    const uint8_t* W;   // packed tiles [NB][KB][64 lanes][16 B]
+    const void* X;      // session rows [Sp][K] in the activation type
+    int K, KB, NB, P, MG, MT, Sp, S;
+    float* part;        // split-K partial tiles (P > 1)
+    int* cnt;           // split-K arrival counters [n_groups * MG], zero between launches
+    int epi;
+    // row scaling by the RMS norm of the GEMM input: rstd[m] = (sum_i ss[i][m] / d + eps)^-1/2
+    const float* ss_in;
+    int nss;
+    float inv_d, eps;
+    // EPI_QKV
+    float* q_out;          // [Sp][hq*hd] fp32
+    int hq, hkv, hd;
+    const float* rope;     // [T][hd/2] x (cos, sin)
+    int rope_T;
+    const float* qscale;   // [hkv] for this layer
+    const float* kvsig;    // [2][hkv] for this layer (FP8 scales; unused for fp32 caches)
+    int kv_fp8;
+    uint8_t* arena;        // cache base of this layer for slot 0 (base + layer offset)
+    uint64_t slot_stride, kv_stride, head_stride, pos_stride;
+    const int* active;
+    const int* pos;
+    int pos_override;      // >= 0: every row is at this position (depth stack)
+    // EPI_RESID
+    float* x;              // [Sp][ld] residual stream
+    void* xg;              // [Sp][ld] act(x * g_next)
+    const float* g_next;
+    float* ss_out;         // [n_groups][Sp]
+    int ld;
+    // EPI_GU
+    void* h_out;           // [Sp][F]
+    int F;
+    // EPI_F32
+    float* y;              // [Sp][ld]
+};
+
+struct AttnArgs {
+    const float* q;        // [Sp][hq*hd] fp32, pre-scaled by log2(e) * sigma_K / sqrt(hd)
+    const uint8_t* arena;  // cache base of this layer for slot 0
+    uint64_t slot_stride, kv_stride, head_stride, pos_stride;
+    const float* vscale;   // [hkv] sigma_V of this layer
+    const int* active;
+    const int* pos;
+    int pos_override;
+    int S, hq, hkv, tc, n_chunks;
+    int T;                 // cache positions per slot
+    float* part;           // [S][hkv][n_chunks][G][hd + 2]
+    int* cnt;              // [S][hkv] arrival counters, zero between launches
+    void* o_out;           // [Sp][hq*hd] activation type
+};
+
+struct EmbedArgs {
+    const void* x_in;      // caller rows [S][d] (activation type), or null
+    const float* c;        // depth input projection [Sp][d] fp32 (when x_in is null)
+    const float* z;        // previous depth output [Sp][d] fp32 or null (= 0)
+    const int* active;
+    int S, d;
+    float* x;              // [Sp][d]
+    void* xg;              // [Sp][d]
+    const float* g;        // gain of the first norm
+    float* ss_out;         // [1][Sp]
+};
+
+struct FinalArgs {
+    const float* x;
+    const float* ss;
+    int nss;
+    float inv_d, eps;
+    const float* g;
+    const int* active;
+    int S, d;
+    void* y_out;           // caller rows, element (m, i) at y_out[m * ldy + y_off + i]; may be null
+    int ldy, y_off;
+    void* yw;              // [Sp][d] activation-type copy, or null
+    float* zf;             // [Sp][d] fp32 copy, or null
+    int* pos;              // advanced by one for active rows when `advance`
+    int advance;
+};
+
+struct PackArgs {
+    const void* src[3];
+    int rows[3];
+    int interleave;        // 1: packed row 2j = src0 row j, 2j+1 = src1 row j
+    int N, K, KB;
+    uint8_t* dst;
+};
+
+struct KvWriteArgs {
+    const float* src;      // [2][hkv][n][hd]
+    uint8_t* dst;          // slot + layer base
+    uint64_t kv_stride, head_stride, pos_stride;
+    const float* kvsig;    // [2][hkv]
+    int hkv, hd, t0, n, kv_fp8;
+};
+
+// Launchers (enqueue on `st`; return the launch error).
+hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, int wt, int R, int MTG, int grid, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, int wt, int kv_fp8, int hd, int G, int grid, hipStream_t st);
+hipError_t launch_embed(const EmbedArgs& a, int wt, int rows, hipStream_t st);
+hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st);
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st);
+
+}  // namespace fd

@@ -1,0 +1,231 @@
+// Serving-profile validation and layout planning (pure host code).
+#include "fd_plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <sstream>
+
+namespace fd {
+
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
+    GemmShape g;
+    g.N = N;
+    g.K = K;
+    g.KT = KT;
+    g.NB = N / 16;
+    g.KB = K / KT;
+    g.MG = cdiv(MT, kMaxMTG);
+    g.MTG = cdiv(MT, g.MG);
+    // Two n-blocks per wave when the projection is wide enough to still give
+    // every CU work: this halves the re-reads of the session rows X.
+    g.R = (g.NB >= kWaves * 2 * 64) ? 2 : 1;
+    g.n_groups = cdiv(g.NB, kWaves * g.R);
+    int base = g.n_groups * g.MG;
+    // Split K until there are about two workgroups per CU, keeping at
+    // least 8 tiles of K per split.
+    int p = (2 * n_cu + base - 1) / base;
+    p = std::min(p, std::max(1, g.KB / 8));
+    p = std::min(p, 16);
+    g.P = std::max(1, p);
+    g.part_floats = g.P > 1 ? (uint64_t)g.n_groups * g.MG * g.P * kWaves * g.R * g.MTG * 256 : 0;
+    g.counters = g.n_groups * g.MG;
+    return g;
+}
+
+namespace {
+
+bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
+
+fd_status check_stack(const char* name, int L, int d, int hq, int hkv, int hd, int f, int KT,
+                      std::string* err) {
+    std::ostringstream m;
+    if (L < 0 || L > 1024) m << name << ": n_layers " << L << " outside 0..1024";
+    else if (d <= 0 || d % KT) m << name << ": d_model " << d << " must be a positive multiple of " << KT;
+    else if (d > 65536) m << name << ": d_model too large";
+    else if (hq <= 0 || hkv <= 0 || hq % hkv) m << name << ": n_heads must be a positive multiple of n_kv_heads";
+    else if (!(hq / hkv == 1 || hq / hkv == 2 || hq / hkv == 4))
+        m << name << ": n_heads / n_kv_heads must be 1, 2 or 4";
+    else if (!valid_hd(hd)) m << name << ": head_dim must be 64, 128 or 256";
+    else if ((hq * hd) % KT) m << name << ": n_heads*head_dim must be a multiple of " << KT;
+    else if (f <= 0 || f % KT || f > 262144) m << name << ": d_ffn must be a positive multiple of " << KT;
+    if (!m.str().empty()) {
+        *err = m.str();
+        return FD_E_UNSUPPORTED;
+    }
+    return FD_OK;
+}
+
+void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int kv_fp8,
+                uint64_t& off) {
+    sp.dims = dims;
+    sp.qkv = choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256);
+    sp.o = choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256);
+    sp.gu = choose_gemm(2 * dims.f, dims.d, KT, MT, 256);
+    sp.down = choose_gemm(dims.d, dims.f, KT, MT, 256);
+    sp.layers.resize(dims.L);
+    auto tiles = [](const GemmShape& g) { return (uint64_t)g.NB * g.KB * kTileBytes; };
+    for (int l = 0; l < dims.L; ++l) {
+        LayerOffsets& lo = sp.layers[l];
+        lo.qkv = off; off = align_up(off + tiles(sp.qkv));
+        lo.o = off;   off = align_up(off + tiles(sp.o));
+        lo.gu = off;  off = align_up(off + tiles(sp.gu));
+        lo.down = off; off = align_up(off + tiles(sp.down));
+        lo.g_attn = off; off = align_up(off + 4ull * dims.d);
+        lo.g_ffn = off;  off = align_up(off + 4ull * dims.d);
+    }
+    sp.g_final = off; off = align_up(off + 4ull * dims.d);
+    int Lm = std::max(dims.L, 1);
+    sp.qscale = off; off = align_up(off + 4ull * Lm * dims.hkv);
+    sp.kvsig = off;   off = align_up(off + 4ull * Lm * 2 * dims.hkv);
+    sp.vscale = off; off = align_up(off + 4ull * Lm * dims.hkv);
+    sp.rope = off;   off = align_up(off + 4ull * dims.T * dims.hd);
+    // attention chunking: lanes per position give each lane 16 bytes (FP8)
+    // or 32 bytes (fp32) of a position's head vector
+    AttnShape& a = sp.attn;
+    a.lpp = kv_fp8 ? dims.hd / 16 : dims.hd / 8;
+    a.tc = kWaves * kAttnIters * (64 / a.lpp);
+    a.n_chunks = cdiv(dims.T, a.tc);
+}
+
+}  // namespace
+
+fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
+    Plan p;
+    p.cfg = c;
+    if (!(c.w_dtype == FD_F32 || c.w_dtype == FD_BF16)) {
+        *err = "w_dtype must be FD_F32 or FD_BF16";
+        return FD_E_UNSUPPORTED;
+    }
+    if (c.act_dtype != c.w_dtype) {
+        *err = "act_dtype must equal w_dtype";
+        return FD_E_UNSUPPORTED;
+    }
+    if (!(c.kv_dtype == FD_F32 || c.kv_dtype == FD_FP8_E4M3)) {
+        *err = "kv_dtype must be FD_F32 or FD_FP8_E4M3";
+        return FD_E_UNSUPPORTED;
+    }
+    if (!(c.rms_eps >= 0.0f) || !std::isfinite(c.rms_eps)) {
+        *err = "rms_eps must be finite and >= 0";
+        return FD_E_INVAL;
+    }
+    if (!(c.rope_base > 0.0f) || !std::isfinite(c.rope_base)) {
+        *err = "rope_base must be finite and > 0";
+        return FD_E_INVAL;
+    }
+    if (c.max_slots < 1 || c.max_slots > 4096) {
+        *err = "max_slots outside 1..4096";
+        return FD_E_UNSUPPORTED;
+    }
+    if (c.max_context < 1 || c.max_context > 65536) {
+        *err = "max_context outside 1..65536";
+        return FD_E_UNSUPPORTED;
+    }
+    p.wt = c.w_dtype == FD_BF16 ? 1 : 0;
+    p.act_bytes = p.wt ? 2 : 4;
+    p.kv_fp8 = c.kv_dtype == FD_FP8_E4M3;
+    p.kv_bytes = p.kv_fp8 ? 1 : 4;
+    const int KT = p.wt ? 32 : 16;
+    fd_status st = check_stack("main", c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim,
+                               c.d_ffn, KT, err);
+    if (st != FD_OK) return st;
+    p.depth = c.depth_steps > 0;
+    if (c.depth_steps < 0 || c.depth_steps > 64) {
+        *err = "depth_steps outside 0..64";
+        return FD_E_UNSUPPORTED;
+    }
+    if (p.depth) {
+        if (p.wt || p.kv_fp8) {
+            *err = "the depth stack requires fp32 weights and an fp32 cache";
+            return FD_E_UNSUPPORTED;
+        }
+        st = check_stack("depth", c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads,
+                         c.depth_head_dim, c.depth_ffn, KT, err);
+        if (st != FD_OK) return st;
+    }
+    p.S = c.max_slots;
+    p.Sp = align_up(c.max_slots, 16);
+    p.MT = p.Sp / 16;
+
+    uint64_t off = 0;
+    StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};
+    plan_stack(p.main, md, KT, p.MT, p.kv_fp8, off);
+    if (p.depth) {
+        StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
+                     c.depth_ffn, c.depth_steps};
+        p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
+        p.w_in = off;
+        off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
+        plan_stack(p.dstack, dd, KT, p.MT, 0, off);
+    }
+    p.packed_bytes = std::max<uint64_t>(off, kAlign);
+
+    // workspace
+    const StackDims& m = p.main.dims;
+    int dmax = m.d, hqd = m.hq * m.hd, fmax = m.f, dd = 0;
+    if (p.depth) {
+        const StackDims& z = p.dstack.dims;
+        dmax = std::max(dmax, z.d);
+        hqd = std::max(hqd, z.hq * z.hd);
+        fmax = std::max(fmax, z.f);
+        dd = z.d;
+    }
+    uint64_t Sp = p.Sp;
+    uint64_t w = 0;
+    auto take = [&](uint64_t bytes) { uint64_t o = w; w = align_up(w + std::max<uint64_t>(bytes, 4)); return o; };
+    p.ws_x = take(Sp * dmax * 4);
+    p.ws_xg = take(Sp * dmax * p.act_bytes);
+    p.ws_q = take(Sp * hqd * 4);
+    p.ws_o = take(Sp * hqd * p.act_bytes);
+    p.ws_h = take(Sp * fmax * p.act_bytes);
+    p.ws_yw = take(Sp * m.d * p.act_bytes);
+    p.ws_c = take(Sp * std::max(dd, 1) * 4);
+    p.ws_z = take(Sp * std::max(dd, 1) * 4);
+    int nss = 1;
+    uint64_t part = 0;
+    int cnt = 1;
+    uint64_t apart = 0;
+    int acnt = 1;
+    auto acc_stack = [&](const StackPlan& s) {
+        nss = std::max({nss, s.o.n_groups, s.down.n_groups});
+        for (const GemmShape* g : {&s.qkv, &s.o, &s.gu, &s.down}) {
+            part = std::max(part, g->part_floats);
+            cnt = std::max(cnt, g->counters);
+        }
+        apart = std::max(apart, (uint64_t)p.S * s.dims.hkv * s.attn.n_chunks * s.dims.G() *
+                                    (s.dims.hd + 2));
+        acnt = std::max(acnt, p.S * s.dims.hkv);
+    };
+    acc_stack(p.main);
+    if (p.depth) {
+        acc_stack(p.dstack);
+        part = std::max(part, p.win.part_floats);
+        cnt = std::max(cnt, p.win.counters);
+    }
+    p.nss_max = nss;
+    p.ws_ss_a = take(4ull * nss * Sp);
+    p.ws_ss_f = take(4ull * nss * Sp);
+    p.ws_part = take(4ull * part);
+    p.ws_cnt = take(4ull * cnt);
+    p.ws_apart = take(4ull * apart);
+    p.ws_acnt = take(4ull * acnt);
+    if (p.depth) {
+        const StackDims& z = p.dstack.dims;
+        p.ws_dkv = take(Sp * z.L * 2ull * z.hkv * z.T * z.hd * 4);
+        p.dstack.kv_off = p.ws_dkv;
+    }
+    p.ws_err = take(64);
+    p.workspace_bytes = w;
+
+    // cache arena: [S][L][K|V][H_kv][T][D]
+    p.kv_pos_stride = (uint64_t)m.hd * p.kv_bytes;
+    p.kv_head_stride = p.kv_pos_stride * m.T;
+    p.kv_kv_stride = p.kv_head_stride * m.hkv;
+    p.kv_layer_stride = p.kv_kv_stride * 2;
+    p.kv_slot_stride = p.kv_layer_stride * m.L;
+    p.kv_bytes_total = std::max<uint64_t>(p.kv_slot_stride * p.S, kAlign);
+    p.slot_table_bytes = align_up(8ull * p.S);
+    *out = p;
+    return FD_OK;
+}
+
+}  // namespace fd

@@ -1,0 +1,109 @@
+// Host-side plan of one serving profile: tiling of every projection,
+// attention chunking, and the byte layout of the packed-weight buffer and
+// the workspace.  Pure host code (no HIP): compiled into the HIP library
+// and into the host-only test library.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/fd.h"
+
+namespace fd {
+
+constexpr int kWaves = 4;          // waves per workgroup in the GEMM and attention kernels
+constexpr int kTileBytes = 1024;   // one packed weight tile = 64 lanes x 16 bytes
+constexpr int kMaxMTG = 8;         // most 16-row tiles of sessions one GEMM workgroup holds
+constexpr int kAttnIters = 8;      // position groups each attention wave walks per chunk
+constexpr uint64_t kAlign = 256;
+
+inline uint64_t align_up(uint64_t v, uint64_t a = kAlign) { return (v + a - 1) / a * a; }
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Tiling of one projection Y[M][N] = X[M][K] . W[N][K]^T.
+struct GemmShape {
+    int N = 0, K = 0;
+    int KT = 0;        // k-width of a tile: 32 (bf16) or 16 (fp32)
+    int NB = 0, KB = 0;  // tiles along N (16 rows each) and K
+    int R = 1;         // n-blocks per wave
+    int P = 1;         // k-splits (workgroups sharing one n-group)
+    int MG = 1;        // m-groups
+    int MTG = 1;       // 16-row m-tiles per m-group
+    int n_groups = 0;  // ceil(NB / (kWaves * R))
+    uint64_t w_off = 0;   // offset of the packed tiles in the packed buffer
+    uint64_t part_floats = 0;  // partial-sum floats needed when P > 1
+    int counters = 0;
+    int grid() const { return n_groups * P * MG; }
+};
+
+struct StackDims {
+    int L = 0, d = 0, hq = 0, hkv = 0, hd = 0, f = 0;
+    int T = 0;          // cache positions per slot (window / depth steps)
+    int G() const { return hkv ? hq / hkv : 0; }
+    int qkv_n() const { return (hq + 2 * hkv) * hd; }
+};
+
+struct LayerOffsets {
+    uint64_t qkv = 0, o = 0, gu = 0, down = 0;  // packed tiles
+    uint64_t g_attn = 0, g_ffn = 0;              // fp32 gains
+};
+
+struct AttnShape {
+    int lpp = 0;      // lanes per position
+    int tc = 0;       // positions per chunk (one workgroup)
+    int n_chunks = 0; // chunks per (slot, kv-head) for a full window
+    uint64_t part_floats = 0;
+};
+
+struct StackPlan {
+    StackDims dims;
+    GemmShape qkv, o, gu, down;
+    AttnShape attn;
+    std::vector<LayerOffsets> layers;
+    uint64_t g_final = 0;  // fp32 [d]
+    uint64_t qscale = 0;   // fp32 [L][H_kv]: log2(e) * sigma_K / sqrt(D)
+    uint64_t kvsig = 0;    // fp32 [L][2][H_kv]: FP8 scale sigma (1 for fp32 caches)
+    uint64_t vscale = 0;   // fp32 [L][H_kv]: sigma_V
+    uint64_t rope = 0;     // fp32 [T][D/2][2] (cos, sin)
+    // workspace (per stack) cache for the depth stack
+    uint64_t kv_off = 0;
+};
+
+struct Plan {
+    fd_config cfg{};
+    int wt = 0;       // 1 = bf16 weights/activations, 0 = fp32
+    int act_bytes = 4;
+    int kv_fp8 = 0;
+    int kv_bytes = 4;
+    int S = 0;        // max_slots
+    int Sp = 0;       // S rounded up to 16
+    int MT = 0;       // Sp / 16
+    bool depth = false;
+    StackPlan main, dstack;
+    GemmShape win;    // depth input projection
+    uint64_t w_in = 0;
+
+    // packed-weight buffer
+    uint64_t packed_bytes = 0;
+    // workspace layout
+    uint64_t ws_x = 0, ws_xg = 0, ws_q = 0, ws_o = 0, ws_h = 0, ws_c = 0, ws_z = 0, ws_yw = 0;
+    uint64_t ws_ss_a = 0, ws_ss_f = 0, ws_part = 0, ws_cnt = 0, ws_apart = 0, ws_acnt = 0;
+    uint64_t ws_dkv = 0, ws_err = 0;
+    int nss_max = 0;
+    uint64_t workspace_bytes = 0;
+    // cache arena
+    uint64_t kv_slot_stride = 0, kv_layer_stride = 0, kv_kv_stride = 0, kv_head_stride = 0,
+             kv_pos_stride = 0;
+    uint64_t kv_bytes_total = 0;
+    uint64_t slot_table_bytes = 0;
+};
+
+// Validates cfg and builds the plan.  Returns FD_OK or an error code with
+// a message in *err.
+fd_status make_plan(const fd_config& cfg, Plan* out, std::string* err);
+
+// Tile choice for one projection (exposed for tests).
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu);
+
+}  // namespace fd

@@ -1,0 +1,60 @@
+// Host-only entry points over the same plan and slot-pool code that the HIP
+// library links, so the profile validation and the slot state machine can
+// be exercised on a machine without a GPU.  Built with the host compiler
+// into libfd_host.so; never linked into the product library.
+#include <new>
+#include <string>
+
+#include "../../include/fd.h"
+#include "fd_plan.h"
+#include "slot_pool.h"
+
+namespace {
+thread_local std::string g_err;
+}
+
+extern "C" {
+
+fd_status fdh_plan(const fd_config* cfg, fd_sizes* out) {
+    if (!cfg || !out) return FD_E_INVAL;
+    fd::Plan p;
+    fd_status st = fd::make_plan(*cfg, &p, &g_err);
+    if (st != FD_OK) return st;
+    out->packed_weights = p.packed_bytes;
+    out->kv_arena = p.kv_bytes_total;
+    out->workspace = p.workspace_bytes;
+    out->slot_table = p.slot_table_bytes;
+    return FD_OK;
+}
+
+const char* fdh_last_error(void) { return g_err.c_str(); }
+
+// Tiling chosen for one projection: out[0..8] = NB, KB, R, P, MG, MTG, n_groups, grid, KT.
+void fdh_gemm_shape(int N, int K, int wt, int MT, int32_t* out) {
+    fd::GemmShape g = fd::choose_gemm(N, K, wt ? 32 : 16, MT, 256);
+    out[0] = g.NB; out[1] = g.KB; out[2] = g.R; out[3] = g.P; out[4] = g.MG; out[5] = g.MTG;
+    out[6] = g.n_groups; out[7] = g.grid(); out[8] = g.KT;
+}
+
+void* fdh_pool_new(int n_slots, int max_context) {
+    return new (std::nothrow) fd::SlotPool(n_slots, max_context);
+}
+void fdh_pool_delete(void* p) { delete (fd::SlotPool*)p; }
+fd_status fdh_pool_alloc(void* p, int32_t n, int32_t* out) { return ((fd::SlotPool*)p)->alloc(n, out); }
+fd_status fdh_pool_free(void* p, const int32_t* ids, int32_t n) { return ((fd::SlotPool*)p)->free(ids, n); }
+fd_status fdh_pool_set_position(void* p, int32_t s, int32_t pos) {
+    return ((fd::SlotPool*)p)->set_position(s, pos);
+}
+fd_status fdh_pool_state(void* p, int32_t s, int32_t* a, int32_t* pos) {
+    return ((fd::SlotPool*)p)->state(s, a, pos);
+}
+int fdh_pool_any_full(void* p) {
+    int w = -1;
+    return ((fd::SlotPool*)p)->any_full(&w) ? w : -1;
+}
+void fdh_pool_advance(void* p) { ((fd::SlotPool*)p)->advance(); }
+int fdh_pool_dirty(void* p) { return ((fd::SlotPool*)p)->dirty() ? 1 : 0; }
+void fdh_pool_clear_dirty(void* p) { ((fd::SlotPool*)p)->clear_dirty(); }
+void fdh_pool_image(void* p, int32_t* dst) { ((fd::SlotPool*)p)->image(dst); }
+
+}  // extern "C"

@@ -1,0 +1,762 @@
+// Device code of the frame-synchronous decode step, written for gfx950
+// (CDNA4: 64-lane wavefronts, MFMA matrix cores, OCP FP8 conversions).
+//
+// Phases of one frame (one decoder layer = QKV, attention, O, gate/up,
+// down), after the textbook pre-norm decoder the pages' stacks are built
+// from:
+//   embed   x = new frame (active rows) ; xg = act(x * g_attn[0]) ; sum x^2
+//   QKV     [q k v] = rstd * (xg . Wqkv^T); rotary on q, k; k, v appended to
+//           the session's cache slot at its position (FP8: code(v / sigma))
+//   attn    per (slot, kv head, chunk of positions): scores over the cache,
+//           softmax, weighted sum of values; chunks merged by the last one
+//   O       x += o . Wo^T ; xg = act(x * g_ffn) ; partial sums of x^2
+//   GU      h = silu(rstd * gate) * (rstd * up)
+//   down    x += h . Wdown^T ; xg = act(x * g_next) ; partial sums of x^2
+//   final   y = x * rstd * g_final ; inactive rows 0 ; positions advance
+//
+// The projections are skinny GEMMs: every session row shares one streamed
+// read of each weight tile (the shared weight read of the Nemotron VoiceChat
+// case study, "Under the hood", and of the bandwidth blog, section 2 on
+// concurrent requests).  Weight tiles are pre-packed in the MFMA A-operand
+// lane order so each wave load is one contiguous 1 KiB.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fd_kernels.h"
+
+namespace fd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// OCP E4M3 encoder: round to nearest, ties to the even mantissa, finite
+// values beyond 448 saturate to +-448, NaN -> 0x7F | sign.  Written from the
+// format definition (bias 7, 3 mantissa bits, subnormal spacing 2^-9).
+__device__ __forceinline__ uint32_t enc_e4m3(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7Fu;       // NaN
+    if (a >= 0x43E00000u) return sign | 0x7Eu;      // >= 448 (and inf): saturate
+    if (a < 0x3C800000u) {                           // < 2^-6: subnormal codes m * 2^-9
+        float v = __uint_as_float(a) * 512.0f;       // exact power-of-two scaling
+        return sign | (uint32_t)__builtin_rintf(v);  // 0..8; 8 is the smallest normal
+    }
+    int e = (int)(a >> 23) - 127;                    // -6..8
+    uint32_t mant = a & 0x7FFFFFu;
+    uint32_t m3 = mant >> 20;
+    uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) {
+        ++m3;
+        if (m3 == 8u) { m3 = 0u; ++e; }
+    }
+    return sign | ((uint32_t)(e + 7) << 3) | m3;
+}
+
+template <int W>
+__device__ __forceinline__ float warp_sum_xor(float v) {
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Stores 4 consecutive activations at p (fp32 or bf16).
+template <int WT>
+__device__ __forceinline__ void store_act4(void* p, size_t idx, f32x4 v) {
+    if (WT) {
+        u32x2 w;
+        w[0] = f2bf(v[0]) | (f2bf(v[1]) << 16);
+        w[1] = f2bf(v[2]) | (f2bf(v[3]) << 16);
+        *(u32x2*)((uint16_t*)p + idx) = w;
+    } else {
+        *(f32x4*)((float*)p + idx) = v;
+    }
+}
+
+template <int WT>
+__device__ __forceinline__ void store_act1(void* p, size_t idx, float v) {
+    if (WT) ((uint16_t*)p)[idx] = (uint16_t)f2bf(v);
+    else ((float*)p)[idx] = v;
+}
+
+template <int WT>
+__device__ __forceinline__ float load_act1(const void* p, size_t idx) {
+    if (WT) return bf2f(((const uint16_t*)p)[idx]);
+    return ((const float*)p)[idx];
+}
+
+// ---------------------------------------------------------------------------
+// weight packing: [N][K] row-major -> tiles [NB][KB][64 lanes][16 B].
+// bf16 tile = 16 rows x 32 k; lane l holds row l%16, k 8*(l/16) .. +8.
+// fp32 tile = 16 rows x 16 k; lane l holds row l%16, k 4*(l/16) .. +4.
+template <int WT>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+    size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t total = (size_t)(a.N / 16) * a.KB * 64;
+    if (id >= total) return;
+    int lane = (int)(id & 63);
+    size_t tile = id >> 6;
+    int nb = (int)(tile / a.KB), kb = (int)(tile % a.KB);
+    int n = nb * 16 + (lane & 15);
+    int k0 = WT ? kb * 32 + (lane >> 4) * 8 : kb * 16 + (lane >> 4) * 4;
+    const void* src;
+    int row;
+    if (a.interleave) {
+        src = (n & 1) ? a.src[1] : a.src[0];
+        row = n >> 1;
+    } else if (n < a.rows[0]) {
+        src = a.src[0];
+        row = n;
+    } else if (n < a.rows[0] + a.rows[1]) {
+        src = a.src[1];
+        row = n - a.rows[0];
+    } else {
+        src = a.src[2];
+        row = n - a.rows[0] - a.rows[1];
+    }
+    const int eb = WT ? 2 : 4;
+    const u32x4 v = *(const u32x4*)((const uint8_t*)src + ((size_t)row * a.K + k0) * eb);
+    *(u32x4*)(a.dst + tile * 1024 + (size_t)lane * 16) = v;
+}
+
+// ---------------------------------------------------------------------------
+// skinny GEMM: Y[m][n] = sum_k X[m][k] W[n][k] with the MFMA A operand = W
+// (16 n-rows) and B operand = X^T (16 session columns), fp32 accumulation.
+//
+// Workgroup task (n-group, m-group, k-split): 4 waves, wave w owns n-blocks
+// (n-group*4 + w)*R .. +R; all waves share the same k-range so X fragments
+// are re-read from the CU's L1.  With P > 1 the k-splits write partial tiles
+// and the last to arrive sums them in split order (deterministic).
+
+template <int WT>
+struct BFrag;
+template <>
+struct BFrag<1> { typedef u32x4 T; };
+template <>
+struct BFrag<0> { typedef f32x4 T; };
+
+template <int WT>
+__device__ __forceinline__ f32x4 mfma_tile(u32x4 a, typename BFrag<WT>::T b, f32x4 c) {
+    if constexpr (WT) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        f32x4 af = __builtin_bit_cast(f32x4, a);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], b[3], c, 0, 0, 0);
+        return c;
+    }
+}
+
+template <int WT, int R, int MTG>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+    typedef typename BFrag<WT>::T BT;
+    constexpr int U = 4;  // k-tiles loaded per batch
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int bid = blockIdx.x;
+    const int ks = bid % a.P;
+    bid /= a.P;
+    const int mg = bid % a.MG;
+    const int ng = bid / a.MG;
+    const int kb0 = (int)((long)ks * a.KB / a.P);
+    const int kb1 = (int)((long)(ks + 1) * a.KB / a.P);
+    const int nbw = (ng * 4 + wave) * R;  // first n-block of this wave
+    const int mt0 = mg * MTG;
+    const int mtn = min(MTG, a.MT - mt0);
+
+    f32x4 acc[R][MTG];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    bool rv[R];
+    const u32x4* wp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        rv[r] = (nbw + r) < a.NB;
+        int nb = rv[r] ? nbw + r : 0;
+        wp[r] = (const u32x4*)(a.W + (size_t)nb * a.KB * 1024) + lane;
+    }
+    // X fragment: row (mt0 + t)*16 + lane%16; each k-tile advances 64 bytes.
+    const int eb = WT ? 2 : 4;
+    const uint8_t* xp = (const uint8_t*)a.X +
+                        ((size_t)(mt0 * 16 + (lane & 15)) * a.K) * eb + (lane >> 4) * 16;
+    const size_t xrow16 = (size_t)16 * a.K * eb;  // bytes between m-tiles
+
+    for (int kb = kb0; kb < kb1; kb += U) {
+        u32x4 av[U][R];
+        BT bv[U][MTG];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kb + u < kb1) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (rv[r]) av[u][r] = wp[r][(size_t)(kb + u) * 64];
+#pragma unroll
+                for (int t = 0; t < MTG; ++t)
+                    if (t < mtn) bv[u][t] = *(const BT*)(xp + t * xrow16 + (size_t)(kb + u) * 64);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kb + u < kb1) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (rv[r]) {
+#pragma unroll
+                        for (int t = 0; t < MTG; ++t)
+                            if (t < mtn) acc[r][t] = mfma_tile<WT>(av[u][r], bv[u][t], acc[r][t]);
+                    }
+            }
+        }
+    }
+
+    __shared__ int s_last;
+    __shared__ float s_rstd[MTG * 16];
+    __shared__ float s_red[4][MTG * 16];
+
+    if (a.P > 1) {
+        const int task = ng * a.MG + mg;
+        f32x4* pp = (f32x4*)a.part + ((size_t)task * a.P * 4 + wave) * R * MTG * 64 + lane;
+        const size_t split_stride = (size_t)4 * R * MTG * 64;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) pp[ks * split_stride + (r * MTG + t) * 64] = acc[r][t];
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int old = atomicAdd(&a.cnt[task], 1);
+            s_last = (old == a.P - 1);
+            if (s_last) a.cnt[task] = 0;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) {
+                f32x4 s = pp[(r * MTG + t) * 64];
+                for (int q = 1; q < a.P; ++q) s += pp[q * split_stride + (r * MTG + t) * 64];
+                acc[r][t] = s;
+            }
+    }
+
+    // per-row norm scale
+    if (a.ss_in) {
+        for (int i = threadIdx.x; i < mtn * 16; i += blockDim.x) {
+            const int row = mt0 * 16 + i;
+            float s = 0.f;
+            for (int j = 0; j < a.nss; ++j) s += a.ss_in[(size_t)j * a.Sp + row];
+            s_rstd[i] = 1.0f / sqrtf(s * a.inv_d + a.eps);
+        }
+    }
+    __syncthreads();
+
+    float ssum[MTG];
+#pragma unroll
+    for (int t = 0; t < MTG; ++t) ssum[t] = 0.f;
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) {
+            if (!rv[r] || t >= mtn) continue;
+            const int mloc = t * 16 + (lane & 15);
+            const int m = mt0 * 16 + mloc;
+            const int n = (nbw + r) * 16 + (lane >> 4) * 4;
+            f32x4 v = acc[r][t];
+            if (a.ss_in) v *= s_rstd[mloc];
+            if (a.epi == EPI_QKV) {
+                const int hh = n / a.hd;
+                const int d0 = n - hh * a.hd;
+                const bool act = m < a.S && a.active[m];
+                int p = a.pos_override >= 0 ? a.pos_override : (m < a.S ? a.pos[m] : 0);
+                p = min(max(p, 0), a.rope_T - 1);
+                if (hh < a.hq + a.hkv) {
+                    const f32x4 cs = *(const f32x4*)(a.rope + ((size_t)p * (a.hd / 2) + d0 / 2) * 2);
+                    f32x4 w;
+                    w[0] = v[0] * cs[0] - v[1] * cs[1];
+                    w[1] = v[0] * cs[1] + v[1] * cs[0];
+                    w[2] = v[2] * cs[2] - v[3] * cs[3];
+                    w[3] = v[2] * cs[3] + v[3] * cs[2];
+                    v = w;
+                }
+                if (hh < a.hq) {
+                    const int g = hh / (a.hq / a.hkv);
+                    *(f32x4*)(a.q_out + (size_t)m * a.hq * a.hd + n) = v * a.qscale[g];
+                } else if (act) {
+                    const int kv = hh < a.hq + a.hkv ? 0 : 1;
+                    const int g = hh - a.hq - kv * a.hkv;
+                    uint8_t* dst = a.arena + (size_t)m * a.slot_stride + kv * a.kv_stride +
+                                   g * a.head_stride + (size_t)p * a.pos_stride;
+                    if (a.kv_fp8) {
+                        const float sg = a.kvsig[kv * a.hkv + g];
+                        uint32_t w = enc_e4m3(v[0] / sg) | (enc_e4m3(v[1] / sg) << 8) |
+                                     (enc_e4m3(v[2] / sg) << 16) | (enc_e4m3(v[3] / sg) << 24);
+                        *(uint32_t*)(dst + d0) = w;
+                    } else {
+                        *(f32x4*)(dst + (size_t)d0 * 4) = v;
+                    }
+                }
+            } else if (a.epi == EPI_RESID) {
+                float* xr = a.x + (size_t)m * a.ld + n;
+                f32x4 xn = *(f32x4*)xr + v;
+                *(f32x4*)xr = xn;
+                const f32x4 g = *(const f32x4*)(a.g_next + n);
+                store_act4<WT>(a.xg, (size_t)m * a.ld + n, xn * g);
+                ssum[t] += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+            } else if (a.epi == EPI_GU) {
+                const int j = n >> 1;  // rows interleave gate_j, up_j, gate_j+1, up_j+1
+                const float h0 = v[0] / (1.0f + expf(-v[0])) * v[1];
+                const float h1 = v[2] / (1.0f + expf(-v[2])) * v[3];
+                if (WT) {
+                    *(uint32_t*)((uint16_t*)a.h_out + (size_t)m * a.F + j) = f2bf(h0) | (f2bf(h1) << 16);
+                } else {
+                    *(f32x2*)((float*)a.h_out + (size_t)m * a.F + j) = f32x2{h0, h1};
+                }
+            } else {
+                *(f32x4*)(a.y + (size_t)m * a.ld + n) = v;
+            }
+        }
+    }
+
+    if (a.epi == EPI_RESID) {
+        // rows' partial sums of x^2 over this n-group, fixed reduction order
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) {
+            float s = ssum[t];
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            if (lane < 16) s_red[wave][t * 16 + lane] = s;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < mtn * 16; i += blockDim.x) {
+            const float s = ((s_red[0][i] + s_red[1][i]) + s_red[2][i]) + s_red[3][i];
+            a.ss_out[(size_t)ng * a.Sp + mt0 * 16 + i] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decode attention over one (slot, kv head, chunk of positions).
+//
+// Lanes: a position's head vector is spread over LPP consecutive lanes,
+// each holding E elements (16 B of FP8 or 32 B of fp32) in 16-byte pieces
+// c + LPP*j, so one wave load covers 64/LPP whole positions contiguously.
+// Pass 1 streams keys and forms scores (reduced over the LPP lanes), then
+// the workgroup max, exponentials (base 2, log2(e) folded into q), and pass
+// 2 streams values.  All G query heads of the kv head share each load.
+
+template <int FP8>
+__device__ __forceinline__ void unpack16(const u32x4& raw, float* out) {
+    if constexpr (FP8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false);
+            f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true);
+            out[4 * w + 0] = lo[0];
+            out[4 * w + 1] = lo[1];
+            out[4 * w + 2] = hi[0];
+            out[4 * w + 3] = hi[1];
+        }
+    } else {
+        f32x4 f = __builtin_bit_cast(f32x4, raw);
+        out[0] = f[0];
+        out[1] = f[1];
+        out[2] = f[2];
+        out[3] = f[3];
+    }
+}
+
+template <int WT, int FP8, int D, int G>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+    constexpr int EB = FP8 ? 1 : 4;
+    constexpr int LPP = FP8 ? D / 16 : D / 8;
+    constexpr int E = D / LPP;         // elements per lane per position
+    constexpr int VE = 16 / EB;        // elements per 16-byte piece
+    constexpr int J = E / VE;          // pieces per lane
+    constexpr int PPL = 64 / LPP;      // positions per wave load
+    constexpr int NIT = 8;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane % LPP;
+    const int jj = lane / LPP;
+
+    int bid = blockIdx.x;
+    const int chunk = bid % a.n_chunks;
+    bid /= a.n_chunks;
+    const int g = bid % a.hkv;
+    const int s = bid / a.hkv;
+    const int hqd = a.hq * D;
+    if (s >= a.S) return;
+    if (!a.active[s]) {
+        if (chunk == 0)
+            for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+                store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)g * G * D + i, 0.f);
+        return;
+    }
+    const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
+    const int n = p + 1;
+    const int nch = (n + a.tc - 1) / a.tc;
+    if (chunk >= nch) return;
+    const int t0 = chunk * a.tc;
+    const int t1 = min(t0 + a.tc, n);
+
+    float qv[G][E];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int i = 0; i < VE; i += 4) {
+                const f32x4 v = *(const f32x4*)(a.q + (size_t)s * hqd + (size_t)(g * G + h) * D +
+                                                (c + LPP * j) * VE + i);
+                qv[h][j * VE + i + 0] = v[0];
+                qv[h][j * VE + i + 1] = v[1];
+                qv[h][j * VE + i + 2] = v[2];
+                qv[h][j * VE + i + 3] = v[3];
+            }
+
+    const uint8_t* kb = a.arena + (size_t)s * a.slot_stride + (size_t)g * a.head_stride;
+    const uint8_t* vb = kb + a.kv_stride;
+    const int tw = t0 + wave * NIT * PPL + jj;  // this lane's first position
+
+    float sc[NIT][G];
+    u32x4 raw[NIT][J];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int t = tw + it * PPL;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            raw[it][j] = t < t1 ? *(const u32x4*)(kb + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
+                                : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        float kvf[E];
+#pragma unroll
+        for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], kvf + j * VE);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float dsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) dsum += qv[h][e] * kvf[e];
+            dsum = warp_sum_xor<LPP>(dsum);
+            sc[it][h] = (tw + it * PPL) < t1 ? dsum : -INFINITY;
+        }
+    }
+
+    __shared__ float s_m[4][G];
+    __shared__ float s_l[4][G];
+    __shared__ float s_acc[4][G][D];
+    __shared__ int s_last;
+
+    float mx[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float m = sc[0][h];
+#pragma unroll
+        for (int it = 1; it < NIT; ++it) m = fmaxf(m, sc[it][h]);
+#pragma unroll
+        for (int o = LPP; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        mx[h] = m;
+    }
+    if (lane == 0)
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_m[wave][h] = mx[h];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+        mx[h] = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+
+    // values: issue this lane's loads, then exponentials while they fly
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int t = tw + it * PPL;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            raw[it][j] = t < t1 ? *(const u32x4*)(vb + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
+                                : u32x4{0u, 0u, 0u, 0u};
+    }
+    float lsum[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float l = 0.f;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const float e = (tw + it * PPL) < t1 ? __builtin_amdgcn_exp2f(sc[it][h] - mx[h]) : 0.f;
+            sc[it][h] = e;
+            l += e;
+        }
+        lsum[h] = l;
+    }
+    float acc[G][E];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        float vf[E];
+#pragma unroll
+        for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], vf + j * VE);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] += sc[it][h] * vf[e];
+    }
+    // reduce over the wave's position groups (lanes with equal c)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int o = LPP; o < 64; o <<= 1) lsum[h] += __shfl_xor(lsum[h], o);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float v = acc[h][e];
+#pragma unroll
+            for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o);
+            acc[h][e] = v;
+        }
+    }
+    if (jj == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+#pragma unroll
+                for (int i = 0; i < VE; ++i) s_acc[wave][h][(c + LPP * j) * VE + i] = acc[h][j * VE + i];
+            if (c == 0) s_l[wave][h] = lsum[h];
+        }
+    }
+    __syncthreads();
+
+    const float* vs = a.vscale;
+    if (nch == 1) {
+        for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+            const int h = i / D, d = i - h * D;
+            const float o = ((s_acc[0][h][d] + s_acc[1][h][d]) + s_acc[2][h][d]) + s_acc[3][h][d];
+            const float l = ((s_l[0][h] + s_l[1][h]) + s_l[2][h]) + s_l[3][h];
+            store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, o / l * vs[g]);
+        }
+        return;
+    }
+    // several chunks: store this chunk's (max, sum, weighted values); the
+    // last chunk to finish merges all of them in chunk order
+    float* part = a.part + ((size_t)(s * a.hkv + g) * a.n_chunks) * G * (D + 2);
+    const size_t cstride = (size_t)G * (D + 2);
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+        const int h = i / D, d = i - h * D;
+        part[chunk * cstride + h * (D + 2) + d] =
+            ((s_acc[0][h][d] + s_acc[1][h][d]) + s_acc[2][h][d]) + s_acc[3][h][d];
+    }
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        part[chunk * cstride + h * (D + 2) + D] = mx[h];
+        part[chunk * cstride + h * (D + 2) + D + 1] = ((s_l[0][h] + s_l[1][h]) + s_l[2][h]) + s_l[3][h];
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* cp = a.cnt + s * a.hkv + g;
+        int old = atomicAdd(cp, 1);
+        s_last = (old == nch - 1);
+        if (s_last) *cp = 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+        const int h = i / D, d = i - h * D;
+        float M = -INFINITY;
+        for (int q = 0; q < nch; ++q) M = fmaxf(M, part[q * cstride + h * (D + 2) + D]);
+        float L = 0.f, O = 0.f;
+        for (int q = 0; q < nch; ++q) {
+            const float w = __builtin_amdgcn_exp2f(part[q * cstride + h * (D + 2) + D] - M);
+            L += w * part[q * cstride + h * (D + 2) + D + 1];
+            O += w * part[q * cstride + h * (D + 2) + d];
+        }
+        store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, O / L * vs[g]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// row kernels
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+    v = warp_sum_xor<64>(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const float s = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return s;
+}
+
+template <int WT>
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    const bool valid = m < a.S && a.active[m];
+    float ss = 0.f;
+    for (int i = threadIdx.x * 4; i < a.d; i += blockDim.x * 4) {
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (valid) {
+            if (a.x_in) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = load_act1<WT>(a.x_in, (size_t)m * a.d + i + k);
+            } else {
+                v = *(const f32x4*)(a.c + (size_t)m * a.d + i);
+                if (a.z) v += *(const f32x4*)(a.z + (size_t)m * a.d + i);
+            }
+        }
+        *(f32x4*)(a.x + (size_t)m * a.d + i) = v;
+        store_act4<WT>(a.xg, (size_t)m * a.d + i, v * *(const f32x4*)(a.g + i));
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    ss = block_sum_256(ss, red);
+    if (threadIdx.x == 0) a.ss_out[m] = ss;
+}
+
+template <int WT>
+__global__ __launch_bounds__(256) void final_kernel(FinalArgs a) {
+    __shared__ float s_r;
+    const int m = blockIdx.x;
+    const bool valid = m < a.S && a.active[m];
+    if (threadIdx.x == 0) {
+        float s = 0.f;
+        for (int j = 0; j < a.nss; ++j) s += a.ss[(size_t)j * gridDim.x + m];
+        s_r = 1.0f / sqrtf(s * a.inv_d + a.eps);
+    }
+    __syncthreads();
+    const float r = s_r;
+    for (int i = threadIdx.x * 4; i < a.d; i += blockDim.x * 4) {
+        f32x4 y = *(const f32x4*)(a.x + (size_t)m * a.d + i) * r * *(const f32x4*)(a.g + i);
+        if (!valid) y = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.y_out && m < a.S) store_act4<WT>(a.y_out, (size_t)m * a.ldy + a.y_off + i, y);
+        if (a.yw) store_act4<WT>(a.yw, (size_t)m * a.d + i, y);
+        if (a.zf) *(f32x4*)(a.zf + (size_t)m * a.d + i) = y;
+    }
+    if (a.advance && threadIdx.x == 0 && valid) a.pos[m] += 1;
+}
+
+__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
+    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t per_row = a.hd / 4;
+    const size_t total = 2ull * a.hkv * a.n * per_row;
+    if (id >= total) return;
+    const int d0 = (int)(id % per_row) * 4;
+    size_t r = id / per_row;
+    const int t = (int)(r % a.n);
+    r /= a.n;
+    const int g = (int)(r % a.hkv);
+    const int kv = (int)(r / a.hkv);
+    const f32x4 v = *(const f32x4*)(a.src + (((size_t)kv * a.hkv + g) * a.n + t) * a.hd + d0);
+    uint8_t* dst = a.dst + kv * a.kv_stride + g * a.head_stride + (size_t)(a.t0 + t) * a.pos_stride;
+    if (a.kv_fp8) {
+        const float sg = a.kvsig[kv * a.hkv + g];
+        *(uint32_t*)(dst + d0) = enc_e4m3(v[0] / sg) | (enc_e4m3(v[1] / sg) << 8) |
+                                 (enc_e4m3(v[2] / sg) << 16) | (enc_e4m3(v[3] / sg) << 24);
+    } else {
+        *(f32x4*)(dst + (size_t)d0 * 4) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
+    const size_t total = (size_t)(a.N / 16) * a.KB * 64;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (wt) hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int WT, int R>
+static hipError_t gemm_mtg(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    switch (MTG) {
+#define FD_G(MT) case MT: hipLaunchKernelGGL((gemm_kernel<WT, R, MT>), dim3(grid), dim3(256), 0, st, a); break;
+        FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5) FD_G(6) FD_G(7) FD_G(8)
+#undef FD_G
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int wt, int R, int MTG, int grid, hipStream_t st) {
+    if (wt) return R == 2 ? gemm_mtg<1, 2>(a, MTG, grid, st) : gemm_mtg<1, 1>(a, MTG, grid, st);
+    return R == 2 ? gemm_mtg<0, 2>(a, MTG, grid, st) : gemm_mtg<0, 1>(a, MTG, grid, st);
+}
+
+template <int WT, int FP8, int D>
+static hipError_t attn_g(const AttnArgs& a, int G, int grid, hipStream_t st) {
+    switch (G) {
+        case 1: hipLaunchKernelGGL((attn_kernel<WT, FP8, D, 1>), dim3(grid), dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_kernel<WT, FP8, D, 2>), dim3(grid), dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((attn_kernel<WT, FP8, D, 4>), dim3(grid), dim3(256), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int WT, int FP8>
+static hipError_t attn_d(const AttnArgs& a, int hd, int G, int grid, hipStream_t st) {
+    switch (hd) {
+        case 64: return attn_g<WT, FP8, 64>(a, G, grid, st);
+        case 128: return attn_g<WT, FP8, 128>(a, G, grid, st);
+        case 256: return attn_g<WT, FP8, 256>(a, G, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// The attention output takes the activation type (bf16 with bf16 weights,
+// fp32 otherwise); the cache type is independent of it.
+hipError_t launch_attn(const AttnArgs& a, int wt, int kv_fp8, int hd, int G, int grid, hipStream_t st) {
+    if (wt) return kv_fp8 ? attn_d<1, 1>(a, hd, G, grid, st) : attn_d<1, 0>(a, hd, G, grid, st);
+    return kv_fp8 ? attn_d<0, 1>(a, hd, G, grid, st) : attn_d<0, 0>(a, hd, G, grid, st);
+}
+
+hipError_t launch_embed(const EmbedArgs& a, int wt, int rows, hipStream_t st) {
+    if (wt) hipLaunchKernelGGL(embed_kernel<1>, dim3(rows), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(embed_kernel<0>, dim3(rows), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st) {
+    if (wt) hipLaunchKernelGGL(final_kernel<1>, dim3(rows), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(final_kernel<0>, dim3(rows), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st) {
+    const size_t total = 2ull * a.hkv * a.n * (a.hd / 4);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace fd

@@ -1,0 +1,113 @@
+// Host side of the fixed-shape session slots (PersonaPlex 7B page, "A
+// server built around the conversation clock": all sessions advance on one
+// clock in fixed-shape batches; new sessions fill free slots without
+// changing what the GPU runs).  Pure host code.
+//
+// Every operation validates all of its arguments before changing anything,
+// so a failed call leaves the pool as it was.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/fd.h"
+
+namespace fd {
+
+class SlotPool {
+public:
+    SlotPool(int n_slots, int max_context)
+        : active_(n_slots, 0), pos_(n_slots, 0), max_context_(max_context) {}
+
+    int size() const { return (int)active_.size(); }
+    int max_context() const { return max_context_; }
+
+    // n lowest-numbered free slots, ascending; all or nothing.
+    fd_status alloc(int n, int32_t* out) {
+        if (n < 0 || (n > 0 && !out)) return FD_E_INVAL;
+        std::vector<int32_t> pick;
+        for (int s = 0; s < size() && (int)pick.size() < n; ++s)
+            if (!active_[s]) pick.push_back(s);
+        if ((int)pick.size() < n) return FD_E_NOSLOT;
+        for (int i = 0; i < n; ++i) {
+            active_[pick[i]] = 1;
+            pos_[pick[i]] = 0;
+            out[i] = pick[i];
+        }
+        dirty_ = dirty_ || n > 0;
+        return FD_OK;
+    }
+
+    // Marks the listed slots free; rejects out-of-range, unallocated and
+    // repeated ids without changing anything.
+    fd_status free(const int32_t* ids, int n) {
+        if (n < 0 || (n > 0 && !ids)) return FD_E_INVAL;
+        std::vector<char> seen(size(), 0);
+        for (int i = 0; i < n; ++i) {
+            int s = ids[i];
+            if (s < 0 || s >= size() || !active_[s] || seen[s]) return FD_E_BADSLOT;
+            seen[s] = 1;
+        }
+        for (int i = 0; i < n; ++i) active_[ids[i]] = 0;
+        dirty_ = dirty_ || n > 0;
+        return FD_OK;
+    }
+
+    fd_status set_position(int s, int p) {
+        if (s < 0 || s >= size() || !active_[s]) return FD_E_BADSLOT;
+        if (p < 0 || p > max_context_) return FD_E_INVAL;
+        pos_[s] = p;
+        dirty_ = true;
+        return FD_OK;
+    }
+
+    fd_status state(int s, int32_t* a, int32_t* p) const {
+        if (s < 0 || s >= size()) return FD_E_BADSLOT;
+        if (a) *a = active_[s];
+        if (p) *p = pos_[s];
+        return FD_OK;
+    }
+
+    // True if some active slot's window is full (the step may not run).
+    bool any_full(int* which) const {
+        for (int s = 0; s < size(); ++s)
+            if (active_[s] && pos_[s] >= max_context_) {
+                if (which) *which = s;
+                return true;
+            }
+        return false;
+    }
+
+    // After a step: every active slot's position advances by one (the
+    // device does the same on its copy).
+    void advance() {
+        for (int s = 0; s < size(); ++s)
+            if (active_[s]) ++pos_[s];
+    }
+
+    int n_active() const {
+        int n = 0;
+        for (int a : active_) n += a;
+        return n;
+    }
+
+    bool dirty() const { return dirty_; }
+    void clear_dirty() { dirty_ = false; }
+    void mark_dirty() { dirty_ = true; }
+
+    // Device image: int32 active[S] followed by int32 pos[S].
+    void image(int32_t* dst) const {
+        for (int s = 0; s < size(); ++s) {
+            dst[s] = active_[s];
+            dst[size() + s] = pos_[s];
+        }
+    }
+
+private:
+    std::vector<int32_t> active_;
+    std::vector<int32_t> pos_;
+    int max_context_;
+    bool dirty_ = true;
+};
+
+}  // namespace fd

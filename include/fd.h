@@ -1,0 +1,273 @@
+/*
+ * fd.h - C ABI of the frame-synchronous batched decode step (gfx950).
+ *
+ * The problem this library serves (PersonaPlex 7B page, sections "What
+ * Real-time Means for a Full-duplex Agent", "Compressing the Temporal KV
+ * cache" and "A server built around the conversation clock"; Nemotron
+ * VoiceChat case study, "The solution" and "Under the hood"; its
+ * profile.json, serving_profile):
+ *
+ *   - every session advances one frame per step through a decoder stack;
+ *   - all sessions advance together on one clock, in fixed-shape session
+ *     slots; a new session takes a free slot without changing what the GPU
+ *     executes;
+ *   - one read of the weights is shared by every session in the step;
+ *   - conversation state (the temporal cache) stays resident between steps;
+ *     it is stored in FP8 (or fp32 for the talker-style stack) and holds at
+ *     most a fixed window of frames (1500 = 120 s in the profile);
+ *   - a serving profile is fixed per (model, session capacity, context
+ *     length) ahead of time;
+ *   - the GPU does not return to the CPU per operation, and no client I/O
+ *     runs inside the step.
+ *
+ * Conventions for every call:
+ *   - The return value is an fd_status: FD_OK (0) or a negative code.
+ *   - All argument checks run on the host before anything is changed, so a
+ *     call that fails has no effect.  No C++ exception crosses this ABI.
+ *   - "device pointer" means memory allocated on the ctx's GPU (the Python
+ *     binding uses torch uint8 tensors); "host pointer" means CPU memory.
+ *   - A ctx is not thread-safe: one host thread and one stream per ctx.
+ *   - Streams are hipStream_t values passed as void* (NULL = the default
+ *     stream).
+ *   - Errors raised by the HIP runtime are reported as FD_E_DEVICE by the
+ *     call that sees them; fd_last_error() gives the message.
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fd_status;
+
+#define FD_OK             0
+#define FD_E_INVAL       (-1) /* null/misaligned pointer or out-of-range argument */
+#define FD_E_UNSUPPORTED (-2) /* a shape or type the kernels do not implement */
+#define FD_E_NOSLOT      (-3) /* fewer free slots than requested */
+#define FD_E_BADSLOT     (-4) /* slot id out of range, or not allocated */
+#define FD_E_CTXFULL     (-5) /* an active slot has used its whole window */
+#define FD_E_DEVICE      (-6) /* HIP runtime error or device-side fault flag */
+#define FD_E_STATE       (-7) /* call not valid in the ctx's current state */
+
+/* Storage types. */
+#define FD_F32       0
+#define FD_BF16      1
+#define FD_FP8_E4M3  2 /* OCP E4M3 ("e4m3fn"): bias 7, max 448, one NaN pattern */
+
+/*
+ * Serving profile: the decoder shape, slot capacity and window, fixed for
+ * the life of a ctx (Nemotron case study, "Under the hood": profiles are
+ * compiled per model, session capacity and context length).
+ *
+ * Supported: w_dtype == act_dtype in {FD_F32, FD_BF16}; kv_dtype in
+ * {FD_F32, FD_FP8_E4M3}; head_dim in {64, 128, 256}; n_heads a multiple of
+ * n_kv_heads with n_heads / n_kv_heads in {1, 2, 4, 8}; d_model, d_ffn and
+ * n_heads*head_dim multiples of 32 (bf16) or 16 (fp32); max_slots in
+ * 1..4096; max_context in 1..65536.  An optional depth stack (depth_steps >
+ * 0) runs after the main stack on every frame, for depth_steps sequential
+ * sub-steps with its own fp32 cache cleared every frame; it requires
+ * w_dtype == FD_F32 and kv_dtype == FD_F32.
+ */
+typedef struct {
+    int32_t n_layers;
+    int32_t d_model;
+    int32_t n_heads;      /* query heads */
+    int32_t n_kv_heads;   /* key/value heads (GQA: query head h reads kv head h*n_kv_heads/n_heads) */
+    int32_t head_dim;
+    int32_t d_ffn;        /* SwiGLU hidden width */
+    float rms_eps;        /* RMSNorm: x * (mean(x^2) + eps)^(-1/2) * g */
+    float rope_base;      /* rotary angle of pair i at position p: p * base^(-2i/head_dim) */
+    int32_t max_slots;    /* S_cap: session slots, fixed launch shape */
+    int32_t max_context;  /* T_max: frames a slot's cache holds */
+    int32_t w_dtype;      /* FD_F32 or FD_BF16 */
+    int32_t act_dtype;    /* must equal w_dtype */
+    int32_t kv_dtype;     /* FD_F32 or FD_FP8_E4M3 */
+    int32_t depth_steps;  /* 0 = no depth stack */
+    int32_t depth_layers;
+    int32_t depth_d;
+    int32_t depth_heads;
+    int32_t depth_kv_heads;
+    int32_t depth_head_dim;
+    int32_t depth_ffn;
+} fd_config;
+
+/* Byte sizes of the four caller-allocated device buffers. */
+typedef struct {
+    uint64_t packed_weights; /* weights in the kernels' tile layout + constant tables */
+    uint64_t kv_arena;       /* the slot-pooled cache, layout in fd_kv_view */
+    uint64_t workspace;      /* activations, partial results, counters */
+    uint64_t slot_table;     /* device copy of per-slot active flag and position */
+} fd_sizes;
+
+/*
+ * One decoder layer's parameters: device pointers to row-major matrices in
+ * nn.Linear [out, in] layout, in w_dtype (bf16 as raw 16-bit values), and
+ * fp32 RMSNorm gains.
+ *   wq [n_heads*head_dim][d]   wk, wv [n_kv_heads*head_dim][d]
+ *   wo [d][n_heads*head_dim]   w_gate, w_up [d_ffn][d]   w_down [d][d_ffn]
+ *   g_attn, g_ffn [d] (fp32)
+ */
+typedef struct {
+    const void* wq;
+    const void* wk;
+    const void* wv;
+    const void* wo;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+    const float* g_attn;
+    const float* g_ffn;
+} fd_layer_weights;
+
+/*
+ * All parameters.  `layers` and `depth_layers` are HOST arrays of
+ * fd_layer_weights whose members are device pointers.
+ *   g_final [d] fp32 (device)
+ *   kv_scale [n_layers][2 (K|V)][n_kv_heads] fp32 (device); required for
+ *     FD_FP8_E4M3 caches (a cached entry is stored as code(x / scale) and
+ *     read back as scale * decode(code)); ignored for FD_F32 caches
+ *   w_in [depth_d][d_model], depth_layers[depth_layers], depth_g_final
+ *     [depth_d]: the depth stack (only when depth_steps > 0)
+ */
+typedef struct {
+    const fd_layer_weights* layers;
+    const float* g_final;
+    const float* kv_scale;
+    const void* w_in;
+    const fd_layer_weights* depth_layers;
+    const float* depth_g_final;
+} fd_weights;
+
+/* The four device buffers, each at least the size fd_plan reports and
+ * 256-byte aligned.  The ctx borrows them until fd_destroy. */
+typedef struct {
+    void* packed_weights;
+    void* kv_arena;
+    void* workspace;
+    void* slot_table;
+} fd_buffers;
+
+/*
+ * Cache layout (returned by fd_kv_layout).  Slot-major, one contiguous
+ * region per session:
+ *   element (slot s, layer l, kv (0 = K, 1 = V), kv-head g, position t, dim d)
+ *   lives at byte  base + ((((s*L + l)*2 + kv)*H_kv + g)*T_max + t)*D*elem_bytes
+ *                  + d*elem_bytes
+ * Key vectors are stored after the rotary embedding.  For FP8 caches each
+ * byte is an OCP E4M3 code of value / kv_scale[l][kv][g].
+ */
+typedef struct {
+    void* base;              /* device pointer to the arena */
+    uint64_t slot_stride;    /* bytes between consecutive slots */
+    uint64_t layer_stride;   /* bytes between consecutive layers of a slot */
+    uint64_t kv_stride;      /* bytes between the K and V blocks of a layer */
+    uint64_t head_stride;    /* bytes between kv heads */
+    uint64_t pos_stride;     /* bytes between positions (head_dim * elem_bytes) */
+    int32_t elem_bytes;      /* 1 (FP8) or 4 (fp32) */
+    int32_t n_layers, n_kv_heads, max_context, head_dim, max_slots;
+    const float* kv_scale;   /* device copy of the scales [L][2][H_kv] (NULL for fp32) */
+    int32_t* slot_active;    /* device int32 [max_slots] */
+    int32_t* slot_pos;       /* device int32 [max_slots]: next frame index */
+} fd_kv_view;
+
+typedef struct fd_ctx fd_ctx;
+
+/* Pure host function: validates cfg and reports the buffer sizes.
+ * FD_E_INVAL for null pointers, FD_E_UNSUPPORTED for shapes outside the
+ * supported set. */
+fd_status fd_plan(const fd_config* cfg, fd_sizes* out);
+
+/*
+ * Creates a ctx.  Validates cfg and every pointer, then on `stream`:
+ * repacks the weights into buf->packed_weights (the caller's weight
+ * tensors may be freed once the stream has passed this point), writes the
+ * constant tables (rotary cos/sin computed on the host in double and
+ * rounded to fp32; FP8 scales), clears the counters in the workspace and
+ * marks every slot inactive.  The ctx borrows `buf` until fd_destroy.
+ * Errors: FD_E_INVAL, FD_E_UNSUPPORTED, FD_E_DEVICE.
+ */
+fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* buf,
+                  void* stream, fd_ctx** out);
+
+/*
+ * Admits n new sessions at frame position 0.  Takes the n lowest-numbered
+ * free slots and writes their ids, ascending, to the host array slots_out.
+ * All or nothing: FD_E_NOSLOT (and no change) if fewer than n slots are
+ * free.  The change reaches the device with the next fd_step on the ctx's
+ * stream; the launch shape of fd_step does not change.  The slot's old
+ * cache bytes are not cleared: positions >= the slot's position are never
+ * read.
+ */
+fd_status fd_alloc_slots(fd_ctx* ctx, int32_t n, int32_t* slots_out);
+
+/*
+ * Advances every active slot by one frame.
+ *   x_in   device [max_slots][d_model] in act_dtype: slot s's new frame
+ *          embedding in row s; rows of inactive slots are ignored.
+ *   y_out  device [max_slots][d_model] in act_dtype: the final-normed
+ *          output; rows of inactive slots are set to 0.
+ *   depth_out device [max_slots][depth_steps][depth_d] in act_dtype, or
+ *          NULL when the profile has no depth stack; inactive rows set to 0.
+ * Each active slot's new key/value are appended at its position, which then
+ * advances by one.  Enqueued on `stream` without waiting (the caller syncs);
+ * no host I/O and no allocation.  FD_E_CTXFULL (and no launch) if an active
+ * slot's position equals max_context.
+ */
+fd_status fd_step(fd_ctx* ctx, const void* x_in, void* y_out, void* depth_out, void* stream);
+
+/*
+ * Ends sessions: marks the n slots (host array) free.  FD_E_BADSLOT and no
+ * change if any id is out of range, not allocated, or repeated.
+ */
+fd_status fd_free(fd_ctx* ctx, const int32_t* slots, int32_t n);
+
+/* Releases the ctx's host state.  Device buffers belong to the caller. */
+fd_status fd_destroy(fd_ctx* ctx);
+
+/* ---- inspection and bench/test hooks ---- */
+
+/* Fills *out with the cache layout and the device slot-table pointers. */
+fd_status fd_kv_layout(fd_ctx* ctx, fd_kv_view* out);
+
+/*
+ * Sets an allocated slot's next frame index (0..max_context), e.g. after a
+ * caller-side prefill, or to rewind a slot between timed steps.  Reaches
+ * the device with the next fd_step.  FD_E_BADSLOT for an unallocated slot,
+ * FD_E_INVAL for a position outside 0..max_context.
+ */
+fd_status fd_set_position(fd_ctx* ctx, int32_t slot, int32_t pos);
+
+/* Host copy of a slot's state: *active (0/1) and *pos. */
+fd_status fd_slot_state(fd_ctx* ctx, int32_t slot, int32_t* active, int32_t* pos);
+
+/*
+ * Writes cache entries from raw values, stored exactly as the step stores
+ * new frames (FP8: code(value / kv_scale[layer][kv][g]), round to nearest
+ * even, saturating at +-448; fp32: the value).
+ *   src: device fp32 [2 (K|V)][n_kv_heads][n][head_dim], positions t0..t0+n-1
+ * of `slot` at `layer`.  Enqueued on `stream`.  The slot need not be
+ * allocated.  FD_E_INVAL for a range outside the window.
+ */
+fd_status fd_kv_write(fd_ctx* ctx, int32_t slot, int32_t layer, int32_t t0, int32_t n,
+                      const float* src, void* stream);
+
+/* Waits for the ctx's last enqueued work on `stream` and reports device
+ * errors (FD_E_DEVICE) including the kernels' own fault flag. */
+fd_status fd_sync(fd_ctx* ctx, void* stream);
+
+/* Message of the ctx's most recent error ("" if none); valid until the
+ * next call on the ctx.  With ctx == NULL, the last fd_plan/fd_init error. */
+const char* fd_last_error(fd_ctx* ctx);
+
+/* Static name of a status code. */
+const char* fd_status_str(fd_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

@@ -1,0 +1,259 @@
+"""GPU parity of the HIP decode step against the oracle, through the C ABI,
+at sizes the oracle finishes in seconds (several tiles, ragged tails,
+multi-chunk attention).  Tolerances: max relative row error 1e-3 on the
+fp32 path, 2e-2 on the bf16/FP8 path; cache indexing bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import Oracle, fp8
+from tests.helpers import make_context, rel_err_rows, rows_input, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _sentinel_fill(ctx, cfg):
+    if cfg["kv_dtype"] == "fp8":
+        ctx.arena.fill_(0x7F)
+    else:
+        ctx.arena.view(torch.int32)[: ctx.arena.numel() // 4].fill_(0x7FC00001)
+    torch.cuda.synchronize()
+
+
+def _is_sentinel(a: np.ndarray, fp8_cache: bool) -> np.ndarray:
+    if fp8_cache:
+        return a == 0x7F
+    return a.view(np.int32) == 0x7FC00001
+
+
+def test_encoder_bit_exact_and_layout():
+    """fd_kv_write stores code(value / sigma) exactly as the oracle's codec,
+    at the documented offsets; special values included."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=256, n_heads=2, n_kv_heads=2,
+                              d_ffn=256, max_slots=3, max_context=64)
+    model = synth.Model(cfg)
+    say("encoder: build ctx")
+    ctx = make_context(cfg, model)
+    _sentinel_fill(ctx, cfg)
+    rng = np.random.default_rng(3)
+    n = 40
+    vals = (rng.standard_normal((2, 2, n, 128)) * 3.0).astype(np.float32)
+    sig = model.kv_scale[1]  # [2][H_kv]
+    # exact ties between codes, values beyond 448 * sigma, tiny subnormals
+    codes_all = fp8.DECODE_TABLE[np.isfinite(fp8.DECODE_TABLE)]
+    mids = (np.sort(np.unique(np.abs(codes_all)))[:-1] + np.sort(np.unique(np.abs(codes_all)))[1:]) / 2
+    k = min(128, mids.size)
+    vals[0, 0, 1, :k] = (mids[:k] * sig[0, 0]).astype(np.float32)
+    vals[0, 1, 2, :8] = np.array([500, -500, 1e6, -1e-30, 0, -0.0, 448, 449], np.float32) * sig[0, 1]
+    src = torch.from_numpy(vals).cuda()
+    ctx.fd_kv_write(1, 1, 5, src)
+    torch.cuda.synchronize()
+    arena = ctx.arena_view().cpu().numpy()
+    got = arena[1, 1, :, :, 5:5 + n, :]
+    expect = fp8.encode(vals / sig.astype(np.float32)[:, :, None, None])
+    # -0.0 / sigma keeps its sign; the oracle codec returns 0x80 for it
+    assert np.array_equal(got, expect)
+    mask = np.ones(arena.shape, dtype=bool)
+    mask[1, 1, :, :, 5:5 + n, :] = False
+    assert np.all(arena[mask] == 0x7F), "bytes outside the written range changed"
+
+
+def _run_steps(cfg, model, slot_pos, n_steps, *, tol, sentinel=True, gain_noise=False):
+    """Prefill each listed slot to its start position, then step n_steps
+    frames; compare every step's outputs with the oracle."""
+    say(f"parity: cfg L={cfg['n_layers']} d={cfg['d_model']} S={cfg['max_slots']} "
+        f"kv={cfg['kv_dtype']} slots={slot_pos}")
+    ctx = make_context(cfg, model)
+    if sentinel:
+        _sentinel_fill(ctx, cfg)
+    orc = Oracle(cfg, model)
+    slots = ctx.fd_alloc_slots(len(slot_pos))
+    sess = {s: 100 + s for s in slots}
+    pos = dict(zip(slots, slot_pos))
+    for s in slots:
+        p = pos[s]
+        if p:
+            for l in range(cfg["n_layers"]):
+                v = synth.prefill_values(cfg, sess[s], l, p)
+                orc.prefill(s, l, v)
+                ctx.fd_kv_write(s, l, 0, torch.from_numpy(v).cuda())
+            ctx.fd_set_position(s, p)
+    worst = 0.0
+    y = torch.empty((cfg["max_slots"], cfg["d_model"]), device="cuda",
+                    dtype=torch.bfloat16 if cfg["act_dtype"] == "bf16" else torch.float32)
+    dout = None
+    if cfg.get("depth_steps", 0):
+        dout = torch.empty((cfg["max_slots"], cfg["depth_steps"], cfg["depth_d"]), device="cuda",
+                           dtype=y.dtype)
+    for step in range(n_steps):
+        x_np, x = rows_input(cfg, sess, {s: pos[s] for s in slots})
+        y.fill_(7.0)
+        ctx.fd_step(x, y, dout)
+        ctx.fd_sync()
+        act = sorted(slots)
+        ref = orc.step(act, x_np[act], [pos[s] for s in act])
+        if dout is not None:
+            ref, zref = ref
+        yg = to_np(y)
+        e = rel_err_rows(yg[act], ref)
+        worst = max(worst, e)
+        say(f"  step {step}: max rel err {e:.3e}")
+        assert e <= tol, f"step {step}: {e}"
+        inactive = [s for s in range(cfg["max_slots"]) if s not in act]
+        assert np.all(yg[inactive] == 0), "inactive rows must be zero"
+        if dout is not None:
+            zg = to_np(dout)
+            ez = rel_err_rows(zg[act].reshape(-1, cfg["depth_d"]), zref.reshape(-1, cfg["depth_d"]))
+            say(f"  depth: max rel err {ez:.3e}")
+            assert ez <= tol
+            assert np.all(zg[inactive] == 0)
+        for s in slots:
+            pos[s] += 1
+            assert ctx.fd_slot_state(s) == (1, pos[s])
+    dev_pos = ctx.slot_table_view().cpu().numpy()
+    for s in slots:
+        assert dev_pos[1, s] == pos[s], "device position must advance with the host's"
+    return ctx, orc, slots, pos, worst
+
+
+def _check_cache(ctx, orc, cfg, slots, pos, start):
+    """Cache bytes: written exactly at positions start[s]..pos[s]-1 (plus the
+    prefill), never elsewhere; values equal the oracle's up to the rounding
+    of the projection (FP8: codes within one step, almost all identical)."""
+    fp8_cache = cfg["kv_dtype"] == "fp8"
+    arena = ctx.arena_view().cpu().numpy()
+    for s in range(cfg["max_slots"]):
+        a = arena[s]
+        if s not in slots:
+            assert np.all(_is_sentinel(a, fp8_cache)), f"slot {s} touched"
+            continue
+        p = pos[s]
+        assert not np.any(_is_sentinel(a[:, :, :, :p, :], fp8_cache)), f"slot {s}: hole below {p}"
+        assert np.all(_is_sentinel(a[:, :, :, p:, :], fp8_cache)), f"slot {s}: write past {p}"
+        ref = orc.cache.slot(s)[:, :, :, :p, :]
+        got = a[:, :, :, :p, :]
+        new = slice(start[s], p)
+        if fp8_cache:
+            # prefilled entries were encoded from identical fp32 values: bit-exact
+            assert np.array_equal(got[:, :, :, :start[s]], ref[:, :, :, :start[s]])
+            g = got[:, :, :, new].astype(np.int32)
+            r = ref[:, :, :, new].astype(np.int32)
+            # order-preserving map of sign-magnitude codes
+            key = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F)  # noqa: E731
+            assert np.max(np.abs(key(g) - key(r))) <= 1
+            assert np.mean(g == r) > 0.9
+        else:
+            np.testing.assert_allclose(got, ref, rtol=2e-4, atol=2e-5 * np.max(np.abs(ref)))
+
+
+def test_tiny_fp32_sixteen_frames():
+    """Two sessions x 16 frames from an empty fp32 cache (the tiny
+    workload), 1e-3, with the cache checked byte-for-byte against the
+    sentinel fill."""
+    cfg = synth.get_config("tiny")
+    model = synth.Model(cfg, gain_noise=True)
+    ctx, orc, slots, pos, worst = _run_steps(cfg, model, [0, 0], 16, tol=1e-3)
+    _check_cache(ctx, orc, cfg, slots, pos, {s: 0 for s in slots})
+
+
+def test_bf16_fp8_ragged_multichunk():
+    """bf16 weights/activations, FP8 cache, 7B head geometry (128-dim MHA)
+    at reduced width and depth; slots at positions spanning 1..3 attention
+    chunks, one slot left empty."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
+                              d_ffn=1408, max_slots=9, max_context=700)
+    model = synth.Model(cfg, gain_noise=True)
+    start = [0, 1, 255, 256, 257, 300, 511, 690]
+    ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
+    _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
+
+
+def test_fp32_gqa_with_depth_loop():
+    """Talker geometry (GQA 4:1, head_dim 256, fp32) at reduced width, with
+    the 8-step depth loop of a 128-dim-head stack; 1e-3."""
+    cfg = synth.scaled_config("talker_s56", n_layers=2, d_model=384, d_ffn=768, max_slots=5,
+                              max_context=300, depth_layers=2, depth_d=256, depth_heads=2,
+                              depth_kv_heads=2, depth_ffn=512)
+    model = synth.Model(cfg, gain_noise=True)
+    start = [0, 63, 64, 200]
+    ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 2, tol=1e-3)
+    _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
+
+
+def test_admission_and_free_keep_launch_shape():
+    """Sessions freed and admitted between steps: new sessions start at
+    position 0 in the lowest free slot, equal a fresh oracle session, and
+    the other sessions are unaffected (bit-identical to an undisturbed run)."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=256, n_heads=2, n_kv_heads=2,
+                              d_ffn=512, max_slots=4, max_context=64)
+    model = synth.Model(cfg)
+    say("admission: two contexts")
+    a = make_context(cfg, model)
+    b = make_context(cfg, model)
+    sa = a.fd_alloc_slots(3)
+    sb = b.fd_alloc_slots(3)
+    assert sa == sb == [0, 1, 2]
+    y_a = torch.empty((4, 256), device="cuda", dtype=torch.bfloat16)
+    y_b = torch.empty_like(y_a)
+    sess = {0: 10, 1: 11, 2: 12}
+    frames = {0: 0, 1: 0, 2: 0}
+    for t in range(3):
+        _, x = rows_input(cfg, sess, frames)
+        a.fd_step(x, y_a)
+        b.fd_step(x, y_b)
+        for s in frames:
+            frames[s] += 1
+    # in b: end session 1 and admit a new one (goes to slot 1, position 0)
+    b.fd_free([1])
+    assert b.fd_alloc_slots(1) == [1]
+    assert b.fd_slot_state(1) == (1, 0)
+    sess_b = dict(sess)
+    sess_b[1] = 99
+    frames_b = dict(frames)
+    frames_b[1] = 0
+    orc = Oracle(cfg, model)
+    for t in range(4):
+        _, xa = rows_input(cfg, sess, frames)
+        xb_np, xb = rows_input(cfg, sess_b, frames_b)
+        a.fd_step(xa, y_a)
+        b.fd_step(xb, y_b)
+        torch.cuda.synchronize()
+        ya, yb = to_np(y_a), to_np(y_b)
+        assert np.array_equal(ya[[0, 2]], yb[[0, 2]]), "other sessions must be bit-identical"
+        ref = orc.step([1], xb_np[[1]], [frames_b[1]])
+        assert rel_err_rows(yb[[1]], ref) <= 2e-2
+        for s in frames:
+            frames[s] += 1
+            frames_b[s] += 1
+
+
+def test_deterministic_and_isolated():
+    """Two runs give bit-identical outputs; changing other slots' inputs
+    and caches leaves a session's output bit-identical."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                              d_ffn=1024, max_slots=6, max_context=400)
+    model = synth.Model(cfg)
+    say("determinism: ctx")
+    ctx = make_context(cfg, model)
+    slots = ctx.fd_alloc_slots(6)
+    for s in slots:
+        for l in range(cfg["n_layers"]):
+            ctx.fd_kv_write(s, l, 0, torch.from_numpy(synth.prefill_values(cfg, s, l, 350)).cuda())
+    outs = []
+    for run in range(3):
+        for s in slots:
+            ctx.fd_set_position(s, 350)
+        sess = {s: s for s in slots}
+        _, x = rows_input(cfg, sess, {s: 350 for s in slots})
+        if run == 2:  # perturb slots 0 and 5: inputs and caches
+            x[0] = torch.randn_like(x[0]) * 5
+            x[5] = 0
+            ctx.arena_view()[0].random_(0, 127)
+            ctx.arena_view()[5].random_(0, 127)
+        y = torch.empty_like(x)
+        ctx.fd_step(x, y)
+        ctx.fd_sync()
+        outs.append(to_np(y))
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0][1:5], outs[2][1:5])

@@ -1,0 +1,208 @@
+"""Host-side logic of the C ABI, without a GPU: the built libraries load and
+export every declared symbol; profile validation; buffer sizes and the
+cache layout formula; the slot state machine (admission order,
+all-or-nothing allocation, frees, positions, full windows)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+from frame_decode_amd.abi import (FD_E_BADSLOT, FD_E_INVAL, FD_E_NOSLOT, FD_E_UNSUPPORTED, FD_OK,
+                                  FdConfig, FdSizes, config_from_dict)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(ROOT, "frame_decode_amd", "libfd.so")
+HOST = os.path.join(ROOT, "frame_decode_amd", "libfd_host.so")
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fd_status|const char\*)\s+(fd_\w+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def host():
+    if not os.path.exists(HOST):
+        pytest.fail("libfd_host.so not built (run __graft_entry__.build())")
+    h = ctypes.CDLL(HOST)
+    h.fdh_pool_new.restype = ctypes.c_void_p
+    h.fdh_pool_new.argtypes = [ctypes.c_int, ctypes.c_int]
+    for n in ("fdh_pool_alloc", "fdh_pool_free"):
+        getattr(h, n).argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
+    h.fdh_pool_alloc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    h.fdh_pool_set_position.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+    h.fdh_pool_state.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                 ctypes.POINTER(ctypes.c_int32)]
+    for n in ("fdh_pool_any_full", "fdh_pool_advance", "fdh_pool_dirty", "fdh_pool_clear_dirty",
+              "fdh_pool_delete"):
+        getattr(h, n).argtypes = [ctypes.c_void_p]
+    h.fdh_pool_image.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]
+    h.fdh_plan.argtypes = [ctypes.POINTER(FdConfig), ctypes.POINTER(FdSizes)]
+    h.fdh_last_error.restype = ctypes.c_char_p
+    h.fdh_gemm_shape.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_int32)]
+    return h
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "libfd.so not built"
+    lib = ctypes.CDLL(LIB)
+    syms = declared_symbols()
+    assert len(syms) >= 13
+    for s in syms:
+        assert hasattr(lib, s), s
+    from frame_decode_amd.abi import EXPORTS
+    assert sorted(EXPORTS) == syms
+
+
+def test_fd_plan_through_the_product_library():
+    """fd_plan is pure host code: callable without a GPU."""
+    from frame_decode_amd import fd_plan
+    s = fd_plan(synth.get_config("7b_s80_p1499"))
+    # [S][L][K|V][H_kv][T][D] bytes: 80 * 32 * 2 * 32 * 1500 * 128
+    assert s["kv_arena"] == 80 * 32 * 2 * 32 * 1500 * 128
+    # packed weights hold at least every weight once
+    assert s["packed_weights"] >= 13_153_337_344
+    assert s["packed_weights"] < 13_153_337_344 * 1.01
+
+
+def _plan(host, cfg):
+    c = config_from_dict(cfg)
+    s = FdSizes()
+    st = host.fdh_plan(ctypes.byref(c), ctypes.byref(s))
+    return st, s
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_every_workload_is_supported(host, name):
+    st, s = _plan(host, synth.get_config(name))
+    assert st == FD_OK, host.fdh_last_error()
+    cfg = synth.get_config(name)
+    eb = 1 if cfg["kv_dtype"] == "fp8" else 4
+    assert s.kv_arena == max(256, cfg["max_slots"] * cfg["n_layers"] * 2 * cfg["n_kv_heads"] *
+                             cfg["max_context"] * cfg["head_dim"] * eb)
+
+
+def test_fp8_cache_is_half_of_bf16_and_quarter_of_fp32(host):
+    """The FP8 cache halves the cache bytes of a 16-bit cache (PersonaPlex
+    page, "Compressing the Temporal KV cache"); fp32 is four times FP8."""
+    a = synth.get_config("7b_s80_p1499")
+    b = dict(a, kv_dtype="f32", w_dtype="f32", act_dtype="f32")
+    _, sa = _plan(host, a)
+    _, sb = _plan(host, b)
+    assert sb.kv_arena == 4 * sa.kv_arena
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, FD_E_UNSUPPORTED),
+    ("n_kv_heads", 3, FD_E_UNSUPPORTED),
+    ("d_model", 100, FD_E_UNSUPPORTED),
+    ("d_ffn", 0, FD_E_UNSUPPORTED),
+    ("max_slots", 0, FD_E_UNSUPPORTED),
+    ("max_context", 0, FD_E_UNSUPPORTED),
+    ("rope_base", -1.0, FD_E_INVAL),
+    ("rms_eps", float("nan"), FD_E_INVAL),
+    ("act_dtype", "f32", FD_E_UNSUPPORTED),
+])
+def test_bad_profiles_are_rejected(host, field, value, status):
+    cfg = synth.get_config("7b_s8_p256")
+    cfg[field] = value
+    st, _ = _plan(host, cfg)
+    assert st == status
+    assert host.fdh_last_error()
+
+
+def test_depth_stack_needs_fp32(host):
+    cfg = synth.get_config("talker_s56")
+    cfg.update(w_dtype="bf16", act_dtype="bf16")
+    st, _ = _plan(host, cfg)
+    assert st == FD_E_UNSUPPORTED
+
+
+def test_gemm_tiling_covers_the_projection(host):
+    out = (ctypes.c_int32 * 9)()
+    for (N, K, wt, MT) in [(12288, 4096, 1, 5), (4096, 11264, 1, 5), (22528, 4096, 1, 1),
+                           (1536, 1152, 0, 4), (1024, 2816, 0, 4), (4096, 4096, 1, 47)]:
+        host.fdh_gemm_shape(N, K, wt, MT, out)
+        NB, KB, R, P, MG, MTG, ng, grid, KT = list(out)
+        assert NB * 16 == N and KB * KT == K
+        assert ng * 4 * R >= NB and MG * MTG >= MT and MTG <= 8
+        assert 1 <= P <= KB and grid == ng * P * MG
+
+
+class Pool:
+    def __init__(self, h, n, T):
+        self.h = h
+        self.p = h.fdh_pool_new(n, T)
+        self.n = n
+
+    def alloc(self, k):
+        out = (ctypes.c_int32 * max(1, k))()
+        st = self.h.fdh_pool_alloc(self.p, k, out)
+        return st, [out[i] for i in range(k)]
+
+    def free(self, ids):
+        arr = (ctypes.c_int32 * max(1, len(ids)))(*ids)
+        return self.h.fdh_pool_free(self.p, arr, len(ids))
+
+    def state(self, s):
+        a, p = ctypes.c_int32(), ctypes.c_int32()
+        st = self.h.fdh_pool_state(self.p, s, ctypes.byref(a), ctypes.byref(p))
+        return st, a.value, p.value
+
+    def image(self):
+        out = (ctypes.c_int32 * (2 * self.n))()
+        self.h.fdh_pool_image(self.p, out)
+        return list(out)
+
+
+def test_slot_state_machine(host):
+    P = Pool(host, 5, 10)
+    st, ids = P.alloc(3)
+    assert st == FD_OK and ids == [0, 1, 2]
+    assert P.free([1]) == FD_OK
+    st, ids = P.alloc(2)
+    assert st == FD_OK and ids == [1, 3]  # lowest free first
+    before = P.image()
+    st, _ = P.alloc(2)  # only slot 4 is free: all or nothing
+    assert st == FD_E_NOSLOT and P.image() == before
+    # double free / unallocated / out of range / repeated: rejected, no change
+    assert P.free([4]) == FD_E_BADSLOT
+    assert P.free([0, 0]) == FD_E_BADSLOT
+    assert P.free([0, 7]) == FD_E_BADSLOT
+    assert P.free([-1]) == FD_E_BADSLOT
+    assert P.image() == before
+    assert P.free([0, 3]) == FD_OK
+    assert P.state(0)[1] == 0 and P.state(3)[1] == 0
+
+
+def test_positions_advance_and_full_window(host):
+    P = Pool(host, 3, 4)
+    _, ids = P.alloc(2)
+    assert host.fdh_pool_set_position(P.p, 0, 3) == FD_OK
+    assert host.fdh_pool_set_position(P.p, 2, 1) == FD_E_BADSLOT  # not allocated
+    assert host.fdh_pool_set_position(P.p, 1, 5) == FD_E_INVAL    # beyond the window
+    assert host.fdh_pool_any_full(P.p) == -1
+    host.fdh_pool_advance(P.p)
+    assert P.state(0)[1:] == (1, 4) and P.state(1)[1:] == (1, 1)
+    assert P.state(2)[1:] == (0, 0)  # inactive slots do not advance
+    assert host.fdh_pool_any_full(P.p) == 0
+    # re-admission starts at position 0
+    assert P.free([0]) == FD_OK
+    st, ids = P.alloc(1)
+    assert ids == [0] and P.state(0)[1:] == (1, 0)
+
+
+def test_device_image_layout(host):
+    P = Pool(host, 4, 8)
+    P.alloc(2)
+    host.fdh_pool_set_position(P.p, 1, 5)
+    assert P.image() == [1, 1, 0, 0, 0, 5, 0, 0]
+    host.fdh_pool_clear_dirty(P.p)
+    assert host.fdh_pool_dirty(P.p) == 0
+    host.fdh_pool_set_position(P.p, 0, 2)
+    assert host.fdh_pool_dirty(P.p) == 1
