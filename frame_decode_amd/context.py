@@ -124,6 +124,17 @@ class Context:
         _check(_lib().fd_kv_layout(self._ctx, ctypes.byref(v)), self._ctx)
         return {f: getattr(v, f) for f, _ in FdKvView._fields_}
 
+    def fd_profile(self, enable: bool) -> None:
+        _check(_lib().fd_profile(self._ctx, 1 if enable else 0), self._ctx)
+
+    def fd_profile_read(self) -> dict:
+        """{kind: (total ms, launches)} since the last read."""
+        n = abi.FD_N_KINDS
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        _check(_lib().fd_profile_read(self._ctx, ms, cnt, n), self._ctx)
+        return {abi.KIND_NAMES[k]: (float(ms[k]), int(cnt[k])) for k in range(n)}
+
     def fd_sync(self, stream=None) -> None:
         _check(_lib().fd_sync(self._ctx, ctypes.c_void_p(_stream_handle(stream))), self._ctx)
 

@@ -32,6 +32,12 @@ struct fd_ctx {
     hipEvent_t ev[kRing] = {};
     bool ev_used[kRing] = {};
     int ring = 0;
+    // per-kernel timing
+    bool prof = false;
+    std::vector<hipEvent_t> ev_pool;
+    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> prof_pending;
+    double prof_ms[FD_N_KINDS] = {};
+    int64_t prof_n[FD_N_KINDS] = {};
     explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context) {}
 };
 
@@ -137,6 +143,32 @@ hipError_t upload_tables(fd_ctx* c, const fd::StackPlan& sp, const std::vector<f
     return e;
 }
 
+hipEvent_t take_event(fd_ctx* c) {
+    if (!c->ev_pool.empty()) {
+        hipEvent_t e = c->ev_pool.back();
+        c->ev_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs `launch` on stream st; with timing on, brackets it with events.
+template <class F>
+hipError_t timed(fd_ctx* c, int kind, hipStream_t st, F&& launch) {
+    if (!c->prof) return launch();
+    hipEvent_t a = take_event(c), b = take_event(c);
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, st);
+    if (e == hipSuccess) e = launch();
+    if (e == hipSuccess) e = hipEventRecord(b, st);
+    c->prof_pending.push_back({kind, {a, b}});
+    return e;
+}
+
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_O, K_GU, K_DOWN, K_FINAL, K_WIN };
+
 struct CacheRef {
     uint8_t* base;
     uint64_t slot, layer, kv, head, pos;
@@ -189,7 +221,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         q.kv_fp8 = cache.fp8;
         q.arena = layer_cache;
         q.slot_stride = cache.slot; q.kv_stride = cache.kv; q.head_stride = cache.head; q.pos_stride = cache.pos;
-        e = fd::launch_gemm(q, wt, sq.R, sq.MTG, sq.grid(), st);
+        e = timed(c, K_QKV, st, [&] { return fd::launch_gemm(q, wt, sq.R, sq.MTG, sq.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::AttnArgs at{};
@@ -205,7 +237,9 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.part = (float*)Wk(c, pl.ws_apart);
         at.cnt = (int*)Wk(c, pl.ws_acnt);
         at.o_out = Wk(c, pl.ws_o);
-        e = fd::launch_attn(at, wt, q.kv_fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
+        e = timed(c, K_ATTN, st, [&] {
+            return fd::launch_attn(at, wt, q.kv_fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
+        });
         if (e != hipSuccess) break;
 
         fd::GemmArgs o = g;
@@ -219,7 +253,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         o.g_next = (const float*)P(c, lo.g_ffn);
         o.ss_out = (float*)Wk(c, pl.ws_ss_f);
         o.ld = d.d;
-        e = fd::launch_gemm(o, wt, so.R, so.MTG, so.grid(), st);
+        e = timed(c, K_O, st, [&] { return fd::launch_gemm(o, wt, so.R, so.MTG, so.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::GemmArgs u = g;
@@ -232,7 +266,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         u.nss = so.n_groups;
         u.h_out = Wk(c, pl.ws_h);
         u.F = d.f;
-        e = fd::launch_gemm(u, wt, su.R, su.MTG, su.grid(), st);
+        e = timed(c, K_GU, st, [&] { return fd::launch_gemm(u, wt, su.R, su.MTG, su.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::GemmArgs dn = g;
@@ -246,7 +280,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         dn.g_next = (const float*)P(c, l + 1 < d.L ? sp.layers[l + 1].g_attn : sp.g_final);
         dn.ss_out = (float*)Wk(c, pl.ws_ss_a);
         dn.ld = d.d;
-        e = fd::launch_gemm(dn, wt, sd.R, sd.MTG, sd.grid(), st);
+        e = timed(c, K_DOWN, st, [&] { return fd::launch_gemm(dn, wt, sd.R, sd.MTG, sd.grid(), st); });
         nss = sd.n_groups;
     }
     *nss_out = nss;
@@ -420,7 +454,7 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
     em.xg = Wk(c, pl.ws_xg);
     em.g = (const float*)P(c, md.L > 0 ? mp.layers[0].g_attn : mp.g_final);
     em.ss_out = (float*)Wk(c, pl.ws_ss_a);
-    e = fd::launch_embed(em, pl.wt, pl.Sp, st);
+    e = timed(c, K_EMBED, st, [&] { return fd::launch_embed(em, pl.wt, pl.Sp, st); });
     int nss = 1;
     CacheRef mc{(uint8_t*)c->buf.kv_arena, pl.kv_slot_stride, pl.kv_layer_stride, pl.kv_kv_stride,
                 pl.kv_head_stride, pl.kv_pos_stride, pl.kv_fp8};
@@ -442,7 +476,7 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
         f.yw = pl.depth ? Wk(c, pl.ws_yw) : nullptr;
         f.pos = slot_pos(c);
         f.advance = 1;
-        e = fd::launch_final(f, pl.wt, pl.Sp, st);
+        e = timed(c, K_FINAL, st, [&] { return fd::launch_final(f, pl.wt, pl.Sp, st); });
     }
     if (e == hipSuccess && pl.depth) {
         const fd::StackPlan& dp = pl.dstack;
@@ -457,7 +491,7 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
         g.epi = fd::EPI_F32;
         g.y = (float*)Wk(c, pl.ws_c);
         g.ld = dd.d;
-        e = fd::launch_gemm(g, pl.wt, pl.win.R, pl.win.MTG, pl.win.grid(), st);
+        e = timed(c, K_WIN, st, [&] { return fd::launch_gemm(g, pl.wt, pl.win.R, pl.win.MTG, pl.win.grid(), st); });
         const uint64_t pos_b = (uint64_t)dd.hd * 4, head_b = pos_b * dd.T, kv_b = head_b * dd.hkv,
                        layer_b = kv_b * 2, slot_b = layer_b * dd.L;
         CacheRef dc{Wk(c, pl.ws_dkv), slot_b, layer_b, kv_b, head_b, pos_b, 0};
@@ -472,7 +506,7 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
             de.xg = Wk(c, pl.ws_xg);
             de.g = (const float*)P(c, dd.L > 0 ? dp.layers[0].g_attn : dp.g_final);
             de.ss_out = (float*)Wk(c, pl.ws_ss_a);
-            e = fd::launch_embed(de, pl.wt, pl.Sp, st);
+            e = timed(c, K_EMBED, st, [&] { return fd::launch_embed(de, pl.wt, pl.Sp, st); });
             int dnss = 1;
             if (e == hipSuccess) e = run_stack(c, dp, dc, k, st, &dnss);
             if (e == hipSuccess) {
@@ -491,7 +525,7 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
                 f.y_off = k * dd.d;
                 f.zf = (float*)Wk(c, pl.ws_z);
                 f.advance = 0;
-                e = fd::launch_final(f, pl.wt, pl.Sp, st);
+                e = timed(c, K_FINAL, st, [&] { return fd::launch_final(f, pl.wt, pl.Sp, st); });
             }
         }
     }
@@ -548,6 +582,39 @@ fd_status fd_kv_layout(fd_ctx* c, fd_kv_view* out) {
     return FD_OK;
 }
 
+fd_status fd_profile(fd_ctx* c, int32_t enable) {
+    if (!c) return FD_E_INVAL;
+    c->prof = enable != 0;
+    return FD_OK;
+}
+
+fd_status fd_profile_read(fd_ctx* c, double* ms_out, int64_t* launches_out, int32_t n) {
+    if (!c || n < 0 || (n > 0 && (!ms_out || !launches_out))) return FD_E_INVAL;
+    hipError_t e = hipSuccess;
+    for (auto& p : c->prof_pending) {
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventSynchronize(p.second.second);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.second.first, p.second.second);
+        if (e == hipSuccess) {
+            c->prof_ms[p.first] += ms;
+            c->prof_n[p.first] += 1;
+        }
+        c->ev_pool.push_back(p.second.first);
+        c->ev_pool.push_back(p.second.second);
+    }
+    c->prof_pending.clear();
+    for (int k = 0; k < n && k < FD_N_KINDS; ++k) {
+        ms_out[k] = c->prof_ms[k];
+        launches_out[k] = c->prof_n[k];
+    }
+    for (int k = 0; k < FD_N_KINDS; ++k) {
+        c->prof_ms[k] = 0.0;
+        c->prof_n[k] = 0;
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "fd_profile_read");
+    return FD_OK;
+}
+
 fd_status fd_sync(fd_ctx* c, void* stream) {
     if (!c) return FD_E_INVAL;
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
@@ -558,6 +625,12 @@ fd_status fd_sync(fd_ctx* c, void* stream) {
 
 fd_status fd_destroy(fd_ctx* c) {
     if (!c) return FD_E_INVAL;
+    for (auto& p : c->prof_pending) {
+        (void)hipEventSynchronize(p.second.second);
+        (void)hipEventDestroy(p.second.first);
+        (void)hipEventDestroy(p.second.second);
+    }
+    for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
     for (int i = 0; i < kRing; ++i) {
         if (c->ev[i]) {
             if (c->ev_used[i]) (void)hipEventSynchronize(c->ev[i]);

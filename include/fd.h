@@ -65,7 +65,7 @@ typedef int32_t fd_status;
  *
  * Supported: w_dtype == act_dtype in {FD_F32, FD_BF16}; kv_dtype in
  * {FD_F32, FD_FP8_E4M3}; head_dim in {64, 128, 256}; n_heads a multiple of
- * n_kv_heads with n_heads / n_kv_heads in {1, 2, 4, 8}; d_model, d_ffn and
+ * n_kv_heads with n_heads / n_kv_heads in {1, 2, 4}; d_model, d_ffn and
  * n_heads*head_dim multiples of 32 (bf16) or 16 (fp32); max_slots in
  * 1..4096; max_context in 1..65536.  An optional depth stack (depth_steps >
  * 0) runs after the main stack on every frame, for depth_steps sequential
@@ -254,6 +254,19 @@ fd_status fd_slot_state(fd_ctx* ctx, int32_t slot, int32_t* active, int32_t* pos
  */
 fd_status fd_kv_write(fd_ctx* ctx, int32_t slot, int32_t layer, int32_t t0, int32_t n,
                       const float* src, void* stream);
+
+/*
+ * Per-kernel timing (bench hook).  With enable != 0, fd_step brackets every
+ * kernel it launches with a pair of HIP events on its stream; fd_profile_read
+ * waits for them and returns, per kernel kind, the summed duration in
+ * milliseconds and the number of launches since the last read (then resets).
+ * Kinds: 0 embed, 1 qkv, 2 attention, 3 o-projection, 4 gate/up, 5 down,
+ * 6 final norm, 7 depth input projection (FD_N_KINDS = 8).  Timing adds a
+ * small gap between launches; headline step times are taken with it off.
+ */
+#define FD_N_KINDS 8
+fd_status fd_profile(fd_ctx* ctx, int32_t enable);
+fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, int32_t n);
 
 /* Waits for the ctx's last enqueued work on `stream` and reports device
  * errors (FD_E_DEVICE) including the kernels' own fault flag. */

@@ -53,14 +53,20 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def round_to_bf16(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even), returned
-    as float32.  This is the storage format of the bf16 workloads' weights
-    and inputs, applied once when the inputs are made."""
+def round_to_bf16(a: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Round finite float32 values to the nearest bfloat16 (ties to even),
+    returned as float32.  This is the storage format of the bf16 workloads'
+    weights and inputs, applied once when the inputs are made."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    u = a.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u  # finite inputs: no 32-bit overflow
+    r &= np.uint32(0xFFFF0000)
+    if out is not None:
+        out.view(np.uint32)[...] = r
+        return out
+    return r.view(np.float32)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -70,7 +76,7 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def _normal_chunked(key: list[int], shape: tuple[int, ...], std: float,
-                    pool: ThreadPoolExecutor | None) -> np.ndarray:
+                    pool: ThreadPoolExecutor | None, bf16: bool = False) -> np.ndarray:
     rows = shape[0]
     cols = int(np.prod(shape[1:])) if len(shape) > 1 else 1
     out = np.empty((rows, cols), dtype=np.float32)
@@ -84,6 +90,8 @@ def _normal_chunked(key: list[int], shape: tuple[int, ...], std: float,
         blk = out[r0:r1]
         g.standard_normal(out=blk, dtype=np.float32)
         blk *= np.float32(std)
+        if bf16:
+            round_to_bf16(blk, out=blk)
 
     items = list(enumerate(starts))
     if pool is None or len(items) == 1:
@@ -100,10 +108,8 @@ def matrix(cfg: dict, layer: int, name: str, *, depth: bool = False,
     (bf16-representable when the config's weights are bf16)."""
     shape = weight_shape(cfg, name, depth=depth)
     lk = layer + (_DEPTH_OFFSET if depth else 0)
-    a = _normal_chunked([SEED_WEIGHTS, lk, _NAME_ID[name]], shape, 0.02, pool)
-    if cfg["w_dtype"] == "bf16":
-        a = round_to_bf16(a)
-    return a
+    return _normal_chunked([SEED_WEIGHTS, lk, _NAME_ID[name]], shape, 0.02, pool,
+                           bf16=cfg["w_dtype"] == "bf16")
 
 
 def gain(cfg: dict, layer: int, name: str, *, depth: bool = False,

@@ -40,3 +40,37 @@ def device_weights(model, device="cuda") -> dict:
                                for l in range(cfg["depth_layers"])]
         out["depth_g_final"] = _f32(model.depth_g_final, device)
     return out
+
+
+def random_device_weights(cfg: dict, seed: int = 0, device="cuda") -> dict:
+    """Weights of the same distributions (matrices ~N(0, 0.02) in the
+    config's weight type, gains 1, FP8 scales as in ``synth.kv_scales``)
+    drawn directly on the GPU from torch's seeded generator.  Used where the
+    values need not equal the host generator's (timing runs)."""
+    from . import kv_scales, weight_shape
+    wdt = torch.bfloat16 if cfg["w_dtype"] == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def mat(name, depth=False):
+        shape = weight_shape(cfg, name, depth=depth)
+        t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return t.mul_(0.02).to(wdt)
+
+    def layer(depth=False):
+        d = cfg["depth_d"] if depth else cfg["d_model"]
+        out = {n: mat(n, depth) for n in LAYER_MATS}
+        out["g_attn"] = torch.ones(d, device=device)
+        out["g_ffn"] = torch.ones(d, device=device)
+        return out
+
+    out = {
+        "layers": [layer() for _ in range(cfg["n_layers"])],
+        "g_final": torch.ones(cfg["d_model"], device=device),
+        "kv_scale": _f32(kv_scales(cfg), device) if cfg["kv_dtype"] == "fp8" else None,
+    }
+    if cfg.get("depth_steps", 0):
+        out["w_in"] = mat("w_in")
+        out["depth_layers"] = [layer(True) for _ in range(cfg["depth_layers"])]
+        out["depth_g_final"] = torch.ones(cfg["depth_d"], device=device)
+    return out

@@ -52,3 +52,9 @@ def rel_err_rows(y, r):
 
 def to_np(t):
     return t.float().cpu().numpy()
+
+
+def check(cond, msg: str) -> None:
+    """Assertion without pytest's expansion of large arrays in the report."""
+    if not bool(cond):
+        raise AssertionError(msg)
