@@ -196,7 +196,6 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         g.S = pl.S;
         g.MT = pl.MT;
         g.part = (float*)Wk(c, pl.ws_part);
-        g.cnt = (int*)Wk(c, pl.ws_cnt);
         g.inv_d = inv_d;
         g.eps = eps;
         g.active = slot_active(c);
@@ -235,7 +234,6 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.S = pl.S; at.hq = d.hq; at.hkv = d.hkv; at.tc = sp.attn.tc; at.n_chunks = sp.attn.n_chunks;
         at.T = d.T;
         at.part = (float*)Wk(c, pl.ws_apart);
-        at.cnt = (int*)Wk(c, pl.ws_acnt);
         at.o_out = Wk(c, pl.ws_o);
         e = timed(c, K_ATTN, st, [&] {
             return fd::launch_attn(at, wt, q.kv_fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
@@ -487,7 +485,6 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
         g.K = pl.win.K; g.KB = pl.win.KB; g.NB = pl.win.NB; g.P = pl.win.P; g.MG = pl.win.MG;
         g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
         g.part = (float*)Wk(c, pl.ws_part);
-        g.cnt = (int*)Wk(c, pl.ws_cnt);
         g.epi = fd::EPI_F32;
         g.y = (float*)Wk(c, pl.ws_c);
         g.ld = dd.d;

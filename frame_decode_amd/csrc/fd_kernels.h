@@ -18,8 +18,7 @@ struct GemmArgs {
     const uint8_t* W;   // packed tiles [NB][KB][64 lanes][16 B]
     const void* X;      // session rows [Sp][K] in the activation type
     int K, KB, NB, P, MG, MT, Sp, S;
-    float* part;        // split-K partial tiles (P > 1)
-    int* cnt;           // split-K arrival counters [n_groups * MG], zero between launches
+    float* part;        // split-K partial tiles (P > 1), summed by the reduce kernel
     int epi;
     // row scaling by the RMS norm of the GEMM input: rstd[m] = (sum_i ss[i][m] / d + eps)^-1/2
     const float* ss_in;
@@ -62,7 +61,6 @@ struct AttnArgs {
     int S, hq, hkv, tc, n_chunks;
     int T;                 // cache positions per slot
     float* part;           // [S][hkv][n_chunks][G][hd + 2]
-    int* cnt;              // [S][hkv] arrival counters, zero between launches
     void* o_out;           // [Sp][hq*hd] activation type
 };
 

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <sstream>
 
 namespace fd {
@@ -55,13 +56,40 @@ fd_status check_stack(const char* name, int L, int d, int hq, int hkv, int hd, i
     return FD_OK;
 }
 
-void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int kv_fp8,
+// Tuning override for measurements: FD_TUNE="qkv.P=4,o.R=1,attn.chunks=2"
+// replaces the chosen split-K factor (P), n-blocks per wave (R) of a
+// projection, or the attention chunk count.  Unset in normal use.
+int tune_value(const char* key, int dflt) {
+    const char* env = std::getenv("FD_TUNE");
+    if (!env) return dflt;
+    std::string s(env), k = std::string(key) + "=";
+    size_t p = 0;
+    while ((p = s.find(k, p)) != std::string::npos) {
+        if (p == 0 || s[p - 1] == ',') return std::atoi(s.c_str() + p + k.size());
+        p += k.size();
+    }
+    return dflt;
+}
+
+GemmShape tuned(GemmShape g, const char* name) {
+    std::string n(name);
+    int R = tune_value((n + ".R").c_str(), g.R);
+    int P = tune_value((n + ".P").c_str(), g.P);
+    if (R == 1 || R == 2) g.R = R;
+    g.P = std::max(1, std::min(P, g.KB));
+    g.n_groups = cdiv(g.NB, kWaves * g.R);
+    g.part_floats = g.P > 1 ? (uint64_t)g.n_groups * g.MG * g.P * kWaves * g.R * g.MTG * 256 : 0;
+    g.counters = g.n_groups * g.MG;
+    return g;
+}
+
+void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8,
                 uint64_t& off) {
     sp.dims = dims;
-    sp.qkv = choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256);
-    sp.o = choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256);
-    sp.gu = choose_gemm(2 * dims.f, dims.d, KT, MT, 256);
-    sp.down = choose_gemm(dims.d, dims.f, KT, MT, 256);
+    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256), "qkv");
+    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256), "o");
+    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256), "gu");
+    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256), "down");
     sp.layers.resize(dims.L);
     auto tiles = [](const GemmShape& g) { return (uint64_t)g.NB * g.KB * kTileBytes; };
     for (int l = 0; l < dims.L; ++l) {
@@ -81,9 +109,16 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int kv_fp8
     sp.rope = off;   off = align_up(off + 4ull * dims.T * dims.hd);
     // attention chunking: lanes per position give each lane 16 bytes (FP8)
     // or 32 bytes (fp32) of a position's head vector
+    // Chunks of the window per (slot, kv head): one workgroup per chunk.
+    // Enough chunks for about four workgroups per CU when the slot x head
+    // count alone is too small; a single chunk needs no merge kernel.
     AttnShape& a = sp.attn;
     a.lpp = kv_fp8 ? dims.hd / 16 : dims.hd / 8;
-    a.tc = kWaves * kAttnIters * (64 / a.lpp);
+    const int round = kWaves * kAttnIters * (64 / a.lpp);
+    const int pairs = std::max(1, S * dims.hkv);
+    int want = std::max(1, cdiv(1024, pairs));
+    want = std::max(1, tune_value("attn.chunks", want));
+    a.tc = cdiv(cdiv(dims.T, want), round) * round;
     a.n_chunks = cdiv(dims.T, a.tc);
 }
 
@@ -148,14 +183,14 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
 
     uint64_t off = 0;
     StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};
-    plan_stack(p.main, md, KT, p.MT, p.kv_fp8, off);
+    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, off);
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
         p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
         p.w_in = off;
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
-        plan_stack(p.dstack, dd, KT, p.MT, 0, off);
+        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, off);
     }
     p.packed_bytes = std::max<uint64_t>(off, kAlign);
 

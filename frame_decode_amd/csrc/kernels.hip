@@ -143,8 +143,9 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 //
 // Workgroup task (n-group, m-group, k-split): 4 waves, wave w owns n-blocks
 // (n-group*4 + w)*R .. +R; all waves share the same k-range so X fragments
-// are re-read from the CU's L1.  With P > 1 the k-splits write partial tiles
-// and the last to arrive sums them in split order (deterministic).
+// are re-read from the CU's L1.  With P > 1 k-splits, every split stores its
+// partial tiles and a second kernel sums them in split order (deterministic)
+// and applies the epilogue; workgroups of one launch never exchange data.
 
 template <int WT>
 struct BFrag;
@@ -168,104 +169,21 @@ __device__ __forceinline__ f32x4 mfma_tile(u32x4 a, typename BFrag<WT>::T b, f32
     }
 }
 
+// Offset (in f32x4 units) of a wave's partial tiles for one k-split.
+template <int R, int MTG>
+__device__ __forceinline__ size_t part_index(int task, int P, int ks, int wave) {
+    return (((size_t)task * P + ks) * 4 + wave) * (R * MTG * 64);
+}
+
+// Epilogue of a finished accumulator set.  acc[r][t] holds rows n =
+// (nbw + r)*16 + 4*(lane/16) + i, column m = (mt0 + t)*16 + lane%16.
 template <int WT, int R, int MTG>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-    typedef typename BFrag<WT>::T BT;
-    constexpr int U = 4;  // k-tiles loaded per batch
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4 (&acc)[R][MTG], int ng,
+                                              int mt0, int mtn, int nbw, bool (&rv)[R]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    int bid = blockIdx.x;
-    const int ks = bid % a.P;
-    bid /= a.P;
-    const int mg = bid % a.MG;
-    const int ng = bid / a.MG;
-    const int kb0 = (int)((long)ks * a.KB / a.P);
-    const int kb1 = (int)((long)(ks + 1) * a.KB / a.P);
-    const int nbw = (ng * 4 + wave) * R;  // first n-block of this wave
-    const int mt0 = mg * MTG;
-    const int mtn = min(MTG, a.MT - mt0);
-
-    f32x4 acc[R][MTG];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < MTG; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    bool rv[R];
-    const u32x4* wp[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        rv[r] = (nbw + r) < a.NB;
-        int nb = rv[r] ? nbw + r : 0;
-        wp[r] = (const u32x4*)(a.W + (size_t)nb * a.KB * 1024) + lane;
-    }
-    // X fragment: row (mt0 + t)*16 + lane%16; each k-tile advances 64 bytes.
-    const int eb = WT ? 2 : 4;
-    const uint8_t* xp = (const uint8_t*)a.X +
-                        ((size_t)(mt0 * 16 + (lane & 15)) * a.K) * eb + (lane >> 4) * 16;
-    const size_t xrow16 = (size_t)16 * a.K * eb;  // bytes between m-tiles
-
-    for (int kb = kb0; kb < kb1; kb += U) {
-        u32x4 av[U][R];
-        BT bv[U][MTG];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kb + u < kb1) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (rv[r]) av[u][r] = wp[r][(size_t)(kb + u) * 64];
-#pragma unroll
-                for (int t = 0; t < MTG; ++t)
-                    if (t < mtn) bv[u][t] = *(const BT*)(xp + t * xrow16 + (size_t)(kb + u) * 64);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kb + u < kb1) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (rv[r]) {
-#pragma unroll
-                        for (int t = 0; t < MTG; ++t)
-                            if (t < mtn) acc[r][t] = mfma_tile<WT>(av[u][r], bv[u][t], acc[r][t]);
-                    }
-            }
-        }
-    }
-
-    __shared__ int s_last;
     __shared__ float s_rstd[MTG * 16];
     __shared__ float s_red[4][MTG * 16];
-
-    if (a.P > 1) {
-        const int task = ng * a.MG + mg;
-        f32x4* pp = (f32x4*)a.part + ((size_t)task * a.P * 4 + wave) * R * MTG * 64 + lane;
-        const size_t split_stride = (size_t)4 * R * MTG * 64;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < MTG; ++t) pp[ks * split_stride + (r * MTG + t) * 64] = acc[r][t];
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int old = atomicAdd(&a.cnt[task], 1);
-            s_last = (old == a.P - 1);
-            if (s_last) a.cnt[task] = 0;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < MTG; ++t) {
-                f32x4 s = pp[(r * MTG + t) * 64];
-                for (int q = 1; q < a.P; ++q) s += pp[q * split_stride + (r * MTG + t) * 64];
-                acc[r][t] = s;
-            }
-    }
-
-    // per-row norm scale
     if (a.ss_in) {
         for (int i = threadIdx.x; i < mtn * 16; i += blockDim.x) {
             const int row = mt0 * 16 + i;
@@ -361,15 +279,124 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
 }
 
+template <int WT, int R, int MTG>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+    typedef typename BFrag<WT>::T BT;
+    constexpr int U = 4;  // k-tiles loaded per batch
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int bid = blockIdx.x;
+    const int ks = bid % a.P;
+    bid /= a.P;
+    const int mg = bid % a.MG;
+    const int ng = bid / a.MG;
+    const int kb0 = (int)((long)ks * a.KB / a.P);
+    const int kb1 = (int)((long)(ks + 1) * a.KB / a.P);
+    const int nbw = (ng * 4 + wave) * R;  // first n-block of this wave
+    const int mt0 = mg * MTG;
+    const int mtn = min(MTG, a.MT - mt0);
+
+    f32x4 acc[R][MTG];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    bool rv[R];
+    const u32x4* wp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        rv[r] = (nbw + r) < a.NB;
+        int nb = rv[r] ? nbw + r : 0;
+        wp[r] = (const u32x4*)(a.W + (size_t)nb * a.KB * 1024) + lane;
+    }
+    // X fragment: row (mt0 + t)*16 + lane%16; each k-tile advances 64 bytes.
+    const int eb = WT ? 2 : 4;
+    const uint8_t* xp = (const uint8_t*)a.X +
+                        ((size_t)(mt0 * 16 + (lane & 15)) * a.K) * eb + (lane >> 4) * 16;
+    const size_t xrow16 = (size_t)16 * a.K * eb;  // bytes between m-tiles
+
+    for (int kb = kb0; kb < kb1; kb += U) {
+        u32x4 av[U][R];
+        BT bv[U][MTG];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kb + u < kb1) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (rv[r]) av[u][r] = wp[r][(size_t)(kb + u) * 64];
+#pragma unroll
+                for (int t = 0; t < MTG; ++t)
+                    if (t < mtn) bv[u][t] = *(const BT*)(xp + t * xrow16 + (size_t)(kb + u) * 64);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kb + u < kb1) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (rv[r]) {
+#pragma unroll
+                        for (int t = 0; t < MTG; ++t)
+                            if (t < mtn) acc[r][t] = mfma_tile<WT>(av[u][r], bv[u][t], acc[r][t]);
+                    }
+            }
+        }
+    }
+
+    if (a.P > 1) {
+        f32x4* pp = (f32x4*)a.part + part_index<R, MTG>(ng * a.MG + mg, a.P, ks, wave) + lane;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) pp[(r * MTG + t) * 64] = acc[r][t];
+        return;
+    }
+    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, mtn, nbw, rv);
+}
+
+// Sums the P k-split partial tiles of each (n-group, m-group) in split order
+// and applies the epilogue; one workgroup per (n-group, m-group).
+template <int WT, int R, int MTG>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int mg = blockIdx.x % a.MG;
+    const int ng = blockIdx.x / a.MG;
+    const int nbw = (ng * 4 + wave) * R;
+    const int mt0 = mg * MTG;
+    const int mtn = min(MTG, a.MT - mt0);
+    bool rv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rv[r] = (nbw + r) < a.NB;
+    f32x4 acc[R][MTG];
+    const f32x4* pp = (const f32x4*)a.part + part_index<R, MTG>(ng * a.MG + mg, a.P, 0, wave) + lane;
+    const size_t split = (size_t)4 * R * MTG * 64;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) {
+            f32x4 s = pp[(r * MTG + t) * 64];
+            for (int q = 1; q < a.P; ++q) s += pp[q * split + (r * MTG + t) * 64];
+            acc[r][t] = s;
+        }
+    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, mtn, nbw, rv);
+}
+
 // ---------------------------------------------------------------------------
 // decode attention over one (slot, kv head, chunk of positions).
 //
 // Lanes: a position's head vector is spread over LPP consecutive lanes,
 // each holding E elements (16 B of FP8 or 32 B of fp32) in 16-byte pieces
 // c + LPP*j, so one wave load covers 64/LPP whole positions contiguously.
-// Pass 1 streams keys and forms scores (reduced over the LPP lanes), then
-// the workgroup max, exponentials (base 2, log2(e) folded into q), and pass
-// 2 streams values.  All G query heads of the kv head share each load.
+// The 4 waves walk the chunk in interleaved blocks of NIT*64/LPP positions;
+// per block a wave streams keys, forms scores (reduced over the LPP lanes),
+// rescales its running (max, sum, weighted values) and streams values
+// (online softmax, base 2 with log2(e) folded into q).  The waves merge in
+// LDS.  A chunk covering the whole window writes the output; otherwise the
+// chunk's (max, sum, values) go to a partial buffer merged by
+// attn_combine_kernel in chunk order.  All G query heads of the kv head
+// share every load.
 
 template <int FP8>
 __device__ __forceinline__ void unpack16(const u32x4& raw, float* out) {
@@ -401,6 +428,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     constexpr int J = E / VE;          // pieces per lane
     constexpr int PPL = 64 / LPP;      // positions per wave load
     constexpr int NIT = 8;
+    constexpr int SUB = NIT * PPL;     // positions per wave block
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int c = lane % LPP;
@@ -441,99 +469,89 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
                 qv[h][j * VE + i + 3] = v[3];
             }
 
-    const uint8_t* kb = a.arena + (size_t)s * a.slot_stride + (size_t)g * a.head_stride;
-    const uint8_t* vb = kb + a.kv_stride;
-    const int tw = t0 + wave * NIT * PPL + jj;  // this lane's first position
+    const uint8_t* kbase = a.arena + (size_t)s * a.slot_stride + (size_t)g * a.head_stride;
+    const uint8_t* vbase = kbase + a.kv_stride;
 
-    float sc[NIT][G];
-    u32x4 raw[NIT][J];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int t = tw + it * PPL;
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            raw[it][j] = t < t1 ? *(const u32x4*)(kb + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
-                                : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        float kvf[E];
-#pragma unroll
-        for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], kvf + j * VE);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float dsum = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) dsum += qv[h][e] * kvf[e];
-            dsum = warp_sum_xor<LPP>(dsum);
-            sc[it][h] = (tw + it * PPL) < t1 ? dsum : -INFINITY;
-        }
-    }
-
-    __shared__ float s_m[4][G];
-    __shared__ float s_l[4][G];
-    __shared__ float s_acc[4][G][D];
-    __shared__ int s_last;
-
-    float mx[G];
+    float mrun[G], lrun[G], acc[G][E];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float m = sc[0][h];
-#pragma unroll
-        for (int it = 1; it < NIT; ++it) m = fmaxf(m, sc[it][h]);
-#pragma unroll
-        for (int o = LPP; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-        mx[h] = m;
-    }
-    if (lane == 0)
-#pragma unroll
-        for (int h = 0; h < G; ++h) s_m[wave][h] = mx[h];
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        mx[h] = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
-
-    // values: issue this lane's loads, then exponentials while they fly
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int t = tw + it * PPL;
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            raw[it][j] = t < t1 ? *(const u32x4*)(vb + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
-                                : u32x4{0u, 0u, 0u, 0u};
-    }
-    float lsum[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float l = 0.f;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const float e = (tw + it * PPL) < t1 ? __builtin_amdgcn_exp2f(sc[it][h] - mx[h]) : 0.f;
-            sc[it][h] = e;
-            l += e;
-        }
-        lsum[h] = l;
-    }
-    float acc[G][E];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
+        mrun[h] = -INFINITY;
+        lrun[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+
+    for (int base = t0 + wave * SUB; base < t1; base += 4 * SUB) {
+        const int tw = base + jj;  // this lane's first position in the block
+        float sc[NIT][G];
+        u32x4 raw[NIT][J];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        float vf[E];
+        for (int it = 0; it < NIT; ++it) {
+            const int t = tw + it * PPL;
 #pragma unroll
-        for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], vf + j * VE);
+            for (int j = 0; j < J; ++j)
+                raw[it][j] = t < t1 ? *(const u32x4*)(kbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
+                                    : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int it = 0; it < NIT; ++it) {
+            float kvf[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[h][e] += sc[it][h] * vf[e];
+            for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], kvf + j * VE);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float dsum = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) dsum += qv[h][e] * kvf[e];
+                dsum = warp_sum_xor<LPP>(dsum);
+                sc[it][h] = (tw + it * PPL) < t1 ? dsum : -INFINITY;
+            }
+        }
+        // values of this block: issue the loads before the softmax update
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int t = tw + it * PPL;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                raw[it][j] = t < t1 ? *(const u32x4*)(vbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
+                                    : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float m = sc[0][h];
+#pragma unroll
+            for (int it = 1; it < NIT; ++it) m = fmaxf(m, sc[it][h]);
+#pragma unroll
+            for (int o = LPP; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+            const float mnew = fmaxf(mrun[h], m);  // finite: position `base` is valid
+            const float sold = __builtin_amdgcn_exp2f(mrun[h] - mnew);
+            mrun[h] = mnew;
+            lrun[h] *= sold;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] *= sold;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const float w = (tw + it * PPL) < t1 ? __builtin_amdgcn_exp2f(sc[it][h] - mnew) : 0.f;
+                sc[it][h] = w;
+                lrun[h] += w;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            float vf[E];
+#pragma unroll
+            for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], vf + j * VE);
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] += sc[it][h] * vf[e];
+        }
     }
     // reduce over the wave's position groups (lanes with equal c)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int o = LPP; o < 64; o <<= 1) lsum[h] += __shfl_xor(lsum[h], o);
+        for (int o = LPP; o < 64; o <<= 1) lrun[h] += __shfl_xor(lrun[h], o);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             float v = acc[h][e];
@@ -542,6 +560,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             acc[h][e] = v;
         }
     }
+
+    __shared__ float s_m[4][G];
+    __shared__ float s_l[4][G];
+    __shared__ float s_acc[4][G][D];
     if (jj == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -549,57 +571,61 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             for (int j = 0; j < J; ++j)
 #pragma unroll
                 for (int i = 0; i < VE; ++i) s_acc[wave][h][(c + LPP * j) * VE + i] = acc[h][j * VE + i];
-            if (c == 0) s_l[wave][h] = lsum[h];
+            if (c == 0) {
+                s_l[wave][h] = lrun[h];
+                s_m[wave][h] = mrun[h];
+            }
         }
     }
     __syncthreads();
 
     const float* vs = a.vscale;
-    if (nch == 1) {
-        for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-            const int h = i / D, d = i - h * D;
-            const float o = ((s_acc[0][h][d] + s_acc[1][h][d]) + s_acc[2][h][d]) + s_acc[3][h][d];
-            const float l = ((s_l[0][h] + s_l[1][h]) + s_l[2][h]) + s_l[3][h];
-            store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, o / l * vs[g]);
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+        const int h = i / D, d = i - h * D;
+        const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+        float O = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);  // 0 for a wave without positions
+            O += f * s_acc[w][h][d];
+            L += f * s_l[w][h];
         }
-        return;
+        if (nch == 1) {
+            store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, O / L * vs[g]);
+        } else {
+            float* part = a.part + (((size_t)(s * a.hkv + g) * a.n_chunks + chunk) * G + h) * (D + 2);
+            part[d] = O;
+            if (d == 0) {
+                part[D] = M;
+                part[D + 1] = L;
+            }
+        }
     }
-    // several chunks: store this chunk's (max, sum, weighted values); the
-    // last chunk to finish merges all of them in chunk order
-    float* part = a.part + ((size_t)(s * a.hkv + g) * a.n_chunks) * G * (D + 2);
-    const size_t cstride = (size_t)G * (D + 2);
+}
+
+// Merges the chunks of every (slot, query head) in chunk order.
+template <int WT, int D, int G>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+    const int g = blockIdx.x % a.hkv;
+    const int s = blockIdx.x / a.hkv;
+    if (s >= a.S || !a.active[s]) return;  // inactive rows were zeroed by the attention kernel
+    const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
+    const int nch = (p + 1 + a.tc - 1) / a.tc;
+    if (nch == 1) return;  // written directly
+    const int hqd = a.hq * D;
     for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
         const int h = i / D, d = i - h * D;
-        part[chunk * cstride + h * (D + 2) + d] =
-            ((s_acc[0][h][d] + s_acc[1][h][d]) + s_acc[2][h][d]) + s_acc[3][h][d];
-    }
-    if (threadIdx.x < G) {
-        const int h = threadIdx.x;
-        part[chunk * cstride + h * (D + 2) + D] = mx[h];
-        part[chunk * cstride + h * (D + 2) + D + 1] = ((s_l[0][h] + s_l[1][h]) + s_l[2][h]) + s_l[3][h];
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int* cp = a.cnt + s * a.hkv + g;
-        int old = atomicAdd(cp, 1);
-        s_last = (old == nch - 1);
-        if (s_last) *cp = 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-        const int h = i / D, d = i - h * D;
+        const float* part = a.part + ((size_t)(s * a.hkv + g) * a.n_chunks * G + h) * (D + 2);
+        const size_t cs = (size_t)G * (D + 2);
         float M = -INFINITY;
-        for (int q = 0; q < nch; ++q) M = fmaxf(M, part[q * cstride + h * (D + 2) + D]);
+        for (int q = 0; q < nch; ++q) M = fmaxf(M, part[q * cs + D]);
         float L = 0.f, O = 0.f;
         for (int q = 0; q < nch; ++q) {
-            const float w = __builtin_amdgcn_exp2f(part[q * cstride + h * (D + 2) + D] - M);
-            L += w * part[q * cstride + h * (D + 2) + D + 1];
-            O += w * part[q * cstride + h * (D + 2) + d];
+            const float w = __builtin_amdgcn_exp2f(part[q * cs + D] - M);
+            L += w * part[q * cs + D + 1];
+            O += w * part[q * cs + d];
         }
-        store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, O / L * vs[g]);
+        store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, O / L * a.vscale[g]);
     }
 }
 
@@ -698,8 +724,13 @@ hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
 
 template <int WT, int R>
 static hipError_t gemm_mtg(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    const int red = grid / a.P;
     switch (MTG) {
-#define FD_G(MT) case MT: hipLaunchKernelGGL((gemm_kernel<WT, R, MT>), dim3(grid), dim3(256), 0, st, a); break;
+#define FD_G(MT)                                                                                  \
+    case MT:                                                                                      \
+        hipLaunchKernelGGL((gemm_kernel<WT, R, MT>), dim3(grid), dim3(256), 0, st, a);            \
+        if (a.P > 1) hipLaunchKernelGGL((gemm_reduce_kernel<WT, R, MT>), dim3(red), dim3(256), 0, st, a); \
+        break;
         FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5) FD_G(6) FD_G(7) FD_G(8)
 #undef FD_G
         default: return hipErrorInvalidValue;
@@ -714,10 +745,16 @@ hipError_t launch_gemm(const GemmArgs& a, int wt, int R, int MTG, int grid, hipS
 
 template <int WT, int FP8, int D>
 static hipError_t attn_g(const AttnArgs& a, int G, int grid, hipStream_t st) {
+    const int cgrid = a.S * a.hkv;
     switch (G) {
-        case 1: hipLaunchKernelGGL((attn_kernel<WT, FP8, D, 1>), dim3(grid), dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_kernel<WT, FP8, D, 2>), dim3(grid), dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((attn_kernel<WT, FP8, D, 4>), dim3(grid), dim3(256), 0, st, a); break;
+#define FD_A(GG)                                                                                       \
+    case GG:                                                                                           \
+        hipLaunchKernelGGL((attn_kernel<WT, FP8, D, GG>), dim3(grid), dim3(256), 0, st, a);            \
+        if (a.n_chunks > 1)                                                                            \
+            hipLaunchKernelGGL((attn_combine_kernel<WT, D, GG>), dim3(cgrid), dim3(256), 0, st, a);    \
+        break;
+        FD_A(1) FD_A(2) FD_A(4)
+#undef FD_A
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
