@@ -198,6 +198,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         g.part = (float*)Wk(c, pl.ws_part);
         g.inv_d = inv_d;
         g.eps = eps;
+        g.ss_stride = pl.nss_max;
         g.active = slot_active(c);
         g.pos = slot_pos(c);
         g.pos_override = pos_override;
@@ -233,6 +234,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.pos_override = pos_override;
         at.S = pl.S; at.hq = d.hq; at.hkv = d.hkv; at.tc = sp.attn.tc; at.n_chunks = sp.attn.n_chunks;
         at.T = d.T;
+        at.MT = pl.MT;
         at.part = (float*)Wk(c, pl.ws_apart);
         at.o_out = Wk(c, pl.ws_o);
         e = timed(c, K_ATTN, st, [&] {
@@ -448,10 +450,12 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
     em.active = slot_active(c);
     em.S = pl.S;
     em.d = md.d;
+    em.MT = pl.MT;
     em.x = (float*)Wk(c, pl.ws_x);
     em.xg = Wk(c, pl.ws_xg);
     em.g = (const float*)P(c, md.L > 0 ? mp.layers[0].g_attn : mp.g_final);
     em.ss_out = (float*)Wk(c, pl.ws_ss_a);
+    em.ss_stride = pl.nss_max;
     e = timed(c, K_EMBED, st, [&] { return fd::launch_embed(em, pl.wt, pl.Sp, st); });
     int nss = 1;
     CacheRef mc{(uint8_t*)c->buf.kv_arena, pl.kv_slot_stride, pl.kv_layer_stride, pl.kv_kv_stride,
@@ -462,12 +466,14 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
         f.x = (const float*)Wk(c, pl.ws_x);
         f.ss = (const float*)Wk(c, pl.ws_ss_a);
         f.nss = nss;
+        f.ss_stride = pl.nss_max;
         f.inv_d = 1.0f / (float)md.d;
         f.eps = pl.cfg.rms_eps;
         f.g = (const float*)P(c, mp.g_final);
         f.active = slot_active(c);
         f.S = pl.S;
         f.d = md.d;
+        f.MT = pl.MT;
         f.y_out = y_out;
         f.ldy = md.d;
         f.y_off = 0;
@@ -499,10 +505,12 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
             de.active = slot_active(c);
             de.S = pl.S;
             de.d = dd.d;
+            de.MT = pl.MT;
             de.x = (float*)Wk(c, pl.ws_x);
             de.xg = Wk(c, pl.ws_xg);
             de.g = (const float*)P(c, dd.L > 0 ? dp.layers[0].g_attn : dp.g_final);
             de.ss_out = (float*)Wk(c, pl.ws_ss_a);
+            de.ss_stride = pl.nss_max;
             e = timed(c, K_EMBED, st, [&] { return fd::launch_embed(de, pl.wt, pl.Sp, st); });
             int dnss = 1;
             if (e == hipSuccess) e = run_stack(c, dp, dc, k, st, &dnss);
@@ -511,12 +519,14 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
                 f.x = (const float*)Wk(c, pl.ws_x);
                 f.ss = (const float*)Wk(c, pl.ws_ss_a);
                 f.nss = dnss;
+                f.ss_stride = pl.nss_max;
                 f.inv_d = 1.0f / (float)dd.d;
                 f.eps = pl.cfg.rms_eps;
                 f.g = (const float*)P(c, dp.g_final);
                 f.active = slot_active(c);
                 f.S = pl.S;
                 f.d = dd.d;
+                f.MT = pl.MT;
                 f.y_out = depth_out;
                 f.ldy = dd.T * dd.d;
                 f.y_off = k * dd.d;

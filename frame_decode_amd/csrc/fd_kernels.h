@@ -16,13 +16,13 @@ enum Epilogue : int {
 
 struct GemmArgs {
     const uint8_t* W;   // packed tiles [NB][KB][64 lanes][16 B]
-    const void* X;      // session rows [Sp][K] in the activation type
+    const void* X;      // session rows [Sp][K], activation type, fragment-packed layout
     int K, KB, NB, P, MG, MT, Sp, S;
     float* part;        // split-K partial tiles (P > 1), summed by the reduce kernel
     int epi;
     // row scaling by the RMS norm of the GEMM input: rstd[m] = (sum_i ss[i][m] / d + eps)^-1/2
-    const float* ss_in;
-    int nss;
+    const float* ss_in;    // [Sp][ss_stride] partial sums of x^2 of the GEMM input rows
+    int nss, ss_stride;
     float inv_d, eps;
     // EPI_QKV
     float* q_out;          // [Sp][hq*hd] fp32
@@ -41,7 +41,7 @@ struct GemmArgs {
     float* x;              // [Sp][ld] residual stream
     void* xg;              // [Sp][ld] act(x * g_next)
     const float* g_next;
-    float* ss_out;         // [n_groups][Sp]
+    float* ss_out;         // [Sp][ss_stride], entry n-group
     int ld;
     // EPI_GU
     void* h_out;           // [Sp][F]
@@ -59,7 +59,8 @@ struct AttnArgs {
     const int* pos;
     int pos_override;
     int S, hq, hkv, tc, n_chunks;
-    int T;                 // cache positions per slot
+    int T;
+    int MT;                // 16-row tiles of session rows (packed output layout)                 // cache positions per slot
     float* part;           // [S][hkv][n_chunks][G][hd + 2]
     void* o_out;           // [Sp][hq*hd] activation type
 };
@@ -69,21 +70,22 @@ struct EmbedArgs {
     const float* c;        // depth input projection [Sp][d] fp32 (when x_in is null)
     const float* z;        // previous depth output [Sp][d] fp32 or null (= 0)
     const int* active;
-    int S, d;
+    int S, d, MT;
     float* x;              // [Sp][d]
     void* xg;              // [Sp][d]
     const float* g;        // gain of the first norm
-    float* ss_out;         // [1][Sp]
+    float* ss_out;         // [Sp][ss_stride], entry 0
+    int ss_stride;
 };
 
 struct FinalArgs {
     const float* x;
-    const float* ss;
-    int nss;
+    const float* ss;       // [Sp][ss_stride]
+    int nss, ss_stride;
     float inv_d, eps;
     const float* g;
     const int* active;
-    int S, d;
+    int S, d, MT;
     void* y_out;           // caller rows, element (m, i) at y_out[m * ldy + y_off + i]; may be null
     int ldy, y_off;
     void* yw;              // [Sp][d] activation-type copy, or null
@@ -107,6 +109,10 @@ struct KvWriteArgs {
     const float* kvsig;    // [2][hkv]
     int hkv, hd, t0, n, kv_fp8;
 };
+
+// k-tiles per GEMM main-loop chunk for a given m-group height (every
+// k-split covers a whole number of chunks).
+inline int gemm_chunk(int MTG) { return MTG <= 5 ? 8 : 4; }
 
 // Launchers (enqueue on `st`; return the launch error).
 hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st);

@@ -8,6 +8,8 @@
 
 namespace fd {
 
+int gemm_chunk_tiles(int MTG) { return MTG <= 5 ? 8 : 4; }
+
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
     GemmShape g;
     g.N = N;
@@ -17,17 +19,20 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
     g.KB = K / KT;
     g.MG = cdiv(MT, kMaxMTG);
     g.MTG = cdiv(MT, g.MG);
-    // Two n-blocks per wave when the projection is wide enough to still give
-    // every CU work: this halves the re-reads of the session rows X.
-    g.R = (g.NB >= kWaves * 2 * 64) ? 2 : 1;
+    // One n-block per wave: the session rows X are shared through LDS by
+    // the four waves, so wider waves buy little and cost occupancy.
+    g.R = 1;
     g.n_groups = cdiv(g.NB, kWaves * g.R);
     int base = g.n_groups * g.MG;
-    // Split K until there are about two workgroups per CU, keeping at
-    // least 8 tiles of K per split.
-    int p = (2 * n_cu + base - 1) / base;
-    p = std::min(p, std::max(1, g.KB / 8));
-    p = std::min(p, 16);
-    g.P = std::max(1, p);
+    // Split K until there are about two workgroups per CU; every split
+    // covers a whole number of main-loop chunks (P divides KB / chunk).
+    const int chunks = g.KB / gemm_chunk_tiles(g.MTG);
+    int want = (2 * n_cu + base - 1) / base;
+    want = std::min(want, std::max(1, chunks / 2));
+    int p = 1;
+    for (int d = 1; d <= chunks && d <= 16; ++d)
+        if (chunks % d == 0 && d <= want) p = d;
+    g.P = p;
     g.part_floats = g.P > 1 ? (uint64_t)g.n_groups * g.MG * g.P * kWaves * g.R * g.MTG * 256 : 0;
     g.counters = g.n_groups * g.MG;
     return g;
@@ -41,14 +46,15 @@ fd_status check_stack(const char* name, int L, int d, int hq, int hkv, int hd, i
                       std::string* err) {
     std::ostringstream m;
     if (L < 0 || L > 1024) m << name << ": n_layers " << L << " outside 0..1024";
-    else if (d <= 0 || d % KT) m << name << ": d_model " << d << " must be a positive multiple of " << KT;
+    else if (d <= 0 || d % (8 * KT)) m << name << ": d_model " << d << " must be a positive multiple of " << 8 * KT;
     else if (d > 65536) m << name << ": d_model too large";
     else if (hq <= 0 || hkv <= 0 || hq % hkv) m << name << ": n_heads must be a positive multiple of n_kv_heads";
     else if (!(hq / hkv == 1 || hq / hkv == 2 || hq / hkv == 4))
         m << name << ": n_heads / n_kv_heads must be 1, 2 or 4";
     else if (!valid_hd(hd)) m << name << ": head_dim must be 64, 128 or 256";
-    else if ((hq * hd) % KT) m << name << ": n_heads*head_dim must be a multiple of " << KT;
-    else if (f <= 0 || f % KT || f > 262144) m << name << ": d_ffn must be a positive multiple of " << KT;
+    else if ((hq * hd) % (8 * KT)) m << name << ": n_heads*head_dim must be a multiple of " << 8 * KT;
+    else if (f <= 0 || f % (8 * KT) || f > 262144)
+        m << name << ": d_ffn must be a positive multiple of " << 8 * KT;
     if (!m.str().empty()) {
         *err = m.str();
         return FD_E_UNSUPPORTED;
@@ -76,7 +82,7 @@ GemmShape tuned(GemmShape g, const char* name) {
     int R = tune_value((n + ".R").c_str(), g.R);
     int P = tune_value((n + ".P").c_str(), g.P);
     if (R == 1 || R == 2) g.R = R;
-    g.P = std::max(1, std::min(P, g.KB));
+    if (P >= 1 && (g.KB / gemm_chunk_tiles(g.MTG)) % P == 0) g.P = P;
     g.n_groups = cdiv(g.NB, kWaves * g.R);
     g.part_floats = g.P > 1 ? (uint64_t)g.n_groups * g.MG * g.P * kWaves * g.R * g.MTG * 256 : 0;
     g.counters = g.n_groups * g.MG;
@@ -178,8 +184,14 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         if (st != FD_OK) return st;
     }
     p.S = c.max_slots;
-    p.Sp = align_up(c.max_slots, 16);
-    p.MT = p.Sp / 16;
+    // session rows padded to whole m-groups (at most kMaxMTG 16-row tiles
+    // each) so the GEMM main loop needs no row checks
+    {
+        const int mt = cdiv(c.max_slots, 16);
+        const int mg = cdiv(mt, kMaxMTG);
+        p.MT = mg * cdiv(mt, mg);
+        p.Sp = p.MT * 16;
+    }
 
     uint64_t off = 0;
     StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};

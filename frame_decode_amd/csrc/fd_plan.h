@@ -103,6 +103,10 @@ struct Plan {
 // a message in *err.
 fd_status make_plan(const fd_config& cfg, Plan* out, std::string* err);
 
+// k-tiles per GEMM main-loop chunk for an m-group of MTG 16-row tiles (the
+// kernels' own choice, mirrored here so k-splits cover whole chunks).
+int gemm_chunk_tiles(int MTG);
+
 // Tile choice for one projection (exposed for tests).
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu);
 

@@ -103,6 +103,19 @@ __device__ __forceinline__ float load_act1(const void* p, size_t idx) {
     return ((const float*)p)[idx];
 }
 
+// Element index of activation (row m, column k) in the fragment-packed
+// layout [k-tile][m-tile][64 lanes][VE] used for every GEMM input: a k-tile
+// is 32 (bf16) or 16 (fp32) columns, VE = 8 (bf16) or 4 (fp32) elements per
+// lane, lane = m%16 + 16*((k % k-tile) / VE).  One MFMA B fragment (16 rows
+// x one k-tile) is then a contiguous 1 KiB.
+template <int WT>
+__device__ __forceinline__ size_t xoff(int m, int k, int MT) {
+    constexpr int VE = WT ? 8 : 4;
+    constexpr int KT = WT ? 32 : 16;
+    return (((size_t)(k / KT) * MT + (m >> 4)) * 64 + (m & 15) + 16 * ((k % KT) / VE)) * VE +
+           (k % VE);
+}
+
 // ---------------------------------------------------------------------------
 // weight packing: [N][K] row-major -> tiles [NB][KB][64 lanes][16 B].
 // bf16 tile = 16 rows x 32 k; lane l holds row l%16, k 8*(l/16) .. +8.
@@ -175,23 +188,48 @@ __device__ __forceinline__ size_t part_index(int task, int P, int ks, int wave) 
     return (((size_t)task * P + ks) * 4 + wave) * (R * MTG * 64);
 }
 
+// Row scales of the RMS norm from the partial sums of x^2 that the
+// producing kernel wrote as ss[row * ss_stride + j], j < nss.  Phase 1 (all
+// threads): every (row, segment) pair of 8 segments per row sums its share
+// with independent loads into s_seg; phase 2, after a __syncthreads: thread r
+// adds the 8 segments in order and stores (sum / d + eps)^-1/2 in s_rstd[r].
+__device__ __forceinline__ void rstd_phase1(const GemmArgs& a, int row0, int rows, float* s_seg) {
+    const int L = (a.nss + 7) / 8;
+    for (int pr = threadIdx.x; pr < rows * 8; pr += blockDim.x) {
+        const int r = pr >> 3, sg = pr & 7;
+        const float* src = a.ss_in + (size_t)(row0 + r) * a.ss_stride;
+        const int j0 = sg * L, j1 = min(j0 + L, a.nss);
+        float acc = 0.f;
+        for (int jb = j0; jb < j1; jb += 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = (jb + i < j1) ? src[jb + i] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc += v[i];
+        }
+        s_seg[pr] = acc;
+    }
+}
+
+__device__ __forceinline__ void rstd_phase2(const GemmArgs& a, int rows, const float* s_seg,
+                                            float* s_rstd) {
+    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+        float t = 0.f;
+#pragma unroll
+        for (int sg = 0; sg < 8; ++sg) t += s_seg[r * 8 + sg];
+        s_rstd[r] = 1.0f / sqrtf(t * a.inv_d + a.eps);
+    }
+}
+
 // Epilogue of a finished accumulator set.  acc[r][t] holds rows n =
 // (nbw + r)*16 + 4*(lane/16) + i, column m = (mt0 + t)*16 + lane%16.
 template <int WT, int R, int MTG>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4 (&acc)[R][MTG], int ng,
-                                              int mt0, int mtn, int nbw, bool (&rv)[R]) {
+                                              int mt0, int mtn, int nbw, bool (&rv)[R],
+                                              const float* s_rstd) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    __shared__ float s_rstd[MTG * 16];
     __shared__ float s_red[4][MTG * 16];
-    if (a.ss_in) {
-        for (int i = threadIdx.x; i < mtn * 16; i += blockDim.x) {
-            const int row = mt0 * 16 + i;
-            float s = 0.f;
-            for (int j = 0; j < a.nss; ++j) s += a.ss_in[(size_t)j * a.Sp + row];
-            s_rstd[i] = 1.0f / sqrtf(s * a.inv_d + a.eps);
-        }
-    }
     __syncthreads();
 
     float ssum[MTG];
@@ -245,16 +283,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4 (&acc)[R]
                 f32x4 xn = *(f32x4*)xr + v;
                 *(f32x4*)xr = xn;
                 const f32x4 g = *(const f32x4*)(a.g_next + n);
-                store_act4<WT>(a.xg, (size_t)m * a.ld + n, xn * g);
+                store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * g);
                 ssum[t] += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
             } else if (a.epi == EPI_GU) {
                 const int j = n >> 1;  // rows interleave gate_j, up_j, gate_j+1, up_j+1
                 const float h0 = v[0] / (1.0f + expf(-v[0])) * v[1];
                 const float h1 = v[2] / (1.0f + expf(-v[2])) * v[3];
                 if (WT) {
-                    *(uint32_t*)((uint16_t*)a.h_out + (size_t)m * a.F + j) = f2bf(h0) | (f2bf(h1) << 16);
+                    *(uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, j, a.MT)) = f2bf(h0) | (f2bf(h1) << 16);
                 } else {
-                    *(f32x2*)((float*)a.h_out + (size_t)m * a.F + j) = f32x2{h0, h1};
+                    *(f32x2*)((float*)a.h_out + xoff<WT>(m, j, a.MT)) = f32x2{h0, h1};
                 }
             } else {
                 *(f32x4*)(a.y + (size_t)m * a.ld + n) = v;
@@ -274,15 +312,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4 (&acc)[R]
         __syncthreads();
         for (int i = threadIdx.x; i < mtn * 16; i += blockDim.x) {
             const float s = ((s_red[0][i] + s_red[1][i]) + s_red[2][i]) + s_red[3][i];
-            a.ss_out[(size_t)ng * a.Sp + mt0 * 16 + i] = s;
+            a.ss_out[(size_t)(mt0 * 16 + i) * a.ss_stride + ng] = s;
         }
     }
 }
 
-template <int WT, int R, int MTG>
+// Main loop: the k-range is walked in chunks of CK k-tiles.  The session
+// fragments of a chunk (CK x MTG tiles, 1 KiB each) are staged once per
+// workgroup into a double-buffered LDS ring and read back with ds_read by
+// all four waves; each wave keeps its own weight tiles in registers, one
+// whole chunk ahead of the MFMAs, so the vector-memory queue holds weight
+// streams only.
+template <int WT, int R, int MTG, int CK>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     typedef typename BFrag<WT>::T BT;
-    constexpr int U = 4;  // k-tiles loaded per batch
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     int bid = blockIdx.x;
@@ -290,11 +333,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     bid /= a.P;
     const int mg = bid % a.MG;
     const int ng = bid / a.MG;
-    const int kb0 = (int)((long)ks * a.KB / a.P);
-    const int kb1 = (int)((long)(ks + 1) * a.KB / a.P);
+    const int kpb = a.KB / a.P;           // k-tiles per split (a multiple of CK)
+    const int kb0 = ks * kpb;
+    const int nch = kpb / CK;
     const int nbw = (ng * 4 + wave) * R;  // first n-block of this wave
-    const int mt0 = mg * MTG;
-    const int mtn = min(MTG, a.MT - mt0);
+    const int mt0 = mg * MTG;             // session rows are padded to whole m-groups
+
+    __shared__ u32x4 xs[2][CK * MTG * 64];
 
     f32x4 acc[R][MTG];
 #pragma unroll
@@ -307,42 +352,80 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         rv[r] = (nbw + r) < a.NB;
-        int nb = rv[r] ? nbw + r : 0;
+        const int nb = min(nbw + r, a.NB - 1);  // out-of-range blocks re-read a valid one
         wp[r] = (const u32x4*)(a.W + (size_t)nb * a.KB * 1024) + lane;
     }
-    // X fragment: row (mt0 + t)*16 + lane%16; each k-tile advances 64 bytes.
-    const int eb = WT ? 2 : 4;
-    const uint8_t* xp = (const uint8_t*)a.X +
-                        ((size_t)(mt0 * 16 + (lane & 15)) * a.K) * eb + (lane >> 4) * 16;
-    const size_t xrow16 = (size_t)16 * a.K * eb;  // bytes between m-tiles
+    // chunk of X: for each of its CK k-tiles, the MTG fragments of this
+    // m-group are contiguous (MTG KiB); thread i moves 16 B pieces i, i+256, ...
+    const u32x4* xg = (const u32x4*)a.X;
+    constexpr int XQ = CK * MTG / 4;  // 16-byte pieces per thread per chunk
+    auto load_x = [&](u32x4 (&v)[XQ], int kb) {
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int idx = threadIdx.x + q * 256;  // < CK * MTG * 64
+            const int kk = idx / (MTG * 64);
+            const int rem = idx - kk * (MTG * 64);
+            v[q] = xg[((size_t)(kb + kk) * a.MT + mt0) * 64 + rem];
+        }
+    };
+    auto store_x = [&](const u32x4 (&v)[XQ], int buf) {
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) xs[buf][threadIdx.x + q * 256] = v[q];
+    };
+    auto load_a = [&](u32x4 (&A)[CK][R], int kb) {
+#pragma unroll
+        for (int i = 0; i < CK; ++i)
+#pragma unroll
+            for (int r = 0; r < R; ++r) A[i][r] = __builtin_nontemporal_load(&wp[r][(size_t)(kb + i) * 64]);
+    };
+    auto compute = [&](const u32x4 (&A)[CK][R], int buf) {
+#pragma unroll
+        for (int i = 0; i < CK; ++i) {
+            BT b[MTG];
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) b[t] = __builtin_bit_cast(BT, xs[buf][(i * MTG + t) * 64 + lane]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(A[i][r], b[t], acc[r][t]);
+        }
+    };
 
-    for (int kb = kb0; kb < kb1; kb += U) {
-        u32x4 av[U][R];
-        BT bv[U][MTG];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kb + u < kb1) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (rv[r]) av[u][r] = wp[r][(size_t)(kb + u) * 64];
-#pragma unroll
-                for (int t = 0; t < MTG; ++t)
-                    if (t < mtn) bv[u][t] = *(const BT*)(xp + t * xrow16 + (size_t)(kb + u) * 64);
-            }
+    __shared__ float s_seg[MTG * 16 * 8];
+    __shared__ float s_rstd[MTG * 16];
+    const bool norm_here = a.ss_in && a.P == 1;
+
+    u32x4 A0[CK][R], A1[CK][R];
+    u32x4 xr[XQ];
+    load_x(xr, kb0);
+    load_a(A0, kb0);
+    // the norm's partial sums load while the first weight chunk is in flight
+    if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
+    store_x(xr, 0);
+    __syncthreads();
+    if (norm_here) rstd_phase2(a, MTG * 16, s_seg, s_rstd);
+    int c = 0;
+    for (; c + 2 <= nch; c += 2) {
+        const int kb = kb0 + c * CK;
+        load_a(A1, kb + CK);
+        load_x(xr, kb + CK);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        store_x(xr, 1);
+        __syncthreads();
+        const bool more = c + 2 < nch;
+        if (more) {
+            load_a(A0, kb + 2 * CK);
+            load_x(xr, kb + 2 * CK);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kb + u < kb1) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (rv[r]) {
-#pragma unroll
-                        for (int t = 0; t < MTG; ++t)
-                            if (t < mtn) acc[r][t] = mfma_tile<WT>(av[u][r], bv[u][t], acc[r][t]);
-                    }
-            }
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) store_x(xr, 0);
+        __syncthreads();
     }
+    if (c < nch) compute(A0, 0);
 
     if (a.P > 1) {
         f32x4* pp = (f32x4*)a.part + part_index<R, MTG>(ng * a.MG + mg, a.P, ks, wave) + lane;
@@ -352,7 +435,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             for (int t = 0; t < MTG; ++t) pp[(r * MTG + t) * 64] = acc[r][t];
         return;
     }
-    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, mtn, nbw, rv);
+    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, MTG, nbw, rv, s_rstd);
 }
 
 // Sums the P k-split partial tiles of each (n-group, m-group) in split order
@@ -365,22 +448,44 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
     const int ng = blockIdx.x / a.MG;
     const int nbw = (ng * 4 + wave) * R;
     const int mt0 = mg * MTG;
-    const int mtn = min(MTG, a.MT - mt0);
     bool rv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) rv[r] = (nbw + r) < a.NB;
+    __shared__ float s_seg[MTG * 16 * 8];
+    __shared__ float s_rstd[MTG * 16];
+    if (a.ss_in) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
     f32x4 acc[R][MTG];
     const f32x4* pp = (const f32x4*)a.part + part_index<R, MTG>(ng * a.MG + mg, a.P, 0, wave) + lane;
     const size_t split = (size_t)4 * R * MTG * 64;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int t = 0; t < MTG; ++t) {
-            f32x4 s = pp[(r * MTG + t) * 64];
-            for (int q = 1; q < a.P; ++q) s += pp[q * split + (r * MTG + t) * 64];
-            acc[r][t] = s;
-        }
-    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, mtn, nbw, rv);
+        for (int t = 0; t < MTG; ++t) acc[r][t] = pp[(r * MTG + t) * 64];
+    // splits in order, two at a time so each step issues 2*R*MTG independent loads
+    int q = 1;
+    for (; q + 1 < a.P; q += 2) {
+        f32x4 v0[R][MTG], v1[R][MTG];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) {
+                v0[r][t] = pp[q * split + (r * MTG + t) * 64];
+                v1[r][t] = pp[(q + 1) * split + (r * MTG + t) * 64];
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) acc[r][t] = (acc[r][t] + v0[r][t]) + v1[r][t];
+    }
+    if (q < a.P) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) acc[r][t] += pp[q * split + (r * MTG + t) * 64];
+    }
+    __syncthreads();
+    if (a.ss_in) rstd_phase2(a, MTG * 16, s_seg, s_rstd);
+    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, MTG, nbw, rv, s_rstd);
 }
 
 // ---------------------------------------------------------------------------
@@ -444,7 +549,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     if (!a.active[s]) {
         if (chunk == 0)
             for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-                store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)g * G * D + i, 0.f);
+                store_act1<WT>(a.o_out, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
         return;
     }
     const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
@@ -591,7 +696,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             L += f * s_l[w][h];
         }
         if (nch == 1) {
-            store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, O / L * vs[g]);
+            store_act1<WT>(a.o_out, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
         } else {
             float* part = a.part + (((size_t)(s * a.hkv + g) * a.n_chunks + chunk) * G + h) * (D + 2);
             part[d] = O;
@@ -625,7 +730,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
             L += w * part[q * cs + D + 1];
             O += w * part[q * cs + d];
         }
-        store_act1<WT>(a.o_out, (size_t)s * hqd + (size_t)(g * G + h) * D + d, O / L * a.vscale[g]);
+        store_act1<WT>(a.o_out, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
     }
 }
 
@@ -660,30 +765,26 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
             }
         }
         *(f32x4*)(a.x + (size_t)m * a.d + i) = v;
-        store_act4<WT>(a.xg, (size_t)m * a.d + i, v * *(const f32x4*)(a.g + i));
+        store_act4<WT>(a.xg, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
     ss = block_sum_256(ss, red);
-    if (threadIdx.x == 0) a.ss_out[m] = ss;
+    if (threadIdx.x == 0) a.ss_out[(size_t)m * a.ss_stride] = ss;
 }
 
 template <int WT>
 __global__ __launch_bounds__(256) void final_kernel(FinalArgs a) {
-    __shared__ float s_r;
+    __shared__ float red[4];
     const int m = blockIdx.x;
     const bool valid = m < a.S && a.active[m];
-    if (threadIdx.x == 0) {
-        float s = 0.f;
-        for (int j = 0; j < a.nss; ++j) s += a.ss[(size_t)j * gridDim.x + m];
-        s_r = 1.0f / sqrtf(s * a.inv_d + a.eps);
-    }
-    __syncthreads();
-    const float r = s_r;
+    float part = 0.f;
+    for (int j = threadIdx.x; j < a.nss; j += blockDim.x) part += a.ss[(size_t)m * a.ss_stride + j];
+    const float r = 1.0f / sqrtf(block_sum_256(part, red) * a.inv_d + a.eps);
     for (int i = threadIdx.x * 4; i < a.d; i += blockDim.x * 4) {
         f32x4 y = *(const f32x4*)(a.x + (size_t)m * a.d + i) * r * *(const f32x4*)(a.g + i);
         if (!valid) y = f32x4{0.f, 0.f, 0.f, 0.f};
         if (a.y_out && m < a.S) store_act4<WT>(a.y_out, (size_t)m * a.ldy + a.y_off + i, y);
-        if (a.yw) store_act4<WT>(a.yw, (size_t)m * a.d + i, y);
+        if (a.yw) store_act4<WT>(a.yw, xoff<WT>(m, i, a.MT), y);
         if (a.zf) *(f32x4*)(a.zf + (size_t)m * a.d + i) = y;
     }
     if (a.advance && threadIdx.x == 0 && valid) a.pos[m] += 1;
@@ -723,15 +824,15 @@ hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
 }
 
 template <int WT, int R>
-static hipError_t gemm_mtg(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+static hipError_t gemm_mtg(const GemmArgs& a, int MTG, int CK, int grid, hipStream_t st) {
     const int red = grid / a.P;
-    switch (MTG) {
-#define FD_G(MT)                                                                                  \
-    case MT:                                                                                      \
-        hipLaunchKernelGGL((gemm_kernel<WT, R, MT>), dim3(grid), dim3(256), 0, st, a);            \
+    switch (MTG * 16 + CK) {
+#define FD_G(MT, C)                                                                                \
+    case MT * 16 + C:                                                                              \
+        hipLaunchKernelGGL((gemm_kernel<WT, R, MT, C>), dim3(grid), dim3(256), 0, st, a);          \
         if (a.P > 1) hipLaunchKernelGGL((gemm_reduce_kernel<WT, R, MT>), dim3(red), dim3(256), 0, st, a); \
         break;
-        FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5) FD_G(6) FD_G(7) FD_G(8)
+        FD_G(1, 8) FD_G(2, 8) FD_G(3, 8) FD_G(4, 8) FD_G(5, 8) FD_G(6, 4) FD_G(7, 4) FD_G(8, 4)
 #undef FD_G
         default: return hipErrorInvalidValue;
     }
@@ -739,8 +840,9 @@ static hipError_t gemm_mtg(const GemmArgs& a, int MTG, int grid, hipStream_t st)
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int wt, int R, int MTG, int grid, hipStream_t st) {
-    if (wt) return R == 2 ? gemm_mtg<1, 2>(a, MTG, grid, st) : gemm_mtg<1, 1>(a, MTG, grid, st);
-    return R == 2 ? gemm_mtg<0, 2>(a, MTG, grid, st) : gemm_mtg<0, 1>(a, MTG, grid, st);
+    const int CK = gemm_chunk(MTG);
+    if (wt) return R == 2 ? gemm_mtg<1, 2>(a, MTG, CK, grid, st) : gemm_mtg<1, 1>(a, MTG, CK, grid, st);
+    return R == 2 ? gemm_mtg<0, 2>(a, MTG, CK, grid, st) : gemm_mtg<0, 1>(a, MTG, CK, grid, st);
 }
 
 template <int WT, int FP8, int D>

@@ -173,7 +173,7 @@ def test_bf16_fp8_ragged_multichunk():
     at reduced width and depth; slots at positions spanning 1..3 attention
     chunks, one slot left empty."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
-                              d_ffn=1408, max_slots=9, max_context=700)
+                              d_ffn=1536, max_slots=9, max_context=700)
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 1, 255, 256, 257, 300, 511, 690]
     ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
