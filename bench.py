@@ -180,6 +180,34 @@ def max_sessions(cfg, pos, steps=3, warmup=1, budget_ms=80.0):
             "hbm_frac": r["step_bytes"] / (med * 1e-3) / 8e12}
 
 
+def read_probe_gbs(nbytes=16 << 30, reps=5):
+    """Achievable HBM read bandwidth: one streaming read of a 16 GiB buffer
+    by the library's read-probe kernel (the bandwidth blog measures the
+    same quantity by reading large tensors; section 2, 'Direct
+    Verification').  Best over grid sizes, median of `reps` each."""
+    import torch
+    from frame_decode_amd import fd_read_probe
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for grid in (2048, 4096, 8192, 16384):
+        fd_read_probe(buf, sink, grid)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fd_read_probe(buf, sink, grid)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        best = max(best, nbytes / statistics.median(times) / 1e9)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
+
+
 def cpu_baseline(cfg, pos, layers, sessions):
     """The oracle (unchanged) on a bounded sample: `sessions` sessions at
     frame index `pos` through `layers` of the stack's layers; scaled to
@@ -241,6 +269,8 @@ def main():
     pos = cfg.get("position", cfg["max_context"] - 1)
     S = cfg["max_slots"]
 
+    probe = read_probe_gbs()
+    log(f"read probe: {probe:.0f} GB/s")
     r = run_gpu(cfg, pos, args.steps, args.warmup)
     total_ms = r["total_ms"]
     ms_step = total_ms / args.steps
@@ -295,6 +325,8 @@ def main():
         "step_bytes": r["step_bytes"],
         "step_hbm_gbs": step_gbs,
         "step_hbm_frac": step_gbs / rf.MI355X_HBM_PEAK_GBS,
+        "measured_read_gbs": probe,
+        "step_frac_of_measured_read": step_gbs / probe,
         "roofline": {
             "kernel": "attention",
             "bound": "hbm",

@@ -28,4 +28,4 @@ def lib():
     return _lib
 
 
-from .context import Context, fd_plan  # noqa: E402,F401
+from .context import Context, fd_plan, fd_read_probe  # noqa: E402,F401

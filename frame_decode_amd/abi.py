@@ -72,7 +72,7 @@ class FdKvView(ctypes.Structure):
 
 EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_free", "fd_destroy",
            "fd_kv_layout", "fd_set_position", "fd_slot_state", "fd_kv_write", "fd_sync",
-           "fd_profile", "fd_profile_read", "fd_last_error", "fd_status_str"]
+           "fd_profile", "fd_profile_read", "fd_read_probe", "fd_last_error", "fd_status_str"]
 
 FD_N_KINDS = 8
 KIND_NAMES = ["embed", "qkv", "attention", "o_proj", "gate_up", "down", "final", "depth_in"]
@@ -107,6 +107,7 @@ def _proto(lib):
     lib.fd_sync.argtypes = [c_p, c_p]
     lib.fd_profile.argtypes = [c_p, c_i32]
     lib.fd_profile_read.argtypes = [c_p, P(ctypes.c_double), P(ctypes.c_int64), c_i32]
+    lib.fd_read_probe.argtypes = [c_p, ctypes.c_uint64, c_p, c_i32, c_p]
     lib.fd_last_error.argtypes = [c_p]
     lib.fd_last_error.restype = ctypes.c_char_p
     lib.fd_status_str.argtypes = [c_i32]

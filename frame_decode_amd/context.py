@@ -40,6 +40,13 @@ def fd_plan(cfg: dict) -> dict:
             "workspace": s.workspace, "slot_table": s.slot_table}
 
 
+def fd_read_probe(buf, sink, grid: int, stream=None) -> None:
+    """Enqueue one streaming read of the whole uint8 device tensor ``buf``."""
+    _check(_lib().fd_read_probe(ctypes.c_void_p(_ptr(buf)), int(buf.numel() * buf.element_size()),
+                                ctypes.c_void_p(_ptr(sink)), int(grid),
+                                ctypes.c_void_p(_stream_handle(stream))))
+
+
 def _stream_handle(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()

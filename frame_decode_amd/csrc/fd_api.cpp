@@ -630,6 +630,12 @@ fd_status fd_sync(fd_ctx* c, void* stream) {
     return FD_OK;
 }
 
+fd_status fd_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+    if (!buf || !sink || grid < 1 || bytes < 16 || ((uintptr_t)buf & 15)) return FD_E_INVAL;
+    hipError_t e = fd::launch_read_probe(buf, bytes, sink, grid, (hipStream_t)stream);
+    return e == hipSuccess ? FD_OK : FD_E_DEVICE;
+}
+
 fd_status fd_destroy(fd_ctx* c) {
     if (!c) return FD_E_INVAL;
     for (auto& p : c->prof_pending) {

@@ -110,16 +110,18 @@ struct KvWriteArgs {
     int hkv, hd, t0, n, kv_fp8;
 };
 
-// k-tiles per GEMM main-loop chunk for a given m-group height (every
-// k-split covers a whole number of chunks).
-inline int gemm_chunk(int MTG) { return MTG <= 5 ? 8 : 4; }
+// k-tiles a GEMM wave loads per step (each k-split covers a whole number of
+// steps): two while a wave's tile count NG*MTG leaves room for the second
+// register buffer, else one.
+constexpr int gemm_unroll(int NG, int MTG) { return NG * MTG <= 20 ? 2 : 1; }
 
 // Launchers (enqueue on `st`; return the launch error).
 hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st);
-hipError_t launch_gemm(const GemmArgs& a, int wt, int R, int MTG, int grid, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, int wt, int kv_fp8, int hd, int G, int grid, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 
 }  // namespace fd

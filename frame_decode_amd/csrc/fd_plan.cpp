@@ -8,9 +8,10 @@
 
 namespace fd {
 
-int gemm_chunk_tiles(int MTG) { return MTG <= 5 ? 8 : 4; }
+// k-tiles a GEMM wave loads per step; mirrors gemm_unroll in the kernels.
+int gemm_unroll_tiles(int NG, int MTG) { return NG * MTG <= 20 ? 2 : 1; }
 
-GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
+GemmShape shape_with(int N, int K, int KT, int MT, int NG, int P) {
     GemmShape g;
     g.N = N;
     g.K = K;
@@ -19,23 +20,45 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
     g.KB = K / KT;
     g.MG = cdiv(MT, kMaxMTG);
     g.MTG = cdiv(MT, g.MG);
-    // One n-block per wave: the session rows X are shared through LDS by
-    // the four waves, so wider waves buy little and cost occupancy.
-    g.R = 1;
-    g.n_groups = cdiv(g.NB, kWaves * g.R);
-    int base = g.n_groups * g.MG;
-    // Split K until there are about two workgroups per CU; every split
-    // covers a whole number of main-loop chunks (P divides KB / chunk).
-    const int chunks = g.KB / gemm_chunk_tiles(g.MTG);
-    int want = (2 * n_cu + base - 1) / base;
-    want = std::min(want, std::max(1, chunks / 2));
-    int p = 1;
-    for (int d = 1; d <= chunks && d <= 16; ++d)
-        if (chunks % d == 0 && d <= want) p = d;
-    g.P = p;
-    g.part_floats = g.P > 1 ? (uint64_t)g.n_groups * g.MG * g.P * kWaves * g.R * g.MTG * 256 : 0;
+    g.R = NG;
+    g.P = P;
+    g.n_groups = cdiv(g.NB, NG);
+    g.part_floats = P > 1 ? (uint64_t)g.n_groups * g.MG * P * NG * g.MTG * 256 : 0;
     g.counters = g.n_groups * g.MG;
     return g;
+}
+
+bool valid_split(const GemmShape& g, int NG, int P) {
+    const int U = gemm_unroll_tiles(NG, g.MTG);
+    return P >= 1 && g.KB % P == 0 && (g.KB / P) % U == 0 && (g.KB / P) / U >= 4;
+}
+
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
+    // Candidates: 6 or 4 weight blocks per workgroup (6 only while the
+    // accumulators of a 5-tile m-group fit), any split P that gives every
+    // wave at least one step.  Score: how evenly the grid fills whole
+    // rounds of one workgroup per CU, minus a small charge per extra split
+    // (its partial tiles cost a write and a read).
+    GemmShape best = shape_with(N, K, KT, MT, 4, 1);
+    double best_score = -1e9;
+    for (int NG : {6, 4}) {
+        GemmShape base = shape_with(N, K, KT, MT, NG, 1);
+        if (NG == 6 && base.MTG > 5) continue;
+        for (int P = 1; P <= 64; ++P) {
+            if (!valid_split(base, NG, P)) continue;
+            GemmShape g = shape_with(N, K, KT, MT, NG, P);
+            const int grid = g.grid();
+            const int rounds = cdiv(grid, n_cu);
+            const double fill = (double)grid / ((double)rounds * n_cu);
+            double score = fill - 0.04 * (P - 1) - (rounds > 2 ? 0.1 : 0.0);
+            if (grid < n_cu / 2) score -= 0.3;
+            if (score > best_score + 1e-9) {
+                best_score = score;
+                best = g;
+            }
+        }
+    }
+    return best;
 }
 
 namespace {
@@ -79,14 +102,12 @@ int tune_value(const char* key, int dflt) {
 
 GemmShape tuned(GemmShape g, const char* name) {
     std::string n(name);
-    int R = tune_value((n + ".R").c_str(), g.R);
+    int NG = tune_value((n + ".NG").c_str(), g.R);
     int P = tune_value((n + ".P").c_str(), g.P);
-    if (R == 1 || R == 2) g.R = R;
-    if (P >= 1 && (g.KB / gemm_chunk_tiles(g.MTG)) % P == 0) g.P = P;
-    g.n_groups = cdiv(g.NB, kWaves * g.R);
-    g.part_floats = g.P > 1 ? (uint64_t)g.n_groups * g.MG * g.P * kWaves * g.R * g.MTG * 256 : 0;
-    g.counters = g.n_groups * g.MG;
-    return g;
+    if (!(NG == 4 || (NG == 6 && g.MTG <= 5))) NG = g.R;
+    GemmShape base = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, 1);
+    if (!valid_split(base, NG, P)) P = valid_split(base, NG, g.P) ? g.P : 1;
+    return shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, P);
 }
 
 void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8,
@@ -116,15 +137,16 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     // attention chunking: lanes per position give each lane 16 bytes (FP8)
     // or 32 bytes (fp32) of a position's head vector
     // Chunks of the window per (slot, kv head): one workgroup per chunk.
-    // Enough chunks for about four workgroups per CU when the slot x head
-    // count alone is too small; a single chunk needs no merge kernel.
+    // A single chunk (no merge kernel) when the slot x head pairs alone give
+    // about four workgroups per CU; otherwise enough chunks to get there.
     AttnShape& a = sp.attn;
     a.lpp = kv_fp8 ? dims.hd / 16 : dims.hd / 8;
     const int round = kWaves * kAttnIters * (64 / a.lpp);
     const int pairs = std::max(1, S * dims.hkv);
     int want = std::max(1, cdiv(1024, pairs));
     want = std::max(1, tune_value("attn.chunks", want));
-    a.tc = cdiv(cdiv(dims.T, want), round) * round;
+    a.tc = want == 1 ? cdiv(dims.T, round) * round
+                     : std::max(round, cdiv(dims.T, want) / round * round);
     a.n_chunks = cdiv(dims.T, a.tc);
 }
 

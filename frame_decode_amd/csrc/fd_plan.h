@@ -26,13 +26,13 @@ struct GemmShape {
     int N = 0, K = 0;
     int KT = 0;        // k-width of a tile: 32 (bf16) or 16 (fp32)
     int NB = 0, KB = 0;  // tiles along N (16 rows each) and K
-    int R = 1;         // n-blocks per wave
+    int R = 4;         // n-blocks per workgroup (4 or 6), shared by its 4 k-split waves
     int P = 1;         // k-splits (workgroups sharing one n-group)
     int MG = 1;        // m-groups
     int MTG = 1;       // 16-row m-tiles per m-group
-    int n_groups = 0;  // ceil(NB / (kWaves * R))
+    int n_groups = 0;  // ceil(NB / R)
     uint64_t w_off = 0;   // offset of the packed tiles in the packed buffer
-    uint64_t part_floats = 0;  // partial-sum floats needed when P > 1
+    uint64_t part_floats = 0;  // partial-sum floats needed when P > 1 (n_groups*MG*P*R*MTG*256)
     int counters = 0;
     int grid() const { return n_groups * P * MG; }
 };
@@ -103,9 +103,9 @@ struct Plan {
 // a message in *err.
 fd_status make_plan(const fd_config& cfg, Plan* out, std::string* err);
 
-// k-tiles per GEMM main-loop chunk for an m-group of MTG 16-row tiles (the
-// kernels' own choice, mirrored here so k-splits cover whole chunks).
-int gemm_chunk_tiles(int MTG);
+// k-tiles a GEMM wave loads per step (the kernels' own choice, mirrored
+// here so every k-split covers whole steps).
+int gemm_unroll_tiles(int NG, int MTG);
 
 // Tile choice for one projection (exposed for tests).
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu);

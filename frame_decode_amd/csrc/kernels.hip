@@ -154,11 +154,17 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 // skinny GEMM: Y[m][n] = sum_k X[m][k] W[n][k] with the MFMA A operand = W
 // (16 n-rows) and B operand = X^T (16 session columns), fp32 accumulation.
 //
-// Workgroup task (n-group, m-group, k-split): 4 waves, wave w owns n-blocks
-// (n-group*4 + w)*R .. +R; all waves share the same k-range so X fragments
-// are re-read from the CU's L1.  With P > 1 k-splits, every split stores its
-// partial tiles and a second kernel sums them in split order (deterministic)
-// and applies the epilogue; workgroups of one launch never exchange data.
+// Workgroup task (n-group, m-group, k-split): an n-group is NG 16-row weight
+// blocks.  The 4 waves split the k-split's tiles between them (wave w takes
+// runs of U tiles w, w+4, ...) and every wave covers all NG blocks, so each
+// session-row fragment is loaded from L2 once per workgroup straight into
+// the registers that feed the MFMAs, and each weight tile is read once; the
+// main loop has no LDS traffic and no barrier.  The four waves'
+// accumulators are then added through LDS in wave order (deterministic) and
+// each wave finishes every fourth tile.  With P > 1 k-splits the finished
+// tiles are partial sums, stored for gemm_reduce_kernel, which adds them in
+// split order and applies the epilogue; workgroups of one launch never
+// exchange data.
 
 template <int WT>
 struct BFrag;
@@ -180,12 +186,6 @@ __device__ __forceinline__ f32x4 mfma_tile(u32x4 a, typename BFrag<WT>::T b, f32
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], b[3], c, 0, 0, 0);
         return c;
     }
-}
-
-// Offset (in f32x4 units) of a wave's partial tiles for one k-split.
-template <int R, int MTG>
-__device__ __forceinline__ size_t part_index(int task, int P, int ks, int wave) {
-    return (((size_t)task * P + ks) * 4 + wave) * (R * MTG * 64);
 }
 
 // Row scales of the RMS norm from the partial sums of x^2 that the
@@ -221,82 +221,87 @@ __device__ __forceinline__ void rstd_phase2(const GemmArgs& a, int rows, const f
     }
 }
 
-// Epilogue of a finished accumulator set.  acc[r][t] holds rows n =
-// (nbw + r)*16 + 4*(lane/16) + i, column m = (mt0 + t)*16 + lane%16.
-template <int WT, int R, int MTG>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4 (&acc)[R][MTG], int ng,
-                                              int mt0, int mtn, int nbw, bool (&rv)[R],
-                                              const float* s_rstd) {
+// Epilogue of the tiles a wave owns after the cross-wave sum: tile i =
+// wave + 4*j is (block r = i / MTG of the n-group, m-tile t = i % MTG); v[j]
+// holds rows n = (nb0 + r)*16 + 4*(lane/16) + e, column m = (mt0 + t)*16 +
+// lane%16.
+template <int WT, int NG, int MTG, int NWV>
+__device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, int ng, int mt0,
+                                            const float* s_rstd) {
+    constexpr int NTL = NG * MTG;
+    constexpr int OWN = (NTL + NWV - 1) / NWV;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    __shared__ float s_red[4][MTG * 16];
-    __syncthreads();
-
+    const int nb0 = ng * NG;
+    __shared__ float s_red[NWV][MTG * 16];
     float ssum[MTG];
 #pragma unroll
     for (int t = 0; t < MTG; ++t) ssum[t] = 0.f;
 
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int t = 0; t < MTG; ++t) {
-            if (!rv[r] || t >= mtn) continue;
-            const int mloc = t * 16 + (lane & 15);
-            const int m = mt0 * 16 + mloc;
-            const int n = (nbw + r) * 16 + (lane >> 4) * 4;
-            f32x4 v = acc[r][t];
-            if (a.ss_in) v *= s_rstd[mloc];
-            if (a.epi == EPI_QKV) {
-                const int hh = n / a.hd;
-                const int d0 = n - hh * a.hd;
-                const bool act = m < a.S && a.active[m];
-                int p = a.pos_override >= 0 ? a.pos_override : (m < a.S ? a.pos[m] : 0);
-                p = min(max(p, 0), a.rope_T - 1);
-                if (hh < a.hq + a.hkv) {
-                    const f32x4 cs = *(const f32x4*)(a.rope + ((size_t)p * (a.hd / 2) + d0 / 2) * 2);
-                    f32x4 w;
-                    w[0] = v[0] * cs[0] - v[1] * cs[1];
-                    w[1] = v[0] * cs[1] + v[1] * cs[0];
-                    w[2] = v[2] * cs[2] - v[3] * cs[3];
-                    w[3] = v[2] * cs[3] + v[3] * cs[2];
-                    v = w;
-                }
-                if (hh < a.hq) {
-                    const int g = hh / (a.hq / a.hkv);
-                    *(f32x4*)(a.q_out + (size_t)m * a.hq * a.hd + n) = v * a.qscale[g];
-                } else if (act) {
-                    const int kv = hh < a.hq + a.hkv ? 0 : 1;
-                    const int g = hh - a.hq - kv * a.hkv;
-                    uint8_t* dst = a.arena + (size_t)m * a.slot_stride + kv * a.kv_stride +
-                                   g * a.head_stride + (size_t)p * a.pos_stride;
-                    if (a.kv_fp8) {
-                        const float sg = a.kvsig[kv * a.hkv + g];
-                        uint32_t w = enc_e4m3(v[0] / sg) | (enc_e4m3(v[1] / sg) << 8) |
-                                     (enc_e4m3(v[2] / sg) << 16) | (enc_e4m3(v[3] / sg) << 24);
-                        *(uint32_t*)(dst + d0) = w;
-                    } else {
-                        *(f32x4*)(dst + (size_t)d0 * 4) = v;
-                    }
-                }
-            } else if (a.epi == EPI_RESID) {
-                float* xr = a.x + (size_t)m * a.ld + n;
-                f32x4 xn = *(f32x4*)xr + v;
-                *(f32x4*)xr = xn;
-                const f32x4 g = *(const f32x4*)(a.g_next + n);
-                store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * g);
-                ssum[t] += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
-            } else if (a.epi == EPI_GU) {
-                const int j = n >> 1;  // rows interleave gate_j, up_j, gate_j+1, up_j+1
-                const float h0 = v[0] / (1.0f + expf(-v[0])) * v[1];
-                const float h1 = v[2] / (1.0f + expf(-v[2])) * v[3];
-                if (WT) {
-                    *(uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, j, a.MT)) = f2bf(h0) | (f2bf(h1) << 16);
-                } else {
-                    *(f32x2*)((float*)a.h_out + xoff<WT>(m, j, a.MT)) = f32x2{h0, h1};
-                }
-            } else {
-                *(f32x4*)(a.y + (size_t)m * a.ld + n) = v;
+    for (int j = 0; j < OWN; ++j) {
+        const int i = wave + NWV * j;
+        if (i >= NTL) break;
+        const int r = i / MTG, t = i - (i / MTG) * MTG;
+        if (nb0 + r >= a.NB) continue;
+        const int mloc = t * 16 + (lane & 15);
+        const int m = mt0 * 16 + mloc;
+        const int n = (nb0 + r) * 16 + (lane >> 4) * 4;
+        f32x4 x = v[j];
+        if (a.ss_in) x *= s_rstd[mloc];
+        if (a.epi == EPI_QKV) {
+            const int hh = n / a.hd;
+            const int d0 = n - hh * a.hd;
+            const bool act = m < a.S && a.active[m];
+            int p = a.pos_override >= 0 ? a.pos_override : (m < a.S ? a.pos[m] : 0);
+            p = min(max(p, 0), a.rope_T - 1);
+            if (hh < a.hq + a.hkv) {
+                const f32x4 cs = *(const f32x4*)(a.rope + ((size_t)p * (a.hd / 2) + d0 / 2) * 2);
+                f32x4 w;
+                w[0] = x[0] * cs[0] - x[1] * cs[1];
+                w[1] = x[0] * cs[1] + x[1] * cs[0];
+                w[2] = x[2] * cs[2] - x[3] * cs[3];
+                w[3] = x[2] * cs[3] + x[3] * cs[2];
+                x = w;
             }
+            if (hh < a.hq) {
+                const int g = hh / (a.hq / a.hkv);
+                *(f32x4*)(a.q_out + (size_t)m * a.hq * a.hd + n) = x * a.qscale[g];
+            } else if (act) {
+                const int kv = hh < a.hq + a.hkv ? 0 : 1;
+                const int g = hh - a.hq - kv * a.hkv;
+                uint8_t* dst = a.arena + (size_t)m * a.slot_stride + kv * a.kv_stride +
+                               g * a.head_stride + (size_t)p * a.pos_stride;
+                if (a.kv_fp8) {
+                    const float sg = a.kvsig[kv * a.hkv + g];
+                    uint32_t w = enc_e4m3(x[0] / sg) | (enc_e4m3(x[1] / sg) << 8) |
+                                 (enc_e4m3(x[2] / sg) << 16) | (enc_e4m3(x[3] / sg) << 24);
+                    *(uint32_t*)(dst + d0) = w;
+                } else {
+                    *(f32x4*)(dst + (size_t)d0 * 4) = x;
+                }
+            }
+        } else if (a.epi == EPI_RESID) {
+            float* xr = a.x + (size_t)m * a.ld + n;
+            f32x4 xn = *(f32x4*)xr + x;
+            *(f32x4*)xr = xn;
+            const f32x4 g = *(const f32x4*)(a.g_next + n);
+            store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * g);
+            const float sq = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+#pragma unroll
+            for (int tt = 0; tt < MTG; ++tt)
+                if (tt == t) ssum[tt] += sq;
+        } else if (a.epi == EPI_GU) {
+            const int jj = n >> 1;  // rows interleave gate_j, up_j, gate_j+1, up_j+1
+            const float h0 = x[0] / (1.0f + expf(-x[0])) * x[1];
+            const float h1 = x[2] / (1.0f + expf(-x[2])) * x[3];
+            if (WT) {
+                *(uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, jj, a.MT)) = f2bf(h0) | (f2bf(h1) << 16);
+            } else {
+                *(f32x2*)((float*)a.h_out + xoff<WT>(m, jj, a.MT)) = f32x2{h0, h1};
+            }
+        } else {
+            *(f32x4*)(a.y + (size_t)m * a.ld + n) = x;
         }
     }
 
@@ -310,22 +315,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4 (&acc)[R]
             if (lane < 16) s_red[wave][t * 16 + lane] = s;
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < mtn * 16; i += blockDim.x) {
-            const float s = ((s_red[0][i] + s_red[1][i]) + s_red[2][i]) + s_red[3][i];
+        for (int i = threadIdx.x; i < MTG * 16; i += blockDim.x) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) s += s_red[w][i];
             a.ss_out[(size_t)(mt0 * 16 + i) * a.ss_stride + ng] = s;
         }
     }
 }
 
-// Main loop: the k-range is walked in chunks of CK k-tiles.  The session
-// fragments of a chunk (CK x MTG tiles, 1 KiB each) are staged once per
-// workgroup into a double-buffered LDS ring and read back with ds_read by
-// all four waves; each wave keeps its own weight tiles in registers, one
-// whole chunk ahead of the MFMAs, so the vector-memory queue holds weight
-// streams only.
-template <int WT, int R, int MTG, int CK>
+template <int WT, int NG, int MTG, int U>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     typedef typename BFrag<WT>::T BT;
+    constexpr int NTL = NG * MTG;
+    constexpr int OWN = (NTL + 3) / 4;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     int bid = blockIdx.x;
@@ -333,159 +336,128 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     bid /= a.P;
     const int mg = bid % a.MG;
     const int ng = bid / a.MG;
-    const int kpb = a.KB / a.P;           // k-tiles per split (a multiple of CK)
+    const int kpb = a.KB / a.P;  // k-tiles per split (a multiple of U)
     const int kb0 = ks * kpb;
-    const int nch = kpb / CK;
-    const int nbw = (ng * 4 + wave) * R;  // first n-block of this wave
-    const int mt0 = mg * MTG;             // session rows are padded to whole m-groups
+    const int ngrp = kpb / U;
+    const int nb0 = ng * NG;
+    const int mt0 = mg * MTG;    // session rows are padded to whole m-groups
 
-    __shared__ u32x4 xs[2][CK * MTG * 64];
+    __shared__ f32x4 s_acc[4][NTL][64];
+    __shared__ float s_seg[MTG * 16 * 8];
+    __shared__ float s_rstd[MTG * 16];
 
-    f32x4 acc[R][MTG];
+    const u32x4* wp[NG];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < NG; ++r)  // blocks past the matrix re-read the last one (never stored)
+        wp[r] = (const u32x4*)(a.W + (size_t)min(nb0 + r, a.NB - 1) * a.KB * 1024) + lane;
+    // fragment (k-tile kb, m-tile mt) is 1 KiB at ((kb*MT + mt)*64 + lane) * 16 bytes
+    const u32x4* xp = (const u32x4*)a.X + (size_t)mt0 * 64 + lane;
+    const size_t xk = (size_t)a.MT * 64;
+
+    f32x4 acc[NG][MTG];
+#pragma unroll
+    for (int r = 0; r < NG; ++r)
 #pragma unroll
         for (int t = 0; t < MTG; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    bool rv[R];
-    const u32x4* wp[R];
+    u32x4 A0[U][NG], A1[U][NG];
+    BT B0[U][MTG], B1[U][MTG];
+    auto load = [&](u32x4 (&A)[U][NG], BT (&B)[U][MTG], int kb) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        rv[r] = (nbw + r) < a.NB;
-        const int nb = min(nbw + r, a.NB - 1);  // out-of-range blocks re-read a valid one
-        wp[r] = (const u32x4*)(a.W + (size_t)nb * a.KB * 1024) + lane;
-    }
-    // chunk of X: for each of its CK k-tiles, the MTG fragments of this
-    // m-group are contiguous (MTG KiB); thread i moves 16 B pieces i, i+256, ...
-    const u32x4* xg = (const u32x4*)a.X;
-    constexpr int XQ = CK * MTG / 4;  // 16-byte pieces per thread per chunk
-    auto load_x = [&](u32x4 (&v)[XQ], int kb) {
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int q = 0; q < XQ; ++q) {
-            const int idx = threadIdx.x + q * 256;  // < CK * MTG * 64
-            const int kk = idx / (MTG * 64);
-            const int rem = idx - kk * (MTG * 64);
-            v[q] = xg[((size_t)(kb + kk) * a.MT + mt0) * 64 + rem];
+            for (int t = 0; t < MTG; ++t) B[u][t] = __builtin_bit_cast(BT, xp[(size_t)(kb + u) * xk + t * 64]);
+#pragma unroll
+            for (int r = 0; r < NG; ++r) A[u][r] = __builtin_nontemporal_load(&wp[r][(size_t)(kb + u) * 64]);
         }
     };
-    auto store_x = [&](const u32x4 (&v)[XQ], int buf) {
+    auto mma = [&](u32x4 (&A)[U][NG], BT (&B)[U][MTG]) {
 #pragma unroll
-        for (int q = 0; q < XQ; ++q) xs[buf][threadIdx.x + q * 256] = v[q];
-    };
-    auto load_a = [&](u32x4 (&A)[CK][R], int kb) {
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < CK; ++i)
+            for (int r = 0; r < NG; ++r)
 #pragma unroll
-            for (int r = 0; r < R; ++r) A[i][r] = __builtin_nontemporal_load(&wp[r][(size_t)(kb + i) * 64]);
-    };
-    auto compute = [&](const u32x4 (&A)[CK][R], int buf) {
-#pragma unroll
-        for (int i = 0; i < CK; ++i) {
-            BT b[MTG];
-#pragma unroll
-            for (int t = 0; t < MTG; ++t) b[t] = __builtin_bit_cast(BT, xs[buf][(i * MTG + t) * 64 + lane]);
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(A[i][r], b[t], acc[r][t]);
-        }
+                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(A[u][r], B[u][t], acc[r][t]);
     };
 
-    __shared__ float s_seg[MTG * 16 * 8];
-    __shared__ float s_rstd[MTG * 16];
     const bool norm_here = a.ss_in && a.P == 1;
-
-    u32x4 A0[CK][R], A1[CK][R];
-    u32x4 xr[XQ];
-    load_x(xr, kb0);
-    load_a(A0, kb0);
-    // the norm's partial sums load while the first weight chunk is in flight
+    int g = wave;
+    if (g < ngrp) load(A0, B0, kb0 + g * U);
+    // the norm's partial sums load while the first tiles are in flight
     if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
-    store_x(xr, 0);
+    for (; g < ngrp; g += 8) {
+        const bool n1 = g + 4 < ngrp;
+        if (n1) load(A1, B1, kb0 + (g + 4) * U);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(A0, B0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!n1) break;
+        const bool n2 = g + 8 < ngrp;
+        if (n2) load(A0, B0, kb0 + (g + 8) * U);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(A1, B1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!n2) break;
+    }
+
+    // sum the four waves' k-portions; wave w keeps tiles w, w+4, ...
+#pragma unroll
+    for (int r = 0; r < NG; ++r)
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) s_acc[wave][r * MTG + t][lane] = acc[r][t];
     __syncthreads();
     if (norm_here) rstd_phase2(a, MTG * 16, s_seg, s_rstd);
-    int c = 0;
-    for (; c + 2 <= nch; c += 2) {
-        const int kb = kb0 + c * CK;
-        load_a(A1, kb + CK);
-        load_x(xr, kb + CK);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(A0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        store_x(xr, 1);
-        __syncthreads();
-        const bool more = c + 2 < nch;
-        if (more) {
-            load_a(A0, kb + 2 * CK);
-            load_x(xr, kb + 2 * CK);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        compute(A1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) store_x(xr, 0);
-        __syncthreads();
+    f32x4 v[OWN];
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+        const int i = wave + 4 * j;
+        if (i < NTL) v[j] = ((s_acc[0][i][lane] + s_acc[1][i][lane]) + s_acc[2][i][lane]) + s_acc[3][i][lane];
     }
-    if (c < nch) compute(A0, 0);
-
     if (a.P > 1) {
-        f32x4* pp = (f32x4*)a.part + part_index<R, MTG>(ng * a.MG + mg, a.P, ks, wave) + lane;
+        f32x4* pp = (f32x4*)a.part + ((size_t)(ng * a.MG + mg) * a.P + ks) * NTL * 64 + lane;
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < MTG; ++t) pp[(r * MTG + t) * 64] = acc[r][t];
+        for (int j = 0; j < OWN; ++j) {
+            const int i = wave + 4 * j;
+            if (i < NTL) pp[(size_t)i * 64] = v[j];
+        }
         return;
     }
-    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, MTG, nbw, rv, s_rstd);
+    __syncthreads();
+    gemm_finish<WT, NG, MTG, 4>(a, v, ng, mt0, s_rstd);
 }
 
-// Sums the P k-split partial tiles of each (n-group, m-group) in split order
-// and applies the epilogue; one workgroup per (n-group, m-group).
-template <int WT, int R, int MTG>
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
+// Adds the P k-split partial tiles of each (n-group, m-group) in split order
+// and applies the epilogue; one workgroup of 16 waves per (n-group,
+// m-group), wave w finishing tiles w, w+16, ... so every wave has its loads
+// in flight at once.
+constexpr int kReduceWaves = 16;
+
+template <int WT, int NG, int MTG>
+__global__ __launch_bounds__(kReduceWaves * 64) void gemm_reduce_kernel(GemmArgs a) {
+    constexpr int NTL = NG * MTG;
+    constexpr int OWN = (NTL + kReduceWaves - 1) / kReduceWaves;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int mg = blockIdx.x % a.MG;
     const int ng = blockIdx.x / a.MG;
-    const int nbw = (ng * 4 + wave) * R;
     const int mt0 = mg * MTG;
-    bool rv[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) rv[r] = (nbw + r) < a.NB;
     __shared__ float s_seg[MTG * 16 * 8];
     __shared__ float s_rstd[MTG * 16];
     if (a.ss_in) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
-    f32x4 acc[R][MTG];
-    const f32x4* pp = (const f32x4*)a.part + part_index<R, MTG>(ng * a.MG + mg, a.P, 0, wave) + lane;
-    const size_t split = (size_t)4 * R * MTG * 64;
+    const f32x4* pp = (const f32x4*)a.part + (size_t)(ng * a.MG + mg) * a.P * NTL * 64 + lane;
+    const size_t split = (size_t)NTL * 64;
+    f32x4 v[OWN];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < MTG; ++t) acc[r][t] = pp[(r * MTG + t) * 64];
-    // splits in order, two at a time so each step issues 2*R*MTG independent loads
-    int q = 1;
-    for (; q + 1 < a.P; q += 2) {
-        f32x4 v0[R][MTG], v1[R][MTG];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < MTG; ++t) {
-                v0[r][t] = pp[q * split + (r * MTG + t) * 64];
-                v1[r][t] = pp[(q + 1) * split + (r * MTG + t) * 64];
-            }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < MTG; ++t) acc[r][t] = (acc[r][t] + v0[r][t]) + v1[r][t];
-    }
-    if (q < a.P) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < MTG; ++t) acc[r][t] += pp[q * split + (r * MTG + t) * 64];
+    for (int j = 0; j < OWN; ++j) {
+        const int i = min(wave + kReduceWaves * j, NTL - 1);
+        f32x4 s = pp[(size_t)i * 64];
+        for (int q = 1; q < a.P; ++q) s += pp[q * split + (size_t)i * 64];
+        v[j] = s;
     }
     __syncthreads();
     if (a.ss_in) rstd_phase2(a, MTG * 16, s_seg, s_rstd);
-    gemm_epilogue<WT, R, MTG>(a, acc, ng, mt0, MTG, nbw, rv, s_rstd);
+    __syncthreads();
+    gemm_finish<WT, NG, MTG, kReduceWaves>(a, v, ng, mt0, s_rstd);
 }
 
 // ---------------------------------------------------------------------------
@@ -595,7 +567,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             const int t = tw + it * PPL;
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                raw[it][j] = t < t1 ? *(const u32x4*)(kbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
+                raw[it][j] = t < t1 ? __builtin_nontemporal_load((const u32x4*)(kbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
                                     : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
@@ -618,7 +590,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             const int t = tw + it * PPL;
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                raw[it][j] = t < t1 ? *(const u32x4*)(vbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16)
+                raw[it][j] = t < t1 ? __builtin_nontemporal_load((const u32x4*)(vbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
                                     : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
@@ -813,6 +785,30 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// HBM read probe: streams a buffer once with wide loads (8 independent 16-byte
+// loads in flight per lane), folding the words so the loads stay live.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* buf, size_t n16, uint32_t* sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = buf[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u];
+    }
+    for (; i < n16; i += stride) acc ^= buf[i];
+    const uint32_t w = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (w == 0x9E3779B9u) sink[blockIdx.x] = w;  // practically never taken; keeps the loads
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, st, (const u32x4*)buf, bytes / 16, sink);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
@@ -823,26 +819,42 @@ hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int WT, int R>
-static hipError_t gemm_mtg(const GemmArgs& a, int MTG, int CK, int grid, hipStream_t st) {
+template <int WT, int NG>
+static hipError_t gemm_ng(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
     const int red = grid / a.P;
-    switch (MTG * 16 + CK) {
-#define FD_G(MT, C)                                                                                \
-    case MT * 16 + C:                                                                              \
-        hipLaunchKernelGGL((gemm_kernel<WT, R, MT, C>), dim3(grid), dim3(256), 0, st, a);          \
-        if (a.P > 1) hipLaunchKernelGGL((gemm_reduce_kernel<WT, R, MT>), dim3(red), dim3(256), 0, st, a); \
+    switch (MTG) {
+#define FD_G(MT)                                                                                         \
+    case MT:                                                                                             \
+        hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_unroll(NG, MT)>), dim3(grid), dim3(256), 0, st, a); \
+        if (a.P > 1) hipLaunchKernelGGL((gemm_reduce_kernel<WT, NG, MT>), dim3(red), dim3(kReduceWaves * 64), 0, st, a); \
         break;
-        FD_G(1, 8) FD_G(2, 8) FD_G(3, 8) FD_G(4, 8) FD_G(5, 8) FD_G(6, 4) FD_G(7, 4) FD_G(8, 4)
+        FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
 #undef FD_G
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, int wt, int R, int MTG, int grid, hipStream_t st) {
-    const int CK = gemm_chunk(MTG);
-    if (wt) return R == 2 ? gemm_mtg<1, 2>(a, MTG, CK, grid, st) : gemm_mtg<1, 1>(a, MTG, CK, grid, st);
-    return R == 2 ? gemm_mtg<0, 2>(a, MTG, CK, grid, st) : gemm_mtg<0, 1>(a, MTG, CK, grid, st);
+template <int WT>
+static hipError_t gemm_ng4(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    const int red = grid / a.P;
+    switch (MTG) {
+#define FD_G(MT)                                                                                        \
+    case MT:                                                                                            \
+        hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_unroll(4, MT)>), dim3(grid), dim3(256), 0, st, a); \
+        if (a.P > 1) hipLaunchKernelGGL((gemm_reduce_kernel<WT, 4, MT>), dim3(red), dim3(kReduceWaves * 64), 0, st, a); \
+        break;
+        FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5) FD_G(6) FD_G(7) FD_G(8)
+#undef FD_G
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hipStream_t st) {
+    if (NG == 6) return wt ? gemm_ng<1, 6>(a, MTG, grid, st) : gemm_ng<0, 6>(a, MTG, grid, st);
+    if (NG == 4) return wt ? gemm_ng4<1>(a, MTG, grid, st) : gemm_ng4<0>(a, MTG, grid, st);
+    return hipErrorInvalidValue;
 }
 
 template <int WT, int FP8, int D>

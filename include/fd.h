@@ -66,7 +66,7 @@ typedef int32_t fd_status;
  * Supported: w_dtype == act_dtype in {FD_F32, FD_BF16}; kv_dtype in
  * {FD_F32, FD_FP8_E4M3}; head_dim in {64, 128, 256}; n_heads a multiple of
  * n_kv_heads with n_heads / n_kv_heads in {1, 2, 4}; d_model, d_ffn and
- * n_heads*head_dim multiples of 32 (bf16) or 16 (fp32); max_slots in
+ * n_heads*head_dim multiples of 256 (bf16) or 128 (fp32); max_slots in
  * 1..4096; max_context in 1..65536.  An optional depth stack (depth_steps >
  * 0) runs after the main stack on every frame, for depth_steps sequential
  * sub-steps with its own fp32 cache cleared every frame; it requires
@@ -267,6 +267,16 @@ fd_status fd_kv_write(fd_ctx* ctx, int32_t slot, int32_t layer, int32_t t0, int3
 #define FD_N_KINDS 8
 fd_status fd_profile(fd_ctx* ctx, int32_t enable);
 fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, int32_t n);
+
+/*
+ * HBM read probe (bench hook): enqueues one kernel that reads `bytes` of
+ * device memory at `buf` (16-byte aligned) once with wide loads, `grid`
+ * workgroups of 256 threads, and may write to device words sink[0..grid).
+ * Timing it gives the achievable streaming-read bandwidth, the denominator
+ * the bandwidth blog measures directly (section 2, "Direct Verification").
+ * Needs no ctx.  FD_E_INVAL for bad arguments.
+ */
+fd_status fd_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int32_t grid, void* stream);
 
 /* Waits for the ctx's last enqueued work on `stream` and reports device
  * errors (FD_E_DEVICE) including the kernels' own fault flag. */
