@@ -199,36 +199,37 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         g.inv_d = inv_d;
         g.eps = eps;
         g.ss_stride = pl.nss_max;
-        g.active = slot_active(c);
-        g.pos = slot_pos(c);
-        g.pos_override = pos_override;
 
-        // QKV with the attention norm, rotary, append
+        // QKV projection: one plane of sums per k-split; the attention
+        // kernel adds them and applies the norm, rotary and cache append
         fd::GemmArgs q = g;
         const fd::GemmShape& sq = sp.qkv;
         q.W = P(c, lo.qkv);
         q.X = Wk(c, pl.ws_xg);
         q.K = sq.K; q.KB = sq.KB; q.NB = sq.NB; q.P = sq.P; q.MG = sq.MG;
-        q.epi = fd::EPI_QKV;
-        q.ss_in = (const float*)Wk(c, pl.ws_ss_a);
-        q.nss = nss;
-        q.q_out = (float*)Wk(c, pl.ws_q);
-        q.hq = d.hq; q.hkv = d.hkv; q.hd = d.hd;
-        q.rope = (const float*)P(c, sp.rope);
-        q.rope_T = d.T;
-        q.qscale = (const float*)P(c, sp.qscale) + (size_t)l * d.hkv;
-        q.kvsig = (const float*)P(c, sp.kvsig) + (size_t)l * 2 * d.hkv;
-        q.kv_fp8 = cache.fp8;
-        q.arena = layer_cache;
-        q.slot_stride = cache.slot; q.kv_stride = cache.kv; q.head_stride = cache.head; q.pos_stride = cache.pos;
+        q.epi = fd::EPI_PLANES;
+        q.y = (float*)Wk(c, pl.ws_qkv);
+        q.ld = d.qkv_n();
+        q.plane = (uint64_t)pl.Sp * d.qkv_n();
         e = timed(c, K_QKV, st, [&] { return fd::launch_gemm(q, wt, sq.R, sq.MTG, sq.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::AttnArgs at{};
-        at.q = (const float*)Wk(c, pl.ws_q);
+        at.qkv = (const float*)Wk(c, pl.ws_qkv);
+        at.P = sq.P;
+        at.nqkv = d.qkv_n();
+        at.plane = q.plane;
+        at.ss_in = (const float*)Wk(c, pl.ws_ss_a);
+        at.nss = nss;
+        at.ss_stride = pl.nss_max;
+        at.inv_d = inv_d;
+        at.eps = eps;
+        at.rope = (const float*)P(c, sp.rope);
+        at.qscale = (const float*)P(c, sp.qscale) + (size_t)l * d.hkv;
+        at.kvsig = (const float*)P(c, sp.kvsig) + (size_t)l * 2 * d.hkv;
+        at.vscale = (const float*)P(c, sp.vscale) + (size_t)l * d.hkv;
         at.arena = layer_cache;
         at.slot_stride = cache.slot; at.kv_stride = cache.kv; at.head_stride = cache.head; at.pos_stride = cache.pos;
-        at.vscale = (const float*)P(c, sp.vscale) + (size_t)l * d.hkv;
         at.active = slot_active(c);
         at.pos = slot_pos(c);
         at.pos_override = pos_override;
@@ -238,7 +239,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.part = (float*)Wk(c, pl.ws_apart);
         at.o_out = Wk(c, pl.ws_o);
         e = timed(c, K_ATTN, st, [&] {
-            return fd::launch_attn(at, wt, q.kv_fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
+            return fd::launch_attn(at, wt, cache.fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
         });
         if (e != hipSuccess) break;
 

@@ -8,7 +8,8 @@
 namespace fd {
 
 enum Epilogue : int {
-    EPI_QKV = 0,    // rows x rstd, rotary on q and k, q scaled for the softmax, k/v appended to the cache
+    EPI_PLANES = 0, // split ks stores its unnormalised sums to plane ks of y (the attention kernel
+                    // adds the planes, applies the norm, rotary and cache append)
     EPI_RESID = 1,  // x += acc; xg = act(x * g_next); per-row partial sums of x^2
     EPI_GU = 2,     // rows x rstd, h = silu(gate) * up
     EPI_F32 = 3,    // plain fp32 store
@@ -18,25 +19,14 @@ struct GemmArgs {
     const uint8_t* W;   // packed tiles [NB][KB][64 lanes][16 B]
     const void* X;      // session rows [Sp][K], activation type, fragment-packed layout
     int K, KB, NB, P, MG, MT, Sp, S;
-    float* part;        // split-K partial tiles (P > 1), summed by the reduce kernel
+    float* part;        // split-K partial tiles (P > 1): [n-group*MG + m-group][P][tiles][64][4]
     int epi;
     // row scaling by the RMS norm of the GEMM input: rstd[m] = (sum_i ss[i][m] / d + eps)^-1/2
     const float* ss_in;    // [Sp][ss_stride] partial sums of x^2 of the GEMM input rows
     int nss, ss_stride;
     float inv_d, eps;
-    // EPI_QKV
-    float* q_out;          // [Sp][hq*hd] fp32
-    int hq, hkv, hd;
-    const float* rope;     // [T][hd/2] x (cos, sin)
-    int rope_T;
-    const float* qscale;   // [hkv] for this layer
-    const float* kvsig;    // [2][hkv] for this layer (FP8 scales; unused for fp32 caches)
-    int kv_fp8;
-    uint8_t* arena;        // cache base of this layer for slot 0 (base + layer offset)
-    uint64_t slot_stride, kv_stride, head_stride, pos_stride;
-    const int* active;
-    const int* pos;
-    int pos_override;      // >= 0: every row is at this position (depth stack)
+    // EPI_PLANES
+    uint64_t plane;        // floats between consecutive split planes of y
     // EPI_RESID
     float* x;              // [Sp][ld] residual stream
     void* xg;              // [Sp][ld] act(x * g_next)
@@ -46,23 +36,34 @@ struct GemmArgs {
     // EPI_GU
     void* h_out;           // [Sp][F]
     int F;
-    // EPI_F32
-    float* y;              // [Sp][ld]
+    // EPI_F32 / EPI_PLANES
+    float* y;              // [Sp][ld] (EPI_PLANES: [P][Sp][ld])
 };
 
 struct AttnArgs {
-    const float* q;        // [Sp][hq*hd] fp32, pre-scaled by log2(e) * sigma_K / sqrt(hd)
-    const uint8_t* arena;  // cache base of this layer for slot 0
-    uint64_t slot_stride, kv_stride, head_stride, pos_stride;
+    // QKV projection of this layer: P split planes [P][Sp][nqkv] of
+    // unnormalised sums, columns [q heads | k heads | v heads] x hd
+    const float* qkv;
+    int P, nqkv;
+    uint64_t plane;
+    // attention-norm row scale: rstd[s] = (sum_i ss[s][i] / d + eps)^-1/2
+    const float* ss_in;
+    int nss, ss_stride;
+    float inv_d, eps;
+    const float* rope;     // [T][hd/2] x (cos, sin)
+    const float* qscale;   // [hkv] log2(e) * sigma_K / sqrt(hd) of this layer
+    const float* kvsig;    // [2][hkv] FP8 scales of this layer (1 for fp32 caches)
     const float* vscale;   // [hkv] sigma_V of this layer
+    uint8_t* arena;        // cache base of this layer for slot 0
+    uint64_t slot_stride, kv_stride, head_stride, pos_stride;
     const int* active;
     const int* pos;
-    int pos_override;
+    int pos_override;      // >= 0: every row is at this position (depth stack)
     int S, hq, hkv, tc, n_chunks;
-    int T;
-    int MT;                // 16-row tiles of session rows (packed output layout)                 // cache positions per slot
+    int T;                 // cache positions per slot
+    int MT;                // 16-row tiles of session rows (packed output layout)
     float* part;           // [S][hkv][n_chunks][G][hd + 2]
-    void* o_out;           // [Sp][hq*hd] activation type
+    void* o_out;           // [Sp][hq*hd] activation type, fragment-packed
 };
 
 struct EmbedArgs {
@@ -110,10 +111,12 @@ struct KvWriteArgs {
     int hkv, hd, t0, n, kv_fp8;
 };
 
-// k-tiles a GEMM wave loads per step (each k-split covers a whole number of
-// steps): two while a wave's tile count NG*MTG leaves room for the second
-// register buffer, else one.
-constexpr int gemm_unroll(int NG, int MTG) { return NG * MTG <= 20 ? 2 : 1; }
+// Depth of a GEMM wave's register ring of k-tiles: as deep as ~48
+// outstanding 16-byte-per-lane loads allow (the wave's load counter holds
+// 63), at least 2.
+constexpr int gemm_stages(int NG, int MTG) {
+    return 48 / (NG + MTG) < 2 ? 2 : (48 / (NG + MTG) > 8 ? 8 : 48 / (NG + MTG));
+}
 
 // Launchers (enqueue on `st`; return the launch error).
 hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st);

@@ -8,9 +8,6 @@
 
 namespace fd {
 
-// k-tiles a GEMM wave loads per step; mirrors gemm_unroll in the kernels.
-int gemm_unroll_tiles(int NG, int MTG) { return NG * MTG <= 20 ? 2 : 1; }
-
 GemmShape shape_with(int N, int K, int KT, int MT, int NG, int P) {
     GemmShape g;
     g.N = N;
@@ -28,9 +25,10 @@ GemmShape shape_with(int N, int K, int KT, int MT, int NG, int P) {
     return g;
 }
 
-bool valid_split(const GemmShape& g, int NG, int P) {
-    const int U = gemm_unroll_tiles(NG, g.MTG);
-    return P >= 1 && g.KB % P == 0 && (g.KB / P) % U == 0 && (g.KB / P) / U >= 4;
+// A split must divide the k-tiles evenly and leave each of a workgroup's
+// four waves at least one.
+bool valid_split(const GemmShape& g, int P) {
+    return P >= 1 && g.KB % P == 0 && g.KB / P >= 4;
 }
 
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
@@ -45,7 +43,7 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
         GemmShape base = shape_with(N, K, KT, MT, NG, 1);
         if (NG == 6 && base.MTG > 5) continue;
         for (int P = 1; P <= 64; ++P) {
-            if (!valid_split(base, NG, P)) continue;
+            if (!valid_split(base, P)) continue;
             GemmShape g = shape_with(N, K, KT, MT, NG, P);
             const int grid = g.grid();
             const int rounds = cdiv(grid, n_cu);
@@ -106,7 +104,7 @@ GemmShape tuned(GemmShape g, const char* name) {
     int P = tune_value((n + ".P").c_str(), g.P);
     if (!(NG == 4 || (NG == 6 && g.MTG <= 5))) NG = g.R;
     GemmShape base = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, 1);
-    if (!valid_split(base, NG, P)) P = valid_split(base, NG, g.P) ? g.P : 1;
+    if (!valid_split(base, P)) P = valid_split(base, g.P) ? g.P : 1;
     return shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, P);
 }
 
@@ -243,7 +241,11 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     auto take = [&](uint64_t bytes) { uint64_t o = w; w = align_up(w + std::max<uint64_t>(bytes, 4)); return o; };
     p.ws_x = take(Sp * dmax * 4);
     p.ws_xg = take(Sp * dmax * p.act_bytes);
-    p.ws_q = take(Sp * hqd * 4);
+    // QKV projection planes, one per k-split: [P][Sp][(hq + 2 hkv) hd] fp32
+    uint64_t qkv_floats = (uint64_t)p.main.qkv.P * Sp * p.main.dims.qkv_n();
+    if (p.depth)
+        qkv_floats = std::max(qkv_floats, (uint64_t)p.dstack.qkv.P * Sp * p.dstack.dims.qkv_n());
+    p.ws_qkv = take(qkv_floats * 4);
     p.ws_o = take(Sp * hqd * p.act_bytes);
     p.ws_h = take(Sp * fmax * p.act_bytes);
     p.ws_yw = take(Sp * m.d * p.act_bytes);
@@ -256,7 +258,7 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     int acnt = 1;
     auto acc_stack = [&](const StackPlan& s) {
         nss = std::max({nss, s.o.n_groups, s.down.n_groups});
-        for (const GemmShape* g : {&s.qkv, &s.o, &s.gu, &s.down}) {
+        for (const GemmShape* g : {&s.o, &s.gu, &s.down}) {  // (QKV splits write planes)
             part = std::max(part, g->part_floats);
             cnt = std::max(cnt, g->counters);
         }

@@ -87,7 +87,7 @@ struct Plan {
     // packed-weight buffer
     uint64_t packed_bytes = 0;
     // workspace layout
-    uint64_t ws_x = 0, ws_xg = 0, ws_q = 0, ws_o = 0, ws_h = 0, ws_c = 0, ws_z = 0, ws_yw = 0;
+    uint64_t ws_x = 0, ws_xg = 0, ws_qkv = 0, ws_o = 0, ws_h = 0, ws_c = 0, ws_z = 0, ws_yw = 0;
     uint64_t ws_ss_a = 0, ws_ss_f = 0, ws_part = 0, ws_cnt = 0, ws_apart = 0, ws_acnt = 0;
     uint64_t ws_dkv = 0, ws_err = 0;
     int nss_max = 0;
@@ -102,10 +102,6 @@ struct Plan {
 // Validates cfg and builds the plan.  Returns FD_OK or an error code with
 // a message in *err.
 fd_status make_plan(const fd_config& cfg, Plan* out, std::string* err);
-
-// k-tiles a GEMM wave loads per step (the kernels' own choice, mirrored
-// here so every k-split covers whole steps).
-int gemm_unroll_tiles(int NG, int MTG);
 
 // Tile choice for one projection (exposed for tests).
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu);

@@ -78,6 +78,17 @@ __device__ __forceinline__ float warp_sum_xor(float v) {
     return v;
 }
 
+// Sum over a 256-thread block in a fixed order (wave sums, then waves 0..3).
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+    v = warp_sum_xor<64>(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const float s = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return s;
+}
+
 // Stores 4 consecutive activations at p (fp32 or bf16).
 template <int WT>
 __device__ __forceinline__ void store_act4(void* p, size_t idx, f32x4 v) {
@@ -156,15 +167,17 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 //
 // Workgroup task (n-group, m-group, k-split): an n-group is NG 16-row weight
 // blocks.  The 4 waves split the k-split's tiles between them (wave w takes
-// runs of U tiles w, w+4, ...) and every wave covers all NG blocks, so each
+// tiles w, w+4, ...) and every wave covers all NG blocks, so each
 // session-row fragment is loaded from L2 once per workgroup straight into
 // the registers that feed the MFMAs, and each weight tile is read once; the
 // main loop has no LDS traffic and no barrier.  The four waves'
 // accumulators are then added through LDS in wave order (deterministic) and
-// each wave finishes every fourth tile.  With P > 1 k-splits the finished
-// tiles are partial sums, stored for gemm_reduce_kernel, which adds them in
-// split order and applies the epilogue; workgroups of one launch never
-// exchange data.
+// each wave finishes every fourth tile.
+//
+// With P > 1 k-splits the finished tiles are partial sums: each split
+// stores them and gemm_reduce_kernel adds the P partials of a tile in split
+// order before the epilogue (EPI_PLANES instead leaves one plane per split
+// for the consumer to add).  Workgroups of one launch never exchange data.
 
 template <int WT>
 struct BFrag;
@@ -222,79 +235,65 @@ __device__ __forceinline__ void rstd_phase2(const GemmArgs& a, int rows, const f
 }
 
 // Epilogue of the tiles a wave owns after the cross-wave sum: tile i =
-// wave + 4*j is (block r = i / MTG of the n-group, m-tile t = i % MTG); v[j]
-// holds rows n = (nb0 + r)*16 + 4*(lane/16) + e, column m = (mt0 + t)*16 +
-// lane%16.
-template <int WT, int NG, int MTG, int NWV>
-__device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, int ng, int mt0,
-                                            const float* s_rstd) {
+// wave + NWV*j is (block r = i / MTG of the n-group, m-tile t = i % MTG);
+// v[j] holds rows n = (nb0 + r)*16 + 4*(lane/16) + e, column m = (mt0 + t)*16
+// + lane%16.  Every load a tile needs (positions via LDS, rotary factors,
+// residual rows, gains) is issued for all owned tiles before any result is
+// stored, so the tiles' latencies overlap instead of adding up.
+template <int WT, int NG, int MTG, int NWV, int OWN>
+__device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, const int* ti, int ng,
+                                            int mt0, int t_lo, int t_hi, const float* s_rstd) {
     constexpr int NTL = NG * MTG;
-    constexpr int OWN = (NTL + NWV - 1) / NWV;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nb0 = ng * NG;
     __shared__ float s_red[NWV][MTG * 16];
+
+    // pass 1: per-tile coordinates and loads
+    int mm[OWN], nn[OWN], ml[OWN];
+    bool ok[OWN];
+    f32x4 aux0[OWN], aux1[OWN];
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+        const int i = ti[j] < 0 ? 0 : ti[j];
+        const int r = i / MTG, t = i - (i / MTG) * MTG;
+        ok[j] = ti[j] >= 0 && i < NTL && nb0 + r < a.NB;
+        ml[j] = t * 16 + (lane & 15);
+        mm[j] = mt0 * 16 + ml[j];
+        nn[j] = (nb0 + min(r, NG - 1)) * 16 + (lane >> 4) * 4;
+        aux0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aux1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!ok[j]) continue;
+        if (a.epi == EPI_RESID) {
+            aux0[j] = *(const f32x4*)(a.x + (size_t)mm[j] * a.ld + nn[j]);
+            aux1[j] = *(const f32x4*)(a.g_next + nn[j]);
+        }
+    }
+
+    // pass 2: results
     float ssum[MTG];
 #pragma unroll
     for (int t = 0; t < MTG; ++t) ssum[t] = 0.f;
-
 #pragma unroll
     for (int j = 0; j < OWN; ++j) {
-        const int i = wave + NWV * j;
-        if (i >= NTL) break;
-        const int r = i / MTG, t = i - (i / MTG) * MTG;
-        if (nb0 + r >= a.NB) continue;
-        const int mloc = t * 16 + (lane & 15);
-        const int m = mt0 * 16 + mloc;
-        const int n = (nb0 + r) * 16 + (lane >> 4) * 4;
+        if (!ok[j]) continue;
+        const int m = mm[j], n = nn[j], mloc = ml[j];
+        const int t = mloc >> 4;
         f32x4 x = v[j];
         if (a.ss_in) x *= s_rstd[mloc];
-        if (a.epi == EPI_QKV) {
-            const int hh = n / a.hd;
-            const int d0 = n - hh * a.hd;
-            const bool act = m < a.S && a.active[m];
-            int p = a.pos_override >= 0 ? a.pos_override : (m < a.S ? a.pos[m] : 0);
-            p = min(max(p, 0), a.rope_T - 1);
-            if (hh < a.hq + a.hkv) {
-                const f32x4 cs = *(const f32x4*)(a.rope + ((size_t)p * (a.hd / 2) + d0 / 2) * 2);
-                f32x4 w;
-                w[0] = x[0] * cs[0] - x[1] * cs[1];
-                w[1] = x[0] * cs[1] + x[1] * cs[0];
-                w[2] = x[2] * cs[2] - x[3] * cs[3];
-                w[3] = x[2] * cs[3] + x[3] * cs[2];
-                x = w;
-            }
-            if (hh < a.hq) {
-                const int g = hh / (a.hq / a.hkv);
-                *(f32x4*)(a.q_out + (size_t)m * a.hq * a.hd + n) = x * a.qscale[g];
-            } else if (act) {
-                const int kv = hh < a.hq + a.hkv ? 0 : 1;
-                const int g = hh - a.hq - kv * a.hkv;
-                uint8_t* dst = a.arena + (size_t)m * a.slot_stride + kv * a.kv_stride +
-                               g * a.head_stride + (size_t)p * a.pos_stride;
-                if (a.kv_fp8) {
-                    const float sg = a.kvsig[kv * a.hkv + g];
-                    uint32_t w = enc_e4m3(x[0] / sg) | (enc_e4m3(x[1] / sg) << 8) |
-                                 (enc_e4m3(x[2] / sg) << 16) | (enc_e4m3(x[3] / sg) << 24);
-                    *(uint32_t*)(dst + d0) = w;
-                } else {
-                    *(f32x4*)(dst + (size_t)d0 * 4) = x;
-                }
-            }
-        } else if (a.epi == EPI_RESID) {
-            float* xr = a.x + (size_t)m * a.ld + n;
-            f32x4 xn = *(f32x4*)xr + x;
-            *(f32x4*)xr = xn;
-            const f32x4 g = *(const f32x4*)(a.g_next + n);
-            store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * g);
+        if (a.epi == EPI_RESID) {
+            const f32x4 xn = aux0[j] + x;
+            *(f32x4*)(a.x + (size_t)m * a.ld + n) = xn;
+            store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * aux1[j]);
             const float sq = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
 #pragma unroll
             for (int tt = 0; tt < MTG; ++tt)
                 if (tt == t) ssum[tt] += sq;
         } else if (a.epi == EPI_GU) {
             const int jj = n >> 1;  // rows interleave gate_j, up_j, gate_j+1, up_j+1
-            const float h0 = x[0] / (1.0f + expf(-x[0])) * x[1];
-            const float h1 = x[2] / (1.0f + expf(-x[2])) * x[3];
+            // silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal
+            const float h0 = x[0] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x[0])) * x[1];
+            const float h1 = x[2] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x[2])) * x[3];
             if (WT) {
                 *(uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, jj, a.MT)) = f2bf(h0) | (f2bf(h1) << 16);
             } else {
@@ -315,7 +314,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, i
             if (lane < 16) s_red[wave][t * 16 + lane] = s;
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < MTG * 16; i += blockDim.x) {
+        for (int i = t_lo * 16 + threadIdx.x; i < t_hi * 16; i += blockDim.x) {
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < NWV; ++w) s += s_red[w][i];
@@ -324,7 +323,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, i
     }
 }
 
-template <int WT, int NG, int MTG, int U>
+template <int WT, int NG, int MTG, int STG>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     typedef typename BFrag<WT>::T BT;
     constexpr int NTL = NG * MTG;
@@ -336,9 +335,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     bid /= a.P;
     const int mg = bid % a.MG;
     const int ng = bid / a.MG;
-    const int kpb = a.KB / a.P;  // k-tiles per split (a multiple of U)
+    const int kpb = a.KB / a.P;  // k-tiles per split
     const int kb0 = ks * kpb;
-    const int ngrp = kpb / U;
+    // wave w takes k-tiles kb0 + w, kb0 + w + 4, ...
+    const int nmine = kpb > wave ? (kpb - wave + 3) / 4 : 0;
     const int nb0 = ng * NG;
     const int mt0 = mg * MTG;    // session rows are padded to whole m-groups
 
@@ -360,44 +360,55 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < MTG; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 A0[U][NG], A1[U][NG];
-    BT B0[U][MTG], B1[U][MTG];
-    auto load = [&](u32x4 (&A)[U][NG], BT (&B)[U][MTG], int kb) {
+    // STG-deep ring of (weight, activation) fragments in registers: while
+    // one k-tile is multiplied, the next STG-1 are in flight, which is what
+    // keeps enough bytes outstanding per CU to cover HBM latency.
+    u32x4 A[STG][NG];
+    BT B[STG][MTG];
+    auto load = [&](u32x4 (&Ad)[NG], BT (&Bd)[MTG], int j) {
+        const int kb = kb0 + wave + 4 * j;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int t = 0; t < MTG; ++t) Bd[t] = __builtin_bit_cast(BT, xp[(size_t)kb * xk + t * 64]);
 #pragma unroll
-            for (int t = 0; t < MTG; ++t) B[u][t] = __builtin_bit_cast(BT, xp[(size_t)(kb + u) * xk + t * 64]);
-#pragma unroll
-            for (int r = 0; r < NG; ++r) A[u][r] = __builtin_nontemporal_load(&wp[r][(size_t)(kb + u) * 64]);
-        }
+        for (int r = 0; r < NG; ++r) Ad[r] = __builtin_nontemporal_load(&wp[r][(size_t)kb * 64]);
     };
-    auto mma = [&](u32x4 (&A)[U][NG], BT (&B)[U][MTG]) {
+    auto mma = [&](u32x4 (&As)[NG], BT (&Bs)[MTG]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int r = 0; r < NG; ++r)
 #pragma unroll
-            for (int r = 0; r < NG; ++r)
-#pragma unroll
-                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(A[u][r], B[u][t], acc[r][t]);
+            for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(As[r], Bs[t], acc[r][t]);
     };
 
-    const bool norm_here = a.ss_in && a.P == 1;
-    int g = wave;
-    if (g < ngrp) load(A0, B0, kb0 + g * U);
-    // the norm's partial sums load while the first tiles are in flight
+    const bool norm_here = a.ss_in != nullptr;
+    // the norm's partial sums are summed first: their loads are few and
+    // short, and issuing them before the weight stream keeps the in-order
+    // load counter from holding the first weights back
     if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
-    for (; g < ngrp; g += 8) {
-        const bool n1 = g + 4 < ngrp;
-        if (n1) load(A1, B1, kb0 + (g + 4) * U);
+    // (nmine >= 1: each wave has at least one k-tile; a ring slot past the
+    // end re-reads the last tile and is never consumed)
+#pragma unroll
+    for (int s = 0; s < STG - 1; ++s) load(A[s], B[s], min(s, nmine - 1));
+    // steady state: every load of a chunk is in range, so the loads are
+    // unconditional and the compiler's wait before each product only covers
+    // the k-tile it consumes
+    int j0 = 0;
+    for (; j0 + 2 * STG - 2 < nmine; j0 += STG) {
+#pragma unroll
+        for (int s = 0; s < STG; ++s) {
+            load(A[(s + STG - 1) % STG], B[(s + STG - 1) % STG], j0 + s + STG - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(A[s], B[s]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // tail: fewer than 2*STG - 1 k-tiles remain
+#pragma unroll
+    for (int s = 0; s < 2 * STG - 2; ++s) {
+        if (j0 + s >= nmine) break;
+        if (j0 + s + STG - 1 < nmine) load(A[(s + STG - 1) % STG], B[(s + STG - 1) % STG], j0 + s + STG - 1);
         __builtin_amdgcn_sched_barrier(0);
-        mma(A0, B0);
+        mma(A[s % STG], B[s % STG]);
         __builtin_amdgcn_sched_barrier(0);
-        if (!n1) break;
-        const bool n2 = g + 8 < ngrp;
-        if (n2) load(A0, B0, kb0 + (g + 8) * U);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(A1, B1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!n2) break;
     }
 
     // sum the four waves' k-portions; wave w keeps tiles w, w+4, ...
@@ -413,7 +424,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         const int i = wave + 4 * j;
         if (i < NTL) v[j] = ((s_acc[0][i][lane] + s_acc[1][i][lane]) + s_acc[2][i][lane]) + s_acc[3][i][lane];
     }
+    if (a.epi == EPI_PLANES) {
+        // each split writes its own plane; the consumer adds them
+        float* y = a.y + (size_t)ks * a.plane;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int i = wave + 4 * j;
+            const int r = i / MTG, t = i - (i / MTG) * MTG;
+            if (i < NTL && nb0 + r < a.NB)
+                *(f32x4*)(y + (size_t)((mt0 + t) * 16 + (lane & 15)) * a.ld + (nb0 + r) * 16 + (lane >> 4) * 4) = v[j];
+        }
+        return;
+    }
     if (a.P > 1) {
+        // partial tiles of this split, [group][split][tile][64 lanes]
         f32x4* pp = (f32x4*)a.part + ((size_t)(ng * a.MG + mg) * a.P + ks) * NTL * 64 + lane;
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
@@ -422,42 +446,49 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         }
         return;
     }
+    int ti[OWN];
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) ti[j] = wave + 4 * j < NTL ? wave + 4 * j : -1;
     __syncthreads();
-    gemm_finish<WT, NG, MTG, 4>(a, v, ng, mt0, s_rstd);
+    gemm_finish<WT, NG, MTG, 4, OWN>(a, v, ti, ng, mt0, 0, MTG, s_rstd);
 }
 
-// Adds the P k-split partial tiles of each (n-group, m-group) in split order
-// and applies the epilogue; one workgroup of 16 waves per (n-group,
-// m-group), wave w finishing tiles w, w+16, ... so every wave has its loads
-// in flight at once.
-constexpr int kReduceWaves = 16;
-
+// Adds the P k-split partial tiles of one m-tile t of an (n-group, m-group)
+// in split order and applies the epilogue: one 4-wave workgroup per
+// (n-group, m-group, m-tile), wave w finishing blocks w, w+4, ... of the
+// m-tile, so the reduction is spread over many CUs.
 template <int WT, int NG, int MTG>
-__global__ __launch_bounds__(kReduceWaves * 64) void gemm_reduce_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
     constexpr int NTL = NG * MTG;
-    constexpr int OWN = (NTL + kReduceWaves - 1) / kReduceWaves;
+    constexpr int OWN = (NG + 3) / 4;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int mg = blockIdx.x % a.MG;
-    const int ng = blockIdx.x / a.MG;
+    int bid = blockIdx.x;
+    const int t = bid % MTG;
+    bid /= MTG;
+    const int mg = bid % a.MG;
+    const int ng = bid / a.MG;
     const int mt0 = mg * MTG;
-    __shared__ float s_seg[MTG * 16 * 8];
+    __shared__ float s_seg[16 * 8];
     __shared__ float s_rstd[MTG * 16];
-    if (a.ss_in) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
+    if (a.ss_in) rstd_phase1(a, (mt0 + t) * 16, 16, s_seg);
     const f32x4* pp = (const f32x4*)a.part + (size_t)(ng * a.MG + mg) * a.P * NTL * 64 + lane;
     const size_t split = (size_t)NTL * 64;
+    int ti[OWN];
     f32x4 v[OWN];
 #pragma unroll
     for (int j = 0; j < OWN; ++j) {
-        const int i = min(wave + kReduceWaves * j, NTL - 1);
+        const int r = wave + 4 * j;
+        ti[j] = r < NG ? r * MTG + t : -1;
+        const int i = r < NG ? r * MTG + t : t;
         f32x4 s = pp[(size_t)i * 64];
         for (int q = 1; q < a.P; ++q) s += pp[q * split + (size_t)i * 64];
         v[j] = s;
     }
     __syncthreads();
-    if (a.ss_in) rstd_phase2(a, MTG * 16, s_seg, s_rstd);
+    if (a.ss_in) rstd_phase2(a, 16, s_seg, s_rstd + t * 16);
     __syncthreads();
-    gemm_finish<WT, NG, MTG, kReduceWaves>(a, v, ng, mt0, s_rstd);
+    gemm_finish<WT, NG, MTG, 4, OWN>(a, v, ti, ng, mt0, t, t + 1, s_rstd);
 }
 
 // ---------------------------------------------------------------------------
@@ -516,7 +547,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     bid /= a.n_chunks;
     const int g = bid % a.hkv;
     const int s = bid / a.hkv;
-    const int hqd = a.hq * D;
     if (s >= a.S) return;
     if (!a.active[s]) {
         if (chunk == 0)
@@ -529,7 +559,110 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int nch = (n + a.tc - 1) / a.tc;
     if (chunk >= nch) return;
     const int t0 = chunk * a.tc;
-    const int t1 = min(t0 + a.tc, n);
+
+    uint8_t* kbase = a.arena + (size_t)s * a.slot_stride + (size_t)g * a.head_stride;
+    uint8_t* vbase = kbase + a.kv_stride;
+
+    // Prologue: this row's q heads of the group (and, in the chunk holding
+    // position p, the new k and v) from the QKV planes: sum the k-split
+    // planes in order, scale by the attention norm's rstd, rotate q and k by
+    // angle p * theta_i per pair (2i, 2i+1) and fold the softmax scale into
+    // q.  The new k, v are appended to the cache (FP8: code(value / sigma))
+    // and kept, as the cache will hold them (decoded codes), in LDS: the
+    // streaming loop skips position p and the merge adds it, so nothing
+    // waits for the append to land.  All loads are issued before any is used.
+    constexpr int QPH = D / 4;                  // 4-element quads per head
+    constexpr int NQ = ((G + 2) * QPH + 255) / 256;
+    constexpr int PMAX = 4;                     // planes loaded at once (more are added in rounds)
+    __shared__ float s_q[G][D];
+    __shared__ float s_kn[D], s_vn[D], s_sn[G];
+    __shared__ float s_red[4];
+    const bool own_new = chunk == nch - 1;
+    const int t1 = own_new ? n - 1 : min(t0 + a.tc, n);  // cached positions this chunk streams
+
+    // the wave's first block of keys does not depend on q: start it now
+    u32x4 raw[NIT][J];
+    auto load_blk = [&](const uint8_t* src, int base) {
+        const int tw = base + jj;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int t = tw + it * PPL;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                raw[it][j] = t < t1 ? __builtin_nontemporal_load((const u32x4*)(src + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
+                                    : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    int base = t0 + wave * SUB;
+
+    const int nquad = (own_new ? G + 2 : G) * QPH;
+    const float ssv = threadIdx.x < a.nss ? a.ss_in[(size_t)s * a.ss_stride + threadIdx.x] : 0.f;
+    float ssv2 = 0.f;
+    for (int i = threadIdx.x + 256; i < a.nss; i += 256) ssv2 += a.ss_in[(size_t)s * a.ss_stride + i];
+    f32x4 qs[NQ], cs[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int idx = threadIdx.x + 256 * k;
+        qs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        cs[k] = f32x4{1.f, 0.f, 1.f, 0.f};
+        if (idx < nquad) {
+            const int hh = idx / QPH, d0 = (idx - hh * QPH) * 4;
+            const int col = hh < G ? (g * G + hh) * D + d0 : (a.hq + (hh - G) * a.hkv + g) * D + d0;
+            const float* src = a.qkv + (size_t)s * a.nqkv + col;
+            if (hh <= G) cs[k] = *(const f32x4*)(a.rope + ((size_t)p * (D / 2) + d0 / 2) * 2);
+            for (int q0 = 0; q0 < a.P; q0 += PMAX) {
+                f32x4 pv[PMAX];
+#pragma unroll
+                for (int q = 0; q < PMAX; ++q)
+                    pv[q] = q0 + q < a.P ? *(const f32x4*)(src + (size_t)(q0 + q) * a.plane)
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < PMAX; ++q) qs[k] += pv[q];
+            }
+        }
+    }
+    const float rstd = 1.0f / sqrtf(block_sum_256(ssv + ssv2, s_red) * a.inv_d + a.eps);
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int idx = threadIdx.x + 256 * k;
+        if (idx >= nquad) continue;
+        const int hh = idx / QPH, d0 = (idx - hh * QPH) * 4;
+        f32x4 x = qs[k] * rstd;
+        if (hh <= G) {  // q heads and k: rotary
+            f32x4 w;
+            w[0] = x[0] * cs[k][0] - x[1] * cs[k][1];
+            w[1] = x[0] * cs[k][1] + x[1] * cs[k][0];
+            w[2] = x[2] * cs[k][2] - x[3] * cs[k][3];
+            w[3] = x[2] * cs[k][3] + x[3] * cs[k][2];
+            x = w;
+        }
+        if (hh < G) {
+            x *= a.qscale[g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_q[hh][d0 + e] = x[e];
+        } else {
+            const int kv = hh - G;
+            uint8_t* dst = (kv ? vbase : kbase) + (size_t)p * a.pos_stride;
+            float* keep = kv ? s_vn : s_kn;
+            if (FP8) {
+                const float sg = a.kvsig[kv * a.hkv + g];
+                const uint32_t w = enc_e4m3(x[0] / sg) | (enc_e4m3(x[1] / sg) << 8) |
+                                   (enc_e4m3(x[2] / sg) << 16) | (enc_e4m3(x[3] / sg) << 24);
+                *(uint32_t*)(dst + d0) = w;
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+                keep[d0 + 0] = lo[0];
+                keep[d0 + 1] = lo[1];
+                keep[d0 + 2] = hi[0];
+                keep[d0 + 3] = hi[1];
+            } else {
+                *(f32x4*)(dst + (size_t)d0 * 4) = x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) keep[d0 + e] = x[e];
+            }
+        }
+    }
+    __syncthreads();
 
     float qv[G][E];
 #pragma unroll
@@ -537,18 +670,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int i = 0; i < VE; i += 4) {
-                const f32x4 v = *(const f32x4*)(a.q + (size_t)s * hqd + (size_t)(g * G + h) * D +
-                                                (c + LPP * j) * VE + i);
-                qv[h][j * VE + i + 0] = v[0];
-                qv[h][j * VE + i + 1] = v[1];
-                qv[h][j * VE + i + 2] = v[2];
-                qv[h][j * VE + i + 3] = v[3];
-            }
+            for (int i = 0; i < VE; ++i) qv[h][j * VE + i] = s_q[h][(c + LPP * j) * VE + i];
 
-    const uint8_t* kbase = a.arena + (size_t)s * a.slot_stride + (size_t)g * a.head_stride;
-    const uint8_t* vbase = kbase + a.kv_stride;
-
+    if (base < t1) load_blk(kbase, base);
     float mrun[G], lrun[G], acc[G][E];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -558,18 +682,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
 
-    for (int base = t0 + wave * SUB; base < t1; base += 4 * SUB) {
+    for (; base < t1; base += 4 * SUB) {
         const int tw = base + jj;  // this lane's first position in the block
         float sc[NIT][G];
-        u32x4 raw[NIT][J];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int t = tw + it * PPL;
-#pragma unroll
-            for (int j = 0; j < J; ++j)
-                raw[it][j] = t < t1 ? __builtin_nontemporal_load((const u32x4*)(kbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
-                                    : u32x4{0u, 0u, 0u, 0u};
-        }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             float kvf[E];
@@ -585,14 +700,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             }
         }
         // values of this block: issue the loads before the softmax update
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int t = tw + it * PPL;
-#pragma unroll
-            for (int j = 0; j < J; ++j)
-                raw[it][j] = t < t1 ? __builtin_nontemporal_load((const u32x4*)(vbase + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
-                                    : u32x4{0u, 0u, 0u, 0u};
-        }
+        load_blk(vbase, base);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float m = sc[0][h];
@@ -623,6 +731,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[h][e] += sc[it][h] * vf[e];
         }
+        if (base + 4 * SUB < t1) load_blk(kbase, base + 4 * SUB);
     }
     // reduce over the wave's position groups (lanes with equal c)
 #pragma unroll
@@ -638,6 +747,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         }
     }
 
+    // score of the new position (one wave per query head)
+    if (own_new && wave < G) {
+        float dq = 0.f;
+        for (int i = lane; i < D; i += 64) dq += s_q[wave][i] * s_kn[i];
+        dq = warp_sum_xor<64>(dq);
+        if (lane == 0) s_sn[wave] = dq;
+    }
     __shared__ float s_m[4][G];
     __shared__ float s_l[4][G];
     __shared__ float s_acc[4][G][D];
@@ -659,13 +775,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const float* vs = a.vscale;
     for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
         const int h = i / D, d = i - h * D;
-        const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+        float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+        if (own_new) M = fmaxf(M, s_sn[h]);
         float O = 0.f, L = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);  // 0 for a wave without positions
             O += f * s_acc[w][h][d];
             L += f * s_l[w][h];
+        }
+        if (own_new) {
+            const float f = __builtin_amdgcn_exp2f(s_sn[h] - M);
+            O += f * s_vn[d];
+            L += f;
         }
         if (nch == 1) {
             store_act1<WT>(a.o_out, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
@@ -709,15 +831,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // row kernels
 
-__device__ __forceinline__ float block_sum_256(float v, float* red) {
-    v = warp_sum_xor<64>(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    const float s = ((red[0] + red[1]) + red[2]) + red[3];
-    __syncthreads();
-    return s;
-}
 
 template <int WT>
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
@@ -821,12 +934,12 @@ hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
 
 template <int WT, int NG>
 static hipError_t gemm_ng(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
-    const int red = grid / a.P;
     switch (MTG) {
 #define FD_G(MT)                                                                                         \
     case MT:                                                                                             \
-        hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_unroll(NG, MT)>), dim3(grid), dim3(256), 0, st, a); \
-        if (a.P > 1) hipLaunchKernelGGL((gemm_reduce_kernel<WT, NG, MT>), dim3(red), dim3(kReduceWaves * 64), 0, st, a); \
+        hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_stages(NG, MT)>), dim3(grid), dim3(256), 0, st, a); \
+        if (a.P > 1 && a.epi != EPI_PLANES)                                                          \
+            hipLaunchKernelGGL((gemm_reduce_kernel<WT, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
         break;
         FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
 #undef FD_G
@@ -837,12 +950,12 @@ static hipError_t gemm_ng(const GemmArgs& a, int MTG, int grid, hipStream_t st) 
 
 template <int WT>
 static hipError_t gemm_ng4(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
-    const int red = grid / a.P;
     switch (MTG) {
 #define FD_G(MT)                                                                                        \
     case MT:                                                                                            \
-        hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_unroll(4, MT)>), dim3(grid), dim3(256), 0, st, a); \
-        if (a.P > 1) hipLaunchKernelGGL((gemm_reduce_kernel<WT, 4, MT>), dim3(red), dim3(kReduceWaves * 64), 0, st, a); \
+        hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_stages(4, MT)>), dim3(grid), dim3(256), 0, st, a); \
+        if (a.P > 1 && a.epi != EPI_PLANES)                                                          \
+            hipLaunchKernelGGL((gemm_reduce_kernel<WT, 4, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
         break;
         FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5) FD_G(6) FD_G(7) FD_G(8)
 #undef FD_G
