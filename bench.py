@@ -243,6 +243,89 @@ def cpu_baseline(cfg, pos, layers, sessions):
                       f"best of 2 steps ({t:.2f} s), scaled by {cfg['n_layers']}/{layers} layers"}
 
 
+COPY_BYTES = 1 << 30
+
+
+def calibration_copy():
+    """One plain copy kernel of known size (1 GiB read, 1 GiB written: an
+    elementwise multiply by one), run before the steps in counter passes so
+    the HBM counters can be scaled against known bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, cmd):
+    """Per-dispatch HBM bytes of the attention kernel from one FETCH_SIZE and
+    one WRITE_SIZE pass (KiB per dispatch), each scaled by the counter's
+    reading for the 1 GiB calibration copy; updates profiles/counters.json
+    and returns a markdown summary."""
+    import numpy as np
+
+    def per_kernel(path):
+        out = {}
+        for r in _read_csv(path):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy = [k for k in f if "MulFunctor" in k]
+    if not copy:
+        raise SystemExit("no calibration copy in the fetch pass")
+    cf = max(max(f[k]) for k in copy) * 1024.0
+    cw = max(max(w.get(k, [0.0])) for k in copy) * 1024.0
+    sf, sw = COPY_BYTES / cf, COPY_BYTES / cw
+    lines = [f"# HBM traffic per dispatch, {workload}", "", "Command (each counter in its own pass):", "",
+             "```", cmd, "```", "",
+             f"Calibration copy ({COPY_BYTES} B read + written): FETCH_SIZE {cf / 1024:.0f} KiB -> "
+             f"scale {sf:.3f}; WRITE_SIZE {cw / 1024:.0f} KiB -> scale {sw:.3f}.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | scaled HBM bytes per dispatch |",
+             "|---|---|---|---|---|"]
+    data = {}
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        data = {}
+    for k in sorted(f):
+        if not k.startswith("void fd::"):
+            continue
+        fm = float(np.mean(f[k]))
+        wm = float(np.mean(w.get(k, [0.0])))
+        b = fm * 1024 * sf + wm * 1024 * sw
+        short = k.replace("void fd::", "").split("(")[0]
+        lines.append(f"| `{short}` | {len(f[k])} | {fm:.0f} | {wm:.0f} | {b:.4g} |")
+        if short.startswith("attn_kernel"):
+            data[f"attention@{workload}"] = {"hbm_bytes_per_launch": b,
+                                             "fetch_kib": fm, "write_kib": wm,
+                                             "scale_fetch": sf, "scale_write": sw,
+                                             "kernel_source_sha": _kernel_source_sha()}
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    return "\n".join(lines) + "\n"
+
+
+def summarize_trace(stats_csv, cmd, title):
+    """Markdown table of a rocprofv3 --kernel-trace --stats summary."""
+    rows = _read_csv(stats_csv)
+    lines = [f"# {title}", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | total ms | average us | % of GPU time |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +336,21 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--cpu-sessions", type=int, default=2)
     ap.add_argument("--no-max-s", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB copy kernel first (scale for HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two counter passes of this workload and exit")
+    ap.add_argument("--summarize-trace", metavar="STATS_CSV",
+                    help="summarise a kernel-trace stats file and exit")
+    ap.add_argument("--cmd", default="", help="command recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(summarize_pmc(*args.summarize_pmc, args.config, args.cmd), end="")
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.cmd,
+                              f"Kernel time per step, {args.config}"), end="")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this decode step runs on one GPU; sessions shard across GPUs "
@@ -269,6 +366,8 @@ def main():
     pos = cfg.get("position", cfg["max_context"] - 1)
     S = cfg["max_slots"]
 
+    if args.calibrate_copy:
+        calibration_copy()
     probe = read_probe_gbs()
     log(f"read probe: {probe:.0f} GB/s")
     r = run_gpu(cfg, pos, args.steps, args.warmup)

@@ -207,6 +207,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         q.W = P(c, lo.qkv);
         q.X = Wk(c, pl.ws_xg);
         q.K = sq.K; q.KB = sq.KB; q.NB = sq.NB; q.P = sq.P; q.MG = sq.MG;
+        q.X_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         q.epi = fd::EPI_PLANES;
         q.y = (float*)Wk(c, pl.ws_qkv);
         q.ld = d.qkv_n();
@@ -238,6 +239,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.MT = pl.MT;
         at.part = (float*)Wk(c, pl.ws_apart);
         at.o_out = Wk(c, pl.ws_o);
+        at.o_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
         e = timed(c, K_ATTN, st, [&] {
             return fd::launch_attn(at, wt, cache.fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
         });
@@ -247,11 +249,13 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         const fd::GemmShape& so = sp.o;
         o.W = P(c, lo.o);
         o.X = Wk(c, pl.ws_o);
+        o.X_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
         o.K = so.K; o.KB = so.KB; o.NB = so.NB; o.P = so.P; o.MG = so.MG;
         o.epi = fd::EPI_RESID;
         o.x = (float*)Wk(c, pl.ws_x);
         o.xg = Wk(c, pl.ws_xg);
         o.g_next = (const float*)P(c, lo.g_ffn);
+        o.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         o.ss_out = (float*)Wk(c, pl.ws_ss_f);
         o.ld = d.d;
         e = timed(c, K_O, st, [&] { return fd::launch_gemm(o, wt, so.R, so.MTG, so.grid(), st); });
@@ -265,7 +269,9 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         u.epi = fd::EPI_GU;
         u.ss_in = (const float*)Wk(c, pl.ws_ss_f);
         u.nss = so.n_groups;
+        u.X_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         u.h_out = Wk(c, pl.ws_h);
+        u.h_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
         u.F = d.f;
         e = timed(c, K_GU, st, [&] { return fd::launch_gemm(u, wt, su.R, su.MTG, su.grid(), st); });
         if (e != hipSuccess) break;
@@ -274,11 +280,13 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         const fd::GemmShape& sd = sp.down;
         dn.W = P(c, lo.down);
         dn.X = Wk(c, pl.ws_h);
+        dn.X_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
         dn.K = sd.K; dn.KB = sd.KB; dn.NB = sd.NB; dn.P = sd.P; dn.MG = sd.MG;
         dn.epi = fd::EPI_RESID;
         dn.x = (float*)Wk(c, pl.ws_x);
         dn.xg = Wk(c, pl.ws_xg);
         dn.g_next = (const float*)P(c, l + 1 < d.L ? sp.layers[l + 1].g_attn : sp.g_final);
+        dn.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         dn.ss_out = (float*)Wk(c, pl.ws_ss_a);
         dn.ld = d.d;
         e = timed(c, K_DOWN, st, [&] { return fd::launch_gemm(dn, wt, sd.R, sd.MTG, sd.grid(), st); });
@@ -454,6 +462,7 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
     em.MT = pl.MT;
     em.x = (float*)Wk(c, pl.ws_x);
     em.xg = Wk(c, pl.ws_xg);
+    em.xg_lo = pl.wt ? Wk(c, pl.ws_xg_lo) : nullptr;
     em.g = (const float*)P(c, md.L > 0 ? mp.layers[0].g_attn : mp.g_final);
     em.ss_out = (float*)Wk(c, pl.ws_ss_a);
     em.ss_stride = pl.nss_max;

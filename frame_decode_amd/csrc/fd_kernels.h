@@ -18,6 +18,7 @@ enum Epilogue : int {
 struct GemmArgs {
     const uint8_t* W;   // packed tiles [NB][KB][64 lanes][16 B]
     const void* X;      // session rows [Sp][K], activation type, fragment-packed layout
+    const void* X_lo;   // optional (bf16 only): low parts, the input being X + X_lo
     int K, KB, NB, P, MG, MT, Sp, S;
     float* part;        // split-K partial tiles (P > 1): [n-group*MG + m-group][P][tiles][64][4]
     int epi;
@@ -30,11 +31,13 @@ struct GemmArgs {
     // EPI_RESID
     float* x;              // [Sp][ld] residual stream
     void* xg;              // [Sp][ld] act(x * g_next)
+    void* xg_lo;           // optional (bf16): x * g_next - xg, rounded to bf16
     const float* g_next;
     float* ss_out;         // [Sp][ss_stride], entry n-group
     int ld;
     // EPI_GU
     void* h_out;           // [Sp][F]
+    void* h_lo;            // optional (bf16): h - h_out, rounded to bf16
     int F;
     // EPI_F32 / EPI_PLANES
     float* y;              // [Sp][ld] (EPI_PLANES: [P][Sp][ld])
@@ -64,6 +67,7 @@ struct AttnArgs {
     int MT;                // 16-row tiles of session rows (packed output layout)
     float* part;           // [S][hkv][n_chunks][G][hd + 2]
     void* o_out;           // [Sp][hq*hd] activation type, fragment-packed
+    void* o_lo;            // optional (bf16): o - o_out, rounded to bf16
 };
 
 struct EmbedArgs {
@@ -74,6 +78,7 @@ struct EmbedArgs {
     int S, d, MT;
     float* x;              // [Sp][d]
     void* xg;              // [Sp][d]
+    void* xg_lo;           // optional (bf16): x * g - xg, rounded to bf16
     const float* g;        // gain of the first norm
     float* ss_out;         // [Sp][ss_stride], entry 0
     int ss_stride;
@@ -113,9 +118,9 @@ struct KvWriteArgs {
 
 // Depth of a GEMM wave's register ring of k-tiles: as deep as ~48
 // outstanding 16-byte-per-lane loads allow (the wave's load counter holds
-// 63), at least 2.
-constexpr int gemm_stages(int NG, int MTG) {
-    return 48 / (NG + MTG) < 2 ? 2 : (48 / (NG + MTG) > 8 ? 8 : 48 / (NG + MTG));
+// 63), at least 2.  SX: the session rows come as two bf16 parts.
+constexpr int gemm_stages(int NG, int MTG, int SX = 0) {
+    return 48 / (NG + MTG * (1 + SX)) < 2 ? 2 : (48 / (NG + MTG * (1 + SX)) > 8 ? 8 : 48 / (NG + MTG * (1 + SX)));
 }
 
 // Launchers (enqueue on `st`; return the launch error).

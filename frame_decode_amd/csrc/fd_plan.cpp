@@ -248,6 +248,14 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     p.ws_qkv = take(qkv_floats * 4);
     p.ws_o = take(Sp * hqd * p.act_bytes);
     p.ws_h = take(Sp * fmax * p.act_bytes);
+    // bf16 low parts of every projection input: in bf16 stacks each GEMM
+    // takes its session rows as two bf16 parts (hi + lo, ~16 significant
+    // bits), so the activations between phases lose no more than fp32
+    // rounding would and the FP8 codes of new cache entries are the ones an
+    // fp32 evaluation picks
+    p.ws_xg_lo = take(p.wt ? Sp * dmax * 2 : 0);
+    p.ws_h_lo = take(p.wt ? Sp * fmax * 2 : 0);
+    p.ws_o_lo = take(p.wt ? Sp * hqd * 2 : 0);
     p.ws_yw = take(Sp * m.d * p.act_bytes);
     p.ws_c = take(Sp * std::max(dd, 1) * 4);
     p.ws_z = take(Sp * std::max(dd, 1) * 4);

@@ -89,7 +89,7 @@ struct Plan {
     // workspace layout
     uint64_t ws_x = 0, ws_xg = 0, ws_qkv = 0, ws_o = 0, ws_h = 0, ws_c = 0, ws_z = 0, ws_yw = 0;
     uint64_t ws_ss_a = 0, ws_ss_f = 0, ws_part = 0, ws_cnt = 0, ws_apart = 0, ws_acnt = 0;
-    uint64_t ws_dkv = 0, ws_err = 0;
+    uint64_t ws_dkv = 0, ws_err = 0, ws_xg_lo = 0, ws_h_lo = 0, ws_o_lo = 0;
     int nss_max = 0;
     uint64_t workspace_bytes = 0;
     // cache arena

@@ -102,6 +102,35 @@ __device__ __forceinline__ void store_act4(void* p, size_t idx, f32x4 v) {
     }
 }
 
+// Stores 4 consecutive values as bf16 high parts at hi and the bf16-rounded
+// remainders at lo (hi + lo carries ~16 significant bits).
+__device__ __forceinline__ void store_split4(void* hi, void* lo, size_t idx, f32x4 v) {
+    u32x2 wh, wl;
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = f2bf(v[e]);
+    wh[0] = b[0] | (b[1] << 16);
+    wh[1] = b[2] | (b[3] << 16);
+    wl[0] = f2bf(v[0] - bf2f(b[0])) | (f2bf(v[1] - bf2f(b[1])) << 16);
+    wl[1] = f2bf(v[2] - bf2f(b[2])) | (f2bf(v[3] - bf2f(b[3])) << 16);
+    *(u32x2*)((uint16_t*)hi + idx) = wh;
+    *(u32x2*)((uint16_t*)lo + idx) = wl;
+}
+
+__device__ __forceinline__ void store_split1(void* hi, void* lo, size_t idx, float v) {
+    const uint32_t b = f2bf(v);
+    ((uint16_t*)hi)[idx] = (uint16_t)b;
+    ((uint16_t*)lo)[idx] = (uint16_t)f2bf(v - bf2f(b));
+}
+
+// Stores one activation (with its bf16 remainder when lo is given).
+template <int WT>
+__device__ __forceinline__ void store_act1x(void* p, void* lo, size_t idx, float v) {
+    if (WT && lo) store_split1(p, lo, idx, v);
+    else if (WT) ((uint16_t*)p)[idx] = (uint16_t)f2bf(v);
+    else ((float*)p)[idx] = v;
+}
+
 template <int WT>
 __device__ __forceinline__ void store_act1(void* p, size_t idx, float v) {
     if (WT) ((uint16_t*)p)[idx] = (uint16_t)f2bf(v);
@@ -284,7 +313,8 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
         if (a.epi == EPI_RESID) {
             const f32x4 xn = aux0[j] + x;
             *(f32x4*)(a.x + (size_t)m * a.ld + n) = xn;
-            store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * aux1[j]);
+            if (WT && a.xg_lo) store_split4(a.xg, a.xg_lo, xoff<WT>(m, n, a.MT), xn * aux1[j]);
+            else store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * aux1[j]);
             const float sq = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
 #pragma unroll
             for (int tt = 0; tt < MTG; ++tt)
@@ -295,7 +325,11 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
             const float h0 = x[0] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x[0])) * x[1];
             const float h1 = x[2] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x[2])) * x[3];
             if (WT) {
-                *(uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, jj, a.MT)) = f2bf(h0) | (f2bf(h1) << 16);
+                const uint32_t b0 = f2bf(h0), b1 = f2bf(h1);
+                *(uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, jj, a.MT)) = b0 | (b1 << 16);
+                if (a.h_lo)
+                    *(uint32_t*)((uint16_t*)a.h_lo + xoff<WT>(m, jj, a.MT)) =
+                        f2bf(h0 - bf2f(b0)) | (f2bf(h1 - bf2f(b1)) << 16);
             } else {
                 *(f32x2*)((float*)a.h_out + xoff<WT>(m, jj, a.MT)) = f32x2{h0, h1};
             }
@@ -323,7 +357,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
     }
 }
 
-template <int WT, int NG, int MTG, int STG>
+template <int WT, int NG, int MTG, int STG, int SX>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     typedef typename BFrag<WT>::T BT;
     constexpr int NTL = NG * MTG;
@@ -352,6 +386,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         wp[r] = (const u32x4*)(a.W + (size_t)min(nb0 + r, a.NB - 1) * a.KB * 1024) + lane;
     // fragment (k-tile kb, m-tile mt) is 1 KiB at ((kb*MT + mt)*64 + lane) * 16 bytes
     const u32x4* xp = (const u32x4*)a.X + (size_t)mt0 * 64 + lane;
+    const u32x4* xlp = SX ? (const u32x4*)a.X_lo + (size_t)mt0 * 64 + lane : xp;
     const size_t xk = (size_t)a.MT * 64;
 
     f32x4 acc[NG][MTG];
@@ -363,20 +398,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     // STG-deep ring of (weight, activation) fragments in registers: while
     // one k-tile is multiplied, the next STG-1 are in flight, which is what
     // keeps enough bytes outstanding per CU to cover HBM latency.
+    // (SX: B[.][MTG + t] holds the low part of m-tile t)
+    constexpr int NB_ = MTG * (1 + SX);
     u32x4 A[STG][NG];
-    BT B[STG][MTG];
-    auto load = [&](u32x4 (&Ad)[NG], BT (&Bd)[MTG], int j) {
+    BT B[STG][NB_];
+    auto load = [&](u32x4 (&Ad)[NG], BT (&Bd)[NB_], int j) {
         const int kb = kb0 + wave + 4 * j;
 #pragma unroll
         for (int t = 0; t < MTG; ++t) Bd[t] = __builtin_bit_cast(BT, xp[(size_t)kb * xk + t * 64]);
+        if constexpr (SX) {
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) Bd[MTG + t] = __builtin_bit_cast(BT, xlp[(size_t)kb * xk + t * 64]);
+        }
 #pragma unroll
         for (int r = 0; r < NG; ++r) Ad[r] = __builtin_nontemporal_load(&wp[r][(size_t)kb * 64]);
     };
-    auto mma = [&](u32x4 (&As)[NG], BT (&Bs)[MTG]) {
+    // (high parts of every tile first, then low parts: consecutive products
+    // never chain on one accumulator)
+    auto mma = [&](u32x4 (&As)[NG], BT (&Bs)[NB_]) {
 #pragma unroll
-        for (int r = 0; r < NG; ++r)
+        for (int h = 0; h <= SX; ++h)
 #pragma unroll
-            for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(As[r], Bs[t], acc[r][t]);
+            for (int r = 0; r < NG; ++r)
+#pragma unroll
+                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(As[r], Bs[h * MTG + t], acc[r][t]);
     };
 
     const bool norm_here = a.ss_in != nullptr;
@@ -551,7 +596,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     if (!a.active[s]) {
         if (chunk == 0)
             for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-                store_act1<WT>(a.o_out, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
+                store_act1x<WT>(a.o_out, a.o_lo, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
         return;
     }
     const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
@@ -790,7 +835,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             L += f;
         }
         if (nch == 1) {
-            store_act1<WT>(a.o_out, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
+            store_act1x<WT>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
         } else {
             float* part = a.part + (((size_t)(s * a.hkv + g) * a.n_chunks + chunk) * G + h) * (D + 2);
             part[d] = O;
@@ -824,7 +869,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
             L += w * part[q * cs + D + 1];
             O += w * part[q * cs + d];
         }
-        store_act1<WT>(a.o_out, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
+        store_act1x<WT>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
     }
 }
 
@@ -850,7 +895,8 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
             }
         }
         *(f32x4*)(a.x + (size_t)m * a.d + i) = v;
-        store_act4<WT>(a.xg, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
+        if (WT && a.xg_lo) store_split4(a.xg, a.xg_lo, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
+        else store_act4<WT>(a.xg, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
     ss = block_sum_256(ss, red);
@@ -937,7 +983,10 @@ static hipError_t gemm_ng(const GemmArgs& a, int MTG, int grid, hipStream_t st) 
     switch (MTG) {
 #define FD_G(MT)                                                                                         \
     case MT:                                                                                             \
-        hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_stages(NG, MT)>), dim3(grid), dim3(256), 0, st, a); \
+        if (WT && a.X_lo)                                                                              \
+            hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_stages(NG, MT, WT), WT>), dim3(grid), dim3(256), 0, st, a); \
+        else                                                                                           \
+            hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_stages(NG, MT), 0>), dim3(grid), dim3(256), 0, st, a); \
         if (a.P > 1 && a.epi != EPI_PLANES)                                                          \
             hipLaunchKernelGGL((gemm_reduce_kernel<WT, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
         break;
@@ -953,7 +1002,10 @@ static hipError_t gemm_ng4(const GemmArgs& a, int MTG, int grid, hipStream_t st)
     switch (MTG) {
 #define FD_G(MT)                                                                                        \
     case MT:                                                                                            \
-        hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_stages(4, MT)>), dim3(grid), dim3(256), 0, st, a); \
+        if (WT && a.X_lo)                                                                              \
+            hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_stages(4, MT, WT), WT>), dim3(grid), dim3(256), 0, st, a); \
+        else                                                                                           \
+            hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_stages(4, MT), 0>), dim3(grid), dim3(256), 0, st, a); \
         if (a.P > 1 && a.epi != EPI_PLANES)                                                          \
             hipLaunchKernelGGL((gemm_reduce_kernel<WT, 4, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
         break;
