@@ -136,15 +136,20 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     // or 32 bytes (fp32) of a position's head vector
     // Chunks of the window per (slot, kv head): one workgroup per chunk.
     // A single chunk (no merge kernel) when the slot x head pairs alone give
-    // about four workgroups per CU; otherwise enough chunks to get there.
+    // about four workgroups per CU; otherwise enough chunks to get there,
+    // but no chunk shorter than ~512 KiB of keys and values (per-workgroup
+    // set-up and merge costs would dominate).
     AttnShape& a = sp.attn;
     a.lpp = kv_fp8 ? dims.hd / 16 : dims.hd / 8;
     const int round = kWaves * kAttnIters * (64 / a.lpp);
     const int pairs = std::max(1, S * dims.hkv);
-    int want = std::max(1, cdiv(1024, pairs));
+    const int64_t window_bytes = (int64_t)dims.T * 2 * dims.hd * (kv_fp8 ? 1 : 4);
+    int want = std::max(1, std::min(cdiv(1024, pairs), (int)((window_bytes + (512 << 10) - 1) >> 19)));
     want = std::max(1, tune_value("attn.chunks", want));
     a.tc = want == 1 ? cdiv(dims.T, round) * round
                      : std::max(round, cdiv(dims.T, want) / round * round);
+    // the merge kernel holds one chunk per thread: at most 256 chunks
+    a.tc = std::max(a.tc, cdiv(cdiv(dims.T, 256), round) * round);
     a.n_chunks = cdiv(dims.T, a.tc);
 }
 

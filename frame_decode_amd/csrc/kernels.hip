@@ -847,28 +847,53 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
 }
 
-// Merges the chunks of every (slot, query head) in chunk order.
+// Merges the chunks of one (slot, query head) in chunk order: one
+// workgroup per (slot, kv head, query head of the group); the chunks'
+// (max, sum) pairs are read once into LDS, then each thread adds its
+// elements' chunk values (8 loads in flight per step).
 template <int WT, int D, int G>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-    const int g = blockIdx.x % a.hkv;
-    const int s = blockIdx.x / a.hkv;
+    int bid = blockIdx.x;
+    const int h = bid % G;
+    bid /= G;
+    const int g = bid % a.hkv;
+    const int s = bid / a.hkv;
     if (s >= a.S || !a.active[s]) return;  // inactive rows were zeroed by the attention kernel
     const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
     const int nch = (p + 1 + a.tc - 1) / a.tc;
     if (nch == 1) return;  // written directly
-    const int hqd = a.hq * D;
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-        const int h = i / D, d = i - h * D;
-        const float* part = a.part + ((size_t)(s * a.hkv + g) * a.n_chunks * G + h) * (D + 2);
-        const size_t cs = (size_t)G * (D + 2);
-        float M = -INFINITY;
-        for (int q = 0; q < nch; ++q) M = fmaxf(M, part[q * cs + D]);
-        float L = 0.f, O = 0.f;
-        for (int q = 0; q < nch; ++q) {
-            const float w = __builtin_amdgcn_exp2f(part[q * cs + D] - M);
-            L += w * part[q * cs + D + 1];
-            O += w * part[q * cs + d];
+    __shared__ float s_w[256];
+    __shared__ float s_red[4], s_lsum[4];
+    const float* part = a.part + ((size_t)(s * a.hkv + g) * a.n_chunks * G + h) * (D + 2);
+    const size_t cs = (size_t)G * (D + 2);
+    // chunk weights exp2(M_q - M) (nch <= blockDim: chunks are at least one
+    // block of positions per wave, so a window of T <= 65536 has < 256)
+    const int q = threadIdx.x;
+    const float mq = q < nch ? part[q * cs + D] : -INFINITY;
+    const float lq = q < nch ? part[q * cs + D + 1] : 0.f;
+    float m = mq;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float wq = q < nch ? __builtin_amdgcn_exp2f(mq - M) : 0.f;
+    s_w[q] = wq;
+    const float lw = warp_sum_xor<64>(wq * lq);
+    if ((threadIdx.x & 63) == 0) s_lsum[threadIdx.x >> 6] = lw;
+    __syncthreads();
+    const float L = ((s_lsum[0] + s_lsum[1]) + s_lsum[2]) + s_lsum[3];
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float O = 0.f;
+        int c = 0;
+        for (; c + 8 <= nch; c += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[(c + u) * cs + d];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) O += s_w[c + u] * v[u];
         }
+        for (; c < nch; ++c) O += s_w[c] * part[c * cs + d];
         store_act1x<WT>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
     }
 }
@@ -1024,7 +1049,7 @@ hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hip
 
 template <int WT, int FP8, int D>
 static hipError_t attn_g(const AttnArgs& a, int G, int grid, hipStream_t st) {
-    const int cgrid = a.S * a.hkv;
+    const int cgrid = a.S * a.hkv * G;
     switch (G) {
 #define FD_A(GG)                                                                                       \
     case GG:                                                                                           \

@@ -2,6 +2,8 @@
 at sizes the oracle finishes in seconds (several tiles, ragged tails,
 multi-chunk attention).  Tolerances: max relative row error 1e-3 on the
 fp32 path, 2e-2 on the bf16/FP8 path; cache indexing bit-exact."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -176,7 +178,13 @@ def test_bf16_fp8_ragged_multichunk():
                               d_ffn=1536, max_slots=9, max_context=700)
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 1, 255, 256, 257, 300, 511, 690]
-    ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
+    # this window is short enough for one chunk by default: ask the plan
+    # for three (256-position chunks) so the chunk merge is exercised
+    os.environ["FD_TUNE"] = "attn.chunks=3"
+    try:
+        ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
+    finally:
+        del os.environ["FD_TUNE"]
     _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
 
 
