@@ -315,6 +315,37 @@ def summarize_pmc(fetch_csv, write_csv, workload, cmd):
     return "\n".join(lines) + "\n"
 
 
+def summarize_mfma(csv_path, workload, cmd):
+    """Matrix-core use per GEMM dispatch from one counter pass:
+    SQ_VALU_MFMA_BUSY_CYCLES / (GPU-active cycles x 1024 SIMDs), and the MFMA
+    flops the dispatch issued (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512).  The
+    collected GRBM_GUI_ACTIVE is the sum over the 8 XCDs, so the GPU-active
+    cycle count is that sum / 8."""
+    per = {}
+    for r in _read_csv(csv_path):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    agg = {}
+    for (name, _), c in per.items():
+        if not name.startswith("void fd::gemm_kernel"):
+            continue
+        a = agg.setdefault(name, {"n": 0, "busy": 0.0, "active": 0.0, "mops": 0.0})
+        a["n"] += 1
+        a["busy"] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a["active"] += c.get("GRBM_GUI_ACTIVE", 0.0)
+        a["mops"] += c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+    lines = [f"# Matrix-core use of the projections, {workload}", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | dispatches | MFMA busy / (GPU-active cycles x 1024 SIMDs) | MFMA flops per dispatch |",
+             "|---|---|---|---|"]
+    for name, a in sorted(agg.items()):
+        util = a["busy"] / (a["active"] / 8 * 1024) if a["active"] else float("nan")
+        short = name.replace("void fd::", "").split("(")[0]
+        lines.append(f"| `{short}` | {a['n']} | {100 * util:.1f}% | {a['mops'] * 512 / a['n']:.3g} |")
+    lines += ["", "The projections are bound by HBM bandwidth (each weight byte is read once per step and "
+              "multiplies 80 session rows), so the matrix cores are expected to idle most of the time."]
+    return "\n".join(lines) + "\n"
+
+
 def summarize_trace(stats_csv, cmd, title):
     """Markdown table of a rocprofv3 --kernel-trace --stats summary."""
     rows = _read_csv(stats_csv)
@@ -342,10 +373,15 @@ def main():
                     help="summarise two counter passes of this workload and exit")
     ap.add_argument("--summarize-trace", metavar="STATS_CSV",
                     help="summarise a kernel-trace stats file and exit")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="summarise a matrix-core counter pass and exit")
     ap.add_argument("--cmd", default="", help="command recorded in a summary")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc, args.config, args.cmd), end="")
+        return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma, args.config, args.cmd), end="")
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.cmd,
