@@ -367,6 +367,8 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--cpu-sessions", type=int, default=2)
     ap.add_argument("--no-max-s", action="store_true")
+    ap.add_argument("--exec-mode", type=int, default=0,
+                    help="0: kernel sequence per step; 1: persistent walk of the depth stack")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB copy kernel first (scale for HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -399,6 +401,7 @@ def main():
     from frame_decode_amd import roofline as rf
     torch.cuda.set_device(0)
     cfg = synth.get_config(args.config)
+    cfg["exec_mode"] = args.exec_mode
     pos = cfg.get("position", cfg["max_context"] - 1)
     S = cfg["max_slots"]
 
@@ -454,7 +457,8 @@ def main():
         "config": {"workload": args.config, "layers": cfg["n_layers"], "d_model": cfg["d_model"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} (kv {cfg['n_kv_heads']})",
                    "d_ffn": cfg["d_ffn"], "sessions": S, "frame_index": pos,
-                   "weights": cfg["w_dtype"], "cache": cfg["kv_dtype"]},
+                   "weights": cfg["w_dtype"], "cache": cfg["kv_dtype"],
+                   "exec_mode": "depth_walk" if args.exec_mode else "kernels"},
         "p50_ms": p50,
         "p99_ms": p99,
         "step_bytes": r["step_bytes"],

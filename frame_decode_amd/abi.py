@@ -16,6 +16,7 @@ FD_E_STATE = -7
 FD_F32 = 0
 FD_BF16 = 1
 FD_FP8_E4M3 = 2
+FD_EXEC_KERNELS, FD_EXEC_DEPTH_WALK = 0, 1
 
 _DT = {"f32": FD_F32, "bf16": FD_BF16, "fp8": FD_FP8_E4M3}
 
@@ -37,7 +38,7 @@ class FdConfig(ctypes.Structure):
         ("w_dtype", c_i32), ("act_dtype", c_i32), ("kv_dtype", c_i32),
         ("depth_steps", c_i32), ("depth_layers", c_i32), ("depth_d", c_i32),
         ("depth_heads", c_i32), ("depth_kv_heads", c_i32), ("depth_head_dim", c_i32),
-        ("depth_ffn", c_i32),
+        ("depth_ffn", c_i32), ("exec_mode", c_i32),
     ]
 
 
@@ -74,8 +75,9 @@ EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_free", "fd_des
            "fd_kv_layout", "fd_set_position", "fd_slot_state", "fd_kv_write", "fd_sync",
            "fd_profile", "fd_profile_read", "fd_read_probe", "fd_last_error", "fd_status_str"]
 
-FD_N_KINDS = 8
-KIND_NAMES = ["embed", "qkv", "attention", "o_proj", "gate_up", "down", "final", "depth_in"]
+FD_N_KINDS = 9
+KIND_NAMES = ["embed", "qkv", "attention", "o_proj", "gate_up", "down", "final", "depth_in",
+              "depth_walk"]
 
 
 def config_from_dict(cfg: dict) -> FdConfig:
@@ -89,6 +91,7 @@ def config_from_dict(cfg: dict) -> FdConfig:
     c.w_dtype = _DT[cfg["w_dtype"]]
     c.act_dtype = _DT[cfg["act_dtype"]]
     c.kv_dtype = _DT[cfg["kv_dtype"]]
+    c.exec_mode = int(cfg.get("exec_mode", 0))
     return c
 
 

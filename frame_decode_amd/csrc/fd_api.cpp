@@ -38,6 +38,10 @@ struct fd_ctx {
     std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> prof_pending;
     double prof_ms[FD_N_KINDS] = {};
     int64_t prof_n[FD_N_KINDS] = {};
+    // persistent walk of the depth stack (built at init when the plan has one)
+    fd::WalkArgs walk{};
+    int walk_grid = 0;
+    bool walk_launched = false;
     explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context) {}
 };
 
@@ -167,7 +171,7 @@ hipError_t timed(fd_ctx* c, int kind, hipStream_t st, F&& launch) {
     return e;
 }
 
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_O, K_GU, K_DOWN, K_FINAL, K_WIN };
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_O, K_GU, K_DOWN, K_FINAL, K_WIN, K_WALK };
 
 struct CacheRef {
     uint8_t* base;
@@ -296,6 +300,222 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
     return e;
 }
 
+// The depth loop of one frame as a persistent walk: the phase list and the
+// argument blocks of every task, built once here and kept in the workspace.
+// Every phase output gets a region of its own (nothing is overwritten within
+// a launch, so no XCD can hold a stale L2 line of data it reads).
+hipError_t build_depth_walk(fd_ctx* c, hipStream_t s, std::string* err) {
+    const fd::Plan& pl = c->plan;
+    const fd::StackPlan& dp = pl.dstack;
+    const fd::StackDims& dd = dp.dims;
+    uint64_t cur = pl.ws_walk_act;
+    const uint64_t end = pl.ws_walk_act + pl.walk_act_bytes;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t o = cur;
+        cur += fd::walk_region(bytes);
+        return Wk(c, o);
+    };
+    std::vector<fd::WalkPhase> phases;
+    std::vector<fd::GemmArgs> gemm;
+    std::vector<fd::AttnArgs> attn;
+    std::vector<fd::EmbedArgs> embed;
+    std::vector<fd::FinalArgs> fin;
+    const uint64_t Sp = pl.Sp;
+    auto gemm_phases = [&](const fd::GemmArgs& g, const fd::GemmShape& sh) {
+        const int idx = (int)gemm.size();
+        gemm.push_back(g);
+        phases.push_back({sh.R == 6 ? fd::WALK_GEMM6 : fd::WALK_GEMM4, idx, sh.grid(), 1});
+        if (sh.P > 1 && g.epi != fd::EPI_PLANES)
+            phases.push_back({sh.R == 6 ? fd::WALK_REDUCE6 : fd::WALK_REDUCE4, idx, sh.grid() / sh.P * sh.MTG, 1});
+    };
+    auto shaped = [&](fd::GemmArgs g, const fd::GemmShape& sh, uint64_t w_off) {
+        g.W = P(c, w_off);
+        g.K = sh.K; g.KB = sh.KB; g.NB = sh.NB; g.P = sh.P; g.MG = sh.MG;
+        g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
+        g.ss_stride = pl.nss_max;
+        g.inv_d = 1.0f / (float)dd.d;
+        g.eps = pl.cfg.rms_eps;
+        g.part = sh.P > 1 && g.epi != fd::EPI_PLANES ? (float*)take(4ull * sh.part_floats) : nullptr;
+        return g;
+    };
+    // input projection c = W_in y
+    {
+        fd::GemmArgs g{};
+        g.X = Wk(c, pl.ws_yw);
+        g.epi = fd::EPI_F32;
+        g.y = (float*)Wk(c, pl.ws_c);
+        g.ld = dd.d;
+        g = shaped(g, pl.win, pl.w_in);
+        g.inv_d = 1.0f / (float)pl.main.dims.d;
+        gemm_phases(g, pl.win);
+    }
+    const uint64_t pos_b = (uint64_t)dd.hd * 4, head_b = pos_b * dd.T, kv_b = head_b * dd.hkv,
+                   layer_b = kv_b * 2, slot_b = layer_b * dd.L;
+    const float* z_prev = nullptr;
+    for (int k = 0; k < dd.T; ++k) {
+        fd::EmbedArgs de{};
+        de.c = (const float*)Wk(c, pl.ws_c);
+        de.z = z_prev;
+        de.active = slot_active(c);
+        de.S = pl.S;
+        de.d = dd.d;
+        de.MT = pl.MT;
+        de.x = (float*)take(4 * Sp * dd.d);
+        de.xg = take(4 * Sp * dd.d);
+        de.g = (const float*)P(c, dd.L > 0 ? dp.layers[0].g_attn : dp.g_final);
+        de.ss_out = (float*)take(4 * Sp * pl.nss_max);
+        de.ss_stride = pl.nss_max;
+        phases.push_back({fd::WALK_EMBED, (int)embed.size(), pl.Sp, 1});
+        embed.push_back(de);
+        const float* x_cur = de.x;
+        const void* xg_cur = de.xg;
+        const float* ss_cur = de.ss_out;
+        int nss = 1;
+        for (int l = 0; l < dd.L; ++l) {
+            const fd::LayerOffsets& lo = dp.layers[l];
+            fd::GemmArgs q{};
+            q.X = xg_cur;
+            q.epi = fd::EPI_PLANES;
+            q.y = (float*)take(4ull * dp.qkv.P * Sp * dd.qkv_n());
+            q.ld = dd.qkv_n();
+            q.plane = Sp * dd.qkv_n();
+            q = shaped(q, dp.qkv, lo.qkv);
+            gemm_phases(q, dp.qkv);
+
+            fd::AttnArgs at{};
+            at.qkv = q.y;
+            at.P = dp.qkv.P;
+            at.nqkv = dd.qkv_n();
+            at.plane = q.plane;
+            at.ss_in = ss_cur;
+            at.nss = nss;
+            at.ss_stride = pl.nss_max;
+            at.inv_d = 1.0f / (float)dd.d;
+            at.eps = pl.cfg.rms_eps;
+            at.rope = (const float*)P(c, dp.rope);
+            at.qscale = (const float*)P(c, dp.qscale) + (size_t)l * dd.hkv;
+            at.kvsig = (const float*)P(c, dp.kvsig) + (size_t)l * 2 * dd.hkv;
+            at.vscale = (const float*)P(c, dp.vscale) + (size_t)l * dd.hkv;
+            at.arena = Wk(c, pl.ws_dkv) + (size_t)l * layer_b;
+            at.slot_stride = slot_b; at.kv_stride = kv_b; at.head_stride = head_b; at.pos_stride = pos_b;
+            at.active = slot_active(c);
+            at.pos = slot_pos(c);
+            at.pos_override = k;
+            at.S = pl.S; at.hq = dd.hq; at.hkv = dd.hkv; at.tc = dp.attn.tc; at.n_chunks = dp.attn.n_chunks;
+            at.T = dd.T;
+            at.MT = pl.MT;
+            at.part = dp.attn.n_chunks > 1
+                          ? (float*)take(4ull * pl.S * dd.hkv * dp.attn.n_chunks * dd.G() * (dd.hd + 2))
+                          : nullptr;
+            at.o_out = take(4 * Sp * dd.hq * dd.hd);
+            const int ai = (int)attn.size();
+            attn.push_back(at);
+            phases.push_back({fd::WALK_ATTN, ai, pl.S * dd.hkv * dp.attn.n_chunks, 1});
+            if (dp.attn.n_chunks > 1) phases.push_back({fd::WALK_COMBINE, ai, pl.S * dd.hkv * dd.G(), 1});
+
+            fd::GemmArgs o{};
+            o.X = at.o_out;
+            o.epi = fd::EPI_RESID;
+            o.x_src = x_cur;
+            o.x = (float*)take(4 * Sp * dd.d);
+            o.xg = take(4 * Sp * dd.d);
+            o.g_next = (const float*)P(c, lo.g_ffn);
+            o.ss_out = (float*)take(4 * Sp * pl.nss_max);
+            o.ld = dd.d;
+            o = shaped(o, dp.o, lo.o);
+            gemm_phases(o, dp.o);
+
+            fd::GemmArgs u{};
+            u.X = o.xg;
+            u.epi = fd::EPI_GU;
+            u.ss_in = o.ss_out;
+            u.nss = dp.o.n_groups;
+            u.h_out = take(4 * Sp * dd.f);
+            u.F = dd.f;
+            u = shaped(u, dp.gu, lo.gu);
+            gemm_phases(u, dp.gu);
+
+            fd::GemmArgs dn{};
+            dn.X = u.h_out;
+            dn.epi = fd::EPI_RESID;
+            dn.x_src = o.x;
+            dn.x = (float*)take(4 * Sp * dd.d);
+            dn.xg = take(4 * Sp * dd.d);
+            dn.g_next = (const float*)P(c, l + 1 < dd.L ? dp.layers[l + 1].g_attn : dp.g_final);
+            dn.ss_out = (float*)take(4 * Sp * pl.nss_max);
+            dn.ld = dd.d;
+            dn = shaped(dn, dp.down, lo.down);
+            gemm_phases(dn, dp.down);
+            x_cur = dn.x;
+            xg_cur = dn.xg;
+            ss_cur = dn.ss_out;
+            nss = dp.down.n_groups;
+        }
+        fd::FinalArgs f{};
+        f.x = x_cur;
+        f.ss = ss_cur;
+        f.nss = nss;
+        f.ss_stride = pl.nss_max;
+        f.inv_d = 1.0f / (float)dd.d;
+        f.eps = pl.cfg.rms_eps;
+        f.g = (const float*)P(c, dp.g_final);
+        f.active = slot_active(c);
+        f.S = pl.S;
+        f.d = dd.d;
+        f.MT = pl.MT;
+        f.ldy = dd.T * dd.d;
+        f.y_off = k * dd.d;
+        f.zf = (float*)take(4 * Sp * dd.d);
+        f.advance = 0;
+        phases.push_back({fd::WALK_FINAL_OUT, (int)fin.size(), pl.Sp, k + 1 < dd.T ? 1 : 0});
+        fin.push_back(f);
+        z_prev = f.zf;
+    }
+    if (cur > end || (int)phases.size() > pl.walk_max_phases || (int)gemm.size() > pl.walk_max_gemm ||
+        (int)attn.size() > pl.walk_max_attn || (int)embed.size() > pl.walk_max_embed ||
+        (int)fin.size() > pl.walk_max_fin) {
+        *err = "depth walk layout exceeds its plan";
+        return hipErrorInvalidValue;
+    }
+    // argument region: [phases][gemm][attn][embed][fin], each block 256-aligned
+    std::vector<uint8_t> host(pl.walk_args_bytes, 0);
+    uint64_t o = 0;
+    auto put = [&](const void* src, uint64_t bytes) {
+        const uint64_t at = o;
+        std::memcpy(host.data() + at, src, bytes);
+        o = fd::align_up(o + bytes);
+        return at;
+    };
+    static_assert(sizeof(fd::GemmArgs) <= fd::kWalkArgSlot && sizeof(fd::AttnArgs) <= fd::kWalkArgSlot &&
+                  sizeof(fd::EmbedArgs) <= fd::kWalkArgSlot && sizeof(fd::FinalArgs) <= fd::kWalkArgSlot,
+                  "argument blocks larger than their reserved slot");
+    const uint64_t ph_o = put(phases.data(), phases.size() * sizeof(fd::WalkPhase));
+    const uint64_t g_o = put(gemm.data(), gemm.size() * sizeof(fd::GemmArgs));
+    const uint64_t a_o = put(attn.data(), attn.size() * sizeof(fd::AttnArgs));
+    const uint64_t e_o = put(embed.data(), embed.size() * sizeof(fd::EmbedArgs));
+    const uint64_t f_o = put(fin.data(), fin.size() * sizeof(fd::FinalArgs));
+    if (o > pl.walk_args_bytes) {
+        *err = "depth walk arguments exceed their region";
+        return hipErrorInvalidValue;
+    }
+    uint8_t* dev = Wk(c, pl.ws_walk_args);
+    hipError_t e = hipMemcpyAsync(dev, host.data(), o, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    fd::WalkArgs& w = c->walk;
+    w.phases = (const fd::WalkPhase*)(dev + ph_o);
+    w.n_phases = (int)phases.size();
+    w.gemm = (const fd::GemmArgs*)(dev + g_o);
+    w.attn = (const fd::AttnArgs*)(dev + a_o);
+    w.embed = (const fd::EmbedArgs*)(dev + e_o);
+    w.fin = (const fd::FinalArgs*)(dev + f_o);
+    w.out = nullptr;
+    w.bar = (unsigned*)Wk(c, pl.ws_walk_bar);
+    w.abort_flag = (int*)(Wk(c, pl.ws_walk_bar) + 64);
+    c->walk_grid = fd::walk_grid(dp.qkv.MTG, dd.hd, dd.G());
+    return hipSuccess;
+}
+
 hipError_t flush_slots(fd_ctx* c, hipStream_t st) {
     if (!c->slots.dirty()) return hipSuccess;
     const int i = c->ring;
@@ -402,8 +622,10 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
         if (e == hipSuccess) e = upload_tables(c, p.dstack, std::vector<float>(), false, s);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(s);
+    std::string werr;
+    if (e == hipSuccess && p.dwalk) e = build_depth_walk(c, s, &werr);
     if (e != hipSuccess) {
-        std::string msg = std::string("fd_init: ") + hipGetErrorString(e);
+        std::string msg = std::string("fd_init: ") + (werr.empty() ? hipGetErrorString(e) : werr.c_str());
         fd_destroy(c);
         return fail(nullptr, FD_E_DEVICE, msg);
     }
@@ -492,7 +714,15 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
         f.advance = 1;
         e = timed(c, K_FINAL, st, [&] { return fd::launch_final(f, pl.wt, pl.Sp, st); });
     }
-    if (e == hipSuccess && pl.depth) {
+    if (e == hipSuccess && pl.depth && pl.dwalk && c->walk_grid > 0) {
+        const fd::StackDims& dd = pl.dstack.dims;
+        fd::WalkArgs w = c->walk;
+        w.out = depth_out;
+        e = timed(c, K_WALK, st, [&] {
+            return fd::launch_walk(w, pl.dstack.qkv.MTG, dd.hd, dd.G(), c->walk_grid, st);
+        });
+        c->walk_launched = true;
+    } else if (e == hipSuccess && pl.depth) {
         const fd::StackPlan& dp = pl.dstack;
         const fd::StackDims& dd = dp.dims;
         fd::GemmArgs g{};
@@ -637,6 +867,13 @@ fd_status fd_sync(fd_ctx* c, void* stream) {
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(c, e, "fd_sync");
+    if (c->walk_launched) {
+        int flag = 0;
+        e = hipMemcpy(&flag, c->walk.abort_flag, sizeof(int), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(c, e, "fd_sync");
+        c->walk_launched = false;
+        if (flag) return fail(c, FD_E_DEVICE, "depth walk: a grid barrier timed out");
+    }
     return FD_OK;
 }
 

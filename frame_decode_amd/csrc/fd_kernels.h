@@ -29,7 +29,8 @@ struct GemmArgs {
     // EPI_PLANES
     uint64_t plane;        // floats between consecutive split planes of y
     // EPI_RESID
-    float* x;              // [Sp][ld] residual stream
+    float* x;              // [Sp][ld] residual stream (written)
+    const float* x_src;    // residual input when not x itself (persistent walk), else null
     void* xg;              // [Sp][ld] act(x * g_next)
     void* xg_lo;           // optional (bf16): x * g_next - xg, rounded to bf16
     const float* g_next;
@@ -116,6 +117,30 @@ struct KvWriteArgs {
     int hkv, hd, t0, n, kv_fp8;
 };
 
+// Persistent stack walk: one cooperative launch runs a list of phases, each
+// over n_items workgroup tasks (the bodies of the separate kernels), with a
+// grid barrier after every phase whose outputs a later one reads.
+enum WalkKind : int {
+    WALK_GEMM4 = 0, WALK_GEMM6, WALK_REDUCE4, WALK_REDUCE6, WALK_ATTN, WALK_COMBINE,
+    WALK_EMBED, WALK_FINAL, WALK_FINAL_OUT
+};
+
+struct WalkPhase {
+    int kind, idx, n_items, barrier;
+};
+
+struct WalkArgs {
+    const WalkPhase* phases;
+    int n_phases;
+    const GemmArgs* gemm;
+    const AttnArgs* attn;
+    const EmbedArgs* embed;
+    const FinalArgs* fin;
+    void* out;             // y_out of WALK_FINAL_OUT phases (the caller's rows)
+    unsigned* bar;         // barrier counter, zeroed before the launch
+    int* abort_flag;       // set when a barrier wait times out
+};
+
 // Depth of a GEMM wave's register ring of k-tiles: as deep as ~48
 // outstanding 16-byte-per-lane loads allow (the wave's load counter holds
 // 63), at least 2.  SX: the session rows come as two bf16 parts.
@@ -131,5 +156,12 @@ hipError_t launch_embed(const EmbedArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
+// Persistent walk of an fp32 stack with MTG m-tiles per m-group (1..4),
+// head_dim 128 and G = 1 query heads per kv head.  walk_supported() says
+// whether a shape has a compiled walk; walk_grid() is the co-resident grid
+// (0 if none); launch_walk() zeroes the barrier state and launches.
+bool walk_supported(int MTG, int hd, int G);
+int walk_grid(int MTG, int hd, int G);
+hipError_t launch_walk(const WalkArgs& w, int MTG, int hd, int G, int grid, hipStream_t st);
 
 }  // namespace fd

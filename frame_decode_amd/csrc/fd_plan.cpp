@@ -83,9 +83,9 @@ fd_status check_stack(const char* name, int L, int d, int hq, int hkv, int hd, i
     return FD_OK;
 }
 
-// Tuning override for measurements: FD_TUNE="qkv.P=4,o.R=1,attn.chunks=2"
-// replaces the chosen split-K factor (P), n-blocks per wave (R) of a
-// projection, or the attention chunk count.  Unset in normal use.
+// Tuning override for measurements: FD_TUNE="qkv.P=4,o.NG=4,attn.chunks=2"
+// replaces the chosen split-K factor (P) or n-blocks per workgroup (NG) of
+// a projection, or the attention chunk count.  Unset in normal use.
 int tune_value(const char* key, int dflt) {
     const char* env = std::getenv("FD_TUNE");
     if (!env) return dflt;
@@ -168,6 +168,14 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     }
     if (!(c.kv_dtype == FD_F32 || c.kv_dtype == FD_FP8_E4M3)) {
         *err = "kv_dtype must be FD_F32 or FD_FP8_E4M3";
+        return FD_E_UNSUPPORTED;
+    }
+    if (c.exec_mode != FD_EXEC_KERNELS && c.exec_mode != FD_EXEC_DEPTH_WALK) {
+        *err = "exec_mode must be FD_EXEC_KERNELS or FD_EXEC_DEPTH_WALK";
+        return FD_E_INVAL;
+    }
+    if (c.exec_mode == FD_EXEC_DEPTH_WALK && c.depth_steps <= 0) {
+        *err = "FD_EXEC_DEPTH_WALK needs a depth stack";
         return FD_E_UNSUPPORTED;
     }
     if (!(c.rms_eps >= 0.0f) || !std::isfinite(c.rms_eps)) {
@@ -296,6 +304,45 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         const StackDims& z = p.dstack.dims;
         p.ws_dkv = take(Sp * z.L * 2ull * z.hkv * z.T * z.hd * 4);
         p.dstack.kv_off = p.ws_dkv;
+    }
+    if (p.depth) {
+        // The walk is compiled for fp32 stacks with head_dim 128, one query
+        // head per kv head and at most 4 row tiles.
+        const StackPlan& dp = p.dstack;
+        const StackDims& z = dp.dims;
+        p.dwalk = c.exec_mode == FD_EXEC_DEPTH_WALK;
+        if (p.dwalk && !(!p.wt && !p.kv_fp8 && z.hd == 128 && z.G() == 1 && p.MT <= 4 &&
+                         dp.qkv.MG == 1 && dp.qkv.MTG <= 4)) {
+            *err = "FD_EXEC_DEPTH_WALK needs an fp32 depth stack with depth_head_dim 128, one query "
+                   "head per kv head and at most 64 slots";
+            return FD_E_UNSUPPORTED;
+        }
+        if (p.dwalk) {
+            const uint64_t f4 = 4;
+            uint64_t per_layer = 0, per_step = 0;
+            per_layer += walk_region(f4 * dp.qkv.P * Sp * z.qkv_n());           // QKV planes
+            per_layer += walk_region(f4 * Sp * z.hq * z.hd);                     // o
+            if (dp.attn.n_chunks > 1)
+                per_layer += walk_region(f4 * p.S * z.hkv * dp.attn.n_chunks * z.G() * (z.hd + 2));
+            for (const GemmShape* g : {&dp.o, &dp.gu, &dp.down})
+                if (g->P > 1) per_layer += walk_region(f4 * g->part_floats);       // k-split partials
+            per_layer += 2 * (2 * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max));  // x, xg, ss x2
+            per_layer += walk_region(f4 * Sp * z.f);                              // h
+            per_step += 2 * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max);  // embed x, xg, ss
+            per_step += walk_region(f4 * Sp * z.d);                               // z_k
+            p.walk_act_bytes = (uint64_t)z.T * (per_step + (uint64_t)z.L * per_layer);
+            if (p.win.P > 1) p.walk_act_bytes += walk_region(f4 * p.win.part_floats);
+            p.walk_max_gemm = 1 + z.T * z.L * 4;
+            p.walk_max_attn = z.T * z.L;
+            p.walk_max_embed = z.T;
+            p.walk_max_fin = z.T;
+            p.walk_max_phases = 2 + z.T * (2 + z.L * 9);
+            const int slots = p.walk_max_gemm + p.walk_max_attn + p.walk_max_embed + p.walk_max_fin;
+            p.walk_args_bytes = align_up((uint64_t)slots * kWalkArgSlot + (uint64_t)p.walk_max_phases * 16);
+            p.ws_walk_act = take(p.walk_act_bytes);
+            p.ws_walk_args = take(p.walk_args_bytes);
+            p.ws_walk_bar = take(256);
+        }
     }
     p.ws_err = take(64);
     p.workspace_bytes = w;

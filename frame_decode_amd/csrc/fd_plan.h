@@ -90,6 +90,13 @@ struct Plan {
     uint64_t ws_x = 0, ws_xg = 0, ws_qkv = 0, ws_o = 0, ws_h = 0, ws_c = 0, ws_z = 0, ws_yw = 0;
     uint64_t ws_ss_a = 0, ws_ss_f = 0, ws_part = 0, ws_cnt = 0, ws_apart = 0, ws_acnt = 0;
     uint64_t ws_dkv = 0, ws_err = 0, ws_xg_lo = 0, ws_h_lo = 0, ws_o_lo = 0;
+    // persistent walk of the depth stack (one launch per frame for the 8
+    // sequential steps): whether it is used, and its workspace regions
+    bool dwalk = false;
+    uint64_t ws_walk_act = 0, ws_walk_args = 0, ws_walk_bar = 0;
+    uint64_t walk_act_bytes = 0, walk_args_bytes = 0;
+    int walk_max_gemm = 0, walk_max_attn = 0, walk_max_embed = 0, walk_max_fin = 0,
+        walk_max_phases = 0;
     int nss_max = 0;
     uint64_t workspace_bytes = 0;
     // cache arena
@@ -102,6 +109,13 @@ struct Plan {
 // Validates cfg and builds the plan.  Returns FD_OK or an error code with
 // a message in *err.
 fd_status make_plan(const fd_config& cfg, Plan* out, std::string* err);
+
+// Bytes of one walk buffer region: every cross-phase output of the walk has
+// a region of its own (no L2 line of it can be stale in another XCD).
+inline uint64_t walk_region(uint64_t bytes) { return align_up(bytes > 0 ? bytes : 4); }
+
+// Bytes per argument block reserved in the walk's argument region.
+constexpr uint64_t kWalkArgSlot = 512;
 
 // Tile choice for one projection (exposed for tests).
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu);

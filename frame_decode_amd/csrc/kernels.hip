@@ -89,16 +89,49 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
     return s;
 }
 
-// Stores 4 consecutive activations at p (fp32 or bf16).
-template <int WT>
+// Stores of data that another workgroup of the same launch reads (the
+// persistent walk, CO = 1): every 32-bit word is a device-scope store, which
+// is written through the XCD's L2, so no cache flush is needed before the
+// grid barrier.  CO = 0: plain stores (kernel boundaries order the rest).
+template <int CO>
+__device__ __forceinline__ void st1(float* p, float v) {
+    if constexpr (CO) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+template <int CO>
+__device__ __forceinline__ void stw(uint32_t* p, uint32_t v) {
+    if constexpr (CO) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// (16-byte aligned p: two 8-byte device-scope stores)
+template <int CO>
+__device__ __forceinline__ void st4(float* p, f32x4 v) {
+    if constexpr (CO) {
+        const u32x4 w = __builtin_bit_cast(u32x4, v);
+        unsigned long long* q = (unsigned long long*)p;
+        __hip_atomic_store(q, (unsigned long long)w[0] | ((unsigned long long)w[1] << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 1, (unsigned long long)w[2] | ((unsigned long long)w[3] << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *(f32x4*)p = v;
+    }
+}
+
+// Stores 4 consecutive activations at p (fp32 or bf16; coherent stores are
+// fp32 only).
+template <int WT, int CO = 0>
 __device__ __forceinline__ void store_act4(void* p, size_t idx, f32x4 v) {
+    static_assert(!(WT && CO), "coherent stores are fp32 only");
     if (WT) {
         u32x2 w;
         w[0] = f2bf(v[0]) | (f2bf(v[1]) << 16);
         w[1] = f2bf(v[2]) | (f2bf(v[3]) << 16);
         *(u32x2*)((uint16_t*)p + idx) = w;
     } else {
-        *(f32x4*)((float*)p + idx) = v;
+        st4<CO>((float*)p + idx, v);
     }
 }
 
@@ -124,11 +157,12 @@ __device__ __forceinline__ void store_split1(void* hi, void* lo, size_t idx, flo
 }
 
 // Stores one activation (with its bf16 remainder when lo is given).
-template <int WT>
+template <int WT, int CO = 0>
 __device__ __forceinline__ void store_act1x(void* p, void* lo, size_t idx, float v) {
+    static_assert(!(WT && CO), "coherent stores are fp32 only");
     if (WT && lo) store_split1(p, lo, idx, v);
     else if (WT) ((uint16_t*)p)[idx] = (uint16_t)f2bf(v);
-    else ((float*)p)[idx] = v;
+    else st1<CO>((float*)p + idx, v);
 }
 
 template <int WT>
@@ -269,9 +303,10 @@ __device__ __forceinline__ void rstd_phase2(const GemmArgs& a, int rows, const f
 // + lane%16.  Every load a tile needs (positions via LDS, rotary factors,
 // residual rows, gains) is issued for all owned tiles before any result is
 // stored, so the tiles' latencies overlap instead of adding up.
-template <int WT, int NG, int MTG, int NWV, int OWN>
+template <int WT, int NG, int MTG, int NWV, int OWN, int CO>
 __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, const int* ti, int ng,
                                             int mt0, int t_lo, int t_hi, const float* s_rstd) {
+    static_assert(!(WT && CO), "coherent stores are fp32 only");
     constexpr int NTL = NG * MTG;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -294,7 +329,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
         aux1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!ok[j]) continue;
         if (a.epi == EPI_RESID) {
-            aux0[j] = *(const f32x4*)(a.x + (size_t)mm[j] * a.ld + nn[j]);
+            aux0[j] = *(const f32x4*)((a.x_src ? a.x_src : a.x) + (size_t)mm[j] * a.ld + nn[j]);
             aux1[j] = *(const f32x4*)(a.g_next + nn[j]);
         }
     }
@@ -312,9 +347,9 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
         if (a.ss_in) x *= s_rstd[mloc];
         if (a.epi == EPI_RESID) {
             const f32x4 xn = aux0[j] + x;
-            *(f32x4*)(a.x + (size_t)m * a.ld + n) = xn;
+            st4<CO>(a.x + (size_t)m * a.ld + n, xn);
             if (WT && a.xg_lo) store_split4(a.xg, a.xg_lo, xoff<WT>(m, n, a.MT), xn * aux1[j]);
-            else store_act4<WT>(a.xg, xoff<WT>(m, n, a.MT), xn * aux1[j]);
+            else store_act4<WT, CO>(a.xg, xoff<WT>(m, n, a.MT), xn * aux1[j]);
             const float sq = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
 #pragma unroll
             for (int tt = 0; tt < MTG; ++tt)
@@ -331,10 +366,12 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
                     *(uint32_t*)((uint16_t*)a.h_lo + xoff<WT>(m, jj, a.MT)) =
                         f2bf(h0 - bf2f(b0)) | (f2bf(h1 - bf2f(b1)) << 16);
             } else {
-                *(f32x2*)((float*)a.h_out + xoff<WT>(m, jj, a.MT)) = f32x2{h0, h1};
+                float* hp = (float*)a.h_out + xoff<WT>(m, jj, a.MT);
+                st1<CO>(hp, h0);
+                st1<CO>(hp + 1, h1);
             }
         } else {
-            *(f32x4*)(a.y + (size_t)m * a.ld + n) = x;
+            st4<CO>(a.y + (size_t)m * a.ld + n, x);
         }
     }
 
@@ -352,19 +389,19 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < NWV; ++w) s += s_red[w][i];
-            a.ss_out[(size_t)(mt0 * 16 + i) * a.ss_stride + ng] = s;
+            st1<CO>(a.ss_out + (size_t)(mt0 * 16 + i) * a.ss_stride + ng, s);
         }
     }
 }
 
-template <int WT, int NG, int MTG, int STG, int SX>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+// One workgroup task of a projection; s_acc: 4 * NG * MTG * 64 f32x4 of LDS.
+template <int WT, int NG, int MTG, int STG, int SX, int CO>
+__device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc_mem) {
     typedef typename BFrag<WT>::T BT;
     constexpr int NTL = NG * MTG;
     constexpr int OWN = (NTL + 3) / 4;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    int bid = blockIdx.x;
     const int ks = bid % a.P;
     bid /= a.P;
     const int mg = bid % a.MG;
@@ -376,7 +413,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int nb0 = ng * NG;
     const int mt0 = mg * MTG;    // session rows are padded to whole m-groups
 
-    __shared__ f32x4 s_acc[4][NTL][64];
+    f32x4 (*s_acc)[NTL][64] = (f32x4 (*)[NTL][64])s_acc_mem;
     __shared__ float s_seg[MTG * 16 * 8];
     __shared__ float s_rstd[MTG * 16];
 
@@ -477,7 +514,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             const int i = wave + 4 * j;
             const int r = i / MTG, t = i - (i / MTG) * MTG;
             if (i < NTL && nb0 + r < a.NB)
-                *(f32x4*)(y + (size_t)((mt0 + t) * 16 + (lane & 15)) * a.ld + (nb0 + r) * 16 + (lane >> 4) * 4) = v[j];
+                st4<CO>(y + (size_t)((mt0 + t) * 16 + (lane & 15)) * a.ld + (nb0 + r) * 16 + (lane >> 4) * 4, v[j]);
         }
         return;
     }
@@ -487,7 +524,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             const int i = wave + 4 * j;
-            if (i < NTL) pp[(size_t)i * 64] = v[j];
+            if (i < NTL) st4<CO>((float*)(pp + (size_t)i * 64), v[j]);
         }
         return;
     }
@@ -495,20 +532,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < OWN; ++j) ti[j] = wave + 4 * j < NTL ? wave + 4 * j : -1;
     __syncthreads();
-    gemm_finish<WT, NG, MTG, 4, OWN>(a, v, ti, ng, mt0, 0, MTG, s_rstd);
+    gemm_finish<WT, NG, MTG, 4, OWN, CO>(a, v, ti, ng, mt0, 0, MTG, s_rstd);
+}
+
+template <int WT, int NG, int MTG, int STG, int SX>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+    __shared__ f32x4 s_acc[4 * NG * MTG * 64];
+    gemm_wg<WT, NG, MTG, STG, SX, 0>(a, blockIdx.x, s_acc);
 }
 
 // Adds the P k-split partial tiles of one m-tile t of an (n-group, m-group)
 // in split order and applies the epilogue: one 4-wave workgroup per
 // (n-group, m-group, m-tile), wave w finishing blocks w, w+4, ... of the
 // m-tile, so the reduction is spread over many CUs.
-template <int WT, int NG, int MTG>
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
+template <int WT, int NG, int MTG, int CO>
+__device__ __forceinline__ void gemm_reduce_wg(const GemmArgs& a, int bid) {
     constexpr int NTL = NG * MTG;
     constexpr int OWN = (NG + 3) / 4;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    int bid = blockIdx.x;
     const int t = bid % MTG;
     bid /= MTG;
     const int mg = bid % a.MG;
@@ -533,7 +575,12 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
     __syncthreads();
     if (a.ss_in) rstd_phase2(a, 16, s_seg, s_rstd + t * 16);
     __syncthreads();
-    gemm_finish<WT, NG, MTG, 4, OWN>(a, v, ti, ng, mt0, t, t + 1, s_rstd);
+    gemm_finish<WT, NG, MTG, 4, OWN, CO>(a, v, ti, ng, mt0, t, t + 1, s_rstd);
+}
+
+template <int WT, int NG, int MTG>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
+    gemm_reduce_wg<WT, NG, MTG, 0>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -572,8 +619,8 @@ __device__ __forceinline__ void unpack16(const u32x4& raw, float* out) {
     }
 }
 
-template <int WT, int FP8, int D, int G>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+template <int WT, int FP8, int D, int G, int CO>
+__device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid) {
     constexpr int EB = FP8 ? 1 : 4;
     constexpr int LPP = FP8 ? D / 16 : D / 8;
     constexpr int E = D / LPP;         // elements per lane per position
@@ -587,7 +634,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int c = lane % LPP;
     const int jj = lane / LPP;
 
-    int bid = blockIdx.x;
     const int chunk = bid % a.n_chunks;
     bid /= a.n_chunks;
     const int g = bid % a.hkv;
@@ -596,7 +642,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     if (!a.active[s]) {
         if (chunk == 0)
             for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-                store_act1x<WT>(a.o_out, a.o_lo, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
+                store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
         return;
     }
     const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
@@ -693,7 +739,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
                 const float sg = a.kvsig[kv * a.hkv + g];
                 const uint32_t w = enc_e4m3(x[0] / sg) | (enc_e4m3(x[1] / sg) << 8) |
                                    (enc_e4m3(x[2] / sg) << 16) | (enc_e4m3(x[3] / sg) << 24);
-                *(uint32_t*)(dst + d0) = w;
+                stw<CO>((uint32_t*)(dst + d0), w);
                 const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
                 const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
                 keep[d0 + 0] = lo[0];
@@ -701,7 +747,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
                 keep[d0 + 2] = hi[0];
                 keep[d0 + 3] = hi[1];
             } else {
-                *(f32x4*)(dst + (size_t)d0 * 4) = x;
+                st4<CO>((float*)(dst + (size_t)d0 * 4), x);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) keep[d0 + e] = x[e];
             }
@@ -835,25 +881,29 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             L += f;
         }
         if (nch == 1) {
-            store_act1x<WT>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
+            store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
         } else {
             float* part = a.part + (((size_t)(s * a.hkv + g) * a.n_chunks + chunk) * G + h) * (D + 2);
-            part[d] = O;
+            st1<CO>(part + d, O);
             if (d == 0) {
-                part[D] = M;
-                part[D + 1] = L;
+                st1<CO>(part + D, M);
+                st1<CO>(part + D + 1, L);
             }
         }
     }
+}
+
+template <int WT, int FP8, int D, int G>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+    attn_wg<WT, FP8, D, G, 0>(a, blockIdx.x);
 }
 
 // Merges the chunks of one (slot, query head) in chunk order: one
 // workgroup per (slot, kv head, query head of the group); the chunks'
 // (max, sum) pairs are read once into LDS, then each thread adds its
 // elements' chunk values (8 loads in flight per step).
-template <int WT, int D, int G>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-    int bid = blockIdx.x;
+template <int WT, int D, int G, int CO>
+__device__ __forceinline__ void attn_combine_wg(const AttnArgs& a, int bid) {
     const int h = bid % G;
     bid /= G;
     const int g = bid % a.hkv;
@@ -894,18 +944,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
             for (int u = 0; u < 8; ++u) O += s_w[c + u] * v[u];
         }
         for (; c < nch; ++c) O += s_w[c] * part[c * cs + d];
-        store_act1x<WT>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
+        store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
     }
+}
+
+template <int WT, int D, int G>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+    attn_combine_wg<WT, D, G, 0>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
 // row kernels
 
 
-template <int WT>
-__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+template <int WT, int CO>
+__device__ __forceinline__ void embed_row(const EmbedArgs& a, int m) {
     __shared__ float red[4];
-    const int m = blockIdx.x;
     const bool valid = m < a.S && a.active[m];
     float ss = 0.f;
     for (int i = threadIdx.x * 4; i < a.d; i += blockDim.x * 4) {
@@ -919,19 +973,23 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
                 if (a.z) v += *(const f32x4*)(a.z + (size_t)m * a.d + i);
             }
         }
-        *(f32x4*)(a.x + (size_t)m * a.d + i) = v;
+        st4<CO>(a.x + (size_t)m * a.d + i, v);
         if (WT && a.xg_lo) store_split4(a.xg, a.xg_lo, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
-        else store_act4<WT>(a.xg, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
+        else store_act4<WT, CO>(a.xg, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
     ss = block_sum_256(ss, red);
-    if (threadIdx.x == 0) a.ss_out[(size_t)m * a.ss_stride] = ss;
+    if (threadIdx.x == 0) st1<CO>(a.ss_out + (size_t)m * a.ss_stride, ss);
 }
 
 template <int WT>
-__global__ __launch_bounds__(256) void final_kernel(FinalArgs a) {
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+    embed_row<WT, 0>(a, blockIdx.x);
+}
+
+template <int WT, int CO>
+__device__ __forceinline__ void final_row(const FinalArgs& a, int m) {
     __shared__ float red[4];
-    const int m = blockIdx.x;
     const bool valid = m < a.S && a.active[m];
     float part = 0.f;
     for (int j = threadIdx.x; j < a.nss; j += blockDim.x) part += a.ss[(size_t)m * a.ss_stride + j];
@@ -939,11 +997,16 @@ __global__ __launch_bounds__(256) void final_kernel(FinalArgs a) {
     for (int i = threadIdx.x * 4; i < a.d; i += blockDim.x * 4) {
         f32x4 y = *(const f32x4*)(a.x + (size_t)m * a.d + i) * r * *(const f32x4*)(a.g + i);
         if (!valid) y = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (a.y_out && m < a.S) store_act4<WT>(a.y_out, (size_t)m * a.ldy + a.y_off + i, y);
-        if (a.yw) store_act4<WT>(a.yw, xoff<WT>(m, i, a.MT), y);
-        if (a.zf) *(f32x4*)(a.zf + (size_t)m * a.d + i) = y;
+        if (a.y_out && m < a.S) store_act4<WT, CO>(a.y_out, (size_t)m * a.ldy + a.y_off + i, y);
+        if (a.yw) store_act4<WT, CO>(a.yw, xoff<WT>(m, i, a.MT), y);
+        if (a.zf) st4<CO>(a.zf + (size_t)m * a.d + i, y);
     }
     if (a.advance && threadIdx.x == 0 && valid) a.pos[m] += 1;
+}
+
+template <int WT>
+__global__ __launch_bounds__(256) void final_kernel(FinalArgs a) {
+    final_row<WT, 0>(a, blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
@@ -965,6 +1028,75 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
                                  (enc_e4m3(v[2] / sg) << 16) | (enc_e4m3(v[3] / sg) << 24);
     } else {
         *(f32x4*)(dst + (size_t)d0 * 4) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// persistent stack walk
+
+// Grid barrier of a co-resident launch: every workgroup adds itself to a
+// device-scope counter after its stores have completed (the stores that
+// others read are device-scope, see st1), then waits until the counter
+// reaches `target`.  The wait is bounded: a workgroup that waits too long
+// sets the abort flag and every workgroup leaves at its next barrier.
+__device__ __forceinline__ bool grid_barrier(unsigned* cnt, unsigned target, int* abort_flag) {
+    __shared__ int s_ok;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int ok = 1;
+        for (unsigned spin = 0;; ++spin) {
+            if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+            if (spin > (1u << 21) || __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
+template <int MTG, int D, int G>
+__global__ __launch_bounds__(256) void walk_kernel(WalkArgs w) {
+    __shared__ f32x4 s_acc[4 * 6 * MTG * 64];
+    unsigned target = 0;
+    for (int ph = 0; ph < w.n_phases; ++ph) {
+        const WalkPhase P = w.phases[ph];
+        for (int it = blockIdx.x; it < P.n_items; it += gridDim.x) {
+            switch (P.kind) {
+                case WALK_GEMM4: gemm_wg<0, 4, MTG, gemm_stages(4, MTG), 0, 1>(w.gemm[P.idx], it, s_acc); break;
+                case WALK_GEMM6: gemm_wg<0, 6, MTG, gemm_stages(6, MTG), 0, 1>(w.gemm[P.idx], it, s_acc); break;
+                case WALK_REDUCE4: gemm_reduce_wg<0, 4, MTG, 1>(w.gemm[P.idx], it); break;
+                case WALK_REDUCE6: gemm_reduce_wg<0, 6, MTG, 1>(w.gemm[P.idx], it); break;
+                case WALK_ATTN: attn_wg<0, 0, D, G, 1>(w.attn[P.idx], it); break;
+                case WALK_COMBINE: attn_combine_wg<0, D, G, 1>(w.attn[P.idx], it); break;
+                case WALK_EMBED: embed_row<0, 1>(w.embed[P.idx], it); break;
+                case WALK_FINAL: final_row<0, 1>(w.fin[P.idx], it); break;
+                case WALK_FINAL_OUT: {
+                    FinalArgs f = w.fin[P.idx];
+                    f.y_out = w.out;
+                    final_row<0, 1>(f, it);
+                } break;
+                default: break;
+            }
+            __syncthreads();  // LDS of this task is free before the next one
+        }
+        if (P.barrier) {
+            target += gridDim.x;
+            if (!grid_barrier(w.bar, target, w.abort_flag)) return;
+        }
+    }
+}
+
+__global__ void walk_reset_kernel(unsigned* bar, int* abort_flag) {
+    if (threadIdx.x == 0) {
+        *bar = 0u;
+        *abort_flag = 0;
     }
 }
 
@@ -1098,6 +1230,45 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st) {
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+// walk shapes compiled: fp32 stacks, head_dim 128, one query head per kv
+// head, up to 4 m-tiles (64 session rows)
+template <int MTG>
+static const void* walk_fn() { return (const void*)walk_kernel<MTG, 128, 1>; }
+
+static const void* walk_fn_for(int MTG, int hd, int G) {
+    if (hd != 128 || G != 1) return nullptr;
+    switch (MTG) {
+        case 1: return walk_fn<1>();
+        case 2: return walk_fn<2>();
+        case 3: return walk_fn<3>();
+        case 4: return walk_fn<4>();
+        default: return nullptr;
+    }
+}
+
+bool walk_supported(int MTG, int hd, int G) { return walk_fn_for(MTG, hd, G) != nullptr; }
+
+int walk_grid(int MTG, int hd, int G) {
+    const void* fn = walk_fn_for(MTG, hd, G);
+    if (!fn) return 0;
+    int dev = 0, ncu = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess) return 0;
+    return per > 0 ? ncu * per : 0;
+}
+
+hipError_t launch_walk(const WalkArgs& w, int MTG, int hd, int G, int grid, hipStream_t st) {
+    const void* fn = walk_fn_for(MTG, hd, G);
+    if (!fn || grid <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(walk_reset_kernel, dim3(1), dim3(64), 0, st, w.bar, w.abort_flag);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    WalkArgs a = w;
+    void* args[] = {&a};
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(256), args, 0, st);
 }
 
 }  // namespace fd

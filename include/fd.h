@@ -93,7 +93,22 @@ typedef struct {
     int32_t depth_kv_heads;
     int32_t depth_head_dim;
     int32_t depth_ffn;
+    int32_t exec_mode;    /* FD_EXEC_KERNELS (0) or FD_EXEC_DEPTH_WALK (1), see below */
 } fd_config;
+
+/*
+ * Execution of a step.  FD_EXEC_KERNELS: fd_step enqueues a fixed sequence
+ * of kernels (no host work or synchronisation between them).
+ * FD_EXEC_DEPTH_WALK: as FD_EXEC_KERNELS for the main stack, but the depth
+ * stack's per-frame loop (input projection, then depth_steps x depth_layers
+ * layers) runs as ONE persistent cooperative launch whose workgroups walk the
+ * layers with device-side grid barriers (the case study's persistent
+ * program, "Under the hood"); supported for fp32 depth stacks with
+ * depth_head_dim 128, one query head per kv head and at most 64 slots
+ * (FD_E_UNSUPPORTED otherwise).
+ */
+#define FD_EXEC_KERNELS 0
+#define FD_EXEC_DEPTH_WALK 1
 
 /* Byte sizes of the four caller-allocated device buffers. */
 typedef struct {
@@ -261,10 +276,11 @@ fd_status fd_kv_write(fd_ctx* ctx, int32_t slot, int32_t layer, int32_t t0, int3
  * waits for them and returns, per kernel kind, the summed duration in
  * milliseconds and the number of launches since the last read (then resets).
  * Kinds: 0 embed, 1 qkv, 2 attention, 3 o-projection, 4 gate/up, 5 down,
- * 6 final norm, 7 depth input projection (FD_N_KINDS = 8).  Timing adds a
+ * 6 final norm, 7 depth input projection, 8 the persistent walk of the
+ * depth stack when one is used (FD_N_KINDS = 9).  Timing adds a
  * small gap between launches; headline step times are taken with it off.
  */
-#define FD_N_KINDS 8
+#define FD_N_KINDS 9
 fd_status fd_profile(fd_ctx* ctx, int32_t enable);
 fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, int32_t n);
 

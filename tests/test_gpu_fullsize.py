@@ -275,12 +275,15 @@ def test_7b_ragged_with_admission_and_retirement(model7b):
     ctx.fd_destroy()
 
 
-def test_talker_fifty_six_sessions_with_depth_loop_sampled():
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "depth_walk"])
+def test_talker_fifty_six_sessions_with_depth_loop_sampled(exec_mode):
     """The talker workload in full (26-layer fp32 main stack with GQA 4:1 and
     head_dim 256, 56 sessions at index 1499, then the 8-step depth loop of
-    the 6-layer depth stack): two seeded sessions recomputed, 1e-3 on the
-    main output and on all eight depth outputs."""
+    the 6-layer depth stack, as separate launches or as one persistent
+    walk): two seeded sessions recomputed, 1e-3 on the main output and on
+    all eight depth outputs."""
     cfg = synth.get_config("talker_s56")
+    cfg["exec_mode"] = exec_mode
     p0 = cfg["position"]
     say("C5: weights")
     model = synth.Model(cfg)

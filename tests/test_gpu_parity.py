@@ -188,12 +188,14 @@ def test_bf16_fp8_ragged_multichunk():
     _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
 
 
-def test_fp32_gqa_with_depth_loop():
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "depth_walk"])
+def test_fp32_gqa_with_depth_loop(exec_mode):
     """Talker geometry (GQA 4:1, head_dim 256, fp32) at reduced width, with
-    the 8-step depth loop of a 128-dim-head stack; 1e-3."""
+    the 8-step depth loop of a 128-dim-head stack (as separate launches and
+    as one persistent walk); 1e-3."""
     cfg = synth.scaled_config("talker_s56", n_layers=2, d_model=384, d_ffn=768, max_slots=5,
                               max_context=300, depth_layers=2, depth_d=256, depth_heads=2,
-                              depth_kv_heads=2, depth_ffn=512)
+                              depth_kv_heads=2, depth_ffn=512, exec_mode=exec_mode)
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 63, 64, 200]
     ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 2, tol=1e-3)

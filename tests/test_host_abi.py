@@ -123,6 +123,26 @@ def test_depth_stack_needs_fp32(host):
     assert st == FD_E_UNSUPPORTED
 
 
+def test_depth_walk_mode(host):
+    """The persistent depth walk is planned for the talker's fp32 depth
+    stack (it needs workspace for its own buffers) and refused elsewhere."""
+    cfg = synth.get_config("talker_s56")
+    st0, s0 = _plan(host, cfg)
+    cfg["exec_mode"] = 1
+    st1, s1 = _plan(host, cfg)
+    assert st0 == FD_OK and st1 == FD_OK and s1.workspace > s0.workspace
+    assert s1.packed_weights == s0.packed_weights and s1.kv_arena == s0.kv_arena
+    no_depth = synth.get_config("7b_s8_p256")
+    no_depth["exec_mode"] = 1
+    assert _plan(host, no_depth)[0] == FD_E_UNSUPPORTED
+    many = synth.get_config("talker_s56")
+    many.update(exec_mode=1, max_slots=80)
+    assert _plan(host, many)[0] == FD_E_UNSUPPORTED
+    bad = synth.get_config("talker_s56")
+    bad["exec_mode"] = 7
+    assert _plan(host, bad)[0] == FD_E_INVAL
+
+
 def test_gemm_tiling_covers_the_projection(host):
     out = (ctypes.c_int32 * 9)()
     for (N, K, wt, MT) in [(12288, 4096, 1, 5), (4096, 11264, 1, 5), (22528, 4096, 1, 1),
