@@ -12,7 +12,7 @@ import os
 
 from .abi import (FD_OK, FD_E_INVAL, FD_E_UNSUPPORTED, FD_E_NOSLOT, FD_E_BADSLOT,  # noqa: F401
                   FD_E_CTXFULL, FD_E_DEVICE, FD_E_STATE, FD_F32, FD_BF16, FD_FP8_E4M3,
-                  FD_EXEC_KERNELS, FD_EXEC_DEPTH_WALK,
+                  FD_EXEC_KERNELS, FD_EXEC_WALK,
                   FdConfig, FdSizes, FdKvView, FdError, config_from_dict, load_library)
 
 HERE = os.path.dirname(os.path.abspath(__file__))

@@ -16,7 +16,7 @@ FD_E_STATE = -7
 FD_F32 = 0
 FD_BF16 = 1
 FD_FP8_E4M3 = 2
-FD_EXEC_KERNELS, FD_EXEC_DEPTH_WALK = 0, 1
+FD_EXEC_KERNELS, FD_EXEC_WALK = 0, 1
 
 _DT = {"f32": FD_F32, "bf16": FD_BF16, "fp8": FD_FP8_E4M3}
 
@@ -77,7 +77,7 @@ EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_free", "fd_des
 
 FD_N_KINDS = 9
 KIND_NAMES = ["embed", "qkv", "attention", "o_proj", "gate_up", "down", "final", "depth_in",
-              "depth_walk"]
+              "walk"]
 
 
 def config_from_dict(cfg: dict) -> FdConfig:

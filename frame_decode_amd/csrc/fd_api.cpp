@@ -38,8 +38,9 @@ struct fd_ctx {
     std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> prof_pending;
     double prof_ms[FD_N_KINDS] = {};
     int64_t prof_n[FD_N_KINDS] = {};
-    // persistent walk of the depth stack (built at init when the plan has one)
+    // persistent walk of the whole step (built at init for FD_EXEC_WALK)
     fd::WalkArgs walk{};
+    fd::WalkShape walk_shape{};
     int walk_grid = 0;
     bool walk_launched = false;
     explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context) {}
@@ -300,14 +301,15 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
     return e;
 }
 
-// The depth loop of one frame as a persistent walk: the phase list and the
-// argument blocks of every task, built once here and kept in the workspace.
-// Every phase output gets a region of its own (nothing is overwritten within
-// a launch, so no XCD can hold a stale L2 line of data it reads).
-hipError_t build_depth_walk(fd_ctx* c, hipStream_t s, std::string* err) {
+// The whole step as a persistent walk: the phase list and the argument
+// blocks of every task, built once here and kept in the workspace.  Every
+// phase output gets a region of its own (nothing is overwritten within a
+// launch, so no XCD can hold a stale L2 line of data it reads); the caller's
+// x_in, y_out and depth_out are filled in at each launch.
+hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     const fd::Plan& pl = c->plan;
-    const fd::StackPlan& dp = pl.dstack;
-    const fd::StackDims& dd = dp.dims;
+    const int wt = pl.wt;
+    const uint64_t Sp = pl.Sp;
     uint64_t cur = pl.ws_walk_act;
     const uint64_t end = pl.ws_walk_act + pl.walk_act_bytes;
     auto take = [&](uint64_t bytes) {
@@ -315,12 +317,12 @@ hipError_t build_depth_walk(fd_ctx* c, hipStream_t s, std::string* err) {
         cur += fd::walk_region(bytes);
         return Wk(c, o);
     };
+    auto take_lo = [&](uint64_t bytes) { return wt ? (void*)take(bytes) : nullptr; };
     std::vector<fd::WalkPhase> phases;
     std::vector<fd::GemmArgs> gemm;
     std::vector<fd::AttnArgs> attn;
     std::vector<fd::EmbedArgs> embed;
     std::vector<fd::FinalArgs> fin;
-    const uint64_t Sp = pl.Sp;
     auto gemm_phases = [&](const fd::GemmArgs& g, const fd::GemmShape& sh) {
         const int idx = (int)gemm.size();
         gemm.push_back(g);
@@ -328,153 +330,198 @@ hipError_t build_depth_walk(fd_ctx* c, hipStream_t s, std::string* err) {
         if (sh.P > 1 && g.epi != fd::EPI_PLANES)
             phases.push_back({sh.R == 6 ? fd::WALK_REDUCE6 : fd::WALK_REDUCE4, idx, sh.grid() / sh.P * sh.MTG, 1});
     };
-    auto shaped = [&](fd::GemmArgs g, const fd::GemmShape& sh, uint64_t w_off) {
+    auto shaped = [&](fd::GemmArgs g, const fd::GemmShape& sh, uint64_t w_off, int d) {
         g.W = P(c, w_off);
         g.K = sh.K; g.KB = sh.KB; g.NB = sh.NB; g.P = sh.P; g.MG = sh.MG;
         g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
         g.ss_stride = pl.nss_max;
-        g.inv_d = 1.0f / (float)dd.d;
+        g.inv_d = 1.0f / (float)d;
         g.eps = pl.cfg.rms_eps;
         g.part = sh.P > 1 && g.epi != fd::EPI_PLANES ? (float*)take(4ull * sh.part_floats) : nullptr;
         return g;
     };
-    // input projection c = W_in y
-    {
-        fd::GemmArgs g{};
-        g.X = Wk(c, pl.ws_yw);
-        g.epi = fd::EPI_F32;
-        g.y = (float*)Wk(c, pl.ws_c);
-        g.ld = dd.d;
-        g = shaped(g, pl.win, pl.w_in);
-        g.inv_d = 1.0f / (float)pl.main.dims.d;
-        gemm_phases(g, pl.win);
-    }
-    const uint64_t pos_b = (uint64_t)dd.hd * 4, head_b = pos_b * dd.T, kv_b = head_b * dd.hkv,
-                   layer_b = kv_b * 2, slot_b = layer_b * dd.L;
-    const float* z_prev = nullptr;
-    for (int k = 0; k < dd.T; ++k) {
-        fd::EmbedArgs de{};
-        de.c = (const float*)Wk(c, pl.ws_c);
-        de.z = z_prev;
-        de.active = slot_active(c);
-        de.S = pl.S;
-        de.d = dd.d;
-        de.MT = pl.MT;
-        de.x = (float*)take(4 * Sp * dd.d);
-        de.xg = take(4 * Sp * dd.d);
-        de.g = (const float*)P(c, dd.L > 0 ? dp.layers[0].g_attn : dp.g_final);
-        de.ss_out = (float*)take(4 * Sp * pl.nss_max);
-        de.ss_stride = pl.nss_max;
-        phases.push_back({fd::WALK_EMBED, (int)embed.size(), pl.Sp, 1});
-        embed.push_back(de);
-        const float* x_cur = de.x;
-        const void* xg_cur = de.xg;
-        const float* ss_cur = de.ss_out;
-        int nss = 1;
-        for (int l = 0; l < dd.L; ++l) {
-            const fd::LayerOffsets& lo = dp.layers[l];
+    // rows entering a stack: residual x, its normed activation (bf16: two
+    // parts) and the partial sums of x^2
+    struct Rows {
+        const float* x;
+        const void* xg;
+        const void* xg_lo;
+        const float* ss;
+        int nss;
+    };
+    auto embed_rows = [&](fd::EmbedArgs e, const fd::StackPlan& sp, int kind) {
+        const fd::StackDims& z = sp.dims;
+        e.active = slot_active(c);
+        e.S = pl.S;
+        e.d = z.d;
+        e.MT = pl.MT;
+        e.x = (float*)take(4 * Sp * z.d);
+        e.xg = take(4 * Sp * z.d);
+        e.xg_lo = take_lo(4 * Sp * z.d);
+        e.g = (const float*)P(c, z.L > 0 ? sp.layers[0].g_attn : sp.g_final);
+        e.ss_out = (float*)take(4 * Sp * pl.nss_max);
+        e.ss_stride = pl.nss_max;
+        phases.push_back({kind, (int)embed.size(), pl.Sp, 1});
+        embed.push_back(e);
+        return Rows{e.x, e.xg, e.xg_lo, e.ss_out, 1};
+    };
+    // one decoder stack's layers, as in run_stack
+    auto stack = [&](const fd::StackPlan& sp, const CacheRef& cache, int pos_override, int attn_kind,
+                     int combine_kind, Rows r) {
+        const fd::StackDims& z = sp.dims;
+        for (int l = 0; l < z.L; ++l) {
+            const fd::LayerOffsets& lo = sp.layers[l];
             fd::GemmArgs q{};
-            q.X = xg_cur;
+            q.X = r.xg;
+            q.X_lo = r.xg_lo;
             q.epi = fd::EPI_PLANES;
-            q.y = (float*)take(4ull * dp.qkv.P * Sp * dd.qkv_n());
-            q.ld = dd.qkv_n();
-            q.plane = Sp * dd.qkv_n();
-            q = shaped(q, dp.qkv, lo.qkv);
-            gemm_phases(q, dp.qkv);
+            q.y = (float*)take(4ull * sp.qkv.P * Sp * z.qkv_n());
+            q.ld = z.qkv_n();
+            q.plane = Sp * z.qkv_n();
+            q = shaped(q, sp.qkv, lo.qkv, z.d);
+            gemm_phases(q, sp.qkv);
 
             fd::AttnArgs at{};
             at.qkv = q.y;
-            at.P = dp.qkv.P;
-            at.nqkv = dd.qkv_n();
+            at.P = sp.qkv.P;
+            at.nqkv = z.qkv_n();
             at.plane = q.plane;
-            at.ss_in = ss_cur;
-            at.nss = nss;
+            at.ss_in = r.ss;
+            at.nss = r.nss;
             at.ss_stride = pl.nss_max;
-            at.inv_d = 1.0f / (float)dd.d;
+            at.inv_d = 1.0f / (float)z.d;
             at.eps = pl.cfg.rms_eps;
-            at.rope = (const float*)P(c, dp.rope);
-            at.qscale = (const float*)P(c, dp.qscale) + (size_t)l * dd.hkv;
-            at.kvsig = (const float*)P(c, dp.kvsig) + (size_t)l * 2 * dd.hkv;
-            at.vscale = (const float*)P(c, dp.vscale) + (size_t)l * dd.hkv;
-            at.arena = Wk(c, pl.ws_dkv) + (size_t)l * layer_b;
-            at.slot_stride = slot_b; at.kv_stride = kv_b; at.head_stride = head_b; at.pos_stride = pos_b;
+            at.rope = (const float*)P(c, sp.rope);
+            at.qscale = (const float*)P(c, sp.qscale) + (size_t)l * z.hkv;
+            at.kvsig = (const float*)P(c, sp.kvsig) + (size_t)l * 2 * z.hkv;
+            at.vscale = (const float*)P(c, sp.vscale) + (size_t)l * z.hkv;
+            at.arena = cache.base + (size_t)l * cache.layer;
+            at.slot_stride = cache.slot; at.kv_stride = cache.kv; at.head_stride = cache.head;
+            at.pos_stride = cache.pos;
             at.active = slot_active(c);
             at.pos = slot_pos(c);
-            at.pos_override = k;
-            at.S = pl.S; at.hq = dd.hq; at.hkv = dd.hkv; at.tc = dp.attn.tc; at.n_chunks = dp.attn.n_chunks;
-            at.T = dd.T;
+            at.pos_override = pos_override;
+            at.S = pl.S; at.hq = z.hq; at.hkv = z.hkv; at.tc = sp.attn.tc; at.n_chunks = sp.attn.n_chunks;
+            at.T = z.T;
             at.MT = pl.MT;
-            at.part = dp.attn.n_chunks > 1
-                          ? (float*)take(4ull * pl.S * dd.hkv * dp.attn.n_chunks * dd.G() * (dd.hd + 2))
+            at.part = sp.attn.n_chunks > 1
+                          ? (float*)take(4ull * pl.S * z.hkv * sp.attn.n_chunks * z.G() * (z.hd + 2))
                           : nullptr;
-            at.o_out = take(4 * Sp * dd.hq * dd.hd);
+            at.o_out = take(4 * Sp * z.hq * z.hd);
+            at.o_lo = take_lo(4 * Sp * z.hq * z.hd);
             const int ai = (int)attn.size();
             attn.push_back(at);
-            phases.push_back({fd::WALK_ATTN, ai, pl.S * dd.hkv * dp.attn.n_chunks, 1});
-            if (dp.attn.n_chunks > 1) phases.push_back({fd::WALK_COMBINE, ai, pl.S * dd.hkv * dd.G(), 1});
+            phases.push_back({attn_kind, ai, pl.S * z.hkv * sp.attn.n_chunks, 1});
+            if (sp.attn.n_chunks > 1) phases.push_back({combine_kind, ai, pl.S * z.hkv * z.G(), 1});
 
             fd::GemmArgs o{};
             o.X = at.o_out;
+            o.X_lo = at.o_lo;
             o.epi = fd::EPI_RESID;
-            o.x_src = x_cur;
-            o.x = (float*)take(4 * Sp * dd.d);
-            o.xg = take(4 * Sp * dd.d);
+            o.x_src = r.x;
+            o.x = (float*)take(4 * Sp * z.d);
+            o.xg = take(4 * Sp * z.d);
+            o.xg_lo = take_lo(4 * Sp * z.d);
             o.g_next = (const float*)P(c, lo.g_ffn);
             o.ss_out = (float*)take(4 * Sp * pl.nss_max);
-            o.ld = dd.d;
-            o = shaped(o, dp.o, lo.o);
-            gemm_phases(o, dp.o);
+            o.ld = z.d;
+            o = shaped(o, sp.o, lo.o, z.d);
+            gemm_phases(o, sp.o);
 
             fd::GemmArgs u{};
             u.X = o.xg;
+            u.X_lo = o.xg_lo;
             u.epi = fd::EPI_GU;
             u.ss_in = o.ss_out;
-            u.nss = dp.o.n_groups;
-            u.h_out = take(4 * Sp * dd.f);
-            u.F = dd.f;
-            u = shaped(u, dp.gu, lo.gu);
-            gemm_phases(u, dp.gu);
+            u.nss = sp.o.n_groups;
+            u.h_out = take(4 * Sp * z.f);
+            u.h_lo = take_lo(4 * Sp * z.f);
+            u.F = z.f;
+            u = shaped(u, sp.gu, lo.gu, z.d);
+            gemm_phases(u, sp.gu);
 
             fd::GemmArgs dn{};
             dn.X = u.h_out;
+            dn.X_lo = u.h_lo;
             dn.epi = fd::EPI_RESID;
             dn.x_src = o.x;
-            dn.x = (float*)take(4 * Sp * dd.d);
-            dn.xg = take(4 * Sp * dd.d);
-            dn.g_next = (const float*)P(c, l + 1 < dd.L ? dp.layers[l + 1].g_attn : dp.g_final);
+            dn.x = (float*)take(4 * Sp * z.d);
+            dn.xg = take(4 * Sp * z.d);
+            dn.xg_lo = take_lo(4 * Sp * z.d);
+            dn.g_next = (const float*)P(c, l + 1 < z.L ? sp.layers[l + 1].g_attn : sp.g_final);
             dn.ss_out = (float*)take(4 * Sp * pl.nss_max);
-            dn.ld = dd.d;
-            dn = shaped(dn, dp.down, lo.down);
-            gemm_phases(dn, dp.down);
-            x_cur = dn.x;
-            xg_cur = dn.xg;
-            ss_cur = dn.ss_out;
-            nss = dp.down.n_groups;
+            dn.ld = z.d;
+            dn = shaped(dn, sp.down, lo.down, z.d);
+            gemm_phases(dn, sp.down);
+            r = Rows{dn.x, dn.xg, dn.xg_lo, dn.ss_out, sp.down.n_groups};
         }
-        fd::FinalArgs f{};
-        f.x = x_cur;
-        f.ss = ss_cur;
-        f.nss = nss;
+        return r;
+    };
+    auto final_rows = [&](fd::FinalArgs f, const fd::StackPlan& sp, const Rows& r) {
+        f.x = r.x;
+        f.ss = r.ss;
+        f.nss = r.nss;
         f.ss_stride = pl.nss_max;
-        f.inv_d = 1.0f / (float)dd.d;
+        f.inv_d = 1.0f / (float)sp.dims.d;
         f.eps = pl.cfg.rms_eps;
-        f.g = (const float*)P(c, dp.g_final);
+        f.g = (const float*)P(c, sp.g_final);
         f.active = slot_active(c);
         f.S = pl.S;
-        f.d = dd.d;
+        f.d = sp.dims.d;
         f.MT = pl.MT;
-        f.ldy = dd.T * dd.d;
-        f.y_off = k * dd.d;
-        f.zf = (float*)take(4 * Sp * dd.d);
-        f.advance = 0;
-        phases.push_back({fd::WALK_FINAL_OUT, (int)fin.size(), pl.Sp, k + 1 < dd.T ? 1 : 0});
-        fin.push_back(f);
-        z_prev = f.zf;
+        return f;
+    };
+
+    // main stack
+    const fd::StackPlan& mp = pl.main;
+    Rows r = embed_rows(fd::EmbedArgs{}, mp, fd::WALK_EMBED_IN);
+    CacheRef mc{(uint8_t*)c->buf.kv_arena, pl.kv_slot_stride, pl.kv_layer_stride, pl.kv_kv_stride,
+                pl.kv_head_stride, pl.kv_pos_stride, pl.kv_fp8};
+    r = stack(mp, mc, -1, fd::WALK_ATTN, fd::WALK_COMBINE, r);
+    fd::FinalArgs mf = final_rows(fd::FinalArgs{}, mp, r);
+    mf.ldy = mp.dims.d;
+    mf.y_off = 0;
+    mf.yw = pl.depth ? take(4 * Sp * mp.dims.d) : nullptr;
+    mf.pos = slot_pos(c);
+    mf.advance = 1;
+    phases.push_back({fd::WALK_FINAL_MAIN, (int)fin.size(), pl.Sp, pl.depth ? 1 : 0});
+    fin.push_back(mf);
+
+    if (pl.depth) {
+        const fd::StackPlan& dp = pl.dstack;
+        const fd::StackDims& dd = dp.dims;
+        // input projection c = W_in y
+        fd::GemmArgs g{};
+        g.X = mf.yw;
+        g.epi = fd::EPI_F32;
+        g.y = (float*)take(4 * Sp * dd.d);
+        g.ld = dd.d;
+        g = shaped(g, pl.win, pl.w_in, mp.dims.d);
+        gemm_phases(g, pl.win);
+        const uint64_t pos_b = (uint64_t)dd.hd * 4, head_b = pos_b * dd.T, kv_b = head_b * dd.hkv,
+                       layer_b = kv_b * 2, slot_b = layer_b * dd.L;
+        CacheRef dc{Wk(c, pl.ws_dkv), slot_b, layer_b, kv_b, head_b, pos_b, 0};
+        const float* z_prev = nullptr;
+        for (int k = 0; k < dd.T; ++k) {
+            fd::EmbedArgs de{};
+            de.c = g.y;
+            de.z = z_prev;
+            Rows dr = embed_rows(de, dp, fd::WALK_EMBED);
+            dr = stack(dp, dc, k, fd::WALK_ATTN_DEPTH, fd::WALK_COMBINE_DEPTH, dr);
+            fd::FinalArgs f = final_rows(fd::FinalArgs{}, dp, dr);
+            f.ldy = dd.T * dd.d;
+            f.y_off = k * dd.d;
+            f.zf = (float*)take(4 * Sp * dd.d);
+            f.advance = 0;
+            phases.push_back({fd::WALK_FINAL_DEPTH, (int)fin.size(), pl.Sp, k + 1 < dd.T ? 1 : 0});
+            fin.push_back(f);
+            z_prev = f.zf;
+        }
     }
     if (cur > end || (int)phases.size() > pl.walk_max_phases || (int)gemm.size() > pl.walk_max_gemm ||
         (int)attn.size() > pl.walk_max_attn || (int)embed.size() > pl.walk_max_embed ||
         (int)fin.size() > pl.walk_max_fin) {
-        *err = "depth walk layout exceeds its plan";
+        *err = "walk layout exceeds its plan";
         return hipErrorInvalidValue;
     }
     // argument region: [phases][gemm][attn][embed][fin], each block 256-aligned
@@ -482,7 +529,7 @@ hipError_t build_depth_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     uint64_t o = 0;
     auto put = [&](const void* src, uint64_t bytes) {
         const uint64_t at = o;
-        std::memcpy(host.data() + at, src, bytes);
+        if (bytes) std::memcpy(host.data() + at, src, bytes);
         o = fd::align_up(o + bytes);
         return at;
     };
@@ -495,7 +542,7 @@ hipError_t build_depth_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     const uint64_t e_o = put(embed.data(), embed.size() * sizeof(fd::EmbedArgs));
     const uint64_t f_o = put(fin.data(), fin.size() * sizeof(fd::FinalArgs));
     if (o > pl.walk_args_bytes) {
-        *err = "depth walk arguments exceed their region";
+        *err = "walk arguments exceed their region";
         return hipErrorInvalidValue;
     }
     uint8_t* dev = Wk(c, pl.ws_walk_args);
@@ -509,10 +556,18 @@ hipError_t build_depth_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     w.attn = (const fd::AttnArgs*)(dev + a_o);
     w.embed = (const fd::EmbedArgs*)(dev + e_o);
     w.fin = (const fd::FinalArgs*)(dev + f_o);
-    w.out = nullptr;
+    w.x_in = nullptr;
+    w.y_out = nullptr;
+    w.depth_out = nullptr;
     w.bar = (unsigned*)Wk(c, pl.ws_walk_bar);
     w.abort_flag = (int*)(Wk(c, pl.ws_walk_bar) + 64);
-    c->walk_grid = fd::walk_grid(dp.qkv.MTG, dd.hd, dd.G());
+    c->walk_shape = fd::WalkShape{wt, pl.kv_fp8 ? 1 : 0, mp.qkv.MTG, mp.dims.hd, mp.dims.G(),
+                                  pl.depth ? pl.dstack.dims.hd : 0};
+    c->walk_grid = fd::walk_grid(c->walk_shape);
+    if (c->walk_grid <= 0) {
+        *err = "no co-resident grid for the walk kernel of this shape";
+        return hipErrorInvalidValue;
+    }
     return hipSuccess;
 }
 
@@ -623,7 +678,7 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
     }
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     std::string werr;
-    if (e == hipSuccess && p.dwalk) e = build_depth_walk(c, s, &werr);
+    if (e == hipSuccess && p.walk) e = build_walk(c, s, &werr);
     if (e != hipSuccess) {
         std::string msg = std::string("fd_init: ") + (werr.empty() ? hipGetErrorString(e) : werr.c_str());
         fd_destroy(c);
@@ -674,6 +729,18 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
     hipError_t e = flush_slots(c, st);
     if (e != hipSuccess) return hip_fail(c, e, "slot table upload");
 
+    if (pl.walk) {
+        fd::WalkArgs w = c->walk;
+        w.x_in = x_in;
+        w.y_out = y_out;
+        w.depth_out = depth_out;
+        e = timed(c, K_WALK, st, [&] { return fd::launch_walk(w, c->walk_shape, c->walk_grid, st); });
+        if (e != hipSuccess) return hip_fail(c, e, "fd_step launch");
+        c->walk_launched = true;
+        c->slots.advance();
+        return FD_OK;
+    }
+
     const fd::StackPlan& mp = pl.main;
     const fd::StackDims& md = mp.dims;
     fd::EmbedArgs em{};
@@ -714,15 +781,7 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
         f.advance = 1;
         e = timed(c, K_FINAL, st, [&] { return fd::launch_final(f, pl.wt, pl.Sp, st); });
     }
-    if (e == hipSuccess && pl.depth && pl.dwalk && c->walk_grid > 0) {
-        const fd::StackDims& dd = pl.dstack.dims;
-        fd::WalkArgs w = c->walk;
-        w.out = depth_out;
-        e = timed(c, K_WALK, st, [&] {
-            return fd::launch_walk(w, pl.dstack.qkv.MTG, dd.hd, dd.G(), c->walk_grid, st);
-        });
-        c->walk_launched = true;
-    } else if (e == hipSuccess && pl.depth) {
+    if (e == hipSuccess && pl.depth) {
         const fd::StackPlan& dp = pl.dstack;
         const fd::StackDims& dd = dp.dims;
         fd::GemmArgs g{};
@@ -872,7 +931,7 @@ fd_status fd_sync(fd_ctx* c, void* stream) {
         e = hipMemcpy(&flag, c->walk.abort_flag, sizeof(int), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return hip_fail(c, e, "fd_sync");
         c->walk_launched = false;
-        if (flag) return fail(c, FD_E_DEVICE, "depth walk: a grid barrier timed out");
+        if (flag) return fail(c, FD_E_DEVICE, "walk: a grid barrier wait timed out");
     }
     return FD_OK;
 }

@@ -117,12 +117,17 @@ struct KvWriteArgs {
     int hkv, hd, t0, n, kv_fp8;
 };
 
-// Persistent stack walk: one cooperative launch runs a list of phases, each
-// over n_items workgroup tasks (the bodies of the separate kernels), with a
-// grid barrier after every phase whose outputs a later one reads.
+// Persistent walk: one cooperative launch runs a list of phases, each over
+// n_items workgroup tasks (the bodies of the separate kernels), with a grid
+// barrier after every phase whose outputs a later one reads.
 enum WalkKind : int {
-    WALK_GEMM4 = 0, WALK_GEMM6, WALK_REDUCE4, WALK_REDUCE6, WALK_ATTN, WALK_COMBINE,
-    WALK_EMBED, WALK_FINAL, WALK_FINAL_OUT
+    WALK_GEMM4 = 0, WALK_GEMM6, WALK_REDUCE4, WALK_REDUCE6,
+    WALK_ATTN, WALK_COMBINE,               // main stack attention (and chunk merge)
+    WALK_ATTN_DEPTH, WALK_COMBINE_DEPTH,   // depth stack attention
+    WALK_EMBED,                            // rows from EmbedArgs (depth input c + z)
+    WALK_EMBED_IN,                         // rows of the launch's x_in
+    WALK_FINAL_MAIN,                       // final norm into the launch's y_out, positions advance
+    WALK_FINAL_DEPTH                       // final norm of a depth step into the launch's depth_out
 };
 
 struct WalkPhase {
@@ -136,9 +141,18 @@ struct WalkArgs {
     const AttnArgs* attn;
     const EmbedArgs* embed;
     const FinalArgs* fin;
-    void* out;             // y_out of WALK_FINAL_OUT phases (the caller's rows)
+    const void* x_in;      // the caller's buffers of this step
+    void* y_out;
+    void* depth_out;
     unsigned* bar;         // barrier counter, zeroed before the launch
     int* abort_flag;       // set when a barrier wait times out
+};
+
+// Shape a walk kernel is compiled for: weight / cache types, m-tiles per
+// GEMM m-group, head_dim and query heads per kv head of the main stack, and
+// head_dim of the depth stack (0: none).
+struct WalkShape {
+    int wt, fp8, MTG, hd, G, dhd;
 };
 
 // Depth of a GEMM wave's register ring of k-tiles: as deep as ~48
@@ -156,12 +170,10 @@ hipError_t launch_embed(const EmbedArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
-// Persistent walk of an fp32 stack with MTG m-tiles per m-group (1..4),
-// head_dim 128 and G = 1 query heads per kv head.  walk_supported() says
-// whether a shape has a compiled walk; walk_grid() is the co-resident grid
-// (0 if none); launch_walk() zeroes the barrier state and launches.
-bool walk_supported(int MTG, int hd, int G);
-int walk_grid(int MTG, int hd, int G);
-hipError_t launch_walk(const WalkArgs& w, int MTG, int hd, int G, int grid, hipStream_t st);
+// Persistent walk: walk_grid() is the co-resident grid of the shape's
+// compiled kernel (0 if the shape has none); launch_walk() zeroes the
+// barrier state and launches.
+int walk_grid(const WalkShape& s);
+hipError_t launch_walk(const WalkArgs& w, const WalkShape& s, int grid, hipStream_t st);
 
 }  // namespace fd

@@ -170,13 +170,9 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         *err = "kv_dtype must be FD_F32 or FD_FP8_E4M3";
         return FD_E_UNSUPPORTED;
     }
-    if (c.exec_mode != FD_EXEC_KERNELS && c.exec_mode != FD_EXEC_DEPTH_WALK) {
-        *err = "exec_mode must be FD_EXEC_KERNELS or FD_EXEC_DEPTH_WALK";
+    if (c.exec_mode != FD_EXEC_KERNELS && c.exec_mode != FD_EXEC_WALK) {
+        *err = "exec_mode must be FD_EXEC_KERNELS or FD_EXEC_WALK";
         return FD_E_INVAL;
-    }
-    if (c.exec_mode == FD_EXEC_DEPTH_WALK && c.depth_steps <= 0) {
-        *err = "FD_EXEC_DEPTH_WALK needs a depth stack";
-        return FD_E_UNSUPPORTED;
     }
     if (!(c.rms_eps >= 0.0f) || !std::isfinite(c.rms_eps)) {
         *err = "rms_eps must be finite and >= 0";
@@ -305,44 +301,61 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         p.ws_dkv = take(Sp * z.L * 2ull * z.hkv * z.T * z.hd * 4);
         p.dstack.kv_off = p.ws_dkv;
     }
-    if (p.depth) {
-        // The walk is compiled for fp32 stacks with head_dim 128, one query
-        // head per kv head and at most 4 row tiles.
-        const StackPlan& dp = p.dstack;
-        const StackDims& z = dp.dims;
-        p.dwalk = c.exec_mode == FD_EXEC_DEPTH_WALK;
-        if (p.dwalk && !(!p.wt && !p.kv_fp8 && z.hd == 128 && z.G() == 1 && p.MT <= 4 &&
-                         dp.qkv.MG == 1 && dp.qkv.MTG <= 4)) {
-            *err = "FD_EXEC_DEPTH_WALK needs an fp32 depth stack with depth_head_dim 128, one query "
-                   "head per kv head and at most 64 slots";
+    p.walk = c.exec_mode == FD_EXEC_WALK;
+    if (p.walk) {
+        const StackDims& m = p.main.dims;
+        const int dhd = p.depth ? p.dstack.dims.hd : 0, dG = p.depth ? p.dstack.dims.G() : 0;
+        if (!walk_shape_compiled(p.wt, p.kv_fp8, p.main.qkv.MTG, m.hd, m.G(), dhd, dG) ||
+            (p.depth && p.dstack.qkv.MTG != p.main.qkv.MTG)) {
+            *err = "FD_EXEC_WALK is compiled for: fp32 with head_dim 64, G 1, no depth stack, <= 32 "
+                   "slots; fp32 with head_dim 256, G 4 and a depth stack of head_dim 128, G 1, <= 64 "
+                   "slots; bf16 weights with an FP8 cache, head_dim 128, G 1, no depth stack, <= 80 "
+                   "slots per m-group";
             return FD_E_UNSUPPORTED;
         }
-        if (p.dwalk) {
-            const uint64_t f4 = 4;
-            uint64_t per_layer = 0, per_step = 0;
-            per_layer += walk_region(f4 * dp.qkv.P * Sp * z.qkv_n());           // QKV planes
-            per_layer += walk_region(f4 * Sp * z.hq * z.hd);                     // o
-            if (dp.attn.n_chunks > 1)
-                per_layer += walk_region(f4 * p.S * z.hkv * dp.attn.n_chunks * z.G() * (z.hd + 2));
-            for (const GemmShape* g : {&dp.o, &dp.gu, &dp.down})
-                if (g->P > 1) per_layer += walk_region(f4 * g->part_floats);       // k-split partials
-            per_layer += 2 * (2 * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max));  // x, xg, ss x2
-            per_layer += walk_region(f4 * Sp * z.f);                              // h
-            per_step += 2 * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max);  // embed x, xg, ss
-            per_step += walk_region(f4 * Sp * z.d);                               // z_k
-            p.walk_act_bytes = (uint64_t)z.T * (per_step + (uint64_t)z.L * per_layer);
+        // every cross-phase output gets a region of its own; sizes at 4 bytes
+        // per element (bf16 parts use half)
+        const uint64_t f4 = 4;
+        auto stack_layer = [&](const StackPlan& sp) {
+            const StackDims& z = sp.dims;
+            uint64_t b = 0;
+            b += walk_region(f4 * sp.qkv.P * Sp * z.qkv_n());                      // QKV planes
+            b += (p.wt ? 2 : 1) * walk_region(f4 * Sp * z.hq * z.hd);             // o (+ low part)
+            if (sp.attn.n_chunks > 1)
+                b += walk_region(f4 * p.S * z.hkv * sp.attn.n_chunks * z.G() * (z.hd + 2));
+            for (const GemmShape* g : {&sp.o, &sp.gu, &sp.down})
+                if (g->P > 1) b += walk_region(f4 * g->part_floats);                // k-split partials
+            // x, xg (+ low part), ss after O and after down
+            b += 2 * ((p.wt ? 3 : 2) * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max));
+            b += (p.wt ? 2 : 1) * walk_region(f4 * Sp * z.f);                      // h (+ low part)
+            return b;
+        };
+        auto stack_in = [&](const StackDims& z) {   // embed: x, xg (+ low part), ss
+            return (p.wt ? 3 : 2) * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max);
+        };
+        p.walk_act_bytes = stack_in(m) + (uint64_t)m.L * stack_layer(p.main);
+        p.walk_max_gemm = 4 * m.L;
+        p.walk_max_attn = m.L;
+        p.walk_max_embed = 1;
+        p.walk_max_fin = 1;
+        p.walk_max_phases = 2 + m.L * 9;
+        if (p.depth) {
+            const StackDims& z = p.dstack.dims;
+            p.walk_act_bytes += walk_region(f4 * Sp * m.d) + walk_region(f4 * Sp * z.d);  // y (W_in input), c
             if (p.win.P > 1) p.walk_act_bytes += walk_region(f4 * p.win.part_floats);
-            p.walk_max_gemm = 1 + z.T * z.L * 4;
-            p.walk_max_attn = z.T * z.L;
-            p.walk_max_embed = z.T;
-            p.walk_max_fin = z.T;
-            p.walk_max_phases = 2 + z.T * (2 + z.L * 9);
-            const int slots = p.walk_max_gemm + p.walk_max_attn + p.walk_max_embed + p.walk_max_fin;
-            p.walk_args_bytes = align_up((uint64_t)slots * kWalkArgSlot + (uint64_t)p.walk_max_phases * 16);
-            p.ws_walk_act = take(p.walk_act_bytes);
-            p.ws_walk_args = take(p.walk_args_bytes);
-            p.ws_walk_bar = take(256);
+            p.walk_act_bytes += (uint64_t)z.T * (stack_in(z) + walk_region(f4 * Sp * z.d) +  // z_k
+                                                 (uint64_t)z.L * stack_layer(p.dstack));
+            p.walk_max_gemm += 1 + z.T * z.L * 4;
+            p.walk_max_attn += z.T * z.L;
+            p.walk_max_embed += z.T;
+            p.walk_max_fin += z.T;
+            p.walk_max_phases += 2 + z.T * (2 + z.L * 9);
         }
+        const int slots = p.walk_max_gemm + p.walk_max_attn + p.walk_max_embed + p.walk_max_fin;
+        p.walk_args_bytes = align_up((uint64_t)slots * kWalkArgSlot + (uint64_t)p.walk_max_phases * 16);
+        p.ws_walk_act = take(p.walk_act_bytes);
+        p.ws_walk_args = take(p.walk_args_bytes);
+        p.ws_walk_bar = take(256);
     }
     p.ws_err = take(64);
     p.workspace_bytes = w;

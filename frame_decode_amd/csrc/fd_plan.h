@@ -90,9 +90,9 @@ struct Plan {
     uint64_t ws_x = 0, ws_xg = 0, ws_qkv = 0, ws_o = 0, ws_h = 0, ws_c = 0, ws_z = 0, ws_yw = 0;
     uint64_t ws_ss_a = 0, ws_ss_f = 0, ws_part = 0, ws_cnt = 0, ws_apart = 0, ws_acnt = 0;
     uint64_t ws_dkv = 0, ws_err = 0, ws_xg_lo = 0, ws_h_lo = 0, ws_o_lo = 0;
-    // persistent walk of the depth stack (one launch per frame for the 8
-    // sequential steps): whether it is used, and its workspace regions
-    bool dwalk = false;
+    // persistent walk (the whole step as one launch): whether it is used,
+    // and its workspace regions
+    bool walk = false;
     uint64_t ws_walk_act = 0, ws_walk_args = 0, ws_walk_bar = 0;
     uint64_t walk_act_bytes = 0, walk_args_bytes = 0;
     int walk_max_gemm = 0, walk_max_attn = 0, walk_max_embed = 0, walk_max_fin = 0,
@@ -113,6 +113,19 @@ fd_status make_plan(const fd_config& cfg, Plan* out, std::string* err);
 // Bytes of one walk buffer region: every cross-phase output of the walk has
 // a region of its own (no L2 line of it can be stale in another XCD).
 inline uint64_t walk_region(uint64_t bytes) { return align_up(bytes > 0 ? bytes : 4); }
+
+// Shapes the persistent walk kernel is compiled for: fp32 stacks with
+// head_dim 64, one query head per kv head and no depth stack (up to 2
+// m-tiles); fp32 stacks with head_dim 256, 4 query heads per kv head and a
+// depth stack of head_dim 128 with one query head per kv head (up to 4);
+// bf16 weights with an FP8 cache, head_dim 128, one query head per kv head,
+// no depth stack (up to 5).
+inline bool walk_shape_compiled(bool wt, bool fp8, int MTG, int hd, int G, int dhd, int dG) {
+    if (!wt && !fp8 && hd == 64 && G == 1 && dhd == 0) return MTG >= 1 && MTG <= 2;
+    if (!wt && !fp8 && hd == 256 && G == 4 && dhd == 128 && dG == 1) return MTG >= 1 && MTG <= 4;
+    if (wt && fp8 && hd == 128 && G == 1 && dhd == 0) return MTG >= 1 && MTG <= 5;
+    return false;
+}
 
 // Bytes per argument block reserved in the walk's argument region.
 constexpr uint64_t kWalkArgSlot = 512;

@@ -90,9 +90,9 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 }
 
 // Stores of data that another workgroup of the same launch reads (the
-// persistent walk, CO = 1): every 32-bit word is a device-scope store, which
-// is written through the XCD's L2, so no cache flush is needed before the
-// grid barrier.  CO = 0: plain stores (kernel boundaries order the rest).
+// persistent walk, CO = 1): device-scope stores, which are written through
+// the XCD's L2, so no cache flush is needed before the grid barrier.
+// CO = 0: plain stores (kernel boundaries order the rest).
 template <int CO>
 __device__ __forceinline__ void st1(float* p, float v) {
     if constexpr (CO) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -105,31 +105,41 @@ __device__ __forceinline__ void stw(uint32_t* p, uint32_t v) {
     else *p = v;
 }
 
+template <int CO>
+__device__ __forceinline__ void sth(uint16_t* p, uint16_t v) {
+    if constexpr (CO) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// (8-byte aligned p)
+template <int CO>
+__device__ __forceinline__ void st2w(uint32_t* p, u32x2 w) {
+    if constexpr (CO)
+        __hip_atomic_store((unsigned long long*)p, (unsigned long long)w[0] | ((unsigned long long)w[1] << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *(u32x2*)p = w;
+}
+
 // (16-byte aligned p: two 8-byte device-scope stores)
 template <int CO>
 __device__ __forceinline__ void st4(float* p, f32x4 v) {
     if constexpr (CO) {
         const u32x4 w = __builtin_bit_cast(u32x4, v);
-        unsigned long long* q = (unsigned long long*)p;
-        __hip_atomic_store(q, (unsigned long long)w[0] | ((unsigned long long)w[1] << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(q + 1, (unsigned long long)w[2] | ((unsigned long long)w[3] << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        st2w<1>((uint32_t*)p, u32x2{w[0], w[1]});
+        st2w<1>((uint32_t*)p + 2, u32x2{w[2], w[3]});
     } else {
         *(f32x4*)p = v;
     }
 }
 
-// Stores 4 consecutive activations at p (fp32 or bf16; coherent stores are
-// fp32 only).
+// Stores 4 consecutive activations at p (fp32 or bf16).
 template <int WT, int CO = 0>
 __device__ __forceinline__ void store_act4(void* p, size_t idx, f32x4 v) {
-    static_assert(!(WT && CO), "coherent stores are fp32 only");
     if (WT) {
         u32x2 w;
         w[0] = f2bf(v[0]) | (f2bf(v[1]) << 16);
         w[1] = f2bf(v[2]) | (f2bf(v[3]) << 16);
-        *(u32x2*)((uint16_t*)p + idx) = w;
+        st2w<CO>((uint32_t*)((uint16_t*)p + idx), w);
     } else {
         st4<CO>((float*)p + idx, v);
     }
@@ -137,6 +147,7 @@ __device__ __forceinline__ void store_act4(void* p, size_t idx, f32x4 v) {
 
 // Stores 4 consecutive values as bf16 high parts at hi and the bf16-rounded
 // remainders at lo (hi + lo carries ~16 significant bits).
+template <int CO = 0>
 __device__ __forceinline__ void store_split4(void* hi, void* lo, size_t idx, f32x4 v) {
     u32x2 wh, wl;
     uint32_t b[4];
@@ -146,22 +157,22 @@ __device__ __forceinline__ void store_split4(void* hi, void* lo, size_t idx, f32
     wh[1] = b[2] | (b[3] << 16);
     wl[0] = f2bf(v[0] - bf2f(b[0])) | (f2bf(v[1] - bf2f(b[1])) << 16);
     wl[1] = f2bf(v[2] - bf2f(b[2])) | (f2bf(v[3] - bf2f(b[3])) << 16);
-    *(u32x2*)((uint16_t*)hi + idx) = wh;
-    *(u32x2*)((uint16_t*)lo + idx) = wl;
+    st2w<CO>((uint32_t*)((uint16_t*)hi + idx), wh);
+    st2w<CO>((uint32_t*)((uint16_t*)lo + idx), wl);
 }
 
+template <int CO = 0>
 __device__ __forceinline__ void store_split1(void* hi, void* lo, size_t idx, float v) {
     const uint32_t b = f2bf(v);
-    ((uint16_t*)hi)[idx] = (uint16_t)b;
-    ((uint16_t*)lo)[idx] = (uint16_t)f2bf(v - bf2f(b));
+    sth<CO>((uint16_t*)hi + idx, (uint16_t)b);
+    sth<CO>((uint16_t*)lo + idx, (uint16_t)f2bf(v - bf2f(b)));
 }
 
 // Stores one activation (with its bf16 remainder when lo is given).
 template <int WT, int CO = 0>
 __device__ __forceinline__ void store_act1x(void* p, void* lo, size_t idx, float v) {
-    static_assert(!(WT && CO), "coherent stores are fp32 only");
-    if (WT && lo) store_split1(p, lo, idx, v);
-    else if (WT) ((uint16_t*)p)[idx] = (uint16_t)f2bf(v);
+    if (WT && lo) store_split1<CO>(p, lo, idx, v);
+    else if (WT) sth<CO>((uint16_t*)p + idx, (uint16_t)f2bf(v));
     else st1<CO>((float*)p + idx, v);
 }
 
@@ -306,7 +317,6 @@ __device__ __forceinline__ void rstd_phase2(const GemmArgs& a, int rows, const f
 template <int WT, int NG, int MTG, int NWV, int OWN, int CO>
 __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, const int* ti, int ng,
                                             int mt0, int t_lo, int t_hi, const float* s_rstd) {
-    static_assert(!(WT && CO), "coherent stores are fp32 only");
     constexpr int NTL = NG * MTG;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -348,7 +358,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
         if (a.epi == EPI_RESID) {
             const f32x4 xn = aux0[j] + x;
             st4<CO>(a.x + (size_t)m * a.ld + n, xn);
-            if (WT && a.xg_lo) store_split4(a.xg, a.xg_lo, xoff<WT>(m, n, a.MT), xn * aux1[j]);
+            if (WT && a.xg_lo) store_split4<CO>(a.xg, a.xg_lo, xoff<WT>(m, n, a.MT), xn * aux1[j]);
             else store_act4<WT, CO>(a.xg, xoff<WT>(m, n, a.MT), xn * aux1[j]);
             const float sq = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
 #pragma unroll
@@ -361,10 +371,10 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
             const float h1 = x[2] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x[2])) * x[3];
             if (WT) {
                 const uint32_t b0 = f2bf(h0), b1 = f2bf(h1);
-                *(uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, jj, a.MT)) = b0 | (b1 << 16);
+                stw<CO>((uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, jj, a.MT)), b0 | (b1 << 16));
                 if (a.h_lo)
-                    *(uint32_t*)((uint16_t*)a.h_lo + xoff<WT>(m, jj, a.MT)) =
-                        f2bf(h0 - bf2f(b0)) | (f2bf(h1 - bf2f(b1)) << 16);
+                    stw<CO>((uint32_t*)((uint16_t*)a.h_lo + xoff<WT>(m, jj, a.MT)),
+                            f2bf(h0 - bf2f(b0)) | (f2bf(h1 - bf2f(b1)) << 16));
             } else {
                 float* hp = (float*)a.h_out + xoff<WT>(m, jj, a.MT);
                 st1<CO>(hp, h0);
@@ -394,9 +404,16 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
     }
 }
 
+// Callback of a task that runs without a pending grid barrier.
+struct NoWait {
+    __device__ void operator()() const {}
+};
+
 // One workgroup task of a projection; s_acc: 4 * NG * MTG * 64 f32x4 of LDS.
-template <int WT, int NG, int MTG, int STG, int SX, int CO>
-__device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc_mem) {
+// wait(): called once, before the first read of data an earlier phase wrote
+// (the persistent walk's barrier; NoWait for a kernel launch).
+template <int WT, int NG, int MTG, int STG, int SX, int CO, class Wait>
+__device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc_mem, Wait&& wait) {
     typedef typename BFrag<WT>::T BT;
     constexpr int NTL = NG * MTG;
     constexpr int OWN = (NTL + 3) / 4;
@@ -439,7 +456,7 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     constexpr int NB_ = MTG * (1 + SX);
     u32x4 A[STG][NG];
     BT B[STG][NB_];
-    auto load = [&](u32x4 (&Ad)[NG], BT (&Bd)[NB_], int j) {
+    auto load_x = [&](BT (&Bd)[NB_], int j) {
         const int kb = kb0 + wave + 4 * j;
 #pragma unroll
         for (int t = 0; t < MTG; ++t) Bd[t] = __builtin_bit_cast(BT, xp[(size_t)kb * xk + t * 64]);
@@ -447,8 +464,15 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
 #pragma unroll
             for (int t = 0; t < MTG; ++t) Bd[MTG + t] = __builtin_bit_cast(BT, xlp[(size_t)kb * xk + t * 64]);
         }
+    };
+    auto load_w = [&](u32x4 (&Ad)[NG], int j) {
+        const int kb = kb0 + wave + 4 * j;
 #pragma unroll
         for (int r = 0; r < NG; ++r) Ad[r] = __builtin_nontemporal_load(&wp[r][(size_t)kb * 64]);
+    };
+    auto load = [&](u32x4 (&Ad)[NG], BT (&Bd)[NB_], int j) {
+        load_x(Bd, j);
+        load_w(Ad, j);
     };
     // (high parts of every tile first, then low parts: consecutive products
     // never chain on one accumulator)
@@ -462,14 +486,26 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     };
 
     const bool norm_here = a.ss_in != nullptr;
-    // the norm's partial sums are summed first: their loads are few and
-    // short, and issuing them before the weight stream keeps the in-order
-    // load counter from holding the first weights back
-    if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
     // (nmine >= 1: each wave has at least one k-tile; a ring slot past the
     // end re-reads the last tile and is never consumed)
+    if constexpr (CO) {
+        // persistent walk: the weights do not depend on earlier phases, so
+        // the first stages are requested before the barrier wait and stream
+        // while the last workgroups of the previous phase finish
 #pragma unroll
-    for (int s = 0; s < STG - 1; ++s) load(A[s], B[s], min(s, nmine - 1));
+        for (int s = 0; s < STG - 1; ++s) load_w(A[s], min(s, nmine - 1));
+        wait();
+        if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
+#pragma unroll
+        for (int s = 0; s < STG - 1; ++s) load_x(B[s], min(s, nmine - 1));
+    } else {
+        // the norm's partial sums are summed first: their loads are few and
+        // short, and issuing them before the weight stream keeps the in-order
+        // load counter from holding the first weights back
+        if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
+#pragma unroll
+        for (int s = 0; s < STG - 1; ++s) load(A[s], B[s], min(s, nmine - 1));
+    }
     // steady state: every load of a chunk is in range, so the loads are
     // unconditional and the compiler's wait before each product only covers
     // the k-tile it consumes
@@ -538,7 +574,7 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
 template <int WT, int NG, int MTG, int STG, int SX>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     __shared__ f32x4 s_acc[4 * NG * MTG * 64];
-    gemm_wg<WT, NG, MTG, STG, SX, 0>(a, blockIdx.x, s_acc);
+    gemm_wg<WT, NG, MTG, STG, SX, 0>(a, blockIdx.x, s_acc, NoWait{});
 }
 
 // Adds the P k-split partial tiles of one m-tile t of an (n-group, m-group)
@@ -598,6 +634,14 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
 // attn_combine_kernel in chunk order.  All G query heads of the kv head
 // share every load.
 
+// Position loads a wave keeps in flight per block of attention: 8 in a
+// kernel launch (several workgroups per CU; the plan's chunk rounding uses
+// the same count); in the persistent walk (one workgroup per CU) 16 for an
+// FP8 cache, 8 for fp32 (whose wider lanes already hold twice the bytes).
+constexpr int kAttnNit = 8;
+template <int FP8>
+constexpr int walk_attn_nit() { return FP8 ? 16 : 8; }
+
 template <int FP8>
 __device__ __forceinline__ void unpack16(const u32x4& raw, float* out) {
     if constexpr (FP8) {
@@ -619,15 +663,17 @@ __device__ __forceinline__ void unpack16(const u32x4& raw, float* out) {
     }
 }
 
-template <int WT, int FP8, int D, int G, int CO>
-__device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid) {
+// NIT: loads of 64/LPP positions each that a wave keeps in flight per block
+// (8 for a kernel launch with several workgroups per CU; deeper in the
+// persistent walk, which runs one workgroup per CU).  wait(): as for gemm_wg.
+template <int WT, int FP8, int D, int G, int CO, int NIT, class Wait>
+__device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait) {
     constexpr int EB = FP8 ? 1 : 4;
     constexpr int LPP = FP8 ? D / 16 : D / 8;
     constexpr int E = D / LPP;         // elements per lane per position
     constexpr int VE = 16 / EB;        // elements per 16-byte piece
     constexpr int J = E / VE;          // pieces per lane
     constexpr int PPL = 64 / LPP;      // positions per wave load
-    constexpr int NIT = 8;
     constexpr int SUB = NIT * PPL;     // positions per wave block
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -685,6 +731,12 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid) {
         }
     };
     int base = t0 + wave * SUB;
+    if constexpr (CO) {
+        // persistent walk: cached keys were written by earlier launches or
+        // earlier phases, so the first block streams during the barrier wait
+        if (base < t1) load_blk(kbase, base);
+        wait();
+    }
 
     const int nquad = (own_new ? G + 2 : G) * QPH;
     const float ssv = threadIdx.x < a.nss ? a.ss_in[(size_t)s * a.ss_stride + threadIdx.x] : 0.f;
@@ -763,7 +815,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid) {
 #pragma unroll
             for (int i = 0; i < VE; ++i) qv[h][j * VE + i] = s_q[h][(c + LPP * j) * VE + i];
 
-    if (base < t1) load_blk(kbase, base);
+    if (!CO && base < t1) load_blk(kbase, base);
     float mrun[G], lrun[G], acc[G][E];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -895,7 +947,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid) {
 
 template <int WT, int FP8, int D, int G>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-    attn_wg<WT, FP8, D, G, 0>(a, blockIdx.x);
+    attn_wg<WT, FP8, D, G, 0, kAttnNit>(a, blockIdx.x, NoWait{});
 }
 
 // Merges the chunks of one (slot, query head) in chunk order: one
@@ -974,7 +1026,7 @@ __device__ __forceinline__ void embed_row(const EmbedArgs& a, int m) {
             }
         }
         st4<CO>(a.x + (size_t)m * a.d + i, v);
-        if (WT && a.xg_lo) store_split4(a.xg, a.xg_lo, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
+        if (WT && a.xg_lo) store_split4<CO>(a.xg, a.xg_lo, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
         else store_act4<WT, CO>(a.xg, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
@@ -1032,19 +1084,26 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// persistent stack walk
+// persistent walk: the whole step (or the whole depth loop) as one
+// cooperative launch of one workgroup per CU that runs the phases in order,
+// the tasks of a phase spread over the workgroups.
 
-// Grid barrier of a co-resident launch: every workgroup adds itself to a
-// device-scope counter after its stores have completed (the stores that
-// others read are device-scope, see st1), then waits until the counter
-// reaches `target`.  The wait is bounded: a workgroup that waits too long
-// sets the abort flag and every workgroup leaves at its next barrier.
-__device__ __forceinline__ bool grid_barrier(unsigned* cnt, unsigned target, int* abort_flag) {
-    __shared__ int s_ok;
+// Grid barrier of a co-resident launch, in two halves so that a workgroup
+// can request data that does not depend on the barrier in between.
+// Arrive: this workgroup's stores have completed (those that other
+// workgroups read are device-scope, written through to memory), then it adds
+// itself to a device-scope counter.
+__device__ __forceinline__ void walk_arrive(unsigned* cnt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until the counter reaches `target`.  Bounded: a workgroup that waits
+// too long sets the abort flag, and every workgroup leaves at its next wait.
+__device__ __forceinline__ bool walk_wait(unsigned* cnt, unsigned target, int* abort_flag) {
+    __shared__ int s_ok;
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int ok = 1;
         for (unsigned spin = 0;; ++spin) {
             if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
@@ -1061,34 +1120,72 @@ __device__ __forceinline__ bool grid_barrier(unsigned* cnt, unsigned target, int
     return s_ok != 0;
 }
 
-template <int MTG, int D, int G>
+// WT/FP8: weight and cache types of the main stack; MTG: m-tiles per GEMM
+// m-group; D, G: head_dim and query heads per kv head of the main stack;
+// DD: head_dim of the depth stack (0: none; one query head per kv head).
+template <int WT, int FP8, int MTG, int D, int G, int DD>
 __global__ __launch_bounds__(256) void walk_kernel(WalkArgs w) {
     __shared__ f32x4 s_acc[4 * 6 * MTG * 64];
     unsigned target = 0;
-    for (int ph = 0; ph < w.n_phases; ++ph) {
+    bool pending = false, ok = true;
+    // the barrier wait of the previous phase, taken by the first task at the
+    // point where it first needs that phase's results
+    auto wait = [&]() {
+        if (pending) {
+            pending = false;
+            if (!walk_wait(w.bar, target, w.abort_flag)) ok = false;
+        }
+    };
+    for (int ph = 0; ph < w.n_phases && ok; ++ph) {
         const WalkPhase P = w.phases[ph];
         for (int it = blockIdx.x; it < P.n_items; it += gridDim.x) {
             switch (P.kind) {
-                case WALK_GEMM4: gemm_wg<0, 4, MTG, gemm_stages(4, MTG), 0, 1>(w.gemm[P.idx], it, s_acc); break;
-                case WALK_GEMM6: gemm_wg<0, 6, MTG, gemm_stages(6, MTG), 0, 1>(w.gemm[P.idx], it, s_acc); break;
-                case WALK_REDUCE4: gemm_reduce_wg<0, 4, MTG, 1>(w.gemm[P.idx], it); break;
-                case WALK_REDUCE6: gemm_reduce_wg<0, 6, MTG, 1>(w.gemm[P.idx], it); break;
-                case WALK_ATTN: attn_wg<0, 0, D, G, 1>(w.attn[P.idx], it); break;
-                case WALK_COMBINE: attn_combine_wg<0, D, G, 1>(w.attn[P.idx], it); break;
-                case WALK_EMBED: embed_row<0, 1>(w.embed[P.idx], it); break;
-                case WALK_FINAL: final_row<0, 1>(w.fin[P.idx], it); break;
-                case WALK_FINAL_OUT: {
-                    FinalArgs f = w.fin[P.idx];
-                    f.y_out = w.out;
-                    final_row<0, 1>(f, it);
-                } break;
-                default: break;
+                case WALK_GEMM4:
+                    gemm_wg<WT, 4, MTG, gemm_stages(4, MTG, WT), WT, 1>(w.gemm[P.idx], it, s_acc, wait);
+                    break;
+                case WALK_GEMM6:
+                    gemm_wg<WT, 6, MTG, gemm_stages(6, MTG, WT), WT, 1>(w.gemm[P.idx], it, s_acc, wait);
+                    break;
+                case WALK_ATTN: attn_wg<WT, FP8, D, G, 1, walk_attn_nit<FP8>()>(w.attn[P.idx], it, wait); break;
+                case WALK_ATTN_DEPTH:
+                    if constexpr (DD > 0) attn_wg<WT, 0, DD, 1, 1, walk_attn_nit<0>()>(w.attn[P.idx], it, wait);
+                    break;
+                default:
+                    wait();
+                    switch (P.kind) {
+                        case WALK_REDUCE4: gemm_reduce_wg<WT, 4, MTG, 1>(w.gemm[P.idx], it); break;
+                        case WALK_REDUCE6: gemm_reduce_wg<WT, 6, MTG, 1>(w.gemm[P.idx], it); break;
+                        case WALK_COMBINE: attn_combine_wg<WT, D, G, 1>(w.attn[P.idx], it); break;
+                        case WALK_COMBINE_DEPTH:
+                            if constexpr (DD > 0) attn_combine_wg<WT, DD, 1, 1>(w.attn[P.idx], it);
+                            break;
+                        case WALK_EMBED: embed_row<WT, 1>(w.embed[P.idx], it); break;
+                        case WALK_EMBED_IN: {
+                            EmbedArgs e = w.embed[P.idx];
+                            e.x_in = w.x_in;
+                            embed_row<WT, 1>(e, it);
+                        } break;
+                        case WALK_FINAL_MAIN: {
+                            FinalArgs f = w.fin[P.idx];
+                            f.y_out = w.y_out;
+                            final_row<WT, 1>(f, it);
+                        } break;
+                        case WALK_FINAL_DEPTH: {
+                            FinalArgs f = w.fin[P.idx];
+                            f.y_out = w.depth_out;
+                            final_row<WT, 1>(f, it);
+                        } break;
+                        default: break;
+                    }
             }
+            wait();
             __syncthreads();  // LDS of this task is free before the next one
         }
-        if (P.barrier) {
+        wait();  // (a workgroup without tasks in this phase)
+        if (P.barrier && ok) {
             target += gridDim.x;
-            if (!grid_barrier(w.bar, target, w.abort_flag)) return;
+            walk_arrive(w.bar);
+            pending = true;
         }
     }
 }
@@ -1232,26 +1329,35 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// walk shapes compiled: fp32 stacks, head_dim 128, one query head per kv
-// head, up to 4 m-tiles (64 session rows)
-template <int MTG>
-static const void* walk_fn() { return (const void*)walk_kernel<MTG, 128, 1>; }
-
-static const void* walk_fn_for(int MTG, int hd, int G) {
-    if (hd != 128 || G != 1) return nullptr;
-    switch (MTG) {
-        case 1: return walk_fn<1>();
-        case 2: return walk_fn<2>();
-        case 3: return walk_fn<3>();
-        case 4: return walk_fn<4>();
-        default: return nullptr;
-    }
+// Walk shapes compiled (the plan accepts exactly these, walk_shape_compiled):
+// fp32 stacks with head_dim 64, one query head per kv head, no depth stack,
+// up to 2 m-tiles; fp32 stacks with head_dim 256, 4 query heads per kv head
+// and a head_dim-128 depth stack, up to 4 m-tiles; bf16 weights with an FP8
+// cache, head_dim 128, one query head per kv head, no depth stack, up to 5.
+template <int WT, int FP8, int D, int G, int DD, int MTG>
+static const void* walk_fn_one() {
+    return (const void*)walk_kernel<WT, FP8, MTG, D, G, DD>;
 }
 
-bool walk_supported(int MTG, int hd, int G) { return walk_fn_for(MTG, hd, G) != nullptr; }
+template <int WT, int FP8, int D, int G, int DD, int MAXM>
+static const void* walk_fn_mtg(int MTG) {
+    if (MTG < 1 || MTG > MAXM) return nullptr;
+    if constexpr (MAXM >= 5) if (MTG == 5) return walk_fn_one<WT, FP8, D, G, DD, 5>();
+    if constexpr (MAXM >= 4) if (MTG == 4) return walk_fn_one<WT, FP8, D, G, DD, 4>();
+    if constexpr (MAXM >= 3) if (MTG == 3) return walk_fn_one<WT, FP8, D, G, DD, 3>();
+    if constexpr (MAXM >= 2) if (MTG == 2) return walk_fn_one<WT, FP8, D, G, DD, 2>();
+    return walk_fn_one<WT, FP8, D, G, DD, 1>();
+}
 
-int walk_grid(int MTG, int hd, int G) {
-    const void* fn = walk_fn_for(MTG, hd, G);
+static const void* walk_fn_for(const WalkShape& s) {
+    if (!s.wt && !s.fp8 && s.hd == 64 && s.G == 1 && s.dhd == 0) return walk_fn_mtg<0, 0, 64, 1, 0, 2>(s.MTG);
+    if (!s.wt && !s.fp8 && s.hd == 256 && s.G == 4 && s.dhd == 128) return walk_fn_mtg<0, 0, 256, 4, 128, 4>(s.MTG);
+    if (s.wt && s.fp8 && s.hd == 128 && s.G == 1 && s.dhd == 0) return walk_fn_mtg<1, 1, 128, 1, 0, 5>(s.MTG);
+    return nullptr;
+}
+
+int walk_grid(const WalkShape& s) {
+    const void* fn = walk_fn_for(s);
     if (!fn) return 0;
     int dev = 0, ncu = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -1260,8 +1366,8 @@ int walk_grid(int MTG, int hd, int G) {
     return per > 0 ? ncu * per : 0;
 }
 
-hipError_t launch_walk(const WalkArgs& w, int MTG, int hd, int G, int grid, hipStream_t st) {
-    const void* fn = walk_fn_for(MTG, hd, G);
+hipError_t launch_walk(const WalkArgs& w, const WalkShape& s, int grid, hipStream_t st) {
+    const void* fn = walk_fn_for(s);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(walk_reset_kernel, dim3(1), dim3(64), 0, st, w.bar, w.abort_flag);
     hipError_t e = hipGetLastError();

@@ -93,22 +93,30 @@ typedef struct {
     int32_t depth_kv_heads;
     int32_t depth_head_dim;
     int32_t depth_ffn;
-    int32_t exec_mode;    /* FD_EXEC_KERNELS (0) or FD_EXEC_DEPTH_WALK (1), see below */
+    int32_t exec_mode;    /* FD_EXEC_KERNELS (0) or FD_EXEC_WALK (1), see below */
 } fd_config;
 
 /*
  * Execution of a step.  FD_EXEC_KERNELS: fd_step enqueues a fixed sequence
  * of kernels (no host work or synchronisation between them).
- * FD_EXEC_DEPTH_WALK: as FD_EXEC_KERNELS for the main stack, but the depth
- * stack's per-frame loop (input projection, then depth_steps x depth_layers
- * layers) runs as ONE persistent cooperative launch whose workgroups walk the
- * layers with device-side grid barriers (the case study's persistent
- * program, "Under the hood"); supported for fp32 depth stacks with
- * depth_head_dim 128, one query head per kv head and at most 64 slots
- * (FD_E_UNSUPPORTED otherwise).
+ * FD_EXEC_WALK: fd_step enqueues ONE persistent cooperative launch (after a
+ * one-block reset of its barrier counter) whose workgroups, as many as fit
+ * co-resident (one per CU for the larger shapes), walk
+ * the whole step -- embed, every layer's phases, final norm, and the depth
+ * stack's loop when there is one -- with device-side grid barriers between
+ * dependent phases, requesting each next phase's weights (or first cached
+ * keys) before waiting at the barrier (the case study's persistent program,
+ * "Under the hood").  Compiled for three families of shapes; others give
+ * FD_E_UNSUPPORTED at fd_plan: fp32 stacks with head_dim 64, one query head
+ * per kv head and no depth stack (at most 32 slots); fp32 stacks with
+ * head_dim 256, 4 query heads per kv head and a depth stack of head_dim 128
+ * with one query head per kv head (at most 64 slots); bf16 weights with an
+ * FP8 cache, head_dim 128, one query head per kv head, no depth stack.
+ * A barrier wait that times out makes the launch stop early and the next
+ * fd_sync return FD_E_DEVICE.
  */
 #define FD_EXEC_KERNELS 0
-#define FD_EXEC_DEPTH_WALK 1
+#define FD_EXEC_WALK 1
 
 /* Byte sizes of the four caller-allocated device buffers. */
 typedef struct {
@@ -277,7 +285,7 @@ fd_status fd_kv_write(fd_ctx* ctx, int32_t slot, int32_t layer, int32_t t0, int3
  * milliseconds and the number of launches since the last read (then resets).
  * Kinds: 0 embed, 1 qkv, 2 attention, 3 o-projection, 4 gate/up, 5 down,
  * 6 final norm, 7 depth input projection, 8 the persistent walk of the
- * depth stack when one is used (FD_N_KINDS = 9).  Timing adds a
+ * whole step (FD_EXEC_WALK; then the only kind launched) (FD_N_KINDS = 9).  Timing adds a
  * small gap between launches; headline step times are taken with it off.
  */
 #define FD_N_KINDS 9

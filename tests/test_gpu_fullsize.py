@@ -115,10 +115,13 @@ def _check_new_codes(ctx, orc, cfg, slots, pos):
         check(same > 0.8 and bad <= 1.0, f"slot {s}: appended codes differ from the oracle's")
 
 
-def test_7b_eight_sessions_at_position_256(model7b):
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+def test_7b_eight_sessions_at_position_256(model7b, exec_mode):
     """The 8-session workload in full: 32 layers, every session's cache
-    prefilled to 256 positions, new frame at index 256; every row checked."""
+    prefilled to 256 positions, new frame at index 256; every row checked
+    (kernel sequence and persistent walk)."""
     cfg = synth.get_config("7b_s8_p256")
+    cfg["exec_mode"] = exec_mode
     p0 = cfg["position"]
     say("C2: context")
     ctx = make_context(cfg, model7b)
@@ -143,10 +146,13 @@ def test_7b_eight_sessions_at_position_256(model7b):
     ctx.fd_destroy()
 
 
-def test_7b_eighty_sessions_full_window_sampled(model7b):
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+def test_7b_eighty_sessions_full_window_sampled(model7b, exec_mode):
     """80 sessions at the full 1500-frame window (new frame at index 1499):
-    every slot stepped, three seeded sessions recomputed by the oracle."""
+    every slot stepped, three seeded sessions recomputed by the oracle
+    (kernel sequence and persistent walk)."""
     cfg = synth.get_config("7b_s80_p1499")
+    cfg["exec_mode"] = exec_mode
     p0 = cfg["position"]
     say("C3: context")
     ctx = make_context(cfg, model7b)
@@ -275,13 +281,13 @@ def test_7b_ragged_with_admission_and_retirement(model7b):
     ctx.fd_destroy()
 
 
-@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "depth_walk"])
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
 def test_talker_fifty_six_sessions_with_depth_loop_sampled(exec_mode):
     """The talker workload in full (26-layer fp32 main stack with GQA 4:1 and
     head_dim 256, 56 sessions at index 1499, then the 8-step depth loop of
-    the 6-layer depth stack, as separate launches or as one persistent
-    walk): two seeded sessions recomputed, 1e-3 on the main output and on
-    all eight depth outputs."""
+    the 6-layer depth stack, as separate launches or the whole step as one
+    persistent walk): two seeded sessions recomputed, 1e-3 on the main
+    output and on all eight depth outputs."""
     cfg = synth.get_config("talker_s56")
     cfg["exec_mode"] = exec_mode
     p0 = cfg["position"]

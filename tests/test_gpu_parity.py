@@ -160,22 +160,25 @@ def _check_cache(ctx, orc, cfg, slots, pos, start):
             assert err < 1e-4, f"slot {s}: cache values differ by {err:.3e}"
 
 
-def test_tiny_fp32_sixteen_frames():
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+def test_tiny_fp32_sixteen_frames(exec_mode):
     """Two sessions x 16 frames from an empty fp32 cache (the tiny
     workload), 1e-3, with the cache checked byte-for-byte against the
-    sentinel fill."""
+    sentinel fill; as a kernel sequence and as one persistent walk."""
     cfg = synth.get_config("tiny")
+    cfg["exec_mode"] = exec_mode
     model = synth.Model(cfg, gain_noise=True)
     ctx, orc, slots, pos, worst = _run_steps(cfg, model, [0, 0], 16, tol=1e-3)
     _check_cache(ctx, orc, cfg, slots, pos, {s: 0 for s in slots})
 
 
-def test_bf16_fp8_ragged_multichunk():
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+def test_bf16_fp8_ragged_multichunk(exec_mode):
     """bf16 weights/activations, FP8 cache, 7B head geometry (128-dim MHA)
     at reduced width and depth; slots at positions spanning 1..3 attention
-    chunks, one slot left empty."""
+    chunks, one slot left empty; kernel sequence and persistent walk."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
-                              d_ffn=1536, max_slots=9, max_context=700)
+                              d_ffn=1536, max_slots=9, max_context=700, exec_mode=exec_mode)
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 1, 255, 256, 257, 300, 511, 690]
     # this window is short enough for one chunk by default: ask the plan
@@ -188,11 +191,11 @@ def test_bf16_fp8_ragged_multichunk():
     _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
 
 
-@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "depth_walk"])
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
 def test_fp32_gqa_with_depth_loop(exec_mode):
     """Talker geometry (GQA 4:1, head_dim 256, fp32) at reduced width, with
     the 8-step depth loop of a 128-dim-head stack (as separate launches and
-    as one persistent walk); 1e-3."""
+    as one persistent walk of the whole step); 1e-3."""
     cfg = synth.scaled_config("talker_s56", n_layers=2, d_model=384, d_ffn=768, max_slots=5,
                               max_context=300, depth_layers=2, depth_d=256, depth_heads=2,
                               depth_kv_heads=2, depth_ffn=512, exec_mode=exec_mode)
@@ -249,11 +252,12 @@ def test_admission_and_free_keep_launch_shape():
             frames_b[s] += 1
 
 
-def test_deterministic_and_isolated():
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+def test_deterministic_and_isolated(exec_mode):
     """Two runs give bit-identical outputs; changing other slots' inputs
-    and caches leaves a session's output bit-identical."""
+    and caches leaves a session's output bit-identical (both modes)."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
-                              d_ffn=1024, max_slots=6, max_context=400)
+                              d_ffn=1024, max_slots=6, max_context=400, exec_mode=exec_mode)
     model = synth.Model(cfg)
     say("determinism: ctx")
     ctx = make_context(cfg, model)

@@ -123,18 +123,26 @@ def test_depth_stack_needs_fp32(host):
     assert st == FD_E_UNSUPPORTED
 
 
-def test_depth_walk_mode(host):
-    """The persistent depth walk is planned for the talker's fp32 depth
-    stack (it needs workspace for its own buffers) and refused elsewhere."""
-    cfg = synth.get_config("talker_s56")
-    st0, s0 = _plan(host, cfg)
-    cfg["exec_mode"] = 1
-    st1, s1 = _plan(host, cfg)
-    assert st0 == FD_OK and st1 == FD_OK and s1.workspace > s0.workspace
-    assert s1.packed_weights == s0.packed_weights and s1.kv_arena == s0.kv_arena
-    no_depth = synth.get_config("7b_s8_p256")
-    no_depth["exec_mode"] = 1
-    assert _plan(host, no_depth)[0] == FD_E_UNSUPPORTED
+def test_walk_mode(host):
+    """The persistent walk of the whole step is planned for the three
+    compiled shape families (it needs workspace for its own buffers) and
+    refused for other shapes and for unknown modes."""
+    for name in ("tiny", "7b_s8_p256", "7b_s80_p1499", "7b_ragged_80x56", "talker_s56"):
+        cfg = synth.get_config(name)
+        st0, s0 = _plan(host, cfg)
+        cfg["exec_mode"] = 1
+        st1, s1 = _plan(host, cfg)
+        assert st0 == FD_OK and st1 == FD_OK and s1.workspace > s0.workspace, name
+        assert s1.packed_weights == s0.packed_weights and s1.kv_arena == s0.kv_arena
+    # fp32 7B-shaped stack (head_dim 128 without a depth stack): not compiled
+    f32 = synth.get_config("7b_s8_p256")
+    f32.update(exec_mode=1, w_dtype="f32", act_dtype="f32", kv_dtype="f32")
+    assert _plan(host, f32)[0] == FD_E_UNSUPPORTED
+    # bf16 weights over an fp32 cache: not compiled
+    bf_f32kv = synth.get_config("7b_s8_p256")
+    bf_f32kv.update(exec_mode=1, kv_dtype="f32")
+    assert _plan(host, bf_f32kv)[0] == FD_E_UNSUPPORTED
+    # talker geometry beyond 4 row tiles per m-group
     many = synth.get_config("talker_s56")
     many.update(exec_mode=1, max_slots=80)
     assert _plan(host, many)[0] == FD_E_UNSUPPORTED
