@@ -18,7 +18,13 @@ What the step computes, with the pages it follows:
   page, "Compressing the Temporal KV cache"); the talker cache in fp32
   (Nemotron profile.json, serving_profile precision map).
 * A session's window holds at most 1500 frames (profile.json,
-  serving_profile context_steps).
+  serving_profile context_steps).  Two readings of what happens after the
+  window fills: the fixed window (default) refuses a further frame; the
+  rolling window (``cfg["kv_ring"] = 1``) keeps the session going -- the
+  vLLM-Omni recipe's realtime configuration ("Performance") leaves the
+  session length unbounded -- and attends over the last ``max_context``
+  frames only, each frame keeping its absolute index as its rotary
+  position.
 * The depth stack runs 8 sequential steps per frame (PersonaPlex page,
   "Predictable GPU execution").
 
@@ -86,47 +92,65 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 class Cache:
-    """Per-slot caches of one stack: ``kv[slot]`` is [L][2 (K|V)][H_kv][T][D],
-    uint8 E4M3 codes for an FP8 cache, else values in the oracle dtype."""
+    """Per-slot caches of one stack: ``kv[slot]`` is [L][2 (K|V)][H_kv][n][D],
+    uint8 E4M3 codes for an FP8 cache, else values in the oracle dtype, with
+    entry t holding the frame of absolute index t.  With a fixed window n is
+    max_context; with a rolling window the history grows as frames arrive
+    and reads cover the last max_context frames."""
 
     def __init__(self, n_layers: int, n_kv_heads: int, max_context: int, head_dim: int,
-                 fp8_cache: bool, dtype=np.float32):
+                 fp8_cache: bool, dtype=np.float32, rolling: bool = False):
         self.shape = (n_layers, 2, n_kv_heads, max_context, head_dim)
+        self.window = max_context
+        self.rolling = rolling
         self.fp8 = fp8_cache
         self.dtype = dtype
         self.kv: dict[int, np.ndarray] = {}
 
-    def slot(self, s: int) -> np.ndarray:
+    def slot(self, s: int, upto: int = 0) -> np.ndarray:
+        """The slot's history, grown (rolling window) to hold frames < upto."""
         if s not in self.kv:
             self.kv[s] = np.zeros(self.shape, dtype=np.uint8 if self.fp8 else self.dtype)
-        return self.kv[s]
+        c = self.kv[s]
+        if upto > c.shape[3]:
+            if not self.rolling:
+                raise ValueError("frame index outside the fixed window")
+            grown = np.zeros(c.shape[:3] + (max(upto, 2 * c.shape[3]),) + c.shape[4:], dtype=c.dtype)
+            grown[:, :, :, :c.shape[3]] = c
+            self.kv[s] = c = grown
+        return c
 
     def store(self, s: int, layer: int, kv: int, pos: int, vec: np.ndarray, scale: np.ndarray):
-        """Write the new frame's [H_kv][D] key or value at ``pos``."""
-        c = self.slot(s)
+        """Write the new frame's [H_kv][D] key or value at frame index ``pos``."""
+        c = self.slot(s, pos + 1)
         if self.fp8:
             c[layer, kv, :, pos, :] = fp8.encode(vec.astype(np.float32) /
                                                  scale.astype(np.float32)[:, None])
         else:
             c[layer, kv, :, pos, :] = vec.astype(self.dtype)
 
-    def prefill(self, s: int, layer: int, values: np.ndarray, scale: np.ndarray):
-        """Fill positions 0..n-1 of one layer from raw values [2][H_kv][n][D]
+    def prefill(self, s: int, layer: int, values: np.ndarray, scale: np.ndarray, t0: int = 0):
+        """Fill frames t0..t0+n-1 of one layer from raw values [2][H_kv][n][D]
         stored the same way as new frames."""
-        c = self.slot(s)
         n = values.shape[2]
+        c = self.slot(s, t0 + n)
         if self.fp8:
-            c[layer, :, :, :n, :] = fp8.encode(values.astype(np.float32) /
-                                               scale.astype(np.float32)[:, :, None, None])
+            c[layer, :, :, t0:t0 + n, :] = fp8.encode(values.astype(np.float32) /
+                                                      scale.astype(np.float32)[:, :, None, None])
         else:
-            c[layer, :, :, :n, :] = values.astype(self.dtype)
+            c[layer, :, :, t0:t0 + n, :] = values.astype(self.dtype)
 
-    def read(self, s: int, layer: int, kv: int, g: int, n: int, scale: float) -> np.ndarray:
-        """Positions 0..n-1 of kv-head g read back: [n][D] in the oracle dtype."""
-        c = self.slot(s)[layer, kv, g, :n, :]
+    def read(self, s: int, layer: int, kv: int, g: int, lo: int, hi: int, scale: float) -> np.ndarray:
+        """Frames lo..hi-1 of kv-head g read back: [hi-lo][D] in the oracle dtype."""
+        c = self.slot(s, hi)[layer, kv, g, lo:hi, :]
         if self.fp8:
             return fp8.decode(c, np.float32).astype(self.dtype) * self.dtype(scale)
         return c.astype(self.dtype)
+
+    def first_attended(self, pos: int) -> int:
+        """First frame index the frame at ``pos`` attends to: 0, or with a
+        rolling window the start of the last ``window`` frames."""
+        return max(0, pos + 1 - self.window) if self.rolling else 0
 
 
 # ----------------------------------------------------------------------------
@@ -156,8 +180,9 @@ def _stack_step(x, pos, slots, layers, n_layers, shape, eps, cos, sin, cache, kv
             cache.store(s, l, 1, p, v[i], kv_scale[l, 1])
             for h in range(hq):
                 g = (h * hkv) // hq
-                kh = cache.read(s, l, 0, g, p + 1, kv_scale[l, 0, g])
-                vh = cache.read(s, l, 1, g, p + 1, kv_scale[l, 1, g])
+                lo = cache.first_attended(p)
+                kh = cache.read(s, l, 0, g, lo, p + 1, kv_scale[l, 0, g])
+                vh = cache.read(s, l, 1, g, lo, p + 1, kv_scale[l, 1, g])
                 sc = (kh @ q[i, h]) * inv_sqrt_d
                 sc = sc - np.max(sc)
                 e = np.exp(sc)
@@ -183,8 +208,9 @@ class Oracle:
         self.cfg = cfg
         self.model = model
         self.dtype = dtype
+        self.rolling = bool(cfg.get("kv_ring", 0))
         self.cache = Cache(cfg["n_layers"], cfg["n_kv_heads"], cfg["max_context"],
-                           cfg["head_dim"], cfg["kv_dtype"] == "fp8", dtype)
+                           cfg["head_dim"], cfg["kv_dtype"] == "fp8", dtype, rolling=self.rolling)
         self.cos, self.sin = rope_table(cfg["max_context"], cfg["head_dim"], cfg["rope_base"], dtype)
         if cfg["kv_dtype"] == "fp8":
             self.kv_scale = np.asarray(model.kv_scale, dtype=np.float32)
@@ -204,8 +230,11 @@ class Oracle:
         cfg = self.cfg
         slots = np.asarray(slots, dtype=np.int64)
         pos = np.asarray(pos, dtype=np.int64)
-        if np.any(pos >= cfg["max_context"]) or np.any(pos < 0):
+        if np.any(pos < 0) or (not self.rolling and np.any(pos >= cfg["max_context"])):
             raise ValueError("position outside the context window")
+        if pos.size and int(pos.max()) >= self.cos.shape[0]:  # rolling window: rotary angles further out
+            self.cos, self.sin = rope_table(2 * int(pos.max()) + 2, cfg["head_dim"], cfg["rope_base"],
+                                            self.dtype)
         y = _stack_step(np.asarray(x), pos, slots, self.model.layer, cfg["n_layers"],
                         (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]), cfg["rms_eps"],
                         self.cos, self.sin, self.cache, self.kv_scale, self.model.g_final,
@@ -237,7 +266,7 @@ class Oracle:
             out[:, k] = z
         return out
 
-    def prefill(self, slot: int, layer: int, values: np.ndarray):
-        """Fill positions 0..n-1 of ``slot`` at ``layer`` from raw key/value
+    def prefill(self, slot: int, layer: int, values: np.ndarray, t0: int = 0):
+        """Fill frames t0..t0+n-1 of ``slot`` at ``layer`` from raw key/value
         vectors [2][H_kv][n][D] (quantised like new frames)."""
-        self.cache.prefill(slot, layer, values, self.kv_scale[layer])
+        self.cache.prefill(slot, layer, values, self.kv_scale[layer], t0)

@@ -9,7 +9,8 @@ frames so far: each frame is computed once and never revisited (the
 bandwidth blog, section 4 on cache-aware streaming recognition, and the
 interview answer on it in section 6).  This module is that recompute,
 written as matrix products over the whole sequence [T][d] with a causal
-mask, so it shares no attention or cache-indexing code with the step.  The
+mask, so it shares no attention or cache-indexing code with the step (with
+a rolling window the mask also drops frames max_context or more back).  The
 cache's storage rounding (FP8 codes of x / sigma read back as sigma * decode)
 is applied to the full key/value matrices, since the cache is what the
 attention reads.
@@ -33,12 +34,17 @@ def _rope_rows(x, cos, sin):
     return out
 
 
-def _stack_full(X, layers, n_layers, shape, eps, base, g_final, kv_scale, fp8_cache, dtype):
+def _stack_full(X, layers, n_layers, shape, eps, base, g_final, kv_scale, fp8_cache, dtype,
+                window=None):
     hq, hkv, hd = shape
     T = X.shape[0]
     cos, sin = rope_table(T, hd, base, dtype)
     X = X.astype(dtype)
-    mask = np.triu(np.ones((T, T), dtype=bool), k=1)  # True above the diagonal = future
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    mask = j > i  # True = not attended: the future
+    if window is not None:  # and, with a rolling window, frames window or more back
+        mask = mask | (j <= i - window)
     for l in range(n_layers):
         w = {k: v.astype(dtype) for k, v in layers(l).items()}
         A = rmsnorm(X, w["g_attn"], eps, dtype)
@@ -67,12 +73,14 @@ def _stack_full(X, layers, n_layers, shape, eps, base, g_final, kv_scale, fp8_ca
 
 def forward_full(cfg: dict, model, X: np.ndarray, dtype=np.float32) -> np.ndarray:
     """Outputs [T][d] of the main stack for one session's frames X [T][d]
-    starting at position 0."""
+    starting at position 0 (with ``cfg["kv_ring"]``, each frame attends to
+    the last ``max_context`` frames only)."""
     fp8_cache = cfg["kv_dtype"] == "fp8"
     scale = np.asarray(model.kv_scale, dtype=np.float32) if fp8_cache else None
+    window = cfg["max_context"] if cfg.get("kv_ring", 0) else None
     return _stack_full(X, model.layer, cfg["n_layers"],
                        (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]), cfg["rms_eps"],
-                       cfg["rope_base"], model.g_final, scale, fp8_cache, dtype)
+                       cfg["rope_base"], model.g_final, scale, fp8_cache, dtype, window)
 
 
 def depth_full(cfg: dict, model, Xd: np.ndarray, dtype=np.float32) -> np.ndarray:

@@ -38,8 +38,10 @@ def rel_err(a, b):
 # library-built reference
 
 
-def torch_reference(cfg, model, X, *, depth=False, fp8_cache=None):
-    """Full causal forward in float64 built from torch library routines."""
+def torch_reference(cfg, model, X, *, depth=False, fp8_cache=None, window=None):
+    """Full causal forward in float64 built from torch library routines
+    (window: each frame attends to the last `window` frames only, given to
+    scaled_dot_product_attention as an explicit boolean mask)."""
     if depth:
         L, hq, hkv, hd = (cfg["depth_layers"], cfg["depth_heads"], cfg["depth_kv_heads"],
                           cfg["depth_head_dim"])
@@ -76,9 +78,17 @@ def torch_reference(cfg, model, X, *, depth=False, fp8_cache=None):
             assert float(kq.abs().max()) < 448 and float(vq.abs().max()) < 448
             k = kq.to(torch.float8_e4m3fn).to(torch.float64) * sk.double()
             v = vq.to(torch.float8_e4m3fn).to(torch.float64) * sv.double()
-        o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
-                                           v.transpose(0, 1)[None], is_causal=True,
-                                           enable_gqa=(hq != hkv))
+        if window is None:
+            o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
+                                               v.transpose(0, 1)[None], is_causal=True,
+                                               enable_gqa=(hq != hkv))
+        else:
+            ii = torch.arange(T)[:, None]
+            jj = torch.arange(T)[None, :]
+            keep = (jj <= ii) & (jj > ii - window)
+            o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
+                                               v.transpose(0, 1)[None], attn_mask=keep,
+                                               enable_gqa=(hq != hkv))
         o = o[0].transpose(0, 1).reshape(T, hq * hd)
         x = x + o @ w["wo"].T
         b = F.rms_norm(x, (d,), weight=w["g_ffn"], eps=eps)
@@ -324,3 +334,64 @@ def test_rope_pins():
     zc = (q[0, 0, 0::2] + 1j * q[0, 0, 1::2]) * np.exp(1j * p * base ** (-np.arange(D // 2) * 2.0 / D))
     r = rope(q, np.array([p]), cos, sin)[0, 0]
     assert np.allclose(r[0::2], zc.real, atol=1e-12) and np.allclose(r[1::2], zc.imag, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# rolling window (sessions longer than the window)
+
+
+@pytest.mark.parametrize("kv", ["f32", "fp8"])
+def test_sliding_full_matches_library_reference(kv):
+    """The full recompute with a 5-frame window equals torch's attention
+    with an explicit sliding-window mask, over 14 frames."""
+    cfg = small_cfg(kv_dtype=kv, kv_ring=1, max_context=5)
+    model = synth.Model(cfg, gain_noise=True)
+    X = frames(cfg, 2, 14)
+    ref = torch_reference(cfg, model, X, window=5)
+    got = forward_full(cfg, model, X, dtype=np.float64)
+    assert rel_err(got, ref) < 1e-12
+    # and the window matters: without it the late frames differ
+    plain = torch_reference(cfg, model, X)
+    assert rel_err(got[-1], plain[-1]) > 1e-3
+
+
+@pytest.mark.parametrize("kv", ["f32", "fp8"])
+def test_rolling_window_incremental_equals_sliding_recompute(kv):
+    """A 6-frame rolling window stepped one frame at a time over 20 frames
+    (the window wraps three times) equals the sliding-window recompute at
+    every frame; rotary positions are the absolute frame indices."""
+    cfg = small_cfg(kv_dtype=kv, kv_ring=1, max_context=6)
+    model = synth.Model(cfg, gain_noise=True)
+    outs, _ = _run_incremental(cfg, model, [0, 1], 20, np.float64)
+    for s in (0, 1):
+        full = forward_full(cfg, model, frames(cfg, s, 20), dtype=np.float64)
+        assert rel_err(outs[s], full) < 1e-10
+
+
+def test_rolling_window_before_it_fills_equals_fixed_window(tiny):
+    """Until a session reaches the window length, the rolling and the fixed
+    window are the same computation (bit-identical outputs)."""
+    cfg, model = tiny
+    ring = dict(cfg, kv_ring=1)
+    a, _ = _run_incremental(cfg, model, [0, 1], cfg["max_context"] if cfg["max_context"] < 12 else 12,
+                            np.float32)
+    b, _ = _run_incremental(ring, model, [0, 1], cfg["max_context"] if cfg["max_context"] < 12 else 12,
+                            np.float32)
+    for s in (0, 1):
+        assert np.array_equal(a[s], b[s])
+
+
+def test_rolling_window_prefill_at_absolute_frames():
+    """A session prefilled with the window's earlier frames at their absolute
+    indices and stepped at frame p gives the same output as one that
+    stepped through every frame (the cache only holds what the window
+    reads)."""
+    cfg = small_cfg(kv_ring=1, max_context=6, n_layers=1)
+    model = synth.Model(cfg, gain_noise=True)
+    outs, stepped = _run_incremental(cfg, model, [0], 15, np.float64)
+    # rebuild frames 9..13 of session 0's cache from the stepped oracle, then step frame 14
+    orc = Oracle(cfg, model, dtype=np.float64)
+    hist = stepped.cache.slot(0)[:, :, :, 9:14, :]
+    orc.cache.slot(3, 14)[:, :, :, 9:14, :] = hist
+    y = orc.step([3], synth.frame_input(cfg, 0, 14)[None], [14])
+    assert rel_err(y[0], outs[0][14]) < 1e-12
