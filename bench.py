@@ -119,7 +119,7 @@ def run_gpu(cfg, pos, steps, warmup):
     slots = ctx.fd_alloc_slots(S)
     log(f"ctx ready in {time.time() - t0:.1f}s; prefilling {S} slots x {pos} positions")
     if pos:
-        prefill_all(ctx, cfg, slots, pos, seed=2)
+        prefill_all(ctx, cfg, slots, min(pos, cfg["max_context"]), seed=2)
     act = torch.bfloat16 if cfg["act_dtype"] == "bf16" else torch.float32
     x = torch.from_numpy(np.stack([synth.frame_input(cfg, s, pos) for s in slots])).to("cuda", act)
     y = torch.empty_like(x)
@@ -367,6 +367,10 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--cpu-sessions", type=int, default=2)
     ap.add_argument("--no-max-s", action="store_true")
+    ap.add_argument("--kv-ring", type=int, default=0,
+                    help="1: rolling window (sessions past max_context frames attend to the last window)")
+    ap.add_argument("--position", type=int, default=None,
+                    help="new-frame index of every session (default: the workload's)")
     ap.add_argument("--exec-mode", type=int, default=0,
                     help="0: kernel sequence per step; 1: the whole step as one persistent walk")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -402,7 +406,10 @@ def main():
     torch.cuda.set_device(0)
     cfg = synth.get_config(args.config)
     cfg["exec_mode"] = args.exec_mode
-    pos = cfg.get("position", cfg["max_context"] - 1)
+    cfg["kv_ring"] = args.kv_ring
+    pos = cfg.get("position", cfg["max_context"] - 1) if args.position is None else args.position
+    if pos >= cfg["max_context"] and not args.kv_ring:
+        raise SystemExit("--position beyond the window needs --kv-ring 1")
     S = cfg["max_slots"]
 
     if args.calibrate_copy:
@@ -461,7 +468,8 @@ def main():
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} (kv {cfg['n_kv_heads']})",
                    "d_ffn": cfg["d_ffn"], "sessions": S, "frame_index": pos,
                    "weights": cfg["w_dtype"], "cache": cfg["kv_dtype"],
-                   "exec_mode": "walk" if args.exec_mode else "kernels"},
+                   "exec_mode": "walk" if args.exec_mode else "kernels",
+                   "window": "rolling" if args.kv_ring else "fixed"},
         "p50_ms": p50,
         "p99_ms": p99,
         "step_bytes": r["step_bytes"],

@@ -38,7 +38,7 @@ class FdConfig(ctypes.Structure):
         ("w_dtype", c_i32), ("act_dtype", c_i32), ("kv_dtype", c_i32),
         ("depth_steps", c_i32), ("depth_layers", c_i32), ("depth_d", c_i32),
         ("depth_heads", c_i32), ("depth_kv_heads", c_i32), ("depth_head_dim", c_i32),
-        ("depth_ffn", c_i32), ("exec_mode", c_i32),
+        ("depth_ffn", c_i32), ("exec_mode", c_i32), ("kv_ring", c_i32),
     ]
 
 
@@ -92,6 +92,7 @@ def config_from_dict(cfg: dict) -> FdConfig:
     c.act_dtype = _DT[cfg["act_dtype"]]
     c.kv_dtype = _DT[cfg["kv_dtype"]]
     c.exec_mode = int(cfg.get("exec_mode", 0))
+    c.kv_ring = int(cfg.get("kv_ring", 0))
     return c
 
 

@@ -43,7 +43,7 @@ struct fd_ctx {
     fd::WalkShape walk_shape{};
     int walk_grid = 0;
     bool walk_launched = false;
-    explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context) {}
+    explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context, p.ring) {}
 };
 
 namespace {
@@ -139,7 +139,11 @@ hipError_t upload_tables(fd_ctx* c, const fd::StackPlan& sp, const std::vector<f
             kv[((size_t)l * 2 + 1) * d.hkv + g] = sv;
             vs[(size_t)l * d.hkv + g] = sv;
         }
+    std::vector<double> theta((size_t)d.hd / 2);
+    for (int i = 0; i < d.hd / 2; ++i) theta[i] = std::pow((double)c->plan.cfg.rope_base, -2.0 * i / d.hd);
     hipError_t e = hipMemcpyAsync(P(c, sp.rope), rope.data(), rope.size() * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(P(c, sp.rope_theta), theta.data(), theta.size() * 8, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(P(c, sp.qscale), qs.data(), qs.size() * 4, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(P(c, sp.kvsig), kv.data(), kv.size() * 4, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(P(c, sp.vscale), vs.data(), vs.size() * 4, hipMemcpyHostToDevice, st);
@@ -231,6 +235,8 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.inv_d = inv_d;
         at.eps = eps;
         at.rope = (const float*)P(c, sp.rope);
+        at.rope_theta = (const double*)P(c, sp.rope_theta);
+        at.ring = pos_override < 0 && pl.ring;
         at.qscale = (const float*)P(c, sp.qscale) + (size_t)l * d.hkv;
         at.kvsig = (const float*)P(c, sp.kvsig) + (size_t)l * 2 * d.hkv;
         at.vscale = (const float*)P(c, sp.vscale) + (size_t)l * d.hkv;
@@ -392,6 +398,8 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
             at.inv_d = 1.0f / (float)z.d;
             at.eps = pl.cfg.rms_eps;
             at.rope = (const float*)P(c, sp.rope);
+        at.rope_theta = (const double*)P(c, sp.rope_theta);
+        at.ring = pos_override < 0 && pl.ring;
             at.qscale = (const float*)P(c, sp.qscale) + (size_t)l * z.hkv;
             at.kvsig = (const float*)P(c, sp.kvsig) + (size_t)l * 2 * z.hkv;
             at.vscale = (const float*)P(c, sp.vscale) + (size_t)l * z.hkv;

@@ -65,6 +65,8 @@ struct AttnArgs {
     int pos_override;      // >= 0: every row is at this position (depth stack)
     int S, hq, hkv, tc, n_chunks;
     int T;                 // cache positions per slot
+    int ring;              // rolling window: frame p at cache position p % T, the last T frames attended
+    const double* rope_theta;  // [hd/2] base^(-2i/hd): rotary angles of frames p >= T (rolling window)
     int MT;                // 16-row tiles of session rows (packed output layout)
     float* part;           // [S][hkv][n_chunks][G][hd + 2]
     void* o_out;           // [Sp][hq*hd] activation type, fragment-packed

@@ -132,6 +132,7 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     sp.kvsig = off;   off = align_up(off + 4ull * Lm * 2 * dims.hkv);
     sp.vscale = off; off = align_up(off + 4ull * Lm * dims.hkv);
     sp.rope = off;   off = align_up(off + 4ull * dims.T * dims.hd);
+    sp.rope_theta = off; off = align_up(off + 8ull * dims.hd / 2);
     // attention chunking: lanes per position give each lane 16 bytes (FP8)
     // or 32 bytes (fp32) of a position's head vector
     // Chunks of the window per (slot, kv head): one workgroup per chunk.
@@ -170,6 +171,10 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         *err = "kv_dtype must be FD_F32 or FD_FP8_E4M3";
         return FD_E_UNSUPPORTED;
     }
+    if (c.kv_ring != 0 && c.kv_ring != 1) {
+        *err = "kv_ring must be 0 (fixed window) or 1 (rolling window)";
+        return FD_E_INVAL;
+    }
     if (c.exec_mode != FD_EXEC_KERNELS && c.exec_mode != FD_EXEC_WALK) {
         *err = "exec_mode must be FD_EXEC_KERNELS or FD_EXEC_WALK";
         return FD_E_INVAL;
@@ -193,6 +198,7 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     p.wt = c.w_dtype == FD_BF16 ? 1 : 0;
     p.act_bytes = p.wt ? 2 : 4;
     p.kv_fp8 = c.kv_dtype == FD_FP8_E4M3;
+    p.ring = c.kv_ring == 1;
     p.kv_bytes = p.kv_fp8 ? 1 : 4;
     const int KT = p.wt ? 32 : 16;
     fd_status st = check_stack("main", c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim,

@@ -66,12 +66,14 @@ struct StackPlan {
     uint64_t kvsig = 0;    // fp32 [L][2][H_kv]: FP8 scale sigma (1 for fp32 caches)
     uint64_t vscale = 0;   // fp32 [L][H_kv]: sigma_V
     uint64_t rope = 0;     // fp32 [T][D/2][2] (cos, sin)
+    uint64_t rope_theta = 0;  // float64 [D/2] base^(-2i/D): angles past the table (rolling window)
     // workspace (per stack) cache for the depth stack
     uint64_t kv_off = 0;
 };
 
 struct Plan {
     fd_config cfg{};
+    bool ring = false;  // rolling window (kv_ring = 1)
     int wt = 0;       // 1 = bf16 weights/activations, 0 = fp32
     int act_bytes = 4;
     int kv_fp8 = 0;

@@ -36,8 +36,8 @@ void fdh_gemm_shape(int N, int K, int wt, int MT, int32_t* out) {
     out[6] = g.n_groups; out[7] = g.grid(); out[8] = g.KT;
 }
 
-void* fdh_pool_new(int n_slots, int max_context) {
-    return new (std::nothrow) fd::SlotPool(n_slots, max_context);
+void* fdh_pool_new(int n_slots, int max_context, int rolling) {
+    return new (std::nothrow) fd::SlotPool(n_slots, max_context, rolling != 0);
 }
 void fdh_pool_delete(void* p) { delete (fd::SlotPool*)p; }
 fd_status fdh_pool_alloc(void* p, int32_t n, int32_t* out) { return ((fd::SlotPool*)p)->alloc(n, out); }

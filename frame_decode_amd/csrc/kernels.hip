@@ -691,8 +691,13 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
                 store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
         return;
     }
-    const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
-    const int n = p + 1;
+    // frame index p of the new entry; n cache positions attended; the new
+    // entry goes to cache position `hole` (p itself, or p mod T with a
+    // rolling window, where positions 0..T-1 then hold the last T frames)
+    const int pin = max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0);
+    const int p = a.ring ? pin : min(pin, a.T - 1);
+    const int n = a.ring ? min(p + 1, a.T) : p + 1;
+    const int hole = a.ring ? p % a.T : p;
     const int nch = (n + a.tc - 1) / a.tc;
     if (chunk >= nch) return;
     const int t0 = chunk * a.tc;
@@ -715,7 +720,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     __shared__ float s_kn[D], s_vn[D], s_sn[G];
     __shared__ float s_red[4];
     const bool own_new = chunk == nch - 1;
-    const int t1 = own_new ? n - 1 : min(t0 + a.tc, n);  // cached positions this chunk streams
+    const int t1 = min(t0 + a.tc, n);  // cache positions [t0, t1) this chunk streams, except `hole`
 
     // the wave's first block of keys does not depend on q: start it now
     u32x4 raw[NIT][J];
@@ -726,8 +731,9 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             const int t = tw + it * PPL;
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                raw[it][j] = t < t1 ? __builtin_nontemporal_load((const u32x4*)(src + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
-                                    : u32x4{0u, 0u, 0u, 0u};
+                raw[it][j] = t < t1 && t != hole
+                                 ? __builtin_nontemporal_load((const u32x4*)(src + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
+                                 : u32x4{0u, 0u, 0u, 0u};
         }
     };
     int base = t0 + wave * SUB;
@@ -752,7 +758,14 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             const int hh = idx / QPH, d0 = (idx - hh * QPH) * 4;
             const int col = hh < G ? (g * G + hh) * D + d0 : (a.hq + (hh - G) * a.hkv + g) * D + d0;
             const float* src = a.qkv + (size_t)s * a.nqkv + col;
-            if (hh <= G) cs[k] = *(const f32x4*)(a.rope + ((size_t)p * (D / 2) + d0 / 2) * 2);
+            if (hh <= G) {
+                if (p < a.T) {
+                    cs[k] = *(const f32x4*)(a.rope + ((size_t)p * (D / 2) + d0 / 2) * 2);
+                } else {  // rolling window past the table: the angles in double precision
+                    const double a0 = (double)p * a.rope_theta[d0 / 2], a1 = (double)p * a.rope_theta[d0 / 2 + 1];
+                    cs[k] = f32x4{(float)cos(a0), (float)sin(a0), (float)cos(a1), (float)sin(a1)};
+                }
+            }
             for (int q0 = 0; q0 < a.P; q0 += PMAX) {
                 f32x4 pv[PMAX];
 #pragma unroll
@@ -785,7 +798,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             for (int e = 0; e < 4; ++e) s_q[hh][d0 + e] = x[e];
         } else {
             const int kv = hh - G;
-            uint8_t* dst = (kv ? vbase : kbase) + (size_t)p * a.pos_stride;
+            uint8_t* dst = (kv ? vbase : kbase) + (size_t)hole * a.pos_stride;
             float* keep = kv ? s_vn : s_kn;
             if (FP8) {
                 const float sg = a.kvsig[kv * a.hkv + g];
@@ -839,7 +852,8 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
 #pragma unroll
                 for (int e = 0; e < E; ++e) dsum += qv[h][e] * kvf[e];
                 dsum = warp_sum_xor<LPP>(dsum);
-                sc[it][h] = (tw + it * PPL) < t1 ? dsum : -INFINITY;
+                const int t = tw + it * PPL;
+                sc[it][h] = t < t1 && t != hole ? dsum : -INFINITY;
             }
         }
         // values of this block: issue the loads before the softmax update
@@ -851,15 +865,18 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             for (int it = 1; it < NIT; ++it) m = fmaxf(m, sc[it][h]);
 #pragma unroll
             for (int o = LPP; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-            const float mnew = fmaxf(mrun[h], m);  // finite: position `base` is valid
-            const float sold = __builtin_amdgcn_exp2f(mrun[h] - mnew);
+            const float mnew = fmaxf(mrun[h], m);
+            // (-inf only while this wave has seen no attended position, e.g. a
+            // block holding just the new entry's cache position: nothing to rescale)
+            const float sold = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun[h] - mnew);
             mrun[h] = mnew;
             lrun[h] *= sold;
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[h][e] *= sold;
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
-                const float w = (tw + it * PPL) < t1 ? __builtin_amdgcn_exp2f(sc[it][h] - mnew) : 0.f;
+                const int t = tw + it * PPL;
+                const float w = t < t1 && t != hole ? __builtin_amdgcn_exp2f(sc[it][h] - mnew) : 0.f;
                 sc[it][h] = w;
                 lrun[h] += w;
             }
@@ -961,8 +978,9 @@ __device__ __forceinline__ void attn_combine_wg(const AttnArgs& a, int bid) {
     const int g = bid % a.hkv;
     const int s = bid / a.hkv;
     if (s >= a.S || !a.active[s]) return;  // inactive rows were zeroed by the attention kernel
-    const int p = min(max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0), a.T - 1);
-    const int nch = (p + 1 + a.tc - 1) / a.tc;
+    const int pin = max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0);
+    const int n = a.ring ? min(pin + 1, a.T) : min(pin, a.T - 1) + 1;  // cache positions attended
+    const int nch = (n + a.tc - 1) / a.tc;
     if (nch == 1) return;  // written directly
     __shared__ float s_w[256];
     __shared__ float s_red[4], s_lsum[4];

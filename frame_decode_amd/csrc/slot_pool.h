@@ -14,10 +14,16 @@
 
 namespace fd {
 
+// Largest frame index a rolling-window session may reach (2^30 frames of
+// 80 ms: about 2.7 years).
+constexpr int kRollingMaxFrame = 1 << 30;
+
 class SlotPool {
 public:
-    SlotPool(int n_slots, int max_context)
-        : active_(n_slots, 0), pos_(n_slots, 0), max_context_(max_context) {}
+    // rolling: sessions continue past max_context frames (the cache keeps the
+    // last max_context); otherwise a full window stops the step.
+    SlotPool(int n_slots, int max_context, bool rolling = false)
+        : active_(n_slots, 0), pos_(n_slots, 0), max_context_(max_context), rolling_(rolling) {}
 
     int size() const { return (int)active_.size(); }
     int max_context() const { return max_context_; }
@@ -55,7 +61,7 @@ public:
 
     fd_status set_position(int s, int p) {
         if (s < 0 || s >= size() || !active_[s]) return FD_E_BADSLOT;
-        if (p < 0 || p > max_context_) return FD_E_INVAL;
+        if (p < 0 || p > (rolling_ ? kRollingMaxFrame : max_context_)) return FD_E_INVAL;
         pos_[s] = p;
         dirty_ = true;
         return FD_OK;
@@ -68,10 +74,12 @@ public:
         return FD_OK;
     }
 
-    // True if some active slot's window is full (the step may not run).
+    // True if some active slot's window is full (the step may not run); a
+    // rolling window is full only at the largest frame index.
     bool any_full(int* which) const {
+        const int cap = rolling_ ? kRollingMaxFrame : max_context_;
         for (int s = 0; s < size(); ++s)
-            if (active_[s] && pos_[s] >= max_context_) {
+            if (active_[s] && pos_[s] >= cap) {
                 if (which) *which = s;
                 return true;
             }
@@ -107,6 +115,7 @@ private:
     std::vector<int32_t> active_;
     std::vector<int32_t> pos_;
     int max_context_;
+    bool rolling_;
     bool dirty_ = true;
 };
 

@@ -45,19 +45,26 @@ def kv_bytes_per_position(cfg: dict) -> int:
     return cfg["n_layers"] * 2 * cfg["n_kv_heads"] * cfg["head_dim"] * eb
 
 
+def attended(cfg: dict, p: int) -> int:
+    """Cached positions the frame at index p attends over: p + 1, capped at
+    the window with a rolling window (kv_ring)."""
+    n = int(p) + 1
+    return min(n, cfg["max_context"]) if cfg.get("kv_ring", 0) else n
+
+
 def step_bytes(cfg: dict, positions) -> int:
     """Algorithmic bytes of one step: weights once, plus for each active
-    session the p+1 cached positions it attends over (the new entry is
-    written and read once; counted once)."""
+    session the cached positions it attends over (the new entry is written
+    and read once; counted once)."""
     kvp = kv_bytes_per_position(cfg)
-    return weight_bytes(cfg) + sum((int(p) + 1) * kvp for p in positions)
+    return weight_bytes(cfg) + sum(attended(cfg, p) * kvp for p in positions)
 
 
 def attention_bytes_per_launch(cfg: dict, positions) -> int:
     """Bytes one attention launch (one layer) streams: K and V of every
     cached position of every active session."""
     eb = 1 if cfg["kv_dtype"] == "fp8" else 4
-    return sum((int(p) + 1) for p in positions) * 2 * cfg["n_kv_heads"] * cfg["head_dim"] * eb
+    return sum(attended(cfg, p) for p in positions) * 2 * cfg["n_kv_heads"] * cfg["head_dim"] * eb
 
 
 def step_flops(cfg: dict, n_sessions: int) -> float:

@@ -94,7 +94,22 @@ typedef struct {
     int32_t depth_head_dim;
     int32_t depth_ffn;
     int32_t exec_mode;    /* FD_EXEC_KERNELS (0) or FD_EXEC_WALK (1), see below */
+    int32_t kv_ring;      /* 0: fixed window; 1: rolling window, see below */
 } fd_config;
+
+/*
+ * Window of a session's cache.  kv_ring = 0: a session holds at most
+ * max_context frames; stepping a slot whose position reached max_context
+ * fails with FD_E_CTXFULL (the 1500-frame, 120 s window of the case study's
+ * profile.json serving profile).  kv_ring = 1: sessions continue past the
+ * window (the vLLM-Omni recipe's realtime configuration leaves session
+ * length unbounded, "Performance"): frame t's key/value live in cache
+ * position t mod max_context, the frame at index p attends to frames
+ * max(0, p - max_context + 1) .. p, and its rotary angle uses the absolute
+ * index p.  Positions then run up to 2^30 (fd_set_position accepts them);
+ * the cache layout and fd_kv_write still address cache positions
+ * 0 .. max_context - 1.
+ */
 
 /*
  * Execution of a step.  FD_EXEC_KERNELS: fd_step enqueues a fixed sequence

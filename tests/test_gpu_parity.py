@@ -282,3 +282,84 @@ def test_deterministic_and_isolated(exec_mode):
         outs.append(to_np(y))
     check(np.array_equal(outs[0], outs[1]), "np.array_equal(outs[0], outs[1])")
     check(np.array_equal(outs[0][1:5], outs[2][1:5]), "np.array_equal(outs[0][1:5], outs[2][1:5])")
+
+
+def _prefill_rolling(ctx, orc, cfg, s, session, p):
+    """Fill the window before frame p (frames max(0, p-T+1)..p-1) with
+    seeded values: the oracle at their absolute frame indices, the GPU at
+    cache positions (frame mod T) through its own encoder."""
+    T = cfg["max_context"]
+    n = min(p, T - 1)
+    f0 = p - n
+    for l in range(cfg["n_layers"]):
+        v = synth.prefill_values(cfg, session, l, n)
+        orc.prefill(s, l, v, t0=f0)
+        i = 0
+        while i < n:
+            c0 = (f0 + i) % T
+            run = min(n - i, T - c0)
+            ctx.fd_kv_write(s, l, c0, torch.from_numpy(np.ascontiguousarray(v[:, :, i:i + run])).cuda())
+            i += run
+    ctx.fd_set_position(s, p)
+
+
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+@pytest.mark.parametrize("family", ["fp32", "bf16_fp8"])
+def test_rolling_window_across_the_wrap(family, exec_mode):
+    """Rolling window (kv_ring = 1): sessions before, at and well past the
+    window length step across the wrap of their cache positions; outputs
+    match the oracle (which keeps frames by absolute index) every step, and
+    each new entry lands at cache position (frame mod T)."""
+    if family == "fp32":
+        cfg = synth.scaled_config("tiny", max_slots=6, max_context=64, kv_ring=1, exec_mode=exec_mode)
+        start, tol, tune = [0, 61, 63, 64, 130, 200], 1e-3, None
+    else:
+        cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                                  d_ffn=1024, max_slots=6, max_context=300, kv_ring=1,
+                                  exec_mode=exec_mode)
+        # three chunks of the window: the new entry's position falls in
+        # different chunks as the frame index advances
+        start, tol, tune = [0, 297, 299, 300, 455, 1000], 2e-2, "attn.chunks=3"
+    T = cfg["max_context"]
+    model = synth.Model(cfg, gain_noise=True)
+    say(f"rolling window: {family} {'walk' if exec_mode else 'kernels'} T={T} start={start}")
+    if tune:
+        os.environ["FD_TUNE"] = tune
+    try:
+        ctx = make_context(cfg, model)
+    finally:
+        if tune:
+            del os.environ["FD_TUNE"]
+    orc = Oracle(cfg, model)
+    slots = ctx.fd_alloc_slots(len(start))
+    sess = {s: 300 + s for s in slots}
+    pos = dict(zip(slots, start))
+    for s in slots:
+        if pos[s]:
+            _prefill_rolling(ctx, orc, cfg, s, sess[s], pos[s])
+    y = torch.empty((cfg["max_slots"], cfg["d_model"]), device="cuda",
+                    dtype=torch.bfloat16 if cfg["act_dtype"] == "bf16" else torch.float32)
+    for step in range(4):
+        x_np, x = rows_input(cfg, sess, {s: pos[s] for s in slots})
+        ctx.fd_step(x, y)
+        ctx.fd_sync()
+        ref = orc.step(slots, x_np[slots], [pos[s] for s in slots])
+        e = rel_err_rows(to_np(y)[slots], ref)
+        say(f"  step {step} positions {[pos[s] for s in slots]}: max rel err {e:.3e}")
+        assert e <= tol, f"step {step}: {e}"
+        # the new entries: cache position p mod T holds frame p (layer 1, keys and values)
+        arena = ctx.arena_view().cpu().numpy()
+        for s in slots:
+            p = pos[s]
+            got = arena[s, 1, :, :, p % T, :]
+            want = orc.cache.slot(s)[1, :, :, p, :]
+            if cfg["kv_dtype"] == "fp8":
+                same = float(np.mean(got == want))
+                check(same > 0.8, f"slot {s} frame {p}: only {same:.3f} of the codes agree")
+            else:
+                err = float(np.max(np.abs(got - want)) / np.max(np.abs(want)))
+                check(err < 1e-4, f"slot {s} frame {p}: new entry differs by {err:.3e}")
+        for s in slots:
+            pos[s] += 1
+            assert ctx.fd_slot_state(s) == (1, pos[s])
+    ctx.fd_destroy()

@@ -30,7 +30,7 @@ def host():
         pytest.fail("libfd_host.so not built (run __graft_entry__.build())")
     h = ctypes.CDLL(HOST)
     h.fdh_pool_new.restype = ctypes.c_void_p
-    h.fdh_pool_new.argtypes = [ctypes.c_int, ctypes.c_int]
+    h.fdh_pool_new.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     for n in ("fdh_pool_alloc", "fdh_pool_free"):
         getattr(h, n).argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
     h.fdh_pool_alloc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -163,9 +163,9 @@ def test_gemm_tiling_covers_the_projection(host):
 
 
 class Pool:
-    def __init__(self, h, n, T):
+    def __init__(self, h, n, T, rolling=0):
         self.h = h
-        self.p = h.fdh_pool_new(n, T)
+        self.p = h.fdh_pool_new(n, T, rolling)
         self.n = n
 
     def alloc(self, k):
@@ -223,6 +223,34 @@ def test_positions_advance_and_full_window(host):
     assert P.free([0]) == FD_OK
     st, ids = P.alloc(1)
     assert ids == [0] and P.state(0)[1:] == (1, 0)
+
+
+def test_rolling_window_positions(host):
+    """With a rolling window a session keeps stepping past the window
+    length; only the largest frame index (2^30) stops it."""
+    P = Pool(host, 2, 4, rolling=1)
+    P.alloc(1)
+    assert host.fdh_pool_set_position(P.p, 0, 3) == FD_OK
+    host.fdh_pool_advance(P.p)
+    host.fdh_pool_advance(P.p)
+    assert P.state(0)[1:] == (1, 5) and host.fdh_pool_any_full(P.p) == -1
+    assert host.fdh_pool_set_position(P.p, 0, 1000) == FD_OK
+    assert host.fdh_pool_set_position(P.p, 0, (1 << 30) + 1) == FD_E_INVAL
+    assert host.fdh_pool_set_position(P.p, 0, 1 << 30) == FD_OK
+    assert host.fdh_pool_any_full(P.p) == 0
+
+
+def test_rolling_window_plan(host):
+    """kv_ring 0 and 1 plan with the same buffer sizes; other values are
+    invalid arguments."""
+    cfg = synth.get_config("7b_s8_p256")
+    st0, s0 = _plan(host, cfg)
+    cfg["kv_ring"] = 1
+    st1, s1 = _plan(host, cfg)
+    assert st0 == FD_OK and st1 == FD_OK
+    assert (s0.packed_weights, s0.kv_arena, s0.workspace) == (s1.packed_weights, s1.kv_arena, s1.workspace)
+    cfg["kv_ring"] = 2
+    assert _plan(host, cfg)[0] == FD_E_INVAL
 
 
 def test_device_image_layout(host):

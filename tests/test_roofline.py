@@ -61,3 +61,17 @@ def test_workload_bytes():
     assert rf.step_bytes(c5, [1499] * 56) == 9_734_848_512
     # at 8 TB/s the 80-session, 1500-frame step takes 5.576 ms
     assert abs(rf.roofline_seconds(44_610_617_344) * 1e3 - 5.576) < 1e-3
+
+
+def test_rolling_window_bytes_cap_at_the_window():
+    """With a rolling window a session past the window streams exactly one
+    window of cache per layer, the same bytes as a session at the window's
+    last frame."""
+    import synth
+    from frame_decode_amd import roofline as rf
+    cfg = synth.get_config("7b_s80_p1499")
+    ring = dict(cfg, kv_ring=1)
+    assert rf.attended(ring, 5000) == 1500 and rf.attended(ring, 20) == 21
+    assert rf.attended(cfg, 20) == 21
+    assert rf.step_bytes(ring, [4999] * 80) == rf.step_bytes(cfg, [1499] * 80) == 44_610_617_344
+    assert rf.attention_bytes_per_launch(ring, [3000] * 80) == 983_040_000
