@@ -180,6 +180,92 @@ def max_sessions(cfg, pos, steps=3, warmup=1, budget_ms=80.0):
             "hbm_frac": r["step_bytes"] / (med * 1e-3) / 8e12}
 
 
+def beat_loop(cfg, beats, runs, n_active, seed=6):
+    """Serving-clock measurement: every 160 ms beat (on the host's real
+    clock) the sessions that reached their seeded end frame are retired and
+    replaced by new sessions at frame 0 (lowest free slot), then two 80 ms
+    steps are enqueued; a beat is late when its second step completes more
+    than 160 ms after the beat's scheduled start.  Returns per-run beat
+    latency percentiles and the late count over session-beats."""
+    import numpy as np
+    import torch
+    import synth
+    S, T = cfg["max_slots"], cfg["max_context"]
+    deadline = 0.160
+    ctx = build_ctx(cfg)
+    ctx.arena.zero_()
+    act = torch.bfloat16 if cfg["w_dtype"] == "bf16" else torch.float32
+    x = torch.randn((S, cfg["d_model"]), device="cuda").to(act)
+    y = torch.empty_like(x)
+    d = None
+    if cfg.get("depth_steps", 0):
+        d = torch.empty((S, cfg["depth_steps"], cfg["depth_d"]), device="cuda", dtype=act)
+    st = torch.cuda.current_stream()
+    out = {"p50_ms": [], "p99_ms": [], "max_ms": [], "gpu_p99_ms": [], "late_beats": 0,
+           "admissions": 0, "retirements": 0}
+    for run in range(runs):
+        rng = np.random.default_rng([seed, run])
+        # start: a seeded active subset at seeded positions, each with an end frame
+        live = sorted(int(v) for v in rng.choice(S, size=n_active, replace=False))
+        for s in list(range(S)):
+            if ctx.fd_slot_state(s)[0]:
+                ctx.fd_free([s])
+        assert ctx.fd_alloc_slots(S) == list(range(S))
+        ctx.fd_free([s for s in range(S) if s not in live])
+        end = {}
+        for s in live:
+            p = int(rng.integers(0, T - 1))
+            ctx.fd_set_position(s, p)
+            end[s] = int(rng.integers(p + 1, T + 1))
+        # warm-up (not counted): two steps, then the positions are restored
+        for _ in range(2):
+            ctx.fd_step(x, y, d)
+        ctx.fd_sync()
+        for s in live:
+            ctx.fd_set_position(s, ctx.fd_slot_state(s)[1] - 2)
+        lat, gpu = [], []
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(beats)]
+        t0 = time.perf_counter() + 0.05
+        for b in range(beats):
+            start = t0 + b * deadline
+            now = time.perf_counter()
+            if now < start:
+                time.sleep(start - now)
+            # churn: sessions whose window is used up end; new ones take the freed slots
+            done = [s for s in list(end) if ctx.fd_slot_state(s)[1] + 2 > end[s]]
+            if done:
+                ctx.fd_free(done)
+                for s in done:
+                    del end[s]
+                new = ctx.fd_alloc_slots(len(done))
+                for s in new:
+                    end[s] = int(rng.integers(2, T + 1))
+                out["retirements"] += len(done)
+                out["admissions"] += len(new)
+            ev[b][0].record(st)
+            ctx.fd_step(x, y, d)
+            ctx.fd_step(x, y, d)
+            ev[b][1].record(st)
+            ev[b][1].synchronize()
+            lat.append((time.perf_counter() - start) * 1e3)
+        ctx.fd_sync()
+        gpu = [a.elapsed_time(b_) for a, b_ in ev]
+        late = sum(1 for v in lat if v > deadline * 1e3)
+        out["late_beats"] += late * n_active
+        lat.sort()
+        gpu.sort()
+        pct = lambda v, q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+        out["p50_ms"].append(pct(lat, 0.5))
+        out["p99_ms"].append(pct(lat, 0.99))
+        out["max_ms"].append(lat[-1])
+        out["gpu_p99_ms"].append(pct(gpu, 0.99))
+        log(f"beats run {run}: p50 {pct(lat, 0.5):.2f} ms, p99 {pct(lat, 0.99):.2f} ms, "
+            f"max {lat[-1]:.2f} ms, late {late}/{beats}; GPU p99 {pct(gpu, 0.99):.2f} ms")
+    ctx.fd_destroy()
+    out["session_beats"] = n_active * beats * runs
+    return out
+
+
 def read_probe_gbs(nbytes=16 << 30, reps=5):
     """Achievable HBM read bandwidth: one streaming read of a 16 GiB buffer
     by the library's read-probe kernel (the bandwidth blog measures the
@@ -367,6 +453,10 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--cpu-sessions", type=int, default=2)
     ap.add_argument("--no-max-s", action="store_true")
+    ap.add_argument("--beats", type=int, default=0,
+                    help="serving-clock mode: beats per run (two steps per 160 ms beat)")
+    ap.add_argument("--runs", type=int, default=3)
+    ap.add_argument("--active", type=int, default=None, help="active sessions in --beats mode")
     ap.add_argument("--kv-ring", type=int, default=0,
                     help="1: rolling window (sessions past max_context frames attend to the last window)")
     ap.add_argument("--position", type=int, default=None,
@@ -412,6 +502,14 @@ def main():
         raise SystemExit("--position beyond the window needs --kv-ring 1")
     S = cfg["max_slots"]
 
+    if args.beats:
+        n_active = args.active or cfg.get("n_active", S)
+        r = beat_loop(cfg, args.beats, args.runs, n_active)
+        print(json.dumps({
+            "metric": "beat latency (two 80 ms steps per 160 ms beat, host clock) and late session-beats",
+            "workload": args.config, "sessions": n_active, "slots": S, "beats_per_run": args.beats,
+            "runs": args.runs, "deadline_ms": 160, "data": "synthetic", **r}), flush=True)
+        return
     if args.calibrate_copy:
         calibration_copy()
     probe = read_probe_gbs()
