@@ -266,6 +266,16 @@ class Oracle:
             out[:, k] = z
         return out
 
+    def head(self, y):
+        """Output head after the step: logits = y . W_head^T over the
+        vocabulary and the greedy token (the vLLM-Omni recipe: one text token
+        per acoustic frame, "Summary"; sampling greedy end to end, "Key
+        flags").  Ties go to the lowest token index.  Returns (logits [n][V],
+        tokens [n])."""
+        dt = self.dtype
+        logits = np.asarray(y).astype(dt) @ self.model.w_head.astype(dt).T
+        return logits, np.argmax(logits, axis=1)
+
     def prefill(self, slot: int, layer: int, values: np.ndarray, t0: int = 0):
         """Fill frames t0..t0+n-1 of ``slot`` at ``layer`` from raw key/value
         vectors [2][H_kv][n][D] (quantised like new frames)."""

@@ -37,7 +37,7 @@ SEED_SCALES = 4
 # Stable ids for the per-layer tensors, used as SeedSequence keys.
 _NAME_ID = {
     "wq": 1, "wk": 2, "wv": 3, "wo": 4, "w_gate": 5, "w_up": 6, "w_down": 7,
-    "g_attn": 8, "g_ffn": 9, "g_final": 10, "w_in": 11,
+    "g_attn": 8, "g_ffn": 9, "g_final": 10, "w_in": 11, "w_head": 12,
 }
 _DEPTH_OFFSET = 1000  # layer key offset for the depth stack's layers
 _FINAL_LAYER_KEY = 999_999
@@ -138,6 +138,7 @@ def weight_shape(cfg: dict, name: str, *, depth: bool = False) -> tuple[int, int
         "wq": (hq * hd, d), "wk": (hkv * hd, d), "wv": (hkv * hd, d),
         "wo": (d, hq * hd), "w_gate": (f, d), "w_up": (f, d), "w_down": (d, f),
         "w_in": (cfg.get("depth_d", 0), cfg["d_model"]),
+        "w_head": (cfg.get("vocab", 0), cfg["d_model"]),
     }[name]
 
 
@@ -168,8 +169,8 @@ class Model:
 
     ``layer(l)`` returns the float32 weights of layer ``l`` (generated on
     first use and cached unless ``cache=False``); ``depth_layer(l)`` the same
-    for the depth stack.  ``g_final``, ``depth_g_final``, ``w_in`` and
-    ``kv_scale`` are attributes.
+    for the depth stack.  ``g_final``, ``depth_g_final``, ``w_in``, ``w_head``
+    (output head, with a vocabulary) and ``kv_scale`` are attributes.
     """
 
     def __init__(self, cfg: dict, *, gain_noise: bool = False, cache: bool = True,
@@ -190,6 +191,7 @@ class Model:
         else:
             self.w_in = None
             self.depth_g_final = None
+        self.w_head = matrix(cfg, 0, "w_head", pool=self._pool) if cfg.get("vocab", 0) else None
 
     def _apply_zero(self, w: dict) -> dict:
         for n in self._zero:

@@ -16,6 +16,7 @@ _BASE = dict(
     depth_steps=0, depth_layers=0, depth_d=0, depth_heads=0, depth_kv_heads=0,
     depth_head_dim=0, depth_ffn=0,
     kv_ring=0,
+    vocab=0,
 )
 
 _7B = dict(n_layers=32, d_model=4096, n_heads=32, n_kv_heads=32, head_dim=128, d_ffn=11264,

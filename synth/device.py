@@ -39,6 +39,8 @@ def device_weights(model, device="cuda") -> dict:
         out["depth_layers"] = [_layer(model.depth_layer(l), wdt, device)
                                for l in range(cfg["depth_layers"])]
         out["depth_g_final"] = _f32(model.depth_g_final, device)
+    if cfg.get("vocab", 0):
+        out["w_head"] = _mat(model.w_head, wdt, device)
     return out
 
 
@@ -73,4 +75,6 @@ def random_device_weights(cfg: dict, seed: int = 0, device="cuda") -> dict:
         out["w_in"] = mat("w_in")
         out["depth_layers"] = [layer(True) for _ in range(cfg["depth_layers"])]
         out["depth_g_final"] = torch.ones(cfg["depth_d"], device=device)
+    if cfg.get("vocab", 0):
+        out["w_head"] = mat("w_head")
     return out

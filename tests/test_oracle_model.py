@@ -395,3 +395,34 @@ def test_rolling_window_prefill_at_absolute_frames():
     orc.cache.slot(3, 14)[:, :, :, 9:14, :] = hist
     y = orc.step([3], synth.frame_input(cfg, 0, 14)[None], [14])
     assert rel_err(y[0], outs[0][14]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# output head (greedy token per frame)
+
+
+def test_head_closed_forms_and_ties():
+    """Head rows that are unit vectors pick out coordinates of y; equal
+    logits resolve to the lowest token index (the token equals a plain scan
+    for the largest (logit, -index)); a positive rescaling of the hidden
+    state leaves the tokens unchanged."""
+    cfg = small_cfg(vocab=32)
+    model = synth.Model(cfg)
+    orc = Oracle(cfg, model, dtype=np.float64)
+    d = cfg["d_model"]
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((3, d))
+    y[1, 7] = 50.0  # row 1: tokens 0 and 2 (both coordinate 7) tie for the maximum
+    cols = [7, 3, 7] + list(range(10, 39))
+    model.w_head = np.zeros((32, d))
+    for v, c in enumerate(cols):
+        model.w_head[v, c] = 1.0
+    logits, tok = orc.head(y)
+    assert np.array_equal(logits[:, 0], y[:, 7]) and np.array_equal(logits[:, 1], y[:, 3])
+    assert tok[1] == 0
+    for i in range(3):
+        assert tok[i] == max(range(32), key=lambda v: (logits[i, v], -v))
+    model.w_head = rng.standard_normal((32, d))
+    _, t1 = orc.head(y)
+    _, t2 = orc.head(3.5 * y)
+    assert np.array_equal(t1, t2)
