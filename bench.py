@@ -71,11 +71,18 @@ def prefill_all(ctx, cfg, slots, n_pos, seed):
     torch.cuda.synchronize()
 
 
-def time_steps(ctx, cfg, slots, pos, x, y, d, steps, warmup):
-    """Warm up, then time `steps` consecutive fd_step calls with HIP events
-    on the launch stream; returns (total ms, per-step ms list)."""
+def time_steps(ctx, cfg, slots, pos, x, y, d, steps, warmup, tokens=None):
+    """Warm up, then time `steps` consecutive fd_step calls (fd_step_tokens
+    when a tokens buffer is given) with HIP events on the launch stream;
+    returns (total ms, per-step ms list)."""
     import torch
     st = torch.cuda.current_stream()
+
+    def step():
+        if tokens is None:
+            ctx.fd_step(x, y, d)
+        else:
+            ctx.fd_step_tokens(x, y, tokens, None, d)
 
     def rewind():
         for s in slots:
@@ -83,13 +90,13 @@ def time_steps(ctx, cfg, slots, pos, x, y, d, steps, warmup):
 
     for _ in range(warmup):
         rewind()
-        ctx.fd_step(x, y, d)
+        step()
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record(st)
     for i in range(steps):
         rewind()
-        ctx.fd_step(x, y, d)
+        step()
         evs[i + 1].record(st)
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
@@ -126,20 +133,21 @@ def run_gpu(cfg, pos, steps, warmup):
     d = None
     if cfg.get("depth_steps", 0):
         d = torch.empty((S, cfg["depth_steps"], cfg["depth_d"]), device="cuda", dtype=act)
+    tokens = torch.empty((S,), device="cuda", dtype=torch.int32) if cfg.get("vocab", 0) else None
     log("timing")
-    total_ms, per = time_steps(ctx, cfg, slots, pos, x, y, d, steps, warmup)
+    total_ms, per = time_steps(ctx, cfg, slots, pos, x, y, d, steps, warmup, tokens)
     ctx.fd_sync()
     # per-kernel durations: a second pass of the same steps with event pairs
     # around every launch on the launch stream
     ctx.fd_profile(True)
     ctx.fd_profile_read()
-    time_steps(ctx, cfg, slots, pos, x, y, d, steps, 0)
+    time_steps(ctx, cfg, slots, pos, x, y, d, steps, 0, tokens)
     kern = ctx.fd_profile_read()
     ctx.fd_profile(False)
     positions = [pos] * S
     res = {
         "total_ms": total_ms, "per_step_ms": per, "kernels": kern,
-        "step_bytes": rf.step_bytes(cfg, positions),
+        "step_bytes": rf.step_bytes(cfg, positions, head=tokens is not None),
         "attn_bytes": rf.attention_bytes_per_launch(cfg, positions),
     }
     ctx.fd_destroy()
@@ -457,6 +465,8 @@ def main():
                     help="serving-clock mode: beats per run (two steps per 160 ms beat)")
     ap.add_argument("--runs", type=int, default=3)
     ap.add_argument("--active", type=int, default=None, help="active sessions in --beats mode")
+    ap.add_argument("--vocab", type=int, default=0,
+                    help="output head over this many tokens (synthetic); steps run fd_step_tokens")
     ap.add_argument("--kv-ring", type=int, default=0,
                     help="1: rolling window (sessions past max_context frames attend to the last window)")
     ap.add_argument("--position", type=int, default=None,
@@ -497,6 +507,7 @@ def main():
     cfg = synth.get_config(args.config)
     cfg["exec_mode"] = args.exec_mode
     cfg["kv_ring"] = args.kv_ring
+    cfg["vocab"] = args.vocab
     pos = cfg.get("position", cfg["max_context"] - 1) if args.position is None else args.position
     if pos >= cfg["max_context"] and not args.kv_ring:
         raise SystemExit("--position beyond the window needs --kv-ring 1")
@@ -567,7 +578,8 @@ def main():
                    "d_ffn": cfg["d_ffn"], "sessions": S, "frame_index": pos,
                    "weights": cfg["w_dtype"], "cache": cfg["kv_dtype"],
                    "exec_mode": "walk" if args.exec_mode else "kernels",
-                   "window": "rolling" if args.kv_ring else "fixed"},
+                   "window": "rolling" if args.kv_ring else "fixed",
+                   "vocab": args.vocab},
         "p50_ms": p50,
         "p99_ms": p99,
         "step_bytes": r["step_bytes"],

@@ -38,7 +38,7 @@ class FdConfig(ctypes.Structure):
         ("w_dtype", c_i32), ("act_dtype", c_i32), ("kv_dtype", c_i32),
         ("depth_steps", c_i32), ("depth_layers", c_i32), ("depth_d", c_i32),
         ("depth_heads", c_i32), ("depth_kv_heads", c_i32), ("depth_head_dim", c_i32),
-        ("depth_ffn", c_i32), ("exec_mode", c_i32), ("kv_ring", c_i32),
+        ("depth_ffn", c_i32), ("exec_mode", c_i32), ("kv_ring", c_i32), ("vocab", c_i32),
     ]
 
 
@@ -55,7 +55,7 @@ class FdLayerWeights(ctypes.Structure):
 class FdWeights(ctypes.Structure):
     _fields_ = [("layers", ctypes.POINTER(FdLayerWeights)), ("g_final", c_p), ("kv_scale", c_p),
                 ("w_in", c_p), ("depth_layers", ctypes.POINTER(FdLayerWeights)),
-                ("depth_g_final", c_p)]
+                ("depth_g_final", c_p), ("w_head", c_p)]
 
 
 class FdBuffers(ctypes.Structure):
@@ -71,13 +71,13 @@ class FdKvView(ctypes.Structure):
                 ("max_slots", c_i32), ("kv_scale", c_p), ("slot_active", c_p), ("slot_pos", c_p)]
 
 
-EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_free", "fd_destroy",
+EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_step_tokens", "fd_free", "fd_destroy",
            "fd_kv_layout", "fd_set_position", "fd_slot_state", "fd_kv_write", "fd_sync",
            "fd_profile", "fd_profile_read", "fd_read_probe", "fd_last_error", "fd_status_str"]
 
-FD_N_KINDS = 9
+FD_N_KINDS = 10
 KIND_NAMES = ["embed", "qkv", "attention", "o_proj", "gate_up", "down", "final", "depth_in",
-              "walk"]
+              "walk", "head"]
 
 
 def config_from_dict(cfg: dict) -> FdConfig:
@@ -93,6 +93,7 @@ def config_from_dict(cfg: dict) -> FdConfig:
     c.kv_dtype = _DT[cfg["kv_dtype"]]
     c.exec_mode = int(cfg.get("exec_mode", 0))
     c.kv_ring = int(cfg.get("kv_ring", 0))
+    c.vocab = int(cfg.get("vocab", 0))
     return c
 
 
@@ -102,6 +103,7 @@ def _proto(lib):
     lib.fd_init.argtypes = [P(FdConfig), P(FdWeights), P(FdBuffers), c_p, P(c_p)]
     lib.fd_alloc_slots.argtypes = [c_p, c_i32, P(c_i32)]
     lib.fd_step.argtypes = [c_p, c_p, c_p, c_p, c_p]
+    lib.fd_step_tokens.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p]
     lib.fd_free.argtypes = [c_p, P(c_i32), c_i32]
     lib.fd_destroy.argtypes = [c_p]
     lib.fd_kv_layout.argtypes = [c_p, P(FdKvView)]

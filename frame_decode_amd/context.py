@@ -57,8 +57,9 @@ class Context:
     """Owns the device buffers and the fd_ctx of one profile.
 
     weights: {"layers": [ {wq, wk, wv, wo, w_gate, w_up, w_down, g_attn,
-    g_ffn} ...], "g_final", "kv_scale" (FP8 caches), and with a depth stack
-    "w_in", "depth_layers", "depth_g_final"} as torch device tensors.
+    g_ffn} ...], "g_final", "kv_scale" (FP8 caches), with a depth stack
+    "w_in", "depth_layers", "depth_g_final", and with a vocabulary "w_head"}
+    as torch device tensors.
     """
 
     def __init__(self, cfg: dict, weights: dict, device="cuda", stream=None):
@@ -89,6 +90,8 @@ class Context:
             w.w_in = _ptr(weights["w_in"])
             w.depth_layers = layer_array(weights["depth_layers"])
             w.depth_g_final = _ptr(weights["depth_g_final"])
+        if cfg.get("vocab", 0):
+            w.w_head = _ptr(weights["w_head"])
         b = FdBuffers(_ptr(self.packed), _ptr(self.arena), _ptr(self.workspace),
                       _ptr(self.slot_table))
         self._ctx = ctypes.c_void_p()
@@ -110,6 +113,14 @@ class Context:
         _check(_lib().fd_step(self._ctx, ctypes.c_void_p(_ptr(x_in)), ctypes.c_void_p(_ptr(y_out)),
                               ctypes.c_void_p(_ptr(depth_out)),
                               ctypes.c_void_p(_stream_handle(stream))), self._ctx)
+
+    def fd_step_tokens(self, x_in, y_out, tokens_out, logits_out=None, depth_out=None, stream=None) -> None:
+        """fd_step plus the output head: tokens_out int32 [max_slots], optional
+        logits_out fp32 [max_slots][vocab] (device tensors)."""
+        _check(_lib().fd_step_tokens(self._ctx, ctypes.c_void_p(_ptr(x_in)), ctypes.c_void_p(_ptr(y_out)),
+                                     ctypes.c_void_p(_ptr(depth_out)), ctypes.c_void_p(_ptr(tokens_out)),
+                                     ctypes.c_void_p(_ptr(logits_out)),
+                                     ctypes.c_void_p(_stream_handle(stream))), self._ctx)
 
     def fd_set_position(self, slot: int, pos: int) -> None:
         _check(_lib().fd_set_position(self._ctx, slot, pos), self._ctx)

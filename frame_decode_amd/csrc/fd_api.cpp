@@ -42,6 +42,9 @@ struct fd_ctx {
     fd::WalkArgs walk{};
     fd::WalkShape walk_shape{};
     int walk_grid = 0;
+    // input rows of the output head (written by the step's final norm)
+    const void* head_x = nullptr;
+    const void* head_x_lo = nullptr;
     bool walk_launched = false;
     explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context, p.ring) {}
 };
@@ -176,7 +179,7 @@ hipError_t timed(fd_ctx* c, int kind, hipStream_t st, F&& launch) {
     return e;
 }
 
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_O, K_GU, K_DOWN, K_FINAL, K_WIN, K_WALK };
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_O, K_GU, K_DOWN, K_FINAL, K_WIN, K_WALK, K_HEAD };
 
 struct CacheRef {
     uint8_t* base;
@@ -489,7 +492,10 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     fd::FinalArgs mf = final_rows(fd::FinalArgs{}, mp, r);
     mf.ldy = mp.dims.d;
     mf.y_off = 0;
-    mf.yw = pl.depth ? take(4 * Sp * mp.dims.d) : nullptr;
+    mf.yw = pl.depth ? (void*)take(4 * Sp * mp.dims.d) : (pl.head ? (void*)Wk(c, pl.ws_yw) : nullptr);
+    mf.yw_lo = wt && pl.head ? (void*)Wk(c, pl.ws_yw_lo) : nullptr;
+    c->head_x = mf.yw;
+    c->head_x_lo = mf.yw_lo;
     mf.pos = slot_pos(c);
     mf.advance = 1;
     phases.push_back({fd::WALK_FINAL_MAIN, (int)fin.size(), pl.Sp, pl.depth ? 1 : 0});
@@ -651,6 +657,7 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
             if (check_layer(w->depth_layers[l]) != FD_OK)
                 return fail(nullptr, FD_E_INVAL, "null depth weight pointer");
     }
+    if (p.head && !w->w_head) return fail(nullptr, FD_E_INVAL, "vocab > 0 needs w_head");
 
     fd_ctx* c = new (std::nothrow) fd_ctx(p);
     if (!c) return fail(nullptr, FD_E_DEVICE, "out of host memory");
@@ -684,6 +691,11 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
         if (e == hipSuccess) e = pack_stack(c, p.dstack, w->depth_layers, w->depth_g_final, s);
         if (e == hipSuccess) e = upload_tables(c, p.dstack, std::vector<float>(), false, s);
     }
+    if (e == hipSuccess && p.head)
+        e = pack(p.hshape, p.wt, w->w_head, p.hshape.N, nullptr, 0, nullptr, 0, P(c, p.w_head), s);
+    // the output head reads the final-normed rows (and their bf16 low part)
+    c->head_x = Wk(c, p.ws_yw);
+    c->head_x_lo = p.wt && p.head ? Wk(c, p.ws_yw_lo) : nullptr;
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     std::string werr;
     if (e == hipSuccess && p.walk) e = build_walk(c, s, &werr);
@@ -784,7 +796,8 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
         f.y_out = y_out;
         f.ldy = md.d;
         f.y_off = 0;
-        f.yw = pl.depth ? Wk(c, pl.ws_yw) : nullptr;
+        f.yw = pl.depth || pl.head ? Wk(c, pl.ws_yw) : nullptr;
+        f.yw_lo = pl.wt && pl.head ? Wk(c, pl.ws_yw_lo) : nullptr;
         f.pos = slot_pos(c);
         f.advance = 1;
         e = timed(c, K_FINAL, st, [&] { return fd::launch_final(f, pl.wt, pl.Sp, st); });
@@ -845,6 +858,41 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
     }
     if (e != hipSuccess) return hip_fail(c, e, "fd_step launch");
     c->slots.advance();
+    return FD_OK;
+}
+
+fd_status fd_step_tokens(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, int32_t* tokens_out,
+                         float* logits_out, void* stream) {
+    if (!c) return FD_E_INVAL;
+    const fd::Plan& pl = c->plan;
+    if (!pl.head) return fail(c, FD_E_INVAL, "profile has no output head (vocab 0)");
+    if (!tokens_out) return fail(c, FD_E_INVAL, "null tokens_out");
+    fd_status st = fd_step(c, x_in, y_out, depth_out, stream);
+    if (st != FD_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const fd::GemmShape& h = pl.hshape;
+    fd::GemmArgs g{};
+    g.W = P(c, pl.w_head);
+    g.X = c->head_x;
+    g.X_lo = c->head_x_lo;
+    g.K = h.K; g.KB = h.KB; g.NB = h.NB; g.P = h.P; g.MG = h.MG;
+    g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
+    g.part = (float*)Wk(c, pl.ws_part);
+    g.epi = fd::EPI_F32;
+    g.y = logits_out ? logits_out : (float*)Wk(c, pl.ws_logits);
+    g.ld = pl.cfg.vocab;
+    fd::ArgmaxArgs am{};
+    am.logits = g.y;
+    am.ld = pl.cfg.vocab;
+    am.V = pl.cfg.vocab;
+    am.S = pl.S;
+    am.active = slot_active(c);
+    am.tokens = tokens_out;
+    hipError_t e = timed(c, K_HEAD, s, [&] {
+        hipError_t r = fd::launch_gemm(g, pl.wt, h.R, h.MTG, h.grid(), s);
+        return r == hipSuccess ? fd::launch_argmax(am, s) : r;
+    });
+    if (e != hipSuccess) return hip_fail(c, e, "fd_step_tokens launch");
     return FD_OK;
 }
 

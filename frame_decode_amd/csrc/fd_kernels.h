@@ -97,10 +97,20 @@ struct FinalArgs {
     int S, d, MT;
     void* y_out;           // caller rows, element (m, i) at y_out[m * ldy + y_off + i]; may be null
     int ldy, y_off;
-    void* yw;              // [Sp][d] activation-type copy, or null
+    void* yw;              // [Sp][d] activation-type copy (GEMM input layout), or null
+    void* yw_lo;           // optional (bf16): y - yw, rounded to bf16 (output head input)
     float* zf;             // [Sp][d] fp32 copy, or null
     int* pos;              // advanced by one for active rows when `advance`
     int advance;
+};
+
+// Greedy token per row: argmax over logits[m][0..V) (ties to the lowest
+// index), -1 for inactive rows.
+struct ArgmaxArgs {
+    const float* logits;   // [S..][ld]
+    int ld, V, S;
+    const int* active;
+    int32_t* tokens;       // [S]
 };
 
 struct PackArgs {
@@ -171,6 +181,7 @@ hipError_t launch_attn(const AttnArgs& a, int wt, int kv_fp8, int hd, int G, int
 hipError_t launch_embed(const EmbedArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st);
+hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t st);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 // Persistent walk: walk_grid() is the co-resident grid of the shape's
 // compiled kernel (0 if the shape has none); launch_walk() zeroes the

@@ -171,6 +171,10 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         *err = "kv_dtype must be FD_F32 or FD_FP8_E4M3";
         return FD_E_UNSUPPORTED;
     }
+    if (c.vocab < 0 || c.vocab > (1 << 20) || c.vocab % 16) {
+        *err = "vocab must be 0 (no output head) or a multiple of 16 up to 2^20";
+        return FD_E_UNSUPPORTED;
+    }
     if (c.kv_ring != 0 && c.kv_ring != 1) {
         *err = "kv_ring must be 0 (fixed window) or 1 (rolling window)";
         return FD_E_INVAL;
@@ -199,6 +203,7 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     p.act_bytes = p.wt ? 2 : 4;
     p.kv_fp8 = c.kv_dtype == FD_FP8_E4M3;
     p.ring = c.kv_ring == 1;
+    p.head = c.vocab > 0;
     p.kv_bytes = p.kv_fp8 ? 1 : 4;
     const int KT = p.wt ? 32 : 16;
     fd_status st = check_stack("main", c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim,
@@ -239,6 +244,11 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
         plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, off);
     }
+    if (p.head) {
+        p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256);
+        p.w_head = off;
+        off = align_up(off + (uint64_t)p.hshape.NB * p.hshape.KB * kTileBytes);
+    }
     p.packed_bytes = std::max<uint64_t>(off, kAlign);
 
     // workspace
@@ -272,6 +282,8 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     p.ws_h_lo = take(p.wt ? Sp * fmax * 2 : 0);
     p.ws_o_lo = take(p.wt ? Sp * hqd * 2 : 0);
     p.ws_yw = take(Sp * m.d * p.act_bytes);
+    p.ws_yw_lo = take(p.wt && p.head ? Sp * m.d * 2 : 0);
+    p.ws_logits = take(p.head ? Sp * (uint64_t)c.vocab * 4 : 0);
     p.ws_c = take(Sp * std::max(dd, 1) * 4);
     p.ws_z = take(Sp * std::max(dd, 1) * 4);
     int nss = 1;
@@ -294,6 +306,10 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         acc_stack(p.dstack);
         part = std::max(part, p.win.part_floats);
         cnt = std::max(cnt, p.win.counters);
+    }
+    if (p.head) {
+        part = std::max(part, p.hshape.part_floats);
+        cnt = std::max(cnt, p.hshape.counters);
     }
     p.nss_max = nss;
     p.ws_ss_a = take(4ull * nss * Sp);

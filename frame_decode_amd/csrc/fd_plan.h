@@ -74,6 +74,9 @@ struct StackPlan {
 struct Plan {
     fd_config cfg{};
     bool ring = false;  // rolling window (kv_ring = 1)
+    bool head = false;  // output head (vocab > 0)
+    GemmShape hshape;   // output head projection
+    uint64_t w_head = 0;  // packed offset of the head tiles
     int wt = 0;       // 1 = bf16 weights/activations, 0 = fp32
     int act_bytes = 4;
     int kv_fp8 = 0;
@@ -92,6 +95,7 @@ struct Plan {
     uint64_t ws_x = 0, ws_xg = 0, ws_qkv = 0, ws_o = 0, ws_h = 0, ws_c = 0, ws_z = 0, ws_yw = 0;
     uint64_t ws_ss_a = 0, ws_ss_f = 0, ws_part = 0, ws_cnt = 0, ws_apart = 0, ws_acnt = 0;
     uint64_t ws_dkv = 0, ws_err = 0, ws_xg_lo = 0, ws_h_lo = 0, ws_o_lo = 0;
+    uint64_t ws_yw_lo = 0, ws_logits = 0;  // head input low part (bf16), logits [Sp][vocab]
     // persistent walk (the whole step as one launch): whether it is used,
     // and its workspace regions
     bool walk = false;

@@ -380,7 +380,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
                 st1<CO>(hp, h0);
                 st1<CO>(hp + 1, h1);
             }
-        } else {
+        } else if (m < a.S) {  // EPI_F32: session rows only (the buffer may be the caller's)
             st4<CO>(a.y + (size_t)m * a.ld + n, x);
         }
     }
@@ -1068,7 +1068,10 @@ __device__ __forceinline__ void final_row(const FinalArgs& a, int m) {
         f32x4 y = *(const f32x4*)(a.x + (size_t)m * a.d + i) * r * *(const f32x4*)(a.g + i);
         if (!valid) y = f32x4{0.f, 0.f, 0.f, 0.f};
         if (a.y_out && m < a.S) store_act4<WT, CO>(a.y_out, (size_t)m * a.ldy + a.y_off + i, y);
-        if (a.yw) store_act4<WT, CO>(a.yw, xoff<WT>(m, i, a.MT), y);
+        if (a.yw) {
+            if (WT && a.yw_lo) store_split4<CO>(a.yw, a.yw_lo, xoff<WT>(m, i, a.MT), y);
+            else store_act4<WT, CO>(a.yw, xoff<WT>(m, i, a.MT), y);
+        }
         if (a.zf) st4<CO>(a.zf + (size_t)m * a.d + i, y);
     }
     if (a.advance && threadIdx.x == 0 && valid) a.pos[m] += 1;
@@ -1077,6 +1080,50 @@ __device__ __forceinline__ void final_row(const FinalArgs& a, int m) {
 template <int WT>
 __global__ __launch_bounds__(256) void final_kernel(FinalArgs a) {
     final_row<WT, 0>(a, blockIdx.x);
+}
+
+// Greedy token of one row: each thread scans its columns in ascending order
+// keeping the first maximum, then (value, index) pairs are combined across
+// the block, larger value first and the lower index on equal values.
+__global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
+    const int m = blockIdx.x;
+    if (m >= a.S) return;
+    if (!a.active[m]) {
+        if (threadIdx.x == 0) a.tokens[m] = -1;
+        return;
+    }
+    const float* row = a.logits + (size_t)m * a.ld;
+    float best = -INFINITY;
+    int idx = 0x7FFFFFFF;
+    for (int v0 = threadIdx.x * 4; v0 < a.V; v0 += blockDim.x * 4) {  // (V is a multiple of 16)
+        const f32x4 x = *(const f32x4*)(row + v0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (x[e] > best || (x[e] == best && v0 + e < idx)) {
+                best = x[e];
+                idx = v0 + e;
+            }
+    }
+    auto take = [&](float ob, int oi) {
+        if (ob > best || (ob == best && oi < idx)) {
+            best = ob;
+            idx = oi;
+        }
+    };
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) take(__shfl_xor(best, o), __shfl_xor(idx, o));
+    __shared__ float s_b[4];
+    __shared__ int s_i[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        s_b[wave] = best;
+        s_i[wave] = idx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) take(s_b[w], s_i[w]);
+        a.tokens[m] = idx == 0x7FFFFFFF ? 0 : idx;  // (all NaN: token 0)
+    }
 }
 
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
@@ -1337,6 +1384,12 @@ hipError_t launch_embed(const EmbedArgs& a, int wt, int rows, hipStream_t st) {
 hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st) {
     if (wt) hipLaunchKernelGGL(final_kernel<1>, dim3(rows), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(final_kernel<0>, dim3(rows), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t st) {
+    if (a.S <= 0) return hipSuccess;
+    hipLaunchKernelGGL(argmax_kernel, dim3(a.S), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -28,14 +28,17 @@ def weight_params(cfg: dict, depth: bool = False) -> int:
     return L * per_layer
 
 
-def weight_bytes(cfg: dict) -> int:
+def weight_bytes(cfg: dict, head: bool = False) -> int:
     """One read of every projection weight of the main stack (and, with a
-    depth stack, its weights once per depth step plus the input projection)."""
+    depth stack, its weights once per depth step plus the input projection;
+    with head=True the output head's vocab x d_model weights)."""
     wb = 2 if cfg["w_dtype"] == "bf16" else 4
     b = weight_params(cfg) * wb
     if cfg.get("depth_steps", 0):
         b += cfg["depth_steps"] * weight_params(cfg, depth=True) * wb
         b += cfg["depth_d"] * cfg["d_model"] * wb
+    if head:
+        b += cfg.get("vocab", 0) * cfg["d_model"] * wb
     return b
 
 
@@ -52,12 +55,12 @@ def attended(cfg: dict, p: int) -> int:
     return min(n, cfg["max_context"]) if cfg.get("kv_ring", 0) else n
 
 
-def step_bytes(cfg: dict, positions) -> int:
+def step_bytes(cfg: dict, positions, head: bool = False) -> int:
     """Algorithmic bytes of one step: weights once, plus for each active
     session the cached positions it attends over (the new entry is written
-    and read once; counted once)."""
+    and read once; counted once); head=True adds the output head's weights."""
     kvp = kv_bytes_per_position(cfg)
-    return weight_bytes(cfg) + sum(attended(cfg, p) * kvp for p in positions)
+    return weight_bytes(cfg, head) + sum(attended(cfg, p) * kvp for p in positions)
 
 
 def attention_bytes_per_launch(cfg: dict, positions) -> int:

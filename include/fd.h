@@ -95,6 +95,7 @@ typedef struct {
     int32_t depth_ffn;
     int32_t exec_mode;    /* FD_EXEC_KERNELS (0) or FD_EXEC_WALK (1), see below */
     int32_t kv_ring;      /* 0: fixed window; 1: rolling window, see below */
+    int32_t vocab;        /* 0: no output head; else V, a multiple of 16 (<= 2^20): see fd_step_tokens */
 } fd_config;
 
 /*
@@ -170,6 +171,7 @@ typedef struct {
  *     read back as scale * decode(code)); ignored for FD_F32 caches
  *   w_in [depth_d][d_model], depth_layers[depth_layers], depth_g_final
  *     [depth_d]: the depth stack (only when depth_steps > 0)
+ *   w_head [vocab][d_model] in w_dtype: the output head (only when vocab > 0)
  */
 typedef struct {
     const fd_layer_weights* layers;
@@ -178,6 +180,7 @@ typedef struct {
     const void* w_in;
     const fd_layer_weights* depth_layers;
     const float* depth_g_final;
+    const void* w_head;
 } fd_weights;
 
 /* The four device buffers, each at least the size fd_plan reports and
@@ -258,6 +261,22 @@ fd_status fd_alloc_slots(fd_ctx* ctx, int32_t n, int32_t* slots_out);
 fd_status fd_step(fd_ctx* ctx, const void* x_in, void* y_out, void* depth_out, void* stream);
 
 /*
+ * fd_step followed by the output head on the same stream: for every active
+ * slot, logits = y . W_head^T over the vocabulary (fp32 accumulation of the
+ * final-normed output, before its rounding to act_dtype) and the greedy
+ * token argmax(logits), ties to the lowest index -- one text token per frame,
+ * chosen greedily (vLLM-Omni recipe, "Summary" and "Key flags").
+ *   tokens_out device int32 [max_slots]: the token of each active slot, -1
+ *          for inactive slots.
+ *   logits_out device fp32 [max_slots][vocab] or NULL: the logits (rows of
+ *          inactive slots 0).  Rows max_slots and beyond are never written.
+ * FD_E_INVAL if the profile has no head (vocab 0) or tokens_out is NULL;
+ * otherwise as fd_step.
+ */
+fd_status fd_step_tokens(fd_ctx* ctx, const void* x_in, void* y_out, void* depth_out,
+                         int32_t* tokens_out, float* logits_out, void* stream);
+
+/*
  * Ends sessions: marks the n slots (host array) free.  FD_E_BADSLOT and no
  * change if any id is out of range, not allocated, or repeated.
  */
@@ -300,10 +319,11 @@ fd_status fd_kv_write(fd_ctx* ctx, int32_t slot, int32_t layer, int32_t t0, int3
  * milliseconds and the number of launches since the last read (then resets).
  * Kinds: 0 embed, 1 qkv, 2 attention, 3 o-projection, 4 gate/up, 5 down,
  * 6 final norm, 7 depth input projection, 8 the persistent walk of the
- * whole step (FD_EXEC_WALK; then the only kind launched) (FD_N_KINDS = 9).  Timing adds a
+ * whole step (FD_EXEC_WALK; then the only step kind launched), 9 the output
+ * head of fd_step_tokens (projection and argmax) (FD_N_KINDS = 10).  Timing adds a
  * small gap between launches; headline step times are taken with it off.
  */
-#define FD_N_KINDS 9
+#define FD_N_KINDS 10
 fd_status fd_profile(fd_ctx* ctx, int32_t enable);
 fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, int32_t n);
 

@@ -363,3 +363,69 @@ def test_rolling_window_across_the_wrap(family, exec_mode):
             pos[s] += 1
             assert ctx.fd_slot_state(s) == (1, pos[s])
     ctx.fd_destroy()
+
+
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+@pytest.mark.parametrize("family", ["fp32", "bf16_fp8"])
+def test_output_head_greedy_tokens(family, exec_mode):
+    """fd_step_tokens: logits of every active slot match the oracle's head
+    on the oracle's output; each token is the argmax of the GPU's own logits
+    (first maximum, bit-exact) and equals the oracle's token unless the two
+    are within the measured logit error of each other (a near tie); inactive
+    slots give token -1 and zero logits."""
+    if family == "fp32":
+        cfg = synth.scaled_config("tiny", max_slots=3, vocab=512, exec_mode=exec_mode)
+        start, tol = [0, 7], 1e-3
+    else:
+        cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                                  d_ffn=1024, max_slots=6, max_context=300, vocab=2048,
+                                  exec_mode=exec_mode)
+        start, tol = [0, 5, 100, 255, 256], 2e-2
+    model = synth.Model(cfg, gain_noise=True)
+    say(f"head: {family} {'walk' if exec_mode else 'kernels'} V={cfg['vocab']}")
+    ctx = make_context(cfg, model)
+    orc = Oracle(cfg, model)
+    slots = ctx.fd_alloc_slots(len(start))
+    sess = {s: 400 + s for s in slots}
+    pos = dict(zip(slots, start))
+    for s in slots:
+        if pos[s]:
+            for l in range(cfg["n_layers"]):
+                v = synth.prefill_values(cfg, sess[s], l, pos[s])
+                orc.prefill(s, l, v)
+                ctx.fd_kv_write(s, l, 0, torch.from_numpy(v).cuda())
+            ctx.fd_set_position(s, pos[s])
+    S, V = cfg["max_slots"], cfg["vocab"]
+    y = torch.empty((S, cfg["d_model"]), device="cuda",
+                    dtype=torch.bfloat16 if cfg["act_dtype"] == "bf16" else torch.float32)
+    tokens = torch.full((S,), 12345, device="cuda", dtype=torch.int32)
+    logits = torch.full((S, V), 7.0, device="cuda", dtype=torch.float32)
+    inactive = [s for s in range(S) if s not in slots]
+    for step in range(2):
+        x_np, x = rows_input(cfg, sess, {s: pos[s] for s in slots})
+        ctx.fd_step_tokens(x, y, tokens, logits if step == 0 else None)
+        ctx.fd_sync()
+        yref = orc.step(slots, x_np[slots], [pos[s] for s in slots])
+        lref, tref = orc.head(yref)
+        tg = tokens.cpu().numpy()
+        check(np.all(tg[inactive] == -1), "inactive slots must give token -1")
+        if step == 0:
+            lg = logits.cpu().numpy()
+            e = rel_err_rows(lg[slots], lref)
+            say(f"  step {step}: logits max rel err {e:.3e}")
+            assert e <= tol
+            check(np.all(lg[inactive] == 0), "inactive slots must give zero logits")
+            for i, s in enumerate(slots):
+                check(tg[s] == int(np.argmax(lg[s])), f"slot {s}: token is not the first maximum of its logits")
+                if tg[s] != tref[i]:
+                    gap = float(lref[i].max() - lref[i][tg[s]])
+                    err = float(np.max(np.abs(lg[s] - lref[i])))
+                    say(f"  slot {s}: token {tg[s]} vs {tref[i]} (gap {gap:.3e}, logit error {err:.3e})")
+                    check(gap <= 2 * err + 1e-6, f"slot {s}: token {tg[s]} is not a near-tie of {tref[i]}")
+        else:
+            agree = float(np.mean(tg[slots] == tref))
+            say(f"  step {step}: tokens agree on {agree:.2f} of the sessions")
+            check(agree >= 0.6, "tokens (without a logits buffer) disagree with the oracle")
+        for s in slots:
+            pos[s] += 1
+    ctx.fd_destroy()

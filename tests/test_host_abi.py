@@ -262,3 +262,17 @@ def test_device_image_layout(host):
     assert host.fdh_pool_dirty(P.p) == 0
     host.fdh_pool_set_position(P.p, 0, 2)
     assert host.fdh_pool_dirty(P.p) == 1
+
+
+def test_output_head_plan(host):
+    """A vocabulary adds exactly the head's tiles to the packed weights;
+    sizes that are not a multiple of 16 are refused."""
+    cfg = synth.get_config("7b_s8_p256")
+    st0, s0 = _plan(host, cfg)
+    cfg["vocab"] = 2048
+    st1, s1 = _plan(host, cfg)
+    assert st0 == FD_OK and st1 == FD_OK
+    assert s1.packed_weights - s0.packed_weights == 2048 * 4096 * 2
+    assert s1.kv_arena == s0.kv_arena and s1.workspace > s0.workspace
+    cfg["vocab"] = 2050
+    assert _plan(host, cfg)[0] == FD_E_UNSUPPORTED
