@@ -87,6 +87,21 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
+def quantize_rows(w: np.ndarray):
+    """FP8 E4M3 weights with one scale per output row (an nn.Linear row):
+    scale = max|row| / 448 in float32 (1 for a row of zeros), codes of
+    w / scale, read back as scale * decode(code).  Returns (dequantized
+    float32 weights, scales).  FP8 weights halve the bytes a decode step
+    streams per parameter; the bandwidth blog measured the bf16 -> fp8 switch
+    (section 2, and its section 6 question on quantization), where per-token
+    fixed costs and the conversion back from 8 bits ate part of the gain."""
+    w = np.asarray(w, dtype=np.float32)
+    mx = np.max(np.abs(w), axis=1)
+    sc = np.where(mx > 0, mx / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = fp8.encode(w / sc[:, None])
+    return (fp8.decode(codes, np.float32) * sc[:, None]).astype(np.float32), sc
+
+
 # ----------------------------------------------------------------------------
 # cache
 
@@ -217,6 +232,9 @@ class Oracle:
         else:
             self.kv_scale = np.ones((cfg["n_layers"], 2, cfg["n_kv_heads"]), dtype=np.float32)
         self.depth = cfg.get("depth_steps", 0) > 0
+        # FP8 weights: every projection (and the head) used as scale * decode(code)
+        self.w8 = cfg["w_dtype"] == "fp8"
+        self._qlayers: dict = {}
         if self.depth:
             if cfg["kv_dtype"] != "f32":
                 raise ValueError("the depth stack is defined with an fp32 cache only")
@@ -235,7 +253,7 @@ class Oracle:
         if pos.size and int(pos.max()) >= self.cos.shape[0]:  # rolling window: rotary angles further out
             self.cos, self.sin = rope_table(2 * int(pos.max()) + 2, cfg["head_dim"], cfg["rope_base"],
                                             self.dtype)
-        y = _stack_step(np.asarray(x), pos, slots, self.model.layer, cfg["n_layers"],
+        y = _stack_step(np.asarray(x), pos, slots, self.layer, cfg["n_layers"],
                         (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]), cfg["rms_eps"],
                         self.cos, self.sin, self.cache, self.kv_scale, self.model.g_final,
                         self.dtype)
@@ -266,6 +284,18 @@ class Oracle:
             out[:, k] = z
         return out
 
+    def layer(self, l: int) -> dict:
+        """Weights of main-stack layer l as the step uses them."""
+        w = self.model.layer(l)
+        if not self.w8:
+            return w
+        if l not in self._qlayers:
+            q = dict(w)
+            for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+                q[n] = quantize_rows(w[n])[0]
+            self._qlayers[l] = q
+        return self._qlayers[l]
+
     def head(self, y):
         """Output head after the step: logits = y . W_head^T over the
         vocabulary and the greedy token (the vLLM-Omni recipe: one text token
@@ -273,7 +303,8 @@ class Oracle:
         flags").  Ties go to the lowest token index.  Returns (logits [n][V],
         tokens [n])."""
         dt = self.dtype
-        logits = np.asarray(y).astype(dt) @ self.model.w_head.astype(dt).T
+        wh = quantize_rows(self.model.w_head)[0] if self.w8 else self.model.w_head
+        logits = np.asarray(y).astype(dt) @ wh.astype(dt).T
         return logits, np.argmax(logits, axis=1)
 
     def prefill(self, slot: int, layer: int, values: np.ndarray, t0: int = 0):

@@ -109,7 +109,7 @@ def matrix(cfg: dict, layer: int, name: str, *, depth: bool = False,
     shape = weight_shape(cfg, name, depth=depth)
     lk = layer + (_DEPTH_OFFSET if depth else 0)
     return _normal_chunked([SEED_WEIGHTS, lk, _NAME_ID[name]], shape, 0.02, pool,
-                           bf16=cfg["w_dtype"] == "bf16")
+                           bf16=cfg["w_dtype"] in ("bf16", "fp8"))  # (FP8: bf16 sources)
 
 
 def gain(cfg: dict, layer: int, name: str, *, depth: bool = False,
@@ -122,7 +122,7 @@ def gain(cfg: dict, layer: int, name: str, *, depth: bool = False,
         r = np.random.Generator(np.random.PCG64(
             np.random.SeedSequence([SEED_WEIGHTS, lk, _NAME_ID[name], 7])))
         g = (1.0 + 0.02 * r.standard_normal(d)).astype(np.float32)
-    if cfg["w_dtype"] == "bf16":
+    if cfg["w_dtype"] in ("bf16", "fp8"):
         g = round_to_bf16(g)
     return g
 

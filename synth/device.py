@@ -28,7 +28,7 @@ def _layer(w: dict, wdt, device) -> dict:
 def device_weights(model, device="cuda") -> dict:
     """All weights of ``model`` (a synth.Model) as device tensors."""
     cfg = model.cfg
-    wdt = torch.bfloat16 if cfg["w_dtype"] == "bf16" else torch.float32
+    wdt = torch.bfloat16 if cfg["w_dtype"] in ("bf16", "fp8") else torch.float32
     out = {
         "layers": [_layer(model.layer(l), wdt, device) for l in range(cfg["n_layers"])],
         "g_final": _f32(model.g_final, device),
@@ -50,7 +50,7 @@ def random_device_weights(cfg: dict, seed: int = 0, device="cuda") -> dict:
     drawn directly on the GPU from torch's seeded generator.  Used where the
     values need not equal the host generator's (timing runs)."""
     from . import kv_scales, weight_shape
-    wdt = torch.bfloat16 if cfg["w_dtype"] == "bf16" else torch.float32
+    wdt = torch.bfloat16 if cfg["w_dtype"] in ("bf16", "fp8") else torch.float32
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
 

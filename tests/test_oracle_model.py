@@ -20,6 +20,7 @@ import torch.nn.functional as F
 
 import synth
 from oracle import Oracle, forward_full, depth_full, rope, rope_table, fp8
+from oracle.decoder import quantize_rows
 
 
 def small_cfg(**over):
@@ -426,3 +427,56 @@ def test_head_closed_forms_and_ties():
     _, t1 = orc.head(y)
     _, t2 = orc.head(3.5 * y)
     assert np.array_equal(t1, t2)
+
+
+# ---------------------------------------------------------------------------
+# FP8 weights with per-output-row scales
+
+
+def test_fp8_weight_rows_pins():
+    """Per-row E4M3 quantisation: each row's largest magnitude maps to the
+    code of +-448 and comes back to within an fp32 ulp (the scale max/448 is
+    rounded once), every entry in the normal range is within half a step
+    (2^-4 relative) and in the subnormal range within 2^-10 * scale; a zero
+    row stays zero with scale 1; a row scaled by 2^k keeps its codes."""
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((40, 96)) * np.exp(rng.uniform(-6, 2, (40, 1)))).astype(np.float32)
+    w[3] = 0.0
+    w[7, 5] = -3.75  # a clear row maximum with negative sign
+    wq, sc = quantize_rows(w)
+    for i in range(40):
+        if i == 3:
+            assert sc[i] == 1.0 and not np.any(wq[i])
+            continue
+        j = int(np.argmax(np.abs(w[i])))
+        code = int(fp8.encode(np.asarray([w[i, j] / sc[i]], np.float32))[0])
+        assert code == (0xFE if w[i, j] < 0 else 0x7E)
+        assert abs(float(wq[i, j]) - float(w[i, j])) <= 2.0 ** -22 * abs(float(w[i, j]))
+        rel = np.abs(w[i]) / sc[i]
+        normal = rel >= 2.0 ** -6
+        assert np.all(np.abs(wq[i] - w[i])[normal] <= 2.0 ** -4 * np.abs(w[i])[normal] * (1 + 1e-6))
+        assert np.all(np.abs(wq[i] - w[i])[~normal] <= 2.0 ** -10 * sc[i] * (1 + 1e-6))
+    w2 = w * np.float32(8.0)
+    wq2, sc2 = quantize_rows(w2)
+    assert np.array_equal(wq2, wq * np.float32(8.0)) and np.array_equal(sc2[sc2 != 1], (sc * 8)[sc2 != 1])
+
+
+def test_fp8_weight_stack_is_the_dequantised_model():
+    """With FP8 weights the oracle's step is the bf16-source model run with
+    every projection replaced by its dequantised rows (checked against the
+    full recompute of a model holding those rows)."""
+    cfg = small_cfg(w_dtype="fp8", act_dtype="bf16", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                    head_dim=128, d_ffn=1024)
+    model = synth.Model(cfg, gain_noise=True)
+    outs, orc = _run_incremental(cfg, model, [0], 6, np.float64)
+
+    class Dq:
+        g_final = model.g_final
+        kv_scale = model.kv_scale
+
+        def layer(self, l):
+            return orc.layer(l)
+    full = forward_full(dict(cfg, w_dtype="bf16"), Dq(), frames(cfg, 0, 6), dtype=np.float64)
+    assert rel_err(outs[0], full) < 1e-10
+    plain = forward_full(dict(cfg, w_dtype="bf16"), model, frames(cfg, 0, 6), dtype=np.float64)
+    assert rel_err(outs[0], plain) > 1e-3  # the quantisation is really applied
