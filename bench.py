@@ -202,7 +202,7 @@ def beat_loop(cfg, beats, runs, n_active, seed=6):
     deadline = 0.160
     ctx = build_ctx(cfg)
     ctx.arena.zero_()
-    act = torch.bfloat16 if cfg["w_dtype"] == "bf16" else torch.float32
+    act = torch.bfloat16 if cfg["act_dtype"] == "bf16" else torch.float32
     x = torch.randn((S, cfg["d_model"]), device="cuda").to(act)
     y = torch.empty_like(x)
     d = None
@@ -465,6 +465,8 @@ def main():
                     help="serving-clock mode: beats per run (two steps per 160 ms beat)")
     ap.add_argument("--runs", type=int, default=3)
     ap.add_argument("--active", type=int, default=None, help="active sessions in --beats mode")
+    ap.add_argument("--weights", choices=["config", "fp8"], default="config",
+                    help="fp8: the library quantises the projection weights to E4M3 with per-row scales")
     ap.add_argument("--vocab", type=int, default=0,
                     help="output head over this many tokens (synthetic); steps run fd_step_tokens")
     ap.add_argument("--kv-ring", type=int, default=0,
@@ -508,6 +510,8 @@ def main():
     cfg["exec_mode"] = args.exec_mode
     cfg["kv_ring"] = args.kv_ring
     cfg["vocab"] = args.vocab
+    if args.weights == "fp8":
+        cfg.update(w_dtype="fp8", act_dtype="bf16")
     pos = cfg.get("position", cfg["max_context"] - 1) if args.position is None else args.position
     if pos >= cfg["max_context"] and not args.kv_ring:
         raise SystemExit("--position beyond the window needs --kv-ring 1")
@@ -571,12 +575,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg["w_dtype"] == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp8": "fp8 weights, bf16 activations"}.get(cfg["w_dtype"], "f32"),
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) frames, N(0,(0.02*sqrt(d))^2) cache prefill)",
         "config": {"workload": args.config, "layers": cfg["n_layers"], "d_model": cfg["d_model"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} (kv {cfg['n_kv_heads']})",
                    "d_ffn": cfg["d_ffn"], "sessions": S, "frame_index": pos,
-                   "weights": cfg["w_dtype"], "cache": cfg["kv_dtype"],
+                   "weights": cfg["w_dtype"] + (" (per-row scales)" if cfg["w_dtype"] == "fp8" else ""),
+                   "cache": cfg["kv_dtype"],
                    "exec_mode": "walk" if args.exec_mode else "kernels",
                    "window": "rolling" if args.kv_ring else "fixed",
                    "vocab": args.vocab},

@@ -66,6 +66,11 @@ bool aligned(const void* p) { return p && ((uintptr_t)p % fd::kAlign) == 0; }
 uint8_t* P(const fd_ctx* c, uint64_t off) { return (uint8_t*)c->buf.packed_weights + off; }
 uint8_t* Wk(const fd_ctx* c, uint64_t off) { return (uint8_t*)c->buf.workspace + off; }
 
+// FP8 weights: the per-row scales stored after a matrix's tiles (else null)
+const float* wscale(const fd_ctx* c, uint64_t off, const fd::GemmShape& g) {
+    return c->plan.w8 ? (const float*)(P(c, off) + (size_t)g.NB * g.KB * fd::kTileBytes) : nullptr;
+}
+
 int32_t* slot_active(const fd_ctx* c) { return (int32_t*)c->buf.slot_table; }
 int32_t* slot_pos(const fd_ctx* c) { return (int32_t*)c->buf.slot_table + c->plan.S; }
 
@@ -76,6 +81,8 @@ fd_status check_layer(const fd_layer_weights& lw) {
     return FD_OK;
 }
 
+// wt: weight format (0 fp32, 1 bf16, 2 FP8 codes of bf16 sources, whose
+// per-row scales go right after the tiles)
 hipError_t pack(const fd::GemmShape& g, int wt, const void* s0, int r0, const void* s1, int r1,
                 const void* s2, int interleave, uint8_t* dst, hipStream_t st) {
     fd::PackArgs a{};
@@ -90,13 +97,14 @@ hipError_t pack(const fd::GemmShape& g, int wt, const void* s0, int r0, const vo
     a.K = g.K;
     a.KB = g.KB;
     a.dst = dst;
+    a.scale = wt == 2 ? (float*)(dst + (size_t)g.NB * g.KB * fd::kTileBytes) : nullptr;
     return fd::launch_pack(a, wt, st);
 }
 
 hipError_t pack_stack(fd_ctx* c, const fd::StackPlan& sp, const fd_layer_weights* lw,
                       const float* g_final, hipStream_t st) {
     const fd::StackDims& d = sp.dims;
-    const int wt = c->plan.wt;
+    const int wt = c->plan.wkind;
     hipError_t e = hipSuccess;
     for (int l = 0; l < d.L && e == hipSuccess; ++l) {
         const fd::LayerOffsets& lo = sp.layers[l];
@@ -217,6 +225,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         fd::GemmArgs q = g;
         const fd::GemmShape& sq = sp.qkv;
         q.W = P(c, lo.qkv);
+        q.wscale = wscale(c, lo.qkv, sp.qkv);
         q.X = Wk(c, pl.ws_xg);
         q.K = sq.K; q.KB = sq.KB; q.NB = sq.NB; q.P = sq.P; q.MG = sq.MG;
         q.X_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
@@ -224,7 +233,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         q.y = (float*)Wk(c, pl.ws_qkv);
         q.ld = d.qkv_n();
         q.plane = (uint64_t)pl.Sp * d.qkv_n();
-        e = timed(c, K_QKV, st, [&] { return fd::launch_gemm(q, wt, sq.R, sq.MTG, sq.grid(), st); });
+        e = timed(c, K_QKV, st, [&] { return fd::launch_gemm(q, pl.wkind, sq.R, sq.MTG, sq.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::AttnArgs at{};
@@ -262,6 +271,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         fd::GemmArgs o = g;
         const fd::GemmShape& so = sp.o;
         o.W = P(c, lo.o);
+        o.wscale = wscale(c, lo.o, sp.o);
         o.X = Wk(c, pl.ws_o);
         o.X_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
         o.K = so.K; o.KB = so.KB; o.NB = so.NB; o.P = so.P; o.MG = so.MG;
@@ -272,12 +282,13 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         o.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         o.ss_out = (float*)Wk(c, pl.ws_ss_f);
         o.ld = d.d;
-        e = timed(c, K_O, st, [&] { return fd::launch_gemm(o, wt, so.R, so.MTG, so.grid(), st); });
+        e = timed(c, K_O, st, [&] { return fd::launch_gemm(o, pl.wkind, so.R, so.MTG, so.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::GemmArgs u = g;
         const fd::GemmShape& su = sp.gu;
         u.W = P(c, lo.gu);
+        u.wscale = wscale(c, lo.gu, sp.gu);
         u.X = Wk(c, pl.ws_xg);
         u.K = su.K; u.KB = su.KB; u.NB = su.NB; u.P = su.P; u.MG = su.MG;
         u.epi = fd::EPI_GU;
@@ -287,12 +298,13 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         u.h_out = Wk(c, pl.ws_h);
         u.h_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
         u.F = d.f;
-        e = timed(c, K_GU, st, [&] { return fd::launch_gemm(u, wt, su.R, su.MTG, su.grid(), st); });
+        e = timed(c, K_GU, st, [&] { return fd::launch_gemm(u, pl.wkind, su.R, su.MTG, su.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::GemmArgs dn = g;
         const fd::GemmShape& sd = sp.down;
         dn.W = P(c, lo.down);
+        dn.wscale = wscale(c, lo.down, sp.down);
         dn.X = Wk(c, pl.ws_h);
         dn.X_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
         dn.K = sd.K; dn.KB = sd.KB; dn.NB = sd.NB; dn.P = sd.P; dn.MG = sd.MG;
@@ -303,7 +315,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         dn.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         dn.ss_out = (float*)Wk(c, pl.ws_ss_a);
         dn.ld = d.d;
-        e = timed(c, K_DOWN, st, [&] { return fd::launch_gemm(dn, wt, sd.R, sd.MTG, sd.grid(), st); });
+        e = timed(c, K_DOWN, st, [&] { return fd::launch_gemm(dn, pl.wkind, sd.R, sd.MTG, sd.grid(), st); });
         nss = sd.n_groups;
     }
     *nss_out = nss;
@@ -692,7 +704,7 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
         if (e == hipSuccess) e = upload_tables(c, p.dstack, std::vector<float>(), false, s);
     }
     if (e == hipSuccess && p.head)
-        e = pack(p.hshape, p.wt, w->w_head, p.hshape.N, nullptr, 0, nullptr, 0, P(c, p.w_head), s);
+        e = pack(p.hshape, p.wkind, w->w_head, p.hshape.N, nullptr, 0, nullptr, 0, P(c, p.w_head), s);
     // the output head reads the final-normed rows (and their bf16 low part)
     c->head_x = Wk(c, p.ws_yw);
     c->head_x_lo = p.wt && p.head ? Wk(c, p.ws_yw_lo) : nullptr;
@@ -873,6 +885,7 @@ fd_status fd_step_tokens(fd_ctx* c, const void* x_in, void* y_out, void* depth_o
     const fd::GemmShape& h = pl.hshape;
     fd::GemmArgs g{};
     g.W = P(c, pl.w_head);
+    g.wscale = wscale(c, pl.w_head, h);
     g.X = c->head_x;
     g.X_lo = c->head_x_lo;
     g.K = h.K; g.KB = h.KB; g.NB = h.NB; g.P = h.P; g.MG = h.MG;
@@ -889,7 +902,7 @@ fd_status fd_step_tokens(fd_ctx* c, const void* x_in, void* y_out, void* depth_o
     am.active = slot_active(c);
     am.tokens = tokens_out;
     hipError_t e = timed(c, K_HEAD, s, [&] {
-        hipError_t r = fd::launch_gemm(g, pl.wt, h.R, h.MTG, h.grid(), s);
+        hipError_t r = fd::launch_gemm(g, pl.wkind, h.R, h.MTG, h.grid(), s);
         return r == hipSuccess ? fd::launch_argmax(am, s) : r;
     });
     if (e != hipSuccess) return hip_fail(c, e, "fd_step_tokens launch");

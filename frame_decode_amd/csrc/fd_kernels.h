@@ -42,6 +42,7 @@ struct GemmArgs {
     int F;
     // EPI_F32 / EPI_PLANES
     float* y;              // [Sp][ld] (EPI_PLANES: [P][Sp][ld])
+    const float* wscale;   // FP8 weights: [NB*16] output-row scales (the tiles hold codes of w / scale)
 };
 
 struct AttnArgs {
@@ -119,6 +120,7 @@ struct PackArgs {
     int interleave;        // 1: packed row 2j = src0 row j, 2j+1 = src1 row j
     int N, K, KB;
     uint8_t* dst;
+    float* scale;          // FP8 weights: per packed row, max|w| / 448 (1 for a zero row)
 };
 
 struct KvWriteArgs {
@@ -170,8 +172,10 @@ struct WalkShape {
 // Depth of a GEMM wave's register ring of k-tiles: as deep as ~48
 // outstanding 16-byte-per-lane loads allow (the wave's load counter holds
 // 63), at least 2.  SX: the session rows come as two bf16 parts.
-constexpr int gemm_stages(int NG, int MTG, int SX = 0) {
-    return 48 / (NG + MTG * (1 + SX)) < 2 ? 2 : (48 / (NG + MTG * (1 + SX)) > 8 ? 8 : 48 / (NG + MTG * (1 + SX)));
+constexpr int gemm_stages(int NG, int MTG, int SX = 0, int W8 = 0) {
+    return 48 / (NG + (1 + W8) * MTG * (1 + SX)) < 2
+               ? 2
+               : (48 / (NG + (1 + W8) * MTG * (1 + SX)) > 8 ? 8 : 48 / (NG + (1 + W8) * MTG * (1 + SX)));
 }
 
 // Launchers (enqueue on `st`; return the launch error).

@@ -108,7 +108,7 @@ GemmShape tuned(GemmShape g, const char* name) {
     return shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, P);
 }
 
-void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8,
+void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8, bool w8,
                 uint64_t& off) {
     sp.dims = dims;
     sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256), "qkv");
@@ -116,7 +116,7 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256), "gu");
     sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256), "down");
     sp.layers.resize(dims.L);
-    auto tiles = [](const GemmShape& g) { return (uint64_t)g.NB * g.KB * kTileBytes; };
+    auto tiles = [w8](const GemmShape& g) { return packed_matrix_bytes(g, w8); };
     for (int l = 0; l < dims.L; ++l) {
         LayerOffsets& lo = sp.layers[l];
         lo.qkv = off; off = align_up(off + tiles(sp.qkv));
@@ -159,12 +159,16 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
 fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     Plan p;
     p.cfg = c;
-    if (!(c.w_dtype == FD_F32 || c.w_dtype == FD_BF16)) {
-        *err = "w_dtype must be FD_F32 or FD_BF16";
+    if (!(c.w_dtype == FD_F32 || c.w_dtype == FD_BF16 || c.w_dtype == FD_FP8_E4M3)) {
+        *err = "w_dtype must be FD_F32, FD_BF16 or FD_FP8_E4M3";
         return FD_E_UNSUPPORTED;
     }
-    if (c.act_dtype != c.w_dtype) {
-        *err = "act_dtype must equal w_dtype";
+    if (c.act_dtype != (c.w_dtype == FD_FP8_E4M3 ? FD_BF16 : c.w_dtype)) {
+        *err = "act_dtype must equal w_dtype (FD_BF16 with FD_FP8_E4M3 weights)";
+        return FD_E_UNSUPPORTED;
+    }
+    if (c.w_dtype == FD_FP8_E4M3 && (c.depth_steps > 0 || c.exec_mode == FD_EXEC_WALK)) {
+        *err = "FD_FP8_E4M3 weights: no depth stack and no FD_EXEC_WALK";
         return FD_E_UNSUPPORTED;
     }
     if (!(c.kv_dtype == FD_F32 || c.kv_dtype == FD_FP8_E4M3)) {
@@ -199,13 +203,15 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         *err = "max_context outside 1..65536";
         return FD_E_UNSUPPORTED;
     }
-    p.wt = c.w_dtype == FD_BF16 ? 1 : 0;
+    p.wt = c.act_dtype == FD_BF16 ? 1 : 0;
+    p.w8 = c.w_dtype == FD_FP8_E4M3;
+    p.wkind = p.w8 ? 2 : p.wt;
     p.act_bytes = p.wt ? 2 : 4;
     p.kv_fp8 = c.kv_dtype == FD_FP8_E4M3;
     p.ring = c.kv_ring == 1;
     p.head = c.vocab > 0;
     p.kv_bytes = p.kv_fp8 ? 1 : 4;
-    const int KT = p.wt ? 32 : 16;
+    const int KT = p.w8 ? 64 : (p.wt ? 32 : 16);  // k per weight tile
     fd_status st = check_stack("main", c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim,
                                c.d_ffn, KT, err);
     if (st != FD_OK) return st;
@@ -235,19 +241,19 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
 
     uint64_t off = 0;
     StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};
-    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, off);
+    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, off);
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
         p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
         p.w_in = off;
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
-        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, off);
+        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, off);
     }
     if (p.head) {
         p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256);
         p.w_head = off;
-        off = align_up(off + (uint64_t)p.hshape.NB * p.hshape.KB * kTileBytes);
+        off = align_up(off + packed_matrix_bytes(p.hshape, p.w8));
     }
     p.packed_bytes = std::max<uint64_t>(off, kAlign);
 

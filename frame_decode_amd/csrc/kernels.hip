@@ -205,6 +205,25 @@ __device__ __forceinline__ size_t xoff(int m, int k, int MT) {
 // weight packing: [N][K] row-major -> tiles [NB][KB][64 lanes][16 B].
 // bf16 tile = 16 rows x 32 k; lane l holds row l%16, k 8*(l/16) .. +8.
 // fp32 tile = 16 rows x 16 k; lane l holds row l%16, k 4*(l/16) .. +4.
+// Source matrix and row of packed row n (Q|K|V stacked, or gate/up rows
+// interleaved).
+__device__ __forceinline__ const void* pack_src(const PackArgs& a, int n, int* row) {
+    if (a.interleave) {
+        *row = n >> 1;
+        return (n & 1) ? a.src[1] : a.src[0];
+    }
+    if (n < a.rows[0]) {
+        *row = n;
+        return a.src[0];
+    }
+    if (n < a.rows[0] + a.rows[1]) {
+        *row = n - a.rows[0];
+        return a.src[1];
+    }
+    *row = n - a.rows[0] - a.rows[1];
+    return a.src[2];
+}
+
 template <int WT>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -215,24 +234,62 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     int nb = (int)(tile / a.KB), kb = (int)(tile % a.KB);
     int n = nb * 16 + (lane & 15);
     int k0 = WT ? kb * 32 + (lane >> 4) * 8 : kb * 16 + (lane >> 4) * 4;
-    const void* src;
     int row;
-    if (a.interleave) {
-        src = (n & 1) ? a.src[1] : a.src[0];
-        row = n >> 1;
-    } else if (n < a.rows[0]) {
-        src = a.src[0];
-        row = n;
-    } else if (n < a.rows[0] + a.rows[1]) {
-        src = a.src[1];
-        row = n - a.rows[0];
-    } else {
-        src = a.src[2];
-        row = n - a.rows[0] - a.rows[1];
-    }
+    const void* src = pack_src(a, n, &row);
     const int eb = WT ? 2 : 4;
     const u32x4 v = *(const u32x4*)((const uint8_t*)src + ((size_t)row * a.K + k0) * eb);
     *(u32x4*)(a.dst + tile * 1024 + (size_t)lane * 16) = v;
+}
+
+// FP8 weights, step 1: per packed row (one workgroup each) the scale
+// max|w| / 448 of its bf16 source row (1 for a row of zeros), so the row's
+// largest entry maps to the largest finite E4M3 magnitude.
+__global__ __launch_bounds__(256) void row_scale_kernel(PackArgs a) {
+    const int n = blockIdx.x;
+    int row;
+    const uint16_t* src = (const uint16_t*)pack_src(a, n, &row) + (size_t)row * a.K;
+    float m = 0.f;
+    for (int k = threadIdx.x; k < a.K; k += blockDim.x) m = fmaxf(m, fabsf(bf2f(src[k])));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    __shared__ float s_m[4];
+    if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float mx = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+        a.scale[n] = mx > 0.f ? mx / 448.0f : 1.0f;
+    }
+}
+
+// FP8 weights, step 2: tiles [NB][K/64][64 lanes][16 B] of codes of w / scale.
+// A tile is 16 rows x 64 k; lane l (row l%16, g = l/16) holds k 8g..8g+7 in
+// bytes 0..7 and k 32+8g..32+8g+7 in bytes 8..15, so the two halves are the
+// bf16 MFMA operands for the activation k-tiles 2j and 2j+1 after an exact
+// E4M3 -> bf16 conversion.
+__global__ __launch_bounds__(256) void pack8_kernel(PackArgs a) {
+    size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t total = (size_t)(a.N / 16) * a.KB * 64;
+    if (id >= total) return;
+    const int lane = (int)(id & 63);
+    const size_t tile = id >> 6;
+    const int nb = (int)(tile / a.KB), kb = (int)(tile % a.KB);
+    const int n = nb * 16 + (lane & 15);
+    int row;
+    const uint16_t* src = (const uint16_t*)pack_src(a, n, &row) + (size_t)row * a.K;
+    const float sc = a.scale[n];
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k0 = kb * 64 + h * 32 + (lane >> 4) * 8;
+        const u32x4 v = *(const u32x4*)(src + k0);  // 8 bf16
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t lo = v[2 * q], hi = v[2 * q + 1];
+            w[2 * h + q] = enc_e4m3(bf2f(lo & 0xFFFFu) / sc) | (enc_e4m3(bf2f(lo >> 16) / sc) << 8) |
+                           (enc_e4m3(bf2f(hi & 0xFFFFu) / sc) << 16) | (enc_e4m3(bf2f(hi >> 16) / sc) << 24);
+        }
+    }
+    *(u32x4*)(a.dst + tile * 1024 + (size_t)lane * 16) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -412,8 +469,12 @@ struct NoWait {
 // One workgroup task of a projection; s_acc: 4 * NG * MTG * 64 f32x4 of LDS.
 // wait(): called once, before the first read of data an earlier phase wrote
 // (the persistent walk's barrier; NoWait for a kernel launch).
-template <int WT, int NG, int MTG, int STG, int SX, int CO, class Wait>
+// W8: the weight tiles are FP8 codes (16 rows x 64 k per 1 KiB, see
+// pack8_kernel) that each wave converts exactly to bf16 operands for two
+// activation k-tiles; the per-row scales multiply the summed tiles.
+template <int WT, int NG, int MTG, int STG, int SX, int CO, int W8, class Wait>
 __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc_mem, Wait&& wait) {
+    static_assert(!W8 || (WT && SX), "FP8 weights take bf16 activations in two parts");
     typedef typename BFrag<WT>::T BT;
     constexpr int NTL = NG * MTG;
     constexpr int OWN = (NTL + 3) / 4;
@@ -453,16 +514,21 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     // one k-tile is multiplied, the next STG-1 are in flight, which is what
     // keeps enough bytes outstanding per CU to cover HBM latency.
     // (SX: B[.][MTG + t] holds the low part of m-tile t)
-    constexpr int NB_ = MTG * (1 + SX);
+    constexpr int NBX = MTG * (1 + SX);     // fragments of one activation k-tile
+    constexpr int NB_ = NBX * (1 + W8);     // per weight tile (FP8: two activation k-tiles)
     u32x4 A[STG][NG];
     BT B[STG][NB_];
     auto load_x = [&](BT (&Bd)[NB_], int j) {
         const int kb = kb0 + wave + 4 * j;
 #pragma unroll
-        for (int t = 0; t < MTG; ++t) Bd[t] = __builtin_bit_cast(BT, xp[(size_t)kb * xk + t * 64]);
-        if constexpr (SX) {
+        for (int tt = 0; tt <= W8; ++tt) {
+            const size_t kx = (size_t)((1 + W8) * kb + tt) * xk;
 #pragma unroll
-            for (int t = 0; t < MTG; ++t) Bd[MTG + t] = __builtin_bit_cast(BT, xlp[(size_t)kb * xk + t * 64]);
+            for (int t = 0; t < MTG; ++t) Bd[tt * NBX + t] = __builtin_bit_cast(BT, xp[kx + t * 64]);
+            if constexpr (SX) {
+#pragma unroll
+                for (int t = 0; t < MTG; ++t) Bd[tt * NBX + MTG + t] = __builtin_bit_cast(BT, xlp[kx + t * 64]);
+            }
         }
     };
     auto load_w = [&](u32x4 (&Ad)[NG], int j) {
@@ -477,12 +543,36 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     // (high parts of every tile first, then low parts: consecutive products
     // never chain on one accumulator)
     auto mma = [&](u32x4 (&As)[NG], BT (&Bs)[NB_]) {
-#pragma unroll
-        for (int h = 0; h <= SX; ++h)
+        if constexpr (W8) {
+            // E4M3 -> bf16 is exact (3 mantissa bits): codes c0..c7 of each
+            // half become one bf16 operand
+            u32x4 f[2][NG];
 #pragma unroll
             for (int r = 0; r < NG; ++r)
 #pragma unroll
-                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(As[r], Bs[h * MTG + t], acc[r][t]);
+                for (int q = 0; q < 4; ++q) {
+                    f[q >> 1][r][2 * (q & 1)] = __builtin_bit_cast(
+                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(As[r][q], 1.0f, false));
+                    f[q >> 1][r][2 * (q & 1) + 1] = __builtin_bit_cast(
+                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(As[r][q], 1.0f, true));
+                }
+#pragma unroll
+            for (int h = 0; h <= SX; ++h)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < NG; ++r)
+#pragma unroll
+                        for (int t = 0; t < MTG; ++t)
+                            acc[r][t] = mfma_tile<WT>(f[tt][r], Bs[tt * NBX + h * MTG + t], acc[r][t]);
+        } else {
+#pragma unroll
+            for (int h = 0; h <= SX; ++h)
+#pragma unroll
+                for (int r = 0; r < NG; ++r)
+#pragma unroll
+                    for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(As[r], Bs[h * MTG + t], acc[r][t]);
+        }
     };
 
     const bool norm_here = a.ss_in != nullptr;
@@ -541,6 +631,12 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     for (int j = 0; j < OWN; ++j) {
         const int i = wave + 4 * j;
         if (i < NTL) v[j] = ((s_acc[0][i][lane] + s_acc[1][i][lane]) + s_acc[2][i][lane]) + s_acc[3][i][lane];
+        if constexpr (W8) {  // rows (nb0 + r)*16 + 4*(lane/16) + e: their scales
+            if (i < NTL) {
+                const int r = i / MTG;
+                v[j] *= *(const f32x4*)(a.wscale + min(nb0 + r, a.NB - 1) * 16 + (lane >> 4) * 4);
+            }
+        }
     }
     if (a.epi == EPI_PLANES) {
         // each split writes its own plane; the consumer adds them
@@ -571,10 +667,10 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     gemm_finish<WT, NG, MTG, 4, OWN, CO>(a, v, ti, ng, mt0, 0, MTG, s_rstd);
 }
 
-template <int WT, int NG, int MTG, int STG, int SX>
+template <int WT, int NG, int MTG, int STG, int SX, int W8 = 0>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     __shared__ f32x4 s_acc[4 * NG * MTG * 64];
-    gemm_wg<WT, NG, MTG, STG, SX, 0>(a, blockIdx.x, s_acc, NoWait{});
+    gemm_wg<WT, NG, MTG, STG, SX, 0, W8>(a, blockIdx.x, s_acc, NoWait{});
 }
 
 // Adds the P k-split partial tiles of one m-tile t of an (n-group, m-group)
@@ -1206,10 +1302,10 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkArgs w) {
         for (int it = blockIdx.x; it < P.n_items; it += gridDim.x) {
             switch (P.kind) {
                 case WALK_GEMM4:
-                    gemm_wg<WT, 4, MTG, gemm_stages(4, MTG, WT), WT, 1>(w.gemm[P.idx], it, s_acc, wait);
+                    gemm_wg<WT, 4, MTG, gemm_stages(4, MTG, WT), WT, 1, 0>(w.gemm[P.idx], it, s_acc, wait);
                     break;
                 case WALK_GEMM6:
-                    gemm_wg<WT, 6, MTG, gemm_stages(6, MTG, WT), WT, 1>(w.gemm[P.idx], it, s_acc, wait);
+                    gemm_wg<WT, 6, MTG, gemm_stages(6, MTG, WT), WT, 1, 0>(w.gemm[P.idx], it, s_acc, wait);
                     break;
                 case WALK_ATTN: attn_wg<WT, FP8, D, G, 1, walk_attn_nit<FP8>()>(w.attn[P.idx], it, wait); break;
                 case WALK_ATTN_DEPTH:
@@ -1289,11 +1385,37 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int 
 // ---------------------------------------------------------------------------
 // launchers
 
+// wt: 0 fp32, 1 bf16, 2 FP8 codes of bf16 sources with per-row scales
 hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
     const size_t total = (size_t)(a.N / 16) * a.KB * 64;
     const unsigned blocks = (unsigned)((total + 255) / 256);
-    if (wt) hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(256), 0, st, a);
+    if (wt == 2) {
+        if (!a.scale) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(row_scale_kernel, dim3(a.N), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(pack8_kernel, dim3(blocks), dim3(256), 0, st, a);
+    } else if (wt) {
+        hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(256), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+// FP8 weights (bf16 activations in two parts), 4 or 6 blocks per workgroup
+template <int NG>
+static hipError_t gemm_w8(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    if (!a.X_lo || !a.wscale) return hipErrorInvalidValue;
+    switch (MTG) {
+#define FD_G(MT)                                                                                             \
+    case MT:                                                                                                 \
+        hipLaunchKernelGGL((gemm_kernel<1, NG, MT, gemm_stages(NG, MT, 1, 1), 1, 1>), dim3(grid), dim3(256), 0, st, a); \
+        if (a.P > 1 && a.epi != EPI_PLANES)                                                                \
+            hipLaunchKernelGGL((gemm_reduce_kernel<1, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a);   \
+        break;
+        FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
+#undef FD_G
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -1335,7 +1457,9 @@ static hipError_t gemm_ng4(const GemmArgs& a, int MTG, int grid, hipStream_t st)
     return hipGetLastError();
 }
 
+// wt: 0 fp32, 1 bf16, 2 FP8 weights with bf16 activations
 hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hipStream_t st) {
+    if (wt == 2) return NG == 6 ? gemm_w8<6>(a, MTG, grid, st) : (NG == 4 ? gemm_w8<4>(a, MTG, grid, st) : hipErrorInvalidValue);
     if (NG == 6) return wt ? gemm_ng<1, 6>(a, MTG, grid, st) : gemm_ng<0, 6>(a, MTG, grid, st);
     if (NG == 4) return wt ? gemm_ng4<1>(a, MTG, grid, st) : gemm_ng4<0>(a, MTG, grid, st);
     return hipErrorInvalidValue;

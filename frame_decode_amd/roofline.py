@@ -32,8 +32,11 @@ def weight_bytes(cfg: dict, head: bool = False) -> int:
     """One read of every projection weight of the main stack (and, with a
     depth stack, its weights once per depth step plus the input projection;
     with head=True the output head's vocab x d_model weights)."""
-    wb = 2 if cfg["w_dtype"] == "bf16" else 4
+    wb = {"bf16": 2, "fp8": 1}.get(cfg["w_dtype"], 4)
     b = weight_params(cfg) * wb
+    if cfg["w_dtype"] == "fp8":  # one fp32 scale per output row of every projection
+        d, hq, hkv, hd, f = cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["d_ffn"]
+        b += 4 * cfg["n_layers"] * ((hq + 2 * hkv) * hd + d + 2 * f + d)
     if cfg.get("depth_steps", 0):
         b += cfg["depth_steps"] * weight_params(cfg, depth=True) * wb
         b += cfg["depth_d"] * cfg["d_model"] * wb

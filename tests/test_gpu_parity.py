@@ -429,3 +429,51 @@ def test_output_head_greedy_tokens(family, exec_mode):
         for s in slots:
             pos[s] += 1
     ctx.fd_destroy()
+
+
+def test_fp8_weights_with_per_row_scales():
+    """FP8 E4M3 weights quantised by the library from bf16 sources (one
+    scale per output row), bf16 activations, FP8 cache, with the output
+    head: outputs and logits match the oracle running the dequantised
+    weights (2e-2) over three steps; tokens are the first maximum of the
+    GPU's logits."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
+                              d_ffn=1536, max_slots=7, max_context=400, vocab=1024,
+                              w_dtype="fp8", act_dtype="bf16")
+    model = synth.Model(cfg, gain_noise=True)
+    start = [0, 1, 100, 255, 256, 390]
+    say(f"fp8 weights: slots {start}")
+    ctx = make_context(cfg, model)
+    orc = Oracle(cfg, model)
+    slots = ctx.fd_alloc_slots(len(start))
+    sess = {s: 500 + s for s in slots}
+    pos = dict(zip(slots, start))
+    for s in slots:
+        if pos[s]:
+            for l in range(cfg["n_layers"]):
+                v = synth.prefill_values(cfg, sess[s], l, pos[s])
+                orc.prefill(s, l, v)
+                ctx.fd_kv_write(s, l, 0, torch.from_numpy(v).cuda())
+            ctx.fd_set_position(s, pos[s])
+    S, V = cfg["max_slots"], cfg["vocab"]
+    y = torch.empty((S, cfg["d_model"]), device="cuda", dtype=torch.bfloat16)
+    tokens = torch.empty((S,), device="cuda", dtype=torch.int32)
+    logits = torch.empty((S, V), device="cuda", dtype=torch.float32)
+    for step in range(3):
+        x_np, x = rows_input(cfg, sess, {s: pos[s] for s in slots})
+        ctx.fd_step_tokens(x, y, tokens, logits)
+        ctx.fd_sync()
+        ref = orc.step(slots, x_np[slots], [pos[s] for s in slots])
+        lref, _ = orc.head(ref)
+        e = rel_err_rows(to_np(y)[slots], ref)
+        lg = logits.cpu().numpy()
+        el = rel_err_rows(lg[slots], lref)
+        say(f"  step {step}: output max rel err {e:.3e}, logits {el:.3e}")
+        assert e <= 2e-2 and el <= 2e-2
+        tg = tokens.cpu().numpy()
+        for s in slots:
+            check(tg[s] == int(np.argmax(lg[s])), f"slot {s}: token is not the first maximum")
+        check(tg[S - 1] == -1, "the inactive slot's token must be -1")
+        for s in slots:
+            pos[s] += 1
+    ctx.fd_destroy()

@@ -276,3 +276,25 @@ def test_output_head_plan(host):
     assert s1.kv_arena == s0.kv_arena and s1.workspace > s0.workspace
     cfg["vocab"] = 2050
     assert _plan(host, cfg)[0] == FD_E_UNSUPPORTED
+
+
+def test_fp8_weight_plan(host):
+    """FP8 weights: one byte per parameter plus one fp32 scale per output
+    row; bf16 activations required; no depth stack and no persistent walk."""
+    cfg = synth.get_config("7b_s8_p256")
+    st0, s0 = _plan(host, cfg)
+    cfg.update(w_dtype="fp8", act_dtype="bf16")
+    st1, s1 = _plan(host, cfg)
+    assert st0 == FD_OK and st1 == FD_OK
+    params = 32 * (12288 * 4096 + 4096 * 4096 + 22528 * 4096 + 4096 * 11264)
+    rows = 32 * (12288 + 4096 + 22528 + 4096)
+    # weights halve; tables (gains, rope, scales of the cache) are common to both
+    assert s0.packed_weights - s1.packed_weights == params - 4 * rows
+    assert s1.kv_arena == s0.kv_arena
+    bad = dict(cfg, act_dtype="fp8")
+    assert _plan(host, bad)[0] == FD_E_UNSUPPORTED
+    walk = dict(cfg, exec_mode=1)
+    assert _plan(host, walk)[0] == FD_E_UNSUPPORTED
+    talker = synth.get_config("talker_s56")
+    talker.update(w_dtype="fp8", act_dtype="bf16")
+    assert _plan(host, talker)[0] == FD_E_UNSUPPORTED
