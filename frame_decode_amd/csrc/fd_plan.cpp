@@ -337,8 +337,8 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
             (p.depth && p.dstack.qkv.MTG != p.main.qkv.MTG)) {
             *err = "FD_EXEC_WALK is compiled for: fp32 with head_dim 64, G 1, no depth stack, <= 32 "
                    "slots; fp32 with head_dim 256, G 4 and a depth stack of head_dim 128, G 1, <= 64 "
-                   "slots; bf16 weights with an FP8 cache, head_dim 128, G 1, no depth stack, <= 80 "
-                   "slots per m-group";
+                   "slots; bf16 weights with an FP8 cache, head_dim 128, G 1, no depth stack, <= 5 row "
+                   "tiles per m-group (<= 80 slots, or > 128)";
             return FD_E_UNSUPPORTED;
         }
         // every cross-phase output gets a region of its own; sizes at 4 bytes

@@ -127,7 +127,9 @@ typedef struct {
  * per kv head and no depth stack (at most 32 slots); fp32 stacks with
  * head_dim 256, 4 query heads per kv head and a depth stack of head_dim 128
  * with one query head per kv head (at most 64 slots); bf16 weights with an
- * FP8 cache, head_dim 128, one query head per kv head, no depth stack.
+ * FP8 cache, head_dim 128, one query head per kv head, no depth stack, at
+ * most 5 row tiles of 16 slots per m-group of the projections (up to 80
+ * slots, or more than 128, where the rows split into m-groups).
  * A barrier wait that times out makes the launch stop early and the next
  * fd_sync return FD_E_DEVICE.
  */

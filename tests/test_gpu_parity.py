@@ -477,3 +477,39 @@ def test_fp8_weights_with_per_row_scales():
         for s in slots:
             pos[s] += 1
     ctx.fd_destroy()
+
+
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+def test_many_slots_row_groups(exec_mode):
+    """140 slots (9 row tiles: the projections split the rows into two
+    m-groups of 5 tiles) with 130 active sessions at ragged positions,
+    bf16/FP8: every active row matches the oracle, inactive rows are zero."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                              d_ffn=1024, max_slots=140, max_context=64, exec_mode=exec_mode)
+    model = synth.Model(cfg, gain_noise=True)
+    rng = np.random.default_rng(21)
+    start = [int(v) for v in rng.integers(0, 60, size=130)]
+    ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 2, tol=2e-2, sentinel=False)
+    say(f"many slots: worst {worst:.3e}")
+
+
+@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
+def test_step_with_no_active_session(exec_mode):
+    """A step with every slot free writes zero rows, changes no cache byte
+    and no position; a session admitted afterwards starts at position 0."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=256, n_heads=2, n_kv_heads=2,
+                              d_ffn=512, max_slots=4, max_context=64, exec_mode=exec_mode)
+    model = synth.Model(cfg)
+    ctx = make_context(cfg, model)
+    _sentinel_fill(ctx, cfg)
+    before = ctx.arena_view().cpu().numpy().copy()
+    x = torch.randn((4, 256), device="cuda").to(torch.bfloat16)
+    y = torch.full((4, 256), 3.0, device="cuda", dtype=torch.bfloat16)
+    ctx.fd_step(x, y)
+    ctx.fd_sync()
+    check(bool(torch.all(y == 0)), "rows of free slots must be zero")
+    check(np.array_equal(ctx.arena_view().cpu().numpy(), before), "the cache changed")
+    for s in range(4):
+        assert ctx.fd_slot_state(s) == (0, 0)
+    assert ctx.fd_alloc_slots(1) == [0] and ctx.fd_slot_state(0) == (1, 0)
+    ctx.fd_destroy()
