@@ -142,7 +142,7 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     // set-up and merge costs would dominate).
     AttnShape& a = sp.attn;
     a.lpp = kv_fp8 ? dims.hd / 16 : dims.hd / 8;
-    const int round = kWaves * kAttnIters * (64 / a.lpp);
+    const int round = kWaves * (kv_fp8 ? kAttnItersFp8 : kAttnIters) * (64 / a.lpp);
     const int pairs = std::max(1, S * dims.hkv);
     const int64_t window_bytes = (int64_t)dims.T * 2 * dims.hd * (kv_fp8 ? 1 : 4);
     int want = std::max(1, std::min(cdiv(1024, pairs), (int)((window_bytes + (512 << 10) - 1) >> 19)));

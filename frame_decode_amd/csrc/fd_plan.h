@@ -15,7 +15,8 @@ namespace fd {
 constexpr int kWaves = 4;          // waves per workgroup in the GEMM and attention kernels
 constexpr int kTileBytes = 1024;   // one packed weight tile = 64 lanes x 16 bytes
 constexpr int kMaxMTG = 8;         // most 16-row tiles of sessions one GEMM workgroup holds
-constexpr int kAttnIters = 8;      // position groups each attention wave walks per chunk
+constexpr int kAttnIters = 8;      // position loads per attention wave block (fp32 cache)
+constexpr int kAttnItersFp8 = 16;  // (FP8 cache)
 constexpr uint64_t kAlign = 256;
 
 inline uint64_t align_up(uint64_t v, uint64_t a = kAlign) { return (v + a - 1) / a * a; }

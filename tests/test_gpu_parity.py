@@ -182,7 +182,8 @@ def test_bf16_fp8_ragged_multichunk(exec_mode):
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 1, 255, 256, 257, 300, 511, 690]
     # this window is short enough for one chunk by default: ask the plan
-    # for three (256-position chunks) so the chunk merge is exercised
+    # for three (it rounds chunks to whole 512-position blocks: two chunks)
+    # so the chunk merge is exercised
     os.environ["FD_TUNE"] = "attn.chunks=3"
     try:
         ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
@@ -315,11 +316,11 @@ def test_rolling_window_across_the_wrap(family, exec_mode):
         start, tol, tune = [0, 61, 63, 64, 130, 200], 1e-3, None
     else:
         cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
-                                  d_ffn=1024, max_slots=6, max_context=300, kv_ring=1,
+                                  d_ffn=1024, max_slots=6, max_context=1100, kv_ring=1,
                                   exec_mode=exec_mode)
-        # three chunks of the window: the new entry's position falls in
-        # different chunks as the frame index advances
-        start, tol, tune = [0, 297, 299, 300, 455, 1000], 2e-2, "attn.chunks=3"
+        # three chunks of the window (512, 512, 76 positions): the new
+        # entry's position falls in different chunks as the frame advances
+        start, tol, tune = [0, 1097, 1099, 1100, 1655, 3000], 2e-2, "attn.chunks=3"
     T = cfg["max_context"]
     model = synth.Model(cfg, gain_noise=True)
     say(f"rolling window: {family} {'walk' if exec_mode else 'kernels'} T={T} start={start}")
