@@ -275,6 +275,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         o.X = Wk(c, pl.ws_o);
         o.X_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
         o.K = so.K; o.KB = so.KB; o.NB = so.NB; o.P = so.P; o.MG = so.MG;
+        o.cnt = so.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         o.epi = fd::EPI_RESID;
         o.x = (float*)Wk(c, pl.ws_x);
         o.xg = Wk(c, pl.ws_xg);
@@ -291,6 +292,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         u.wscale = wscale(c, lo.gu, sp.gu);
         u.X = Wk(c, pl.ws_xg);
         u.K = su.K; u.KB = su.KB; u.NB = su.NB; u.P = su.P; u.MG = su.MG;
+        u.cnt = su.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         u.epi = fd::EPI_GU;
         u.ss_in = (const float*)Wk(c, pl.ws_ss_f);
         u.nss = so.n_groups;
@@ -308,6 +310,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         dn.X = Wk(c, pl.ws_h);
         dn.X_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
         dn.K = sd.K; dn.KB = sd.KB; dn.NB = sd.NB; dn.P = sd.P; dn.MG = sd.MG;
+        dn.cnt = sd.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         dn.epi = fd::EPI_RESID;
         dn.x = (float*)Wk(c, pl.ws_x);
         dn.xg = Wk(c, pl.ws_xg);

@@ -21,6 +21,8 @@ struct GemmArgs {
     const void* X_lo;   // optional (bf16 only): low parts, the input being X + X_lo
     int K, KB, NB, P, MG, MT, Sp, S;
     float* part;        // split-K partial tiles (P > 1): [n-group*MG + m-group][P][tiles][64][4]
+    int* cnt;           // P > 1, non-null: per (n-group, m-group) arrival counters (zero between
+                        // launches); the last workgroup to arrive adds the partials and finishes
     int epi;
     // row scaling by the RMS norm of the GEMM input: rstd[m] = (sum_i ss[i][m] / d + eps)^-1/2
     const float* ss_in;    // [Sp][ss_stride] partial sums of x^2 of the GEMM input rows

@@ -35,6 +35,7 @@ struct GemmShape {
     uint64_t w_off = 0;   // offset of the packed tiles in the packed buffer
     uint64_t part_floats = 0;  // partial-sum floats needed when P > 1 (n_groups*MG*P*R*MTG*256)
     int counters = 0;
+    bool fused = false;  // P > 1: the last workgroup of an n-group adds the partials (no reduce launch)
     int grid() const { return n_groups * P * MG; }
 };
 

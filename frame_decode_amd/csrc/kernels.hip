@@ -653,12 +653,45 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     if (a.P > 1) {
         // partial tiles of this split, [group][split][tile][64 lanes]
         f32x4* pp = (f32x4*)a.part + ((size_t)(ng * a.MG + mg) * a.P + ks) * NTL * 64 + lane;
+        if (!a.cnt) {  // a reduce kernel (or walk phase) adds them
+#pragma unroll
+            for (int j = 0; j < OWN; ++j) {
+                const int i = wave + 4 * j;
+                if (i < NTL) st4<CO>((float*)(pp + (size_t)i * 64), v[j]);
+            }
+            return;
+        }
+        // the last of the group's P workgroups to arrive adds the partials:
+        // they are written through to memory (device scope) before the
+        // arrival is counted, and the group's lines were not read on this
+        // XCD earlier in the launch, so the last one reads current data
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             const int i = wave + 4 * j;
-            if (i < NTL) st4<CO>((float*)(pp + (size_t)i * 64), v[j]);
+            if (i < NTL) st4<1>((float*)(pp + (size_t)i * 64), v[j]);
         }
-        return;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        __shared__ int s_last;
+        if (threadIdx.x == 0) {
+            int* cn = a.cnt + ng * a.MG + mg;
+            const int before = __hip_atomic_fetch_add(cn, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = before == a.P - 1;
+            if (s_last) __hip_atomic_store(cn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+        }
+        __syncthreads();
+        if (!s_last) return;
+        // splits added in order 0..P-1 (as the reduce kernel does), this
+        // split's own tiles from registers (the same values it stored)
+        const f32x4* gp = (const f32x4*)a.part + (size_t)(ng * a.MG + mg) * a.P * NTL * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int i = wave + 4 * j;
+            if (i >= NTL) continue;
+            f32x4 s = ks == 0 ? v[j] : gp[(size_t)i * 64];
+            for (int q = 1; q < a.P; ++q) s += q == ks ? v[j] : gp[(size_t)q * NTL * 64 + (size_t)i * 64];
+            v[j] = s;
+        }
     }
     int ti[OWN];
 #pragma unroll
@@ -1410,7 +1443,7 @@ static hipError_t gemm_w8(const GemmArgs& a, int MTG, int grid, hipStream_t st) 
 #define FD_G(MT)                                                                                             \
     case MT:                                                                                                 \
         hipLaunchKernelGGL((gemm_kernel<1, NG, MT, gemm_stages(NG, MT, 1, 1), 1, 1>), dim3(grid), dim3(256), 0, st, a); \
-        if (a.P > 1 && a.epi != EPI_PLANES)                                                                \
+        if (a.P > 1 && a.epi != EPI_PLANES && !a.cnt)                                                                \
             hipLaunchKernelGGL((gemm_reduce_kernel<1, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a);   \
         break;
         FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
@@ -1429,7 +1462,7 @@ static hipError_t gemm_ng(const GemmArgs& a, int MTG, int grid, hipStream_t st) 
             hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_stages(NG, MT, WT), WT>), dim3(grid), dim3(256), 0, st, a); \
         else                                                                                           \
             hipLaunchKernelGGL((gemm_kernel<WT, NG, MT, gemm_stages(NG, MT), 0>), dim3(grid), dim3(256), 0, st, a); \
-        if (a.P > 1 && a.epi != EPI_PLANES)                                                          \
+        if (a.P > 1 && a.epi != EPI_PLANES && !a.cnt)                                                          \
             hipLaunchKernelGGL((gemm_reduce_kernel<WT, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
         break;
         FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
@@ -1448,7 +1481,7 @@ static hipError_t gemm_ng4(const GemmArgs& a, int MTG, int grid, hipStream_t st)
             hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_stages(4, MT, WT), WT>), dim3(grid), dim3(256), 0, st, a); \
         else                                                                                           \
             hipLaunchKernelGGL((gemm_kernel<WT, 4, MT, gemm_stages(4, MT), 0>), dim3(grid), dim3(256), 0, st, a); \
-        if (a.P > 1 && a.epi != EPI_PLANES)                                                          \
+        if (a.P > 1 && a.epi != EPI_PLANES && !a.cnt)                                                          \
             hipLaunchKernelGGL((gemm_reduce_kernel<WT, 4, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
         break;
         FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5) FD_G(6) FD_G(7) FD_G(8)
