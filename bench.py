@@ -421,7 +421,7 @@ def summarize_mfma(csv_path, workload, cmd):
         per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
     agg = {}
     for (name, _), c in per.items():
-        if not name.startswith("void fd::gemm_kernel"):
+        if not name.startswith(("void fd::gemm_kernel", "void fd::gemm_ns_kernel")):
             continue
         a = agg.setdefault(name, {"n": 0, "busy": 0.0, "active": 0.0, "mops": 0.0})
         a["n"] += 1

@@ -45,6 +45,7 @@ struct GemmArgs {
     // EPI_F32 / EPI_PLANES
     float* y;              // [Sp][ld] (EPI_PLANES: [P][Sp][ld])
     const float* wscale;   // FP8 weights: [NB*16] output-row scales (the tiles hold codes of w / scale)
+    int kh;                // row-split variant: k-halves per workgroup (1 or 2; 0 = 1)
 };
 
 struct AttnArgs {

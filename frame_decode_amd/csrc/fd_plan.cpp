@@ -101,25 +101,29 @@ int tune_value(const char* key, int dflt) {
     return dflt;
 }
 
-GemmShape tuned(GemmShape g, const char* name) {
+GemmShape tuned(GemmShape g, const char* name, bool ns) {
     std::string n(name);
     int NG = tune_value((n + ".NG").c_str(), g.R);
     int P = tune_value((n + ".P").c_str(), g.P);
-    if (!(NG == 4 || (NG == 6 && g.MTG <= 5))) NG = g.R;
+    if (!(NG == 4 || (NG == 6 && g.MTG <= 5) || (ns && ns_blocks_ok(NG, g.MTG)))) NG = g.R;
     GemmShape base = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, 1);
     if (!valid_split(base, P)) P = valid_split(base, g.P) ? g.P : 1;
     GemmShape out = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, P);
-    out.fused = P > 1 && tune_value((n + ".fused").c_str(), tune_value("fused", 0)) != 0;
+    if (ns_blocks_ok(NG, out.MTG)) {
+        const int kh = tune_value((n + ".KH").c_str(), g.kh);
+        out.kh = kh == 2 && (out.KB / P) % 2 == 0 ? 2 : 1;
+    }
+    out.fused = P > 1 && NG <= 6 && tune_value((n + ".fused").c_str(), tune_value("fused", 0)) != 0;
     return out;
 }
 
 void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8, bool w8,
-                uint64_t& off) {
+                uint64_t& off, bool ns) {
     sp.dims = dims;
-    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256), "qkv");
-    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256), "o");
-    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256), "gu");
-    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256), "down");
+    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256), "qkv", ns);
+    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256), "o", ns);
+    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256), "gu", ns);
+    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256), "down", ns);
     sp.layers.resize(dims.L);
     auto tiles = [w8](const GemmShape& g) { return packed_matrix_bytes(g, w8); };
     for (int l = 0; l < dims.L; ++l) {
@@ -246,14 +250,17 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
 
     uint64_t off = 0;
     StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};
-    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, off);
+    // the row-split projection variant: bf16 weights with two-part
+    // activations, launched as kernels (the persistent walk runs gemm_wg)
+    const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8;
+    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, off, ns);
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
         p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
         p.w_in = off;
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
-        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, off);
+        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, off, false);
     }
     if (p.head) {
         p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256);

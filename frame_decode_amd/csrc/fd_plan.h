@@ -15,8 +15,8 @@ namespace fd {
 constexpr int kWaves = 4;          // waves per workgroup in the GEMM and attention kernels
 constexpr int kTileBytes = 1024;   // one packed weight tile = 64 lanes x 16 bytes
 constexpr int kMaxMTG = 8;         // most 16-row tiles of sessions one GEMM workgroup holds
-constexpr int kAttnIters = 8;      // position loads per attention wave block (fp32 cache)
-constexpr int kAttnItersFp8 = 16;  // (FP8 cache)
+constexpr int kAttnIters = 4;      // position loads per attention wave block (fp32 cache)
+constexpr int kAttnItersFp8 = 8;   // (FP8 cache)
 constexpr uint64_t kAlign = 256;
 
 inline uint64_t align_up(uint64_t v, uint64_t a = kAlign) { return (v + a - 1) / a * a; }
@@ -27,7 +27,8 @@ struct GemmShape {
     int N = 0, K = 0;
     int KT = 0;        // k-width of a tile: 32 (bf16) or 16 (fp32)
     int NB = 0, KB = 0;  // tiles along N (16 rows each) and K
-    int R = 4;         // n-blocks per workgroup (4 or 6), shared by its 4 k-split waves
+    int R = 4;         // n-blocks per workgroup: 4 or 6 shared by its 4 k-split waves, or
+                       // 8, 12 or 16 split between its waves (row-split variant, bf16)
     int P = 1;         // k-splits (workgroups sharing one n-group)
     int MG = 1;        // m-groups
     int MTG = 1;       // 16-row m-tiles per m-group
@@ -36,6 +37,7 @@ struct GemmShape {
     uint64_t part_floats = 0;  // partial-sum floats needed when P > 1 (n_groups*MG*P*R*MTG*256)
     int counters = 0;
     bool fused = false;  // P > 1: the last workgroup of an n-group adds the partials (no reduce launch)
+    int kh = 1;          // row-split variant: k-halves per workgroup (2: two waves per SIMD)
     int grid() const { return n_groups * P * MG; }
 };
 
@@ -148,5 +150,9 @@ inline uint64_t packed_matrix_bytes(const GemmShape& g, bool w8) {
 
 // Tile choice for one projection (exposed for tests).
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu);
+
+// Row-split projection variant (bf16 weights, two-part activations): 8, 12
+// or 16 blocks per workgroup (2, 3 or 4 per wave), at most 5 m-tiles.
+inline bool ns_blocks_ok(int NG, int MTG) { return (NG == 8 || NG == 12 || NG == 16) && MTG <= 5; }
 
 }  // namespace fd

@@ -36,6 +36,24 @@ void fdh_gemm_shape(int N, int K, int wt, int MT, int32_t* out) {
     out[6] = g.n_groups; out[7] = g.grid(); out[8] = g.KT;
 }
 
+// Tiling of the main stack's projections as the plan of cfg chose it
+// (FD_TUNE applies): out[4*i + 0..3] = R, P, k-halves, grid for i = QKV, O,
+// gate/up, down.
+fd_status fdh_stack_shapes(const fd_config* cfg, int32_t* out) {
+    if (!cfg || !out) return FD_E_INVAL;
+    fd::Plan p;
+    fd_status st = fd::make_plan(*cfg, &p, &g_err);
+    if (st != FD_OK) return st;
+    const fd::GemmShape* g[4] = {&p.main.qkv, &p.main.o, &p.main.gu, &p.main.down};
+    for (int i = 0; i < 4; ++i) {
+        out[4 * i + 0] = g[i]->R;
+        out[4 * i + 1] = g[i]->P;
+        out[4 * i + 2] = g[i]->kh;
+        out[4 * i + 3] = g[i]->grid();
+    }
+    return FD_OK;
+}
+
 void* fdh_pool_new(int n_slots, int max_context, int rolling) {
     return new (std::nothrow) fd::SlotPool(n_slots, max_context, rolling != 0);
 }

@@ -749,6 +749,197 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Skinny projection, row-split variant (bf16 weights, bf16 activations in
+// two parts).  A workgroup has 4*KH waves: wave w owns weight blocks
+// (w % 4)*NGW .. +NGW-1 of the workgroup's 4*NGW (its "row group") and, of
+// every KH consecutive k-tiles, the (w / 4)-th (its "k-half").  Each step
+// covers KH k-tiles; their activation fragments (hi and lo parts of the MTG
+// m-tiles) are fetched once per workgroup, each wave loading a share, and
+// pass through a double-buffered LDS slot, so a wave's registers hold a
+// ring of its own weight tiles plus only its share of activation fragments.
+// One barrier per step.  With KH = 2 the workgroup runs two waves per SIMD,
+// which keeps the matrix cores issuing while one wave waits (a single wave
+// issues 16x16x32 products at about half the peak rate).  A wave adds its
+// k-tiles in order; the k-halves are added through LDS in k-half order.
+// k-split partial tiles use the layout, reduce kernel and epilogue of
+// gemm_wg (NG = 4*NGW blocks per n-group).  Requires (KB / P) % KH == 0.
+constexpr int ns_stages(int NGW, int MTG) {
+    // ring stages: the kernel is built for two waves per SIMD (at most 256
+    // registers a lane, the accumulators in ordinary VGPRs)
+    return NGW == 3 ? 4 : 2;
+}
+
+template <int NGW, int MTG, int STG, int KH>
+__global__ __launch_bounds__(256 * KH, 2) void gemm_ns_kernel(GemmArgs a) {
+    constexpr int NWV = 4 * KH;             // waves
+    constexpr int NG = 4 * NGW;             // blocks of the n-group
+    constexpr int NBX = 2 * MTG;            // activation fragments per k-tile (hi, then lo)
+    constexpr int NFX = KH * NBX;           // fragments per step
+    constexpr int XPW = (NFX + NWV - 1) / NWV;  // fragments each wave fetches per step
+    constexpr int OWN = NGW * MTG;          // output tiles of a row group
+    constexpr int NTL = NG * MTG;
+    static_assert(STG % 2 == 0 && STG >= 2, "the LDS slot of step j is j % 2 = ring slot % 2");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rw = wave & 3;                // row group
+    const int kh = wave >> 2;               // k-half
+    int bid = blockIdx.x;
+    const int ks = bid % a.P;
+    bid /= a.P;
+    const int mg = bid % a.MG;
+    const int ng = bid / a.MG;
+    const int nst = a.KB / a.P / KH;        // steps of KH k-tiles (>= 1)
+    const int kb0 = ks * (a.KB / a.P);
+    const int nb0 = ng * NG;
+    const int mt0 = mg * MTG;
+
+    __shared__ u32x4 s_x[2][NFX + 1][64];  // + a spare row for the surplus fetches
+    __shared__ float s_seg[MTG * 16 * 8];
+    __shared__ float s_rstd[MTG * 16];
+
+    const u32x4* wp[NGW];
+#pragma unroll
+    for (int r = 0; r < NGW; ++r)  // blocks past the matrix re-read the last one (never stored)
+        wp[r] = (const u32x4*)(a.W + (size_t)min(nb0 + rw * NGW + r, a.NB - 1) * a.KB * 1024) + lane;
+    // fragment q = wave + NWV*i of a step: k-tile q / NBX of the step, hi
+    // part of m-tile q % NBX (< MTG) or lo part of m-tile q % NBX - MTG;
+    // fragment (k-tile kb, m-tile mt) is 1 KiB at ((kb*MT + mt)*64 + lane)
+    // * 16 bytes.  Every wave issues XPW fetches per step (q >= NFX
+    // re-fetches fragment NFX - 1 into the spare LDS row): with no
+    // conditional loads the compiler's wait counts stay exact, so the whole
+    // ring stays in flight.
+    const size_t xk = (size_t)a.MT * 64;
+    const u32x4* xs[XPW];
+    int xdst[XPW];
+#pragma unroll
+    for (int i = 0; i < XPW; ++i) {
+        const int q = wave + NWV * i;
+        const int qc = min(q, NFX - 1);
+        const int f = qc % NBX;
+        xdst[i] = q < NFX ? q : NFX;
+        xs[i] = (f < MTG ? (const u32x4*)a.X : (const u32x4*)a.X_lo) + (size_t)(qc / NBX) * xk +
+                (size_t)(mt0 + f % MTG) * 64 + lane;
+    }
+
+    f32x4 acc[NGW][MTG];
+#pragma unroll
+    for (int r = 0; r < NGW; ++r)
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 A[STG][NGW];
+    u32x4 XR[STG][XPW];
+    auto load = [&](u32x4 (&Ad)[NGW], u32x4 (&Xd)[XPW], int j) {
+        const size_t kb = (size_t)(kb0 + KH * j);
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) Xd[i] = xs[i][kb * xk];
+#pragma unroll
+        for (int r = 0; r < NGW; ++r) Ad[r] = __builtin_nontemporal_load(&wp[r][(kb + kh) * 64]);
+    };
+    // one step: publish this wave's fragments, barrier, read the fragments
+    // of this wave's k-tile, request step jn into the ring slot consumed one
+    // step earlier, multiply
+    auto step = [&](u32x4 (&As)[NGW], u32x4 (&Xs)[XPW], int buf, u32x4 (&An)[NGW], u32x4 (&Xn)[XPW],
+                    int jn, bool more) {
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) s_x[buf][xdst[i]][lane] = Xs[i];
+        __syncthreads();
+        u32x4 B[NBX];
+#pragma unroll
+        for (int f = 0; f < NBX; ++f) B[f] = s_x[buf][kh * NBX + f][lane];
+        if (more) load(An, Xn, jn);
+        __builtin_amdgcn_sched_barrier(0);
+        // high parts of every tile first, then low parts: consecutive
+        // products never chain on one accumulator
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < NGW; ++r)
+#pragma unroll
+                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<1>(As[r], B[h * MTG + t], acc[r][t]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // the norm's partial sums first (few short loads ahead of the stream)
+    if (a.ss_in) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
+    // (a ring slot past the end re-reads the last step and is never consumed)
+#pragma unroll
+    for (int s = 0; s < STG - 1; ++s) load(A[s], XR[s], min(s, nst - 1));
+    // steady state: every request of a chunk is in range; j0 stays a
+    // multiple of STG, so step j0 + s uses ring slot s and LDS slot s % 2
+    int j0 = 0;
+    for (; j0 + 2 * STG - 2 < nst; j0 += STG) {
+#pragma unroll
+        for (int s = 0; s < STG; ++s)
+            step(A[s], XR[s], s & 1, A[(s + STG - 1) % STG], XR[(s + STG - 1) % STG], j0 + s + STG - 1, true);
+    }
+    // tail: fewer than 2*STG - 1 steps remain (the bound is uniform over the
+    // workgroup, so every wave reaches the same barriers)
+#pragma unroll
+    for (int s = 0; s < 2 * STG - 2; ++s) {
+        if (j0 + s >= nst) break;
+        step(A[s % STG], XR[s % STG], s & 1, A[(s + STG - 1) % STG], XR[(s + STG - 1) % STG],
+             j0 + s + STG - 1, j0 + s + STG - 1 < nst);
+    }
+    __syncthreads();
+    if (a.ss_in) rstd_phase2(a, MTG * 16, s_seg, s_rstd);
+    if constexpr (KH > 1) {
+        // k-halves 1.. hand their sums to k-half 0 of the same row group
+        __shared__ f32x4 s_kh[KH - 1][4][OWN][64];
+        if (kh > 0) {
+#pragma unroll
+            for (int r = 0; r < NGW; ++r)
+#pragma unroll
+                for (int t = 0; t < MTG; ++t) s_kh[kh - 1][rw][r * MTG + t][lane] = acc[r][t];
+        }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int q = 0; q < KH - 1; ++q)
+#pragma unroll
+                for (int r = 0; r < NGW; ++r)
+#pragma unroll
+                    for (int t = 0; t < MTG; ++t) acc[r][t] += s_kh[q][rw][r * MTG + t][lane];
+        }
+    }
+
+    f32x4 v[OWN];
+    int ti[OWN];
+#pragma unroll
+    for (int r = 0; r < NGW; ++r)
+#pragma unroll
+        for (int t = 0; t < MTG; ++t) {
+            v[r * MTG + t] = acc[r][t];
+            ti[r * MTG + t] = kh == 0 ? (rw * NGW + r) * MTG + t : -1;  // k-half 0 finishes the tiles
+        }
+    if (a.epi == EPI_PLANES) {
+        // each split writes its own plane; the consumer adds them
+        if (kh > 0) return;
+        float* y = a.y + (size_t)ks * a.plane;
+#pragma unroll
+        for (int r = 0; r < NGW; ++r) {
+            const int nb = nb0 + rw * NGW + r;
+            if (nb >= a.NB) continue;
+#pragma unroll
+            for (int t = 0; t < MTG; ++t)
+                st4<0>(y + (size_t)((mt0 + t) * 16 + (lane & 15)) * a.ld + nb * 16 + (lane >> 4) * 4, v[r * MTG + t]);
+        }
+        return;
+    }
+    if (a.P > 1) {
+        // partial tiles of this split, [group][split][tile][64 lanes], added
+        // by gemm_reduce_kernel<1, NG, MTG>
+        if (kh > 0) return;
+        f32x4* pp = (f32x4*)a.part + ((size_t)(ng * a.MG + mg) * a.P + ks) * NTL * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) st4<0>((float*)(pp + (size_t)ti[j] * 64), v[j]);
+        return;
+    }
+    __syncthreads();
+    gemm_finish<1, NG, MTG, NWV, OWN, 0>(a, v, ti, ng, mt0, 0, MTG, s_rstd);
+}
+
+// ---------------------------------------------------------------------------
 // decode attention over one (slot, kv head, chunk of positions).
 //
 // Lanes: a position's head vector is spread over LPP consecutive lanes,
@@ -763,12 +954,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
 // attn_combine_kernel in chunk order.  All G query heads of the kv head
 // share every load.
 
-// Position loads a wave keeps in flight per block of attention: 16 for an
-// FP8 cache, 8 for fp32 (whose wider lanes already hold twice the bytes per
-// load); the plan rounds attention chunks to whole blocks of the same size.
-// (Measured at 80 sessions x 1500 frames: 16 beats 6, 8 and 12 by 1.4-3%.)
+// Position loads per block of attention (a wave holds the keys and the
+// values of one block, two blocks' worth of loads in flight at a time): 8
+// for an FP8 cache, 4 for fp32 (whose wider lanes already hold twice the
+// bytes per load); the plan rounds attention chunks to whole blocks of the
+// same size.
 template <int FP8>
-constexpr int attn_nit() { return FP8 ? 16 : 8; }
+constexpr int attn_nit() { return FP8 ? 8 : 4; }
 template <int FP8>
 constexpr int walk_attn_nit() { return attn_nit<FP8>(); }
 
@@ -852,25 +1044,38 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     const bool own_new = chunk == nch - 1;
     const int t1 = min(t0 + a.tc, n);  // cache positions [t0, t1) this chunk streams, except `hole`
 
-    // the wave's first block of keys does not depend on q: start it now
-    u32x4 raw[NIT][J];
-    auto load_blk = [&](const uint8_t* src, int base) {
+    // Keys and values of a block go to two register buffers: the keys of
+    // block b+1 stream while the values of block b are consumed and the
+    // values of b+1 while the keys of b+1 are, so a wave always has a block
+    // of loads in flight.  Every load is unconditional (positions past the
+    // chunk re-read its last position), which keeps the compiler's wait
+    // counts exact; positions not attended (past the chunk, the new entry's
+    // slot) are masked where the data is used.  The wave's first block does
+    // not depend on q: it starts before the prologue.
+    u32x4 rk[NIT][J], rv[NIT][J];
+    auto load_blk = [&](u32x4 (&dst)[NIT][J], const uint8_t* src, int base) {
         const int tw = base + jj;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int t = tw + it * PPL;
+            const int t = min(tw + it * PPL, t1 - 1);
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                raw[it][j] = t < t1 && t != hole
-                                 ? __builtin_nontemporal_load((const u32x4*)(src + (size_t)t * a.pos_stride + (c + LPP * j) * 16))
-                                 : u32x4{0u, 0u, 0u, 0u};
+                dst[it][j] = __builtin_nontemporal_load((const u32x4*)(src + (size_t)t * a.pos_stride + (c + LPP * j) * 16));
         }
+        // keep the loads here: the compiler would otherwise sink them
+        // towards their first use, one block later, and the blocks would not
+        // overlap
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
     int base = t0 + wave * SUB;
     if constexpr (CO) {
         // persistent walk: cached keys were written by earlier launches or
         // earlier phases, so the first block streams during the barrier wait
-        if (base < t1) load_blk(kbase, base);
+        if (base < t1) {
+            load_blk(rk, kbase, base);
+            load_blk(rv, vbase, base);
+        }
         wait();
     }
 
@@ -958,7 +1163,10 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
 #pragma unroll
             for (int i = 0; i < VE; ++i) qv[h][j * VE + i] = s_q[h][(c + LPP * j) * VE + i];
 
-    if (!CO && base < t1) load_blk(kbase, base);
+    if (!CO && base < t1) {
+        load_blk(rk, kbase, base);
+        load_blk(rv, vbase, base);
+    }
     float mrun[G], lrun[G], acc[G][E];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -975,7 +1183,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
         for (int it = 0; it < NIT; ++it) {
             float kvf[E];
 #pragma unroll
-            for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], kvf + j * VE);
+            for (int j = 0; j < J; ++j) unpack16<FP8>(rk[it][j], kvf + j * VE);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float dsum = 0.f;
@@ -986,8 +1194,9 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
                 sc[it][h] = t < t1 && t != hole ? dsum : -INFINITY;
             }
         }
-        // values of this block: issue the loads before the softmax update
-        load_blk(vbase, base);
+        // keys of the next block (a block past the chunk re-reads its last
+        // position and is never used)
+        load_blk(rk, kbase, base + 4 * SUB);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float m = sc[0][h];
@@ -1013,15 +1222,19 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
+            // a position not attended contributes nothing, whatever its bytes
+            // hold (a stale entry or a NaN fill would survive a zero weight)
+            const int t = tw + it * PPL;
+            const bool use = t < t1 && t != hole;
             float vf[E];
 #pragma unroll
-            for (int j = 0; j < J; ++j) unpack16<FP8>(raw[it][j], vf + j * VE);
+            for (int j = 0; j < J; ++j) unpack16<FP8>(use ? rv[it][j] : u32x4{0u, 0u, 0u, 0u}, vf + j * VE);
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[h][e] += sc[it][h] * vf[e];
         }
-        if (base + 4 * SUB < t1) load_blk(kbase, base + 4 * SUB);
+        load_blk(rv, vbase, base + 4 * SUB);
     }
     // reduce over the wave's position groups (lanes with equal c)
 #pragma unroll
@@ -1491,8 +1704,37 @@ static hipError_t gemm_ng4(const GemmArgs& a, int MTG, int grid, hipStream_t st)
     return hipGetLastError();
 }
 
+// Row-split variant (bf16 weights, two-part activations, reduce launch for
+// k-splits): NGW blocks per row group, 4*NGW per workgroup, a.kh k-halves
+template <int NGW, int KH>
+static hipError_t gemm_ns_kh(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    if (!a.X_lo || a.cnt || a.P < 1 || a.KB % a.P || (a.KB / a.P) % KH) return hipErrorInvalidValue;
+    switch (MTG) {
+#define FD_G(MT)                                                                                          \
+    case MT:                                                                                              \
+        hipLaunchKernelGGL((gemm_ns_kernel<NGW, MT, ns_stages(NGW, MT), KH>), dim3(grid), dim3(256 * KH), 0, st, a); \
+        if (a.P > 1 && a.epi != EPI_PLANES)                                                               \
+            hipLaunchKernelGGL((gemm_reduce_kernel<1, 4 * NGW, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
+        break;
+        FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
+#undef FD_G
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int NGW>
+static hipError_t gemm_ns(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    if (a.kh == 2) return gemm_ns_kh<NGW, 2>(a, MTG, grid, st);
+    if (a.kh <= 1) return gemm_ns_kh<NGW, 1>(a, MTG, grid, st);
+    return hipErrorInvalidValue;
+}
+
 // wt: 0 fp32, 1 bf16, 2 FP8 weights with bf16 activations
 hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hipStream_t st) {
+    if (wt == 1 && NG == 8) return gemm_ns<2>(a, MTG, grid, st);
+    if (wt == 1 && NG == 12) return gemm_ns<3>(a, MTG, grid, st);
+    if (wt == 1 && NG == 16) return gemm_ns<4>(a, MTG, grid, st);
     if (wt == 2) return NG == 6 ? gemm_w8<6>(a, MTG, grid, st) : (NG == 4 ? gemm_w8<4>(a, MTG, grid, st) : hipErrorInvalidValue);
     if (NG == 6) return wt ? gemm_ng<1, 6>(a, MTG, grid, st) : gemm_ng<0, 6>(a, MTG, grid, st);
     if (NG == 4) return wt ? gemm_ng4<1>(a, MTG, grid, st) : gemm_ng4<0>(a, MTG, grid, st);

@@ -182,9 +182,35 @@ def test_bf16_fp8_ragged_multichunk(exec_mode):
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 1, 255, 256, 257, 300, 511, 690]
     # this window is short enough for one chunk by default: ask the plan
-    # for three (it rounds chunks to whole 512-position blocks: two chunks)
-    # so the chunk merge is exercised
+    # for three (it rounds chunks to whole 256-position blocks: three
+    # chunks) so the chunk merge is exercised
     os.environ["FD_TUNE"] = "attn.chunks=3"
+    try:
+        ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
+    finally:
+        del os.environ["FD_TUNE"]
+    _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
+
+
+# every path of the row-split projection variant: k-split planes (QKV),
+# its own epilogue without k-splits (O with one k-half, down with two and a
+# ragged last n-group: residual, next norm input), k-split partials through
+# the reduce kernel with the gate/up epilogue
+ROW_SPLIT_TUNE = ("qkv.NG=12,qkv.P=2,qkv.KH=2,o.NG=8,o.P=1,o.KH=1,gu.NG=16,gu.P=2,gu.KH=2,"
+                  "down.NG=12,down.P=1,down.KH=2")
+
+
+@pytest.mark.parametrize("max_slots", [9, 40])
+def test_row_split_projections(max_slots):
+    """The row-split projection variant (its waves own different weight
+    rows and share the activations through LDS; one or two k-halves) on
+    every projection of a reduced 7B-geometry bf16/FP8 stack, with one and
+    with three 16-row tiles of sessions: 2e-2, cache indexing bit-exact."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                              d_ffn=1536, max_slots=max_slots, max_context=300)
+    model = synth.Model(cfg, gain_noise=True)
+    start = [(37 * i) % 290 for i in range(max_slots - 2)]
+    os.environ["FD_TUNE"] = ROW_SPLIT_TUNE
     try:
         ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
     finally:

@@ -45,6 +45,7 @@ def host():
     h.fdh_last_error.restype = ctypes.c_char_p
     h.fdh_gemm_shape.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_int32)]
+    h.fdh_stack_shapes.argtypes = [ctypes.POINTER(FdConfig), ctypes.POINTER(ctypes.c_int32)]
     return h
 
 
@@ -160,6 +161,42 @@ def test_gemm_tiling_covers_the_projection(host):
         assert NB * 16 == N and KB * KT == K
         assert ng * R >= NB and R in (4, 6) and MG * MTG >= MT and MTG <= 8
         assert 1 <= P <= KB and grid == ng * P * MG
+
+
+def _stack_shapes(host, cfg):
+    out = (ctypes.c_int32 * 16)()
+    st = host.fdh_stack_shapes(ctypes.byref(config_from_dict(cfg)), out)
+    assert st == FD_OK, host.fdh_last_error()
+    v = list(out)
+    return {n: tuple(v[4 * i:4 * i + 4]) for i, n in enumerate(("qkv", "o", "gu", "down"))}
+
+
+def test_row_split_projection_plan(host, monkeypatch):
+    """By default every projection takes the k-split variant (4 or 6 blocks
+    per workgroup); a tuning override selects the row-split variant (bf16
+    kernel sequence only: not the persistent walk, FP8 weights or fp32
+    stacks), with two k-halves only where each split's k-tiles divide
+    evenly."""
+    monkeypatch.delenv("FD_TUNE", raising=False)
+    cfg = synth.get_config("7b_s80_p1499")
+    sh = _stack_shapes(host, cfg)
+    assert all(sh[n][0] in (4, 6) and sh[n][2] == 1 for n in sh)
+    assert sh["gu"] == (6, 1, 1, 235)  # 1408 blocks in groups of 6, no k-split
+    row_split = "gu.NG=12,gu.P=2,gu.KH=2"
+    monkeypatch.setenv("FD_TUNE", row_split)
+    assert _stack_shapes(host, cfg)["gu"] == (12, 2, 2, 236)  # 118 n-groups x 2 k-splits
+    assert _stack_shapes(host, dict(cfg, exec_mode=1))["gu"][0] in (4, 6)
+    assert _stack_shapes(host, dict(cfg, w_dtype="fp8"))["gu"][0] in (4, 6)
+    assert _stack_shapes(host, dict(synth.get_config("talker_s56"), exec_mode=0))["gu"][0] in (4, 6)
+    monkeypatch.setenv("FD_TUNE", "qkv.NG=12,qkv.P=4,qkv.KH=2,o.NG=8,o.P=8,down.NG=16,down.P=11,down.KH=2")
+    sh = _stack_shapes(host, cfg)
+    assert sh["qkv"] == (12, 4, 2, 256)
+    assert sh["o"] == (8, 8, 1, 256)
+    assert sh["down"] == (16, 11, 2, 176)  # 352 k-tiles / 11 splits = 32 per split
+    monkeypatch.setenv("FD_TUNE", "down.NG=12,down.P=32,down.KH=2,o.NG=12,o.P=32,o.KH=2")
+    sh = _stack_shapes(host, cfg)
+    assert sh["down"] == (12, 32, 1, 704)  # 11 k-tiles per split: no even halves
+    assert sh["o"] == (12, 32, 2, 704)  # 4 k-tiles per split: two steps of two
 
 
 class Pool:
