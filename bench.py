@@ -324,17 +324,20 @@ def cpu_baseline(cfg, pos, layers, sessions):
     x = np.stack([synth.frame_input(small, s, pos) for s in range(sessions)])
     for l in range(layers):
         model.layer(l)
+    # repeat the step (same frame, same inputs) until about 10 s of CPU
+    # work has been timed; report the median step
     times = []
-    for _ in range(2):
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 200):
         t = time.perf_counter()
         orc.step(list(range(sessions)), x, [pos] * sessions)
         times.append(time.perf_counter() - t)
-    t = min(times)
+    t = float(np.median(times))
     full_step = t * cfg["n_layers"] / layers
     return {"value": sessions / full_step, "unit": "session-frames/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{sessions} sessions at frame {pos}, {layers} of {cfg['n_layers']} layers, "
-                      f"best of 2 steps ({t:.2f} s), scaled by {cfg['n_layers']}/{layers} layers"}
+                      f"median of {len(times)} steps ({t:.2f} s each, {sum(times):.1f} s timed), "
+                      f"scaled by {cfg['n_layers']}/{layers} layers"}
 
 
 COPY_BYTES = 1 << 30
