@@ -115,11 +115,22 @@ def _check_new_codes(ctx, orc, cfg, slots, pos):
         check(same > 0.8 and bad <= 1.0, f"slot {s}: appended codes differ from the oracle's")
 
 
-@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
-def test_7b_eight_sessions_at_position_256(model7b, exec_mode):
+# every projection on the row-split variant, at full 7B shapes: k-split
+# planes (QKV), its own residual epilogue (O, no k-split), k-split partials
+# with the gate/up and residual epilogues, two k-halves
+ROW_SPLIT_7B = ("qkv.NG=12,qkv.P=2,qkv.KH=2,o.NG=8,o.P=1,gu.NG=12,gu.P=2,gu.KH=2,"
+                "down.NG=12,down.P=11,down.KH=2")
+
+
+@pytest.mark.parametrize("exec_mode,tune", [(0, None), (1, None), (0, ROW_SPLIT_7B)],
+                         ids=["kernels", "walk", "row_split"])
+def test_7b_eight_sessions_at_position_256(model7b, exec_mode, tune, monkeypatch):
     """The 8-session workload in full: 32 layers, every session's cache
     prefilled to 256 positions, new frame at index 256; every row checked
-    (kernel sequence and persistent walk)."""
+    (kernel sequence, persistent walk, and the kernel sequence with every
+    projection on the row-split variant)."""
+    if tune:
+        monkeypatch.setenv("FD_TUNE", tune)
     cfg = synth.get_config("7b_s8_p256")
     cfg["exec_mode"] = exec_mode
     p0 = cfg["position"]
