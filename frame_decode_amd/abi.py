@@ -71,11 +71,13 @@ class FdKvView(ctypes.Structure):
                 ("max_slots", c_i32), ("kv_scale", c_p), ("slot_active", c_p), ("slot_pos", c_p)]
 
 
-EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_step_tokens", "fd_free", "fd_destroy",
+EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_step_tokens", "fd_step_static",
+           "fd_free", "fd_destroy",
            "fd_kv_layout", "fd_set_position", "fd_slot_state", "fd_kv_write", "fd_sync",
            "fd_profile", "fd_profile_read", "fd_read_probe", "fd_last_error", "fd_status_str"]
 
 FD_N_KINDS = 10
+FD_STATIC_SCRATCH_BYTES = 64 << 20
 KIND_NAMES = ["embed", "qkv", "attention", "o_proj", "gate_up", "down", "final", "depth_in",
               "walk", "head"]
 
@@ -104,6 +106,7 @@ def _proto(lib):
     lib.fd_alloc_slots.argtypes = [c_p, c_i32, P(c_i32)]
     lib.fd_step.argtypes = [c_p, c_p, c_p, c_p, c_p]
     lib.fd_step_tokens.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p]
+    lib.fd_step_static.argtypes = [c_p, c_p, c_p, c_p, c_p]
     lib.fd_free.argtypes = [c_p, P(c_i32), c_i32]
     lib.fd_destroy.argtypes = [c_p]
     lib.fd_kv_layout.argtypes = [c_p, P(FdKvView)]

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfd.so")
 HOST_LIB = os.path.join(HERE, "libfd_host.so")
 
-HIP_SOURCES = ["kernels.hip", "fd_api.cpp", "fd_plan.cpp"]
+HIP_SOURCES = ["kernels.hip", "fd_static.hip", "fd_api.cpp", "fd_plan.cpp"]
 HOST_SOURCES = ["host_shim.cpp", "fd_plan.cpp"]
 
 # Packed fp32 VALU instructions are disabled for the device code (the

@@ -114,6 +114,13 @@ class Context:
                               ctypes.c_void_p(_ptr(depth_out)),
                               ctypes.c_void_p(_stream_handle(stream))), self._ctx)
 
+    def fd_step_static(self, x_in, y_out, depth_out=None, stream=None) -> None:
+        """fd_step with the library's static device scratch as the workspace
+        (allocates nothing; calls on one GPU must not overlap)."""
+        _check(_lib().fd_step_static(self._ctx, ctypes.c_void_p(_ptr(x_in)), ctypes.c_void_p(_ptr(y_out)),
+                                     ctypes.c_void_p(_ptr(depth_out)),
+                                     ctypes.c_void_p(_stream_handle(stream))), self._ctx)
+
     def fd_step_tokens(self, x_in, y_out, tokens_out, logits_out=None, depth_out=None, stream=None) -> None:
         """fd_step plus the output head: tokens_out int32 [max_slots], optional
         logits_out fp32 [max_slots][vocab] (device tensors)."""

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/fd.h"
+#include "fd_internal.h"
 #include "fd_kernels.h"
 #include "fd_plan.h"
 #include "slot_pool.h"
@@ -26,6 +27,10 @@ struct fd_ctx {
     fd::Plan plan;
     fd::SlotPool slots;
     fd_buffers buf{};
+    // workspace the step's kernels use: buf.workspace, or the library's
+    // static scratch during fd_step_static
+    uint8_t* ws = nullptr;
+    bool no_timing = false;  // fd_step_static: never create events
     int device = 0;
     std::string err;
     int32_t* pinned[kRing] = {};
@@ -64,7 +69,7 @@ fd_status hip_fail(fd_ctx* c, hipError_t e, const char* where) {
 bool aligned(const void* p) { return p && ((uintptr_t)p % fd::kAlign) == 0; }
 
 uint8_t* P(const fd_ctx* c, uint64_t off) { return (uint8_t*)c->buf.packed_weights + off; }
-uint8_t* Wk(const fd_ctx* c, uint64_t off) { return (uint8_t*)c->buf.workspace + off; }
+uint8_t* Wk(const fd_ctx* c, uint64_t off) { return c->ws + off; }
 
 // FP8 weights: the per-row scales stored after a matrix's tiles (else null)
 const float* wscale(const fd_ctx* c, uint64_t off, const fd::GemmShape& g) {
@@ -177,7 +182,7 @@ hipEvent_t take_event(fd_ctx* c) {
 // Runs `launch` on stream st; with timing on, brackets it with events.
 template <class F>
 hipError_t timed(fd_ctx* c, int kind, hipStream_t st, F&& launch) {
-    if (!c->prof) return launch();
+    if (!c->prof || c->no_timing) return launch();
     hipEvent_t a = take_event(c), b = take_event(c);
     if (!a || !b) return hipErrorOutOfMemory;
     hipError_t e = hipEventRecord(a, st);
@@ -677,6 +682,7 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
     fd_ctx* c = new (std::nothrow) fd_ctx(p);
     if (!c) return fail(nullptr, FD_E_DEVICE, "out of host memory");
     c->buf = *buf;
+    c->ws = (uint8_t*)buf->workspace;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipGetDevice(&c->device);
     for (int i = 0; i < kRing && e == hipSuccess; ++i) {
@@ -752,11 +758,14 @@ fd_status fd_slot_state(fd_ctx* c, int32_t slot, int32_t* active, int32_t* pos) 
     return FD_OK;
 }
 
-fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, void* stream) {
-    if (!c) return FD_E_INVAL;
-    if (!x_in || !y_out) return fail(c, FD_E_INVAL, "null x_in or y_out");
+}  // extern "C"
+
+namespace {
+
+// The step of fd_step on the workspace c->ws (argument checks done by the
+// callers).
+fd_status step_impl(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, void* stream) {
     const fd::Plan& pl = c->plan;
-    if (pl.depth && !depth_out) return fail(c, FD_E_INVAL, "profile has a depth stack: depth_out required");
     int full = -1;
     if (c->slots.any_full(&full))
         return fail(c, FD_E_CTXFULL, "slot " + std::to_string(full) + " has a full window");
@@ -874,6 +883,69 @@ fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, voi
     if (e != hipSuccess) return hip_fail(c, e, "fd_step launch");
     c->slots.advance();
     return FD_OK;
+}
+
+// Checks shared by fd_step and fd_step_static.
+fd_status step_args(fd_ctx* c, const void* x_in, void* y_out, void* depth_out) {
+    if (!x_in || !y_out) return fail(c, FD_E_INVAL, "null x_in or y_out");
+    if (c->plan.depth && !depth_out) return fail(c, FD_E_INVAL, "profile has a depth stack: depth_out required");
+    return FD_OK;
+}
+
+}  // namespace
+
+namespace fd {
+
+int ctx_device(const fd_ctx* c) { return c->device; }
+
+// fd_step on a workspace other than the ctx's own (the library's static
+// scratch): every split-counter region is cleared first, since the
+// scratch holds whatever the last call on this GPU left there.
+fd_status step_on_workspace(fd_ctx* c, void* ws, uint64_t ws_bytes, const void* x_in, void* y_out,
+                            void* depth_out, void* stream) {
+    if (!c) return FD_E_INVAL;
+    fd_status st = step_args(c, x_in, y_out, depth_out);
+    if (st != FD_OK) return st;
+    const Plan& pl = c->plan;
+    if (pl.walk)
+        return fail(c, FD_E_UNSUPPORTED, "fd_step_static: FD_EXEC_WALK profiles keep their phase layout in the fd_init workspace");
+    if (pl.workspace_bytes > ws_bytes)
+        return fail(c, FD_E_UNSUPPORTED, "fd_step_static: the profile needs " + std::to_string(pl.workspace_bytes) +
+                                             " bytes of workspace, the static scratch holds " + std::to_string(ws_bytes));
+    if (!ws || ((uintptr_t)ws % kAlign)) return fail(c, FD_E_INVAL, "fd_step_static: scratch not 256-byte aligned");
+    int full = -1;
+    if (c->slots.any_full(&full))
+        return fail(c, FD_E_CTXFULL, "slot " + std::to_string(full) + " has a full window");
+    hipStream_t s = (hipStream_t)stream;
+    const StackPlan* stacks[2] = {&pl.main, pl.depth ? &pl.dstack : nullptr};
+    bool fused = false;
+    for (const StackPlan* sp : stacks)
+        if (sp) fused = fused || sp->o.fused || sp->gu.fused || sp->down.fused;
+    uint8_t* saved = c->ws;
+    c->ws = (uint8_t*)ws;
+    c->no_timing = true;
+    hipError_t e = hipSuccess;
+    if (fused) {  // arrival counters of the in-kernel k-split reduction start at zero
+        uint64_t cnt = 1;
+        for (const StackPlan* sp : stacks)
+            if (sp) for (const GemmShape* g : {&sp->o, &sp->gu, &sp->down}) cnt = std::max<uint64_t>(cnt, g->counters);
+        e = launch_fill_u32((uint32_t*)Wk(c, pl.ws_cnt), 0u, cnt, s);
+    }
+    st = e == hipSuccess ? step_impl(c, x_in, y_out, depth_out, stream) : hip_fail(c, e, "fd_step_static");
+    c->ws = saved;
+    c->no_timing = false;
+    return st;
+}
+
+}  // namespace fd
+
+extern "C" {
+
+fd_status fd_step(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, void* stream) {
+    if (!c) return FD_E_INVAL;
+    fd_status st = step_args(c, x_in, y_out, depth_out);
+    if (st != FD_OK) return st;
+    return step_impl(c, x_in, y_out, depth_out, stream);
 }
 
 fd_status fd_step_tokens(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, int32_t* tokens_out,

@@ -190,6 +190,8 @@ hipError_t launch_final(const FinalArgs& a, int wt, int rows, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st);
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t st);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
+// Sets n 32-bit words at p to v (a kernel, so it can sit inside a captured graph).
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, uint64_t n, hipStream_t st);
 // Persistent walk: walk_grid() is the co-resident grid of the shape's
 // compiled kernel (0 if the shape has none); launch_walk() zeroes the
 // barrier state and launches.

@@ -1605,6 +1605,18 @@ __global__ void walk_reset_kernel(unsigned* bar, int* abort_flag) {
     }
 }
 
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, uint32_t v, uint64_t n) {
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, uint64_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const uint64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, p, v, n);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // HBM read probe: streams a buffer once with wide loads (8 independent 16-byte
 // loads in flight per lane), folding the words so the loads stay live.

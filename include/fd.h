@@ -279,6 +279,32 @@ fd_status fd_step_tokens(fd_ctx* ctx, const void* x_in, void* y_out, void* depth
                          int32_t* tokens_out, float* logits_out, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): fd_step
+ * with the library's own static device scratch as the step's workspace.
+ * The scratch is a file-scope device array of FD_STATIC_SCRATCH_BYTES bytes
+ * (64 MiB) that every GPU the library runs on holds until the process ends;
+ * the step's activations, projection planes, k-split partial sums, norm
+ * partial sums, attention chunk partials and the depth stack's per-frame
+ * cache live there instead of in the fd_init workspace.  Arguments, outputs
+ * and effects on the cache and positions are those of fd_step; x_in, y_out
+ * and depth_out are still the caller's.  Allocates nothing: no hipMalloc,
+ * hipFree, event creation or other allocating call (the ctx's fd_profile
+ * timing is skipped for this call).  The current device must be the ctx's
+ * (FD_E_INVAL otherwise); its first call on a GPU resolves that GPU's copy
+ * of the array.
+ * FD_E_UNSUPPORTED (no launch) for FD_EXEC_WALK profiles, whose phase
+ * layout is built into the fd_init workspace, and for profiles whose step
+ * workspace (fd_sizes.workspace) exceeds FD_STATIC_SCRATCH_BYTES.
+ * All calls on one GPU share that GPU's array and keep the last call's
+ * contents: calls that overlap on one GPU (several ctxs or streams, or
+ * several host threads) race and give undefined results -- serialize them.
+ * Counters that must start at zero are cleared by each call.
+ */
+#define FD_STATIC_SCRATCH_BYTES (64ull << 20)
+fd_status fd_step_static(fd_ctx* ctx, const void* x_in, void* y_out, void* depth_out, void* stream);
+
+/*
  * Ends sessions: marks the n slots (host array) free.  FD_E_BADSLOT and no
  * change if any id is out of range, not allocated, or repeated.
  */
