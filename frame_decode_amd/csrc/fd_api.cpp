@@ -699,7 +699,7 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
         }
         for (float v : sig)
             if (e == hipSuccess && !(v > 0.0f && std::isfinite(v))) {
-                delete c;
+                fd_destroy(c);
                 return fail(nullptr, FD_E_INVAL, "kv_scale entries must be finite and > 0");
             }
     }
@@ -886,9 +886,18 @@ fd_status step_impl(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, v
 }
 
 // Checks shared by fd_step and fd_step_static.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 fd_status step_args(fd_ctx* c, const void* x_in, void* y_out, void* depth_out) {
     if (!x_in || !y_out) return fail(c, FD_E_INVAL, "null x_in or y_out");
     if (c->plan.depth && !depth_out) return fail(c, FD_E_INVAL, "profile has a depth stack: depth_out required");
+    // the kernels move rows in 8- and 16-byte vectors
+    if (!aligned16(x_in) || !aligned16(y_out) || (depth_out && !aligned16(depth_out)))
+        return fail(c, FD_E_INVAL, "x_in, y_out and depth_out must be 16-byte aligned");
+    int s = -1;
+    if (c->slots.any_stale(&s))
+        return fail(c, FD_E_STATE, "slot " + std::to_string(s) +
+                                       " is stale after a step that stopped early: fd_set_position or fd_free it");
     return FD_OK;
 }
 
@@ -954,6 +963,8 @@ fd_status fd_step_tokens(fd_ctx* c, const void* x_in, void* y_out, void* depth_o
     const fd::Plan& pl = c->plan;
     if (!pl.head) return fail(c, FD_E_INVAL, "profile has no output head (vocab 0)");
     if (!tokens_out) return fail(c, FD_E_INVAL, "null tokens_out");
+    if (((uintptr_t)tokens_out & 3) || (logits_out && !aligned16(logits_out)))
+        return fail(c, FD_E_INVAL, "tokens_out must be 4-byte and logits_out 16-byte aligned");
     fd_status st = fd_step(c, x_in, y_out, depth_out, stream);
     if (st != FD_OK) return st;
     hipStream_t s = (hipStream_t)stream;
@@ -1075,7 +1086,10 @@ fd_status fd_sync(fd_ctx* c, void* stream) {
         e = hipMemcpy(&flag, c->walk.abort_flag, sizeof(int), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return hip_fail(c, e, "fd_sync");
         c->walk_launched = false;
-        if (flag) return fail(c, FD_E_DEVICE, "walk: a grid barrier wait timed out");
+        if (flag) {
+            c->slots.mark_stale();
+            return fail(c, FD_E_DEVICE, "walk: a grid barrier wait timed out; the active slots are stale");
+        }
     }
     return FD_OK;
 }

@@ -8,14 +8,14 @@
 
 namespace fd {
 
-GemmShape shape_with(int N, int K, int KT, int MT, int NG, int P) {
+GemmShape shape_with(int N, int K, int KT, int MT, int NG, int P, int cap = kMaxMTG) {
     GemmShape g;
     g.N = N;
     g.K = K;
     g.KT = KT;
     g.NB = N / 16;
     g.KB = K / KT;
-    g.MG = cdiv(MT, kMaxMTG);
+    g.MG = cdiv(MT, cap);
     g.MTG = cdiv(MT, g.MG);
     g.R = NG;
     g.P = P;
@@ -31,20 +31,20 @@ bool valid_split(const GemmShape& g, int P) {
     return P >= 1 && g.KB % P == 0 && g.KB / P >= 4;
 }
 
-GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu) {
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap) {
     // Candidates: 6 or 4 weight blocks per workgroup (6 only while the
     // accumulators of a 5-tile m-group fit), any split P that gives every
     // wave at least one step.  Score: how evenly the grid fills whole
     // rounds of one workgroup per CU, minus a small charge per extra split
     // (its partial tiles cost a write and a read).
-    GemmShape best = shape_with(N, K, KT, MT, 4, 1);
+    GemmShape best = shape_with(N, K, KT, MT, 4, 1, cap);
     double best_score = -1e9;
     for (int NG : {6, 4}) {
-        GemmShape base = shape_with(N, K, KT, MT, NG, 1);
+        GemmShape base = shape_with(N, K, KT, MT, NG, 1, cap);
         if (NG == 6 && base.MTG > 5) continue;
         for (int P = 1; P <= 64; ++P) {
             if (!valid_split(base, P)) continue;
-            GemmShape g = shape_with(N, K, KT, MT, NG, P);
+            GemmShape g = shape_with(N, K, KT, MT, NG, P, cap);
             const int grid = g.grid();
             const int rounds = cdiv(grid, n_cu);
             const double fill = (double)grid / ((double)rounds * n_cu);
@@ -101,14 +101,14 @@ int tune_value(const char* key, int dflt) {
     return dflt;
 }
 
-GemmShape tuned(GemmShape g, const char* name, bool ns) {
+GemmShape tuned(GemmShape g, const char* name, bool ns, int cap) {
     std::string n(name);
     int NG = tune_value((n + ".NG").c_str(), g.R);
     int P = tune_value((n + ".P").c_str(), g.P);
     if (!(NG == 4 || (NG == 6 && g.MTG <= 5) || (ns && ns_blocks_ok(NG, g.MTG)))) NG = g.R;
-    GemmShape base = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, 1);
+    GemmShape base = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, 1, cap);
     if (!valid_split(base, P)) P = valid_split(base, g.P) ? g.P : 1;
-    GemmShape out = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, P);
+    GemmShape out = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, P, cap);
     if (ns_blocks_ok(NG, out.MTG)) {
         const int kh = tune_value((n + ".KH").c_str(), g.kh);
         out.kh = kh == 2 && (out.KB / P) % 2 == 0 ? 2 : 1;
@@ -120,10 +120,11 @@ GemmShape tuned(GemmShape g, const char* name, bool ns) {
 void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8, bool w8,
                 uint64_t& off, bool ns) {
     sp.dims = dims;
-    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256), "qkv", ns);
-    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256), "o", ns);
-    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256), "gu", ns);
-    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256), "down", ns);
+    const int cap = w8 ? kMaxMTG8 : kMaxMTG;
+    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256, cap), "qkv", ns, cap);
+    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256, cap), "o", ns, cap);
+    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256, cap), "gu", ns, cap);
+    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256, cap), "down", ns, cap);
     sp.layers.resize(dims.L);
     auto tiles = [w8](const GemmShape& g) { return packed_matrix_bytes(g, w8); };
     for (int l = 0; l < dims.L; ++l) {
@@ -240,13 +241,9 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     }
     p.S = c.max_slots;
     // session rows padded to whole m-groups (at most kMaxMTG 16-row tiles
-    // each) so the GEMM main loop needs no row checks
-    {
-        const int mt = cdiv(c.max_slots, 16);
-        const int mg = cdiv(mt, kMaxMTG);
-        p.MT = mg * cdiv(mt, mg);
-        p.Sp = p.MT * 16;
-    }
+    // each, kMaxMTG8 with FP8 weights) so the GEMM main loop needs no row checks
+    p.MT = padded_mtiles(c.max_slots, p.w8 ? kMaxMTG8 : kMaxMTG);
+    p.Sp = p.MT * 16;
 
     uint64_t off = 0;
     StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};
@@ -263,7 +260,7 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, off, false);
     }
     if (p.head) {
-        p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256);
+        p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256, p.w8 ? kMaxMTG8 : kMaxMTG);
         p.w_head = off;
         off = align_up(off + packed_matrix_bytes(p.hshape, p.w8));
     }

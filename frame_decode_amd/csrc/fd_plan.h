@@ -15,6 +15,7 @@ namespace fd {
 constexpr int kWaves = 4;          // waves per workgroup in the GEMM and attention kernels
 constexpr int kTileBytes = 1024;   // one packed weight tile = 64 lanes x 16 bytes
 constexpr int kMaxMTG = 8;         // most 16-row tiles of sessions one GEMM workgroup holds
+constexpr int kMaxMTG8 = 5;        // (FP8 weights: the kernels are built for up to 5)
 constexpr int kAttnIters = 4;      // position loads per attention wave block (fp32 cache)
 constexpr int kAttnItersFp8 = 8;   // (FP8 cache)
 constexpr uint64_t kAlign = 256;
@@ -149,7 +150,15 @@ inline uint64_t packed_matrix_bytes(const GemmShape& g, bool w8) {
 }
 
 // Tile choice for one projection (exposed for tests).
-GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu);
+// cap: most m-tiles per m-group (kMaxMTG, or kMaxMTG8 for FP8 weights).
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap = kMaxMTG);
+
+// Session rows padded to whole m-groups of at most `cap` 16-row tiles.
+inline int padded_mtiles(int slots, int cap) {
+    const int mt = cdiv(slots, 16);
+    const int mg = cdiv(mt, cap);
+    return mg * cdiv(mt, mg);
+}
 
 // Row-split projection variant (bf16 weights, two-part activations): 8, 12
 // or 16 blocks per workgroup (2, 3 or 4 per wave), at most 5 m-tiles.

@@ -54,6 +54,23 @@ fd_status fdh_stack_shapes(const fd_config* cfg, int32_t* out) {
     return FD_OK;
 }
 
+// Row tiling as the plan of cfg chose it: out[0] = padded 16-row tiles;
+// out[1 + 2*i], out[2 + 2*i] = m-groups and tiles per m-group of QKV, O,
+// gate/up, down and (with a vocabulary) the output head.
+fd_status fdh_stack_mtiles(const fd_config* cfg, int32_t* out) {
+    if (!cfg || !out) return FD_E_INVAL;
+    fd::Plan p;
+    fd_status st = fd::make_plan(*cfg, &p, &g_err);
+    if (st != FD_OK) return st;
+    out[0] = p.MT;
+    const fd::GemmShape* g[5] = {&p.main.qkv, &p.main.o, &p.main.gu, &p.main.down, &p.hshape};
+    for (int i = 0; i < 5; ++i) {
+        out[1 + 2 * i] = g[i]->MG;
+        out[2 + 2 * i] = g[i]->MTG;
+    }
+    return FD_OK;
+}
+
 void* fdh_pool_new(int n_slots, int max_context, int rolling) {
     return new (std::nothrow) fd::SlotPool(n_slots, max_context, rolling != 0);
 }
@@ -74,5 +91,10 @@ void fdh_pool_advance(void* p) { ((fd::SlotPool*)p)->advance(); }
 int fdh_pool_dirty(void* p) { return ((fd::SlotPool*)p)->dirty() ? 1 : 0; }
 void fdh_pool_clear_dirty(void* p) { ((fd::SlotPool*)p)->clear_dirty(); }
 void fdh_pool_image(void* p, int32_t* dst) { ((fd::SlotPool*)p)->image(dst); }
+void fdh_pool_mark_stale(void* p) { ((fd::SlotPool*)p)->mark_stale(); }
+int fdh_pool_any_stale(void* p) {
+    int w = -1;
+    return ((fd::SlotPool*)p)->any_stale(&w) ? w : -1;
+}
 
 }  // extern "C"

@@ -23,7 +23,8 @@ public:
     // rolling: sessions continue past max_context frames (the cache keeps the
     // last max_context); otherwise a full window stops the step.
     SlotPool(int n_slots, int max_context, bool rolling = false)
-        : active_(n_slots, 0), pos_(n_slots, 0), max_context_(max_context), rolling_(rolling) {}
+        : active_(n_slots, 0), pos_(n_slots, 0), stale_(n_slots, 0), max_context_(max_context),
+          rolling_(rolling) {}
 
     int size() const { return (int)active_.size(); }
     int max_context() const { return max_context_; }
@@ -38,6 +39,7 @@ public:
         for (int i = 0; i < n; ++i) {
             active_[pick[i]] = 1;
             pos_[pick[i]] = 0;
+            stale_[pick[i]] = 0;
             out[i] = pick[i];
         }
         dirty_ = dirty_ || n > 0;
@@ -54,7 +56,10 @@ public:
             if (s < 0 || s >= size() || !active_[s] || seen[s]) return FD_E_BADSLOT;
             seen[s] = 1;
         }
-        for (int i = 0; i < n; ++i) active_[ids[i]] = 0;
+        for (int i = 0; i < n; ++i) {
+            active_[ids[i]] = 0;
+            stale_[ids[i]] = 0;
+        }
         dirty_ = dirty_ || n > 0;
         return FD_OK;
     }
@@ -63,8 +68,27 @@ public:
         if (s < 0 || s >= size() || !active_[s]) return FD_E_BADSLOT;
         if (p < 0 || p > (rolling_ ? kRollingMaxFrame : max_context_)) return FD_E_INVAL;
         pos_[s] = p;
+        stale_[s] = 0;
         dirty_ = true;
         return FD_OK;
+    }
+
+    // A step that stopped early (a persistent-walk barrier timed out) left
+    // the device positions and the new cache entries of every active slot
+    // unknown: those slots stay stale until the caller gives each a
+    // position (set_position) or frees it.
+    void mark_stale() {
+        for (int s = 0; s < size(); ++s)
+            if (active_[s]) stale_[s] = 1;
+    }
+
+    bool any_stale(int* which) const {
+        for (int s = 0; s < size(); ++s)
+            if (active_[s] && stale_[s]) {
+                if (which) *which = s;
+                return true;
+            }
+        return false;
     }
 
     fd_status state(int s, int32_t* a, int32_t* p) const {
@@ -114,6 +138,7 @@ public:
 private:
     std::vector<int32_t> active_;
     std::vector<int32_t> pos_;
+    std::vector<char> stale_;
     int max_context_;
     bool rolling_;
     bool dirty_ = true;

@@ -63,14 +63,20 @@ typedef int32_t fd_status;
  * the life of a ctx (Nemotron case study, "Under the hood": profiles are
  * compiled per model, session capacity and context length).
  *
- * Supported: w_dtype == act_dtype in {FD_F32, FD_BF16}; kv_dtype in
- * {FD_F32, FD_FP8_E4M3}; head_dim in {64, 128, 256}; n_heads a multiple of
- * n_kv_heads with n_heads / n_kv_heads in {1, 2, 4}; d_model, d_ffn and
- * n_heads*head_dim multiples of 256 (bf16) or 128 (fp32); max_slots in
- * 1..4096; max_context in 1..65536.  An optional depth stack (depth_steps >
- * 0) runs after the main stack on every frame, for depth_steps sequential
- * sub-steps with its own fp32 cache cleared every frame; it requires
- * w_dtype == FD_F32 and kv_dtype == FD_F32.
+ * Supported (w_dtype / act_dtype):
+ *   FD_F32 / FD_F32, FD_BF16 / FD_BF16: weights in that type;
+ *   FD_FP8_E4M3 / FD_BF16: the caller passes bf16 weight tensors (as for
+ *     FD_BF16) and fd_init quantises each output row to OCP E4M3 codes of
+ *     w / scale with scale = max|row| / 448 (1 for a zero row), one fp32
+ *     scale per row; the step uses scale * decode(code).  Not combined with
+ *     a depth stack or FD_EXEC_WALK.
+ * kv_dtype in {FD_F32, FD_FP8_E4M3}; head_dim in {64, 128, 256}; n_heads a
+ * multiple of n_kv_heads with n_heads / n_kv_heads in {1, 2, 4}; d_model,
+ * d_ffn and n_heads*head_dim multiples of 256 (bf16), 512 (FP8 weights) or
+ * 128 (fp32); max_slots in 1..4096; max_context in 1..65536.  An optional
+ * depth stack (depth_steps > 0) runs after the main stack on every frame,
+ * for depth_steps sequential sub-steps with its own fp32 cache cleared
+ * every frame; it requires w_dtype == FD_F32 and kv_dtype == FD_F32.
  */
 typedef struct {
     int32_t n_layers;
@@ -83,8 +89,8 @@ typedef struct {
     float rope_base;      /* rotary angle of pair i at position p: p * base^(-2i/head_dim) */
     int32_t max_slots;    /* S_cap: session slots, fixed launch shape */
     int32_t max_context;  /* T_max: frames a slot's cache holds */
-    int32_t w_dtype;      /* FD_F32 or FD_BF16 */
-    int32_t act_dtype;    /* must equal w_dtype */
+    int32_t w_dtype;      /* FD_F32, FD_BF16 or FD_FP8_E4M3 (see above) */
+    int32_t act_dtype;    /* w_dtype, or FD_BF16 with FD_FP8_E4M3 weights */
     int32_t kv_dtype;     /* FD_F32 or FD_FP8_E4M3 */
     int32_t depth_steps;  /* 0 = no depth stack */
     int32_t depth_layers;
@@ -131,7 +137,10 @@ typedef struct {
  * most 5 row tiles of 16 slots per m-group of the projections (up to 80
  * slots, or more than 128, where the rows split into m-groups).
  * A barrier wait that times out makes the launch stop early and the next
- * fd_sync return FD_E_DEVICE.
+ * fd_sync return FD_E_DEVICE; the slots that were active are then stale
+ * (their device positions and newest cache entries are unknown): fd_step
+ * and fd_step_static return FD_E_STATE until each is given a position with
+ * fd_set_position or freed with fd_free.
  */
 #define FD_EXEC_KERNELS 0
 #define FD_EXEC_WALK 1
@@ -255,10 +264,16 @@ fd_status fd_alloc_slots(fd_ctx* ctx, int32_t n, int32_t* slots_out);
  *          output; rows of inactive slots are set to 0.
  *   depth_out device [max_slots][depth_steps][depth_d] in act_dtype, or
  *          NULL when the profile has no depth stack; inactive rows set to 0.
+ * x_in, y_out and depth_out must be 16-byte aligned (FD_E_INVAL, no launch).
  * Each active slot's new key/value are appended at its position, which then
  * advances by one.  Enqueued on `stream` without waiting (the caller syncs);
- * no host I/O and no allocation.  FD_E_CTXFULL (and no launch) if an active
- * slot's position equals max_context.
+ * no host I/O and no allocation.  With FD_EXEC_KERNELS it enqueues the fixed
+ * kernel sequence of the profile (per layer: the QKV projection, attention,
+ * the O projection, gate/up and down, plus a k-split reduction after a
+ * projection split over K; embed before and the final norm after); with
+ * FD_EXEC_WALK one persistent launch.  FD_E_CTXFULL (and no launch) if an
+ * active slot's position equals max_context; FD_E_STATE (no launch) while a
+ * slot is stale (see FD_EXEC_WALK).
  */
 fd_status fd_step(fd_ctx* ctx, const void* x_in, void* y_out, void* depth_out, void* stream);
 
@@ -272,8 +287,9 @@ fd_status fd_step(fd_ctx* ctx, const void* x_in, void* y_out, void* depth_out, v
  *          for inactive slots.
  *   logits_out device fp32 [max_slots][vocab] or NULL: the logits (rows of
  *          inactive slots 0).  Rows max_slots and beyond are never written.
- * FD_E_INVAL if the profile has no head (vocab 0) or tokens_out is NULL;
- * otherwise as fd_step.
+ * FD_E_INVAL if the profile has no head (vocab 0), tokens_out is NULL or not
+ * 4-byte aligned, or logits_out is not 16-byte aligned; otherwise as
+ * fd_step.
  */
 fd_status fd_step_tokens(fd_ctx* ctx, const void* x_in, void* y_out, void* depth_out,
                          int32_t* tokens_out, float* logits_out, void* stream);
@@ -366,7 +382,8 @@ fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, in
 fd_status fd_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int32_t grid, void* stream);
 
 /* Waits for the ctx's last enqueued work on `stream` and reports device
- * errors (FD_E_DEVICE) including the kernels' own fault flag. */
+ * errors (FD_E_DEVICE) including the persistent walk's timed-out barrier
+ * flag (after which the active slots are stale, see FD_EXEC_WALK). */
 fd_status fd_sync(fd_ctx* ctx, void* stream);
 
 /* Message of the ctx's most recent error ("" if none); valid until the

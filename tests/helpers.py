@@ -50,6 +50,15 @@ def rel_err_rows(y, r):
     return float(np.max(num / den))
 
 
+def rel_err_elem(y, r):
+    """max over elements of |y - r| / max(|r|, 1e-2 ||r_row||_inf): the
+    elementwise companion of rel_err_rows."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    floor = 1e-2 * np.max(np.abs(r), axis=-1, keepdims=True)
+    return float(np.max(np.abs(y - r) / np.maximum(np.abs(r), np.maximum(floor, 1e-30))))
+
+
 def to_np(t):
     return t.float().cpu().numpy()
 

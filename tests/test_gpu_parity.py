@@ -10,7 +10,7 @@ import torch
 
 import synth
 from oracle import Oracle, fp8
-from tests.helpers import check, make_context, rel_err_rows, rows_input, say, to_np
+from tests.helpers import check, make_context, rel_err_elem, rel_err_rows, rows_input, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -503,6 +503,101 @@ def test_fp8_weights_with_per_row_scales():
         check(tg[S - 1] == -1, "the inactive slot's token must be -1")
         for s in slots:
             pos[s] += 1
+    ctx.fd_destroy()
+
+
+# every projection split over K, with 4- and with 6-block workgroups
+FP8_SPLITS = {
+    "ng6": "qkv.NG=6,qkv.P=2,o.NG=6,o.P=4,gu.NG=6,gu.P=2,down.NG=6,down.P=4",
+    "ng4": "qkv.NG=4,qkv.P=4,o.NG=4,o.P=2,gu.NG=4,gu.P=4,down.NG=4,down.P=8",
+}
+
+
+@pytest.mark.parametrize("split", sorted(FP8_SPLITS))
+def test_fp8_weights_eighty_slots(split, monkeypatch):
+    """FP8 weights at 80 slots: five 16-row tiles per m-group (the kernels
+    the 80-session FP8-weight step runs), 7B head geometry (MHA, 128-dim
+    heads) at reduced width and depth, every projection split over K (QKV
+    planes, k-split partial sums with the residual and gate/up epilogues),
+    with the output head.  All 80 sessions at positions 0..150 against the
+    oracle running the dequantised weights: outputs and logits 2e-2."""
+    monkeypatch.setenv("FD_TUNE", FP8_SPLITS[split])
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=1024, n_heads=8, n_kv_heads=8,
+                              d_ffn=2048, max_slots=80, max_context=160, vocab=512,
+                              w_dtype="fp8", act_dtype="bf16")
+    model = synth.Model(cfg, gain_noise=True)
+    say(f"fp8 weights, 80 slots, splits {FP8_SPLITS[split]}")
+    ctx = make_context(cfg, model)
+    orc = Oracle(cfg, model)
+    slots = ctx.fd_alloc_slots(80)
+    rng = np.random.default_rng(21)
+    start = rng.integers(0, 151, size=80)
+    start[:4] = [0, 1, 150, 2]
+    sess = {s: 700 + s for s in slots}
+    pos = {s: int(p) for s, p in zip(slots, start)}
+    for s in slots:
+        if pos[s]:
+            for l in range(cfg["n_layers"]):
+                v = synth.prefill_values(cfg, sess[s], l, pos[s])
+                orc.prefill(s, l, v)
+                ctx.fd_kv_write(s, l, 0, torch.from_numpy(v).cuda())
+            ctx.fd_set_position(s, pos[s])
+    S, V = cfg["max_slots"], cfg["vocab"]
+    y = torch.empty((S, cfg["d_model"]), device="cuda", dtype=torch.bfloat16)
+    tokens = torch.empty((S,), device="cuda", dtype=torch.int32)
+    logits = torch.empty((S, V), device="cuda", dtype=torch.float32)
+    for step in range(2):
+        x_np, x = rows_input(cfg, sess, {s: pos[s] for s in slots})
+        ctx.fd_step_tokens(x, y, tokens, logits)
+        ctx.fd_sync()
+        ref = orc.step(slots, x_np[slots], [pos[s] for s in slots])
+        lref, _ = orc.head(ref)
+        yg, lg = to_np(y), logits.cpu().numpy()
+        e, el = rel_err_rows(yg[slots], ref), rel_err_rows(lg[slots], lref)
+        say(f"  step {step}: output max rel err {e:.3e} (elementwise {rel_err_elem(yg[slots], ref):.3e}), "
+            f"logits {el:.3e}")
+        assert e <= 2e-2 and el <= 2e-2
+        tg = tokens.cpu().numpy()
+        for s in slots:
+            check(tg[s] == int(np.argmax(lg[s])), f"slot {s}: token is not the first maximum")
+        for s in slots:
+            pos[s] += 1
+    ctx.fd_destroy()
+
+
+def test_misaligned_output_is_refused_without_effect():
+    """A y_out that is not 16-byte aligned: FD_E_INVAL, no launch, no cache
+    byte or position changed."""
+    from frame_decode_amd import FdError
+    from frame_decode_amd.abi import FD_E_INVAL
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=256, n_heads=2, n_kv_heads=2,
+                              d_ffn=256, max_slots=4, max_context=32)
+    model = synth.Model(cfg)
+    ctx = make_context(cfg, model)
+    _sentinel_fill(ctx, cfg)
+    slots = ctx.fd_alloc_slots(2)
+    _, x = rows_input(cfg, {s: 40 + s for s in slots}, {s: 0 for s in slots})
+    buf = torch.zeros(cfg["max_slots"] * cfg["d_model"] + 8, device="cuda", dtype=torch.bfloat16)
+    y_bad = buf[4:4 + cfg["max_slots"] * cfg["d_model"]].view(cfg["max_slots"], cfg["d_model"])
+    check(y_bad.data_ptr() % 16 == 8, "test buffer is misaligned by 8 bytes")
+    before = ctx.arena.clone()
+    with pytest.raises(FdError) as ei:
+        ctx.fd_step(x, y_bad)
+    check(ei.value.status == FD_E_INVAL, f"status {ei.value.status}")
+    x_bad = torch.zeros(cfg["max_slots"] * cfg["d_model"] + 8, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(FdError):
+        ctx.fd_step(x_bad[4:4 + x.numel()].view_as(x), torch.empty_like(x))
+    ctx.fd_sync()
+    check(torch.equal(before, ctx.arena), "cache bytes changed")
+    check(bool(torch.all(buf == 0)), "the misaligned output was written")
+    for s in slots:
+        check(ctx.fd_slot_state(s) == (1, 0), "position moved")
+    # an aligned step afterwards still runs
+    y = torch.empty_like(x)
+    ctx.fd_step(x, y)
+    ctx.fd_sync()
+    for s in slots:
+        check(ctx.fd_slot_state(s) == (1, 1), "the aligned step did not advance")
     ctx.fd_destroy()
 
 

@@ -46,6 +46,9 @@ def host():
     h.fdh_gemm_shape.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_int32)]
     h.fdh_stack_shapes.argtypes = [ctypes.POINTER(FdConfig), ctypes.POINTER(ctypes.c_int32)]
+    h.fdh_stack_mtiles.argtypes = [ctypes.POINTER(FdConfig), ctypes.POINTER(ctypes.c_int32)]
+    h.fdh_pool_mark_stale.argtypes = [ctypes.c_void_p]
+    h.fdh_pool_any_stale.argtypes = [ctypes.c_void_p]
     return h
 
 
@@ -335,3 +338,48 @@ def test_fp8_weight_plan(host):
     talker = synth.get_config("talker_s56")
     talker.update(w_dtype="fp8", act_dtype="bf16")
     assert _plan(host, talker)[0] == FD_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("slots", [7, 80, 96, 112, 128, 140, 709, 4096])
+def test_fp8_weight_row_groups_stay_within_the_built_kernels(host, slots):
+    """FP8-weight projections are built for at most 5 row tiles per m-group:
+    every slot count plans within that (rows padded to whole m-groups), and
+    bf16 profiles keep their own limit of 8."""
+    for wdt, cap in (("fp8", 5), ("bf16", 8)):
+        cfg = synth.scaled_config("7b_s80_p1499", max_slots=slots, w_dtype=wdt, act_dtype="bf16",
+                                  vocab=1024)
+        for k in ("position",):
+            cfg.pop(k, None)
+        out = (ctypes.c_int32 * 11)()
+        assert host.fdh_stack_mtiles(ctypes.byref(config_from_dict(cfg)), out) == FD_OK
+        mt = out[0]
+        assert mt * 16 >= slots and (mt - 1) * 16 < slots + 16 * cap
+        for i in range(5):
+            mg, mtg = out[1 + 2 * i], out[2 + 2 * i]
+            assert 1 <= mtg <= cap, (wdt, slots, i, mtg)
+            assert mg * mtg == mt, (wdt, slots, i, mg, mtg, mt)
+
+
+def test_stale_slots_after_an_interrupted_step(host):
+    """A step that stopped early marks every active slot stale; each slot
+    leaves that state when given a position or freed, and a newly admitted
+    slot is never stale."""
+    p = host.fdh_pool_new(4, 100, 0)
+    try:
+        out = (ctypes.c_int32 * 4)()
+        assert host.fdh_pool_alloc(p, 3, out) == FD_OK
+        assert host.fdh_pool_any_stale(p) == -1
+        host.fdh_pool_mark_stale(p)
+        assert host.fdh_pool_any_stale(p) == 0
+        assert host.fdh_pool_set_position(p, 0, 5) == FD_OK
+        assert host.fdh_pool_any_stale(p) == 1
+        ids = (ctypes.c_int32 * 1)(1)
+        assert host.fdh_pool_free(p, ids, 1) == FD_OK
+        assert host.fdh_pool_any_stale(p) == 2
+        assert host.fdh_pool_set_position(p, 2, 0) == FD_OK
+        assert host.fdh_pool_any_stale(p) == -1
+        one = (ctypes.c_int32 * 1)()
+        assert host.fdh_pool_alloc(p, 1, one) == FD_OK and one[0] == 1
+        assert host.fdh_pool_any_stale(p) == -1
+    finally:
+        host.fdh_pool_delete(p)
