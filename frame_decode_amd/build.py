@@ -46,6 +46,15 @@ def build_host() -> str:
     return HOST_LIB
 
 
+def build_host_sanitized(out: str) -> str:
+    """The host-only library with AddressSanitizer and UndefinedBehavior-
+    Sanitizer (host compiler only; no device code is involved), for running
+    the host ABI tests under the sanitizers."""
+    _run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-fno-omit-frame-pointer",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", *HOST_SOURCES, "-o", out])
+    return out
+
+
 def build_hip() -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"

@@ -1618,8 +1618,9 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, uint64_t n, hipStream_t st) 
 }
 
 // ---------------------------------------------------------------------------
-// HBM read probe: streams a buffer once with wide loads (8 independent 16-byte
-// loads in flight per lane), folding the words so the loads stay live.
+// HBM read probe: streams a buffer once with wide non-temporal loads (8
+// independent 16-byte loads in flight per lane), folding the words so the
+// loads stay live.
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* buf, size_t n16, uint32_t* sink) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1627,7 +1628,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* buf, size_
     for (; i + 7 * stride < n16; i += 8 * stride) {
         u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = buf[i + u * stride];
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&buf[i + u * stride]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc ^= v[u];
     }

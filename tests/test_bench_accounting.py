@@ -1,0 +1,112 @@
+"""Host logic of the benchmark's serving clock (two 80 ms steps per 160 ms
+beat, p99 per beat, late session-beats: the Nemotron VoiceChat case
+study's measurement notes), driven by a stub context and a stub clock, so
+the percentile and late-beat accounting is checked without a GPU."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_beat_stats_percentiles_and_late_count():
+    lat = [10.0] * 98 + [170.0, 200.0]
+    st = bench.beat_stats(lat, [9.0] * 100, n_active=56)
+    assert st["p50_ms"] == 10.0
+    assert st["p99_ms"] == 170.0          # nearest rank of 100 beats
+    assert st["max_ms"] == 200.0
+    assert st["late_beats"] == 2
+    assert st["late_session_beats"] == 2 * 56
+    assert st["gpu_p99_ms"] == 9.0
+    # exactly at the deadline is on time
+    assert bench.beat_stats([160.0, 160.0], [], n_active=3)["late_beats"] == 0
+    assert bench.beat_stats([160.0001], [], n_active=3)["late_session_beats"] == 3
+
+
+class _Clock:
+    def __init__(self):
+        self.t = 100.0
+
+    def __call__(self):
+        return self.t
+
+    def sleep(self, dt):
+        assert dt >= 0
+        self.t += dt
+
+
+class _StubCtx:
+    """The slot calls run_beats makes, with fd_step's position rules."""
+
+    def __init__(self, slots, window):
+        self.max_slots, self.window = slots, window
+        self.active, self.pos = [0] * slots, [0] * slots
+        self.steps = 0
+
+    def fd_slot_state(self, s):
+        return self.active[s], self.pos[s]
+
+    def fd_free(self, ids):
+        assert len(set(ids)) == len(ids)
+        for s in ids:
+            assert self.active[s], "freeing a free slot"
+            self.active[s] = 0
+
+    def fd_alloc_slots(self, n):
+        free = [s for s in range(self.max_slots) if not self.active[s]]
+        assert len(free) >= n
+        for s in free[:n]:
+            self.active[s], self.pos[s] = 1, 0
+        return free[:n]
+
+    def fd_set_position(self, s, p):
+        assert self.active[s] and 0 <= p <= self.window
+        self.pos[s] = p
+
+    def step(self):
+        for s in range(self.max_slots):
+            if self.active[s]:
+                assert self.pos[s] < self.window, "stepping a full window (FD_E_CTXFULL)"
+                self.pos[s] += 1
+        self.steps += 1
+
+
+@pytest.mark.parametrize("slow_beat", [None, 7])
+def test_run_beats_churn_and_late_beats(slow_beat):
+    """40 beats x 2 runs, 12 of 16 slots active in a 30-frame window (so
+    sessions end and new ones are admitted every few beats); one beat may
+    take 200 ms of a 160 ms budget."""
+    clock = _Clock()
+    ctx = _StubCtx(16, 30)
+    beat = {"n": 0}
+
+    def two_steps():
+        ctx.step()
+        ctx.step()
+        b = beat["n"]
+        beat["n"] += 1
+        # the first call of each run is its warm-up pair
+        dur = 0.200 if (slow_beat is not None and b == slow_beat + 1) else 0.012
+        clock.t += dur
+        assert sum(ctx.active) == 12, "the active count changes only by churn"
+        return dur * 1e3
+
+    out = bench.run_beats(ctx, two_steps, beats=40, runs=2, n_active=12, max_context=30,
+                          seed=3, clock=clock, sleep=clock.sleep)
+    assert out["session_beats"] == 12 * 40 * 2
+    assert out["admissions"] == out["retirements"] > 0
+    assert ctx.steps == 2 * (40 + 1) * 2
+    if slow_beat is None:
+        assert out["late_beats"] == 0 and out["late_session_beats"] == 0
+        assert out["max_ms"][0] == pytest.approx(12.0)
+    else:
+        # only the slow beat misses: the next starts 40 ms behind its
+        # schedule and still finishes within 160 ms of it
+        assert out["late_beats"] == 1 and out["late_session_beats"] == 12
+        assert out["max_ms"][0] == pytest.approx(200.0)
+        assert out["p99_ms"][0] == pytest.approx(200.0)
+    assert all(p <= 30 for p in ctx.pos)

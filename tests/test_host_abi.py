@@ -26,9 +26,10 @@ def declared_symbols():
 
 @pytest.fixture(scope="module")
 def host():
-    if not os.path.exists(HOST):
-        pytest.fail("libfd_host.so not built (run __graft_entry__.build())")
-    h = ctypes.CDLL(HOST)
+    path = os.environ.get("FD_HOST_LIB", HOST)  # (a sanitizer build of the same sources)
+    if not os.path.exists(path):
+        pytest.fail(f"{path} not built (run __graft_entry__.build())")
+    h = ctypes.CDLL(path)
     h.fdh_pool_new.restype = ctypes.c_void_p
     h.fdh_pool_new.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     for n in ("fdh_pool_alloc", "fdh_pool_free"):
