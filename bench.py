@@ -148,11 +148,37 @@ def prefill_ragged(ctx, cfg, where, seed):
     torch.cuda.synchronize()
 
 
-def run_gpu(cfg, pos, steps, warmup, runs=1):
+def attention_trace_summary(stamps, clock_hz=1e8, concurrent=512):
+    """Per-workgroup phases of one attention launch from its device-clock
+    stamps [workgroups][4] (entry, prologue done, stream done, exit): the
+    median / p90 / max of each phase in microseconds, the launch span from
+    the first entry to the last exit, when the last workgroup entered, and
+    the busy fraction of the `concurrent` workgroup places over the span."""
+    import numpy as np
+    st = np.asarray(stamps, dtype=np.int64).reshape(-1, 4)
+    st = st[st[:, 0] != 0]
+    if len(st) == 0:
+        return None
+    us = 1e6 / clock_hz
+    t0 = st[:, 0].min()
+    span = (st[:, 3].max() - t0) * us
+    out = {"workgroups": int(len(st)), "span_us": float(span),
+           "last_entry_us": float((st[:, 0].max() - t0) * us)}
+    for name, (a, b) in (("prologue", (0, 1)), ("stream", (1, 2)), ("epilogue", (2, 3)),
+                         ("total", (0, 3))):
+        d = np.sort((st[:, b] - st[:, a]) * us)
+        out[name + "_us"] = {"p50": float(d[len(d) // 2]), "p90": float(d[int(0.9 * (len(d) - 1))]),
+                             "max": float(d[-1]), "sum": float(d.sum())}
+    out["busy_frac"] = out["total_us"]["sum"] / (span * concurrent) if span > 0 else None
+    return out
+
+
+def run_gpu(cfg, pos, steps, warmup, runs=1, trace_layer=None):
     """The timed steps of one workload: `steps` steps after `warmup`
     (the headline), then runs-1 more repetitions of `steps` steps, then a
-    pass with per-kernel event pairs.  pos=None with a ragged workload puts
-    its seeded active set at their own positions."""
+    pass with per-kernel event pairs, then (trace_layer set) one step with
+    device-clock stamps in that layer's attention launch.  pos=None with a
+    ragged workload puts its seeded active set at their own positions."""
     import numpy as np
     import torch
     import synth
@@ -191,10 +217,18 @@ def run_gpu(cfg, pos, steps, warmup, runs=1):
     time_steps(ctx, cfg, active, where, x, y, d, steps, 0, tokens)
     kern = ctx.fd_profile_read()
     ctx.fd_profile(False)
+    trace = None
+    if trace_layer is not None:
+        # room for every chunking the plan can choose (at most 256 chunks)
+        stamps = torch.zeros((S * cfg["n_kv_heads"] * 256, 4), device="cuda", dtype=torch.int64)
+        ctx.fd_trace_attention(stamps, trace_layer)
+        time_steps(ctx, cfg, active, where, x, y, d, 1, 0, tokens)
+        ctx.fd_trace_attention(None)
+        trace = attention_trace_summary(stamps.cpu().numpy())
     positions = [where[s] for s in active]
     res = {
         "total_ms": total_ms, "per_step_ms": per, "kernels": kern, "runs_ms_per_step": runs_ms,
-        "active": len(active),
+        "active": len(active), "attn_trace": trace,
         "step_bytes": rf.step_bytes(cfg, positions, head=tokens is not None),
         "attn_bytes": rf.attention_bytes_per_launch(cfg, positions),
     }
@@ -582,6 +616,8 @@ def main():
                     help="new-frame index of every session (default: the workload's)")
     ap.add_argument("--exec-mode", type=int, default=0,
                     help="0: kernel sequence per step; 1: the whole step as one persistent walk")
+    ap.add_argument("--attn-trace", type=int, default=None, metavar="LAYER",
+                    help="stamp one step's attention launch of this layer and report its phases")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB copy kernel first (scale for HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -641,7 +677,7 @@ def main():
         calibration_copy()
     probe = read_probe_gbs()
     log(f"read probe: {probe:.0f} GB/s")
-    r = run_gpu(cfg, pos, args.steps, args.warmup, runs=args.runs)
+    r = run_gpu(cfg, pos, args.steps, args.warmup, runs=args.runs, trace_layer=args.attn_trace)
     total_ms = r["total_ms"]
     ms_step = total_ms / args.steps
     per = sorted(r["per_step_ms"])
@@ -726,6 +762,7 @@ def main():
             "avg_launch_ms": attn_avg_s * 1e3,
         },
         "sanity": sanity,
+        **({"attn_trace": r["attn_trace"]} if r["attn_trace"] else {}),
         "kernels": kern_report,
         "max_sessions_80ms": maxs,
         "cpu_baseline": cpu,

@@ -22,9 +22,14 @@ HOST_SOURCES = ["host_shim.cpp", "fd_plan.cpp"]
 # Packed fp32 VALU instructions are disabled for the device code (the
 # compiler would otherwise form them from plain fp32 code); the host pass
 # prints a harmless "not a recognized feature" warning for it.
+# MFMA accumulators in ordinary VGPRs (amdgpu-mfma-vgpr-form): with the
+# default AGPR form the projection loops copied accumulators between the
+# two register files every iteration (about 1.5 move instructions per MFMA
+# at six blocks per workgroup) and spilled at five row tiles in the walk.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 

@@ -149,6 +149,13 @@ class Context:
         _check(_lib().fd_kv_layout(self._ctx, ctypes.byref(v)), self._ctx)
         return {f: getattr(v, f) for f, _ in FdKvView._fields_}
 
+    def fd_trace_attention(self, stamps=None, layer: int = 0) -> None:
+        """Device-clock stamps of one layer's attention launch into the int64
+        device tensor ``stamps`` [workgroups][4] (None turns it off)."""
+        n = 0 if stamps is None else stamps.numel() // 4
+        _check(_lib().fd_trace_attention(self._ctx, ctypes.c_void_p(_ptr(stamps)), int(layer), int(n)),
+               self._ctx)
+
     def fd_profile(self, enable: bool) -> None:
         _check(_lib().fd_profile(self._ctx, 1 if enable else 0), self._ctx)
 

@@ -51,6 +51,9 @@ struct fd_ctx {
     const void* head_x = nullptr;
     const void* head_x_lo = nullptr;
     bool walk_launched = false;
+    // device-clock trace of one layer's attention launch (fd_trace_attention)
+    uint64_t* trace = nullptr;
+    int trace_layer = -1;
     explicit fd_ctx(const fd::Plan& p) : plan(p), slots(p.S, p.cfg.max_context, p.ring) {}
 };
 
@@ -268,6 +271,8 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.part = (float*)Wk(c, pl.ws_apart);
         at.o_out = Wk(c, pl.ws_o);
         at.o_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
+        at.early = sp.attn.early;
+        at.trace = (&sp == &pl.main && l == c->trace_layer) ? c->trace : nullptr;
         e = timed(c, K_ATTN, st, [&] {
             return fd::launch_attn(at, wt, cache.fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
         });
@@ -1040,6 +1045,25 @@ fd_status fd_kv_layout(fd_ctx* c, fd_kv_view* out) {
     out->kv_scale = pl.kv_fp8 ? (const float*)P(c, pl.main.kvsig) : nullptr;
     out->slot_active = slot_active(c);
     out->slot_pos = slot_pos(c);
+    return FD_OK;
+}
+
+fd_status fd_trace_attention(fd_ctx* c, uint64_t* stamps, int32_t layer, int32_t max_workgroups) {
+    if (!c) return FD_E_INVAL;
+    if (!stamps) {
+        c->trace = nullptr;
+        c->trace_layer = -1;
+        return FD_OK;
+    }
+    const fd::Plan& pl = c->plan;
+    const int grid = pl.S * pl.main.dims.hkv * pl.main.attn.n_chunks;
+    if (pl.walk) return fail(c, FD_E_UNSUPPORTED, "fd_trace_attention: kernel-sequence profiles only");
+    if (layer < 0 || layer >= pl.main.dims.L) return fail(c, FD_E_INVAL, "layer out of range");
+    if (max_workgroups < grid)
+        return fail(c, FD_E_INVAL, "the stamp buffer needs " + std::to_string(grid) + " workgroups");
+    if ((uintptr_t)stamps & 7) return fail(c, FD_E_INVAL, "stamps must be 8-byte aligned");
+    c->trace = stamps;
+    c->trace_layer = layer;
     return FD_OK;
 }
 

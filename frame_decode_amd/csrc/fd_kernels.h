@@ -75,6 +75,9 @@ struct AttnArgs {
     float* part;           // [S][hkv][n_chunks][G][hd + 2]
     void* o_out;           // [Sp][hq*hd] activation type, fragment-packed
     void* o_lo;            // optional (bf16): o - o_out, rounded to bf16
+    int early;             // request each wave's first block of keys/values before the prologue
+    uint64_t* trace;       // optional: 4 device-clock stamps per workgroup [grid][4]
+                           // (entry, prologue done, stream done, exit)
 };
 
 struct EmbedArgs {

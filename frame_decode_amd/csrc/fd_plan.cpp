@@ -162,6 +162,7 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     // the merge kernel holds one chunk per thread: at most 256 chunks
     a.tc = std::max(a.tc, cdiv(cdiv(dims.T, 256), round) * round);
     a.n_chunks = cdiv(dims.T, a.tc);
+    a.early = tune_value("attn.early", 0);
 }
 
 }  // namespace

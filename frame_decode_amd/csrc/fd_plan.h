@@ -58,6 +58,7 @@ struct AttnShape {
     int lpp = 0;      // lanes per position
     int tc = 0;       // positions per chunk (one workgroup)
     int n_chunks = 0; // chunks per (slot, kv-head) for a full window
+    int early = 0;    // first block of the stream requested before the prologue
     uint64_t part_floats = 0;
 };
 

@@ -1002,15 +1002,35 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     const int c = lane % LPP;
     const int jj = lane / LPP;
 
+    // optional device-clock stamps of this workgroup (kernel launches only)
+    uint64_t* const trace = CO ? nullptr : a.trace;
+    const int wg = bid;
+    auto stamp = [&](int i) {
+        if (trace) {
+            const uint64_t t = __builtin_amdgcn_s_memrealtime();
+            if (threadIdx.x == 0) trace[(size_t)wg * 4 + i] = t;
+        }
+    };
+    auto stamp_all = [&]() {
+        if (trace) {
+            const uint64_t t = __builtin_amdgcn_s_memrealtime();
+            if (threadIdx.x < 3) trace[(size_t)wg * 4 + 1 + threadIdx.x] = t;
+        }
+    };
+    stamp(0);
     const int chunk = bid % a.n_chunks;
     bid /= a.n_chunks;
     const int g = bid % a.hkv;
     const int s = bid / a.hkv;
-    if (s >= a.S) return;
+    if (s >= a.S) {
+        stamp_all();
+        return;
+    }
     if (!a.active[s]) {
         if (chunk == 0)
             for (int i = threadIdx.x; i < G * D; i += blockDim.x)
                 store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
+        stamp_all();
         return;
     }
     // frame index p of the new entry; n cache positions attended; the new
@@ -1021,7 +1041,10 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     const int n = a.ring ? min(p + 1, a.T) : p + 1;
     const int hole = a.ring ? p % a.T : p;
     const int nch = (n + a.tc - 1) / a.tc;
-    if (chunk >= nch) return;
+    if (chunk >= nch) {
+        stamp_all();
+        return;
+    }
     const int t0 = chunk * a.tc;
 
     uint8_t* kbase = a.arena + (size_t)s * a.slot_stride + (size_t)g * a.head_stride;
@@ -1069,15 +1092,16 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
         __builtin_amdgcn_sched_barrier(0);
     };
     int base = t0 + wave * SUB;
-    if constexpr (CO) {
-        // persistent walk: cached keys were written by earlier launches or
-        // earlier phases, so the first block streams during the barrier wait
-        if (base < t1) {
-            load_blk(rk, kbase, base);
-            load_blk(rv, vbase, base);
-        }
-        wait();
+    // the first block does not depend on q: in the persistent walk it
+    // streams during the barrier wait (cached keys were written by earlier
+    // launches or phases); in a kernel launch, with `early`, during the
+    // prologue
+    const bool first_early = CO || a.early;
+    if (first_early && base < t1) {
+        load_blk(rk, kbase, base);
+        load_blk(rv, vbase, base);
     }
+    if constexpr (CO) wait();
 
     const int nquad = (own_new ? G + 2 : G) * QPH;
     const float ssv = threadIdx.x < a.nss ? a.ss_in[(size_t)s * a.ss_stride + threadIdx.x] : 0.f;
@@ -1163,7 +1187,8 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
 #pragma unroll
             for (int i = 0; i < VE; ++i) qv[h][j * VE + i] = s_q[h][(c + LPP * j) * VE + i];
 
-    if (!CO && base < t1) {
+    stamp(1);
+    if (!first_early && base < t1) {
         load_blk(rk, kbase, base);
         load_blk(rv, vbase, base);
     }
@@ -1236,6 +1261,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
         }
         load_blk(rv, vbase, base + 4 * SUB);
     }
+    stamp(2);
     // reduce over the wave's position groups (lanes with equal c)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -1303,6 +1329,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             }
         }
     }
+    stamp(3);
 }
 
 template <int WT, int FP8, int D, int G>

@@ -372,6 +372,22 @@ fd_status fd_profile(fd_ctx* ctx, int32_t enable);
 fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, int32_t n);
 
 /*
+ * Device-clock trace of the attention kernel (bench hook, off by default).
+ * With stamps != NULL, every later fd_step's attention launch of main-stack
+ * layer `layer` has each workgroup write four 64-bit readings of the
+ * device's constant-rate clock (s_memrealtime, 100 MHz) with ordinary
+ * vector stores to stamps[4*w + i]: i = 0 on entry, 1 when its prologue
+ * (the norm, rotary, cache append and query set-up) is done, 2 when its
+ * stream over the cached positions is done, 3 on exit (a workgroup with no
+ * work writes entry then three equal exit stamps).  w is the workgroup
+ * index, (slot * n_kv_heads + kv-head) * chunks + chunk.  stamps: device,
+ * 8-byte aligned, at least 4 * max_workgroups entries; max_workgroups must
+ * cover the launch (FD_E_INVAL).  NULL turns it off.  FD_EXEC_KERNELS
+ * profiles only (FD_E_UNSUPPORTED otherwise).
+ */
+fd_status fd_trace_attention(fd_ctx* ctx, uint64_t* stamps, int32_t layer, int32_t max_workgroups);
+
+/*
  * HBM read probe (bench hook): enqueues one kernel that reads `bytes` of
  * device memory at `buf` (16-byte aligned) once with wide loads, `grid`
  * workgroups of 256 threads, and may write to device words sink[0..grid).

@@ -110,3 +110,18 @@ def test_run_beats_churn_and_late_beats(slow_beat):
         assert out["max_ms"][0] == pytest.approx(200.0)
         assert out["p99_ms"][0] == pytest.approx(200.0)
     assert all(p <= 30 for p in ctx.pos)
+
+
+def test_attention_trace_summary_phases():
+    """Stamps in 10 ns ticks: two workgroups, one entering 1 us late."""
+    stamps = [[1000, 1100, 1500, 1520],
+              [1100, 1150, 1400, 1410],
+              [0, 0, 0, 0]]  # a row no workgroup wrote
+    t = bench.attention_trace_summary(stamps, concurrent=2)
+    assert t["workgroups"] == 2
+    assert t["span_us"] == pytest.approx(5.2)
+    assert t["last_entry_us"] == pytest.approx(1.0)
+    assert t["prologue_us"]["max"] == pytest.approx(1.0)
+    assert t["stream_us"]["p50"] == pytest.approx(4.0)
+    assert t["epilogue_us"]["sum"] == pytest.approx(0.3)
+    assert t["busy_frac"] == pytest.approx((5.2 + 3.1) / (5.2 * 2))
