@@ -591,6 +591,31 @@ def summarize_trace(stats_csv, cmd, title):
     return "\n".join(lines) + "\n"
 
 
+# setup kernels of a benchmark run (weight packing, cache prefill, torch's
+# fills and copies, the bandwidth probe): not part of the decode step
+_SETUP = ("pack_kernel", "kv_write_kernel", "read_probe_kernel", "elementwise", "rocclr", "fill_u32")
+
+
+def summarize_launches(trace_csv, cmd, title):
+    """Markdown table of a rocprofv3 --kernel-trace CSV: the decode step's
+    dispatches grouped by kernel and grid size, in first-dispatch order, with
+    their mean and median durations."""
+    rows = _read_csv(trace_csv)
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if any(k in name for k in _SETUP):
+            continue
+        key = (name.split("(")[0].replace("void ", ""), r.get("Grid_Size_X") or r.get("Grid_Size", ""))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = [f"# {title}", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | grid (work-items) | dispatches | mean us | median us |", "|---|---|---|---|---|"]
+    for (name, grid), d in groups.items():
+        d2 = sorted(d)
+        lines.append(f"| `{name}` | {grid} | {len(d)} | {sum(d) / len(d) / 1e3:.2f} | {d2[len(d2) // 2] / 1e3:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,6 +649,8 @@ def main():
                     help="summarise two counter passes of this workload and exit")
     ap.add_argument("--summarize-trace", metavar="STATS_CSV",
                     help="summarise a kernel-trace stats file and exit")
+    ap.add_argument("--summarize-launches", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-launch table of a rocprofv3 kernel trace")
     ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
                     help="summarise a matrix-core counter pass and exit")
     ap.add_argument("--cmd", default="", help="command recorded in a summary")
@@ -633,6 +660,10 @@ def main():
         return
     if args.summarize_mfma:
         print(summarize_mfma(args.summarize_mfma, args.config, args.cmd), end="")
+        return
+    if args.summarize_launches:
+        print(summarize_launches(args.summarize_launches, args.cmd,
+                                 f"Decode-step dispatches, {args.config}"), end="")
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.cmd,

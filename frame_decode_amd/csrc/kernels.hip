@@ -589,12 +589,13 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
 #pragma unroll
         for (int s = 0; s < STG - 1; ++s) load_x(B[s], min(s, nmine - 1));
     } else {
-        // the norm's partial sums are summed first: their loads are few and
-        // short, and issuing them before the weight stream keeps the in-order
-        // load counter from holding the first weights back
-        if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
+        // the first stages are requested before the norm's partial sums, so
+        // the two round trips overlap: the sums (consumed only by the
+        // epilogue) wait for everything issued before them, which the first
+        // product would wait for anyway
 #pragma unroll
         for (int s = 0; s < STG - 1; ++s) load(A[s], B[s], min(s, nmine - 1));
+        if (norm_here) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
     }
     // steady state: every load of a chunk is in range, so the loads are
     // unconditional and the compiler's wait before each product only covers
@@ -860,11 +861,11 @@ __global__ __launch_bounds__(256 * KH, 2) void gemm_ns_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // the norm's partial sums first (few short loads ahead of the stream)
-    if (a.ss_in) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
     // (a ring slot past the end re-reads the last step and is never consumed)
 #pragma unroll
     for (int s = 0; s < STG - 1; ++s) load(A[s], XR[s], min(s, nst - 1));
+    // the norm's partial sums after the first stages: both round trips overlap
+    if (a.ss_in) rstd_phase1(a, mt0 * 16, MTG * 16, s_seg);
     // steady state: every request of a chunk is in range; j0 stays a
     // multiple of STG, so step j0 + s uses ring slot s and LDS slot s % 2
     int j0 = 0;

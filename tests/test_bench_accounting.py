@@ -125,3 +125,21 @@ def test_attention_trace_summary_phases():
     assert t["stream_us"]["p50"] == pytest.approx(4.0)
     assert t["epilogue_us"]["sum"] == pytest.approx(0.3)
     assert t["busy_frac"] == pytest.approx((5.2 + 3.1) / (5.2 * 2))
+
+
+def test_summarize_launches_groups_step_kernels(tmp_path):
+    """Setup kernels are dropped; step kernels group by name and grid."""
+    f = tmp_path / "k.csv"
+    f.write_text(
+        "Kernel_Name,Grid_Size_X,Start_Timestamp,End_Timestamp\n"
+        '"void fd::pack_kernel<1>(fd::PackArgs)",1024,0,5000\n'
+        '"void fd::gemm_kernel<1, 6, 5, 3, 1, 0>(fd::GemmArgs)",65536,100,2100\n'
+        '"void fd::attn_kernel<1, 1, 128, 1>(fd::AttnArgs)",655360,2200,12200\n'
+        '"void fd::gemm_kernel<1, 6, 5, 3, 1, 0>(fd::GemmArgs)",65536,13000,17000\n'
+        '"void fd::gemm_kernel<1, 6, 5, 3, 1, 0>(fd::GemmArgs)",60160,18000,19000\n')
+    out = bench.summarize_launches(str(f), "cmd", "t")
+    rows = [l for l in out.splitlines() if l.startswith("| `")]
+    assert len(rows) == 3
+    assert rows[0].startswith("| `fd::gemm_kernel<1, 6, 5, 3, 1, 0>` | 65536 | 2 | 3.00 |")
+    assert "attn_kernel" in rows[1] and "| 10.00 |" in rows[1]
+    assert "pack_kernel" not in out
