@@ -499,7 +499,7 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_pmc(fetch_csv, write_csv, workload, cmd):
+def summarize_pmc(fetch_csv, write_csv, workload, cmd, counters_path=None):
     """Per-dispatch HBM bytes of the attention kernel from one FETCH_SIZE and
     one WRITE_SIZE pass (KiB per dispatch), each scaled by the counter's
     reading for the 1 GiB calibration copy; updates profiles/counters.json
@@ -509,11 +509,12 @@ def summarize_pmc(fetch_csv, write_csv, workload, cmd):
     def per_kernel(path):
         out = {}
         for r in _read_csv(path):
-            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            key = (r["Kernel_Name"], r.get("Grid_Size", ""))
+            out.setdefault(key, []).append(float(r["Counter_Value"]))
         return out
 
     f, w = per_kernel(fetch_csv), per_kernel(write_csv)
-    copy = [k for k in f if "MulFunctor" in k]
+    copy = [k for k in f if "MulFunctor" in k[0]]
     if not copy:
         raise SystemExit("no calibration copy in the fetch pass")
     cf = max(max(f[k]) for k in copy) * 1024.0
@@ -523,23 +524,32 @@ def summarize_pmc(fetch_csv, write_csv, workload, cmd):
              "```", cmd, "```", "",
              f"Calibration copy ({COPY_BYTES} B read + written): FETCH_SIZE {cf / 1024:.0f} KiB -> "
              f"scale {sf:.3f}; WRITE_SIZE {cw / 1024:.0f} KiB -> scale {sw:.3f}.", "",
-             "| kernel | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | scaled HBM bytes per dispatch |",
-             "|---|---|---|---|---|"]
+             "| kernel | grid (work-items) | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | "
+             "scaled HBM bytes per dispatch |",
+             "|---|---|---|---|---|---|"]
     data = {}
-    path = os.path.join(ROOT, "profiles", "counters.json")
+    path = counters_path or os.path.join(ROOT, "profiles", "counters.json")
     try:
         data = json.load(open(path))
     except (OSError, ValueError):
         data = {}
+    # the workload's own attention launches: one workgroup of 256 per (slot,
+    # kv head, chunk), so the grid is a multiple of slots x kv heads x 256
+    # (a largest-S run in the same process has other grids)
+    import synth
+    cfg = synth.get_config(workload)
+    unit = cfg["max_slots"] * cfg["n_kv_heads"] * 256
+    attn_grid = min((int(g) for (n, g) in f if "attn_kernel" in n and g and int(g) % unit == 0), default=None)
     for k in sorted(f):
-        if not k.startswith("void fd::"):
+        name, grid = k
+        if not name.startswith("void fd::"):
             continue
         fm = float(np.mean(f[k]))
         wm = float(np.mean(w.get(k, [0.0])))
         b = fm * 1024 * sf + wm * 1024 * sw
-        short = k.replace("void fd::", "").split("(")[0]
-        lines.append(f"| `{short}` | {len(f[k])} | {fm:.0f} | {wm:.0f} | {b:.4g} |")
-        if short.startswith("attn_kernel"):
+        short = name.replace("void fd::", "").split("(")[0]
+        lines.append(f"| `{short}` | {grid} | {len(f[k])} | {fm:.0f} | {wm:.0f} | {b:.4g} |")
+        if short.startswith("attn_kernel") and grid and int(grid) == attn_grid:
             data[f"attention@{workload}"] = {"hbm_bytes_per_launch": b,
                                              "fetch_kib": fm, "write_kib": wm,
                                              "scale_fetch": sf, "scale_write": sw,
@@ -575,8 +585,8 @@ def summarize_mfma(csv_path, workload, cmd):
         util = a["busy"] / (a["active"] / 8 * 1024) if a["active"] else float("nan")
         short = name.replace("void fd::", "").split("(")[0]
         lines.append(f"| `{short}` | {a['n']} | {100 * util:.1f}% | {a['mops'] * 512 / a['n']:.3g} |")
-    lines += ["", "The projections are bound by HBM bandwidth (each weight byte is read once per step and "
-              "multiplies 80 session rows), so the matrix cores are expected to idle most of the time."]
+    lines += ["", "MFMA busy: matrix-core busy cycles over every SIMD's GPU-active cycles, per projection "
+              "kernel over all of its dispatches in the run."]
     return "\n".join(lines) + "\n"
 
 

@@ -77,10 +77,11 @@ EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_step_tokens", 
            "fd_profile", "fd_profile_read", "fd_trace_attention", "fd_read_probe", "fd_last_error",
            "fd_status_str"]
 
-FD_N_KINDS = 10
+FD_N_KINDS = 15
 FD_STATIC_SCRATCH_BYTES = 64 << 20
 KIND_NAMES = ["embed", "qkv", "attention", "o_proj", "gate_up", "down", "final", "depth_in",
-              "walk", "head"]
+              "walk", "head", "depth_qkv", "depth_attention", "depth_o_proj", "depth_gate_up",
+              "depth_down"]
 
 
 def config_from_dict(cfg: dict) -> FdConfig:

@@ -195,7 +195,11 @@ hipError_t timed(fd_ctx* c, int kind, hipStream_t st, F&& launch) {
     return e;
 }
 
-enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_O, K_GU, K_DOWN, K_FINAL, K_WIN, K_WALK, K_HEAD };
+// Kinds of fd_profile_read; the depth stack's projections and attention
+// have kinds of their own (K_DQKV.. = K_QKV.. + kDepthKinds)
+enum Kind { K_EMBED = 0, K_QKV, K_ATTN, K_O, K_GU, K_DOWN, K_FINAL, K_WIN, K_WALK, K_HEAD,
+            K_DQKV, K_DATTN, K_DO, K_DGU, K_DDOWN };
+constexpr int kDepthKinds = K_DQKV - K_QKV;
 
 struct CacheRef {
     uint8_t* base;
@@ -213,6 +217,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
     const int wt = pl.wt;
     const float inv_d = 1.0f / (float)d.d;
     const float eps = pl.cfg.rms_eps;
+    const int dk = &sp == &pl.dstack ? kDepthKinds : 0;  // profile kinds of this stack
     int nss = 1;
     hipError_t e = hipSuccess;
     for (int l = 0; l < d.L && e == hipSuccess; ++l) {
@@ -241,7 +246,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         q.y = (float*)Wk(c, pl.ws_qkv);
         q.ld = d.qkv_n();
         q.plane = (uint64_t)pl.Sp * d.qkv_n();
-        e = timed(c, K_QKV, st, [&] { return fd::launch_gemm(q, pl.wkind, sq.R, sq.MTG, sq.grid(), st); });
+        e = timed(c, K_QKV + dk, st, [&] { return fd::launch_gemm(q, pl.wkind, sq.R, sq.MTG, sq.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::AttnArgs at{};
@@ -273,7 +278,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.o_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
         at.early = sp.attn.early;
         at.trace = (&sp == &pl.main && l == c->trace_layer) ? c->trace : nullptr;
-        e = timed(c, K_ATTN, st, [&] {
+        e = timed(c, K_ATTN + dk, st, [&] {
             return fd::launch_attn(at, wt, cache.fp8, d.hd, d.G(), pl.S * d.hkv * sp.attn.n_chunks, st);
         });
         if (e != hipSuccess) break;
@@ -293,7 +298,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         o.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         o.ss_out = (float*)Wk(c, pl.ws_ss_f);
         o.ld = d.d;
-        e = timed(c, K_O, st, [&] { return fd::launch_gemm(o, pl.wkind, so.R, so.MTG, so.grid(), st); });
+        e = timed(c, K_O + dk, st, [&] { return fd::launch_gemm(o, pl.wkind, so.R, so.MTG, so.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::GemmArgs u = g;
@@ -310,7 +315,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         u.h_out = Wk(c, pl.ws_h);
         u.h_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
         u.F = d.f;
-        e = timed(c, K_GU, st, [&] { return fd::launch_gemm(u, pl.wkind, su.R, su.MTG, su.grid(), st); });
+        e = timed(c, K_GU + dk, st, [&] { return fd::launch_gemm(u, pl.wkind, su.R, su.MTG, su.grid(), st); });
         if (e != hipSuccess) break;
 
         fd::GemmArgs dn = g;
@@ -328,7 +333,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         dn.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
         dn.ss_out = (float*)Wk(c, pl.ws_ss_a);
         dn.ld = d.d;
-        e = timed(c, K_DOWN, st, [&] { return fd::launch_gemm(dn, pl.wkind, sd.R, sd.MTG, sd.grid(), st); });
+        e = timed(c, K_DOWN + dk, st, [&] { return fd::launch_gemm(dn, pl.wkind, sd.R, sd.MTG, sd.grid(), st); });
         nss = sd.n_groups;
     }
     *nss_out = nss;

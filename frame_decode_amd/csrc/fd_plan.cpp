@@ -85,7 +85,8 @@ fd_status check_stack(const char* name, int L, int d, int hq, int hkv, int hd, i
 
 // Tuning override for measurements: FD_TUNE="qkv.P=4,o.NG=4,attn.chunks=2"
 // replaces the chosen split-K factor (P) or n-blocks per workgroup (NG) of
-// a projection, or the attention chunk count; "fused=1" (or "o.fused=1")
+// a projection ("d.gu.P=1": of the depth stack's), or the attention chunk
+// count; "fused=1" (or "o.fused=1")
 // makes the last workgroup of each n-group add the k-split partials
 // instead of a reduce launch (measured slower at 80 sessions: 9.76 vs
 // 9.43 ms per step).  Unset in normal use.
@@ -117,14 +118,15 @@ GemmShape tuned(GemmShape g, const char* name, bool ns, int cap) {
     return out;
 }
 
+// pre: prefix of the stack's tuning keys ("" main, "d." depth stack)
 void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8, bool w8,
-                uint64_t& off, bool ns) {
+                uint64_t& off, bool ns, const std::string& pre) {
     sp.dims = dims;
     const int cap = w8 ? kMaxMTG8 : kMaxMTG;
-    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256, cap), "qkv", ns, cap);
-    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256, cap), "o", ns, cap);
-    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256, cap), "gu", ns, cap);
-    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256, cap), "down", ns, cap);
+    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256, cap), (pre + "qkv").c_str(), ns, cap);
+    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256, cap), (pre + "o").c_str(), ns, cap);
+    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256, cap), (pre + "gu").c_str(), ns, cap);
+    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256, cap), (pre + "down").c_str(), ns, cap);
     sp.layers.resize(dims.L);
     auto tiles = [w8](const GemmShape& g) { return packed_matrix_bytes(g, w8); };
     for (int l = 0; l < dims.L; ++l) {
@@ -251,14 +253,14 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     // the row-split projection variant: bf16 weights with two-part
     // activations, launched as kernels (the persistent walk runs gemm_wg)
     const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8;
-    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, off, ns);
+    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, off, ns, "");
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
         p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
         p.w_in = off;
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
-        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, off, false);
+        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, off, false, "d.");
     }
     if (p.head) {
         p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256, p.w8 ? kMaxMTG8 : kMaxMTG);

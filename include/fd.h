@@ -364,10 +364,12 @@ fd_status fd_kv_write(fd_ctx* ctx, int32_t slot, int32_t layer, int32_t t0, int3
  * Kinds: 0 embed, 1 qkv, 2 attention, 3 o-projection, 4 gate/up, 5 down,
  * 6 final norm, 7 depth input projection, 8 the persistent walk of the
  * whole step (FD_EXEC_WALK; then the only step kind launched), 9 the output
- * head of fd_step_tokens (projection and argmax) (FD_N_KINDS = 10).  Timing adds a
- * small gap between launches; headline step times are taken with it off.
+ * head of fd_step_tokens (projection and argmax); 10..14 the depth stack's
+ * qkv, attention, o-projection, gate/up and down (kinds 1..5 then count the
+ * main stack only) (FD_N_KINDS = 15).  Timing adds a small gap between
+ * launches; headline step times are taken with it off.
  */
-#define FD_N_KINDS 10
+#define FD_N_KINDS 15
 fd_status fd_profile(fd_ctx* ctx, int32_t enable);
 fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, int32_t n);
 

@@ -143,3 +143,27 @@ def test_summarize_launches_groups_step_kernels(tmp_path):
     assert rows[0].startswith("| `fd::gemm_kernel<1, 6, 5, 3, 1, 0>` | 65536 | 2 | 3.00 |")
     assert "attn_kernel" in rows[1] and "| 10.00 |" in rows[1]
     assert "pack_kernel" not in out
+
+
+def test_summarize_pmc_separates_grids_and_scales_by_the_copy(tmp_path):
+    """Counter passes scale by the 1 GiB copy's reading; the 80-slot
+    attention launches are kept apart from a largest-S run's."""
+    hdr = "Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+    copy = '"void at::native::elementwise_kernel<MulFunctor<float>>(x)",1024,{c},{v}\n'
+    a80 = '"void fd::attn_kernel<1, 1, 128, 1>(fd::AttnArgs)",655360,{c},{v}\n'
+    a709 = '"void fd::attn_kernel<1, 1, 128, 1>(fd::AttnArgs)",5808128,{c},{v}\n'
+    fetch = tmp_path / "f.csv"
+    write = tmp_path / "w.csv"
+    fetch.write_text(hdr + copy.format(c="FETCH_SIZE", v=524288) + a80.format(c="FETCH_SIZE", v=480000)
+                     + a80.format(c="FETCH_SIZE", v=482000) + a709.format(c="FETCH_SIZE", v=4e6))
+    write.write_text(hdr + copy.format(c="WRITE_SIZE", v=1048576) + a80.format(c="WRITE_SIZE", v=2000)
+                     + a80.format(c="WRITE_SIZE", v=2000) + a709.format(c="WRITE_SIZE", v=9000))
+    cpath = tmp_path / "counters.json"
+    md = bench.summarize_pmc(str(fetch), str(write), "7b_s80_p1499", "cmd", counters_path=str(cpath))
+    import json
+    e = json.loads(cpath.read_text())["attention@7b_s80_p1499"]
+    # copy: 1 GiB read shows as 512 MiB fetched -> fetch scale 2, write scale 1
+    assert e["scale_fetch"] == pytest.approx(2.0) and e["scale_write"] == pytest.approx(1.0)
+    assert e["fetch_kib"] == pytest.approx(481000)
+    assert e["hbm_bytes_per_launch"] == pytest.approx(481000 * 1024 * 2 + 2000 * 1024)
+    assert "| 5808128 |" in md and "| 655360 |" in md

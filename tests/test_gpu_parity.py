@@ -615,6 +615,20 @@ def test_many_slots_row_groups(exec_mode):
     say(f"many slots: worst {worst:.3e}")
 
 
+def test_largest_slot_counts_row_groups():
+    """720 slots (45 row tiles: six m-groups of 8 tiles, the shape of the
+    largest session count that fits in HBM), 700 active sessions at ragged
+    positions, bf16/FP8: every active row matches the oracle, inactive rows
+    are zero.  The six m-groups of each weight tile run on one XCD."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                              d_ffn=1024, max_slots=720, max_context=64)
+    model = synth.Model(cfg, gain_noise=True)
+    rng = np.random.default_rng(23)
+    start = [int(v) for v in rng.integers(0, 60, size=700)]
+    ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 2, tol=2e-2, sentinel=False)
+    say(f"720 slots: worst {worst:.3e}")
+
+
 @pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
 def test_step_with_no_active_session(exec_mode):
     """A step with every slot free writes zero rows, changes no cache byte

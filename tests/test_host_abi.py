@@ -64,6 +64,15 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert sorted(EXPORTS) == syms
 
 
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's sizes and kernel-kind count."""
+    from frame_decode_amd import abi
+    text = open(os.path.join(ROOT, "include", "fd.h")).read()
+    kinds = int(re.search(r"#define FD_N_KINDS (\d+)", text).group(1))
+    assert abi.FD_N_KINDS == kinds == len(abi.KIND_NAMES)
+    assert len(set(abi.KIND_NAMES)) == kinds
+
+
 def test_fd_plan_through_the_product_library():
     """fd_plan is pure host code: callable without a GPU."""
     from frame_decode_amd import fd_plan
