@@ -151,16 +151,21 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     // A single chunk (no merge kernel) when the slot x head pairs alone give
     // about four workgroups per CU; otherwise enough chunks to get there,
     // but no chunk shorter than ~512 KiB of keys and values (per-workgroup
-    // set-up and merge costs would dominate).
+    // set-up and merge costs would dominate).  Chunks are whole wave loads
+    // of positions.
     AttnShape& a = sp.attn;
     a.lpp = kv_fp8 ? dims.hd / 16 : dims.hd / 8;
     const int round = kWaves * (kv_fp8 ? kAttnItersFp8 : kAttnIters) * (64 / a.lpp);
     const int pairs = std::max(1, S * dims.hkv);
     const int64_t window_bytes = (int64_t)dims.T * 2 * dims.hd * (kv_fp8 ? 1 : 4);
     int want = std::max(1, std::min(cdiv(1024, pairs), (int)((window_bytes + (512 << 10) - 1) >> 19)));
+    // Fewer pairs than resident workgroups (two per CU): enough chunks of at
+    // least 256 KiB to fill them in one round (the talker's 56 sessions x 1
+    // kv head: 9 chunks, 504 workgroups, 6.39 against 6.48 ms per step with 7)
+    want = std::max(want, std::min(512 / pairs, (int)(window_bytes >> 18)));
     want = std::max(1, tune_value("attn.chunks", want));
-    a.tc = want == 1 ? cdiv(dims.T, round) * round
-                     : std::max(round, cdiv(dims.T, want) / round * round);
+    const int ppl = 64 / a.lpp;  // positions per wave load
+    a.tc = want == 1 ? cdiv(dims.T, round) * round : cdiv(cdiv(dims.T, want), ppl) * ppl;
     // the merge kernel holds one chunk per thread: at most 256 chunks
     a.tc = std::max(a.tc, cdiv(cdiv(dims.T, 256), round) * round);
     a.n_chunks = cdiv(dims.T, a.tc);

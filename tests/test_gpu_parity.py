@@ -180,10 +180,11 @@ def test_bf16_fp8_ragged_multichunk(exec_mode):
     cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
                               d_ffn=1536, max_slots=9, max_context=700, exec_mode=exec_mode)
     model = synth.Model(cfg, gain_noise=True)
-    start = [0, 1, 255, 256, 257, 300, 511, 690]
+    start = [0, 1, 239, 240, 241, 300, 480, 690]
     # this window is short enough for one chunk by default: ask the plan
-    # for three (it rounds chunks to whole 256-position blocks: three
-    # chunks) so the chunk merge is exercised
+    # for three (it rounds chunks up to whole wave loads of 8 positions:
+    # 240, 240, 220) so the chunk merge is exercised; frames 240 and 480
+    # open a chunk holding only the new entry
     os.environ["FD_TUNE"] = "attn.chunks=3"
     try:
         ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 3, tol=2e-2)
@@ -344,7 +345,7 @@ def test_rolling_window_across_the_wrap(family, exec_mode):
         cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
                                   d_ffn=1024, max_slots=6, max_context=1100, kv_ring=1,
                                   exec_mode=exec_mode)
-        # three chunks of the window (512, 512, 76 positions): the new
+        # three chunks of the window (368, 368, 364 positions): the new
         # entry's position falls in different chunks as the frame advances
         start, tol, tune = [0, 1097, 1099, 1100, 1655, 3000], 2e-2, "attn.chunks=3"
     T = cfg["max_context"]
