@@ -690,7 +690,16 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
             const int i = wave + 4 * j;
             if (i >= NTL) continue;
             f32x4 s = ks == 0 ? v[j] : gp[(size_t)i * 64];
-            for (int q = 1; q < a.P; ++q) s += q == ks ? v[j] : gp[(size_t)q * NTL * 64 + (size_t)i * 64];
+            // eight splits requested at a time, added in split order
+            for (int q0 = 1; q0 < a.P; q0 += 8) {
+                f32x4 w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (q0 + u < a.P && q0 + u != ks) w[u] = gp[(size_t)(q0 + u) * NTL * 64 + (size_t)i * 64];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (q0 + u < a.P) s += q0 + u == ks ? v[j] : w[u];
+            }
             v[j] = s;
         }
     }
@@ -735,7 +744,17 @@ __device__ __forceinline__ void gemm_reduce_wg(const GemmArgs& a, int bid) {
         ti[j] = r < NG ? r * MTG + t : -1;
         const int i = r < NG ? r * MTG + t : t;
         f32x4 s = pp[(size_t)i * 64];
-        for (int q = 1; q < a.P; ++q) s += pp[q * split + (size_t)i * 64];
+        // eight splits requested at a time (one round trip each, not one per
+        // split), added in split order
+        for (int q0 = 1; q0 < a.P; q0 += 8) {
+            f32x4 w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < a.P) w[u] = pp[(size_t)(q0 + u) * split + (size_t)i * 64];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < a.P) s += w[u];
+        }
         v[j] = s;
     }
     __syncthreads();
@@ -1061,7 +1080,9 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     // waits for the append to land.  All loads are issued before any is used.
     constexpr int QPH = D / 4;                  // 4-element quads per head
     constexpr int NQ = ((G + 2) * QPH + 255) / 256;
-    constexpr int PMAX = 4;                     // planes loaded at once (more are added in rounds)
+    // planes loaded at once (more are added in rounds): 8 where the
+    // registers allow (fp32 cache, one query head per kv head)
+    constexpr int PMAX = (FP8 || G > 1) ? 4 : 8;
     __shared__ float s_q[G][D];
     __shared__ float s_kn[D], s_vn[D], s_sn[G];
     __shared__ float s_red[4];
