@@ -15,7 +15,9 @@ Modules:
 * ``decoder`` - the incremental step (per-slot cache, one frame per step,
                 optional depth loop).  Pinned by: equality with the full
                 causal recompute, session isolation, closed-form special
-                cases, float64-vs-float32 agreement.
+                cases, float64-vs-float32 agreement; its bf16 rounding of
+                activations by torch's bfloat16 conversion and a one-layer
+                position-0 closed form.
 * ``full``    - the full causal recompute, pinned against a library-built
                 reference (torch CPU rms_norm, scaled_dot_product_attention,
                 silu and complex-multiplication rotary embedding, float64).
@@ -25,5 +27,5 @@ pages, so no function here is pinned to a printed output value; every pin
 is one of the independent checks above.
 """
 from . import fp8  # noqa: F401
-from .decoder import Oracle, Cache, rmsnorm, rope, rope_table, silu  # noqa: F401
+from .decoder import Oracle, Cache, rmsnorm, rope, rope_table, round_bf16, silu  # noqa: F401
 from .full import forward_full, depth_full  # noqa: F401

@@ -40,7 +40,14 @@ v / sigma (static per-(layer, K|V, kv-head) scales) and every position,
 the new one included, is read back as sigma * decode(code).
 
 Arithmetic is float32 by default (``dtype=np.float64`` for the rounding
-check); inputs and weights are used exactly as given.
+check); inputs and weights are used exactly as given, and activations are
+kept at that precision.  ``act_round="bf16"`` instead rounds every
+projection input of the main stack (the normed rows before QKV and
+gate/up, the attention output before O, the SwiGLU product before down) to
+bf16, the activation type the PersonaPlex page names ("Compressing the
+Temporal KV cache"): the method at its stated precision, whose distance from
+the float64 step measures how far rounding at that precision moves a
+session's output.
 """
 from __future__ import annotations
 
@@ -81,6 +88,16 @@ def rope(x: np.ndarray, pos: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np
     out[..., 0::2] = x0 * c - x1 * s
     out[..., 1::2] = x0 * s + x1 * c
     return out
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Each value rounded once to the nearest bf16 number (8 significant
+    bits, ties to the even one), in x's dtype: with x = m * 2^e and
+    0.5 <= |m| < 1, m becomes a multiple of 2^-8.  (Values in bf16's normal
+    range; zero, infinities and NaN pass through.)"""
+    x = np.asarray(x)
+    m, e = np.frexp(x.astype(np.float64))
+    return np.ldexp(np.round(m * 256.0) / 256.0, e).astype(x.dtype)
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -173,16 +190,18 @@ class Cache:
 
 
 def _stack_step(x, pos, slots, layers, n_layers, shape, eps, cos, sin, cache, kv_scale,
-                g_final, dtype):
+                g_final, dtype, act=lambda v: v):
     """Advance rows x [n][d] (row i = slot slots[i] at new-frame index
-    pos[i]) through ``n_layers`` layers; returns the final-normed output."""
+    pos[i]) through ``n_layers`` layers; returns the final-normed output.
+    ``act`` is applied to every projection input (rounding to the
+    activation type, or nothing)."""
     hq, hkv, hd = shape
     n = x.shape[0]
     x = x.astype(dtype)
     inv_sqrt_d = dtype(1.0 / np.sqrt(hd))
     for l in range(n_layers):
         w = {k: v.astype(dtype) for k, v in layers(l).items()}
-        a = rmsnorm(x, w["g_attn"], eps, dtype)
+        a = act(rmsnorm(x, w["g_attn"], eps, dtype))
         q = (a @ w["wq"].T).reshape(n, hq, hd)
         k = (a @ w["wk"].T).reshape(n, hkv, hd)
         v = (a @ w["wv"].T).reshape(n, hkv, hd)
@@ -203,9 +222,9 @@ def _stack_step(x, pos, slots, layers, n_layers, shape, eps, cos, sin, cache, kv
                 e = np.exp(sc)
                 wts = e / np.sum(e)
                 o[i, h] = wts @ vh
-        x = x + o.reshape(n, hq * hd) @ w["wo"].T
-        b = rmsnorm(x, w["g_ffn"], eps, dtype)
-        hid = silu(b @ w["w_gate"].T) * (b @ w["w_up"].T)
+        x = x + act(o.reshape(n, hq * hd)) @ w["wo"].T
+        b = act(rmsnorm(x, w["g_ffn"], eps, dtype))
+        hid = act(silu(b @ w["w_gate"].T) * (b @ w["w_up"].T))
         x = x + hid @ w["w_down"].T
     return rmsnorm(x, g_final, eps, dtype)
 
@@ -219,10 +238,13 @@ class Oracle:
     depth stack w_in, depth_layer(l), depth_g_final.
     """
 
-    def __init__(self, cfg: dict, model, dtype=np.float32):
+    def __init__(self, cfg: dict, model, dtype=np.float32, act_round: str | None = None):
+        if act_round not in (None, "bf16"):
+            raise ValueError("act_round is None or 'bf16'")
         self.cfg = cfg
         self.model = model
         self.dtype = dtype
+        self.act = round_bf16 if act_round == "bf16" else (lambda v: v)
         self.rolling = bool(cfg.get("kv_ring", 0))
         self.cache = Cache(cfg["n_layers"], cfg["n_kv_heads"], cfg["max_context"],
                            cfg["head_dim"], cfg["kv_dtype"] == "fp8", dtype, rolling=self.rolling)
@@ -256,7 +278,7 @@ class Oracle:
         y = _stack_step(np.asarray(x), pos, slots, self.layer, cfg["n_layers"],
                         (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]), cfg["rms_eps"],
                         self.cos, self.sin, self.cache, self.kv_scale, self.model.g_final,
-                        self.dtype)
+                        self.dtype, self.act)
         if not self.depth:
             return y
         return y, self.depth_loop(y)

@@ -19,7 +19,7 @@ import torch
 import torch.nn.functional as F
 
 import synth
-from oracle import Oracle, forward_full, depth_full, rope, rope_table, fp8
+from oracle import Oracle, forward_full, depth_full, rope, rope_table, round_bf16, fp8
 from oracle.decoder import quantize_rows
 
 
@@ -229,6 +229,71 @@ def test_first_frame_attends_to_itself_only():
     cfg2, m2 = _one_layer(zero=("w_gate", "wq", "wk"))
     y2 = Oracle(cfg2, m2, dtype=np.float64).step([0], e[None], [0])[0]
     assert rel_err(y2, y) < 1e-13
+
+
+def _torch_bf16(v):
+    """bf16 rounding by torch's own conversion (float32 -> bfloat16, nearest
+    even), back to float64; v must hold float32 values."""
+    t = torch.from_numpy(np.asarray(v, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_round_bf16_is_torchs_bfloat16_conversion():
+    """The oracle's bf16 rounding equals torch's float32 -> bfloat16
+    conversion on random values over many binades, on exact ties (low 16
+    bits 0x8000, both parities of the kept bits) and on signed zeros; from
+    float64 it rounds once (1 + 2^-8 + 2^-40 lies above the tie, so it
+    goes up, where rounding through float32 first would land on the tie
+    and go to even)."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(200_000) * np.exp2(rng.integers(-40, 40, 200_000))).astype(np.float32)
+    bits = rng.integers(0, 2**32, 50_000, dtype=np.uint64).astype(np.uint32)
+    ties = ((bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    ties = ties[np.isfinite(ties) & (np.abs(ties) > 1e-37) & (np.abs(ties) < 1e37)]
+    for v in (x, ties, np.array([0.0, -0.0], dtype=np.float32)):
+        got = round_bf16(v).astype(np.float64)
+        assert np.array_equal(got.view(np.uint64), _torch_bf16(v).view(np.uint64))
+    one = np.array([1.0 + 2.0 ** -8 + 2.0 ** -40])
+    assert round_bf16(one)[0] == 1.0 + 2.0 ** -7
+    assert _torch_bf16(one.astype(np.float32))[0] == 1.0
+
+
+def test_bf16_activations_first_frame_closed_form():
+    """act_round="bf16" at p = 0 over one layer with an fp32 cache: the
+    attention output is the new value vector, so the step reduces to
+    a = bf(rms(e) g_attn), x = e + W_o bf(W_v a), b = bf(rms(x) g_ffn),
+    y = rms(x + W_down bf(silu(W_gate b) * (W_up b))) g_final, assembled here
+    in float64 with torch's bf16 conversion (the float32 stage of that
+    conversion lands on no bf16 tie for these inputs).  The rounded step
+    also differs from the unrounded one."""
+    cfg, m = _one_layer()
+    e = synth.frame_input(cfg, 0, 0)
+    y = Oracle(cfg, m, dtype=np.float64, act_round="bf16").step([0], e[None], [0])[0]
+    y_full = Oracle(cfg, m, dtype=np.float64).step([0], e[None], [0])[0]
+    w = {k: np.asarray(v, dtype=np.float64) for k, v in m.layer(0).items()}
+    eps = cfg["rms_eps"]
+    ties = []
+
+    def bf(v):
+        f = v.astype(np.float32)
+        ties.append(int(np.sum((f.view(np.uint32) & np.uint32(0xFFFF)) == 0x8000)))
+        return _torch_bf16(f)
+
+    def rms(v, g):
+        return v / np.sqrt(np.mean(v ** 2) + eps) * g
+
+    e64 = e.astype(np.float64)
+    a = bf(rms(e64, w["g_attn"]))
+    x = e64 + w["wo"] @ bf(w["wv"] @ a)
+    b = bf(rms(x, w["g_ffn"]))
+    g = w["w_gate"] @ b
+    x = x + w["w_down"] @ bf(g / (1.0 + np.exp(-g)) * (w["w_up"] @ b))
+    expect = rms(x, np.asarray(m.g_final, dtype=np.float64))
+    assert sum(ties) == 0
+    assert rel_err(y, expect) < 1e-12
+    assert rel_err(y, y_full) > 1e-5
+    with pytest.raises(ValueError):
+        Oracle(cfg, m, act_round="fp16")
 
 
 @pytest.mark.parametrize("kv", ["f32", "fp8"])
