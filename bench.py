@@ -626,6 +626,23 @@ def summarize_launches(trace_csv, cmd, title):
     return "\n".join(lines) + "\n"
 
 
+def _proj_in(cfg):
+    """Form of the projections' session-row inputs the plan resolves to."""
+    if cfg["act_dtype"] != "bf16":
+        return "f32"
+    p = cfg.get("proj_in", "auto")
+    return ("bf16x2" if cfg.get("exec_mode", 0) else "f16") if p == "auto" else p
+
+
+def _dtype_label(cfg):
+    """Arithmetic types of the step: weights, projection inputs, cache."""
+    if cfg["act_dtype"] != "bf16":
+        return "f32"
+    w = "fp8 weights" if cfg["w_dtype"] == "fp8" else "bf16 weights"
+    x = {"f16": "fp16 projection inputs", "bf16x2": "two-part bf16 projection inputs"}[_proj_in(cfg)]
+    return f"{w}, {x}, {cfg['kv_dtype']} cache, bf16 rows in and out"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -643,6 +660,9 @@ def main():
     ap.add_argument("--active", type=int, default=None, help="active sessions in --beats mode")
     ap.add_argument("--weights", choices=["config", "fp8"], default="config",
                     help="fp8: the library quantises the projection weights to E4M3 with per-row scales")
+    ap.add_argument("--proj-in", choices=["auto", "f16", "bf16x2"], default="auto",
+                    help="bf16 profiles: projection inputs as one fp16 part or two bf16 parts "
+                         "(auto: fp16 in the kernel sequence, two parts in the walk)")
     ap.add_argument("--vocab", type=int, default=0,
                     help="output head over this many tokens (synthetic); steps run fd_step_tokens")
     ap.add_argument("--kv-ring", type=int, default=0,
@@ -696,6 +716,8 @@ def main():
     cfg["vocab"] = args.vocab
     if args.weights == "fp8":
         cfg.update(w_dtype="fp8", act_dtype="bf16")
+    if cfg["act_dtype"] == "bf16":
+        cfg["proj_in"] = args.proj_in
     if args.position is not None:
         pos = args.position
     elif cfg.get("n_active"):
@@ -772,7 +794,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8 weights, bf16 activations"}.get(cfg["w_dtype"], "f32"),
+        "dtype": _dtype_label(cfg),
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) frames, N(0,(0.02*sqrt(d))^2) cache prefill)",
         "config": {"workload": args.config, "layers": cfg["n_layers"], "d_model": cfg["d_model"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} (kv {cfg['n_kv_heads']})",
@@ -780,6 +802,7 @@ def main():
                    "frame_index": pos if pos is not None else "ragged L_i - 1, L_i ~ U{1..max_context}",
                    "weights": cfg["w_dtype"] + (" (per-row scales)" if cfg["w_dtype"] == "fp8" else ""),
                    "cache": cfg["kv_dtype"],
+                   "proj_in": _proj_in(cfg),
                    "exec_mode": "walk" if args.exec_mode else "kernels",
                    "window": "rolling" if args.kv_ring else "fixed",
                    "vocab": args.vocab},

@@ -17,8 +17,10 @@ FD_F32 = 0
 FD_BF16 = 1
 FD_FP8_E4M3 = 2
 FD_EXEC_KERNELS, FD_EXEC_WALK = 0, 1
+FD_PROJ_AUTO, FD_PROJ_F16, FD_PROJ_BF16X2 = 0, 1, 2
 
 _DT = {"f32": FD_F32, "bf16": FD_BF16, "fp8": FD_FP8_E4M3}
+PROJ_IN = {"auto": FD_PROJ_AUTO, "f16": FD_PROJ_F16, "bf16x2": FD_PROJ_BF16X2}
 
 c_i32 = ctypes.c_int32
 c_p = ctypes.c_void_p
@@ -39,6 +41,7 @@ class FdConfig(ctypes.Structure):
         ("depth_steps", c_i32), ("depth_layers", c_i32), ("depth_d", c_i32),
         ("depth_heads", c_i32), ("depth_kv_heads", c_i32), ("depth_head_dim", c_i32),
         ("depth_ffn", c_i32), ("exec_mode", c_i32), ("kv_ring", c_i32), ("vocab", c_i32),
+        ("proj_in", c_i32),
     ]
 
 
@@ -98,6 +101,7 @@ def config_from_dict(cfg: dict) -> FdConfig:
     c.exec_mode = int(cfg.get("exec_mode", 0))
     c.kv_ring = int(cfg.get("kv_ring", 0))
     c.vocab = int(cfg.get("vocab", 0))
+    c.proj_in = PROJ_IN[cfg.get("proj_in", "auto")]
     return c
 
 

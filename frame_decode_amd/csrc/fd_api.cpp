@@ -74,9 +74,10 @@ bool aligned(const void* p) { return p && ((uintptr_t)p % fd::kAlign) == 0; }
 uint8_t* P(const fd_ctx* c, uint64_t off) { return (uint8_t*)c->buf.packed_weights + off; }
 uint8_t* Wk(const fd_ctx* c, uint64_t off) { return c->ws + off; }
 
-// FP8 weights: the per-row scales stored after a matrix's tiles (else null)
+// FP8 or fp16 weight codes: the per-row scales stored after a matrix's
+// tiles (else null)
 const float* wscale(const fd_ctx* c, uint64_t off, const fd::GemmShape& g) {
-    return c->plan.w8 ? (const float*)(P(c, off) + (size_t)g.NB * g.KB * fd::kTileBytes) : nullptr;
+    return c->plan.wkind >= 2 ? (const float*)(P(c, off) + (size_t)g.NB * g.KB * fd::kTileBytes) : nullptr;
 }
 
 int32_t* slot_active(const fd_ctx* c) { return (int32_t*)c->buf.slot_table; }
@@ -89,8 +90,8 @@ fd_status check_layer(const fd_layer_weights& lw) {
     return FD_OK;
 }
 
-// wt: weight format (0 fp32, 1 bf16, 2 FP8 codes of bf16 sources, whose
-// per-row scales go right after the tiles)
+// wt: weight format (0 fp32, 1 bf16, 2 FP8 or 3 fp16 codes of bf16 sources,
+// whose per-row scales go right after the tiles)
 hipError_t pack(const fd::GemmShape& g, int wt, const void* s0, int r0, const void* s1, int r1,
                 const void* s2, int interleave, uint8_t* dst, hipStream_t st) {
     fd::PackArgs a{};
@@ -105,7 +106,8 @@ hipError_t pack(const fd::GemmShape& g, int wt, const void* s0, int r0, const vo
     a.K = g.K;
     a.KB = g.KB;
     a.dst = dst;
-    a.scale = wt == 2 ? (float*)(dst + (size_t)g.NB * g.KB * fd::kTileBytes) : nullptr;
+    a.scale = wt >= 2 ? (float*)(dst + (size_t)g.NB * g.KB * fd::kTileBytes) : nullptr;
+    a.f16 = wt == 3;
     return fd::launch_pack(a, wt, st);
 }
 
@@ -215,6 +217,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
     const fd::Plan& pl = c->plan;
     const fd::StackDims& d = sp.dims;
     const int wt = pl.wt;
+    const bool two = wt && !pl.f16;  // projection inputs as two bf16 parts
     const float inv_d = 1.0f / (float)d.d;
     const float eps = pl.cfg.rms_eps;
     const int dk = &sp == &pl.dstack ? kDepthKinds : 0;  // profile kinds of this stack
@@ -232,6 +235,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         g.inv_d = inv_d;
         g.eps = eps;
         g.ss_stride = pl.nss_max;
+        g.f16 = pl.f16;
 
         // QKV projection: one plane of sums per k-split; the attention
         // kernel adds them and applies the norm, rotary and cache append
@@ -241,7 +245,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         q.wscale = wscale(c, lo.qkv, sp.qkv);
         q.X = Wk(c, pl.ws_xg);
         q.K = sq.K; q.KB = sq.KB; q.NB = sq.NB; q.P = sq.P; q.MG = sq.MG; q.kh = sq.kh;
-        q.X_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
+        q.X_lo = two ? Wk(c, pl.ws_xg_lo) : nullptr;
         q.epi = fd::EPI_PLANES;
         q.y = (float*)Wk(c, pl.ws_qkv);
         q.ld = d.qkv_n();
@@ -275,7 +279,8 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.MT = pl.MT;
         at.part = (float*)Wk(c, pl.ws_apart);
         at.o_out = Wk(c, pl.ws_o);
-        at.o_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
+        at.o_lo = two ? Wk(c, pl.ws_o_lo) : nullptr;
+        at.f16 = pl.f16;
         at.early = sp.attn.early;
         at.trace = (&sp == &pl.main && l == c->trace_layer) ? c->trace : nullptr;
         e = timed(c, K_ATTN + dk, st, [&] {
@@ -288,14 +293,14 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         o.W = P(c, lo.o);
         o.wscale = wscale(c, lo.o, sp.o);
         o.X = Wk(c, pl.ws_o);
-        o.X_lo = wt ? Wk(c, pl.ws_o_lo) : nullptr;
+        o.X_lo = two ? Wk(c, pl.ws_o_lo) : nullptr;
         o.K = so.K; o.KB = so.KB; o.NB = so.NB; o.P = so.P; o.MG = so.MG; o.kh = so.kh;
         o.cnt = so.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         o.epi = fd::EPI_RESID;
         o.x = (float*)Wk(c, pl.ws_x);
         o.xg = Wk(c, pl.ws_xg);
         o.g_next = (const float*)P(c, lo.g_ffn);
-        o.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
+        o.xg_lo = two ? Wk(c, pl.ws_xg_lo) : nullptr;
         o.ss_out = (float*)Wk(c, pl.ws_ss_f);
         o.ld = d.d;
         e = timed(c, K_O + dk, st, [&] { return fd::launch_gemm(o, pl.wkind, so.R, so.MTG, so.grid(), st); });
@@ -311,9 +316,9 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         u.epi = fd::EPI_GU;
         u.ss_in = (const float*)Wk(c, pl.ws_ss_f);
         u.nss = so.n_groups;
-        u.X_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
+        u.X_lo = two ? Wk(c, pl.ws_xg_lo) : nullptr;
         u.h_out = Wk(c, pl.ws_h);
-        u.h_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
+        u.h_lo = two ? Wk(c, pl.ws_h_lo) : nullptr;
         u.F = d.f;
         e = timed(c, K_GU + dk, st, [&] { return fd::launch_gemm(u, pl.wkind, su.R, su.MTG, su.grid(), st); });
         if (e != hipSuccess) break;
@@ -323,14 +328,14 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         dn.W = P(c, lo.down);
         dn.wscale = wscale(c, lo.down, sp.down);
         dn.X = Wk(c, pl.ws_h);
-        dn.X_lo = wt ? Wk(c, pl.ws_h_lo) : nullptr;
+        dn.X_lo = two ? Wk(c, pl.ws_h_lo) : nullptr;
         dn.K = sd.K; dn.KB = sd.KB; dn.NB = sd.NB; dn.P = sd.P; dn.MG = sd.MG; dn.kh = sd.kh;
         dn.cnt = sd.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         dn.epi = fd::EPI_RESID;
         dn.x = (float*)Wk(c, pl.ws_x);
         dn.xg = Wk(c, pl.ws_xg);
         dn.g_next = (const float*)P(c, l + 1 < d.L ? sp.layers[l + 1].g_attn : sp.g_final);
-        dn.xg_lo = wt ? Wk(c, pl.ws_xg_lo) : nullptr;
+        dn.xg_lo = two ? Wk(c, pl.ws_xg_lo) : nullptr;
         dn.ss_out = (float*)Wk(c, pl.ws_ss_a);
         dn.ld = d.d;
         e = timed(c, K_DOWN + dk, st, [&] { return fd::launch_gemm(dn, pl.wkind, sd.R, sd.MTG, sd.grid(), st); });
@@ -726,7 +731,7 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
         e = pack(p.hshape, p.wkind, w->w_head, p.hshape.N, nullptr, 0, nullptr, 0, P(c, p.w_head), s);
     // the output head reads the final-normed rows (and their bf16 low part)
     c->head_x = Wk(c, p.ws_yw);
-    c->head_x_lo = p.wt && p.head ? Wk(c, p.ws_yw_lo) : nullptr;
+    c->head_x_lo = p.wt && !p.f16 && p.head ? Wk(c, p.ws_yw_lo) : nullptr;
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     std::string werr;
     if (e == hipSuccess && p.walk) e = build_walk(c, s, &werr);
@@ -805,7 +810,8 @@ fd_status step_impl(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, v
     em.MT = pl.MT;
     em.x = (float*)Wk(c, pl.ws_x);
     em.xg = Wk(c, pl.ws_xg);
-    em.xg_lo = pl.wt ? Wk(c, pl.ws_xg_lo) : nullptr;
+    em.xg_lo = pl.wt && !pl.f16 ? Wk(c, pl.ws_xg_lo) : nullptr;
+    em.f16 = pl.f16;
     em.g = (const float*)P(c, md.L > 0 ? mp.layers[0].g_attn : mp.g_final);
     em.ss_out = (float*)Wk(c, pl.ws_ss_a);
     em.ss_stride = pl.nss_max;
@@ -831,7 +837,8 @@ fd_status step_impl(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, v
         f.ldy = md.d;
         f.y_off = 0;
         f.yw = pl.depth || pl.head ? Wk(c, pl.ws_yw) : nullptr;
-        f.yw_lo = pl.wt && pl.head ? Wk(c, pl.ws_yw_lo) : nullptr;
+        f.yw_lo = pl.wt && !pl.f16 && pl.head ? Wk(c, pl.ws_yw_lo) : nullptr;
+        f.f16 = pl.f16;
         f.pos = slot_pos(c);
         f.advance = 1;
         e = timed(c, K_FINAL, st, [&] { return fd::launch_final(f, pl.wt, pl.Sp, st); });
@@ -984,6 +991,7 @@ fd_status fd_step_tokens(fd_ctx* c, const void* x_in, void* y_out, void* depth_o
     g.wscale = wscale(c, pl.w_head, h);
     g.X = c->head_x;
     g.X_lo = c->head_x_lo;
+    g.f16 = pl.f16;
     g.K = h.K; g.KB = h.KB; g.NB = h.NB; g.P = h.P; g.MG = h.MG;
     g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
     g.part = (float*)Wk(c, pl.ws_part);

@@ -44,8 +44,11 @@ struct GemmArgs {
     int F;
     // EPI_F32 / EPI_PLANES
     float* y;              // [Sp][ld] (EPI_PLANES: [P][Sp][ld])
-    const float* wscale;   // FP8 weights: [NB*16] output-row scales (the tiles hold codes of w / scale)
+    const float* wscale;   // FP8 or fp16 weight codes: [NB*16] output-row scales (the tiles hold
+                           // codes of w / scale)
     int kh;                // row-split variant: k-halves per workgroup (1 or 2; 0 = 1)
+    int f16;               // 2-byte stacks: X is one fp16 part (weights FP8 or fp16 codes), and
+                           // the epilogue stores xg / h as fp16; else bf16
 };
 
 struct AttnArgs {
@@ -75,6 +78,7 @@ struct AttnArgs {
     float* part;           // [S][hkv][n_chunks][G][hd + 2]
     void* o_out;           // [Sp][hq*hd] activation type, fragment-packed
     void* o_lo;            // optional (bf16): o - o_out, rounded to bf16
+    int f16;               // 2-byte stacks: o_out is fp16 (one part)
     int early;             // request each wave's first block of keys/values before the prologue
     uint64_t* trace;       // optional: 4 device-clock stamps per workgroup [grid][4]
                            // (entry, prologue done, stream done, exit)
@@ -89,6 +93,7 @@ struct EmbedArgs {
     float* x;              // [Sp][d]
     void* xg;              // [Sp][d]
     void* xg_lo;           // optional (bf16): x * g - xg, rounded to bf16
+    int f16;               // 2-byte stacks: xg is fp16 (one part)
     const float* g;        // gain of the first norm
     float* ss_out;         // [Sp][ss_stride], entry 0
     int ss_stride;
@@ -106,6 +111,7 @@ struct FinalArgs {
     int ldy, y_off;
     void* yw;              // [Sp][d] activation-type copy (GEMM input layout), or null
     void* yw_lo;           // optional (bf16): y - yw, rounded to bf16 (output head input)
+    int f16;               // 2-byte stacks: yw is fp16 (one part)
     float* zf;             // [Sp][d] fp32 copy, or null
     int* pos;              // advanced by one for active rows when `advance`
     int advance;
@@ -126,7 +132,9 @@ struct PackArgs {
     int interleave;        // 1: packed row 2j = src0 row j, 2j+1 = src1 row j
     int N, K, KB;
     uint8_t* dst;
-    float* scale;          // FP8 weights: per packed row, max|w| / 448 (1 for a zero row)
+    float* scale;          // FP8 / fp16 weight codes: per packed row, max|w| / 448 or a power of
+                           // two (see row_scale_kernel; 1 for a zero row)
+    int f16;               // 1: fp16 codes (power-of-two scales)
 };
 
 struct KvWriteArgs {

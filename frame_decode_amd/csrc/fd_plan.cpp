@@ -119,8 +119,9 @@ GemmShape tuned(GemmShape g, const char* name, bool ns, int cap) {
 }
 
 // pre: prefix of the stack's tuning keys ("" main, "d." depth stack)
+// scaled: the packed matrices carry per-row scales (FP8 or fp16 codes)
 void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8, bool w8,
-                uint64_t& off, bool ns, const std::string& pre) {
+                bool scaled, uint64_t& off, bool ns, const std::string& pre) {
     sp.dims = dims;
     const int cap = w8 ? kMaxMTG8 : kMaxMTG;
     sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256, cap), (pre + "qkv").c_str(), ns, cap);
@@ -128,7 +129,7 @@ void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int
     sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256, cap), (pre + "gu").c_str(), ns, cap);
     sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256, cap), (pre + "down").c_str(), ns, cap);
     sp.layers.resize(dims.L);
-    auto tiles = [w8](const GemmShape& g) { return packed_matrix_bytes(g, w8); };
+    auto tiles = [scaled](const GemmShape& g) { return packed_matrix_bytes(g, scaled); };
     for (int l = 0; l < dims.L; ++l) {
         LayerOffsets& lo = sp.layers[l];
         lo.qkv = off; off = align_up(off + tiles(sp.qkv));
@@ -197,6 +198,18 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         *err = "vocab must be 0 (no output head) or a multiple of 16 up to 2^20";
         return FD_E_UNSUPPORTED;
     }
+    if (!(c.proj_in == FD_PROJ_AUTO || c.proj_in == FD_PROJ_F16 || c.proj_in == FD_PROJ_BF16X2)) {
+        *err = "proj_in must be FD_PROJ_AUTO, FD_PROJ_F16 or FD_PROJ_BF16X2";
+        return FD_E_UNSUPPORTED;
+    }
+    if (c.proj_in != FD_PROJ_AUTO && c.act_dtype != FD_BF16) {
+        *err = "proj_in applies to FD_BF16 profiles (fp32 profiles take FD_PROJ_AUTO)";
+        return FD_E_UNSUPPORTED;
+    }
+    if (c.proj_in == FD_PROJ_F16 && c.exec_mode == FD_EXEC_WALK) {
+        *err = "FD_EXEC_WALK takes the rows as two bf16 parts (FD_PROJ_BF16X2 or FD_PROJ_AUTO)";
+        return FD_E_UNSUPPORTED;
+    }
     if (c.kv_ring != 0 && c.kv_ring != 1) {
         *err = "kv_ring must be 0 (fixed window) or 1 (rolling window)";
         return FD_E_INVAL;
@@ -223,7 +236,9 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     }
     p.wt = c.act_dtype == FD_BF16 ? 1 : 0;
     p.w8 = c.w_dtype == FD_FP8_E4M3;
-    p.wkind = p.w8 ? 2 : p.wt;
+    p.f16 = p.wt && (c.proj_in == FD_PROJ_F16 ||
+                     (c.proj_in == FD_PROJ_AUTO && c.exec_mode == FD_EXEC_KERNELS));
+    p.wkind = p.w8 ? 2 : (p.f16 ? 3 : p.wt);
     p.act_bytes = p.wt ? 2 : 4;
     p.kv_fp8 = c.kv_dtype == FD_FP8_E4M3;
     p.ring = c.kv_ring == 1;
@@ -257,20 +272,21 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};
     // the row-split projection variant: bf16 weights with two-part
     // activations, launched as kernels (the persistent walk runs gemm_wg)
-    const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8;
-    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, off, ns, "");
+    const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8 && !p.f16;
+    const bool scaled = p.wkind >= 2;
+    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, scaled, off, ns, "");
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
         p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
         p.w_in = off;
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
-        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, off, false, "d.");
+        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, false, off, false, "d.");
     }
     if (p.head) {
         p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256, p.w8 ? kMaxMTG8 : kMaxMTG);
         p.w_head = off;
-        off = align_up(off + packed_matrix_bytes(p.hshape, p.w8));
+        off = align_up(off + packed_matrix_bytes(p.hshape, scaled));
     }
     p.packed_bytes = std::max<uint64_t>(off, kAlign);
 
@@ -296,16 +312,16 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     p.ws_qkv = take(qkv_floats * 4);
     p.ws_o = take(Sp * hqd * p.act_bytes);
     p.ws_h = take(Sp * fmax * p.act_bytes);
-    // bf16 low parts of every projection input: in bf16 stacks each GEMM
+    // bf16 low parts of every projection input (FD_PROJ_BF16X2): each GEMM
     // takes its session rows as two bf16 parts (hi + lo, ~16 significant
-    // bits), so the activations between phases lose no more than fp32
-    // rounding would and the FP8 codes of new cache entries are the ones an
-    // fp32 evaluation picks
-    p.ws_xg_lo = take(p.wt ? Sp * dmax * 2 : 0);
-    p.ws_h_lo = take(p.wt ? Sp * fmax * 2 : 0);
-    p.ws_o_lo = take(p.wt ? Sp * hqd * 2 : 0);
+    // bits), so the activations between phases lose little more than fp32
+    // rounding would
+    const bool two = p.wt && !p.f16;
+    p.ws_xg_lo = take(two ? Sp * dmax * 2 : 0);
+    p.ws_h_lo = take(two ? Sp * fmax * 2 : 0);
+    p.ws_o_lo = take(two ? Sp * hqd * 2 : 0);
     p.ws_yw = take(Sp * m.d * p.act_bytes);
-    p.ws_yw_lo = take(p.wt && p.head ? Sp * m.d * 2 : 0);
+    p.ws_yw_lo = take(two && p.head ? Sp * m.d * 2 : 0);
     p.ws_logits = take(p.head ? Sp * (uint64_t)c.vocab * 4 : 0);
     p.ws_c = take(Sp * std::max(dd, 1) * 4);
     p.ws_z = take(Sp * std::max(dd, 1) * 4);

@@ -85,7 +85,10 @@ struct Plan {
     uint64_t w_head = 0;  // packed offset of the head tiles
     int wt = 0;       // 1 = bf16 activations (bf16 or FP8 weights), 0 = fp32
     bool w8 = false;  // FP8 E4M3 weights with per-output-row scales
-    int wkind = 0;    // weight format of the projections: 0 fp32, 1 bf16, 2 FP8
+    bool f16 = false; // 2-byte stack with fp16 projection inputs (FD_PROJ_F16), else two bf16
+                      // parts (FD_PROJ_BF16X2)
+    int wkind = 0;    // weight format of the projections: 0 fp32, 1 bf16, 2 FP8 codes, 3 fp16 codes
+                      // (2 and 3 with per-row scales after the tiles)
     int act_bytes = 4;
     int kv_fp8 = 0;
     int kv_bytes = 4;
@@ -144,10 +147,10 @@ inline bool walk_shape_compiled(bool wt, bool fp8, int MTG, int hd, int G, int d
 // Bytes per argument block reserved in the walk's argument region.
 constexpr uint64_t kWalkArgSlot = 512;
 
-// Bytes of one projection's packed weights: the tiles, then (FP8) one fp32
-// scale per output row.
-inline uint64_t packed_matrix_bytes(const GemmShape& g, bool w8) {
-    return (uint64_t)g.NB * g.KB * kTileBytes + (w8 ? 4ull * g.NB * 16 : 0);
+// Bytes of one projection's packed weights: the tiles, then (FP8 or fp16
+// codes) one fp32 scale per output row.
+inline uint64_t packed_matrix_bytes(const GemmShape& g, bool scaled) {
+    return (uint64_t)g.NB * g.KB * kTileBytes + (scaled ? 4ull * g.NB * 16 : 0);
 }
 
 // Tile choice for one projection (exposed for tests).

@@ -28,6 +28,7 @@
 namespace fd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -46,6 +47,12 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 }
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> fp16 bits, round to nearest even (magnitudes past 65504 round to
+// +-inf, as the conversion instruction does).
+__device__ __forceinline__ uint32_t f2h(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
 
 // OCP E4M3 encoder: round to nearest, ties to the even mantissa, finite
 // values beyond 448 saturate to +-448, NaN -> 0x7F | sign.  Written from the
@@ -161,6 +168,23 @@ __device__ __forceinline__ void store_split4(void* hi, void* lo, size_t idx, f32
     st2w<CO>((uint32_t*)((uint16_t*)lo + idx), wl);
 }
 
+// Stores 4 consecutive values of a projection input: in 2-byte stacks as
+// two bf16 parts (lo non-null), else as one fp16 part (f16) or one bf16
+// part; in fp32 stacks as they are.
+template <int WT, int CO = 0>
+__device__ __forceinline__ void store_in4(void* p, void* lo, int f16, size_t idx, f32x4 v) {
+    if (WT && lo) {
+        store_split4<CO>(p, lo, idx, v);
+    } else if (WT && f16) {
+        u32x2 w;
+        w[0] = f2h(v[0]) | (f2h(v[1]) << 16);
+        w[1] = f2h(v[2]) | (f2h(v[3]) << 16);
+        st2w<CO>((uint32_t*)((uint16_t*)p + idx), w);
+    } else {
+        store_act4<WT, CO>(p, idx, v);
+    }
+}
+
 template <int CO = 0>
 __device__ __forceinline__ void store_split1(void* hi, void* lo, size_t idx, float v) {
     const uint32_t b = f2bf(v);
@@ -168,11 +192,11 @@ __device__ __forceinline__ void store_split1(void* hi, void* lo, size_t idx, flo
     sth<CO>((uint16_t*)lo + idx, (uint16_t)f2bf(v - bf2f(b)));
 }
 
-// Stores one activation (with its bf16 remainder when lo is given).
+// Stores one projection input value (forms as store_in4).
 template <int WT, int CO = 0>
-__device__ __forceinline__ void store_act1x(void* p, void* lo, size_t idx, float v) {
+__device__ __forceinline__ void store_act1x(void* p, void* lo, int f16, size_t idx, float v) {
     if (WT && lo) store_split1<CO>(p, lo, idx, v);
-    else if (WT) sth<CO>((uint16_t*)p + idx, (uint16_t)f2bf(v));
+    else if (WT) sth<CO>((uint16_t*)p + idx, (uint16_t)(f16 ? f2h(v) : f2bf(v)));
     else st1<CO>((float*)p + idx, v);
 }
 
@@ -241,9 +265,12 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     *(u32x4*)(a.dst + tile * 1024 + (size_t)lane * 16) = v;
 }
 
-// FP8 weights, step 1: per packed row (one workgroup each) the scale
-// max|w| / 448 of its bf16 source row (1 for a row of zeros), so the row's
-// largest entry maps to the largest finite E4M3 magnitude.
+// FP8 or fp16 weight codes, step 1: per packed row (one workgroup each) the
+// scale of its bf16 source row, 1 for a row of zeros.  FP8: max|w| / 448,
+// so the row's largest entry maps to the largest finite E4M3 magnitude.
+// fp16 (a.f16): the power of two 2^(e - 14) with 2^e <= max|w| < 2^(e+1),
+// so the largest entry lands in [2^14, 2^15) and every entry of at least
+// 2^-28 max|w| keeps its 8 significant bits as a normal fp16 number.
 __global__ __launch_bounds__(256) void row_scale_kernel(PackArgs a) {
     const int n = blockIdx.x;
     int row;
@@ -257,8 +284,37 @@ __global__ __launch_bounds__(256) void row_scale_kernel(PackArgs a) {
     __syncthreads();
     if (threadIdx.x == 0) {
         const float mx = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-        a.scale[n] = mx > 0.f ? mx / 448.0f : 1.0f;
+        if (a.f16) {
+            int e = 0;
+            (void)frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+            a.scale[n] = mx > 0.f ? ldexpf(1.0f, max(e - 15, -126)) : 1.0f;
+        } else {
+            a.scale[n] = mx > 0.f ? mx / 448.0f : 1.0f;
+        }
     }
+}
+
+// fp16 weight codes, step 2: the bf16 tile layout of pack_kernel holding
+// fp16(w / scale), exact for entries of at least 2^-28 of the row's largest
+// (the division by a power of two is exact; bf16's 8 significant bits fit
+// fp16's 11).
+__global__ __launch_bounds__(256) void pack16_kernel(PackArgs a) {
+    size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t total = (size_t)(a.N / 16) * a.KB * 64;
+    if (id >= total) return;
+    const int lane = (int)(id & 63);
+    const size_t tile = id >> 6;
+    const int nb = (int)(tile / a.KB), kb = (int)(tile % a.KB);
+    const int n = nb * 16 + (lane & 15);
+    int row;
+    const uint16_t* src = (const uint16_t*)pack_src(a, n, &row) + (size_t)row * a.K;
+    const float inv = 1.0f / a.scale[n];  // a power of two: exact
+    const u32x4 v = *(const u32x4*)(src + kb * 32 + (lane >> 4) * 8);  // 8 bf16
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        w[q] = f2h(bf2f(v[q] & 0xFFFFu) * inv) | (f2h(bf2f(v[q] >> 16) * inv) << 16);
+    *(u32x4*)(a.dst + tile * 1024 + (size_t)lane * 16) = w;
 }
 
 // FP8 weights, step 2: tiles [NB][K/64][64 lanes][16 B] of codes of w / scale.
@@ -317,9 +373,13 @@ struct BFrag<1> { typedef u32x4 T; };
 template <>
 struct BFrag<0> { typedef f32x4 T; };
 
-template <int WT>
+// F16: both operands are fp16 (else bf16) in the 2-byte case.
+template <int WT, int F16 = 0>
 __device__ __forceinline__ f32x4 mfma_tile(u32x4 a, typename BFrag<WT>::T b, f32x4 c) {
-    if constexpr (WT) {
+    if constexpr (WT && F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    } else if constexpr (WT) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     } else {
@@ -415,8 +475,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
         if (a.epi == EPI_RESID) {
             const f32x4 xn = aux0[j] + x;
             st4<CO>(a.x + (size_t)m * a.ld + n, xn);
-            if (WT && a.xg_lo) store_split4<CO>(a.xg, a.xg_lo, xoff<WT>(m, n, a.MT), xn * aux1[j]);
-            else store_act4<WT, CO>(a.xg, xoff<WT>(m, n, a.MT), xn * aux1[j]);
+            store_in4<WT, CO>(a.xg, a.xg_lo, a.f16, xoff<WT>(m, n, a.MT), xn * aux1[j]);
             const float sq = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
 #pragma unroll
             for (int tt = 0; tt < MTG; ++tt)
@@ -427,7 +486,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
             const float h0 = x[0] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x[0])) * x[1];
             const float h1 = x[2] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x[2])) * x[3];
             if (WT) {
-                const uint32_t b0 = f2bf(h0), b1 = f2bf(h1);
+                const uint32_t b0 = a.f16 ? f2h(h0) : f2bf(h0), b1 = a.f16 ? f2h(h1) : f2bf(h1);
                 stw<CO>((uint32_t*)((uint16_t*)a.h_out + xoff<WT>(m, jj, a.MT)), b0 | (b1 << 16));
                 if (a.h_lo)
                     stw<CO>((uint32_t*)((uint16_t*)a.h_lo + xoff<WT>(m, jj, a.MT)),
@@ -469,12 +528,20 @@ struct NoWait {
 // One workgroup task of a projection; s_acc: 4 * NG * MTG * 64 f32x4 of LDS.
 // wait(): called once, before the first read of data an earlier phase wrote
 // (the persistent walk's barrier; NoWait for a kernel launch).
+// SX (2-byte stacks): 0 the session rows as one bf16 part, 1 as two bf16
+// parts (X + X_lo), 2 as one fp16 part with fp16 weight codes (pack16_kernel)
+// whose per-row power-of-two scales multiply the summed tiles.
 // W8: the weight tiles are FP8 codes (16 rows x 64 k per 1 KiB, see
-// pack8_kernel) that each wave converts exactly to bf16 operands for two
-// activation k-tiles; the per-row scales multiply the summed tiles.
+// pack8_kernel) that each wave converts exactly to bf16 (SX 1) or fp16
+// (SX 2) operands for two activation k-tiles; the per-row scales multiply
+// the summed tiles.
 template <int WT, int NG, int MTG, int STG, int SX, int CO, int W8, class Wait>
 __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc_mem, Wait&& wait) {
-    static_assert(!W8 || (WT && SX), "FP8 weights take bf16 activations in two parts");
+    static_assert(!W8 || (WT && SX), "FP8 weights take two bf16 parts or one fp16 part");
+    static_assert(SX <= 1 || WT, "fp16 inputs are a 2-byte stack's");
+    constexpr int TWO = SX == 1;     // second (low) part of every fragment
+    constexpr int F16 = SX == 2;     // fp16 operands
+    constexpr bool SCALED = W8 || F16;  // per-row weight scales
     typedef typename BFrag<WT>::T BT;
     constexpr int NTL = NG * MTG;
     constexpr int OWN = (NTL + 3) / 4;
@@ -501,7 +568,7 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
         wp[r] = (const u32x4*)(a.W + (size_t)min(nb0 + r, a.NB - 1) * a.KB * 1024) + lane;
     // fragment (k-tile kb, m-tile mt) is 1 KiB at ((kb*MT + mt)*64 + lane) * 16 bytes
     const u32x4* xp = (const u32x4*)a.X + (size_t)mt0 * 64 + lane;
-    const u32x4* xlp = SX ? (const u32x4*)a.X_lo + (size_t)mt0 * 64 + lane : xp;
+    const u32x4* xlp = TWO ? (const u32x4*)a.X_lo + (size_t)mt0 * 64 + lane : xp;
     const size_t xk = (size_t)a.MT * 64;
 
     f32x4 acc[NG][MTG];
@@ -513,8 +580,8 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     // STG-deep ring of (weight, activation) fragments in registers: while
     // one k-tile is multiplied, the next STG-1 are in flight, which is what
     // keeps enough bytes outstanding per CU to cover HBM latency.
-    // (SX: B[.][MTG + t] holds the low part of m-tile t)
-    constexpr int NBX = MTG * (1 + SX);     // fragments of one activation k-tile
+    // (TWO: B[.][MTG + t] holds the low part of m-tile t)
+    constexpr int NBX = MTG * (1 + TWO);    // fragments of one activation k-tile
     constexpr int NB_ = NBX * (1 + W8);     // per weight tile (FP8: two activation k-tiles)
     u32x4 A[STG][NG];
     BT B[STG][NB_];
@@ -525,7 +592,7 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
             const size_t kx = (size_t)((1 + W8) * kb + tt) * xk;
 #pragma unroll
             for (int t = 0; t < MTG; ++t) Bd[tt * NBX + t] = __builtin_bit_cast(BT, xp[kx + t * 64]);
-            if constexpr (SX) {
+            if constexpr (TWO) {
 #pragma unroll
                 for (int t = 0; t < MTG; ++t) Bd[tt * NBX + MTG + t] = __builtin_bit_cast(BT, xlp[kx + t * 64]);
             }
@@ -544,34 +611,42 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     // never chain on one accumulator)
     auto mma = [&](u32x4 (&As)[NG], BT (&Bs)[NB_]) {
         if constexpr (W8) {
-            // E4M3 -> bf16 is exact (3 mantissa bits): codes c0..c7 of each
-            // half become one bf16 operand
+            // E4M3 -> bf16 or fp16 is exact (3 mantissa bits, exponents
+            // -9..8): codes c0..c7 of each half become one operand
             u32x4 f[2][NG];
 #pragma unroll
             for (int r = 0; r < NG; ++r)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    f[q >> 1][r][2 * (q & 1)] = __builtin_bit_cast(
-                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(As[r][q], 1.0f, false));
-                    f[q >> 1][r][2 * (q & 1) + 1] = __builtin_bit_cast(
-                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(As[r][q], 1.0f, true));
+                    if constexpr (F16) {
+                        f[q >> 1][r][2 * (q & 1)] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(As[r][q], 1.0f, false));
+                        f[q >> 1][r][2 * (q & 1) + 1] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(As[r][q], 1.0f, true));
+                    } else {
+                        f[q >> 1][r][2 * (q & 1)] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(As[r][q], 1.0f, false));
+                        f[q >> 1][r][2 * (q & 1) + 1] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(As[r][q], 1.0f, true));
+                    }
                 }
 #pragma unroll
-            for (int h = 0; h <= SX; ++h)
+            for (int h = 0; h <= TWO; ++h)
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int r = 0; r < NG; ++r)
 #pragma unroll
                         for (int t = 0; t < MTG; ++t)
-                            acc[r][t] = mfma_tile<WT>(f[tt][r], Bs[tt * NBX + h * MTG + t], acc[r][t]);
+                            acc[r][t] = mfma_tile<WT, F16>(f[tt][r], Bs[tt * NBX + h * MTG + t], acc[r][t]);
         } else {
 #pragma unroll
-            for (int h = 0; h <= SX; ++h)
+            for (int h = 0; h <= TWO; ++h)
 #pragma unroll
                 for (int r = 0; r < NG; ++r)
 #pragma unroll
-                    for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<WT>(As[r], Bs[h * MTG + t], acc[r][t]);
+                    for (int t = 0; t < MTG; ++t)
+                        acc[r][t] = mfma_tile<WT, F16>(As[r], Bs[h * MTG + t], acc[r][t]);
         }
     };
 
@@ -632,7 +707,7 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     for (int j = 0; j < OWN; ++j) {
         const int i = wave + 4 * j;
         if (i < NTL) v[j] = ((s_acc[0][i][lane] + s_acc[1][i][lane]) + s_acc[2][i][lane]) + s_acc[3][i][lane];
-        if constexpr (W8) {  // rows (nb0 + r)*16 + 4*(lane/16) + e: their scales
+        if constexpr (SCALED) {  // rows (nb0 + r)*16 + 4*(lane/16) + e: their scales
             if (i < NTL) {
                 const int r = i / MTG;
                 v[j] *= *(const f32x4*)(a.wscale + min(nb0 + r, a.NB - 1) * 16 + (lane >> 4) * 4);
@@ -1049,7 +1124,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     if (!a.active[s]) {
         if (chunk == 0)
             for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-                store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
+                store_act1x<WT, CO>(a.o_out, a.o_lo, a.f16, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
         stamp_all();
         return;
     }
@@ -1341,7 +1416,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             L += f;
         }
         if (nch == 1) {
-            store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
+            store_act1x<WT, CO>(a.o_out, a.o_lo, a.f16, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
         } else {
             float* part = a.part + (((size_t)(s * a.hkv + g) * a.n_chunks + chunk) * G + h) * (D + 2);
             st1<CO>(part + d, O);
@@ -1406,7 +1481,7 @@ __device__ __forceinline__ void attn_combine_wg(const AttnArgs& a, int bid) {
             for (int u = 0; u < 8; ++u) O += s_w[c + u] * v[u];
         }
         for (; c < nch; ++c) O += s_w[c] * part[c * cs + d];
-        store_act1x<WT, CO>(a.o_out, a.o_lo, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
+        store_act1x<WT, CO>(a.o_out, a.o_lo, a.f16, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * a.vscale[g]);
     }
 }
 
@@ -1436,8 +1511,7 @@ __device__ __forceinline__ void embed_row(const EmbedArgs& a, int m) {
             }
         }
         st4<CO>(a.x + (size_t)m * a.d + i, v);
-        if (WT && a.xg_lo) store_split4<CO>(a.xg, a.xg_lo, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
-        else store_act4<WT, CO>(a.xg, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
+        store_in4<WT, CO>(a.xg, a.xg_lo, a.f16, xoff<WT>(m, i, a.MT), v * *(const f32x4*)(a.g + i));
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
     ss = block_sum_256(ss, red);
@@ -1461,8 +1535,7 @@ __device__ __forceinline__ void final_row(const FinalArgs& a, int m) {
         if (!valid) y = f32x4{0.f, 0.f, 0.f, 0.f};
         if (a.y_out && m < a.S) store_act4<WT, CO>(a.y_out, (size_t)m * a.ldy + a.y_off + i, y);
         if (a.yw) {
-            if (WT && a.yw_lo) store_split4<CO>(a.yw, a.yw_lo, xoff<WT>(m, i, a.MT), y);
-            else store_act4<WT, CO>(a.yw, xoff<WT>(m, i, a.MT), y);
+            store_in4<WT, CO>(a.yw, a.yw_lo, a.f16, xoff<WT>(m, i, a.MT), y);
         }
         if (a.zf) st4<CO>(a.zf + (size_t)m * a.d + i, y);
     }
@@ -1694,14 +1767,16 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int 
 // ---------------------------------------------------------------------------
 // launchers
 
-// wt: 0 fp32, 1 bf16, 2 FP8 codes of bf16 sources with per-row scales
+// wt: 0 fp32, 1 bf16, 2 FP8 codes of bf16 sources with per-row scales,
+// 3 fp16 codes of bf16 sources with per-row power-of-two scales
 hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
     const size_t total = (size_t)(a.N / 16) * a.KB * 64;
     const unsigned blocks = (unsigned)((total + 255) / 256);
-    if (wt == 2) {
-        if (!a.scale) return hipErrorInvalidValue;
+    if (wt == 2 || wt == 3) {
+        if (!a.scale || a.f16 != (wt == 3)) return hipErrorInvalidValue;
         hipLaunchKernelGGL(row_scale_kernel, dim3(a.N), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(pack8_kernel, dim3(blocks), dim3(256), 0, st, a);
+        if (wt == 2) hipLaunchKernelGGL(pack8_kernel, dim3(blocks), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL(pack16_kernel, dim3(blocks), dim3(256), 0, st, a);
     } else if (wt) {
         hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(256), 0, st, a);
     } else {
@@ -1710,20 +1785,53 @@ hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
     return hipGetLastError();
 }
 
-// FP8 weights (bf16 activations in two parts), 4 or 6 blocks per workgroup
+// FP8 weights (session rows as two bf16 parts, or one fp16 part), 4 or 6
+// blocks per workgroup
 template <int NG>
 static hipError_t gemm_w8(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
-    if (!a.X_lo || !a.wscale) return hipErrorInvalidValue;
+    if (!a.wscale || (a.f16 ? a.X_lo != nullptr : !a.X_lo)) return hipErrorInvalidValue;
     switch (MTG) {
 #define FD_G(MT)                                                                                             \
     case MT:                                                                                                 \
-        hipLaunchKernelGGL((gemm_kernel<1, NG, MT, gemm_stages(NG, MT, 1, 1), 1, 1>), dim3(grid), dim3(256), 0, st, a); \
+        if (a.f16)                                                                                           \
+            hipLaunchKernelGGL((gemm_kernel<1, NG, MT, gemm_stages(NG, MT, 0, 1), 2, 1>), dim3(grid), dim3(256), 0, st, a); \
+        else                                                                                                 \
+            hipLaunchKernelGGL((gemm_kernel<1, NG, MT, gemm_stages(NG, MT, 1, 1), 1, 1>), dim3(grid), dim3(256), 0, st, a); \
         if (a.P > 1 && a.epi != EPI_PLANES && !a.cnt)                                                                \
             hipLaunchKernelGGL((gemm_reduce_kernel<1, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a);   \
         break;
         FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
 #undef FD_G
         default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// fp16 weight codes with per-row scales, session rows as one fp16 part: 6
+// blocks per workgroup (up to 5 m-tiles) or 4 (up to 8)
+template <int NG, int MT>
+static void gemm_f16_mt(const GemmArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_kernel<1, NG, MT, gemm_stages(NG, MT), 2>), dim3(grid), dim3(256), 0, st, a);
+    if (a.P > 1 && a.epi != EPI_PLANES && !a.cnt)
+        hipLaunchKernelGGL((gemm_reduce_kernel<1, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a);
+}
+
+template <int NG>
+static hipError_t gemm_f16(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    if (!a.wscale || !a.f16 || a.X_lo) return hipErrorInvalidValue;
+    switch (MTG) {
+        case 1: gemm_f16_mt<NG, 1>(a, grid, st); break;
+        case 2: gemm_f16_mt<NG, 2>(a, grid, st); break;
+        case 3: gemm_f16_mt<NG, 3>(a, grid, st); break;
+        case 4: gemm_f16_mt<NG, 4>(a, grid, st); break;
+        case 5: gemm_f16_mt<NG, 5>(a, grid, st); break;
+        default:
+            if constexpr (NG == 4) {
+                if (MTG == 6) { gemm_f16_mt<4, 6>(a, grid, st); break; }
+                if (MTG == 7) { gemm_f16_mt<4, 7>(a, grid, st); break; }
+                if (MTG == 8) { gemm_f16_mt<4, 8>(a, grid, st); break; }
+            }
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -1792,12 +1900,15 @@ static hipError_t gemm_ns(const GemmArgs& a, int MTG, int grid, hipStream_t st) 
     return hipErrorInvalidValue;
 }
 
-// wt: 0 fp32, 1 bf16, 2 FP8 weights with bf16 activations
+// wt: 0 fp32, 1 bf16, 2 FP8 weight codes (session rows as two bf16 parts,
+// or one fp16 part with a.f16), 3 fp16 weight codes (one fp16 part)
 hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hipStream_t st) {
+    if (a.f16 && wt != 2 && wt != 3) return hipErrorInvalidValue;
     if (wt == 1 && NG == 8) return gemm_ns<2>(a, MTG, grid, st);
     if (wt == 1 && NG == 12) return gemm_ns<3>(a, MTG, grid, st);
     if (wt == 1 && NG == 16) return gemm_ns<4>(a, MTG, grid, st);
     if (wt == 2) return NG == 6 ? gemm_w8<6>(a, MTG, grid, st) : (NG == 4 ? gemm_w8<4>(a, MTG, grid, st) : hipErrorInvalidValue);
+    if (wt == 3) return NG == 6 ? gemm_f16<6>(a, MTG, grid, st) : (NG == 4 ? gemm_f16<4>(a, MTG, grid, st) : hipErrorInvalidValue);
     if (NG == 6) return wt ? gemm_ng<1, 6>(a, MTG, grid, st) : gemm_ng<0, 6>(a, MTG, grid, st);
     if (NG == 4) return wt ? gemm_ng4<1>(a, MTG, grid, st) : gemm_ng4<0>(a, MTG, grid, st);
     return hipErrorInvalidValue;

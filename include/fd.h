@@ -59,6 +59,32 @@ typedef int32_t fd_status;
 #define FD_FP8_E4M3  2 /* OCP E4M3 ("e4m3fn"): bias 7, max 448, one NaN pattern */
 
 /*
+ * Form of the projections' session-row inputs in FD_BF16 profiles (bf16 or
+ * FP8 weights), fd_config.proj_in.  The pages keep weights and activations
+ * in BF16 (PersonaPlex 7B page, "Compressing the Temporal KV cache"); these forms carry the
+ * rows between phases at least that precisely:
+ *   FD_PROJ_F16: each row rounded to fp16 (11 significant bits, nearest
+ *     even).  bf16 weights are held as fp16 codes of w / 2^e with one
+ *     power of two per output row (the row's largest magnitude lands in
+ *     [2^14, 2^15)), exact for every entry of at least 2^-28 of that
+ *     largest; FP8 weight codes convert to fp16 exactly.  The matrix cores
+ *     multiply fp16 operands with fp32 sums, and the row scales multiply
+ *     the sums.  A row value beyond fp16's range (|v| > 65504) makes that
+ *     session's outputs non-finite; other sessions are unaffected.
+ *   FD_PROJ_BF16X2: each row as two bf16 parts, hi = bf16(v) and
+ *     lo = bf16(v - hi) (~16 significant bits), multiplied with the bf16
+ *     (or FP8-decoded) weights: twice the matrix-core work and row loads of
+ *     FD_PROJ_F16.
+ *   FD_PROJ_AUTO: FD_PROJ_F16 with FD_EXEC_KERNELS, FD_PROJ_BF16X2 with
+ *     FD_EXEC_WALK (the only form the persistent walk is compiled for).
+ * FD_F32 profiles take FD_PROJ_AUTO (fp32 rows); other values give
+ * FD_E_UNSUPPORTED, as does FD_PROJ_F16 with FD_EXEC_WALK.
+ */
+#define FD_PROJ_AUTO   0
+#define FD_PROJ_F16    1
+#define FD_PROJ_BF16X2 2
+
+/*
  * Serving profile: the decoder shape, slot capacity and window, fixed for
  * the life of a ctx (Nemotron case study, "Under the hood": profiles are
  * compiled per model, session capacity and context length).
@@ -102,6 +128,7 @@ typedef struct {
     int32_t exec_mode;    /* FD_EXEC_KERNELS (0) or FD_EXEC_WALK (1), see below */
     int32_t kv_ring;      /* 0: fixed window; 1: rolling window, see below */
     int32_t vocab;        /* 0: no output head; else V, a multiple of 16 (<= 2^20): see fd_step_tokens */
+    int32_t proj_in;      /* FD_PROJ_AUTO, FD_PROJ_F16 or FD_PROJ_BF16X2 (see above) */
 } fd_config;
 
 /*

@@ -122,17 +122,21 @@ ROW_SPLIT_7B = ("qkv.NG=12,qkv.P=2,qkv.KH=2,o.NG=8,o.P=1,gu.NG=12,gu.P=2,gu.KH=2
                 "down.NG=12,down.P=11,down.KH=2")
 
 
-@pytest.mark.parametrize("exec_mode,tune", [(0, None), (1, None), (0, ROW_SPLIT_7B)],
-                         ids=["kernels", "walk", "row_split"])
-def test_7b_eight_sessions_at_position_256(model7b, exec_mode, tune, monkeypatch):
+@pytest.mark.parametrize("exec_mode,tune,proj_in",
+                         [(0, None, "auto"), (1, None, "auto"), (0, None, "bf16x2"),
+                          (0, ROW_SPLIT_7B, "bf16x2")],
+                         ids=["kernels", "walk", "kernels_bf16x2", "row_split"])
+def test_7b_eight_sessions_at_position_256(model7b, exec_mode, tune, proj_in, monkeypatch):
     """The 8-session workload in full: 32 layers, every session's cache
     prefilled to 256 positions, new frame at index 256; every row checked
-    (kernel sequence, persistent walk, and the kernel sequence with every
-    projection on the row-split variant)."""
+    (kernel sequence with fp16 and with two-part bf16 projection inputs,
+    persistent walk, and the kernel sequence with every projection on the
+    row-split variant)."""
     if tune:
         monkeypatch.setenv("FD_TUNE", tune)
     cfg = synth.get_config("7b_s8_p256")
     cfg["exec_mode"] = exec_mode
+    cfg["proj_in"] = proj_in
     p0 = cfg["position"]
     say("C2: context")
     ctx = make_context(cfg, model7b)
@@ -203,29 +207,35 @@ def test_7b_eighty_sessions_full_window_sampled(model7b, exec_mode):
 # float64 evaluations differ by 1.6e-2, and a 1e-5 relative perturbation of
 # the input moves the output by 3.9e-2; at position 20 the float32/float64
 # gap is 7.5e-4.  Sessions below SHORT positions are therefore compared with
-# the float64 oracle, and the GPU must be as close to it as the float32
-# oracle is (within a factor 3) or within the tolerance.
+# the float64 oracle, and the GPU must be within the tolerance, or as close
+# to it as the float32 oracle is (within a factor 3), or as close as the
+# float64 oracle with its projection inputs rounded to bf16 (the activation
+# type the PersonaPlex page names, "Compressing the Temporal KV cache"): no
+# less precise than the method at its stated precision.
 SHORT = 16
 
 
-@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
-def test_7b_ragged_with_admission_and_retirement(model7b, exec_mode):
+@pytest.mark.parametrize("exec_mode,proj_in", [(0, "auto"), (0, "bf16x2"), (1, "auto")],
+                         ids=["kernels", "kernels_bf16x2", "walk"])
+def test_7b_ragged_with_admission_and_retirement(model7b, exec_mode, proj_in):
     """The ragged workload: 56 of 80 slots active with seeded lengths
     L_i ~ U{1..1500}, new frame at L_i - 1; then sessions that reached the
     window are retired, new sessions are admitted into the lowest free
     slots at position 0 and one sampled session is freed, over three steps
     with an unchanged launch (kernel sequence, and the whole step as one
-    persistent walk).  Sampled sessions (shortest, longest, one in between,
-    and the admitted ones) are recomputed by the oracle; a short session's
-    margin under its bound (bound / error) and the elementwise error are
-    printed."""
+    persistent walk; projection inputs in fp16 and as two bf16 parts).
+    Sampled sessions (shortest, longest, one in between, and the admitted
+    ones) are recomputed by the oracle; a short session's margin under its
+    bound (bound / error) and the elementwise error are printed."""
     cfg = synth.get_config("7b_ragged_80x56")
     cfg["exec_mode"] = exec_mode
+    cfg["proj_in"] = proj_in
     S = cfg["max_slots"]
     say("C4: context")
     ctx = make_context(cfg, model7b)
     orc = Oracle(cfg, model7b)
     orc64 = Oracle(cfg, model7b, dtype=np.float64)  # sessions with short histories
+    orcb = Oracle(cfg, model7b, dtype=np.float64, act_round="bf16")  # (the pages' activation type)
     act, lengths = synth.ragged_slots(cfg, cfg["n_active"])
     got = ctx.fd_alloc_slots(S)
     assert got == list(range(S))
@@ -241,6 +251,7 @@ def test_7b_ragged_with_admission_and_retirement(model7b, exec_mode):
         if pos[s] < SHORT:
             for l in range(cfg["n_layers"]):
                 orc64.prefill(s, l, synth.prefill_values(cfg, sess[s], l, pos[s]))
+                orcb.prefill(s, l, synth.prefill_values(cfg, sess[s], l, pos[s]))
     _prefill_device(ctx, cfg, [s for s in L if s not in sample], pos, seed=6)
     for s in L:
         ctx.fd_set_position(s, pos[s])
@@ -253,19 +264,24 @@ def test_7b_ragged_with_admission_and_retirement(model7b, exec_mode):
         _check_rows(cfg, yg, active)
         ref = orc.step(tracked, x_np[tracked], [pos[s] for s in tracked])
         short = [s for s in tracked if pos[s] < SHORT]
-        ref64 = {}
+        ref64, refb = {}, {}
         if short:
             r64 = orc64.step(short, x_np[short], [pos[s] for s in short])
             ref64 = dict(zip(short, r64))
+            refb = dict(zip(short, orcb.step(short, x_np[short], [pos[s] for s in short])))
         for i, s in enumerate(tracked):
             e = rel_err_rows(yg[s][None], ref[i][None])
             ee = rel_err_elem(yg[s][None], ref[i][None])
             if s in ref64:
                 e64 = rel_err_rows(yg[s][None], ref64[s][None])
                 cond = rel_err_rows(ref[i][None], ref64[s][None])
-                bound = max(2e-2, 3.0 * cond)
+                cond_b = rel_err_rows(refb[s][None], ref64[s][None])
+                # no farther from the exact step than 3x the float32 oracle,
+                # or than the step at the pages' own activation type (bf16)
+                bound = max(2e-2, 3.0 * cond, cond_b)
                 say(f"  slot {s} (position {pos[s]}): vs float32 oracle {e:.3e} (elementwise {ee:.3e}), "
-                    f"vs float64 {e64:.3e}, float32 oracle vs float64 {cond:.3e}, bound {bound:.3e}, "
+                    f"vs float64 {e64:.3e}, float32 oracle vs float64 {cond:.3e}, "
+                    f"bf16-activation oracle vs float64 {cond_b:.3e}, bound {bound:.3e}, "
                     f"margin {bound / max(e64, 1e-30):.2f}x")
                 assert e64 <= bound, f"step {step} slot {s}"
             else:
@@ -295,6 +311,7 @@ def test_7b_ragged_with_admission_and_retirement(model7b, exec_mode):
             pos[s] = 0
             orc.cache.kv.pop(s, None)  # a new session starts from an empty cache
             orc64.cache.kv.pop(s, None)
+            orcb.cache.kv.pop(s, None)
             assert ctx.fd_slot_state(s) == (1, 0)
         tracked = sorted(tracked + new)
     ctx.fd_destroy()

@@ -172,13 +172,16 @@ def test_tiny_fp32_sixteen_frames(exec_mode):
     _check_cache(ctx, orc, cfg, slots, pos, {s: 0 for s in slots})
 
 
-@pytest.mark.parametrize("exec_mode", [0, 1], ids=["kernels", "walk"])
-def test_bf16_fp8_ragged_multichunk(exec_mode):
+@pytest.mark.parametrize("exec_mode,proj_in", [(0, "auto"), (0, "bf16x2"), (1, "auto")],
+                         ids=["kernels", "kernels_bf16x2", "walk"])
+def test_bf16_fp8_ragged_multichunk(exec_mode, proj_in):
     """bf16 weights/activations, FP8 cache, 7B head geometry (128-dim MHA)
     at reduced width and depth; slots at positions spanning 1..3 attention
-    chunks, one slot left empty; kernel sequence and persistent walk."""
+    chunks, one slot left empty; kernel sequence (projection inputs in fp16,
+    and as two bf16 parts) and persistent walk (two bf16 parts)."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
-                              d_ffn=1536, max_slots=9, max_context=700, exec_mode=exec_mode)
+                              d_ffn=1536, max_slots=9, max_context=700, exec_mode=exec_mode,
+                              proj_in=proj_in)
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 1, 239, 240, 241, 300, 480, 690]
     # this window is short enough for one chunk by default: ask the plan
@@ -203,12 +206,13 @@ ROW_SPLIT_TUNE = ("qkv.NG=12,qkv.P=2,qkv.KH=2,o.NG=8,o.P=1,o.KH=1,gu.NG=16,gu.P=
 
 @pytest.mark.parametrize("max_slots", [9, 40])
 def test_row_split_projections(max_slots):
-    """The row-split projection variant (its waves own different weight
-    rows and share the activations through LDS; one or two k-halves) on
+    """The row-split projection variant (two-part rows; its waves own
+    different weight rows and share the activations through LDS; one or two
+    k-halves) on
     every projection of a reduced 7B-geometry bf16/FP8 stack, with one and
     with three 16-row tiles of sessions: 2e-2, cache indexing bit-exact."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
-                              d_ffn=1536, max_slots=max_slots, max_context=300)
+                              d_ffn=1536, max_slots=max_slots, max_context=300, proj_in="bf16x2")
     model = synth.Model(cfg, gain_noise=True)
     start = [(37 * i) % 290 for i in range(max_slots - 2)]
     os.environ["FD_TUNE"] = ROW_SPLIT_TUNE
@@ -459,15 +463,16 @@ def test_output_head_greedy_tokens(family, exec_mode):
     ctx.fd_destroy()
 
 
-def test_fp8_weights_with_per_row_scales():
+@pytest.mark.parametrize("proj_in", ["f16", "bf16x2"])
+def test_fp8_weights_with_per_row_scales(proj_in):
     """FP8 E4M3 weights quantised by the library from bf16 sources (one
-    scale per output row), bf16 activations, FP8 cache, with the output
-    head: outputs and logits match the oracle running the dequantised
-    weights (2e-2) over three steps; tokens are the first maximum of the
-    GPU's logits."""
+    scale per output row), bf16 activations (projection inputs in fp16, or
+    as two bf16 parts), FP8 cache, with the output head: outputs and logits
+    match the oracle running the dequantised weights (2e-2) over three
+    steps; tokens are the first maximum of the GPU's logits."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
                               d_ffn=1536, max_slots=7, max_context=400, vocab=1024,
-                              w_dtype="fp8", act_dtype="bf16")
+                              w_dtype="fp8", act_dtype="bf16", proj_in=proj_in)
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 1, 100, 255, 256, 390]
     say(f"fp8 weights: slots {start}")
@@ -514,18 +519,19 @@ FP8_SPLITS = {
 }
 
 
-@pytest.mark.parametrize("split", sorted(FP8_SPLITS))
-def test_fp8_weights_eighty_slots(split, monkeypatch):
+@pytest.mark.parametrize("split,proj_in", [("ng4", "auto"), ("ng6", "auto"), ("ng6", "bf16x2")])
+def test_fp8_weights_eighty_slots(split, proj_in, monkeypatch):
     """FP8 weights at 80 slots: five 16-row tiles per m-group (the kernels
     the 80-session FP8-weight step runs), 7B head geometry (MHA, 128-dim
     heads) at reduced width and depth, every projection split over K (QKV
     planes, k-split partial sums with the residual and gate/up epilogues),
     with the output head.  All 80 sessions at positions 0..150 against the
-    oracle running the dequantised weights: outputs and logits 2e-2."""
+    oracle running the dequantised weights: outputs and logits 2e-2
+    (projection inputs in fp16, and as two bf16 parts)."""
     monkeypatch.setenv("FD_TUNE", FP8_SPLITS[split])
     cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=1024, n_heads=8, n_kv_heads=8,
                               d_ffn=2048, max_slots=80, max_context=160, vocab=512,
-                              w_dtype="fp8", act_dtype="bf16")
+                              w_dtype="fp8", act_dtype="bf16", proj_in=proj_in)
     model = synth.Model(cfg, gain_noise=True)
     say(f"fp8 weights, 80 slots, splits {FP8_SPLITS[split]}")
     ctx = make_context(cfg, model)

@@ -143,11 +143,17 @@ def test_walk_mode(host):
     refused for other shapes and for unknown modes."""
     for name in ("tiny", "7b_s8_p256", "7b_s80_p1499", "7b_ragged_80x56", "talker_s56"):
         cfg = synth.get_config(name)
+        if cfg["act_dtype"] == "bf16":  # the walk's form of the projection inputs
+            cfg["proj_in"] = "bf16x2"
         st0, s0 = _plan(host, cfg)
         cfg["exec_mode"] = 1
         st1, s1 = _plan(host, cfg)
         assert st0 == FD_OK and st1 == FD_OK and s1.workspace > s0.workspace, name
         assert s1.packed_weights == s0.packed_weights and s1.kv_arena == s0.kv_arena
+        if cfg["act_dtype"] == "bf16":  # AUTO in the walk is the two-part form
+            cfg["proj_in"] = "auto"
+            st2, s2 = _plan(host, cfg)
+            assert st2 == FD_OK and (s2.packed_weights, s2.workspace) == (s1.packed_weights, s1.workspace)
     # fp32 7B-shaped stack (head_dim 128 without a depth stack): not compiled
     f32 = synth.get_config("7b_s8_p256")
     f32.update(exec_mode=1, w_dtype="f32", act_dtype="f32", kv_dtype="f32")
@@ -163,6 +169,38 @@ def test_walk_mode(host):
     bad = synth.get_config("talker_s56")
     bad["exec_mode"] = 7
     assert _plan(host, bad)[0] == FD_E_INVAL
+
+
+def test_projection_input_forms(host):
+    """bf16 profiles: AUTO is the fp16 form in the kernel sequence; the fp16
+    form stores one fp32 scale per output row after each matrix's tiles and
+    needs no low-part buffers; the walk refuses it; fp32 profiles take only
+    AUTO; unknown values are refused."""
+    from frame_decode_amd import abi
+    text = open(os.path.join(ROOT, "include", "fd.h")).read()
+    for n in ("FD_PROJ_AUTO", "FD_PROJ_F16", "FD_PROJ_BF16X2"):
+        assert int(re.search(rf"#define {n}\s+(\d+)", text).group(1)) == getattr(abi, n)
+    cfg = synth.get_config("7b_s80_p1499")
+    (st_a, a), (st_f, f), (st_b, b) = (_plan(host, dict(cfg, proj_in=v)) for v in ("auto", "f16", "bf16x2"))
+    assert st_a == st_f == st_b == FD_OK
+    assert (a.packed_weights, a.workspace) == (f.packed_weights, f.workspace)
+    rows = 32 * (12288 + 4096 + 22528 + 4096)  # output rows of every projection
+    assert f.packed_weights - b.packed_weights == 4 * rows
+    # low parts of xg, h and o: 80 rows x (4096 + 11264 + 4096) x 2 bytes (an
+    # unused region still takes its 256-byte alignment unit)
+    assert b.workspace - f.workspace == 80 * (4096 + 11264 + 4096) * 2 - 3 * 256
+    assert _plan(host, dict(cfg, proj_in="f16", exec_mode=1))[0] == FD_E_UNSUPPORTED
+    assert _plan(host, dict(cfg, proj_in="bf16x2", exec_mode=1))[0] == FD_OK
+    fp8 = dict(cfg, w_dtype="fp8")
+    assert _plan(host, dict(fp8, proj_in="f16"))[0] == FD_OK
+    assert _plan(host, dict(fp8, proj_in="bf16x2"))[0] == FD_OK
+    tiny = synth.get_config("tiny")
+    assert _plan(host, dict(tiny, proj_in="auto"))[0] == FD_OK
+    for v in ("f16", "bf16x2"):
+        assert _plan(host, dict(tiny, proj_in=v))[0] == FD_E_UNSUPPORTED
+    c = config_from_dict(cfg)
+    c.proj_in = 3
+    assert host.fdh_plan(ctypes.byref(c), ctypes.byref(FdSizes())) == FD_E_UNSUPPORTED
 
 
 def test_gemm_tiling_covers_the_projection(host):
@@ -187,17 +225,19 @@ def _stack_shapes(host, cfg):
 def test_row_split_projection_plan(host, monkeypatch):
     """By default every projection takes the k-split variant (4 or 6 blocks
     per workgroup); a tuning override selects the row-split variant (bf16
-    kernel sequence only: not the persistent walk, FP8 weights or fp32
-    stacks), with two k-halves only where each split's k-tiles divide
-    evenly."""
+    kernel sequence with two-part rows only: not the persistent walk, FP8
+    weights, fp16 rows or fp32 stacks), with two k-halves only where each
+    split's k-tiles divide evenly."""
     monkeypatch.delenv("FD_TUNE", raising=False)
     cfg = synth.get_config("7b_s80_p1499")
+    cfg["proj_in"] = "bf16x2"  # (the variant takes the rows as two bf16 parts)
     sh = _stack_shapes(host, cfg)
     assert all(sh[n][0] in (4, 6) and sh[n][2] == 1 for n in sh)
     assert sh["gu"] == (6, 1, 1, 235)  # 1408 blocks in groups of 6, no k-split
     row_split = "gu.NG=12,gu.P=2,gu.KH=2"
     monkeypatch.setenv("FD_TUNE", row_split)
     assert _stack_shapes(host, cfg)["gu"] == (12, 2, 2, 236)  # 118 n-groups x 2 k-splits
+    assert _stack_shapes(host, dict(cfg, proj_in="f16"))["gu"][0] in (4, 6)
     assert _stack_shapes(host, dict(cfg, exec_mode=1))["gu"][0] in (4, 6)
     assert _stack_shapes(host, dict(cfg, w_dtype="fp8"))["gu"][0] in (4, 6)
     assert _stack_shapes(host, dict(synth.get_config("talker_s56"), exec_mode=0))["gu"][0] in (4, 6)
@@ -315,14 +355,18 @@ def test_device_image_layout(host):
 
 
 def test_output_head_plan(host):
-    """A vocabulary adds exactly the head's tiles to the packed weights;
-    sizes that are not a multiple of 16 are refused."""
+    """A vocabulary adds exactly the head's tiles to the packed weights (and,
+    as fp16 codes, one fp32 scale per row); sizes that are not a multiple of
+    16 are refused."""
     cfg = synth.get_config("7b_s8_p256")
     st0, s0 = _plan(host, cfg)
     cfg["vocab"] = 2048
     st1, s1 = _plan(host, cfg)
     assert st0 == FD_OK and st1 == FD_OK
-    assert s1.packed_weights - s0.packed_weights == 2048 * 4096 * 2
+    assert s1.packed_weights - s0.packed_weights == 2048 * 4096 * 2 + 2048 * 4
+    st2, s2 = _plan(host, dict(cfg, proj_in="bf16x2"))
+    st3, s3 = _plan(host, dict(cfg, proj_in="bf16x2", vocab=0))
+    assert st2 == st3 == FD_OK and s2.packed_weights - s3.packed_weights == 2048 * 4096 * 2
     assert s1.kv_arena == s0.kv_arena and s1.workspace > s0.workspace
     cfg["vocab"] = 2050
     assert _plan(host, cfg)[0] == FD_E_UNSUPPORTED
@@ -332,6 +376,7 @@ def test_fp8_weight_plan(host):
     """FP8 weights: one byte per parameter plus one fp32 scale per output
     row; bf16 activations required; no depth stack and no persistent walk."""
     cfg = synth.get_config("7b_s8_p256")
+    cfg["proj_in"] = "bf16x2"  # (bf16 weights as they are)
     st0, s0 = _plan(host, cfg)
     cfg.update(w_dtype="fp8", act_dtype="bf16")
     st1, s1 = _plan(host, cfg)
