@@ -562,9 +562,10 @@ def summarize_pmc(fetch_csv, write_csv, workload, cmd, counters_path=None):
 def summarize_mfma(csv_path, workload, cmd):
     """Matrix-core use per GEMM dispatch from one counter pass:
     SQ_VALU_MFMA_BUSY_CYCLES / (GPU-active cycles x 1024 SIMDs), and the MFMA
-    flops the dispatch issued (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512).  The
+    flops the dispatch issued (SQ_INSTS_VALU_MFMA_MOPS_* x 512).  The
     collected GRBM_GUI_ACTIVE is the sum over the 8 XCDs, so the GPU-active
-    cycle count is that sum / 8."""
+    cycle count is that sum / 8.  (fp16 products count under
+    SQ_INSTS_VALU_MFMA_MOPS_F16, fp32 ones under ..._F32.)"""
     per = {}
     for r in _read_csv(csv_path):
         key = (r["Kernel_Name"], r["Dispatch_Id"])
@@ -577,7 +578,7 @@ def summarize_mfma(csv_path, workload, cmd):
         a["n"] += 1
         a["busy"] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
         a["active"] += c.get("GRBM_GUI_ACTIVE", 0.0)
-        a["mops"] += c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+        a["mops"] += sum(c.get("SQ_INSTS_VALU_MFMA_MOPS_" + t, 0.0) for t in ("BF16", "F16", "F32"))
     lines = [f"# Matrix-core use of the projections, {workload}", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | dispatches | MFMA busy / (GPU-active cycles x 1024 SIMDs) | MFMA flops per dispatch |",
              "|---|---|---|---|"]
@@ -603,7 +604,8 @@ def summarize_trace(stats_csv, cmd, title):
 
 # setup kernels of a benchmark run (weight packing, cache prefill, torch's
 # fills and copies, the bandwidth probe): not part of the decode step
-_SETUP = ("pack_kernel", "kv_write_kernel", "read_probe_kernel", "elementwise", "rocclr", "fill_u32")
+_SETUP = ("pack_kernel", "pack8_kernel", "pack16_kernel", "row_scale_kernel", "kv_write_kernel",
+          "read_probe_kernel", "elementwise", "rocclr", "fill_u32")
 
 
 def summarize_launches(trace_csv, cmd, title):
