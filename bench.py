@@ -657,6 +657,8 @@ def main():
     ap.add_argument("--runs", type=int, default=3,
                     help="timed repetitions of --steps steps (the first is the headline)")
     ap.add_argument("--no-max-s", action="store_true")
+    ap.add_argument("--no-alt", action="store_true",
+                    help="skip the second timing with two-part bf16 projection inputs")
     ap.add_argument("--beats", type=int, default=0,
                     help="serving-clock mode: beats per run (two steps per 160 ms beat)")
     ap.add_argument("--active", type=int, default=None, help="active sessions in --beats mode")
@@ -774,6 +776,16 @@ def main():
     log(f"step {ms_step:.3f} ms (p50 {p50:.3f}, p99 {p99:.3f}); {value:.0f} session-frames/s; "
         f"step {step_gbs:.0f} GB/s; {dom} {achieved and round(achieved)} GB/s")
 
+    # the same workload with the projection inputs as two bf16 parts, timed
+    # the same way (one run), when the headline ran them as one fp16 part
+    alt = None
+    if _proj_in(cfg) == "f16" and not args.no_alt:
+        log("timing with two-part bf16 projection inputs")
+        ra = run_gpu(dict(cfg, proj_in="bf16x2"), pos, args.steps, args.warmup, runs=1)
+        alt = {"proj_in": "bf16x2", "ms_per_step": ra["total_ms"] / args.steps,
+               "value": ra["active"] * args.steps / (ra["total_ms"] * 1e-3)}
+        log(f"two-part rows: {alt['ms_per_step']:.3f} ms per step")
+
     maxs = None
     if not args.no_max_s and pos is not None:
         maxs = max_sessions(cfg, pos)
@@ -831,6 +843,7 @@ def main():
         **({"attn_trace": r["attn_trace"]} if r["attn_trace"] else {}),
         "kernels": kern_report,
         "max_sessions_80ms": maxs,
+        "proj_in_bf16x2": alt,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

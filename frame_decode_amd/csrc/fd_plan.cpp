@@ -270,9 +270,9 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
 
     uint64_t off = 0;
     StackDims md{c.n_layers, c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.max_context};
-    // the row-split projection variant: bf16 weights with two-part
-    // activations, launched as kernels (the persistent walk runs gemm_wg)
-    const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8 && !p.f16;
+    // the row-split projection variant: bf16 weights (two-part or fp16
+    // rows), launched as kernels (the persistent walk runs gemm_wg)
+    const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8;
     const bool scaled = p.wkind >= 2;
     plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, scaled, off, ns, "");
     if (p.depth) {

@@ -844,12 +844,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny projection, row-split variant (bf16 weights, bf16 activations in
-// two parts).  A workgroup has 4*KH waves: wave w owns weight blocks
+// Skinny projection, row-split variant (bf16 weights with the session rows
+// in two bf16 parts, or fp16 weight codes with the rows in one fp16 part,
+// F16).  A workgroup has 4*KH waves: wave w owns weight blocks
 // (w % 4)*NGW .. +NGW-1 of the workgroup's 4*NGW (its "row group") and, of
 // every KH consecutive k-tiles, the (w / 4)-th (its "k-half").  Each step
-// covers KH k-tiles; their activation fragments (hi and lo parts of the MTG
-// m-tiles) are fetched once per workgroup, each wave loading a share, and
+// covers KH k-tiles; their activation fragments (the MTG m-tiles, hi and lo
+// parts when there are two) are fetched once per workgroup, each wave loading a share, and
 // pass through a double-buffered LDS slot, so a wave's registers hold a
 // ring of its own weight tiles plus only its share of activation fragments.
 // One barrier per step.  With KH = 2 the workgroup runs two waves per SIMD,
@@ -858,17 +859,18 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
 // k-tiles in order; the k-halves are added through LDS in k-half order.
 // k-split partial tiles use the layout, reduce kernel and epilogue of
 // gemm_wg (NG = 4*NGW blocks per n-group).  Requires (KB / P) % KH == 0.
-constexpr int ns_stages(int NGW, int MTG) {
+constexpr int ns_stages(int NGW, int MTG, int F16 = 0) {
     // ring stages: the kernel is built for two waves per SIMD (at most 256
     // registers a lane, the accumulators in ordinary VGPRs)
-    return NGW == 3 ? 4 : 2;
+    return F16 ? 2 : (NGW == 3 ? 4 : 2);
 }
 
-template <int NGW, int MTG, int STG, int KH>
+template <int NGW, int MTG, int STG, int KH, int F16 = 0>
 __global__ __launch_bounds__(256 * KH, 2) void gemm_ns_kernel(GemmArgs a) {
     constexpr int NWV = 4 * KH;             // waves
     constexpr int NG = 4 * NGW;             // blocks of the n-group
-    constexpr int NBX = 2 * MTG;            // activation fragments per k-tile (hi, then lo)
+    constexpr int NPT = F16 ? 1 : 2;        // parts of each activation fragment
+    constexpr int NBX = NPT * MTG;          // activation fragments per k-tile (hi, then lo)
     constexpr int NFX = KH * NBX;           // fragments per step
     constexpr int XPW = (NFX + NWV - 1) / NWV;  // fragments each wave fetches per step
     constexpr int OWN = NGW * MTG;          // output tiles of a row group
@@ -947,11 +949,11 @@ __global__ __launch_bounds__(256 * KH, 2) void gemm_ns_kernel(GemmArgs a) {
         // high parts of every tile first, then low parts: consecutive
         // products never chain on one accumulator
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NPT; ++h)
 #pragma unroll
             for (int r = 0; r < NGW; ++r)
 #pragma unroll
-                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<1>(As[r], B[h * MTG + t], acc[r][t]);
+                for (int t = 0; t < MTG; ++t) acc[r][t] = mfma_tile<1, F16>(As[r], B[h * MTG + t], acc[r][t]);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -1001,12 +1003,16 @@ __global__ __launch_bounds__(256 * KH, 2) void gemm_ns_kernel(GemmArgs a) {
     f32x4 v[OWN];
     int ti[OWN];
 #pragma unroll
-    for (int r = 0; r < NGW; ++r)
+    for (int r = 0; r < NGW; ++r) {
+        // fp16 weight codes: rows (nb0 + rw*NGW + r)*16 + 4*(lane/16) + e take their scales
+        f32x4 sc = f32x4{1.f, 1.f, 1.f, 1.f};
+        if constexpr (F16) sc = *(const f32x4*)(a.wscale + min(nb0 + rw * NGW + r, a.NB - 1) * 16 + (lane >> 4) * 4);
 #pragma unroll
         for (int t = 0; t < MTG; ++t) {
-            v[r * MTG + t] = acc[r][t];
+            v[r * MTG + t] = F16 ? acc[r][t] * sc : acc[r][t];
             ti[r * MTG + t] = kh == 0 ? (rw * NGW + r) * MTG + t : -1;  // k-half 0 finishes the tiles
         }
+    }
     if (a.epi == EPI_PLANES) {
         // each split writes its own plane; the consumer adds them
         if (kh > 0) return;
@@ -1874,15 +1880,20 @@ static hipError_t gemm_ng4(const GemmArgs& a, int MTG, int grid, hipStream_t st)
     return hipGetLastError();
 }
 
-// Row-split variant (bf16 weights, two-part activations, reduce launch for
-// k-splits): NGW blocks per row group, 4*NGW per workgroup, a.kh k-halves
+// Row-split variant (bf16 weights with two-part rows, or fp16 weight codes
+// with one fp16 part; reduce launch for k-splits): NGW blocks per row
+// group, 4*NGW per workgroup, a.kh k-halves
 template <int NGW, int KH>
 static hipError_t gemm_ns_kh(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
-    if (!a.X_lo || a.cnt || a.P < 1 || a.KB % a.P || (a.KB / a.P) % KH) return hipErrorInvalidValue;
+    if (a.cnt || a.P < 1 || a.KB % a.P || (a.KB / a.P) % KH) return hipErrorInvalidValue;
+    if (a.f16 ? (a.X_lo || !a.wscale) : (!a.X_lo || a.wscale)) return hipErrorInvalidValue;
     switch (MTG) {
 #define FD_G(MT)                                                                                          \
     case MT:                                                                                              \
-        hipLaunchKernelGGL((gemm_ns_kernel<NGW, MT, ns_stages(NGW, MT), KH>), dim3(grid), dim3(256 * KH), 0, st, a); \
+        if (a.f16)                                                                                        \
+            hipLaunchKernelGGL((gemm_ns_kernel<NGW, MT, ns_stages(NGW, MT, 1), KH, 1>), dim3(grid), dim3(256 * KH), 0, st, a); \
+        else                                                                                              \
+            hipLaunchKernelGGL((gemm_ns_kernel<NGW, MT, ns_stages(NGW, MT), KH>), dim3(grid), dim3(256 * KH), 0, st, a); \
         if (a.P > 1 && a.epi != EPI_PLANES)                                                               \
             hipLaunchKernelGGL((gemm_reduce_kernel<1, 4 * NGW, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
         break;
@@ -1904,9 +1915,9 @@ static hipError_t gemm_ns(const GemmArgs& a, int MTG, int grid, hipStream_t st) 
 // or one fp16 part with a.f16), 3 fp16 weight codes (one fp16 part)
 hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hipStream_t st) {
     if (a.f16 && wt != 2 && wt != 3) return hipErrorInvalidValue;
-    if (wt == 1 && NG == 8) return gemm_ns<2>(a, MTG, grid, st);
-    if (wt == 1 && NG == 12) return gemm_ns<3>(a, MTG, grid, st);
-    if (wt == 1 && NG == 16) return gemm_ns<4>(a, MTG, grid, st);
+    if ((wt == 1 || wt == 3) && NG == 8) return gemm_ns<2>(a, MTG, grid, st);
+    if ((wt == 1 || wt == 3) && NG == 12) return gemm_ns<3>(a, MTG, grid, st);
+    if ((wt == 1 || wt == 3) && NG == 16) return gemm_ns<4>(a, MTG, grid, st);
     if (wt == 2) return NG == 6 ? gemm_w8<6>(a, MTG, grid, st) : (NG == 4 ? gemm_w8<4>(a, MTG, grid, st) : hipErrorInvalidValue);
     if (wt == 3) return NG == 6 ? gemm_f16<6>(a, MTG, grid, st) : (NG == 4 ? gemm_f16<4>(a, MTG, grid, st) : hipErrorInvalidValue);
     if (NG == 6) return wt ? gemm_ng<1, 6>(a, MTG, grid, st) : gemm_ng<0, 6>(a, MTG, grid, st);

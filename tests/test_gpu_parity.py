@@ -204,15 +204,15 @@ ROW_SPLIT_TUNE = ("qkv.NG=12,qkv.P=2,qkv.KH=2,o.NG=8,o.P=1,o.KH=1,gu.NG=16,gu.P=
                   "down.NG=12,down.P=1,down.KH=2")
 
 
-@pytest.mark.parametrize("max_slots", [9, 40])
-def test_row_split_projections(max_slots):
-    """The row-split projection variant (two-part rows; its waves own
+@pytest.mark.parametrize("max_slots,proj_in", [(9, "bf16x2"), (40, "bf16x2"), (9, "f16"), (40, "f16")])
+def test_row_split_projections(max_slots, proj_in):
+    """The row-split projection variant (two-part or fp16 rows; its waves own
     different weight rows and share the activations through LDS; one or two
     k-halves) on
     every projection of a reduced 7B-geometry bf16/FP8 stack, with one and
     with three 16-row tiles of sessions: 2e-2, cache indexing bit-exact."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
-                              d_ffn=1536, max_slots=max_slots, max_context=300, proj_in="bf16x2")
+                              d_ffn=1536, max_slots=max_slots, max_context=300, proj_in=proj_in)
     model = synth.Model(cfg, gain_noise=True)
     start = [(37 * i) % 290 for i in range(max_slots - 2)]
     os.environ["FD_TUNE"] = ROW_SPLIT_TUNE

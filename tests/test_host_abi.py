@@ -225,9 +225,9 @@ def _stack_shapes(host, cfg):
 def test_row_split_projection_plan(host, monkeypatch):
     """By default every projection takes the k-split variant (4 or 6 blocks
     per workgroup); a tuning override selects the row-split variant (bf16
-    kernel sequence with two-part rows only: not the persistent walk, FP8
-    weights, fp16 rows or fp32 stacks), with two k-halves only where each
-    split's k-tiles divide evenly."""
+    weights in the kernel sequence, two-part or fp16 rows: not the
+    persistent walk, FP8 weights or fp32 stacks), with two k-halves only
+    where each split's k-tiles divide evenly."""
     monkeypatch.delenv("FD_TUNE", raising=False)
     cfg = synth.get_config("7b_s80_p1499")
     cfg["proj_in"] = "bf16x2"  # (the variant takes the rows as two bf16 parts)
@@ -237,7 +237,7 @@ def test_row_split_projection_plan(host, monkeypatch):
     row_split = "gu.NG=12,gu.P=2,gu.KH=2"
     monkeypatch.setenv("FD_TUNE", row_split)
     assert _stack_shapes(host, cfg)["gu"] == (12, 2, 2, 236)  # 118 n-groups x 2 k-splits
-    assert _stack_shapes(host, dict(cfg, proj_in="f16"))["gu"][0] in (4, 6)
+    assert _stack_shapes(host, dict(cfg, proj_in="f16"))["gu"] == (12, 2, 2, 236)  # fp16 rows too
     assert _stack_shapes(host, dict(cfg, exec_mode=1))["gu"][0] in (4, 6)
     assert _stack_shapes(host, dict(cfg, w_dtype="fp8"))["gu"][0] in (4, 6)
     assert _stack_shapes(host, dict(synth.get_config("talker_s56"), exec_mode=0))["gu"][0] in (4, 6)
