@@ -316,6 +316,40 @@ def test_deterministic_and_isolated(exec_mode):
     check(np.array_equal(outs[0][1:5], outs[2][1:5]), "np.array_equal(outs[0][1:5], outs[2][1:5])")
 
 
+@pytest.mark.parametrize("proj_in", ["f16", "bf16x2"])
+def test_row_beyond_fp16_range_stays_in_its_session(proj_in):
+    """A session whose frame is scaled by 1e6 (finite in bf16, beyond fp16's
+    65504 once it is a projection input): with fp16 rows its own output row
+    is non-finite, with two bf16 parts it is finite; either way every other
+    session's row is bit-identical to the run without it."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=512, n_heads=4, n_kv_heads=4,
+                              d_ffn=1024, max_slots=6, max_context=400, proj_in=proj_in)
+    model = synth.Model(cfg, gain_noise=True)
+    say(f"fp16 range: {proj_in}")
+    ctx = make_context(cfg, model)
+    slots = ctx.fd_alloc_slots(6)
+    for s in slots:
+        for l in range(cfg["n_layers"]):
+            ctx.fd_kv_write(s, l, 0, torch.from_numpy(synth.prefill_values(cfg, s, l, 350)).cuda())
+    outs = []
+    for big in (False, True):
+        for s in slots:
+            ctx.fd_set_position(s, 350)
+        _, x = rows_input(cfg, {s: s for s in slots}, {s: 350 for s in slots})
+        if big:
+            x[2] = x[2] * 1e6
+        y = torch.empty_like(x)
+        ctx.fd_step(x, y)
+        ctx.fd_sync()
+        outs.append(to_np(y))
+    rest = [s for s in slots if s != 2]
+    check(np.array_equal(outs[0][rest], outs[1][rest]), "another session's row changed")
+    check(bool(np.all(np.isfinite(outs[0]))), "the plain run must be finite")
+    finite = bool(np.all(np.isfinite(outs[1][2])))
+    check(finite == (proj_in == "bf16x2"), f"scaled session finite: {finite}")
+    ctx.fd_destroy()
+
+
 def _prefill_rolling(ctx, orc, cfg, s, session, p):
     """Fill the window before frame p (frames max(0, p-T+1)..p-1) with
     seeded values: the oracle at their absolute frame indices, the GPU at
