@@ -1127,22 +1127,55 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
         stamp_all();
         return;
     }
-    if (!a.active[s]) {
-        if (chunk == 0)
-            for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-                store_act1x<WT, CO>(a.o_out, a.o_lo, a.f16, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
-        stamp_all();
-        return;
-    }
+    constexpr int QPH = D / 4;                  // 4-element quads per head
+    constexpr int NQ = ((G + 2) * QPH + 255) / 256;
+    // planes loaded at once (more are added in rounds): 8 where the
+    // registers allow (fp32 cache, one query head per kv head)
+    constexpr int PMAX = (FP8 || G > 1) ? 4 : 8;
+    const int nall = (G + 2) * QPH;
+    // The row's norm partial sums and the first PMAX k-split planes of its
+    // q, k and v quads, requested without a branch: quads past the head
+    // re-read the last one, splits past P the last plane, and what is not
+    // needed is masked where it is used.  They depend only on (slot, head):
+    // a kernel launch requests them with the slot's state (one round trip);
+    // the persistent walk after its barrier wait (an earlier phase wrote
+    // them).
+    float ssl = 0.f;
+    f32x4 pv[NQ][PMAX];
+    const float* srcq[NQ];
+    auto request_rows = [&]() {
+        ssl = a.ss_in[(size_t)s * a.ss_stride + min((int)threadIdx.x, a.nss - 1)];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int idx = min((int)threadIdx.x + 256 * k, nall - 1);
+            const int hh = idx / QPH, d0 = (idx - hh * QPH) * 4;
+            const int col = hh < G ? (g * G + hh) * D + d0 : (a.hq + (hh - G) * a.hkv + g) * D + d0;
+            srcq[k] = a.qkv + (size_t)s * a.nqkv + col;
+#pragma unroll
+            for (int q = 0; q < PMAX; ++q) pv[k][q] = *(const f32x4*)(srcq[k] + (size_t)min(q, a.P - 1) * a.plane);
+        }
+    };
+    // the slot's state and this layer's per-head scales in one round trip
+    // (every load unconditional, so none waits for another)
+    const int act = a.active[s];
+    const int pos_s = a.pos[s];
+    const float qsc = a.qscale[g];
+    const float sig_k = a.kvsig[g], sig_v = a.kvsig[a.hkv + g];
+    if constexpr (!CO) request_rows();
+    __builtin_amdgcn_sched_barrier(0);  // (all requested before any is used)
     // frame index p of the new entry; n cache positions attended; the new
     // entry goes to cache position `hole` (p itself, or p mod T with a
     // rolling window, where positions 0..T-1 then hold the last T frames)
-    const int pin = max(a.pos_override >= 0 ? a.pos_override : a.pos[s], 0);
+    const int pin = max(a.pos_override >= 0 ? a.pos_override : pos_s, 0);
     const int p = a.ring ? pin : min(pin, a.T - 1);
     const int n = a.ring ? min(p + 1, a.T) : p + 1;
     const int hole = a.ring ? p % a.T : p;
     const int nch = (n + a.tc - 1) / a.tc;
-    if (chunk >= nch) {
+    // (both values tested together, so both loads are issued before the wait)
+    if (!((act != 0) & (chunk < nch))) {
+        if (!act && chunk == 0)
+            for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+                store_act1x<WT, CO>(a.o_out, a.o_lo, a.f16, xoff<WT>(s, g * G * D + i, a.MT), 0.f);
         stamp_all();
         return;
     }
@@ -1158,12 +1191,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     // q.  The new k, v are appended to the cache (FP8: code(value / sigma))
     // and kept, as the cache will hold them (decoded codes), in LDS: the
     // streaming loop skips position p and the merge adds it, so nothing
-    // waits for the append to land.  All loads are issued before any is used.
-    constexpr int QPH = D / 4;                  // 4-element quads per head
-    constexpr int NQ = ((G + 2) * QPH + 255) / 256;
-    // planes loaded at once (more are added in rounds): 8 where the
-    // registers allow (fp32 cache, one query head per kv head)
-    constexpr int PMAX = (FP8 || G > 1) ? 4 : 8;
+    // waits for the append to land.
     __shared__ float s_q[G][D];
     __shared__ float s_kn[D], s_vn[D], s_sn[G];
     __shared__ float s_red[4];
@@ -1204,38 +1232,56 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
         load_blk(rk, kbase, base);
         load_blk(rv, vbase, base);
     }
-    if constexpr (CO) wait();
+    if constexpr (CO) {
+        wait();
+        request_rows();
+    }
 
     const int nquad = (own_new ? G + 2 : G) * QPH;
-    const float ssv = threadIdx.x < a.nss ? a.ss_in[(size_t)s * a.ss_stride + threadIdx.x] : 0.f;
+    const float ssv = (int)threadIdx.x < a.nss ? ssl : 0.f;
     float ssv2 = 0.f;
     for (int i = threadIdx.x + 256; i < a.nss; i += 256) ssv2 += a.ss_in[(size_t)s * a.ss_stride + i];
+    // the rotary factors of frame p (the row clamped into the table);
+    // further k-splits, where there are more than PMAX, are added in rounds
+    const int prow = min(p, a.T - 1);
+    // rolling window past the table: the angles in double precision,
+    // before the requests (a branch between a request and its use would
+    // let the compiler move the request behind the other round trip)
+    f32x4 cr[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) cr[k] = f32x4{1.f, 0.f, 1.f, 0.f};
+    if (p >= a.T) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int idx = min((int)threadIdx.x + 256 * k, nall - 1);
+            const int d0 = (idx - (idx / QPH) * QPH) * 4;
+            const double a0 = (double)p * a.rope_theta[d0 / 2], a1 = (double)p * a.rope_theta[d0 / 2 + 1];
+            cr[k] = f32x4{(float)cos(a0), (float)sin(a0), (float)cos(a1), (float)sin(a1)};
+        }
+    }
     f32x4 qs[NQ], cs[NQ];
 #pragma unroll
     for (int k = 0; k < NQ; ++k) {
-        const int idx = threadIdx.x + 256 * k;
+        const int idx = min((int)threadIdx.x + 256 * k, nall - 1);
+        const int d0 = (idx - (idx / QPH) * QPH) * 4;
+        cs[k] = *(const f32x4*)(a.rope + ((size_t)prow * (D / 2) + d0 / 2) * 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        cs[k] = p >= a.T ? cr[k] : cs[k];
         qs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        cs[k] = f32x4{1.f, 0.f, 1.f, 0.f};
-        if (idx < nquad) {
-            const int hh = idx / QPH, d0 = (idx - hh * QPH) * 4;
-            const int col = hh < G ? (g * G + hh) * D + d0 : (a.hq + (hh - G) * a.hkv + g) * D + d0;
-            const float* src = a.qkv + (size_t)s * a.nqkv + col;
-            if (hh <= G) {
-                if (p < a.T) {
-                    cs[k] = *(const f32x4*)(a.rope + ((size_t)p * (D / 2) + d0 / 2) * 2);
-                } else {  // rolling window past the table: the angles in double precision
-                    const double a0 = (double)p * a.rope_theta[d0 / 2], a1 = (double)p * a.rope_theta[d0 / 2 + 1];
-                    cs[k] = f32x4{(float)cos(a0), (float)sin(a0), (float)cos(a1), (float)sin(a1)};
-                }
-            }
-            for (int q0 = 0; q0 < a.P; q0 += PMAX) {
-                f32x4 pv[PMAX];
+#pragma unroll
+        for (int q = 0; q < PMAX; ++q) qs[k] += q < a.P ? pv[k][q] : f32x4{0.f, 0.f, 0.f, 0.f};
+        if ((int)threadIdx.x + 256 * k < nquad) {
+            for (int q0 = PMAX; q0 < a.P; q0 += PMAX) {
+                f32x4 pw[PMAX];
 #pragma unroll
                 for (int q = 0; q < PMAX; ++q)
-                    pv[q] = q0 + q < a.P ? *(const f32x4*)(src + (size_t)(q0 + q) * a.plane)
+                    pw[q] = q0 + q < a.P ? *(const f32x4*)(srcq[k] + (size_t)(q0 + q) * a.plane)
                                          : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < PMAX; ++q) qs[k] += pv[q];
+                for (int q = 0; q < PMAX; ++q) qs[k] += pw[q];
             }
         }
     }
@@ -1255,7 +1301,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             x = w;
         }
         if (hh < G) {
-            x *= a.qscale[g];
+            x *= qsc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) s_q[hh][d0 + e] = x[e];
         } else {
@@ -1263,7 +1309,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             uint8_t* dst = (kv ? vbase : kbase) + (size_t)hole * a.pos_stride;
             float* keep = kv ? s_vn : s_kn;
             if (FP8) {
-                const float sg = a.kvsig[kv * a.hkv + g];
+                const float sg = kv ? sig_v : sig_k;
                 const uint32_t w = enc_e4m3(x[0] / sg) | (enc_e4m3(x[1] / sg) << 8) |
                                    (enc_e4m3(x[2] / sg) << 16) | (enc_e4m3(x[3] / sg) << 24);
                 stw<CO>((uint32_t*)(dst + d0), w);
