@@ -431,9 +431,31 @@ __device__ __forceinline__ void rstd_phase2(const GemmArgs& a, int rows, const f
 // + lane%16.  Every load a tile needs (positions via LDS, rotary factors,
 // residual rows, gains) is issued for all owned tiles before any result is
 // stored, so the tiles' latencies overlap instead of adding up.
+// Requests the residual rows and gains EPI_RESID needs for the owned tiles
+// ti (gemm_finish takes them instead of loading them itself), so a caller
+// can issue them together with its own loads.  Tiles not stored re-read a
+// valid row and column.
+template <int NG, int MTG, int OWN>
+__device__ __forceinline__ void finish_aux(const GemmArgs& a, const int* ti, int ng, int mt0, f32x4* aux0,
+                                           f32x4* aux1) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+        const int i = min(ti[j] < 0 ? 0 : ti[j], NG * MTG - 1);
+        const int r = i / MTG, t = i - (i / MTG) * MTG;
+        const int m = mt0 * 16 + t * 16 + (lane & 15);
+        const int n = (min(ng * NG + r, a.NB - 1)) * 16 + (lane >> 4) * 4;
+        aux0[j] = *(const f32x4*)((a.x_src ? a.x_src : a.x) + (size_t)m * a.ld + n);
+        aux1[j] = *(const f32x4*)(a.g_next + n);
+    }
+}
+
+// pre0/pre1: the EPI_RESID operands already requested by finish_aux, or
+// null (loaded here).
 template <int WT, int NG, int MTG, int NWV, int OWN, int CO>
 __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, const int* ti, int ng,
-                                            int mt0, int t_lo, int t_hi, const float* s_rstd) {
+                                            int mt0, int t_lo, int t_hi, const float* s_rstd,
+                                            const f32x4* pre0 = nullptr, const f32x4* pre1 = nullptr) {
     constexpr int NTL = NG * MTG;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -456,8 +478,13 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, const f32x4* v, c
         aux1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!ok[j]) continue;
         if (a.epi == EPI_RESID) {
-            aux0[j] = *(const f32x4*)((a.x_src ? a.x_src : a.x) + (size_t)mm[j] * a.ld + nn[j]);
-            aux1[j] = *(const f32x4*)(a.g_next + nn[j]);
+            if (pre0) {
+                aux0[j] = pre0[j];
+                aux1[j] = pre1[j];
+            } else {
+                aux0[j] = *(const f32x4*)((a.x_src ? a.x_src : a.x) + (size_t)mm[j] * a.ld + nn[j]);
+                aux1[j] = *(const f32x4*)(a.g_next + nn[j]);
+            }
         }
     }
 
@@ -813,15 +840,31 @@ __device__ __forceinline__ void gemm_reduce_wg(const GemmArgs& a, int bid) {
     const size_t split = (size_t)NTL * 64;
     int ti[OWN];
     f32x4 v[OWN];
+    // The first nine splits of every owned tile and the epilogue's residual
+    // rows and gains are requested together, unconditionally (splits past P
+    // re-read the last one and are not added), before any is used: one
+    // round trip.  Further splits follow eight at a time; all are added in
+    // split order.
+    f32x4 w0[OWN][9];
 #pragma unroll
     for (int j = 0; j < OWN; ++j) {
         const int r = wave + 4 * j;
         ti[j] = r < NG ? r * MTG + t : -1;
         const int i = r < NG ? r * MTG + t : t;
-        f32x4 s = pp[(size_t)i * 64];
-        // eight splits requested at a time (one round trip each, not one per
-        // split), added in split order
-        for (int q0 = 1; q0 < a.P; q0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 9; ++u) w0[j][u] = pp[(size_t)min(u, a.P - 1) * split + (size_t)i * 64];
+    }
+    f32x4 pre0[OWN], pre1[OWN];
+    if (a.epi == EPI_RESID) finish_aux<NG, MTG, OWN>(a, ti, ng, mt0, pre0, pre1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+        const int i = ti[j] >= 0 ? ti[j] : t;
+        f32x4 s = w0[j][0];
+#pragma unroll
+        for (int u = 1; u < 9; ++u)
+            if (u < a.P) s += w0[j][u];
+        for (int q0 = 9; q0 < a.P; q0 += 8) {
             f32x4 w[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
@@ -835,7 +878,8 @@ __device__ __forceinline__ void gemm_reduce_wg(const GemmArgs& a, int bid) {
     __syncthreads();
     if (a.ss_in) rstd_phase2(a, 16, s_seg, s_rstd + t * 16);
     __syncthreads();
-    gemm_finish<WT, NG, MTG, 4, OWN, CO>(a, v, ti, ng, mt0, t, t + 1, s_rstd);
+    gemm_finish<WT, NG, MTG, 4, OWN, CO>(a, v, ti, ng, mt0, t, t + 1, s_rstd,
+                                         a.epi == EPI_RESID ? pre0 : nullptr, pre1);
 }
 
 template <int WT, int NG, int MTG>
@@ -1161,6 +1205,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     const int pos_s = a.pos[s];
     const float qsc = a.qscale[g];
     const float sig_k = a.kvsig[g], sig_v = a.kvsig[a.hkv + g];
+    const float vsc = a.vscale[g];  // (used by the epilogue: no round trip there)
     if constexpr (!CO) request_rows();
     __builtin_amdgcn_sched_barrier(0);  // (all requested before any is used)
     // frame index p of the new entry; n cache positions attended; the new
@@ -1450,7 +1495,6 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     }
     __syncthreads();
 
-    const float* vs = a.vscale;
     for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
         const int h = i / D, d = i - h * D;
         float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
@@ -1468,7 +1512,7 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
             L += f;
         }
         if (nch == 1) {
-            store_act1x<WT, CO>(a.o_out, a.o_lo, a.f16, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vs[g]);
+            store_act1x<WT, CO>(a.o_out, a.o_lo, a.f16, xoff<WT>(s, (g * G + h) * D + d, a.MT), O / L * vsc);
         } else {
             float* part = a.part + (((size_t)(s * a.hkv + g) * a.n_chunks + chunk) * G + h) * (D + 2);
             st1<CO>(part + d, O);
