@@ -633,7 +633,7 @@ def _proj_in(cfg):
     if cfg["act_dtype"] != "bf16":
         return "f32"
     p = cfg.get("proj_in", "auto")
-    return ("bf16x2" if cfg.get("exec_mode", 0) else "f16") if p == "auto" else p
+    return "f16" if p == "auto" else p
 
 
 def _dtype_label(cfg):

@@ -361,7 +361,8 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
         cur += fd::walk_region(bytes);
         return Wk(c, o);
     };
-    auto take_lo = [&](uint64_t bytes) { return wt ? (void*)take(bytes) : nullptr; };
+    const bool two = wt && !pl.f16;  // rows as two bf16 parts (else fp16, or fp32)
+    auto take_lo = [&](uint64_t bytes) { return two ? (void*)take(bytes) : nullptr; };
     std::vector<fd::WalkPhase> phases;
     std::vector<fd::GemmArgs> gemm;
     std::vector<fd::AttnArgs> attn;
@@ -376,6 +377,8 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     };
     auto shaped = [&](fd::GemmArgs g, const fd::GemmShape& sh, uint64_t w_off, int d) {
         g.W = P(c, w_off);
+        g.wscale = wscale(c, w_off, sh);
+        g.f16 = pl.f16;
         g.K = sh.K; g.KB = sh.KB; g.NB = sh.NB; g.P = sh.P; g.MG = sh.MG;
         g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
         g.ss_stride = pl.nss_max;
@@ -402,6 +405,7 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
         e.x = (float*)take(4 * Sp * z.d);
         e.xg = take(4 * Sp * z.d);
         e.xg_lo = take_lo(4 * Sp * z.d);
+        e.f16 = pl.f16;
         e.g = (const float*)P(c, z.L > 0 ? sp.layers[0].g_attn : sp.g_final);
         e.ss_out = (float*)take(4 * Sp * pl.nss_max);
         e.ss_stride = pl.nss_max;
@@ -455,6 +459,7 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
                           : nullptr;
             at.o_out = take(4 * Sp * z.hq * z.hd);
             at.o_lo = take_lo(4 * Sp * z.hq * z.hd);
+            at.f16 = pl.f16;
             const int ai = (int)attn.size();
             attn.push_back(at);
             phases.push_back({attn_kind, ai, pl.S * z.hkv * sp.attn.n_chunks, 1});
@@ -528,7 +533,8 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     mf.ldy = mp.dims.d;
     mf.y_off = 0;
     mf.yw = pl.depth ? (void*)take(4 * Sp * mp.dims.d) : (pl.head ? (void*)Wk(c, pl.ws_yw) : nullptr);
-    mf.yw_lo = wt && pl.head ? (void*)Wk(c, pl.ws_yw_lo) : nullptr;
+    mf.yw_lo = two && pl.head ? (void*)Wk(c, pl.ws_yw_lo) : nullptr;
+    mf.f16 = pl.f16;
     c->head_x = mf.yw;
     c->head_x_lo = mf.yw_lo;
     mf.pos = slot_pos(c);
@@ -611,7 +617,7 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
     w.bar = (unsigned*)Wk(c, pl.ws_walk_bar);
     w.abort_flag = (int*)(Wk(c, pl.ws_walk_bar) + 64);
     c->walk_shape = fd::WalkShape{wt, pl.kv_fp8 ? 1 : 0, mp.qkv.MTG, mp.dims.hd, mp.dims.G(),
-                                  pl.depth ? pl.dstack.dims.hd : 0};
+                                  pl.depth ? pl.dstack.dims.hd : 0, pl.f16 ? 1 : 0};
     c->walk_grid = fd::walk_grid(c->walk_shape);
     if (c->walk_grid <= 0) {
         *err = "no co-resident grid for the walk kernel of this shape";

@@ -177,10 +177,11 @@ struct WalkArgs {
 };
 
 // Shape a walk kernel is compiled for: weight / cache types, m-tiles per
-// GEMM m-group, head_dim and query heads per kv head of the main stack, and
-// head_dim of the depth stack (0: none).
+// GEMM m-group, head_dim and query heads per kv head of the main stack,
+// head_dim of the depth stack (0: none), and (2-byte stacks) whether the
+// projections take their rows as one fp16 part (else two bf16 parts).
 struct WalkShape {
-    int wt, fp8, MTG, hd, G, dhd;
+    int wt, fp8, MTG, hd, G, dhd, f16;
 };
 
 // Depth of a GEMM wave's register ring of k-tiles: as deep as ~48

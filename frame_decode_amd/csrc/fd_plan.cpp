@@ -206,10 +206,6 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         *err = "proj_in applies to FD_BF16 profiles (fp32 profiles take FD_PROJ_AUTO)";
         return FD_E_UNSUPPORTED;
     }
-    if (c.proj_in == FD_PROJ_F16 && c.exec_mode == FD_EXEC_WALK) {
-        *err = "FD_EXEC_WALK takes the rows as two bf16 parts (FD_PROJ_BF16X2 or FD_PROJ_AUTO)";
-        return FD_E_UNSUPPORTED;
-    }
     if (c.kv_ring != 0 && c.kv_ring != 1) {
         *err = "kv_ring must be 0 (fixed window) or 1 (rolling window)";
         return FD_E_INVAL;
@@ -236,8 +232,7 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     }
     p.wt = c.act_dtype == FD_BF16 ? 1 : 0;
     p.w8 = c.w_dtype == FD_FP8_E4M3;
-    p.f16 = p.wt && (c.proj_in == FD_PROJ_F16 ||
-                     (c.proj_in == FD_PROJ_AUTO && c.exec_mode == FD_EXEC_KERNELS));
+    p.f16 = p.wt && c.proj_in != FD_PROJ_BF16X2;
     p.wkind = p.w8 ? 2 : (p.f16 ? 3 : p.wt);
     p.act_bytes = p.wt ? 2 : 4;
     p.kv_fp8 = c.kv_dtype == FD_FP8_E4M3;
@@ -375,24 +370,25 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
             return FD_E_UNSUPPORTED;
         }
         // every cross-phase output gets a region of its own; sizes at 4 bytes
-        // per element (bf16 parts use half)
+        // per element (2-byte rows use half); two-part rows add low parts
         const uint64_t f4 = 4;
+        const int lo = p.wt && !p.f16 ? 1 : 0;
         auto stack_layer = [&](const StackPlan& sp) {
             const StackDims& z = sp.dims;
             uint64_t b = 0;
             b += walk_region(f4 * sp.qkv.P * Sp * z.qkv_n());                      // QKV planes
-            b += (p.wt ? 2 : 1) * walk_region(f4 * Sp * z.hq * z.hd);             // o (+ low part)
+            b += (1 + lo) * walk_region(f4 * Sp * z.hq * z.hd);                  // o (+ low part)
             if (sp.attn.n_chunks > 1)
                 b += walk_region(f4 * p.S * z.hkv * sp.attn.n_chunks * z.G() * (z.hd + 2));
             for (const GemmShape* g : {&sp.o, &sp.gu, &sp.down})
                 if (g->P > 1) b += walk_region(f4 * g->part_floats);                // k-split partials
             // x, xg (+ low part), ss after O and after down
-            b += 2 * ((p.wt ? 3 : 2) * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max));
-            b += (p.wt ? 2 : 1) * walk_region(f4 * Sp * z.f);                      // h (+ low part)
+            b += 2 * ((2 + lo) * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max));
+            b += (1 + lo) * walk_region(f4 * Sp * z.f);                           // h (+ low part)
             return b;
         };
         auto stack_in = [&](const StackDims& z) {   // embed: x, xg (+ low part), ss
-            return (p.wt ? 3 : 2) * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max);
+            return (2 + lo) * walk_region(f4 * Sp * z.d) + walk_region(f4 * Sp * p.nss_max);
         };
         p.walk_act_bytes = stack_in(m) + (uint64_t)m.L * stack_layer(p.main);
         p.walk_max_gemm = 4 * m.L;

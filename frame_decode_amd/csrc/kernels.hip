@@ -1749,8 +1749,10 @@ __device__ __forceinline__ bool walk_wait(unsigned* cnt, unsigned target, int* a
 // WT/FP8: weight and cache types of the main stack; MTG: m-tiles per GEMM
 // m-group; D, G: head_dim and query heads per kv head of the main stack;
 // DD: head_dim of the depth stack (0: none; one query head per kv head).
-template <int WT, int FP8, int MTG, int D, int G, int DD>
+// F16: the projections take fp16 rows and fp16 weight codes (2-byte stacks)
+template <int WT, int FP8, int MTG, int D, int G, int DD, int F16 = 0>
 __global__ __launch_bounds__(256) void walk_kernel(WalkArgs w) {
+    constexpr int SXW = F16 ? 2 : WT;  // the GEMM bodies' row form
     __shared__ f32x4 s_acc[4 * 6 * MTG * 64];
     unsigned target = 0;
     bool pending = false, ok = true;
@@ -1767,10 +1769,10 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkArgs w) {
         for (int it = blockIdx.x; it < P.n_items; it += gridDim.x) {
             switch (P.kind) {
                 case WALK_GEMM4:
-                    gemm_wg<WT, 4, MTG, gemm_stages(4, MTG, WT), WT, 1, 0>(w.gemm[P.idx], it, s_acc, wait);
+                    gemm_wg<WT, 4, MTG, gemm_stages(4, MTG, SXW == 1), SXW, 1, 0>(w.gemm[P.idx], it, s_acc, wait);
                     break;
                 case WALK_GEMM6:
-                    gemm_wg<WT, 6, MTG, gemm_stages(6, MTG, WT), WT, 1, 0>(w.gemm[P.idx], it, s_acc, wait);
+                    gemm_wg<WT, 6, MTG, gemm_stages(6, MTG, SXW == 1), SXW, 1, 0>(w.gemm[P.idx], it, s_acc, wait);
                     break;
                 case WALK_ATTN: attn_wg<WT, FP8, D, G, 1, walk_attn_nit<FP8>()>(w.attn[P.idx], it, wait); break;
                 case WALK_ATTN_DEPTH:
@@ -2079,25 +2081,28 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t st) {
 // up to 2 m-tiles; fp32 stacks with head_dim 256, 4 query heads per kv head
 // and a head_dim-128 depth stack, up to 4 m-tiles; bf16 weights with an FP8
 // cache, head_dim 128, one query head per kv head, no depth stack, up to 5.
-template <int WT, int FP8, int D, int G, int DD, int MTG>
+template <int WT, int FP8, int D, int G, int DD, int F16, int MTG>
 static const void* walk_fn_one() {
-    return (const void*)walk_kernel<WT, FP8, MTG, D, G, DD>;
+    return (const void*)walk_kernel<WT, FP8, MTG, D, G, DD, F16>;
 }
 
-template <int WT, int FP8, int D, int G, int DD, int MAXM>
+template <int WT, int FP8, int D, int G, int DD, int F16, int MAXM>
 static const void* walk_fn_mtg(int MTG) {
     if (MTG < 1 || MTG > MAXM) return nullptr;
-    if constexpr (MAXM >= 5) if (MTG == 5) return walk_fn_one<WT, FP8, D, G, DD, 5>();
-    if constexpr (MAXM >= 4) if (MTG == 4) return walk_fn_one<WT, FP8, D, G, DD, 4>();
-    if constexpr (MAXM >= 3) if (MTG == 3) return walk_fn_one<WT, FP8, D, G, DD, 3>();
-    if constexpr (MAXM >= 2) if (MTG == 2) return walk_fn_one<WT, FP8, D, G, DD, 2>();
-    return walk_fn_one<WT, FP8, D, G, DD, 1>();
+    if constexpr (MAXM >= 5) if (MTG == 5) return walk_fn_one<WT, FP8, D, G, DD, F16, 5>();
+    if constexpr (MAXM >= 4) if (MTG == 4) return walk_fn_one<WT, FP8, D, G, DD, F16, 4>();
+    if constexpr (MAXM >= 3) if (MTG == 3) return walk_fn_one<WT, FP8, D, G, DD, F16, 3>();
+    if constexpr (MAXM >= 2) if (MTG == 2) return walk_fn_one<WT, FP8, D, G, DD, F16, 2>();
+    return walk_fn_one<WT, FP8, D, G, DD, F16, 1>();
 }
 
 static const void* walk_fn_for(const WalkShape& s) {
-    if (!s.wt && !s.fp8 && s.hd == 64 && s.G == 1 && s.dhd == 0) return walk_fn_mtg<0, 0, 64, 1, 0, 2>(s.MTG);
-    if (!s.wt && !s.fp8 && s.hd == 256 && s.G == 4 && s.dhd == 128) return walk_fn_mtg<0, 0, 256, 4, 128, 4>(s.MTG);
-    if (s.wt && s.fp8 && s.hd == 128 && s.G == 1 && s.dhd == 0) return walk_fn_mtg<1, 1, 128, 1, 0, 5>(s.MTG);
+    if (!s.wt && !s.fp8 && s.hd == 64 && s.G == 1 && s.dhd == 0 && !s.f16)
+        return walk_fn_mtg<0, 0, 64, 1, 0, 0, 2>(s.MTG);
+    if (!s.wt && !s.fp8 && s.hd == 256 && s.G == 4 && s.dhd == 128 && !s.f16)
+        return walk_fn_mtg<0, 0, 256, 4, 128, 0, 4>(s.MTG);
+    if (s.wt && s.fp8 && s.hd == 128 && s.G == 1 && s.dhd == 0)
+        return s.f16 ? walk_fn_mtg<1, 1, 128, 1, 0, 1, 5>(s.MTG) : walk_fn_mtg<1, 1, 128, 1, 0, 0, 5>(s.MTG);
     return nullptr;
 }
 

@@ -75,10 +75,9 @@ typedef int32_t fd_status;
  *     lo = bf16(v - hi) (~16 significant bits), multiplied with the bf16
  *     (or FP8-decoded) weights: twice the matrix-core work and row loads of
  *     FD_PROJ_F16.
- *   FD_PROJ_AUTO: FD_PROJ_F16 with FD_EXEC_KERNELS, FD_PROJ_BF16X2 with
- *     FD_EXEC_WALK (the only form the persistent walk is compiled for).
- * FD_F32 profiles take FD_PROJ_AUTO (fp32 rows); other values give
- * FD_E_UNSUPPORTED, as does FD_PROJ_F16 with FD_EXEC_WALK.
+ *   FD_PROJ_AUTO: FD_PROJ_F16.
+ * Both forms run in either exec_mode.  FD_F32 profiles take FD_PROJ_AUTO
+ * (fp32 rows); other values give FD_E_UNSUPPORTED.
  */
 #define FD_PROJ_AUTO   0
 #define FD_PROJ_F16    1

@@ -123,15 +123,15 @@ ROW_SPLIT_7B = ("qkv.NG=12,qkv.P=2,qkv.KH=2,o.NG=8,o.P=1,gu.NG=12,gu.P=2,gu.KH=2
 
 
 @pytest.mark.parametrize("exec_mode,tune,proj_in",
-                         [(0, None, "auto"), (1, None, "auto"), (0, None, "bf16x2"),
+                         [(0, None, "auto"), (1, None, "auto"), (0, None, "bf16x2"), (1, None, "bf16x2"),
                           (0, ROW_SPLIT_7B, "bf16x2")],
-                         ids=["kernels", "walk", "kernels_bf16x2", "row_split"])
+                         ids=["kernels", "walk", "kernels_bf16x2", "walk_bf16x2", "row_split"])
 def test_7b_eight_sessions_at_position_256(model7b, exec_mode, tune, proj_in, monkeypatch):
     """The 8-session workload in full: 32 layers, every session's cache
     prefilled to 256 positions, new frame at index 256; every row checked
-    (kernel sequence with fp16 and with two-part bf16 projection inputs,
-    persistent walk, and the kernel sequence with every projection on the
-    row-split variant)."""
+    (kernel sequence and persistent walk, each with fp16 and with two-part
+    bf16 projection inputs, and the kernel sequence with every projection
+    on the row-split variant)."""
     if tune:
         monkeypatch.setenv("FD_TUNE", tune)
     cfg = synth.get_config("7b_s8_p256")

@@ -172,13 +172,13 @@ def test_tiny_fp32_sixteen_frames(exec_mode):
     _check_cache(ctx, orc, cfg, slots, pos, {s: 0 for s in slots})
 
 
-@pytest.mark.parametrize("exec_mode,proj_in", [(0, "auto"), (0, "bf16x2"), (1, "auto")],
-                         ids=["kernels", "kernels_bf16x2", "walk"])
+@pytest.mark.parametrize("exec_mode,proj_in", [(0, "auto"), (0, "bf16x2"), (1, "auto"), (1, "bf16x2")],
+                         ids=["kernels", "kernels_bf16x2", "walk", "walk_bf16x2"])
 def test_bf16_fp8_ragged_multichunk(exec_mode, proj_in):
     """bf16 weights/activations, FP8 cache, 7B head geometry (128-dim MHA)
     at reduced width and depth; slots at positions spanning 1..3 attention
-    chunks, one slot left empty; kernel sequence (projection inputs in fp16,
-    and as two bf16 parts) and persistent walk (two bf16 parts)."""
+    chunks, one slot left empty; kernel sequence and persistent walk, each
+    with the projection inputs in fp16 and as two bf16 parts."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
                               d_ffn=1536, max_slots=9, max_context=700, exec_mode=exec_mode,
                               proj_in=proj_in)

@@ -150,10 +150,11 @@ def test_walk_mode(host):
         st1, s1 = _plan(host, cfg)
         assert st0 == FD_OK and st1 == FD_OK and s1.workspace > s0.workspace, name
         assert s1.packed_weights == s0.packed_weights and s1.kv_arena == s0.kv_arena
-        if cfg["act_dtype"] == "bf16":  # AUTO in the walk is the two-part form
-            cfg["proj_in"] = "auto"
-            st2, s2 = _plan(host, cfg)
-            assert st2 == FD_OK and (s2.packed_weights, s2.workspace) == (s1.packed_weights, s1.workspace)
+        if cfg["act_dtype"] == "bf16":  # AUTO in the walk is the fp16 form
+            st2, s2 = _plan(host, dict(cfg, proj_in="auto"))
+            st3, s3 = _plan(host, dict(cfg, proj_in="f16"))
+            assert st2 == st3 == FD_OK and (s2.packed_weights, s2.workspace) == (s3.packed_weights, s3.workspace)
+            assert s3.workspace < s1.workspace  # no low parts
     # fp32 7B-shaped stack (head_dim 128 without a depth stack): not compiled
     f32 = synth.get_config("7b_s8_p256")
     f32.update(exec_mode=1, w_dtype="f32", act_dtype="f32", kv_dtype="f32")
@@ -172,10 +173,10 @@ def test_walk_mode(host):
 
 
 def test_projection_input_forms(host):
-    """bf16 profiles: AUTO is the fp16 form in the kernel sequence; the fp16
-    form stores one fp32 scale per output row after each matrix's tiles and
-    needs no low-part buffers; the walk refuses it; fp32 profiles take only
-    AUTO; unknown values are refused."""
+    """bf16 profiles: AUTO is the fp16 form in either mode; the fp16 form
+    stores one fp32 scale per output row after each matrix's tiles and needs
+    no low-part buffers; fp32 profiles take only AUTO; unknown values are
+    refused."""
     from frame_decode_amd import abi
     text = open(os.path.join(ROOT, "include", "fd.h")).read()
     for n in ("FD_PROJ_AUTO", "FD_PROJ_F16", "FD_PROJ_BF16X2"):
@@ -189,7 +190,7 @@ def test_projection_input_forms(host):
     # low parts of xg, h and o: 80 rows x (4096 + 11264 + 4096) x 2 bytes (an
     # unused region still takes its 256-byte alignment unit)
     assert b.workspace - f.workspace == 80 * (4096 + 11264 + 4096) * 2 - 3 * 256
-    assert _plan(host, dict(cfg, proj_in="f16", exec_mode=1))[0] == FD_E_UNSUPPORTED
+    assert _plan(host, dict(cfg, proj_in="f16", exec_mode=1))[0] == FD_OK
     assert _plan(host, dict(cfg, proj_in="bf16x2", exec_mode=1))[0] == FD_OK
     fp8 = dict(cfg, w_dtype="fp8")
     assert _plan(host, dict(fp8, proj_in="f16"))[0] == FD_OK
