@@ -31,7 +31,7 @@ bool valid_split(const GemmShape& g, int P) {
     return P >= 1 && g.KB % P == 0 && g.KB / P >= 4;
 }
 
-GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap) {
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool small) {
     // Candidates: 6 or 4 weight blocks per workgroup (6 only while the
     // accumulators of a 5-tile m-group fit), any split P that gives every
     // wave at least one step.  Score: how evenly the grid fills whole
@@ -54,6 +54,17 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap) {
                 best_score = score;
                 best = g;
             }
+        }
+    }
+    // One weight block per workgroup (small: fp32 stacks in the kernel
+    // sequence).  Each activation k-tile is then fetched once per block
+    // rather than once per 4-6, so it pays only where it removes most of a
+    // k-split (no reduce launch, fewer planes for attention to add) while
+    // still filling the CUs: at most 2 splits and 192-512 workgroups.
+    if (small && best.P > 1) {
+        for (int P = 1; P <= 2 && P < best.P; ++P) {
+            GemmShape g = shape_with(N, K, KT, MT, 1, P, cap);
+            if (g.MTG <= 5 && valid_split(g, P) && g.grid() >= 192 && g.grid() <= 2 * n_cu) return g;
         }
     }
     return best;
@@ -102,11 +113,13 @@ int tune_value(const char* key, int dflt) {
     return dflt;
 }
 
-GemmShape tuned(GemmShape g, const char* name, bool ns, int cap) {
+GemmShape tuned(GemmShape g, const char* name, bool ns, int cap, bool small) {
     std::string n(name);
     int NG = tune_value((n + ".NG").c_str(), g.R);
     int P = tune_value((n + ".P").c_str(), g.P);
-    if (!(NG == 4 || (NG == 6 && g.MTG <= 5) || (ns && ns_blocks_ok(NG, g.MTG)))) NG = g.R;
+    if (!(NG == 4 || (NG == 6 && g.MTG <= 5) || (ns && ns_blocks_ok(NG, g.MTG)) ||
+          (small && small_blocks_ok(NG, g.MTG))))
+        NG = g.R;
     GemmShape base = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, 1, cap);
     if (!valid_split(base, P)) P = valid_split(base, g.P) ? g.P : 1;
     GemmShape out = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, P, cap);
@@ -120,14 +133,15 @@ GemmShape tuned(GemmShape g, const char* name, bool ns, int cap) {
 
 // pre: prefix of the stack's tuning keys ("" main, "d." depth stack)
 // scaled: the packed matrices carry per-row scales (FP8 or fp16 codes)
+// small: the 1- and 2-block fp32 kernels may be chosen (kernel sequence)
 void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8, bool w8,
-                bool scaled, uint64_t& off, bool ns, const std::string& pre) {
+                bool scaled, uint64_t& off, bool ns, bool small, const std::string& pre) {
     sp.dims = dims;
     const int cap = w8 ? kMaxMTG8 : kMaxMTG;
-    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256, cap), (pre + "qkv").c_str(), ns, cap);
-    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256, cap), (pre + "o").c_str(), ns, cap);
-    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256, cap), (pre + "gu").c_str(), ns, cap);
-    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256, cap), (pre + "down").c_str(), ns, cap);
+    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256, cap, small), (pre + "qkv").c_str(), ns, cap, small);
+    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256, cap, small), (pre + "o").c_str(), ns, cap, small);
+    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256, cap, small), (pre + "gu").c_str(), ns, cap, small);
+    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256, cap, small), (pre + "down").c_str(), ns, cap, small);
     sp.layers.resize(dims.L);
     auto tiles = [scaled](const GemmShape& g) { return packed_matrix_bytes(g, scaled); };
     for (int l = 0; l < dims.L; ++l) {
@@ -269,14 +283,15 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     // rows), launched as kernels (the persistent walk runs gemm_wg)
     const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8;
     const bool scaled = p.wkind >= 2;
-    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, scaled, off, ns, "");
+    const bool small = c.exec_mode == FD_EXEC_KERNELS && !p.wt;
+    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, scaled, off, ns, small, "");
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
         p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
         p.w_in = off;
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
-        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, false, off, false, "d.");
+        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, false, off, false, small, "d.");
     }
     if (p.head) {
         p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256, p.w8 ? kMaxMTG8 : kMaxMTG);

@@ -155,7 +155,8 @@ inline uint64_t packed_matrix_bytes(const GemmShape& g, bool scaled) {
 
 // Tile choice for one projection (exposed for tests).
 // cap: most m-tiles per m-group (kMaxMTG, or kMaxMTG8 for FP8 weights).
-GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap = kMaxMTG);
+// small: one weight block per workgroup may be chosen (fp32 kernel sequence).
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap = kMaxMTG, bool small = false);
 
 // Session rows padded to whole m-groups of at most `cap` 16-row tiles.
 inline int padded_mtiles(int slots, int cap) {
@@ -167,5 +168,8 @@ inline int padded_mtiles(int slots, int cap) {
 // Row-split projection variant (bf16 weights, two-part activations): 8, 12
 // or 16 blocks per workgroup (2, 3 or 4 per wave), at most 5 m-tiles.
 inline bool ns_blocks_ok(int NG, int MTG) { return (NG == 8 || NG == 12 || NG == 16) && MTG <= 5; }
+// One or two weight blocks per workgroup (fp32 weights, kernel sequence):
+// built for m-groups of up to 5 tiles.
+inline bool small_blocks_ok(int NG, int MTG) { return (NG == 1 || NG == 2) && MTG <= 5; }
 
 }  // namespace fd

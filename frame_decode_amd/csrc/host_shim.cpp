@@ -36,20 +36,22 @@ void fdh_gemm_shape(int N, int K, int wt, int MT, int32_t* out) {
     out[6] = g.n_groups; out[7] = g.grid(); out[8] = g.KT;
 }
 
-// Tiling of the main stack's projections as the plan of cfg chose it
-// (FD_TUNE applies): out[4*i + 0..3] = R, P, k-halves, grid for i = QKV, O,
-// gate/up, down.
+// Tiling of the projections as the plan of cfg chose it (FD_TUNE applies):
+// out[4*i + 0..3] = R, P, k-halves, grid for i = QKV, O, gate/up, down of
+// the main stack, then (i = 4..7) of the depth stack (zeros without one).
 fd_status fdh_stack_shapes(const fd_config* cfg, int32_t* out) {
     if (!cfg || !out) return FD_E_INVAL;
     fd::Plan p;
     fd_status st = fd::make_plan(*cfg, &p, &g_err);
     if (st != FD_OK) return st;
-    const fd::GemmShape* g[4] = {&p.main.qkv, &p.main.o, &p.main.gu, &p.main.down};
-    for (int i = 0; i < 4; ++i) {
-        out[4 * i + 0] = g[i]->R;
-        out[4 * i + 1] = g[i]->P;
-        out[4 * i + 2] = g[i]->kh;
-        out[4 * i + 3] = g[i]->grid();
+    const fd::GemmShape* g[8] = {&p.main.qkv, &p.main.o, &p.main.gu, &p.main.down,
+                                 &p.dstack.qkv, &p.dstack.o, &p.dstack.gu, &p.dstack.down};
+    for (int i = 0; i < 8; ++i) {
+        const bool have = i < 4 || p.depth;
+        out[4 * i + 0] = have ? g[i]->R : 0;
+        out[4 * i + 1] = have ? g[i]->P : 0;
+        out[4 * i + 2] = have ? g[i]->kh : 0;
+        out[4 * i + 3] = have ? g[i]->grid() : 0;
     }
     return FD_OK;
 }

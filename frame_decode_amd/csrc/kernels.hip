@@ -2014,6 +2014,8 @@ hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hip
     if (wt == 3) return NG == 6 ? gemm_f16<6>(a, MTG, grid, st) : (NG == 4 ? gemm_f16<4>(a, MTG, grid, st) : hipErrorInvalidValue);
     if (NG == 6) return wt ? gemm_ng<1, 6>(a, MTG, grid, st) : gemm_ng<0, 6>(a, MTG, grid, st);
     if (NG == 4) return wt ? gemm_ng4<1>(a, MTG, grid, st) : gemm_ng4<0>(a, MTG, grid, st);
+    if (NG == 2 && !wt) return gemm_ng<0, 2>(a, MTG, grid, st);
+    if (NG == 1 && !wt) return gemm_ng<0, 1>(a, MTG, grid, st);
     return hipErrorInvalidValue;
 }
 

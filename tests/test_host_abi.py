@@ -216,11 +216,12 @@ def test_gemm_tiling_covers_the_projection(host):
 
 
 def _stack_shapes(host, cfg):
-    out = (ctypes.c_int32 * 16)()
+    out = (ctypes.c_int32 * 32)()
     st = host.fdh_stack_shapes(ctypes.byref(config_from_dict(cfg)), out)
     assert st == FD_OK, host.fdh_last_error()
     v = list(out)
-    return {n: tuple(v[4 * i:4 * i + 4]) for i, n in enumerate(("qkv", "o", "gu", "down"))}
+    names = ("qkv", "o", "gu", "down", "d.qkv", "d.o", "d.gu", "d.down")
+    return {n: tuple(v[4 * i:4 * i + 4]) for i, n in enumerate(names) if v[4 * i]}
 
 
 def test_row_split_projection_plan(host, monkeypatch):
@@ -251,6 +252,30 @@ def test_row_split_projection_plan(host, monkeypatch):
     sh = _stack_shapes(host, cfg)
     assert sh["down"] == (12, 32, 1, 704)  # 11 k-tiles per split: no even halves
     assert sh["o"] == (12, 32, 2, 704)  # 4 k-tiles per split: two steps of two
+
+
+def test_one_block_projections_for_fp32_stacks(host, monkeypatch):
+    """fp32 stacks in the kernel sequence take one weight block per
+    workgroup where that removes most of a k-split and still gives 192-512
+    workgroups (the talker's QKV with 2 splits, its depth QKV and gate/up
+    with none); the other projections, the persistent walk and bf16 stacks
+    keep 4 or 6 blocks per workgroup."""
+    monkeypatch.delenv("FD_TUNE", raising=False)
+    talker = dict(synth.get_config("talker_s56"), exec_mode=0)
+    sh = _stack_shapes(host, talker)
+    assert sh["qkv"] == (1, 2, 1, 192)      # 96 blocks x 2 splits (9 splits of 4 blocks before)
+    assert sh["d.qkv"] == (1, 1, 1, 192)    # 192 blocks, no split
+    assert sh["d.gu"] == (1, 1, 1, 352)     # 352 blocks, no split, no reduce launch
+    for n in ("o", "gu", "down", "d.o", "d.down"):
+        assert sh[n][0] in (4, 6), n
+    walk = _stack_shapes(host, dict(talker, exec_mode=1))
+    assert all(v[0] in (4, 6) for v in walk.values())
+    big = _stack_shapes(host, synth.get_config("7b_s80_p1499"))
+    assert set(big) == {"qkv", "o", "gu", "down"} and all(v[0] in (4, 6) for v in big.values())
+    monkeypatch.setenv("FD_TUNE", "d.gu.NG=6,d.gu.P=4,o.NG=1,o.P=2")
+    sh = _stack_shapes(host, talker)
+    assert sh["d.gu"] == (6, 4, 1, 236) and sh["o"] == (1, 2, 1, 144)
+    assert _stack_shapes(host, dict(talker, exec_mode=1))["o"][0] in (4, 6)
 
 
 class Pool:
