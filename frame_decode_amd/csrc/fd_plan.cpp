@@ -33,15 +33,17 @@ bool valid_split(const GemmShape& g, int P) {
 
 GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool small) {
     // Candidates: 6 or 4 weight blocks per workgroup (6 only while the
-    // accumulators of a 5-tile m-group fit), any split P that gives every
-    // wave at least one step.  Score: how evenly the grid fills whole
-    // rounds of one workgroup per CU, minus a small charge per extra split
-    // (its partial tiles cost a write and a read).
+    // accumulators of a 5-tile m-group fit; small: also 2, which fills as
+    // many CUs with half the splits), any split P that gives every wave at
+    // least one step.  Score: how evenly the grid fills whole rounds of one
+    // workgroup per CU, minus a small charge per extra split (its partial
+    // tiles cost a write and a read); ties keep more blocks per workgroup.
     GemmShape best = shape_with(N, K, KT, MT, 4, 1, cap);
     double best_score = -1e9;
-    for (int NG : {6, 4}) {
+    for (int NG : {6, 4, 2}) {
         GemmShape base = shape_with(N, K, KT, MT, NG, 1, cap);
         if (NG == 6 && base.MTG > 5) continue;
+        if (NG == 2 && !(small && small_blocks_ok(2, base.MTG))) continue;
         for (int P = 1; P <= 64; ++P) {
             if (!valid_split(base, P)) continue;
             GemmShape g = shape_with(N, K, KT, MT, NG, P, cap);

@@ -258,16 +258,20 @@ def test_one_block_projections_for_fp32_stacks(host, monkeypatch):
     """fp32 stacks in the kernel sequence take one weight block per
     workgroup where that removes most of a k-split and still gives 192-512
     workgroups (the talker's QKV with 2 splits, its depth QKV and gate/up
-    with none); the other projections, the persistent walk and bf16 stacks
-    keep 4 or 6 blocks per workgroup."""
+    with none), and two blocks where those fill as many CUs with fewer
+    splits (its O and down projections); the main gate/up, where two blocks
+    only tie, keeps four.  The persistent walk and bf16 stacks keep 4 or 6
+    blocks per workgroup."""
     monkeypatch.delenv("FD_TUNE", raising=False)
     talker = dict(synth.get_config("talker_s56"), exec_mode=0)
     sh = _stack_shapes(host, talker)
     assert sh["qkv"] == (1, 2, 1, 192)      # 96 blocks x 2 splits (9 splits of 4 blocks before)
     assert sh["d.qkv"] == (1, 1, 1, 192)    # 192 blocks, no split
     assert sh["d.gu"] == (1, 1, 1, 352)     # 352 blocks, no split, no reduce launch
-    for n in ("o", "gu", "down", "d.o", "d.down"):
-        assert sh[n][0] in (4, 6), n
+    assert sh["o"] == (2, 4, 1, 144)        # 36 pairs of blocks x 4 splits
+    assert sh["down"] == (2, 6, 1, 216)     # 432 k-tiles in 6 splits (12 of 4 blocks before)
+    assert sh["d.o"] == (2, 8, 1, 256) and sh["d.down"] == (2, 8, 1, 256)  # 16 splits before
+    assert sh["gu"] == (4, 1, 1, 216)
     walk = _stack_shapes(host, dict(talker, exec_mode=1))
     assert all(v[0] in (4, 6) for v in walk.values())
     big = _stack_shapes(host, synth.get_config("7b_s80_p1499"))
