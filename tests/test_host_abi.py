@@ -445,6 +445,33 @@ def test_fp8_weight_row_groups_stay_within_the_built_kernels(host, slots):
             assert mg * mtg == mt, (wdt, slots, i, mg, mtg, mt)
 
 
+@pytest.mark.parametrize("slots", [1, 7, 16, 33, 56, 80, 81, 96, 128, 140, 200, 709])
+def test_fp32_block_counts_stay_within_the_built_kernels(host, slots, monkeypatch):
+    """One- and two-block projections are built for fp32 weights with at
+    most 5 row tiles per m-group: at every slot count the fp32 plan (main
+    and depth stack) picks them only there, and the persistent walk (where
+    it takes the profile) keeps 4 or 6 blocks."""
+    monkeypatch.delenv("FD_TUNE", raising=False)
+    base = synth.scaled_config("talker_s56", max_slots=slots)
+    base.pop("position", None)
+    for mode in (0, 1):
+        cfg = dict(base, exec_mode=mode)
+        mt_out = (ctypes.c_int32 * 11)()
+        st = host.fdh_stack_mtiles(ctypes.byref(config_from_dict(cfg)), mt_out)
+        if mode == 1 and st == FD_E_UNSUPPORTED:
+            continue  # (the walk is built for a few row tilings only)
+        assert st == FD_OK, host.fdh_last_error()
+        mtg = {n: mt_out[2 + 2 * i] for i, n in enumerate(("qkv", "o", "gu", "down"))}
+        sh = _stack_shapes(host, cfg)
+        assert set(sh) == {"qkv", "o", "gu", "down", "d.qkv", "d.o", "d.gu", "d.down"}
+        for n, (R, P, kh, grid) in sh.items():
+            assert R in ((1, 2, 4, 6) if mode == 0 else (4, 6)), (slots, mode, n, R)
+            if R in (1, 2, 6):
+                # (the depth stack has the main stack's rows, so the same tiling)
+                assert mtg[n.split(".")[-1]] <= 5, (slots, n, R)
+            assert P >= 1 and kh == 1 and grid % P == 0
+
+
 def test_stale_slots_after_an_interrupted_step(host):
     """A step that stopped early marks every active slot stale; each slot
     leaves that state when given a position or freed, and a newly admitted
