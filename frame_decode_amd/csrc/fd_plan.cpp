@@ -58,15 +58,21 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool smal
             }
         }
     }
-    // One weight block per workgroup (small: fp32 stacks in the kernel
-    // sequence).  Each activation k-tile is then fetched once per block
-    // rather than once per 4-6, so it pays only where it removes most of a
-    // k-split (no reduce launch, fewer planes for attention to add) while
-    // still filling the CUs: at most 2 splits and 192-512 workgroups.
+    // Two or one weight blocks per workgroup without the k-split (small:
+    // fp32 stacks in the kernel sequence).  Each activation k-tile is then
+    // fetched once per 2 or 1 blocks rather than once per 4-6, which pays
+    // where it removes the split (no reduce launch, fewer planes for
+    // attention to add) and still fills two thirds of the CUs in at most
+    // two rounds: the first of (2 blocks, no split), (1, no split),
+    // (1, 2 splits) that does.
     if (small && best.P > 1) {
-        for (int P = 1; P <= 2 && P < best.P; ++P) {
-            GemmShape g = shape_with(N, K, KT, MT, 1, P, cap);
-            if (g.MTG <= 5 && valid_split(g, P) && g.grid() >= 192 && g.grid() <= 2 * n_cu) return g;
+        const int cand[3][2] = {{2, 1}, {1, 1}, {1, 2}};
+        for (const auto& c : cand) {
+            if (c[1] >= best.P) continue;
+            GemmShape g = shape_with(N, K, KT, MT, c[0], c[1], cap);
+            if (small_blocks_ok(c[0], g.MTG) && valid_split(g, c[1]) && 3 * g.grid() >= 2 * n_cu &&
+                g.grid() <= 2 * n_cu)
+                return g;
         }
     }
     return best;

@@ -255,19 +255,19 @@ def test_row_split_projection_plan(host, monkeypatch):
 
 
 def test_one_block_projections_for_fp32_stacks(host, monkeypatch):
-    """fp32 stacks in the kernel sequence take one weight block per
-    workgroup where that removes most of a k-split and still gives 192-512
-    workgroups (the talker's QKV with 2 splits, its depth QKV and gate/up
-    with none), and two blocks where those fill as many CUs with fewer
-    splits (its O and down projections); the main gate/up, where two blocks
-    only tie, keeps four.  The persistent walk and bf16 stacks keep 4 or 6
-    blocks per workgroup."""
+    """fp32 stacks in the kernel sequence drop the k-split with two or one
+    weight blocks per workgroup where that still fills two thirds of the
+    CUs (the talker's depth gate/up and QKV; its main QKV keeps 2 splits of
+    one block), and take two blocks where those fill as many CUs as four
+    with fewer splits (its O and down projections); the main gate/up, where
+    two blocks only tie, keeps four.  The persistent walk and bf16 stacks
+    keep 4 or 6 blocks per workgroup."""
     monkeypatch.delenv("FD_TUNE", raising=False)
     talker = dict(synth.get_config("talker_s56"), exec_mode=0)
     sh = _stack_shapes(host, talker)
     assert sh["qkv"] == (1, 2, 1, 192)      # 96 blocks x 2 splits (9 splits of 4 blocks before)
-    assert sh["d.qkv"] == (1, 1, 1, 192)    # 192 blocks, no split
-    assert sh["d.gu"] == (1, 1, 1, 352)     # 352 blocks, no split, no reduce launch
+    assert sh["d.qkv"] == (1, 1, 1, 192)    # 192 blocks, no split (two blocks: only 96 workgroups)
+    assert sh["d.gu"] == (2, 1, 1, 176)     # 176 pairs of blocks, no split, no reduce launch
     assert sh["o"] == (2, 4, 1, 144)        # 36 pairs of blocks x 4 splits
     assert sh["down"] == (2, 6, 1, 216)     # 432 k-tiles in 6 splits (12 of 4 blocks before)
     assert sh["d.o"] == (2, 8, 1, 256) and sh["d.down"] == (2, 8, 1, 256)  # 16 splits before
