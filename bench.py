@@ -628,10 +628,19 @@ def summarize_launches(trace_csv, cmd, title):
     return "\n".join(lines) + "\n"
 
 
+def _fp32_three_products(cfg):
+    """fp32 stacks in the kernel sequence multiply in three bf16 products per
+    k-step (weights and rows split into bf16 high and low parts) unless
+    FD_TUNE holds x3=0."""
+    tune = os.environ.get("FD_TUNE", "")
+    off = any(kv.strip() == "x3=0" for kv in tune.split(","))
+    return cfg["act_dtype"] != "bf16" and not cfg.get("exec_mode", 0) and not off
+
+
 def _proj_in(cfg):
     """Form of the projections' session-row inputs the plan resolves to."""
     if cfg["act_dtype"] != "bf16":
-        return "f32"
+        return "f32 (split into bf16 high and low parts in the projections)" if _fp32_three_products(cfg) else "f32"
     p = cfg.get("proj_in", "auto")
     return "f16" if p == "auto" else p
 
@@ -639,6 +648,9 @@ def _proj_in(cfg):
 def _dtype_label(cfg):
     """Arithmetic types of the step: weights, projection inputs, cache."""
     if cfg["act_dtype"] != "bf16":
+        if _fp32_three_products(cfg):
+            return ("f32; projections as three bf16 products per k-step "
+                    "(w_lo*x_hi + w_hi*x_lo + w_hi*x_hi, fp32 sums)")
         return "f32"
     w = "fp8 weights" if cfg["w_dtype"] == "fp8" else "bf16 weights"
     x = {"f16": "fp16 projection inputs", "bf16x2": "two-part bf16 projection inputs"}[_proj_in(cfg)]

@@ -108,6 +108,7 @@ hipError_t pack(const fd::GemmShape& g, int wt, const void* s0, int r0, const vo
     a.dst = dst;
     a.scale = wt >= 2 ? (float*)(dst + (size_t)g.NB * g.KB * fd::kTileBytes) : nullptr;
     a.f16 = wt == 3;
+    a.x3 = g.x3;
     return fd::launch_pack(a, wt, st);
 }
 
@@ -244,7 +245,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         q.W = P(c, lo.qkv);
         q.wscale = wscale(c, lo.qkv, sp.qkv);
         q.X = Wk(c, pl.ws_xg);
-        q.K = sq.K; q.KB = sq.KB; q.NB = sq.NB; q.P = sq.P; q.MG = sq.MG; q.kh = sq.kh;
+        q.K = sq.K; q.KB = sq.KB; q.NB = sq.NB; q.P = sq.P; q.MG = sq.MG; q.kh = sq.kh; q.x3 = sq.x3;
         q.X_lo = two ? Wk(c, pl.ws_xg_lo) : nullptr;
         q.epi = fd::EPI_PLANES;
         q.y = (float*)Wk(c, pl.ws_qkv);
@@ -294,7 +295,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         o.wscale = wscale(c, lo.o, sp.o);
         o.X = Wk(c, pl.ws_o);
         o.X_lo = two ? Wk(c, pl.ws_o_lo) : nullptr;
-        o.K = so.K; o.KB = so.KB; o.NB = so.NB; o.P = so.P; o.MG = so.MG; o.kh = so.kh;
+        o.K = so.K; o.KB = so.KB; o.NB = so.NB; o.P = so.P; o.MG = so.MG; o.kh = so.kh; o.x3 = so.x3;
         o.cnt = so.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         o.epi = fd::EPI_RESID;
         o.x = (float*)Wk(c, pl.ws_x);
@@ -311,7 +312,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         u.W = P(c, lo.gu);
         u.wscale = wscale(c, lo.gu, sp.gu);
         u.X = Wk(c, pl.ws_xg);
-        u.K = su.K; u.KB = su.KB; u.NB = su.NB; u.P = su.P; u.MG = su.MG; u.kh = su.kh;
+        u.K = su.K; u.KB = su.KB; u.NB = su.NB; u.P = su.P; u.MG = su.MG; u.kh = su.kh; u.x3 = su.x3;
         u.cnt = su.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         u.epi = fd::EPI_GU;
         u.ss_in = (const float*)Wk(c, pl.ws_ss_f);
@@ -329,7 +330,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         dn.wscale = wscale(c, lo.down, sp.down);
         dn.X = Wk(c, pl.ws_h);
         dn.X_lo = two ? Wk(c, pl.ws_h_lo) : nullptr;
-        dn.K = sd.K; dn.KB = sd.KB; dn.NB = sd.NB; dn.P = sd.P; dn.MG = sd.MG; dn.kh = sd.kh;
+        dn.K = sd.K; dn.KB = sd.KB; dn.NB = sd.NB; dn.P = sd.P; dn.MG = sd.MG; dn.kh = sd.kh; dn.x3 = sd.x3;
         dn.cnt = sd.fused ? (int*)Wk(c, pl.ws_cnt) : nullptr;
         dn.epi = fd::EPI_RESID;
         dn.x = (float*)Wk(c, pl.ws_x);

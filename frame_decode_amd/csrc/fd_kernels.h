@@ -49,6 +49,9 @@ struct GemmArgs {
     int kh;                // row-split variant: k-halves per workgroup (1 or 2; 0 = 1)
     int f16;               // 2-byte stacks: X is one fp16 part (weights FP8 or fp16 codes), and
                            // the epilogue stores xg / h as fp16; else bf16
+    int x3;                // fp32 stacks: W holds bf16 high and low parts of the fp32 weights
+                           // (tiles of 16 rows x 32 k, see pack3_kernel) and the products are
+                           // three bf16 ones per k-step (lo*hi + hi*lo + hi*hi of weight*row)
 };
 
 struct AttnArgs {
@@ -135,6 +138,7 @@ struct PackArgs {
     float* scale;          // FP8 / fp16 weight codes: per packed row, max|w| / 448 or a power of
                            // two (see row_scale_kernel; 1 for a zero row)
     int f16;               // 1: fp16 codes (power-of-two scales)
+    int x3;                // fp32 source split into bf16 high and low tiles (KB: k-tiles of 32)
 };
 
 struct KvWriteArgs {
@@ -191,6 +195,14 @@ constexpr int gemm_stages(int NG, int MTG, int SX = 0, int W8 = 0) {
     return 48 / (NG + (1 + W8) * MTG * (1 + SX)) < 2
                ? 2
                : (48 / (NG + (1 + W8) * MTG * (1 + SX)) > 8 ? 8 : 48 / (NG + (1 + W8) * MTG * (1 + SX)));
+}
+// Ring depth of the three-product fp32 loop: a stage holds 2 * (NG + MTG)
+// 16-byte fragments; as many stages as ~232 registers allow next to the
+// accumulators and the split rows, at least 2, at most 8.
+constexpr int x3_stages(int NG, int MTG) {
+    return (232 - 4 * NG * MTG - 8) / (8 * (NG + MTG)) < 2
+               ? 2
+               : ((232 - 4 * NG * MTG - 8) / (8 * (NG + MTG)) > 8 ? 8 : (232 - 4 * NG * MTG - 8) / (8 * (NG + MTG)));
 }
 
 // Launchers (enqueue on `st`; return the launch error).

@@ -31,7 +31,7 @@ bool valid_split(const GemmShape& g, int P) {
     return P >= 1 && g.KB % P == 0 && g.KB / P >= 4;
 }
 
-GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool small) {
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool small, bool x3) {
     // Candidates: 6 or 4 weight blocks per workgroup (6 only while the
     // accumulators of a 5-tile m-group fit; small: also 2, which fills as
     // many CUs with half the splits), any split P that gives every wave at
@@ -42,7 +42,7 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool smal
     double best_score = -1e9;
     for (int NG : {6, 4, 2}) {
         GemmShape base = shape_with(N, K, KT, MT, NG, 1, cap);
-        if (NG == 6 && base.MTG > 5) continue;
+        if (NG == 6 && (base.MTG > 5 || x3)) continue;
         if (NG == 2 && !(small && small_blocks_ok(2, base.MTG))) continue;
         for (int P = 1; P <= 64; ++P) {
             if (!valid_split(base, P)) continue;
@@ -121,11 +121,11 @@ int tune_value(const char* key, int dflt) {
     return dflt;
 }
 
-GemmShape tuned(GemmShape g, const char* name, bool ns, int cap, bool small) {
+GemmShape tuned(GemmShape g, const char* name, bool ns, int cap, bool small, bool x3) {
     std::string n(name);
     int NG = tune_value((n + ".NG").c_str(), g.R);
     int P = tune_value((n + ".P").c_str(), g.P);
-    if (!(NG == 4 || (NG == 6 && g.MTG <= 5) || (ns && ns_blocks_ok(NG, g.MTG)) ||
+    if (!(NG == 4 || (NG == 6 && g.MTG <= 5 && !x3) || (ns && ns_blocks_ok(NG, g.MTG)) ||
           (small && small_blocks_ok(NG, g.MTG))))
         NG = g.R;
     GemmShape base = shape_with(g.N, g.K, g.KT, g.MG * g.MTG, NG, 1, cap);
@@ -136,20 +136,26 @@ GemmShape tuned(GemmShape g, const char* name, bool ns, int cap, bool small) {
         out.kh = kh == 2 && (out.KB / P) % 2 == 0 ? 2 : 1;
     }
     out.fused = P > 1 && NG <= 6 && tune_value((n + ".fused").c_str(), tune_value("fused", 0)) != 0;
+    out.x3 = x3 ? 1 : 0;
     return out;
 }
 
 // pre: prefix of the stack's tuning keys ("" main, "d." depth stack)
 // scaled: the packed matrices carry per-row scales (FP8 or fp16 codes)
-// small: the 1- and 2-block fp32 kernels may be chosen (kernel sequence)
+// small: the 1- and 2-block fp32 kernels may be chosen (kernel sequence);
+// x3: the fp32 projections run the three-product loop on tiles of 32 k
 void plan_stack(StackPlan& sp, const StackDims& dims, int KT, int MT, int S, int kv_fp8, bool w8,
-                bool scaled, uint64_t& off, bool ns, bool small, const std::string& pre) {
+                bool scaled, uint64_t& off, bool ns, bool small, bool x3, const std::string& pre) {
     sp.dims = dims;
-    const int cap = w8 ? kMaxMTG8 : kMaxMTG;
-    sp.qkv = tuned(choose_gemm(dims.qkv_n(), dims.d, KT, MT, 256, cap, small), (pre + "qkv").c_str(), ns, cap, small);
-    sp.o = tuned(choose_gemm(dims.d, dims.hq * dims.hd, KT, MT, 256, cap, small), (pre + "o").c_str(), ns, cap, small);
-    sp.gu = tuned(choose_gemm(2 * dims.f, dims.d, KT, MT, 256, cap, small), (pre + "gu").c_str(), ns, cap, small);
-    sp.down = tuned(choose_gemm(dims.d, dims.f, KT, MT, 256, cap, small), (pre + "down").c_str(), ns, cap, small);
+    const int cap = (w8 || x3) ? kMaxMTG8 : kMaxMTG;
+    const int kt = x3 ? 32 : KT;
+    auto pick = [&](int N, int K, const char* name) {
+        return tuned(choose_gemm(N, K, kt, MT, 256, cap, small, x3), (pre + name).c_str(), ns, cap, small, x3);
+    };
+    sp.qkv = pick(dims.qkv_n(), dims.d, "qkv");
+    sp.o = pick(dims.d, dims.hq * dims.hd, "o");
+    sp.gu = pick(2 * dims.f, dims.d, "gu");
+    sp.down = pick(dims.d, dims.f, "down");
     sp.layers.resize(dims.L);
     auto tiles = [scaled](const GemmShape& g) { return packed_matrix_bytes(g, scaled); };
     for (int l = 0; l < dims.L; ++l) {
@@ -280,9 +286,14 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         if (st != FD_OK) return st;
     }
     p.S = c.max_slots;
+    // fp32 stacks in the kernel sequence: one- and two-block projections,
+    // and the three-product loop (FD_TUNE "x3=0" keeps fp32 products)
+    const bool small = c.exec_mode == FD_EXEC_KERNELS && !p.wt;
+    const bool x3 = small && tune_value("x3", 1) != 0;
     // session rows padded to whole m-groups (at most kMaxMTG 16-row tiles
-    // each, kMaxMTG8 with FP8 weights) so the GEMM main loop needs no row checks
-    p.MT = padded_mtiles(c.max_slots, p.w8 ? kMaxMTG8 : kMaxMTG);
+    // each, kMaxMTG8 with FP8 weights or the three-product loop) so the GEMM
+    // main loop needs no row checks
+    p.MT = padded_mtiles(c.max_slots, (p.w8 || x3) ? kMaxMTG8 : kMaxMTG);
     p.Sp = p.MT * 16;
 
     uint64_t off = 0;
@@ -291,15 +302,14 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     // rows), launched as kernels (the persistent walk runs gemm_wg)
     const bool ns = c.exec_mode == FD_EXEC_KERNELS && p.wt && !p.w8;
     const bool scaled = p.wkind >= 2;
-    const bool small = c.exec_mode == FD_EXEC_KERNELS && !p.wt;
-    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, scaled, off, ns, small, "");
+    plan_stack(p.main, md, KT, p.MT, p.S, p.kv_fp8, p.w8, scaled, off, ns, small, x3, "");
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
         p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
         p.w_in = off;
         off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
-        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, false, off, false, small, "d.");
+        plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, false, off, false, small, x3, "d.");
     }
     if (p.head) {
         p.hshape = choose_gemm(c.vocab, c.d_model, KT, p.MT, 256, p.w8 ? kMaxMTG8 : kMaxMTG);

@@ -39,6 +39,8 @@ struct GemmShape {
     int counters = 0;
     bool fused = false;  // P > 1: the last workgroup of an n-group adds the partials (no reduce launch)
     int kh = 1;          // row-split variant: k-halves per workgroup (2: two waves per SIMD)
+    int x3 = 0;          // fp32 weights as bf16 high and low tiles of 32 k (2 KiB per tile),
+                         // three bf16 products per k-step (kernel sequence)
     int grid() const { return n_groups * P * MG; }
 };
 
@@ -150,13 +152,15 @@ constexpr uint64_t kWalkArgSlot = 512;
 // Bytes of one projection's packed weights: the tiles, then (FP8 or fp16
 // codes) one fp32 scale per output row.
 inline uint64_t packed_matrix_bytes(const GemmShape& g, bool scaled) {
-    return (uint64_t)g.NB * g.KB * kTileBytes + (scaled ? 4ull * g.NB * 16 : 0);
+    return (uint64_t)g.NB * g.KB * kTileBytes * (g.x3 ? 2 : 1) + (scaled ? 4ull * g.NB * 16 : 0);
 }
 
 // Tile choice for one projection (exposed for tests).
 // cap: most m-tiles per m-group (kMaxMTG, or kMaxMTG8 for FP8 weights).
-// small: one weight block per workgroup may be chosen (fp32 kernel sequence).
-GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap = kMaxMTG, bool small = false);
+// small: one or two weight blocks per workgroup may be chosen (fp32 kernel
+// sequence); x3: the three-product fp32 loop (no 6-block shapes).
+GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap = kMaxMTG, bool small = false,
+                      bool x3 = false);
 
 // Session rows padded to whole m-groups of at most `cap` 16-row tiles.
 inline int padded_mtiles(int slots, int cap) {

@@ -28,6 +28,7 @@
 namespace fd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -317,6 +318,36 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackArgs a) {
     *(u32x4*)(a.dst + tile * 1024 + (size_t)lane * 16) = w;
 }
 
+// fp32 weights as two bf16 parts: tiles [NB][K/32][2][64 lanes][16 B], the
+// high parts bf16(w) then the low parts bf16(w - bf16(w)) (together ~16
+// significant bits).  Lane l (row l%16, g = l/16) holds in slot j = 0..7
+// the k offset 16*(j/4) + 4g + j%4: the order in which the fp32 row
+// fragments of two consecutive 16-k tiles reach the lane, so one bf16
+// product of 32 k covers both.
+__global__ __launch_bounds__(256) void pack3_kernel(PackArgs a) {
+    size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t total = (size_t)(a.N / 16) * a.KB * 64;
+    if (id >= total) return;
+    const int lane = (int)(id & 63);
+    const size_t tile = id >> 6;
+    const int nb = (int)(tile / a.KB), kb = (int)(tile % a.KB);
+    const int n = nb * 16 + (lane & 15);
+    int row;
+    const float* src = (const float*)pack_src(a, n, &row) + (size_t)row * a.K + kb * 32 + (lane >> 4) * 4;
+    const f32x4 v0 = *(const f32x4*)src;
+    const f32x4 v1 = *(const f32x4*)(src + 16);
+    const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    u32x4 hi, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t h0 = f2bf(x[2 * q]), h1 = f2bf(x[2 * q + 1]);
+        hi[q] = h0 | (h1 << 16);
+        lo[q] = f2bf(x[2 * q] - bf2f(h0)) | (f2bf(x[2 * q + 1] - bf2f(h1)) << 16);
+    }
+    *(u32x4*)(a.dst + tile * 2048 + (size_t)lane * 16) = hi;
+    *(u32x4*)(a.dst + tile * 2048 + 1024 + (size_t)lane * 16) = lo;
+}
+
 // FP8 weights, step 2: tiles [NB][K/64][64 lanes][16 B] of codes of w / scale.
 // A tile is 16 rows x 64 k; lane l (row l%16, g = l/16) holds k 8g..8g+7 in
 // bytes 0..7 and k 32+8g..32+8g+7 in bytes 8..15, so the two halves are the
@@ -562,10 +593,18 @@ struct NoWait {
 // pack8_kernel) that each wave converts exactly to bf16 (SX 1) or fp16
 // (SX 2) operands for two activation k-tiles; the per-row scales multiply
 // the summed tiles.
-template <int WT, int NG, int MTG, int STG, int SX, int CO, int W8, class Wait>
+// X3 (fp32 stacks): the weight tiles hold bf16 high and low parts of 16
+// rows x 32 k (pack3_kernel); each k-step splits the rows' two fp32 16-k
+// fragments into bf16 high and low parts in registers and accumulates three
+// bf16 products, weight lo * row hi + weight hi * row lo + weight hi * row hi
+// (the lo * lo term, below 2^-16 of the product, is dropped).
+template <int WT, int NG, int MTG, int STG, int SX, int CO, int W8, int X3 = 0, class Wait>
 __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc_mem, Wait&& wait) {
     static_assert(!W8 || (WT && SX), "FP8 weights take two bf16 parts or one fp16 part");
     static_assert(SX <= 1 || WT, "fp16 inputs are a 2-byte stack's");
+    static_assert(!X3 || (!WT && !SX && !W8), "the three-product loop is the fp32 stacks'");
+    constexpr int WP = X3 ? 2 : 1;          // weight parts per tile
+    constexpr int XT = (W8 || X3) ? 2 : 1;  // activation k-tiles per weight tile
     constexpr int TWO = SX == 1;     // second (low) part of every fragment
     constexpr int F16 = SX == 2;     // fp16 operands
     constexpr bool SCALED = W8 || F16;  // per-row weight scales
@@ -592,7 +631,7 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     const u32x4* wp[NG];
 #pragma unroll
     for (int r = 0; r < NG; ++r)  // blocks past the matrix re-read the last one (never stored)
-        wp[r] = (const u32x4*)(a.W + (size_t)min(nb0 + r, a.NB - 1) * a.KB * 1024) + lane;
+        wp[r] = (const u32x4*)(a.W + (size_t)min(nb0 + r, a.NB - 1) * a.KB * 1024 * WP) + lane;
     // fragment (k-tile kb, m-tile mt) is 1 KiB at ((kb*MT + mt)*64 + lane) * 16 bytes
     const u32x4* xp = (const u32x4*)a.X + (size_t)mt0 * 64 + lane;
     const u32x4* xlp = TWO ? (const u32x4*)a.X_lo + (size_t)mt0 * 64 + lane : xp;
@@ -609,14 +648,14 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     // keeps enough bytes outstanding per CU to cover HBM latency.
     // (TWO: B[.][MTG + t] holds the low part of m-tile t)
     constexpr int NBX = MTG * (1 + TWO);    // fragments of one activation k-tile
-    constexpr int NB_ = NBX * (1 + W8);     // per weight tile (FP8: two activation k-tiles)
-    u32x4 A[STG][NG];
+    constexpr int NB_ = NBX * XT;           // per weight tile (FP8, X3: two activation k-tiles)
+    u32x4 A[STG][NG * WP];
     BT B[STG][NB_];
     auto load_x = [&](BT (&Bd)[NB_], int j) {
         const int kb = kb0 + wave + 4 * j;
 #pragma unroll
-        for (int tt = 0; tt <= W8; ++tt) {
-            const size_t kx = (size_t)((1 + W8) * kb + tt) * xk;
+        for (int tt = 0; tt < XT; ++tt) {
+            const size_t kx = (size_t)(XT * kb + tt) * xk;
 #pragma unroll
             for (int t = 0; t < MTG; ++t) Bd[tt * NBX + t] = __builtin_bit_cast(BT, xp[kx + t * 64]);
             if constexpr (TWO) {
@@ -625,19 +664,48 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
             }
         }
     };
-    auto load_w = [&](u32x4 (&Ad)[NG], int j) {
+    auto load_w = [&](u32x4 (&Ad)[NG * WP], int j) {
         const int kb = kb0 + wave + 4 * j;
 #pragma unroll
-        for (int r = 0; r < NG; ++r) Ad[r] = __builtin_nontemporal_load(&wp[r][(size_t)kb * 64]);
+        for (int r = 0; r < NG; ++r)
+#pragma unroll
+            for (int p = 0; p < WP; ++p) Ad[r * WP + p] = __builtin_nontemporal_load(&wp[r][((size_t)kb * WP + p) * 64]);
     };
-    auto load = [&](u32x4 (&Ad)[NG], BT (&Bd)[NB_], int j) {
+    auto load = [&](u32x4 (&Ad)[NG * WP], BT (&Bd)[NB_], int j) {
         load_x(Bd, j);
         load_w(Ad, j);
     };
     // (high parts of every tile first, then low parts: consecutive products
     // never chain on one accumulator)
-    auto mma = [&](u32x4 (&As)[NG], BT (&Bs)[NB_]) {
-        if constexpr (W8) {
+    auto mma = [&](u32x4 (&As)[NG * WP], BT (&Bs)[NB_]) {
+        if constexpr (X3) {
+            // per m-tile: split the 8 fp32 row values (k offsets as in
+            // pack3_kernel) into bf16 high and low parts, then the three
+            // products with every weight block (consecutive products go to
+            // different accumulators where NG > 1)
+#pragma unroll
+            for (int t = 0; t < MTG; ++t) {
+                u32x4 xh, xl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4& src = q < 2 ? Bs[t] : Bs[NBX + t];
+                    const float x0 = src[2 * (q & 1)], x1 = src[2 * (q & 1) + 1];
+                    const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+                    const uint32_t hu = __builtin_bit_cast(uint32_t, h);
+                    const bf16x2 l = {(__bf16)(x0 - __uint_as_float(hu << 16)),
+                                      (__bf16)(x1 - __uint_as_float(hu & 0xFFFF0000u))};
+                    xh[q] = hu;
+                    xl[q] = __builtin_bit_cast(uint32_t, l);
+                }
+#pragma unroll
+                for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+                    for (int r = 0; r < NG; ++r)
+                        acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, As[r * WP + (pass == 0 ? 1 : 0)]),
+                            __builtin_bit_cast(bf16x8, pass == 1 ? xl : xh), acc[r][t], 0, 0, 0);
+            }
+        } else if constexpr (W8) {
             // E4M3 -> bf16 or fp16 is exact (3 mantissa bits, exponents
             // -9..8): codes c0..c7 of each half become one operand
             u32x4 f[2][NG];
@@ -812,10 +880,10 @@ __device__ __forceinline__ void gemm_wg(const GemmArgs& a, int bid, f32x4* s_acc
     gemm_finish<WT, NG, MTG, 4, OWN, CO>(a, v, ti, ng, mt0, 0, MTG, s_rstd);
 }
 
-template <int WT, int NG, int MTG, int STG, int SX, int W8 = 0>
+template <int WT, int NG, int MTG, int STG, int SX, int W8 = 0, int X3 = 0>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     __shared__ f32x4 s_acc[4 * NG * MTG * 64];
-    gemm_wg<WT, NG, MTG, STG, SX, 0, W8>(a, blockIdx.x, s_acc, NoWait{});
+    gemm_wg<WT, NG, MTG, STG, SX, 0, W8, X3>(a, blockIdx.x, s_acc, NoWait{});
 }
 
 // Adds the P k-split partial tiles of one m-tile t of an (n-group, m-group)
@@ -1870,7 +1938,10 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int 
 hipError_t launch_pack(const PackArgs& a, int wt, hipStream_t st) {
     const size_t total = (size_t)(a.N / 16) * a.KB * 64;
     const unsigned blocks = (unsigned)((total + 255) / 256);
-    if (wt == 2 || wt == 3) {
+    if (a.x3) {
+        if (wt != 0 || a.K % 32 || a.KB * 32 != a.K) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(pack3_kernel, dim3(blocks), dim3(256), 0, st, a);
+    } else if (wt == 2 || wt == 3) {
         if (!a.scale || a.f16 != (wt == 3)) return hipErrorInvalidValue;
         hipLaunchKernelGGL(row_scale_kernel, dim3(a.N), dim3(256), 0, st, a);
         if (wt == 2) hipLaunchKernelGGL(pack8_kernel, dim3(blocks), dim3(256), 0, st, a);
@@ -1930,6 +2001,25 @@ static hipError_t gemm_f16(const GemmArgs& a, int MTG, int grid, hipStream_t st)
                 if (MTG == 8) { gemm_f16_mt<4, 8>(a, grid, st); break; }
             }
             return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// fp32 weights as bf16 high and low tiles, three products per k-step: 1, 2
+// or 4 blocks per workgroup, up to 5 m-tiles
+template <int NG>
+static hipError_t gemm_x3(const GemmArgs& a, int MTG, int grid, hipStream_t st) {
+    if (a.X_lo || a.wscale || a.f16 || a.KB * 32 != a.K) return hipErrorInvalidValue;
+    switch (MTG) {
+#define FD_G(MT)                                                                                        \
+    case MT:                                                                                            \
+        hipLaunchKernelGGL((gemm_kernel<0, NG, MT, x3_stages(NG, MT), 0, 0, 1>), dim3(grid), dim3(256), 0, st, a); \
+        if (a.P > 1 && a.epi != EPI_PLANES && !a.cnt)                                                   \
+            hipLaunchKernelGGL((gemm_reduce_kernel<0, NG, MT>), dim3(grid / a.P * MT), dim3(256), 0, st, a); \
+        break;
+        FD_G(1) FD_G(2) FD_G(3) FD_G(4) FD_G(5)
+#undef FD_G
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -2007,6 +2097,13 @@ static hipError_t gemm_ns(const GemmArgs& a, int MTG, int grid, hipStream_t st) 
 // or one fp16 part with a.f16), 3 fp16 weight codes (one fp16 part)
 hipError_t launch_gemm(const GemmArgs& a, int wt, int NG, int MTG, int grid, hipStream_t st) {
     if (a.f16 && wt != 2 && wt != 3) return hipErrorInvalidValue;
+    if (a.x3) {
+        if (wt != 0) return hipErrorInvalidValue;
+        if (NG == 4) return gemm_x3<4>(a, MTG, grid, st);
+        if (NG == 2) return gemm_x3<2>(a, MTG, grid, st);
+        if (NG == 1) return gemm_x3<1>(a, MTG, grid, st);
+        return hipErrorInvalidValue;
+    }
     if ((wt == 1 || wt == 3) && NG == 8) return gemm_ns<2>(a, MTG, grid, st);
     if ((wt == 1 || wt == 3) && NG == 12) return gemm_ns<3>(a, MTG, grid, st);
     if ((wt == 1 || wt == 3) && NG == 16) return gemm_ns<4>(a, MTG, grid, st);

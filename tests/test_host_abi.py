@@ -276,9 +276,12 @@ def test_one_block_projections_for_fp32_stacks(host, monkeypatch):
     assert all(v[0] in (4, 6) for v in walk.values())
     big = _stack_shapes(host, synth.get_config("7b_s80_p1499"))
     assert set(big) == {"qkv", "o", "gu", "down"} and all(v[0] in (4, 6) for v in big.values())
-    monkeypatch.setenv("FD_TUNE", "d.gu.NG=6,d.gu.P=4,o.NG=1,o.P=2")
+    monkeypatch.setenv("FD_TUNE", "d.gu.NG=4,d.gu.P=4,o.NG=1,o.P=2,qkv.NG=6")
     sh = _stack_shapes(host, talker)
-    assert sh["d.gu"] == (6, 4, 1, 236) and sh["o"] == (1, 2, 1, 144)
+    assert sh["d.gu"] == (4, 4, 1, 352) and sh["o"] == (1, 2, 1, 144)
+    assert sh["qkv"][0] == 1  # (6 blocks: not built for the three-product loop)
+    monkeypatch.setenv("FD_TUNE", "x3=0,d.gu.NG=6,d.gu.P=4")  # fp32 products
+    assert _stack_shapes(host, talker)["d.gu"] == (6, 4, 1, 236)
     assert _stack_shapes(host, dict(talker, exec_mode=1))["o"][0] in (4, 6)
 
 
