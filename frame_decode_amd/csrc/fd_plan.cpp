@@ -58,16 +58,17 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool smal
             }
         }
     }
-    // Two or one weight blocks per workgroup without the k-split (small:
+    // Two or one weight blocks per workgroup with no or 2 k-splits (small:
     // fp32 stacks in the kernel sequence).  Each activation k-tile is then
     // fetched once per 2 or 1 blocks rather than once per 4-6, which pays
-    // where it removes the split (no reduce launch, fewer planes for
-    // attention to add) and still fills two thirds of the CUs in at most
-    // two rounds: the first of (2 blocks, no split), (1, no split),
-    // (1, 2 splits) that does.
+    // where it removes most of the split (no reduce launch, fewer planes
+    // for attention to add) and still fills two thirds of the CUs in at
+    // most two rounds: the first of (2 blocks, no split), (2, 2 splits),
+    // (1, no split), (1, 2 splits) that does.
     if (small && best.P > 1) {
-        const int cand[3][2] = {{2, 1}, {1, 1}, {1, 2}};
+        const int cand[4][2] = {{2, 1}, {2, 2}, {1, 1}, {1, 2}};
         for (const auto& c : cand) {
+            if (c[0] == best.R && c[1] == best.P) break;  // the score's choice comes first
             if (c[1] >= best.P) continue;
             GemmShape g = shape_with(N, K, KT, MT, c[0], c[1], cap);
             if (small_blocks_ok(c[0], g.MTG) && valid_split(g, c[1]) && 3 * g.grid() >= 2 * n_cu &&

@@ -255,18 +255,19 @@ def test_row_split_projection_plan(host, monkeypatch):
 
 
 def test_one_block_projections_for_fp32_stacks(host, monkeypatch):
-    """fp32 stacks in the kernel sequence drop the k-split with two or one
-    weight blocks per workgroup where that still fills two thirds of the
-    CUs (the talker's depth gate/up and QKV; its main QKV keeps 2 splits of
-    one block), and take two blocks where those fill as many CUs as four
-    with fewer splits (its O and down projections); the main gate/up, where
-    two blocks only tie, keeps four.  The persistent walk and bf16 stacks
-    keep 4 or 6 blocks per workgroup."""
+    """fp32 stacks in the kernel sequence cut the k-split to none or 2 with
+    two or one weight blocks per workgroup where that still fills two
+    thirds of the CUs (the talker's depth gate/up with no split, its depth
+    QKV with 2 splits of two blocks, its main QKV with 2 splits of one),
+    and take two blocks where those fill as many CUs as four with fewer
+    splits (its O and down projections); the main gate/up, where two blocks
+    only tie, keeps four.  The persistent walk and bf16 stacks keep 4 or 6
+    blocks per workgroup."""
     monkeypatch.delenv("FD_TUNE", raising=False)
     talker = dict(synth.get_config("talker_s56"), exec_mode=0)
     sh = _stack_shapes(host, talker)
     assert sh["qkv"] == (1, 2, 1, 192)      # 96 blocks x 2 splits (9 splits of 4 blocks before)
-    assert sh["d.qkv"] == (1, 1, 1, 192)    # 192 blocks, no split (two blocks: only 96 workgroups)
+    assert sh["d.qkv"] == (2, 2, 1, 192)    # 96 pairs of blocks x 2 splits (8 splits of 6 before)
     assert sh["d.gu"] == (2, 1, 1, 176)     # 176 pairs of blocks, no split, no reduce launch
     assert sh["o"] == (2, 4, 1, 144)        # 36 pairs of blocks x 4 splits
     assert sh["down"] == (2, 6, 1, 216)     # 432 k-tiles in 6 splits (12 of 4 blocks before)
