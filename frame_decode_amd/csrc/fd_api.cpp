@@ -856,7 +856,7 @@ fd_status step_impl(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, v
         fd::GemmArgs g{};
         g.W = P(c, pl.w_in);
         g.X = Wk(c, pl.ws_yw);
-        g.K = pl.win.K; g.KB = pl.win.KB; g.NB = pl.win.NB; g.P = pl.win.P; g.MG = pl.win.MG;
+        g.K = pl.win.K; g.KB = pl.win.KB; g.NB = pl.win.NB; g.P = pl.win.P; g.MG = pl.win.MG; g.x3 = pl.win.x3;
         g.MT = pl.MT; g.Sp = pl.Sp; g.S = pl.S;
         g.part = (float*)Wk(c, pl.ws_part);
         g.epi = fd::EPI_F32;

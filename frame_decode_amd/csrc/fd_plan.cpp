@@ -307,9 +307,11 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     if (p.depth) {
         StackDims dd{c.depth_layers, c.depth_d, c.depth_heads, c.depth_kv_heads, c.depth_head_dim,
                      c.depth_ffn, c.depth_steps};
-        p.win = choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
+        p.win = x3 ? choose_gemm(c.depth_d, c.d_model, 32, p.MT, 256, kMaxMTG8, small, true)
+                   : choose_gemm(c.depth_d, c.d_model, KT, p.MT, 256);
+        p.win.x3 = x3 ? 1 : 0;
         p.w_in = off;
-        off = align_up(off + (uint64_t)p.win.NB * p.win.KB * kTileBytes);
+        off = align_up(off + packed_matrix_bytes(p.win, false));
         plan_stack(p.dstack, dd, KT, p.MT, p.S, 0, false, false, off, false, small, x3, "d.");
     }
     if (p.head) {

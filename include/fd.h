@@ -78,7 +78,7 @@ typedef int32_t fd_status;
  *   FD_PROJ_AUTO: FD_PROJ_F16.
  * Both forms run in either exec_mode.  FD_F32 profiles take FD_PROJ_AUTO
  * (fp32 rows); other values give FD_E_UNSUPPORTED.  In FD_EXEC_KERNELS the
- * projections of FD_F32 stacks (not the depth input projection or the
+ * projections of FD_F32 stacks and the depth input projection (not the
  * output head) multiply as three bf16 products per k-step: fd_init stores
  * each weight as hi = bf16(w) and lo = bf16(w - hi), each session row value
  * is split the same way as it is loaded, and the matrix cores add
