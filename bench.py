@@ -604,7 +604,7 @@ def summarize_trace(stats_csv, cmd, title):
 
 # setup kernels of a benchmark run (weight packing, cache prefill, torch's
 # fills and copies, the bandwidth probe): not part of the decode step
-_SETUP = ("pack_kernel", "pack8_kernel", "pack16_kernel", "row_scale_kernel", "kv_write_kernel",
+_SETUP = ("pack_kernel", "pack3_kernel", "pack8_kernel", "pack16_kernel", "row_scale_kernel", "kv_write_kernel",
           "read_probe_kernel", "elementwise", "rocclr", "fill_u32")
 
 
@@ -630,11 +630,11 @@ def summarize_launches(trace_csv, cmd, title):
 
 def _fp32_three_products(cfg):
     """fp32 stacks in the kernel sequence multiply in three bf16 products per
-    k-step (weights and rows split into bf16 high and low parts) unless
-    FD_TUNE holds x3=0."""
+    k-step (weights and rows split into bf16 high and low parts) only when
+    FD_TUNE holds x3=1; by default they multiply in fp32."""
     tune = os.environ.get("FD_TUNE", "")
-    off = any(kv.strip() == "x3=0" for kv in tune.split(","))
-    return cfg["act_dtype"] != "bf16" and not cfg.get("exec_mode", 0) and not off
+    on = any(kv.strip() == "x3=1" for kv in tune.split(","))
+    return cfg["act_dtype"] != "bf16" and not cfg.get("exec_mode", 0) and on
 
 
 def _proj_in(cfg):

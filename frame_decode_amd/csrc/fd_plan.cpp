@@ -63,11 +63,16 @@ GemmShape choose_gemm(int N, int K, int KT, int MT, int n_cu, int cap, bool smal
     // fetched once per 2 or 1 blocks rather than once per 4-6, which pays
     // where it removes most of the split (no reduce launch, fewer planes
     // for attention to add) and still fills two thirds of the CUs in at
-    // most two rounds: the first of (2 blocks, no split), (2, 2 splits),
-    // (1, no split), (1, 2 splits) that does.
+    // most two rounds: the first of (2 blocks, no split), (1, no split),
+    // (1, 2 splits) that does; with the three-product loop, whose products
+    // cost less per block, (2 blocks, 2 splits) comes second.
     if (small && best.P > 1) {
-        const int cand[4][2] = {{2, 1}, {2, 2}, {1, 1}, {1, 2}};
-        for (const auto& c : cand) {
+        const int cand_f32[3][2] = {{2, 1}, {1, 1}, {1, 2}};
+        const int cand_x3[4][2] = {{2, 1}, {2, 2}, {1, 1}, {1, 2}};
+        const int (*cand)[2] = x3 ? cand_x3 : cand_f32;
+        const int n_cand = x3 ? 4 : 3;
+        for (int i = 0; i < n_cand; ++i) {
+            const int* c = cand[i];
             if (c[0] == best.R && c[1] == best.P) break;  // the score's choice comes first
             if (c[1] >= best.P) continue;
             GemmShape g = shape_with(N, K, KT, MT, c[0], c[1], cap);
@@ -287,10 +292,11 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
         if (st != FD_OK) return st;
     }
     p.S = c.max_slots;
-    // fp32 stacks in the kernel sequence: one- and two-block projections,
-    // and the three-product loop (FD_TUNE "x3=0" keeps fp32 products)
+    // fp32 stacks in the kernel sequence: one- and two-block projections;
+    // the three-product loop only on request (FD_TUNE "x3=1": ~16-bit
+    // operands, not the exact fp32 products the fp32 path is defined by)
     const bool small = c.exec_mode == FD_EXEC_KERNELS && !p.wt;
-    const bool x3 = small && tune_value("x3", 1) != 0;
+    const bool x3 = small && tune_value("x3", 0) != 0;
     // session rows padded to whole m-groups (at most kMaxMTG 16-row tiles
     // each, kMaxMTG8 with FP8 weights or the three-product loop) so the GEMM
     // main loop needs no row checks

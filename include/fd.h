@@ -77,14 +77,16 @@ typedef int32_t fd_status;
  *     FD_PROJ_F16.
  *   FD_PROJ_AUTO: FD_PROJ_F16.
  * Both forms run in either exec_mode.  FD_F32 profiles take FD_PROJ_AUTO
- * (fp32 rows); other values give FD_E_UNSUPPORTED.  In FD_EXEC_KERNELS the
- * projections of FD_F32 stacks and the depth input projection (not the
- * output head) multiply as three bf16 products per k-step: fd_init stores
- * each weight as hi = bf16(w) and lo = bf16(w - hi), each session row value
- * is split the same way as it is loaded, and the matrix cores add
- * w_lo*x_hi + w_hi*x_lo + w_hi*x_hi with fp32 sums (~16 significant bits
- * per operand; the dropped w_lo*x_lo term is below 2^-16 of the product).
- * The weight bytes are those of fp32.  FD_EXEC_WALK multiplies in fp32.
+ * (fp32 rows); other values give FD_E_UNSUPPORTED.  FD_F32 stacks multiply
+ * in fp32 (exact fp32 products, fp32 sums; no TF32-like reduction).  As a
+ * measurement option only (environment FD_TUNE containing "x3=1" at
+ * fd_plan / fd_init, FD_EXEC_KERNELS), their projections and the depth
+ * input projection instead multiply as three bf16 products per k-step:
+ * each weight is stored as hi = bf16(w) and lo = bf16(w - hi), each
+ * session row value is split the same way as it is loaded, and the matrix
+ * cores add w_lo*x_hi + w_hi*x_lo + w_hi*x_hi with fp32 sums (~16
+ * significant bits per operand; the dropped w_lo*x_lo term is below 2^-16
+ * of the product), in the weight bytes of fp32.
  */
 #define FD_PROJ_AUTO   0
 #define FD_PROJ_F16    1

@@ -237,6 +237,26 @@ def test_fp32_gqa_with_depth_loop(exec_mode):
     _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
 
 
+@pytest.mark.parametrize("max_slots", [5, 56, 90])
+def test_fp32_three_product_projections(max_slots):
+    """The opt-in three-product fp32 projections (FD_TUNE x3=1: weights and
+    rows as bf16 high and low parts, w_lo*x_hi + w_hi*x_lo + w_hi*x_hi with
+    fp32 sums) on the talker geometry with its depth loop and input
+    projection, with one, four and (two m-groups of at most five) six
+    16-row tiles of sessions: 1e-3, cache indexing bit-exact."""
+    cfg = synth.scaled_config("talker_s56", n_layers=2, d_model=384, d_ffn=768, max_slots=max_slots,
+                              max_context=300, depth_layers=2, depth_d=256, depth_heads=2,
+                              depth_kv_heads=2, depth_ffn=512, exec_mode=0)
+    model = synth.Model(cfg, gain_noise=True)
+    start = [0, 63, 64, 200] if max_slots == 5 else [(37 * i) % 290 for i in range(max_slots - 2)]
+    os.environ["FD_TUNE"] = "x3=1"
+    try:
+        ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 2, tol=1e-3)
+    finally:
+        del os.environ["FD_TUNE"]
+    _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
+
+
 def test_admission_and_free_keep_launch_shape():
     """Sessions freed and admitted between steps: new sessions start at
     position 0 in the lowest free slot, equal a fresh oracle session, and

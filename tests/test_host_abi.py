@@ -257,17 +257,18 @@ def test_row_split_projection_plan(host, monkeypatch):
 def test_one_block_projections_for_fp32_stacks(host, monkeypatch):
     """fp32 stacks in the kernel sequence cut the k-split to none or 2 with
     two or one weight blocks per workgroup where that still fills two
-    thirds of the CUs (the talker's depth gate/up with no split, its depth
-    QKV with 2 splits of two blocks, its main QKV with 2 splits of one),
-    and take two blocks where those fill as many CUs as four with fewer
-    splits (its O and down projections); the main gate/up, where two blocks
-    only tie, keeps four.  The persistent walk and bf16 stacks keep 4 or 6
-    blocks per workgroup."""
+    thirds of the CUs (the talker's depth gate/up with two blocks and its
+    depth QKV with one, no split; its main QKV with 2 splits of one), and
+    take two blocks where those fill as many CUs as four with fewer splits
+    (its O and down projections); the main gate/up, where two blocks only
+    tie, keeps four.  With the opt-in three-product loop (tiles of 32 k, no
+    6-block shapes) the depth QKV takes 2 splits of two blocks.  The
+    persistent walk and bf16 stacks keep 4 or 6 blocks per workgroup."""
     monkeypatch.delenv("FD_TUNE", raising=False)
     talker = dict(synth.get_config("talker_s56"), exec_mode=0)
     sh = _stack_shapes(host, talker)
     assert sh["qkv"] == (1, 2, 1, 192)      # 96 blocks x 2 splits (9 splits of 4 blocks before)
-    assert sh["d.qkv"] == (2, 2, 1, 192)    # 96 pairs of blocks x 2 splits (8 splits of 6 before)
+    assert sh["d.qkv"] == (1, 1, 1, 192)    # 192 blocks, no split (8 splits of 6 before)
     assert sh["d.gu"] == (2, 1, 1, 176)     # 176 pairs of blocks, no split, no reduce launch
     assert sh["o"] == (2, 4, 1, 144)        # 36 pairs of blocks x 4 splits
     assert sh["down"] == (2, 6, 1, 216)     # 432 k-tiles in 6 splits (12 of 4 blocks before)
@@ -277,12 +278,16 @@ def test_one_block_projections_for_fp32_stacks(host, monkeypatch):
     assert all(v[0] in (4, 6) for v in walk.values())
     big = _stack_shapes(host, synth.get_config("7b_s80_p1499"))
     assert set(big) == {"qkv", "o", "gu", "down"} and all(v[0] in (4, 6) for v in big.values())
-    monkeypatch.setenv("FD_TUNE", "d.gu.NG=4,d.gu.P=4,o.NG=1,o.P=2,qkv.NG=6")
+    monkeypatch.setenv("FD_TUNE", "d.gu.NG=6,d.gu.P=4,o.NG=1,o.P=2")
     sh = _stack_shapes(host, talker)
-    assert sh["d.gu"] == (4, 4, 1, 352) and sh["o"] == (1, 2, 1, 144)
+    assert sh["d.gu"] == (6, 4, 1, 236) and sh["o"] == (1, 2, 1, 144)
+    monkeypatch.setenv("FD_TUNE", "x3=1")
+    sh = _stack_shapes(host, talker)
+    assert sh["d.qkv"] == (2, 2, 1, 192)    # 96 pairs of blocks x 2 splits
+    monkeypatch.setenv("FD_TUNE", "x3=1,qkv.NG=6,d.gu.NG=4,d.gu.P=4")
+    sh = _stack_shapes(host, talker)
     assert sh["qkv"][0] == 1  # (6 blocks: not built for the three-product loop)
-    monkeypatch.setenv("FD_TUNE", "x3=0,d.gu.NG=6,d.gu.P=4")  # fp32 products
-    assert _stack_shapes(host, talker)["d.gu"] == (6, 4, 1, 236)
+    assert sh["d.gu"] == (4, 4, 1, 352)     # 32 k-tiles of 32 in 4 splits
     assert _stack_shapes(host, dict(talker, exec_mode=1))["o"][0] in (4, 6)
 
 
@@ -474,6 +479,15 @@ def test_fp32_block_counts_stay_within_the_built_kernels(host, slots, monkeypatc
                 # (the depth stack has the main stack's rows, so the same tiling)
                 assert mtg[n.split(".")[-1]] <= 5, (slots, n, R)
             assert P >= 1 and kh == 1 and grid % P == 0
+    # the opt-in three-product loop is built for 1, 2 and 4 blocks and at
+    # most 5 row tiles per m-group (the rows are padded to such m-groups)
+    monkeypatch.setenv("FD_TUNE", "x3=1")
+    cfg = dict(base, exec_mode=0)
+    mt_out = (ctypes.c_int32 * 11)()
+    assert host.fdh_stack_mtiles(ctypes.byref(config_from_dict(cfg)), mt_out) == FD_OK
+    assert all(1 <= mt_out[2 + 2 * i] <= 5 for i in range(4))
+    assert mt_out[1] * mt_out[2] == mt_out[0] and mt_out[0] * 16 >= slots
+    assert all(v[0] in (1, 2, 4) for v in _stack_shapes(host, cfg).values())
 
 
 def test_stale_slots_after_an_interrupted_step(host):
