@@ -82,6 +82,7 @@ const float* wscale(const fd_ctx* c, uint64_t off, const fd::GemmShape& g) {
 
 int32_t* slot_active(const fd_ctx* c) { return (int32_t*)c->buf.slot_table; }
 int32_t* slot_pos(const fd_ctx* c) { return (int32_t*)c->buf.slot_table + c->plan.S; }
+int32_t* slot_order(const fd_ctx* c) { return (int32_t*)c->buf.slot_table + 2 * c->plan.S; }
 
 fd_status check_layer(const fd_layer_weights& lw) {
     if (!lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.w_gate || !lw.w_up || !lw.w_down ||
@@ -274,6 +275,7 @@ hipError_t run_stack(fd_ctx* c, const fd::StackPlan& sp, const CacheRef& cache, 
         at.slot_stride = cache.slot; at.kv_stride = cache.kv; at.head_stride = cache.head; at.pos_stride = cache.pos;
         at.active = slot_active(c);
         at.pos = slot_pos(c);
+        at.order = pos_override < 0 ? slot_order(c) : nullptr;  // (depth rows: all one length)
         at.pos_override = pos_override;
         at.S = pl.S; at.hq = d.hq; at.hkv = d.hkv; at.tc = sp.attn.tc; at.n_chunks = sp.attn.n_chunks;
         at.T = d.T;
@@ -451,6 +453,7 @@ hipError_t build_walk(fd_ctx* c, hipStream_t s, std::string* err) {
             at.pos_stride = cache.pos;
             at.active = slot_active(c);
             at.pos = slot_pos(c);
+            at.order = pos_override < 0 ? slot_order(c) : nullptr;
             at.pos_override = pos_override;
             at.S = pl.S; at.hq = z.hq; at.hkv = z.hkv; at.tc = sp.attn.tc; at.n_chunks = sp.attn.n_chunks;
             at.T = z.T;
@@ -635,7 +638,7 @@ hipError_t flush_slots(fd_ctx* c, hipStream_t st) {
     if (c->ev_used[i]) e = hipEventSynchronize(c->ev[i]);
     if (e != hipSuccess) return e;
     c->slots.image(c->pinned[i]);
-    e = hipMemcpyAsync(c->buf.slot_table, c->pinned[i], 8ull * c->plan.S, hipMemcpyHostToDevice, st);
+    e = hipMemcpyAsync(c->buf.slot_table, c->pinned[i], 12ull * c->plan.S, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return e;
     e = hipEventRecord(c->ev[i], st);
     if (e != hipSuccess) return e;
@@ -708,7 +711,7 @@ fd_status fd_init(const fd_config* cfg, const fd_weights* w, const fd_buffers* b
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipGetDevice(&c->device);
     for (int i = 0; i < kRing && e == hipSuccess; ++i) {
-        e = hipHostMalloc((void**)&c->pinned[i], 8ull * p.S, hipHostMallocDefault);
+        e = hipHostMalloc((void**)&c->pinned[i], 12ull * p.S, hipHostMallocDefault);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
     }
     // scales to the host (FP8 only) for the derived tables

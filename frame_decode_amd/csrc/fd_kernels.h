@@ -72,6 +72,8 @@ struct AttnArgs {
     uint64_t slot_stride, kv_stride, head_stride, pos_stride;
     const int* active;
     const int* pos;
+    const int* order;      // or null: task row r runs slot order[r] (a permutation of the
+                           // slots, longest windows first); null: slot r
     int pos_override;      // >= 0: every row is at this position (depth stack)
     int S, hq, hkv, tc, n_chunks;
     int T;                 // cache positions per slot

@@ -466,7 +466,7 @@ fd_status make_plan(const fd_config& c, Plan* out, std::string* err) {
     p.kv_layer_stride = p.kv_kv_stride * 2;
     p.kv_slot_stride = p.kv_layer_stride * m.L;
     p.kv_bytes_total = std::max<uint64_t>(p.kv_slot_stride * p.S, kAlign);
-    p.slot_table_bytes = align_up(8ull * p.S);
+    p.slot_table_bytes = align_up(12ull * p.S);  // active, pos, attention task order
     *out = p;
     return FD_OK;
 }

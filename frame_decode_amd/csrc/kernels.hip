@@ -1234,11 +1234,12 @@ __device__ __forceinline__ void attn_wg(const AttnArgs& a, int bid, Wait&& wait)
     const int chunk = bid % a.n_chunks;
     bid /= a.n_chunks;
     const int g = bid % a.hkv;
-    const int s = bid / a.hkv;
-    if (s >= a.S) {
+    const int row = bid / a.hkv;
+    if (row >= a.S) {
         stamp_all();
         return;
     }
+    const int s = a.order ? a.order[row] : row;
     constexpr int QPH = D / 4;                  // 4-element quads per head
     constexpr int NQ = ((G + 2) * QPH + 255) / 256;
     // planes loaded at once (more are added in rounds): 8 where the

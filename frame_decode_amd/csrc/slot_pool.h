@@ -7,7 +7,9 @@
 // so a failed call leaves the pool as it was.
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
+#include <numeric>
 #include <vector>
 
 #include "../../include/fd.h"
@@ -127,12 +129,24 @@ public:
     void clear_dirty() { dirty_ = false; }
     void mark_dirty() { dirty_ = true; }
 
-    // Device image: int32 active[S] followed by int32 pos[S].
+    // Device image: int32 active[S], int32 pos[S], then int32 order[S]: the
+    // active slots by descending position (ties by slot), then the inactive
+    // ones ascending.  Attention takes its (slot, head) tasks in this order,
+    // so the longest windows start first and the shortest fill the last
+    // round (positions advance together between uploads, so the order
+    // holds until the next change).
     void image(int32_t* dst) const {
-        for (int s = 0; s < size(); ++s) {
+        const int n = size();
+        for (int s = 0; s < n; ++s) {
             dst[s] = active_[s];
-            dst[size() + s] = pos_[s];
+            dst[n + s] = pos_[s];
         }
+        int32_t* order = dst + 2 * n;
+        std::iota(order, order + n, 0);
+        std::stable_sort(order, order + n, [&](int32_t a, int32_t b) {
+            if (active_[a] != active_[b]) return active_[a] > active_[b];
+            return active_[a] && pos_[a] > pos_[b];
+        });
     }
 
 private:

@@ -185,7 +185,8 @@ typedef struct {
     uint64_t packed_weights; /* weights in the kernels' tile layout + constant tables */
     uint64_t kv_arena;       /* the slot-pooled cache, layout in fd_kv_view */
     uint64_t workspace;      /* activations, partial results, counters */
-    uint64_t slot_table;     /* device copy of per-slot active flag and position */
+    uint64_t slot_table;     /* device copy of per-slot active flag and position, and the
+                                order attention takes the slots in */
 } fd_sizes;
 
 /*
@@ -417,7 +418,10 @@ fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, in
  * (the norm, rotary, cache append and query set-up) is done, 2 when its
  * stream over the cached positions is done, 3 on exit (a workgroup with no
  * work writes entry then three equal exit stamps).  w is the workgroup
- * index, (slot * n_kv_heads + kv-head) * chunks + chunk.  stamps: device,
+ * index, (r * n_kv_heads + kv-head) * chunks + chunk, where the r-th slot
+ * in the attention order is the r-th active slot by descending position
+ * (ties by slot number), the inactive slots following in ascending order
+ * (attention runs the longest windows first).  stamps: device,
  * 8-byte aligned, at least 4 * max_workgroups entries; max_workgroups must
  * cover the launch (FD_E_INVAL).  NULL turns it off.  FD_EXEC_KERNELS
  * profiles only (FD_E_UNSUPPORTED otherwise).

@@ -30,7 +30,8 @@ def test_attention_trace_stamps_every_task_and_changes_nothing():
     sessions at frames 0, 70 and 300: the traced step's outputs, cache and
     positions equal the untraced step's bit for bit; every task of the
     traced layer writes four non-decreasing stamps (a task with no work:
-    three equal exit stamps); bad arguments are refused."""
+    three equal exit stamps; the tasks run the slots longest window
+    first); bad arguments are refused."""
     cfg = synth.scaled_config("7b_s8_p256", n_layers=3, d_model=512, n_heads=4, n_kv_heads=4,
                               d_ffn=1024, max_slots=4, max_context=512)
     say("trace: bf16/FP8, 4 slots, 2 chunks")
@@ -70,9 +71,13 @@ def test_attention_trace_stamps_every_task_and_changes_nothing():
     check(bool(np.all(np.diff(st, axis=1) >= 0)), "stamps go backwards")
     span_us = (st[:, 3].max() - st[:, 0].min()) / 100.0
     check(0 < span_us < 1e5, f"span {span_us} us")
-    # task (slot, head, chunk) has work when its slot is active and the chunk
-    # starts below the slot's p + 1 attended positions
-    idle = [((s * cfg["n_kv_heads"] + g) * 2 + c) for s in range(cfg["max_slots"])
+    # workgroup (r, head, chunk) runs slot order[r]: the active slots by
+    # descending position (ties by slot), then the free one; it has work
+    # when its slot is active and the chunk starts below the slot's p + 1
+    # attended positions
+    order = sorted(slots, key=lambda s: (-start[s], s)) + [s for s in range(cfg["max_slots"])
+                                                        if s not in slots]
+    idle = [((r * cfg["n_kv_heads"] + g) * 2 + c) for r, s in enumerate(order)
             for g in range(cfg["n_kv_heads"]) for c in range(2)
             if s not in slots or c * 256 >= start[s] + 1]
     check(len(idle) == 4 * 2 + 2 * 4, f"{len(idle)} idle tasks")

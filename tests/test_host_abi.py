@@ -312,9 +312,32 @@ class Pool:
         return st, a.value, p.value
 
     def image(self):
-        out = (ctypes.c_int32 * (2 * self.n))()
+        """active[S] + pos[S] (the attention order is checked separately)."""
+        return self.full_image()[:2 * self.n]
+
+    def full_image(self):
+        out = (ctypes.c_int32 * (3 * self.n))()
         self.h.fdh_pool_image(self.p, out)
         return list(out)
+
+
+def test_attention_order_is_longest_first(host):
+    """The slot table's third part orders the slots for attention: active
+    slots by descending position (ties by slot number), then the inactive
+    slots ascending; a permutation of every slot, refreshed with the table."""
+    P = Pool(host, 7, 100)
+    st, ids = P.alloc(5)
+    assert st == FD_OK and ids == [0, 1, 2, 3, 4]
+    for s, p in zip(ids, [10, 70, 10, 99, 0]):
+        assert host.fdh_pool_set_position(P.p, s, p) == FD_OK
+    assert P.free([2]) == FD_OK
+    img = P.full_image()
+    order = img[14:]
+    assert order == [3, 1, 0, 4, 2, 5, 6]
+    assert sorted(order) == list(range(7))
+    act, pos = img[:7], img[7:14]
+    lens = [pos[s] for s in order if act[s]]
+    assert lens == sorted(lens, reverse=True)
 
 
 def test_slot_state_machine(host):
