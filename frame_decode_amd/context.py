@@ -194,5 +194,7 @@ class Context:
                       c["head_dim"])
 
     def slot_table_view(self) -> torch.Tensor:
+        """Device slot table as int32 [3][S]: active flags, positions, and
+        the order attention takes the slots in."""
         S = self.cfg["max_slots"]
-        return self.slot_table[: 8 * S].view(torch.int32).view(2, S)
+        return self.slot_table[: 12 * S].view(torch.int32).view(3, S)

@@ -113,9 +113,15 @@ def _run_steps(cfg, model, slot_pos, n_steps, *, tol, sentinel=True, gain_noise=
         for s in slots:
             pos[s] += 1
             assert ctx.fd_slot_state(s) == (1, pos[s])
-    dev_pos = ctx.slot_table_view().cpu().numpy()
+    dev = ctx.slot_table_view().cpu().numpy()
     for s in slots:
-        assert dev_pos[1, s] == pos[s], "device position must advance with the host's"
+        assert dev[1, s] == pos[s], "device position must advance with the host's"
+    # attention order: a permutation, the active slots first by descending
+    # position (ties by slot), then the inactive ones ascending
+    order = [int(v) for v in dev[2]]
+    S = cfg["max_slots"]
+    want = sorted(slots, key=lambda s: (-pos[s], s)) + [s for s in range(S) if s not in slots]
+    check(order == want, f"attention order {order[:8]}... differs from {want[:8]}...")
     return ctx, orc, slots, pos, worst
 
 
