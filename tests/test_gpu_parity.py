@@ -243,23 +243,28 @@ def test_fp32_gqa_with_depth_loop(exec_mode):
     _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
 
 
-@pytest.mark.parametrize("max_slots", [5, 56, 90])
-def test_fp32_three_product_projections(max_slots):
-    """The opt-in three-product fp32 projections (FD_TUNE x3=1: weights and
-    rows as bf16 high and low parts, w_lo*x_hi + w_hi*x_lo + w_hi*x_hi with
-    fp32 sums) on the talker geometry with its depth loop and input
-    projection, with one, four and (two m-groups of at most five) six
-    16-row tiles of sessions: 1e-3, cache indexing bit-exact."""
+@pytest.mark.parametrize("max_slots,x3", [(40, 0), (70, 0), (5, 1), (56, 1), (90, 1)],
+                         ids=["f32-3tiles", "f32-5tiles", "x3-1tile", "x3-4tiles", "x3-6tiles"])
+def test_fp32_projection_tilings(max_slots, x3):
+    """fp32 projections of the talker geometry (with its depth loop and
+    input projection) at several 16-row tilings of sessions: with fp32
+    products at three and five tiles (the one- and two-block kernels with
+    and without k-splits, planes, reduce and direct epilogues), and with the
+    opt-in three-product loop (FD_TUNE x3=1: weights and rows as bf16 high
+    and low parts, w_lo*x_hi + w_hi*x_lo + w_hi*x_hi with fp32 sums) at one,
+    four and (two m-groups of at most five) six tiles: 1e-3, cache indexing
+    bit-exact."""
     cfg = synth.scaled_config("talker_s56", n_layers=2, d_model=384, d_ffn=768, max_slots=max_slots,
                               max_context=300, depth_layers=2, depth_d=256, depth_heads=2,
                               depth_kv_heads=2, depth_ffn=512, exec_mode=0)
     model = synth.Model(cfg, gain_noise=True)
     start = [0, 63, 64, 200] if max_slots == 5 else [(37 * i) % 290 for i in range(max_slots - 2)]
-    os.environ["FD_TUNE"] = "x3=1"
+    if x3:
+        os.environ["FD_TUNE"] = "x3=1"
     try:
         ctx, orc, slots, pos, worst = _run_steps(cfg, model, start, 2, tol=1e-3)
     finally:
-        del os.environ["FD_TUNE"]
+        os.environ.pop("FD_TUNE", None)
     _check_cache(ctx, orc, cfg, slots, pos, dict(zip(slots, start)))
 
 
