@@ -77,7 +77,8 @@ class FdKvView(ctypes.Structure):
 EXPORTS = ["fd_plan", "fd_init", "fd_alloc_slots", "fd_step", "fd_step_tokens", "fd_step_static",
            "fd_free", "fd_destroy",
            "fd_kv_layout", "fd_set_position", "fd_slot_state", "fd_kv_write", "fd_sync",
-           "fd_profile", "fd_profile_read", "fd_trace_attention", "fd_read_probe", "fd_last_error",
+           "fd_profile", "fd_profile_read", "fd_trace_attention", "fd_walk_abort_next", "fd_read_probe",
+           "fd_last_error",
            "fd_status_str"]
 
 FD_N_KINDS = 15
@@ -122,6 +123,7 @@ def _proto(lib):
     lib.fd_sync.argtypes = [c_p, c_p]
     lib.fd_profile.argtypes = [c_p, c_i32]
     lib.fd_trace_attention.argtypes = [c_p, c_p, c_i32, c_i32]
+    lib.fd_walk_abort_next.argtypes = [c_p]
     lib.fd_profile_read.argtypes = [c_p, P(ctypes.c_double), P(ctypes.c_int64), c_i32]
     lib.fd_read_probe.argtypes = [c_p, ctypes.c_uint64, c_p, c_i32, c_p]
     lib.fd_last_error.argtypes = [c_p]

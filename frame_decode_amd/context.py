@@ -156,6 +156,11 @@ class Context:
         _check(_lib().fd_trace_attention(self._ctx, ctypes.c_void_p(_ptr(stamps)), int(layer), int(n)),
                self._ctx)
 
+    def fd_walk_abort_next(self) -> None:
+        """The next step's persistent walk starts with its abort flag set
+        (every workgroup leaves at its first barrier wait)."""
+        _check(_lib().fd_walk_abort_next(self._ctx), self._ctx)
+
     def fd_profile(self, enable: bool) -> None:
         _check(_lib().fd_profile(self._ctx, 1 if enable else 0), self._ctx)
 

@@ -51,6 +51,7 @@ struct fd_ctx {
     const void* head_x = nullptr;
     const void* head_x_lo = nullptr;
     bool walk_launched = false;
+    bool walk_abort_next = false;  // fd_walk_abort_next: the next walk starts aborted
     // device-clock trace of one layer's attention launch (fd_trace_attention)
     uint64_t* trace = nullptr;
     int trace_layer = -1;
@@ -803,6 +804,8 @@ fd_status step_impl(fd_ctx* c, const void* x_in, void* y_out, void* depth_out, v
         w.x_in = x_in;
         w.y_out = y_out;
         w.depth_out = depth_out;
+        w.abort_init = c->walk_abort_next ? 1 : 0;
+        c->walk_abort_next = false;
         e = timed(c, K_WALK, st, [&] { return fd::launch_walk(w, c->walk_shape, c->walk_grid, st); });
         if (e != hipSuccess) return hip_fail(c, e, "fd_step launch");
         c->walk_launched = true;
@@ -1068,6 +1071,13 @@ fd_status fd_kv_layout(fd_ctx* c, fd_kv_view* out) {
     out->kv_scale = pl.kv_fp8 ? (const float*)P(c, pl.main.kvsig) : nullptr;
     out->slot_active = slot_active(c);
     out->slot_pos = slot_pos(c);
+    return FD_OK;
+}
+
+fd_status fd_walk_abort_next(fd_ctx* c) {
+    if (!c) return FD_E_INVAL;
+    if (!c->plan.walk) return fail(c, FD_E_UNSUPPORTED, "fd_walk_abort_next: FD_EXEC_WALK profiles only");
+    c->walk_abort_next = true;
     return FD_OK;
 }
 

@@ -180,6 +180,8 @@ struct WalkArgs {
     void* depth_out;
     unsigned* bar;         // barrier counter, zeroed before the launch
     int* abort_flag;       // set when a barrier wait times out
+    int abort_init;        // value the flag starts at (1: every workgroup leaves at its first
+                           // barrier wait, the abort path forced from the host)
 };
 
 // Shape a walk kernel is compiled for: weight / cache types, m-tiles per

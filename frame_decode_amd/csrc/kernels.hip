@@ -1795,14 +1795,19 @@ __device__ __forceinline__ void walk_arrive(unsigned* cnt) {
 }
 
 // Wait until the counter reaches `target`.  Bounded: a workgroup that waits
-// too long sets the abort flag, and every workgroup leaves at its next wait.
+// too long sets the abort flag, and every workgroup leaves at its next wait
+// (the flag is read first, so a set flag ends every later wait at once).
 __device__ __forceinline__ bool walk_wait(unsigned* cnt, unsigned target, int* abort_flag) {
     __shared__ int s_ok;
     if (threadIdx.x == 0) {
         int ok = 1;
         for (unsigned spin = 0;; ++spin) {
+            if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                ok = 0;
+                break;
+            }
             if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
-            if (spin > (1u << 21) || __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            if (spin > (1u << 21)) {
                 __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
                 break;
@@ -1887,10 +1892,10 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkArgs w) {
     }
 }
 
-__global__ void walk_reset_kernel(unsigned* bar, int* abort_flag) {
+__global__ void walk_reset_kernel(unsigned* bar, int* abort_flag, int abort_init) {
     if (threadIdx.x == 0) {
         *bar = 0u;
-        *abort_flag = 0;
+        *abort_flag = abort_init;
     }
 }
 
@@ -2219,7 +2224,7 @@ int walk_grid(const WalkShape& s) {
 hipError_t launch_walk(const WalkArgs& w, const WalkShape& s, int grid, hipStream_t st) {
     const void* fn = walk_fn_for(s);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(walk_reset_kernel, dim3(1), dim3(64), 0, st, w.bar, w.abort_flag);
+    hipLaunchKernelGGL(walk_reset_kernel, dim3(1), dim3(64), 0, st, w.bar, w.abort_flag, w.abort_init);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     WalkArgs a = w;

@@ -429,6 +429,18 @@ fd_status fd_profile_read(fd_ctx* ctx, double* ms_out, int64_t* launches_out, in
 fd_status fd_trace_attention(fd_ctx* ctx, uint64_t* stamps, int32_t layer, int32_t max_workgroups);
 
 /*
+ * Forces the persistent walk's abort path (test hook, FD_EXEC_WALK profiles;
+ * FD_E_UNSUPPORTED otherwise): the ctx's next fd_step launches the walk with
+ * its abort flag already set, so every workgroup leaves at its first grid
+ * barrier wait, as after a timed-out wait, without any wait running out.
+ * That step's outputs, cache entries and device positions are then
+ * incomplete; fd_sync reports FD_E_DEVICE and marks the active slots stale
+ * (fd_step gives FD_E_STATE until each is given a position with
+ * fd_set_position or freed).  Applies to one step.
+ */
+fd_status fd_walk_abort_next(fd_ctx* ctx);
+
+/*
  * HBM read probe (bench hook): enqueues one kernel that reads `bytes` of
  * device memory at `buf` (16-byte aligned) once with wide loads, `grid`
  * workgroups of 256 threads, and may write to device words sink[0..grid).

@@ -1,6 +1,8 @@
-"""The measurement hooks on the GPU: the attention kernel's device-clock
-trace (fd_trace_attention) and the per-kind launch timing (fd_profile).
-Neither may change what a step computes."""
+"""The measurement and test hooks on the GPU: the attention kernel's
+device-clock trace (fd_trace_attention), the per-kind launch timing
+(fd_profile) and the persistent walk's forced abort (fd_walk_abort_next).
+The first two may not change what a step computes; after the third the
+ctx must recover to the undisturbed result."""
 import os
 
 import numpy as np
@@ -8,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from frame_decode_amd.abi import FD_E_INVAL, FD_E_UNSUPPORTED, FdError
+from frame_decode_amd.abi import FD_E_DEVICE, FD_E_INVAL, FD_E_STATE, FD_E_UNSUPPORTED, FdError
 from tests.helpers import check, make_context, rows_input, say
 
 pytestmark = pytest.mark.gpu
@@ -112,6 +114,63 @@ def test_attention_trace_refused_by_the_walk():
         ctx.fd_trace_attention(stamps, layer=0)
     assert e.value.status == FD_E_UNSUPPORTED
     ctx.fd_destroy()
+
+
+def test_walk_abort_path_marks_slots_stale_and_recovers():
+    """The persistent walk's bounded-wait abort path, forced from the host
+    (fd_walk_abort_next: the launch starts with its abort flag set, so every
+    workgroup leaves at its first barrier wait and nothing waits out a
+    timeout): fd_sync reports FD_E_DEVICE, fd_step then refuses the stale
+    slots with FD_E_STATE, and after fd_set_position the step gives the
+    outputs, cache and positions of an undisturbed context bit for bit.
+    The kernel-sequence profile refuses the hook."""
+    cfg = synth.scaled_config("7b_s8_p256", n_layers=2, d_model=256, n_heads=2, n_kv_heads=2,
+                              d_ffn=512, max_slots=4, max_context=64, exec_mode=1)
+    say("walk abort: two contexts")
+    a = _ctx(cfg)
+    b = _ctx(cfg)
+    sa, sb = a.fd_alloc_slots(3), b.fd_alloc_slots(3)
+    assert sa == sb == [0, 1, 2]
+    for ctx in (a, b):  # (the arenas start uninitialised: compare them from zero)
+        ctx.arena_view().zero_()
+    torch.cuda.synchronize()
+    sess = {s: 700 + s for s in sa}
+    frames = {s: 0 for s in sa}
+    _, x = rows_input(cfg, sess, frames)
+    ya = torch.empty((cfg["max_slots"], cfg["d_model"]), device="cuda", dtype=torch.bfloat16)
+    yb = torch.empty_like(ya)
+    for ctx, y in ((a, ya), (b, yb)):  # one normal step on both
+        ctx.fd_step(x, y)
+        ctx.fd_sync()
+    frames = {s: 1 for s in sa}
+    _, x = rows_input(cfg, sess, frames)
+
+    a.fd_walk_abort_next()
+    a.fd_step(x, ya)
+    with pytest.raises(FdError) as e:
+        a.fd_sync()
+    assert e.value.status == FD_E_DEVICE
+    with pytest.raises(FdError) as e:
+        a.fd_step(x, ya)
+    assert e.value.status == FD_E_STATE
+    for s in sa:
+        a.fd_set_position(s, 1)
+    a.fd_step(x, ya)
+    a.fd_sync()
+    b.fd_step(x, yb)
+    b.fd_sync()
+    check(torch.equal(ya, yb), "the recovered step's outputs differ from an undisturbed step's")
+    check(torch.equal(a.arena_view(), b.arena_view()), "the recovered step's cache differs")
+    for s in sa:
+        assert a.fd_slot_state(s) == b.fd_slot_state(s) == (1, 2)
+    a.fd_destroy()
+    b.fd_destroy()
+
+    k = _ctx(dict(cfg, exec_mode=0))
+    with pytest.raises(FdError) as e:
+        k.fd_walk_abort_next()
+    assert e.value.status == FD_E_UNSUPPORTED
+    k.fd_destroy()
 
 
 def test_profile_kinds_split_the_depth_stack():
